@@ -1,0 +1,190 @@
+"""CPU oracle for the exact causal long FFT convolution (float64).
+
+TEST INFRASTRUCTURE ONLY: the tests, the package smoke check and the
+benchmark's CPU-baseline leg are the only users.  The HIP library never
+imports, links or calls anything here, and this module imports nothing from
+the HIP package.
+
+What is computed (FlashFFTConv summary page: "Summary" and "Key results" say
+the method computes exact FFT convolutions; the "Measured effects" row on
+fusing gating gives the gated form; "Approach" names partial and
+frequency-sparse filters):
+
+    y[b,h,t] = v[b,h,t] * sum_{s<=min(t,L-1)} k[h,s] * (u*w)[b,h,t-s],  t < N
+
+Route D (``direct``) writes that sum out; route F (``fft_conv``) uses the
+convolution theorem with the oracle's own radix-2 FFT (``fft``), which is the
+only route that can apply a frequency mask (``oracle_fft_conv`` in the C file
+states the mask reading).  Every function is pinned by the ``-m "not gpu"``
+tests to brute force, closed forms or an independent library routine.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fftconv_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "_oracle.so")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+
+
+def build(src: str = _SRC, out: str = _LIB_PATH) -> str:
+    """Compile the oracle C file with gcc (plain -O2, OpenMP, no FMA contraction)."""
+    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+           "-std=c11", src, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def _bind(lib):
+    lib.oracle_fft.argtypes = [_dp, _dp, ctypes.c_int64, ctypes.c_int]
+    lib.oracle_fft.restype = ctypes.c_int
+    lib.oracle_direct.argtypes = [_dp, _dp, _dp, _dp] + [ctypes.c_int64] * 4 + [_dp, ctypes.c_int]
+    lib.oracle_direct.restype = ctypes.c_int
+    lib.oracle_direct_points.argtypes = ([_dp, _dp, _dp, _dp] + [ctypes.c_int64] * 4
+                                         + [_i64p, ctypes.c_int64, _dp, ctypes.c_int])
+    lib.oracle_direct_points.restype = ctypes.c_int
+    lib.oracle_fft_conv.argtypes = ([_dp, _dp, _dp, _dp] + [ctypes.c_int64] * 4
+                                    + [_u8p, ctypes.c_int64, _dp, _dp, ctypes.c_int])
+    lib.oracle_fft_conv.restype = ctypes.c_int
+    lib.oracle_masked_filter.argtypes = [_dp, ctypes.c_int64, ctypes.c_int64, _u8p, _dp]
+    lib.oracle_masked_filter.restype = ctypes.c_int
+    lib.oracle_circular_points.argtypes = [_dp, _dp, _dp, _dp, ctypes.c_int64, _i64p,
+                                           ctypes.c_int64, _dp]
+    lib.oracle_circular_points.restype = ctypes.c_int
+    lib.oracle_mask_blocks.argtypes = [ctypes.c_int64]
+    lib.oracle_mask_blocks.restype = ctypes.c_int64
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = ctypes.c_int
+    return lib
+
+
+def load(path: str | None = None):
+    """Load the compiled oracle (building it only when no library exists)."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        _lib = _bind(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def _f64(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a, typ=_dp):
+    return None if a is None else a.ctypes.data_as(typ)
+
+
+def max_threads(lib=None) -> int:
+    return (lib or load()).oracle_max_threads()
+
+
+def mask_blocks(N: int) -> int:
+    return int(load().oracle_mask_blocks(N))
+
+
+def fft(x, sign: int = -1, lib=None):
+    """Complex FFT of length M (power of two); sign=-1 forward, +1 unnormalised inverse."""
+    lib = lib or load()
+    x = np.asarray(x, dtype=np.complex128)
+    re = np.ascontiguousarray(x.real.copy())
+    im = np.ascontiguousarray(x.imag.copy())
+    rc = lib.oracle_fft(_ptr(re), _ptr(im), x.size, sign)
+    if rc:
+        raise ValueError("oracle_fft: length must be a power of two")
+    return re + 1j * im
+
+
+def direct(u, k, w=None, v=None, L=None, threads: int = 0, lib=None):
+    """Route D over whole tensors: u, w, v (B, H, N); k (H, L)."""
+    lib = lib or load()
+    u, w, v, k = _f64(u), _f64(w), _f64(v), _f64(k)
+    B, H, N = u.shape
+    L = k.shape[1] if L is None else L
+    y = np.empty((B, H, N), dtype=np.float64)
+    rc = lib.oracle_direct(_ptr(u), _ptr(w), _ptr(v), _ptr(k), B, H, N, L, _ptr(y), threads)
+    if rc:
+        raise ValueError("oracle_direct: bad arguments")
+    return y
+
+
+def direct_points(u, k, pts, w=None, v=None, threads: int = 0, lib=None):
+    """Route D at sampled (b, h, t) triples (pts: (P, 3) int64)."""
+    lib = lib or load()
+    u, w, v, k = _f64(u), _f64(w), _f64(v), _f64(k)
+    B, H, N = u.shape
+    L = k.shape[1]
+    pts = np.ascontiguousarray(pts, dtype=np.int64)
+    out = np.empty(pts.shape[0], dtype=np.float64)
+    rc = lib.oracle_direct_points(_ptr(u), _ptr(w), _ptr(v), _ptr(k), B, H, N, L,
+                                  _ptr(pts, _i64p), pts.shape[0], _ptr(out), threads)
+    if rc:
+        raise ValueError("oracle_direct_points: bad arguments")
+    return out
+
+
+def fft_conv(u, k, w=None, v=None, mask=None, M=None, threads: int = 0, lib=None,
+             return_imag: bool = False):
+    """Route F over whole tensors, FFT size M (default 2N), optional (H, 128) mask."""
+    lib = lib or load()
+    u, w, v, k = _f64(u), _f64(w), _f64(v), _f64(k)
+    B, H, N = u.shape
+    L = k.shape[1]
+    M = 2 * N if M is None else M
+    m = None if mask is None else np.ascontiguousarray(mask, dtype=np.uint8)
+    y = np.empty((B, H, N), dtype=np.float64)
+    imag = ctypes.c_double(0.0)
+    rc = lib.oracle_fft_conv(_ptr(u), _ptr(w), _ptr(v), _ptr(k), B, H, N, L,
+                             _ptr(m, _u8p), M, _ptr(y), ctypes.byref(imag), threads)
+    if rc:
+        raise ValueError(f"oracle_fft_conv failed ({rc})")
+    return (y, imag.value) if return_imag else y
+
+
+def masked_filter(k_row, N: int, mask_row, lib=None):
+    """k' = Re IFFT(mask * FFT(pad(k, 2N))), length 2N."""
+    lib = lib or load()
+    k_row = _f64(k_row)
+    m = np.ascontiguousarray(mask_row, dtype=np.uint8)
+    kp = np.empty(2 * N, dtype=np.float64)
+    rc = lib.oracle_masked_filter(_ptr(k_row), k_row.size, N, _ptr(m, _u8p), _ptr(kp))
+    if rc:
+        raise ValueError("oracle_masked_filter: bad arguments")
+    return kp
+
+
+def circular_points(u_row, kp, ts, w_row=None, v_row=None, lib=None):
+    """Masked output of one sequence at times ts through the circular form."""
+    lib = lib or load()
+    u_row, w_row, v_row, kp = _f64(u_row), _f64(w_row), _f64(v_row), _f64(kp)
+    ts = np.ascontiguousarray(ts, dtype=np.int64)
+    out = np.empty(ts.size, dtype=np.float64)
+    rc = lib.oracle_circular_points(_ptr(u_row), _ptr(w_row), _ptr(v_row), _ptr(kp),
+                                    u_row.size, _ptr(ts, _i64p), ts.size, _ptr(out))
+    if rc:
+        raise ValueError("oracle_circular_points: bad arguments")
+    return out
+
+
+def rel_l2(a, b) -> float:
+    """||a - b||_2 / ||b||_2 in float64 (b is the oracle's value)."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    den = np.sqrt(np.sum(b * b))
+    num = np.sqrt(np.sum((a - b) ** 2))
+    return float(num / den) if den > 0 else float(num)
