@@ -1,0 +1,136 @@
+/*
+ * fftconv.h -- C ABI of the MI355X (gfx950) exact long causal FFT convolution.
+ *
+ * The operation (FlashFFTConv summary page, "Summary": a fused kernel that
+ * computes *exact* FFT convolutions for long sequences, with partial and
+ * frequency-sparse variants; "Problem": filters as long as the sequence;
+ * "Measured effects", row on fusing gating into the convolution: the gated
+ * form) is, for every batch row b and channel h,
+ *
+ *     out[b,h,t] = v[b,h,t] * sum_{s=0}^{min(t, L-1)} k[h,s] * u[b,h,t-s] * w[b,h,t-s]
+ *                = v * irfft( rfft(pad(u*w, 2N)) * rfft(pad(k, 2N)) )[:N]      (t < N)
+ *
+ * computed through the convolution theorem with an FFT of size 2N.  With a
+ * frequency mask ("Approach": sparsity realised by skipping blocks of the
+ * matmuls; "Key results": 79 % of frequency-domain filter entries zeroed) the
+ * filter spectrum's bins in zeroed blocks are treated as zero:
+ *
+ *     out = v * irfft( rfft(pad(u*w, 2N)) * (mask o rfft(pad(k, 2N))) )[:N]
+ *
+ * Mask blocks: the N+1 rfft bins f in [0, N] form 128 blocks of N/128 bins
+ * (block = min(f / (N/128), 127), so the Nyquist bin N joins block 127); the
+ * Hermitian mirror 2N-f of each bin follows it.
+ *
+ * Conventions for every function below:
+ *  - Tensors are DEVICE pointers owned by the caller, dense and row-major:
+ *      u, w, v, out : (B, H, N)  storage dtype
+ *      k            : (H, L)     storage dtype
+ *      mask         : (H, fftconv_mask_blocks(N)) uint8, 1 = keep, 0 = zero
+ *    Every tensor pointer must be 16-byte aligned.  `out` must not overlap
+ *    any input.
+ *  - K_f (the prepared filter) is a caller-allocated device buffer of
+ *    fftconv_filter_bytes() bytes.  Its contents are library-defined and
+ *    opaque: a header (magic, version, N, H, L, dtype), one fp32 scale per
+ *    channel, then the filter spectrum in the order the forward kernels read
+ *    it (fp32 bins for FFTCONV_F32, scaled fp16 bins for FFTCONV_F16 and
+ *    FFTCONV_BF16).  It depends on N and dtype, not on B.
+ *  - Workspace: sequences longer than the largest on-chip size stream through
+ *    HBM in several passes and need fftconv_workspace_bytes() bytes of device
+ *    scratch, owned by the caller; 0 bytes (and a NULL pointer) suffice
+ *    otherwise.
+ *  - Supported sizes: N a power of two in [1024, 4194304]; 1 <= L <= N;
+ *    B, H >= 0 (B*H == 0 enqueues nothing and returns FFTCONV_OK).
+ *  - Every call is asynchronous on `stream` (a HIP stream, NULL = the default
+ *    stream) unless stated otherwise, and returns a status; arguments are
+ *    validated before anything is enqueued, so on any error status nothing
+ *    was launched.  fftconv_last_error() gives the detail of the calling
+ *    thread's last non-OK status.  Calls on different streams may run
+ *    concurrently; the library's only shared state is a per-device cache of
+ *    twiddle tables guarded by a mutex.
+ */
+#ifndef FFTCONV_H
+#define FFTCONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same opaque type as HIP's hipStream_t. */
+typedef struct ihipStream_t *hipStream_t;
+
+typedef enum {
+    FFTCONV_F32 = 0,  /* fp32 storage, fp32 arithmetic                          */
+    FFTCONV_F16 = 1,  /* fp16 storage, fp32 accumulation                        */
+    FFTCONV_BF16 = 2  /* bf16 storage, fp32 accumulation                        */
+} fftconv_dtype_t;
+
+typedef enum {
+    FFTCONV_OK = 0,
+    FFTCONV_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size, overlap  */
+    FFTCONV_ERR_UNSUPPORTED = 2,      /* N not a supported power of two, bad dtype   */
+    FFTCONV_ERR_WORKSPACE = 3,        /* workspace smaller than required             */
+    FFTCONV_ERR_FILTER_MISMATCH = 4,  /* K_f prepared for another N, H, L or dtype   */
+    FFTCONV_ERR_HIP = 5               /* a HIP runtime call or kernel launch failed  */
+} fftconv_status_t;
+
+/* Bytes of the prepared-filter buffer K_f for H channels at sequence length N.
+ * Returns 0 for unsupported N, dtype or H < 1. */
+size_t fftconv_filter_bytes(int64_t H, int64_t N, fftconv_dtype_t dtype);
+
+/* Bytes of device scratch fftconv_fwd needs for B*H sequences of length N
+ * (fftconv_prepare_filter needs the value for B = 1).  0 when the whole
+ * sequence fits on chip.  Returns 0 for unsupported arguments. */
+size_t fftconv_workspace_bytes(int64_t B, int64_t H, int64_t N, fftconv_dtype_t dtype);
+
+/* Number of frequency blocks per channel the mask addresses (128 for every
+ * supported N; 0 for unsupported N). */
+int64_t fftconv_mask_blocks(int64_t N);
+
+/* Transform the time-domain filter k (H, L_filter) into K_f for sequences of
+ * length N: K_f holds rfft(pad(k, 2N)) ("Approach": the filter spectrum the
+ * convolution multiplies by; partial convolution = L_filter < N, where only
+ * the input blocks holding taps are transformed).  Needs workspace of
+ * fftconv_workspace_bytes(1, H, N, dtype) bytes for N beyond the on-chip
+ * size.  K_f_bytes must be >= fftconv_filter_bytes(H, N, dtype). */
+fftconv_status_t fftconv_prepare_filter(const void *k, int64_t H, int64_t L_filter, int64_t N,
+                                        fftconv_dtype_t dtype, void *K_f, size_t K_f_bytes,
+                                        void *workspace, size_t workspace_bytes,
+                                        hipStream_t stream);
+
+/* Gated causal FFT convolution (formula in the file header).
+ *   u        input (B, H, N), required
+ *   K_f      filter prepared by fftconv_prepare_filter for the same H, L_filter,
+ *            N and dtype (checked against its header only when the
+ *            environment variable FFTCONV_CHECK=1 is set, since that check
+ *            synchronises)
+ *   w, v     input and output gates (B, H, N); NULL = no gate
+ *   out      output (B, H, N)
+ *   sparsity_mask  (H, fftconv_mask_blocks(N)) uint8 device array, or NULL
+ *            for a dense filter spectrum
+ *   workspace / workspace_bytes  device scratch, see fftconv_workspace_bytes */
+fftconv_status_t fftconv_fwd(const void *u, const void *K_f, const void *w, const void *v,
+                             void *out, int64_t B, int64_t H, int64_t N, int64_t L_filter,
+                             const uint8_t *sparsity_mask, fftconv_dtype_t dtype,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Static text for a status code. */
+const char *fftconv_status_string(fftconv_status_t status);
+
+/* Detail of the calling thread's last non-OK status ("" if none). */
+const char *fftconv_last_error(void);
+
+/* Test helper, SYNCHRONOUS: decode K_f into natural-order rfft bins
+ * K[h, f] = rfft(pad(k[h], 2N))[f], f in [0, N], as float64 (re, im) pairs in
+ * host memory host_out[(H, N+1, 2)]. */
+fftconv_status_t fftconv_export_filter_rfft(const void *K_f, int64_t H, int64_t N,
+                                            fftconv_dtype_t dtype, double *host_out,
+                                            hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FFTCONV_H */

@@ -1,0 +1,355 @@
+// api.cpp -- host side of the C ABI declared in include/fftconv.h:
+// argument validation, status codes and per-thread error text, the per-device
+// twiddle-table cache, K_f layout, and dispatch to the fused (N <= 16384) or
+// multi-pass (larger N) kernels.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "../../include/fftconv.h"
+#include "fftconv_internal.hpp"
+
+using namespace fftconv;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fftconv_status_t fail(fftconv_status_t st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+fftconv_status_t ok() { return FFTCONV_OK; }
+
+int log2_exact(int64_t n) {
+    if (n <= 0 || (n & (n - 1)) != 0) return -1;
+    int l = 0;
+    while ((int64_t(1) << l) < n) ++l;
+    return l;
+}
+
+bool dtype_ok(int dt) { return dt == FFTCONV_F32 || dt == FFTCONV_F16 || dt == FFTCONV_BF16; }
+size_t elem_bytes(int dt) { return dt == FFTCONV_F32 ? 4 : 2; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    auto pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
+std::mutex g_tables_mu;
+std::map<std::pair<int, int>, Tables> g_tables;
+
+hipError_t build_tables(int logn, Tables *out) {
+    const int64_t n = int64_t(1) << logn;
+    std::vector<float2> tw(n), tw2(n);
+    const double pi = 3.14159265358979323846264338327950288;
+    for (int64_t j = 0; j < n; ++j) {
+        const double a = -2.0 * pi * (double)j / (double)n;
+        tw[j] = make_float2((float)std::cos(a), (float)std::sin(a));
+        const double b = -pi * (double)j / (double)n;
+        tw2[j] = make_float2((float)std::cos(b), (float)std::sin(b));
+    }
+    float2 *d = nullptr;
+    hipError_t e = hipMalloc(&d, sizeof(float2) * 2 * n);
+    if (e != hipSuccess) return e;
+    e = hipMemcpy(d, tw.data(), sizeof(float2) * n, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(d + n, tw2.data(), sizeof(float2) * n, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        (void)hipFree(d);
+        return e;
+    }
+    out->tw = d;
+    out->tw2 = d + n;
+    return hipSuccess;
+}
+
+}  // namespace
+
+namespace fftconv {
+
+hipError_t get_tables(int logn, Tables *out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lk(g_tables_mu);
+    auto key = std::make_pair(dev, logn);
+    auto it = g_tables.find(key);
+    if (it != g_tables.end()) {
+        *out = it->second;
+        return hipSuccess;
+    }
+    Tables t{};
+    e = build_tables(logn, &t);
+    if (e != hipSuccess) return e;
+    g_tables[key] = t;
+    *out = t;
+    return hipSuccess;
+}
+
+MpSplit mp_split(int logn) {
+    // inner (on-chip) transform of 2^log2 points, outer of 2^log1 points
+    MpSplit s;
+    s.log2 = logn - 8 < kFusedMaxLog ? logn - 8 : kFusedMaxLog;
+    if (s.log2 < 10) s.log2 = 10;
+    s.log1 = logn - s.log2;
+    return s;
+}
+
+int64_t mp_chunk(int logn) {
+    // keep one chunk's fp32 complex intermediate near 128 MiB
+    const int64_t per_seq = (int64_t(8)) << logn;
+    int64_t c = (int64_t(128) << 20) / per_seq;
+    return c < 1 ? 1 : c;
+}
+
+}  // namespace fftconv
+
+// ----------------------------------------------------------------- C ABI
+extern "C" {
+
+const char *fftconv_status_string(fftconv_status_t s) {
+    switch (s) {
+    case FFTCONV_OK: return "ok";
+    case FFTCONV_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case FFTCONV_ERR_UNSUPPORTED: return "unsupported size or dtype";
+    case FFTCONV_ERR_WORKSPACE: return "workspace too small";
+    case FFTCONV_ERR_FILTER_MISMATCH: return "prepared filter does not match the call";
+    case FFTCONV_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *fftconv_last_error(void) { return g_last_error.c_str(); }
+
+int64_t fftconv_mask_blocks(int64_t N) {
+    const int l = log2_exact(N);
+    return (l >= kMinLog && l <= kMaxLog) ? kMaskBlocks : 0;
+}
+
+size_t fftconv_filter_bytes(int64_t H, int64_t N, fftconv_dtype_t dtype) {
+    const int l = log2_exact(N);
+    if (l < kMinLog || l > kMaxLog || H < 1 || !dtype_ok(dtype)) return 0;
+    return kf_bins_off(H) + (size_t)H * (size_t)N * bin_bytes(dtype);
+}
+
+size_t fftconv_workspace_bytes(int64_t B, int64_t H, int64_t N, fftconv_dtype_t dtype) {
+    const int l = log2_exact(N);
+    if (l < kMinLog || l > kMaxLog || B < 0 || H < 0 || !dtype_ok(dtype)) return 0;
+    if (l <= kFusedMaxLog) return 0;
+    int64_t S = B * H;
+    const int64_t c = mp_chunk(l);
+    if (S > c) S = c;
+    return (size_t)S * (size_t)N * sizeof(float2);
+}
+
+fftconv_status_t fftconv_prepare_filter(const void *k, int64_t H, int64_t L, int64_t N,
+                                        fftconv_dtype_t dtype, void *K_f, size_t K_f_bytes,
+                                        void *workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+    g_last_error.clear();
+    if (!dtype_ok(dtype)) return fail(FFTCONV_ERR_UNSUPPORTED, "dtype %d is not supported", (int)dtype);
+    const int l = log2_exact(N);
+    if (l < kMinLog || l > kMaxLog)
+        return fail(FFTCONV_ERR_UNSUPPORTED, "N=%lld must be a power of two in [2^%d, 2^%d]",
+                    (long long)N, kMinLog, kMaxLog);
+    if (H < 1) return fail(FFTCONV_ERR_INVALID_ARGUMENT, "H=%lld must be >= 1", (long long)H);
+    if (L < 1 || L > N)
+        return fail(FFTCONV_ERR_INVALID_ARGUMENT, "L_filter=%lld must be in [1, N=%lld]",
+                    (long long)L, (long long)N);
+    if (!k || !K_f) return fail(FFTCONV_ERR_INVALID_ARGUMENT, "k and K_f must be non-null");
+    if (!aligned16(k) || !aligned16(K_f))
+        return fail(FFTCONV_ERR_INVALID_ARGUMENT, "k and K_f must be 16-byte aligned");
+    const size_t need = fftconv_filter_bytes(H, N, dtype);
+    if (K_f_bytes < need)
+        return fail(FFTCONV_ERR_INVALID_ARGUMENT, "K_f has %zu bytes, needs %zu", K_f_bytes, need);
+    if (overlap(k, (size_t)H * (size_t)L * elem_bytes(dtype), K_f, need))
+        return fail(FFTCONV_ERR_INVALID_ARGUMENT, "k overlaps K_f");
+    const size_t wneed = fftconv_workspace_bytes(1, H, N, dtype);
+    if (wneed > 0 && (workspace == nullptr || workspace_bytes < wneed))
+        return fail(FFTCONV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, wneed);
+    if (wneed > 0 && !aligned16(workspace))
+        return fail(FFTCONV_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+
+    char *base = static_cast<char *>(K_f);
+    float *kscale = reinterpret_cast<float *>(base + kf_scale_off());
+    void *kbins = base + kf_bins_off(H);
+    const bool fused = l <= kFusedMaxLog;
+    const MpSplit sp = mp_split(l);
+    KfHeader hdr{};
+    hdr.magic = kKfMagic;
+    hdr.version = kKfVersion;
+    hdr.N = N;
+    hdr.H = H;
+    hdr.L = L;
+    hdr.dtype = (int32_t)dtype;
+    hdr.layout = fused ? KF_NATURAL : KF_ROWS;
+    hdr.scale_off = (int64_t)kf_scale_off();
+    hdr.bins_off = (int64_t)kf_bins_off(H);
+    hdr.n1 = fused ? 0 : (int64_t(1) << sp.log1);
+    hdr.n2 = fused ? N : (int64_t(1) << sp.log2);
+
+    hipError_t e = launch_write_header(hdr, K_f, stream);
+    if (e == hipSuccess) e = launch_filter_scale(dtype, k, H, L, N, kscale, stream);
+    if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "filter setup launch: %s", hipGetErrorString(e));
+    if (fused) {
+        Tables tb{};
+        e = get_tables(l, &tb);
+        if (e == hipSuccess) e = launch_fused_prepare(l, dtype, k, L, kbins, kscale, tb, H, stream);
+    } else {
+        const int64_t c = mp_chunk(l);
+        for (int64_t h0 = 0; h0 < H && e == hipSuccess; h0 += c) {
+            const int64_t n = H - h0 < c ? H - h0 : c;
+            e = launch_multipass_prepare(l, dtype, k, L, kbins, kscale, workspace, H, h0, n, stream);
+        }
+    }
+    if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "prepare launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+fftconv_status_t fftconv_fwd(const void *u, const void *K_f, const void *w, const void *v,
+                             void *out, int64_t B, int64_t H, int64_t N, int64_t L,
+                             const uint8_t *mask, fftconv_dtype_t dtype, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+    g_last_error.clear();
+    if (!dtype_ok(dtype)) return fail(FFTCONV_ERR_UNSUPPORTED, "dtype %d is not supported", (int)dtype);
+    const int l = log2_exact(N);
+    if (l < kMinLog || l > kMaxLog)
+        return fail(FFTCONV_ERR_UNSUPPORTED, "N=%lld must be a power of two in [2^%d, 2^%d]",
+                    (long long)N, kMinLog, kMaxLog);
+    if (B < 0 || H < 0)
+        return fail(FFTCONV_ERR_INVALID_ARGUMENT, "B=%lld and H=%lld must be >= 0", (long long)B,
+                    (long long)H);
+    if (L < 1 || L > N)
+        return fail(FFTCONV_ERR_INVALID_ARGUMENT, "L_filter=%lld must be in [1, N=%lld]",
+                    (long long)L, (long long)N);
+    if (B * H == 0) return ok();
+    if (!u || !K_f || !out) return fail(FFTCONV_ERR_INVALID_ARGUMENT, "u, K_f and out must be non-null");
+    if (!aligned16(u) || !aligned16(K_f) || !aligned16(out) || (w && !aligned16(w)) ||
+        (v && !aligned16(v)) || (mask && !aligned16(mask)))
+        return fail(FFTCONV_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+    const size_t nbytes = (size_t)B * (size_t)H * (size_t)N * elem_bytes(dtype);
+    const size_t kfb = fftconv_filter_bytes(H, N, dtype);
+    if (overlap(out, nbytes, u, nbytes) || overlap(out, nbytes, w, nbytes) ||
+        overlap(out, nbytes, v, nbytes) || overlap(out, nbytes, K_f, kfb) ||
+        overlap(out, nbytes, mask, (size_t)H * kMaskBlocks))
+        return fail(FFTCONV_ERR_INVALID_ARGUMENT, "out overlaps an input");
+    const size_t wneed = fftconv_workspace_bytes(B, H, N, dtype);
+    if (wneed > 0 && (workspace == nullptr || workspace_bytes < wneed))
+        return fail(FFTCONV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, wneed);
+    if (wneed > 0 && !aligned16(workspace))
+        return fail(FFTCONV_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+    if (wneed > 0 && (overlap(workspace, wneed, out, nbytes) || overlap(workspace, wneed, u, nbytes)))
+        return fail(FFTCONV_ERR_INVALID_ARGUMENT, "workspace overlaps a tensor");
+
+    const char *chk = std::getenv("FFTCONV_CHECK");
+    if (chk && chk[0] == '1') {
+        KfHeader hdr{};
+        hipError_t e = hipMemcpyAsync(&hdr, K_f, sizeof hdr, hipMemcpyDeviceToHost, stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "reading the K_f header: %s", hipGetErrorString(e));
+        if (hdr.magic != kKfMagic || hdr.version != kKfVersion || hdr.N != N || hdr.H != H ||
+            hdr.L != L || hdr.dtype != (int32_t)dtype)
+            return fail(FFTCONV_ERR_FILTER_MISMATCH,
+                        "K_f header (N=%lld H=%lld L=%lld dtype=%d) does not match the call "
+                        "(N=%lld H=%lld L=%lld dtype=%d)",
+                        (long long)hdr.N, (long long)hdr.H, (long long)hdr.L, hdr.dtype,
+                        (long long)N, (long long)H, (long long)L, (int)dtype);
+    }
+
+    const char *base = static_cast<const char *>(K_f);
+    const float *kscale = reinterpret_cast<const float *>(base + kf_scale_off());
+    const void *kbins = base + kf_bins_off(H);
+    hipError_t e = hipSuccess;
+    if (l <= kFusedMaxLog) {
+        Tables tb{};
+        e = get_tables(l, &tb);
+        if (e == hipSuccess)
+            e = launch_fused_conv(l, dtype, u, w, v, out, kbins, kscale, mask, tb, B, H, stream);
+    } else {
+        if (w || v)
+            return fail(FFTCONV_ERR_UNSUPPORTED, "gates are not supported beyond N=%d",
+                        1 << kFusedMaxLog);
+        const int64_t S = B * H, c = mp_chunk(l);
+        for (int64_t s0 = 0; s0 < S && e == hipSuccess; s0 += c) {
+            const int64_t n = S - s0 < c ? S - s0 : c;
+            e = launch_multipass_conv(l, dtype, u, out, kbins, kscale, mask, workspace, B, H, s0,
+                                      n, stream);
+        }
+    }
+    if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "fwd launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+fftconv_status_t fftconv_export_filter_rfft(const void *K_f, int64_t H, int64_t N,
+                                            fftconv_dtype_t dtype, double *host_out,
+                                            hipStream_t stream) {
+    g_last_error.clear();
+    if (!dtype_ok(dtype)) return fail(FFTCONV_ERR_UNSUPPORTED, "dtype %d is not supported", (int)dtype);
+    const int l = log2_exact(N);
+    if (l < kMinLog || l > kMaxLog) return fail(FFTCONV_ERR_UNSUPPORTED, "unsupported N=%lld", (long long)N);
+    if (H < 1 || !K_f || !host_out) return fail(FFTCONV_ERR_INVALID_ARGUMENT, "bad arguments");
+    const size_t bytes = fftconv_filter_bytes(H, N, dtype);
+    std::vector<unsigned char> hbuf(bytes);
+    hipError_t e = hipMemcpyAsync(hbuf.data(), K_f, bytes, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "copy: %s", hipGetErrorString(e));
+    KfHeader hdr;
+    std::memcpy(&hdr, hbuf.data(), sizeof hdr);
+    if (hdr.magic != kKfMagic || hdr.N != N || hdr.H != H || hdr.dtype != (int32_t)dtype)
+        return fail(FFTCONV_ERR_FILTER_MISMATCH, "K_f header does not match");
+    const float *kscale = reinterpret_cast<const float *>(hbuf.data() + hdr.scale_off);
+    const unsigned char *bins = hbuf.data() + hdr.bins_off;
+    const int64_t n1 = hdr.n1, n2 = hdr.n2;
+    for (int64_t h = 0; h < H; ++h) {
+        // stored = K * s_h with s_h = 1 / (scale * 4N)
+        const double inv_sh = (double)kscale[h] * 4.0 * (double)N;
+        auto get = [&](int64_t slot, double *re, double *im) {
+            if (dtype == FFTCONV_F32) {
+                const float *p = reinterpret_cast<const float *>(bins) + 2 * (h * N + slot);
+                *re = p[0];
+                *im = p[1];
+            } else {
+                const _Float16 *p = reinterpret_cast<const _Float16 *>(bins) + 2 * (h * N + slot);
+                *re = (double)p[0];
+                *im = (double)p[1];
+            }
+            *re *= inv_sh;
+            *im *= inv_sh;
+        };
+        double *o = host_out + h * (N + 1) * 2;
+        double r0, i0;
+        get(0, &r0, &i0);
+        o[0] = r0; o[1] = 0.0;
+        o[2 * N] = i0; o[2 * N + 1] = 0.0;
+        for (int64_t f = 1; f < N; ++f) {
+            int64_t slot = f;
+            if (hdr.layout == KF_ROWS) {
+                // bin f = f1 + n1 f2 lives at row f1, column f2
+                const int64_t f1 = f % n1, f2 = f / n1;
+                slot = f1 * n2 + f2;
+            }
+            get(slot, &o[2 * f], &o[2 * f + 1]);
+        }
+    }
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,172 @@
+// fft_device.hpp -- device building blocks for the gfx950 FFT convolution:
+// complex arithmetic in fp32, storage-type conversion, in-register radix-R
+// DFTs and the twiddle lookups shared by the fused and multi-pass kernels.
+//
+// The convolution is evaluated with the convolution theorem (FlashFFTConv
+// summary page, "Summary": exact FFT convolution).  Each DFT is split into
+// radix stages ("Approach": an order-p decomposition of the FFT into small
+// dense transforms with permutations done on chip).  Here each small transform
+// is a radix-R DFT held in registers of one lane, and the permutations between
+// stages go through LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <hip/hip_bf16.h>
+#include <stdint.h>
+
+namespace fftconv {
+
+// --------------------------------------------------------------- complex fp32
+__device__ __forceinline__ float2 cadd(float2 a, float2 b) { return make_float2(a.x + b.x, a.y + b.y); }
+__device__ __forceinline__ float2 csub(float2 a, float2 b) { return make_float2(a.x - b.x, a.y - b.y); }
+__device__ __forceinline__ float2 cmul(float2 a, float2 b) {
+    return make_float2(fmaf(a.x, b.x, -a.y * b.y), fmaf(a.x, b.y, a.y * b.x));
+}
+__device__ __forceinline__ float2 cconj(float2 a) { return make_float2(a.x, -a.y); }
+// multiply by -i
+__device__ __forceinline__ float2 cmul_negi(float2 a) { return make_float2(a.y, -a.x); }
+// multiply by +i
+__device__ __forceinline__ float2 cmul_posi(float2 a) { return make_float2(-a.y, a.x); }
+__device__ __forceinline__ float2 cscale(float2 a, float s) { return make_float2(a.x * s, a.y * s); }
+
+// ------------------------------------------------------- storage conversions
+template <typename T> struct io;
+template <> struct io<float> {
+    static __device__ __forceinline__ float2 load2(const float *p) { return *reinterpret_cast<const float2 *>(p); }
+    static __device__ __forceinline__ void store2(float *p, float2 v) { *reinterpret_cast<float2 *>(p) = v; }
+    static __device__ __forceinline__ float load1(const float *p) { return *p; }
+};
+template <> struct io<__half> {
+    static __device__ __forceinline__ float2 load2(const __half *p) {
+        __half2 h = *reinterpret_cast<const __half2 *>(p);
+        return __half22float2(h);
+    }
+    static __device__ __forceinline__ void store2(__half *p, float2 v) {
+        *reinterpret_cast<__half2 *>(p) = __floats2half2_rn(v.x, v.y);
+    }
+    static __device__ __forceinline__ float load1(const __half *p) { return __half2float(*p); }
+};
+template <> struct io<__hip_bfloat16> {
+    static __device__ __forceinline__ float2 load2(const __hip_bfloat16 *p) {
+        uint32_t bits = *reinterpret_cast<const uint32_t *>(p);
+        return make_float2(__uint_as_float(bits << 16), __uint_as_float(bits & 0xffff0000u));
+    }
+    static __device__ __forceinline__ void store2(__hip_bfloat16 *p, float2 v) {
+        __hip_bfloat16 a = __float2bfloat16(v.x), b = __float2bfloat16(v.y);
+        uint32_t bits = (uint32_t)(*reinterpret_cast<uint16_t *>(&a)) |
+                        ((uint32_t)(*reinterpret_cast<uint16_t *>(&b)) << 16);
+        *reinterpret_cast<uint32_t *>(p) = bits;
+    }
+    static __device__ __forceinline__ float load1(const __hip_bfloat16 *p) { return __bfloat162float(*p); }
+};
+
+// Filter-spectrum bins: fp32 complex or fp16 complex.
+template <typename TK> struct kio;
+template <> struct kio<float2> {
+    static __device__ __forceinline__ float2 load(const float2 *p) { return *p; }
+    static __device__ __forceinline__ void store(float2 *p, float2 v) { *p = v; }
+};
+template <> struct kio<__half2> {
+    static __device__ __forceinline__ float2 load(const __half2 *p) { return __half22float2(*p); }
+    static __device__ __forceinline__ void store(__half2 *p, float2 v) { *p = __floats2half2_rn(v.x, v.y); }
+};
+
+// ------------------------------------------------ radix-R DFT in registers
+// exp(-2 pi i q / 32) for q in [0, 16), from the double-precision values.
+__device__ __forceinline__ float2 w32(int q) {
+    switch (q) {
+    case 0: return make_float2(1.0f, 0.0f);
+    case 1: return make_float2(9.807852804e-01f, -1.950903220e-01f);
+    case 2: return make_float2(9.238795325e-01f, -3.826834324e-01f);
+    case 3: return make_float2(8.314696123e-01f, -5.555702330e-01f);
+    case 4: return make_float2(7.071067812e-01f, -7.071067812e-01f);
+    case 5: return make_float2(5.555702330e-01f, -8.314696123e-01f);
+    case 6: return make_float2(3.826834324e-01f, -9.238795325e-01f);
+    case 7: return make_float2(1.950903220e-01f, -9.807852804e-01f);
+    case 8: return make_float2(0.0f, -1.0f);
+    case 9: return make_float2(-1.950903220e-01f, -9.807852804e-01f);
+    case 10: return make_float2(-3.826834324e-01f, -9.238795325e-01f);
+    case 11: return make_float2(-5.555702330e-01f, -8.314696123e-01f);
+    case 12: return make_float2(-7.071067812e-01f, -7.071067812e-01f);
+    case 13: return make_float2(-8.314696123e-01f, -5.555702330e-01f);
+    case 14: return make_float2(-9.238795325e-01f, -3.826834324e-01f);
+    default: return make_float2(-9.807852804e-01f, -1.950903220e-01f);
+    }
+}
+
+// Multiply by exp(-2 pi i q / R) with the trivial angles done exactly.
+template <int R>
+__device__ __forceinline__ float2 twiddle_const(float2 a, int q) {
+    if (q == 0) return a;
+    if (4 * q == R) return cmul_negi(a);
+    if (8 * q == R) {
+        const float c = 7.071067812e-01f;
+        return make_float2((a.x + a.y) * c, (a.y - a.x) * c);
+    }
+    if (8 * q == 3 * R) {
+        const float c = 7.071067812e-01f;
+        return make_float2((a.y - a.x) * c, -(a.x + a.y) * c);
+    }
+    return cmul(a, w32(q * (32 / R)));
+}
+
+// out[q] = sum_r in[r] exp(-2 pi i r q / R), radix-2 decimation in time,
+// fully unrolled; in and out may not alias.
+template <int R> struct Dft {
+    static __device__ __forceinline__ void run(const float2 *in, float2 *out) {
+        float2 e[R / 2], o[R / 2], E[R / 2], O[R / 2];
+#pragma unroll
+        for (int i = 0; i < R / 2; ++i) { e[i] = in[2 * i]; o[i] = in[2 * i + 1]; }
+        Dft<R / 2>::run(e, E);
+        Dft<R / 2>::run(o, O);
+#pragma unroll
+        for (int q = 0; q < R / 2; ++q) {
+            float2 t = twiddle_const<R>(O[q], q);
+            out[q] = cadd(E[q], t);
+            out[q + R / 2] = csub(E[q], t);
+        }
+    }
+};
+template <> struct Dft<1> {
+    static __device__ __forceinline__ void run(const float2 *in, float2 *out) { out[0] = in[0]; }
+};
+template <> struct Dft<2> {
+    static __device__ __forceinline__ void run(const float2 *in, float2 *out) {
+        out[0] = cadd(in[0], in[1]);
+        out[1] = csub(in[0], in[1]);
+    }
+};
+template <> struct Dft<4> {
+    static __device__ __forceinline__ void run(const float2 *in, float2 *out) {
+        float2 s0 = cadd(in[0], in[2]), d0 = csub(in[0], in[2]);
+        float2 s1 = cadd(in[1], in[3]), d1 = cmul_negi(csub(in[1], in[3]));
+        out[0] = cadd(s0, s1);
+        out[2] = csub(s0, s1);
+        out[1] = cadd(d0, d1);
+        out[3] = csub(d0, d1);
+    }
+};
+
+// In-place radix-R DFT of a register array.
+template <int R>
+__device__ __forceinline__ void dft_inplace(float2 *a) {
+    float2 t[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) t[i] = a[i];
+    Dft<R>::run(t, a);
+}
+
+// ------------------------------------------------------------ XCD mapping
+// Workgroups are dispatched round-robin over the 8 XCDs of the MI355X
+// (workgroup i runs on XCD i % 8).  This maps the hardware block id to a
+// logical block id so that each XCD works on one contiguous range of logical
+// blocks (a bijection on [0, nblocks)).
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t nblocks) {
+    const uint32_t xcds = 8;
+    uint32_t x = bid % xcds, local = bid / xcds;
+    uint32_t q = nblocks / xcds, r = nblocks % xcds;
+    return x * q + (x < r ? x : r) + local;
+}
+
+}  // namespace fftconv

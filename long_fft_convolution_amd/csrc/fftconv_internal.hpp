@@ -1,0 +1,87 @@
+// fftconv_internal.hpp -- declarations shared by the HIP kernel sources and
+// the host-side C ABI (api.cpp).  Not installed; the public interface is
+// include/fftconv.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fftconv {
+
+// Largest sequence length evaluated by the single fused kernel (the whole
+// N-point complex transform of one sequence lives in LDS).
+constexpr int kFusedMaxLog = 14;
+constexpr int kMinLog = 10;
+constexpr int kMaxLog = 22;
+constexpr int kMaskBlocks = 128;
+
+enum StorageType : int { ST_F32 = 0, ST_F16 = 1, ST_BF16 = 2 };
+enum KfLayout : int { KF_NATURAL = 0, KF_ROWS = 1 };
+
+// Prepared-filter buffer: header at offset 0, per-channel fp32 scales at
+// scale_off, bins at bins_off.  Bin element: float2 (fp32 storage) or
+// __half2 (fp16 / bf16 storage).  Channel h's bins start at
+// bins_off + h * N * sizeof(bin).  Bin slot 0 holds (K[0], K[N]) (both real
+// for a real filter); slot f in [1, N) holds K[f] in natural order
+// (KF_NATURAL) or in the multi-pass row order (KF_ROWS).  The stored bins are
+// K * s_h with s_h a power of two; scale[h] = 1 / (s_h * 4 N) folds the
+// normalisation of the half-length real transform pair.
+struct KfHeader {
+    uint32_t magic;
+    uint32_t version;
+    int64_t N;
+    int64_t H;
+    int64_t L;
+    int32_t dtype;
+    int32_t layout;
+    int64_t scale_off;
+    int64_t bins_off;
+    int64_t n1;   // multi-pass outer size (0 for the fused layout)
+    int64_t n2;   // multi-pass inner size
+};
+constexpr uint32_t kKfMagic = 0x4b544646u;  // "FFTK"
+constexpr uint32_t kKfVersion = 1;
+constexpr size_t kKfHeaderBytes = 256;
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline size_t bin_bytes(int st) { return st == ST_F32 ? 8 : 4; }
+inline size_t kf_scale_off() { return kKfHeaderBytes; }
+inline size_t kf_bins_off(int64_t H) { return kKfHeaderBytes + align_up((size_t)H * 4, 256); }
+
+// Multi-pass split N = n1 * n2 (n2 on chip).
+struct MpSplit {
+    int log1, log2;
+};
+MpSplit mp_split(int logn);
+// Sequences processed per multi-pass chunk (bounds the workspace).
+int64_t mp_chunk(int logn);
+
+// Per-device, per-size tables (allocated once, read only afterwards).
+struct Tables {
+    const float2 *tw;    // exp(-2 pi i j / N), j < N
+    const float2 *tw2;   // exp(-pi i j / N),   j < N   (= omega_{2N}^j)
+};
+hipError_t get_tables(int logn, Tables *out);
+
+// ---- launchers (return the launch status) --------------------------------
+hipError_t launch_fused_conv(int logn, int st, const void *u,
+                             const void *w, const void *v, void *out, const void *kbins,
+                             const float *kscale, const uint8_t *mask, const Tables &tb,
+                             int64_t B, int64_t H, hipStream_t stream);
+hipError_t launch_fused_prepare(int logn, int st, const void *k, int64_t L, void *kbins,
+                                const float *kscale, const Tables &tb, int64_t H,
+                                hipStream_t stream);
+hipError_t launch_filter_scale(int st, const void *k, int64_t H, int64_t L, int64_t N,
+                               float *kscale, hipStream_t stream);
+hipError_t launch_write_header(const KfHeader &hdr, void *K_f, hipStream_t stream);
+
+hipError_t launch_multipass_conv(int logn, int st, const void *u, void *out,
+                                 const void *kbins, const float *kscale, const uint8_t *mask,
+                                 void *work, int64_t B, int64_t H, int64_t seq0, int64_t nseq,
+                                 hipStream_t stream);
+hipError_t launch_multipass_prepare(int logn, int st, const void *k, int64_t L, void *kbins,
+                                    const float *kscale, void *work, int64_t H, int64_t h0,
+                                    int64_t nseq, hipStream_t stream);
+
+}  // namespace fftconv

@@ -1,0 +1,113 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/fftconv.h declares, computes its size helpers, and rejects bad
+arguments before it would touch the device (every case below fails
+validation, so nothing is launched).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fftconv.h")
+
+fc = pytest.importorskip("long_fft_convolution_amd")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fftconv_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for n in ["fftconv_prepare_filter", "fftconv_fwd", "fftconv_filter_bytes",
+              "fftconv_workspace_bytes", "fftconv_mask_blocks", "fftconv_status_string",
+              "fftconv_last_error", "fftconv_export_filter_rfft"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(fc.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert hasattr(fc, name), f"binding lacks {name}"
+
+
+def test_size_helpers():
+    F32, F16, BF16 = fc.FFTCONV_F32, fc.FFTCONV_F16, fc.FFTCONV_BF16
+    # header 256 B + scales rounded to 256 B + H*N bins of 8 B (fp32) or 4 B (fp16)
+    assert fc.fftconv_filter_bytes(4, 1024, F32) == 256 + 256 + 4 * 1024 * 8
+    assert fc.fftconv_filter_bytes(768, 1024, F16) == 256 + 3072 + 768 * 1024 * 4
+    assert fc.fftconv_filter_bytes(2560, 16384, BF16) == 256 + 10240 + 2560 * 16384 * 4
+    assert fc.fftconv_filter_bytes(0, 1024, F32) == 0
+    assert fc.fftconv_filter_bytes(4, 1000, F32) == 0
+    assert fc.fftconv_filter_bytes(4, 1 << 23, F32) == 0
+    assert fc.fftconv_filter_bytes(4, 1024, 7) == 0
+    for n in (1024, 16384):
+        assert fc.fftconv_workspace_bytes(64, 768, n, F16) == 0
+    ws = fc.fftconv_workspace_bytes(1, 256, 1 << 20, F16)
+    assert ws > 0 and ws % ((1 << 20) * 8) == 0
+    assert fc.fftconv_workspace_bytes(1, 1, 1 << 20, F16) == (1 << 20) * 8
+    assert fc.fftconv_mask_blocks(1 << 22) == 128
+    assert fc.fftconv_mask_blocks(1024) == 128
+    assert fc.fftconv_mask_blocks(512) == 0
+    assert fc.fftconv_status_string(0) == "ok"
+    assert "workspace" in fc.fftconv_status_string(3)
+
+
+def _fwd(**kw):
+    lib = fc.lib()
+    a = dict(u=0x10000, K_f=0x20000, w=None, v=None, out=0x30000, B=1, H=1, N=1024, L=1024,
+             mask=None, dtype=0, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.fftconv_fwd(a["u"], a["K_f"], a["w"], a["v"], a["out"], a["B"], a["H"], a["N"],
+                           a["L"], a["mask"], a["dtype"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(N=1000), 2, "power of two"),
+    (dict(N=512), 2, "power of two"),
+    (dict(N=1 << 23), 2, "power of two"),
+    (dict(dtype=9), 2, "dtype"),
+    (dict(L=0), 1, "L_filter"),
+    (dict(L=2048), 1, "L_filter"),
+    (dict(B=-1), 1, ">= 0"),
+    (dict(u=None), 1, "non-null"),
+    (dict(out=None), 1, "non-null"),
+    (dict(K_f=None), 1, "non-null"),
+    (dict(u=0x10004), 1, "aligned"),
+    (dict(w=0x40008), 1, "aligned"),
+    (dict(out=0x10000 + 16), 1, "overlaps"),
+    (dict(N=1 << 20, L=1 << 20, out=0x10000000 * 4), 3, "workspace"),
+])
+def test_fwd_validation(kw, status, text):
+    assert _fwd(**kw) == status
+    assert text in fc.fftconv_last_error()
+
+
+def test_fwd_empty_batch_is_a_no_op():
+    assert _fwd(B=0, u=None, out=None, K_f=None) == 0
+    assert _fwd(H=0) == 0
+
+
+def test_prepare_validation():
+    lib = fc.lib()
+    good = dict(k=0x10000, H=2, L=100, N=1024, dt=0, K_f=0x100000, kb=1 << 20, ws=None, wsb=0)
+
+    def call(**kw):
+        a = dict(good)
+        a.update(kw)
+        return lib.fftconv_prepare_filter(a["k"], a["H"], a["L"], a["N"], a["dt"], a["K_f"],
+                                          a["kb"], a["ws"], a["wsb"], None)
+
+    assert call(H=0) == 1
+    assert call(L=2000) == 1
+    assert call(N=3000) == 2
+    assert call(kb=100) == 1 and "needs" in fc.fftconv_last_error()
+    assert call(k=None) == 1
+    assert call(k=0x10002) == 1
+    assert call(K_f=0x10000 + 256) == 1 and "overlaps" in fc.fftconv_last_error()
+    assert call(N=1 << 20, L=5, kb=1 << 30) == 3
