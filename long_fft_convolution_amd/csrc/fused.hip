@@ -115,7 +115,7 @@ __device__ __forceinline__ void middle_pair(float2 &zf, float2 &zg, float2 Kf, f
     const float2 ye = cadd(yf, ygc);
     const float2 yo = cmul(csub(yf, ygc), cconj(Wf));
     // conj(Z'[f]) = conj(ye) - i conj(yo);  conj(Z'[g]) = ye - i yo
-    zf = make_float2(ye.x + yo.y, -ye.y + yo.x);
+    zf = make_float2(ye.x - yo.y, -ye.y - yo.x);
     zg = make_float2(ye.x + yo.y, ye.y - yo.x);
 }
 
