@@ -81,9 +81,62 @@ hipError_t build_tables(int logn, Tables *out) {
     return hipSuccess;
 }
 
+std::mutex g_mp_mu;
+std::map<std::pair<int, int>, MpTables> g_mp_tables;
+
+hipError_t upload(const std::vector<float2> &v, const float2 **out) {
+    float2 *d = nullptr;
+    hipError_t e = hipMalloc(&d, sizeof(float2) * v.size());
+    if (e != hipSuccess) return e;
+    e = hipMemcpy(d, v.data(), sizeof(float2) * v.size(), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        (void)hipFree(d);
+        return e;
+    }
+    *out = d;
+    return hipSuccess;
+}
+
 }  // namespace
 
 namespace fftconv {
+
+hipError_t get_mp_tables(int logn, MpTables *out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lk(g_mp_mu);
+    auto key = std::make_pair(dev, logn);
+    auto it = g_mp_tables.find(key);
+    if (it != g_mp_tables.end()) {
+        *out = it->second;
+        return hipSuccess;
+    }
+    const MpSplit sp = mp_split(logn);
+    const int64_t n = int64_t(1) << logn, n1 = int64_t(1) << sp.log1;
+    const double pi = 3.14159265358979323846264338327950288;
+    std::vector<float2> w2row(n1), lo(2048), hi(n / 2048);
+    for (int64_t j = 0; j < n1; ++j) {
+        const double a = -pi * (double)j / (double)n;
+        w2row[j] = make_float2((float)std::cos(a), (float)std::sin(a));
+    }
+    for (int64_t j = 0; j < 2048; ++j) {
+        const double a = -2.0 * pi * (double)j / (double)n;
+        lo[j] = make_float2((float)std::cos(a), (float)std::sin(a));
+    }
+    for (int64_t j = 0; j < n / 2048; ++j) {
+        const double a = -2.0 * pi * (double)(2048 * j) / (double)n;
+        hi[j] = make_float2((float)std::cos(a), (float)std::sin(a));
+    }
+    MpTables t{};
+    e = upload(w2row, &t.w2row);
+    if (e == hipSuccess) e = upload(lo, &t.big_lo);
+    if (e == hipSuccess) e = upload(hi, &t.big_hi);
+    if (e != hipSuccess) return e;
+    g_mp_tables[key] = t;
+    *out = t;
+    return hipSuccess;
+}
 
 hipError_t get_tables(int logn, Tables *out) {
     int dev = 0;
@@ -107,8 +160,7 @@ hipError_t get_tables(int logn, Tables *out) {
 MpSplit mp_split(int logn) {
     // inner (on-chip) transform of 2^log2 points, outer of 2^log1 points
     MpSplit s;
-    s.log2 = logn - 8 < kFusedMaxLog ? logn - 8 : kFusedMaxLog;
-    if (s.log2 < 10) s.log2 = 10;
+    s.log2 = 13;            // on-chip rows of 8192 points (two rows of fp32 fill 128 KiB of LDS)
     s.log1 = logn - s.log2;
     return s;
 }
@@ -284,14 +336,11 @@ fftconv_status_t fftconv_fwd(const void *u, const void *K_f, const void *w, cons
         if (e == hipSuccess)
             e = launch_fused_conv(l, dtype, u, w, v, out, kbins, kscale, mask, tb, B, H, stream);
     } else {
-        if (w || v)
-            return fail(FFTCONV_ERR_UNSUPPORTED, "gates are not supported beyond N=%d",
-                        1 << kFusedMaxLog);
         const int64_t S = B * H, c = mp_chunk(l);
         for (int64_t s0 = 0; s0 < S && e == hipSuccess; s0 += c) {
             const int64_t n = S - s0 < c ? S - s0 : c;
-            e = launch_multipass_conv(l, dtype, u, out, kbins, kscale, mask, workspace, B, H, s0,
-                                      n, stream);
+            e = launch_multipass_conv(l, dtype, u, w, v, out, kbins, kscale, mask, workspace, H,
+                                      s0, n, stream);
         }
     }
     if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "fwd launch: %s", hipGetErrorString(e));

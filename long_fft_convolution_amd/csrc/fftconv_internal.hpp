@@ -64,6 +64,15 @@ struct Tables {
 };
 hipError_t get_tables(int logn, Tables *out);
 
+// Multi-pass extras for N = 2^logn: omega_{2N}^j (j < N1), and the two
+// factors of the two-level lookup omega_N^a = hi[a >> 11] * lo[a & 2047].
+struct MpTables {
+    const float2 *w2row;   // exp(-pi i j / N),          j < N1
+    const float2 *big_lo;  // exp(-2 pi i j / N),        j < 2048
+    const float2 *big_hi;  // exp(-2 pi i 2048 j / N),   j < N / 2048
+};
+hipError_t get_mp_tables(int logn, MpTables *out);
+
 // ---- launchers (return the launch status) --------------------------------
 hipError_t launch_fused_conv(int logn, int st, const void *u,
                              const void *w, const void *v, void *out, const void *kbins,
@@ -76,10 +85,10 @@ hipError_t launch_filter_scale(int st, const void *k, int64_t H, int64_t L, int6
                                float *kscale, hipStream_t stream);
 hipError_t launch_write_header(const KfHeader &hdr, void *K_f, hipStream_t stream);
 
-hipError_t launch_multipass_conv(int logn, int st, const void *u, void *out,
-                                 const void *kbins, const float *kscale, const uint8_t *mask,
-                                 void *work, int64_t B, int64_t H, int64_t seq0, int64_t nseq,
-                                 hipStream_t stream);
+hipError_t launch_multipass_conv(int logn, int st, const void *u, const void *w, const void *v,
+                                 void *out, const void *kbins, const float *kscale,
+                                 const uint8_t *mask, void *work, int64_t H, int64_t seq0,
+                                 int64_t nseq, hipStream_t stream);
 hipError_t launch_multipass_prepare(int logn, int st, const void *k, int64_t L, void *kbins,
                                     const float *kscale, void *work, int64_t H, int64_t h0,
                                     int64_t nseq, hipStream_t stream);

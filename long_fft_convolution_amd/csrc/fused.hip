@@ -21,6 +21,7 @@
 //
 // All arithmetic is fp32; storage is fp32, fp16 or bf16.
 #include "fft_device.hpp"
+#include "fft_stages.hpp"
 #include "fftconv_internal.hpp"
 
 namespace fftconv {
@@ -37,38 +38,6 @@ template <int LOGN> struct FusedPlan {
     static constexpr int THREADS = TS * SPW;
     static_assert(R1 >= 2 && R1 <= 16, "radix plan");
 };
-
-// Generic Stockham stage through LDS: radix R, NS = product of the previous
-// radices.  Butterfly j reads src[j + r P], multiplies by the twiddle
-// omega_{NS R}^{r k} (k = j mod NS), takes the radix-R DFT and writes
-// dst[(j - k) R + k + q NS].  In place: all lanes read, barrier, all write.
-template <int NC, int R, int TS, int NS>
-__device__ __forceinline__ void stage_lds(float2 *buf, int ts, const float2 *__restrict__ tw) {
-    constexpr int P = NC / R;
-    constexpr int NB = P / TS;
-    float2 a[NB][R];
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-        const int j = ts + i * TS;
-#pragma unroll
-        for (int r = 0; r < R; ++r) a[i][r] = buf[j + r * P];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-        const int j = ts + i * TS;
-        const int k = j & (NS - 1);
-        if (NS > 1) {
-#pragma unroll
-            for (int r = 1; r < R; ++r) a[i][r] = cmul(a[i][r], tw[(r * k) * (NC / (NS * R))]);
-        }
-        dft_inplace<R>(a[i]);
-        const int base = (j - k) * R + k;
-#pragma unroll
-        for (int q = 0; q < R; ++q) buf[base + q * NS] = a[i][q];
-    }
-    __syncthreads();
-}
 
 // Forward middle stages: stage index I (0-based among the radix-R stages),
 // NS = R1 * R^I, for I < MR - 1 (the last radix-R stage is done separately).
@@ -90,33 +59,6 @@ __device__ __forceinline__ void inv_middle(float2 *buf, int ts, const float2 *__
         stage_lds<Pl::NC, Pl::R, Pl::TS, NS>(buf, ts, tw);
         inv_middle<LOGN, I + 1>(buf, ts, tw);
     }
-}
-
-// One bin pair (f, g = N - f) of the half-length real transform.  In: the
-// complex spectrum values Z[f], Z[g]; the filter bins Kf = K[f]/(4N),
-// Kg = K[g]/(4N); Wf = omega_{2N}^f.  Out (in place): conj(Z'[f]),
-// conj(Z'[g]) where Z' is the half-length spectrum of the product's inverse.
-//   X[f] = Xe + Wf Xo, X[g] = conj(Xe - Wf Xo) with Xe = Z[f] + conj(Z[g]),
-//   Xo = -i (Z[f] - conj(Z[g]))  (both twice their textbook values);
-//   Y = X K;  Ye = Y[f] + conj(Y[g]),  Yo = (Y[f] - conj(Y[g])) conj(Wf);
-//   Z'[f] = Ye + i Yo,  Z'[g] = conj(Ye) + i conj(Yo).
-// f = 0 fits the same formula with Z[g] = Z[0] and Kg = K[N]; the self-paired
-// f = N/2 with Z[g] = Z[f], Kg = Kf.
-__device__ __forceinline__ void middle_pair(float2 &zf, float2 &zg, float2 Kf, float2 Kg,
-                                            float2 Wf) {
-    const float2 bc = cconj(zg);
-    const float2 xe = cadd(zf, bc);
-    const float2 xo = cmul_negi(csub(zf, bc));
-    const float2 wxo = cmul(Wf, xo);
-    const float2 xf = cadd(xe, wxo);
-    const float2 xg = cconj(csub(xe, wxo));
-    const float2 yf = cmul(xf, Kf);
-    const float2 ygc = cconj(cmul(xg, Kg));
-    const float2 ye = cadd(yf, ygc);
-    const float2 yo = cmul(csub(yf, ygc), cconj(Wf));
-    // conj(Z'[f]) = conj(ye) - i conj(yo);  conj(Z'[g]) = ye - i yo
-    zf = make_float2(ye.x - yo.y, -ye.y - yo.x);
-    zg = make_float2(ye.x + yo.y, ye.y - yo.x);
 }
 
 template <typename TK>
