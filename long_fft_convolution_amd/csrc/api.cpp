@@ -101,6 +101,94 @@ hipError_t upload(const std::vector<float2> &v, const float2 **out) {
 
 namespace fftconv {
 
+namespace {
+std::mutex g_pair_mu;
+std::map<int, PairTables> g_pair_tables;
+
+// K slot 8g + j of a chained operand <-> row index within a 32-row span
+int rho(int k) {
+    const int g = k / 8, j = k % 8;
+    return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4);
+}
+
+hipError_t upload_h(const std::vector<_Float16> &v, const void **out) {
+    void *d = nullptr;
+    hipError_t e = hipMalloc(&d, sizeof(_Float16) * v.size());
+    if (e != hipSuccess) return e;
+    e = hipMemcpy(d, v.data(), sizeof(_Float16) * v.size(), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        (void)hipFree(d);
+        return e;
+    }
+    *out = d;
+    return hipSuccess;
+}
+}  // namespace
+
+hipError_t get_pair_tables(PairTables *out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lk(g_pair_mu);
+    auto it = g_pair_tables.find(dev);
+    if (it != g_pair_tables.end()) {
+        *out = it->second;
+        return hipSuccess;
+    }
+    const double pi = 3.14159265358979323846264338327950288;
+    auto ang = [&](double num, double den) { return 2.0 * pi * num / den; };
+    std::vector<_Float16> f1r(4 * 64 * 8), f1i(4 * 64 * 8), f2r(2 * 64 * 8), f2i(2 * 64 * 8),
+        f3r(4 * 64 * 8), f3i(4 * 64 * 8);
+    std::vector<float2> tw1(2048), tw3(2048);
+    for (int l = 0; l < 64; ++l) {
+        const int g = l / 16, c = l % 16;
+        for (int j = 0; j < 8; ++j) {
+            const int r = rho(8 * g + j);
+            for (int nt = 0; nt < 4; ++nt) {   // S1: F64[n_s = r][f_s = 16 nt + c]
+                const double a = -ang((double)r * (16 * nt + c), 64);
+                f1r[(nt * 64 + l) * 8 + j] = (_Float16)std::cos(a);
+                f1i[(nt * 64 + l) * 8 + j] = (_Float16)std::sin(a);
+            }
+            for (int mt = 0; mt < 2; ++mt) {   // S2: F32[f_f = 16 mt + c][n_f = r]
+                const double a = -ang((double)(16 * mt + c) * r, 32);
+                f2r[(mt * 64 + l) * 8 + j] = (_Float16)std::cos(a);
+                f2i[(mt * 64 + l) * 8 + j] = (_Float16)std::sin(a);
+            }
+            for (int ks = 0; ks < 2; ++ks)     // S1': conj F64[f_s = 32 ks + r][n_s = 16 nt + c]
+                for (int nt = 0; nt < 2; ++nt) {
+                    const double a = ang((double)(32 * ks + r) * (16 * nt + c), 64);
+                    f3r[((ks * 2 + nt) * 64 + l) * 8 + j] = (_Float16)std::cos(a);
+                    f3i[((ks * 2 + nt) * 64 + l) * 8 + j] = (_Float16)std::sin(a);
+                }
+        }
+        for (int i = 0; i < 4; ++i) {
+            for (int mt = 0; mt < 2; ++mt)     // rows n_f = 16 mt + 4g + i, cols f_s = 16 nt + c
+                for (int nt = 0; nt < 4; ++nt) {
+                    const double a = -ang((double)(16 * mt + 4 * g + i) * (16 * nt + c), 2048);
+                    tw1[((mt * 4 + nt) * 64 + l) * 4 + i] = make_float2((float)std::cos(a), (float)std::sin(a));
+                }
+            for (int nt = 0; nt < 4; ++nt)     // rows f_s = 16 nt + 4g + i, cols n_f = 16 nt2 + c
+                for (int nt2 = 0; nt2 < 2; ++nt2) {
+                    const double a = ang((double)(16 * nt2 + c) * (16 * nt + 4 * g + i), 2048);
+                    tw3[((nt * 2 + nt2) * 64 + l) * 4 + i] = make_float2((float)std::cos(a), (float)std::sin(a));
+                }
+        }
+    }
+    PairTables t{};
+    e = upload_h(f1r, &t.f1r);
+    if (e == hipSuccess) e = upload_h(f1i, &t.f1i);
+    if (e == hipSuccess) e = upload_h(f2r, &t.f2r);
+    if (e == hipSuccess) e = upload_h(f2i, &t.f2i);
+    if (e == hipSuccess) e = upload_h(f3r, &t.f3r);
+    if (e == hipSuccess) e = upload_h(f3i, &t.f3i);
+    if (e == hipSuccess) e = upload(tw1, &t.tw1);
+    if (e == hipSuccess) e = upload(tw3, &t.tw3);
+    if (e != hipSuccess) return e;
+    g_pair_tables[dev] = t;
+    *out = t;
+    return hipSuccess;
+}
+
 hipError_t get_mp_tables(int logn, MpTables *out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -199,7 +287,7 @@ int64_t fftconv_mask_blocks(int64_t N) {
 size_t fftconv_filter_bytes(int64_t H, int64_t N, fftconv_dtype_t dtype) {
     const int l = log2_exact(N);
     if (l < kMinLog || l > kMaxLog || H < 1 || !dtype_ok(dtype)) return 0;
-    return kf_bins_off(H) + (size_t)H * (size_t)N * bin_bytes(dtype);
+    return kf_bins_off(H) + (size_t)H * (size_t)kf_slots(l, dtype) * bin_bytes(dtype);
 }
 
 size_t fftconv_workspace_bytes(int64_t B, int64_t H, int64_t N, fftconv_dtype_t dtype) {
@@ -252,14 +340,14 @@ fftconv_status_t fftconv_prepare_filter(const void *k, int64_t H, int64_t L, int
     hdr.H = H;
     hdr.L = L;
     hdr.dtype = (int32_t)dtype;
-    hdr.layout = fused ? KF_NATURAL : KF_ROWS;
+    hdr.layout = !fused ? KF_ROWS : (use_pair_kernel(l, dtype) ? KF_PAIR : KF_NATURAL);
     hdr.scale_off = (int64_t)kf_scale_off();
     hdr.bins_off = (int64_t)kf_bins_off(H);
     hdr.n1 = fused ? 0 : (int64_t(1) << sp.log1);
     hdr.n2 = fused ? N : (int64_t(1) << sp.log2);
 
     hipError_t e = launch_write_header(hdr, K_f, stream);
-    if (e == hipSuccess) e = launch_filter_scale(dtype, k, H, L, N, kscale, stream);
+    if (e == hipSuccess) e = launch_filter_scale(dtype, k, H, L, kf_norm_log2(l, dtype), kscale, stream);
     if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "filter setup launch: %s", hipGetErrorString(e));
     if (fused) {
         Tables tb{};
@@ -330,7 +418,9 @@ fftconv_status_t fftconv_fwd(const void *u, const void *K_f, const void *w, cons
     const float *kscale = reinterpret_cast<const float *>(base + kf_scale_off());
     const void *kbins = base + kf_bins_off(H);
     hipError_t e = hipSuccess;
-    if (l <= kFusedMaxLog) {
+    if (use_pair_kernel(l, dtype)) {
+        e = launch_pair_conv(l, dtype, u, w, v, out, kbins, kscale, mask, B, H, stream);
+    } else if (l <= kFusedMaxLog) {
         Tables tb{};
         e = get_tables(l, &tb);
         if (e == hipSuccess)
@@ -368,15 +458,16 @@ fftconv_status_t fftconv_export_filter_rfft(const void *K_f, int64_t H, int64_t 
     const unsigned char *bins = hbuf.data() + hdr.bins_off;
     const int64_t n1 = hdr.n1, n2 = hdr.n2;
     for (int64_t h = 0; h < H; ++h) {
-        // stored = K * s_h with s_h = 1 / (scale * 4N)
-        const double inv_sh = (double)kscale[h] * 4.0 * (double)N;
+        // stored = K * s_h with s_h = 1 / (scale * norm)
+        const int64_t slots = kf_slots(l, dtype);
+        const double inv_sh = (double)kscale[h] * std::ldexp(1.0, kf_norm_log2(l, dtype));
         auto get = [&](int64_t slot, double *re, double *im) {
             if (dtype == FFTCONV_F32) {
-                const float *p = reinterpret_cast<const float *>(bins) + 2 * (h * N + slot);
+                const float *p = reinterpret_cast<const float *>(bins) + 2 * (h * slots + slot);
                 *re = p[0];
                 *im = p[1];
             } else {
-                const _Float16 *p = reinterpret_cast<const _Float16 *>(bins) + 2 * (h * N + slot);
+                const _Float16 *p = reinterpret_cast<const _Float16 *>(bins) + 2 * (h * slots + slot);
                 *re = (double)p[0];
                 *im = (double)p[1];
             }
@@ -384,6 +475,15 @@ fftconv_status_t fftconv_export_filter_rfft(const void *K_f, int64_t H, int64_t 
             *im *= inv_sh;
         };
         double *o = host_out + h * (N + 1) * 2;
+        if (hdr.layout == KF_PAIR) {
+            const _Float16 *p = reinterpret_cast<const _Float16 *>(bins) + h * slots * 2;
+            for (int64_t f = 0; f <= N; ++f) {
+                const int64_t a = pair_kf_index(f);
+                o[2 * f] = (double)p[a] * inv_sh;
+                o[2 * f + 1] = (double)p[a + 4] * inv_sh;
+            }
+            continue;
+        }
         double r0, i0;
         get(0, &r0, &i0);
         o[0] = r0; o[1] = 0.0;

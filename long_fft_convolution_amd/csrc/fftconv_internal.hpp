@@ -17,7 +17,7 @@ constexpr int kMaxLog = 22;
 constexpr int kMaskBlocks = 128;
 
 enum StorageType : int { ST_F32 = 0, ST_F16 = 1, ST_BF16 = 2 };
-enum KfLayout : int { KF_NATURAL = 0, KF_ROWS = 1 };
+enum KfLayout : int { KF_NATURAL = 0, KF_ROWS = 1, KF_PAIR = 2 };
 
 // Prepared-filter buffer: header at offset 0, per-channel fp32 scales at
 // scale_off, bins at bins_off.  Bin element: float2 (fp32 storage) or
@@ -45,6 +45,24 @@ constexpr uint32_t kKfVersion = 1;
 constexpr size_t kKfHeaderBytes = 256;
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// The matrix-core pair kernel handles N = 1024 in fp16/bf16 storage.  Its
+// filter layout holds the full 2N-bin spectrum in the order its lanes read
+// it: 16-byte chunk q = (mt2 * 4 + nt) * 64 + lane, lane = 16 g + c, holds
+// re[0..3] then im[0..3] (fp16) of bins f = 16 nt + c + 64 (16 mt2 + 4 g + i).
+inline bool use_pair_kernel(int logn, int st) { return logn == 10 && st != ST_F32; }
+inline int64_t kf_slots(int logn, int st) {
+    return use_pair_kernel(logn, st) ? (int64_t(2) << logn) : (int64_t(1) << logn);
+}
+// log2 of the normalisation folded into scale[h]: 4N for the half-length
+// real transform (fused, multi-pass), 2N for the pair kernel.
+inline int kf_norm_log2(int logn, int st) { return use_pair_kernel(logn, st) ? logn + 1 : logn + 2; }
+// fp16 element offset of the real part of bin f in the pair layout (imag at +4)
+__host__ __device__ inline int64_t pair_kf_index(int64_t f) {
+    const int64_t fs = f % 64, ff = f / 64;
+    const int64_t mt2 = ff / 16, g = (ff % 16) / 4, i = ff % 4, nt = fs / 16, c = fs % 16;
+    return (((mt2 * 4 + nt) * 64 + g * 16 + c) * 8) + i;
+}
 inline size_t bin_bytes(int st) { return st == ST_F32 ? 8 : 4; }
 inline size_t kf_scale_off() { return kKfHeaderBytes; }
 inline size_t kf_bins_off(int64_t H) { return kKfHeaderBytes + align_up((size_t)H * 4, 256); }
@@ -81,8 +99,21 @@ hipError_t launch_fused_conv(int logn, int st, const void *u,
 hipError_t launch_fused_prepare(int logn, int st, const void *k, int64_t L, void *kbins,
                                 const float *kscale, const Tables &tb, int64_t H,
                                 hipStream_t stream);
-hipError_t launch_filter_scale(int st, const void *k, int64_t H, int64_t L, int64_t N,
+hipError_t launch_filter_scale(int st, const void *k, int64_t H, int64_t L, int norm_log2,
                                float *kscale, hipStream_t stream);
+
+// Lane-order constant tables of the pair kernel (see pair_mfma.hip).
+struct PairTables {
+    const void *f1r, *f1i;   // S1 DFT-64 blocks, [4][64 lanes][8] fp16
+    const void *f2r, *f2i;   // S2 DFT-32 blocks, [2][64][8] fp16
+    const void *f3r, *f3i;   // S1' conj DFT-64 blocks, [2 ks * 2 nt][64][8] fp16
+    const float2 *tw1;       // forward twiddles, [2 mt][4 nt][64][4]
+    const float2 *tw3;       // inverse twiddles, [4 nt][2 nt2][64][4]
+};
+hipError_t get_pair_tables(PairTables *out);
+hipError_t launch_pair_conv(int logn, int st, const void *u, const void *w, const void *v,
+                            void *out, const void *kbins, const float *kscale, const uint8_t *mask,
+                            int64_t B, int64_t H, hipStream_t stream);
 hipError_t launch_write_header(const KfHeader &hdr, void *K_f, hipStream_t stream);
 
 hipError_t launch_multipass_conv(int logn, int st, const void *u, const void *w, const void *v,

@@ -5,8 +5,10 @@
 // inequality on the DFT sum), so s_h = 2^floor(log2(2^14 / sum|k|)) keeps every
 // stored bin below 2^14, well inside fp16's range, while the largest bins keep
 // fp16's full 11-bit significand.  fp32 bins use s_h = 1.  The stored scale is
-// scale[h] = 1 / (s_h * 4 N), which also folds the normalisation of the
-// half-length real transform pair, so the forward kernels multiply once.
+// scale[h] = 1 / (s_h * norm), which also folds the normalisation of the
+// transform pair (norm = 4N for the half-length real transform, 2N for the
+// two-sequence complex packing of the matrix-core kernel), so the forward
+// kernels multiply once.
 #include "fft_device.hpp"
 #include "fftconv_internal.hpp"
 
@@ -14,7 +16,7 @@ namespace fftconv {
 
 template <typename T>
 __global__ void __launch_bounds__(256)
-filter_scale_kernel(const T *__restrict__ k, int64_t L, int64_t N, bool unit, float *__restrict__ kscale) {
+filter_scale_kernel(const T *__restrict__ k, int64_t L, int norm_log2, bool unit, float *__restrict__ kscale) {
     __shared__ float part[256];
     const int64_t h = blockIdx.x;
     float s = 0.f;
@@ -35,10 +37,8 @@ filter_scale_kernel(const T *__restrict__ k, int64_t L, int64_t N, bool unit, fl
             e = (int)floorf(log2f(16384.0f / tot));
             e = e < -60 ? -60 : (e > 60 ? 60 : e);
         }
-        int logn = 0;
-        while ((int64_t(1) << logn) < N) ++logn;
-        // scale[h] = 1 / (s_h * 4N) with s_h = 2^e: a power of two, exact in fp32
-        kscale[h] = ldexpf(1.0f, -e - logn - 2);
+        // scale[h] = 1 / (s_h * 2^norm_log2) with s_h = 2^e: a power of two, exact in fp32
+        kscale[h] = ldexpf(1.0f, -e - norm_log2);
     }
 }
 
@@ -46,21 +46,21 @@ __global__ void write_header_kernel(KfHeader hdr, KfHeader *dst) {
     if (threadIdx.x == 0 && blockIdx.x == 0) *dst = hdr;
 }
 
-hipError_t launch_filter_scale(int st, const void *k, int64_t H, int64_t L, int64_t N,
+hipError_t launch_filter_scale(int st, const void *k, int64_t H, int64_t L, int norm_log2,
                                float *kscale, hipStream_t stream) {
     const bool unit = st == ST_F32;
     switch (st) {
     case ST_F32:
         hipLaunchKernelGGL(filter_scale_kernel<float>, dim3((unsigned)H), dim3(256), 0, stream,
-                           (const float *)k, L, N, unit, kscale);
+                           (const float *)k, L, norm_log2, unit, kscale);
         break;
     case ST_F16:
         hipLaunchKernelGGL(filter_scale_kernel<__half>, dim3((unsigned)H), dim3(256), 0, stream,
-                           (const __half *)k, L, N, unit, kscale);
+                           (const __half *)k, L, norm_log2, unit, kscale);
         break;
     default:
         hipLaunchKernelGGL(filter_scale_kernel<__hip_bfloat16>, dim3((unsigned)H), dim3(256), 0,
-                           stream, (const __hip_bfloat16 *)k, L, N, unit, kscale);
+                           stream, (const __hip_bfloat16 *)k, L, norm_log2, unit, kscale);
     }
     return hipGetLastError();
 }

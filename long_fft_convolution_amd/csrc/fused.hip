@@ -24,6 +24,8 @@
 #include "fft_stages.hpp"
 #include "fftconv_internal.hpp"
 
+#include <type_traits>
+
 namespace fftconv {
 
 template <int LOGN> struct FusedPlan {
@@ -225,7 +227,7 @@ fused_conv_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__r
 // partial filter only the loads holding taps are issued), then the real
 // spectrum X[f], f in [0, N], scaled by s_h, stored in natural order with
 // slot 0 = (X[0], X[N]).
-template <int LOGN, typename T, typename TK>
+template <int LOGN, typename T, typename TK, bool PAIR>
 __global__ void __launch_bounds__(FusedPlan<LOGN>::THREADS)
 fused_prepare_kernel(const T *__restrict__ k, int64_t L, TK *__restrict__ kbins,
                      const float *__restrict__ kscale, const float2 *__restrict__ tw,
@@ -277,26 +279,47 @@ fused_prepare_kernel(const T *__restrict__ k, int64_t L, TK *__restrict__ kbins,
     dft_inplace<R>(Bv);
     if (!valid) return;
 
-    // s_h = 1 / (scale[h] * 4N), exact (both powers of two)
-    const float sh = 1.0f / (kscale[h] * (float)(4 * NC));
-    TK *krow = kbins + h * (int64_t)NC;
+    // s_h = 1 / (scale[h] * norm), exact (both powers of two)
+    const float sh = 1.0f / (kscale[h] * (float)(PAIR ? 2 * NC : 4 * NC));
+    TK *krow = kbins + h * (int64_t)(PAIR ? 2 * NC : NC);
+    // one real-spectrum bin: natural order, or the pair kernel's lane order
+    // (with the Hermitian mirror 2N - f stored as well)
+    auto put = [&](int f, float2 x) {
+        if (!PAIR) {
+            kio<TK>::store(krow + f, x);
+        } else {
+            _Float16 *kh = reinterpret_cast<_Float16 *>(krow);
+            const int64_t a = pair_kf_index(f);
+            kh[a] = (_Float16)x.x;
+            kh[a + 4] = (_Float16)x.y;
+            if (f != 0 && f != NC) {
+                const int64_t b = pair_kf_index(2 * NC - f);
+                kh[b] = (_Float16)x.x;
+                kh[b + 4] = (_Float16)(-x.y);
+            }
+        }
+    };
     // X[f] = (Xe + Wf Xo)/2, X[g] = conj(Xe - Wf Xo)/2 (Xe, Xo as in middle_pair)
     auto emit = [&](float2 zf, float2 zg, int f, bool both) {
         const float2 bc = cconj(zg);
         const float2 xe = cadd(zf, bc);
         const float2 xo = cmul_negi(csub(zf, bc));
         const float2 wxo = cmul(tw2[f], xo);
-        const float2 xf = cscale(cadd(xe, wxo), 0.5f * sh);
-        const float2 xg = cscale(cconj(csub(xe, wxo)), 0.5f * sh);
-        kio<TK>::store(krow + f, xf);
-        if (both) kio<TK>::store(krow + (NC - f), xg);
+        put(f, cscale(cadd(xe, wxo), 0.5f * sh));
+        if (both) put(NC - f, cscale(cconj(csub(xe, wxo)), 0.5f * sh));
     };
     if (ts != 0) {
 #pragma unroll
         for (int q = 0; q < R; ++q) emit(A[q], Bv[R - 1 - q], jA + q * P, true);
     } else {
-        // slot 0 = (X[0], X[N]) = (Re Z0 + Im Z0, Re Z0 - Im Z0)
-        kio<TK>::store(krow, make_float2((A[0].x + A[0].y) * sh, (A[0].x - A[0].y) * sh));
+        // X[0] = Re Z0 + Im Z0, X[N] = Re Z0 - Im Z0 (both real)
+        const float x0 = (A[0].x + A[0].y) * sh, xn = (A[0].x - A[0].y) * sh;
+        if (!PAIR) {
+            kio<TK>::store(krow, make_float2(x0, xn));   // natural layout: slot 0 = (X[0], X[N])
+        } else {
+            put(0, make_float2(x0, 0.f));
+            put(NC, make_float2(xn, 0.f));
+        }
         emit(A[R / 2], A[R / 2], NC / 2, false);
 #pragma unroll
         for (int q = 1; q < R / 2; ++q) emit(A[q], A[R - q], q * P, true);
@@ -331,7 +354,9 @@ static hipError_t launch_prep_t(const void *k, int64_t L, void *kbins, const flo
     using Pl = FusedPlan<LOGN>;
     const int64_t blocks = (H + Pl::SPW - 1) / Pl::SPW;
     const size_t lds = (size_t)Pl::SPW * Pl::NC * sizeof(float2);
-    auto kern = fused_prepare_kernel<LOGN, T, TK>;
+    constexpr bool kPair = LOGN == 10 && !std::is_same<T, float>::value;
+    static_assert(!kPair || std::is_same<TK, __half2>::value, "pair layout stores fp16 bins");
+    auto kern = fused_prepare_kernel<LOGN, T, TK, kPair>;
     hipError_t e = hipFuncSetAttribute((const void *)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;

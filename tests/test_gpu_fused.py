@@ -140,3 +140,54 @@ def test_prepared_filter_matches_oracle_spectrum(dtype, logn, L):
         want = oracle.fft(x)[:N + 1]
         tol = 1e-6 if dtype == "f32" else 2e-3
         assert np.linalg.norm(got[h] - want) / np.linalg.norm(want) < tol
+
+
+# ---- N = 1024 in fp16 / bf16 storage runs on the matrix-core pair kernel
+@pytest.mark.parametrize("B,H", [(1, 1), (2, 1), (3, 5), (1, 7), (64, 3)])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_pair_kernel_batches(B, H, dtype):
+    _say(f"pair kernel B={B} H={H} {dtype}")
+    inp = synth.generate(B, H, 1024, 1024, dtype, gated=True, seed=B * 100 + H)
+    y = run_gpu(inp)
+    ref = oracle_full(inp)
+    assert oracle.rel_l2(y, ref) < TOL[dtype]
+
+
+@pytest.mark.parametrize("gates", ["none", "w", "v"])
+def test_pair_kernel_gates(gates):
+    _say(f"pair kernel gates={gates}")
+    inp = synth.generate(4, 3, 1024, 700, "f16", gated=True, seed=31)
+    if gates in ("none", "v"):
+        inp.w = None
+    if gates in ("none", "w"):
+        inp.v = None
+    y = run_gpu(inp)
+    ref = oracle.direct(inp.f64("u"), inp.f64("k"), inp.f64("w"), inp.f64("v"))
+    assert oracle.rel_l2(y, ref) < TOL["f16"]
+
+
+@pytest.mark.parametrize("kind", ["band", "random"])
+def test_pair_kernel_mask(kind):
+    _say(f"pair kernel mask {kind}")
+    inp = synth.generate(3, 4, 1024, 1024, "f16", gated=True, seed=32)
+    mask = synth.band_mask(4, 27) if kind == "band" else synth.random_mask(4, seed=3)
+    y = run_gpu(inp, mask)
+    ref = oracle_full(inp, mask)
+    assert oracle.rel_l2(y, ref) < TOL["f16"]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_pair_layout_spectrum(dtype):
+    _say(f"pair layout export {dtype}")
+    N, L = 1024, 555
+    inp = synth.generate(1, 3, N, L, dtype, seed=33)
+    k = inp.k.cuda()
+    K_f = fc.alloc_filter(3, N, k.dtype)
+    fc.fftconv_prepare_filter(k, N, K_f)
+    got = fc.fftconv_export_filter_rfft(K_f, 3, N, k.dtype)
+    k64 = inp.f64("k")
+    for h in range(3):
+        x = np.zeros(2 * N, complex)
+        x[:L] = k64[h]
+        want = oracle.fft(x)[:N + 1]
+        assert np.linalg.norm(got[h] - want) / np.linalg.norm(want) < 2e-3
