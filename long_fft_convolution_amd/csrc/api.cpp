@@ -139,7 +139,7 @@ hipError_t get_pair_tables(PairTables *out) {
     auto ang = [&](double num, double den) { return 2.0 * pi * num / den; };
     std::vector<_Float16> f1r(4 * 64 * 8), f1i(4 * 64 * 8), f2r(2 * 64 * 8), f2i(2 * 64 * 8),
         f3r(4 * 64 * 8), f3i(4 * 64 * 8);
-    std::vector<float2> tw1(2048), tw3(2048);
+    std::vector<_Float16> tw1(512 * 8), tw3(512 * 8);
     for (int l = 0; l < 64; ++l) {
         const int g = l / 16, c = l % 16;
         for (int j = 0; j < 8; ++j) {
@@ -165,12 +165,14 @@ hipError_t get_pair_tables(PairTables *out) {
             for (int mt = 0; mt < 2; ++mt)     // rows n_f = 16 mt + 4g + i, cols f_s = 16 nt + c
                 for (int nt = 0; nt < 4; ++nt) {
                     const double a = -ang((double)(16 * mt + 4 * g + i) * (16 * nt + c), 2048);
-                    tw1[((mt * 4 + nt) * 64 + l) * 4 + i] = make_float2((float)std::cos(a), (float)std::sin(a));
+                    tw1[((mt * 4 + nt) * 64 + l) * 8 + i] = (_Float16)std::cos(a);
+                    tw1[((mt * 4 + nt) * 64 + l) * 8 + 4 + i] = (_Float16)std::sin(a);
                 }
             for (int nt = 0; nt < 4; ++nt)     // rows f_s = 16 nt + 4g + i, cols n_f = 16 nt2 + c
                 for (int nt2 = 0; nt2 < 2; ++nt2) {
                     const double a = ang((double)(16 * nt2 + c) * (16 * nt + 4 * g + i), 2048);
-                    tw3[((nt * 2 + nt2) * 64 + l) * 4 + i] = make_float2((float)std::cos(a), (float)std::sin(a));
+                    tw3[((nt * 2 + nt2) * 64 + l) * 8 + i] = (_Float16)std::cos(a);
+                    tw3[((nt * 2 + nt2) * 64 + l) * 8 + 4 + i] = (_Float16)std::sin(a);
                 }
         }
     }
@@ -181,8 +183,8 @@ hipError_t get_pair_tables(PairTables *out) {
     if (e == hipSuccess) e = upload_h(f2i, &t.f2i);
     if (e == hipSuccess) e = upload_h(f3r, &t.f3r);
     if (e == hipSuccess) e = upload_h(f3i, &t.f3i);
-    if (e == hipSuccess) e = upload(tw1, &t.tw1);
-    if (e == hipSuccess) e = upload(tw3, &t.tw3);
+    if (e == hipSuccess) e = upload_h(tw1, &t.tw1);
+    if (e == hipSuccess) e = upload_h(tw3, &t.tw3);
     if (e != hipSuccess) return e;
     g_pair_tables[dev] = t;
     *out = t;
@@ -347,7 +349,9 @@ fftconv_status_t fftconv_prepare_filter(const void *k, int64_t H, int64_t L, int
     hdr.n2 = fused ? N : (int64_t(1) << sp.log2);
 
     hipError_t e = launch_write_header(hdr, K_f, stream);
-    if (e == hipSuccess) e = launch_filter_scale(dtype, k, H, L, kf_norm_log2(l, dtype), kscale, stream);
+    if (e == hipSuccess)
+        e = launch_filter_scale(dtype, k, H, L, kf_norm_log2(l, dtype), kf_target_log2(l, dtype), kscale,
+                                stream);
     if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "filter setup launch: %s", hipGetErrorString(e));
     if (fused) {
         Tables tb{};

@@ -57,6 +57,9 @@ inline int64_t kf_slots(int logn, int st) {
 // log2 of the normalisation folded into scale[h]: 4N for the half-length
 // real transform (fused, multi-pass), 2N for the pair kernel.
 inline int kf_norm_log2(int logn, int st) { return use_pair_kernel(logn, st) ? logn + 1 : logn + 2; }
+// Bound on the stored bins |K| * s_h: 2^14 for the layouts the VALU kernels
+// rescale in fp32, 1 for the pair layout whose product is taken in fp16.
+inline int kf_target_log2(int logn, int st) { return use_pair_kernel(logn, st) ? 0 : 14; }
 // fp16 element offset of the real part of bin f in the pair layout (imag at +4)
 __host__ __device__ inline int64_t pair_kf_index(int64_t f) {
     const int64_t fs = f % 64, ff = f / 64;
@@ -100,15 +103,15 @@ hipError_t launch_fused_prepare(int logn, int st, const void *k, int64_t L, void
                                 const float *kscale, const Tables &tb, int64_t H,
                                 hipStream_t stream);
 hipError_t launch_filter_scale(int st, const void *k, int64_t H, int64_t L, int norm_log2,
-                               float *kscale, hipStream_t stream);
+                               int target_log2, float *kscale, hipStream_t stream);
 
 // Lane-order constant tables of the pair kernel (see pair_mfma.hip).
 struct PairTables {
     const void *f1r, *f1i;   // S1 DFT-64 blocks, [4][64 lanes][8] fp16
     const void *f2r, *f2i;   // S2 DFT-32 blocks, [2][64][8] fp16
     const void *f3r, *f3i;   // S1' conj DFT-64 blocks, [2 ks * 2 nt][64][8] fp16
-    const float2 *tw1;       // forward twiddles, [2 mt][4 nt][64][4]
-    const float2 *tw3;       // inverse twiddles, [4 nt][2 nt2][64][4]
+    const void *tw1;         // forward twiddles, [2 mt][4 nt][64 lanes]: cos[4], sin[4] fp16
+    const void *tw3;         // inverse twiddles, [4 nt][2 nt2][64]: cos[4], sin[4] fp16
 };
 hipError_t get_pair_tables(PairTables *out);
 hipError_t launch_pair_conv(int logn, int st, const void *u, const void *w, const void *v,

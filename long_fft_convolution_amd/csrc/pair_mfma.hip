@@ -19,16 +19,23 @@
 //    stage's operand layout by permuting the contraction index:
 //    K slot 8g + j <-> row 4g + j (j < 4) of tile 0, row 4g + j - 4 of tile 1.
 //    So the stages chain in registers; only the input goes through LDS.
-//  * Twiddles and the filter product are fp32 on the VALU between stages.
+//  * Twiddles and the filter product are packed fp16 on the VALU between
+//    stages (the stored spectrum is scaled so |K| <= 1; the per-channel fp32
+//    scale is applied to the fp32 result of the last stage).
 //
 // One wave owns one sequence pair at a time and loops over pairs
-// (persistent); the DFT blocks stay in registers across pairs.
+// (persistent), prefetching the next pair's inputs, filter and gate chunks;
+// twiddles and two of the three DFT block sets live in LDS so that two
+// workgroups of four waves fit per CU.
 #include "fft_device.hpp"
 #include "fftconv_internal.hpp"
+
+#include <type_traits>
 
 namespace fftconv {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) {
@@ -46,6 +53,11 @@ template <> struct io8<__half> {
     }
     static __device__ __forceinline__ void load4(const __half *p, float *o) {
         const uint2 raw = *reinterpret_cast<const uint2 *>(p);
+        const _Float16 *hv = reinterpret_cast<const _Float16 *>(&raw);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = (float)hv[i];
+    }
+    static __device__ __forceinline__ void unpack4(const uint2 &raw, float *o) {
         const _Float16 *hv = reinterpret_cast<const _Float16 *>(&raw);
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = (float)hv[i];
@@ -69,6 +81,12 @@ template <> struct io8<__hip_bfloat16> {
     }
     static __device__ __forceinline__ void load4(const __hip_bfloat16 *p, float *o) {
         const uint2 raw = *reinterpret_cast<const uint2 *>(p);
+        o[0] = __uint_as_float(raw.x << 16);
+        o[1] = __uint_as_float(raw.x & 0xffff0000u);
+        o[2] = __uint_as_float(raw.y << 16);
+        o[3] = __uint_as_float(raw.y & 0xffff0000u);
+    }
+    static __device__ __forceinline__ void unpack4(const uint2 &raw, float *o) {
         o[0] = __uint_as_float(raw.x << 16);
         o[1] = __uint_as_float(raw.x & 0xffff0000u);
         o[2] = __uint_as_float(raw.y << 16);
@@ -106,35 +124,116 @@ __device__ __forceinline__ int kslot_of(int ns) {
 constexpr int kPairWaves = 4;
 constexpr int kPlane = 32 * 32;     // fp16 elements per LDS plane (rows n_f, K slots)
 
+// raw 16-byte input chunks of one pair: [u_a, w_a, u_b, w_b] x [r = 0, 1]
+struct PairRaw {
+    uint4 q[2][4];
+};
+
 template <typename T>
-__global__ void __launch_bounds__(64 * kPairWaves)
+__device__ __forceinline__ void load_pair_raw(PairRaw &raw, const T *__restrict__ u,
+                                              const T *__restrict__ w, int64_t oa, int64_t ob,
+                                              bool has_b, int lane) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int m0 = 8 * lane + 512 * r;
+        raw.q[r][0] = *reinterpret_cast<const uint4 *>(u + oa + m0);
+        raw.q[r][1] = w != nullptr ? *reinterpret_cast<const uint4 *>(w + oa + m0) : make_uint4(0, 0, 0, 0);
+        raw.q[r][2] = has_b ? *reinterpret_cast<const uint4 *>(u + ob + m0) : make_uint4(0, 0, 0, 0);
+        raw.q[r][3] = (has_b && w != nullptr) ? *reinterpret_cast<const uint4 *>(w + ob + m0)
+                                              : make_uint4(0, 0, 0, 0);
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void unpack8(const uint4 &q, float *o);
+template <>
+__device__ __forceinline__ void unpack8<__half>(const uint4 &q, float *o) {
+    const _Float16 *hv = reinterpret_cast<const _Float16 *>(&q);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = (float)hv[i];
+}
+template <>
+__device__ __forceinline__ void unpack8<__hip_bfloat16>(const uint4 &q, float *o) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        o[2 * i] = __uint_as_float(w[i] << 16);
+        o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+
+__device__ __forceinline__ h4 to_h4(const f4 &a) {
+    h4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = (_Float16)a[i];
+    return r;
+}
+__device__ __forceinline__ h8 cat8(const h4 &lo, const h4 &hi) {
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ h4 lo4(const h8 &a) { return __builtin_shufflevector(a, a, 0, 1, 2, 3); }
+__device__ __forceinline__ h4 hi4(const h8 &a) { return __builtin_shufflevector(a, a, 4, 5, 6, 7); }
+
+// (re, im) <- (re, im) * (c + i s), four values, packed fp16; t = {c[0..3], s[0..3]}
+__device__ __forceinline__ void cmul4(h4 &re, h4 &im, const h8 &t) {
+    const h4 c = lo4(t), s = hi4(t);
+    const h4 r = re * c - im * s;
+    im = re * s + im * c;
+    re = r;
+}
+
+// x = u * w as eight fp16 values (w absent: x = u).  fp16 storage: one packed
+// product (the fp16 product of two fp16 values, correctly rounded, equals the
+// fp32 product rounded to fp16); bf16 storage: fp32 product rounded to fp16.
+template <typename T>
+__device__ __forceinline__ void gate_product(const uint4 &uq, const uint4 &wq, bool gated, h8 &x);
+template <>
+__device__ __forceinline__ void gate_product<__half>(const uint4 &uq, const uint4 &wq, bool gated, h8 &x) {
+    const h8 uu = *reinterpret_cast<const h8 *>(&uq);
+    x = gated ? uu * *reinterpret_cast<const h8 *>(&wq) : uu;
+}
+template <>
+__device__ __forceinline__ void gate_product<__hip_bfloat16>(const uint4 &uq, const uint4 &wq, bool gated,
+                                                             h8 &x) {
+    float a[8], b[8];
+    unpack8<__hip_bfloat16>(uq, a);
+    if (gated) {
+        unpack8<__hip_bfloat16>(wq, b);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] *= b[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (_Float16)a[e];
+}
+
+template <typename T, bool MASKED>
+__global__ void __launch_bounds__(64 * kPairWaves, MASKED ? 1 : 2)
 pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restrict__ v,
               T *__restrict__ out, const uint4 *__restrict__ kbins, const float *__restrict__ kscale,
               const uint8_t *__restrict__ mask, PairTables tb, int64_t B, int64_t H) {
     constexpr int N = 1024;
-    __shared__ float2 s_tw1[2 * 4 * 64 * 4];
-    __shared__ float2 s_tw3[4 * 2 * 64 * 4];
+    __shared__ h8 s_tw1[2 * 4 * 64];     // per (mt, nt, lane): cos[4], sin[4]
+    __shared__ h8 s_tw3[4 * 2 * 64];     // per (nt, nt2, lane)
     __shared__ _Float16 s_z[kPairWaves][2][kPlane];
+    __shared__ h8 s_f1[2][4][64];     // S1 DFT blocks (re, im) per column tile nt
+    __shared__ h8 s_f3[2][4][64];     // S1' DFT blocks (re, im) per (ks, nt3)
 
     const int tid = threadIdx.x;
-    for (int i = tid; i < 2048; i += 64 * kPairWaves) {
-        s_tw1[i] = tb.tw1[i];
-        s_tw3[i] = tb.tw3[i];
+    for (int i = tid; i < 512; i += 64 * kPairWaves) {
+        s_tw1[i] = reinterpret_cast<const h8 *>(tb.tw1)[i];
+        s_tw3[i] = reinterpret_cast<const h8 *>(tb.tw3)[i];
+    }
+    for (int i = tid; i < 256; i += 64 * kPairWaves) {
+        s_f1[0][i / 64][i % 64] = reinterpret_cast<const h8 *>(tb.f1r)[i];
+        s_f1[1][i / 64][i % 64] = reinterpret_cast<const h8 *>(tb.f1i)[i];
+        s_f3[0][i / 64][i % 64] = reinterpret_cast<const h8 *>(tb.f3r)[i];
+        s_f3[1][i / 64][i % 64] = reinterpret_cast<const h8 *>(tb.f3i)[i];
     }
     __syncthreads();
 
     const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
-    const h8 *F1r = reinterpret_cast<const h8 *>(tb.f1r), *F1i = reinterpret_cast<const h8 *>(tb.f1i);
     const h8 *F2r = reinterpret_cast<const h8 *>(tb.f2r), *F2i = reinterpret_cast<const h8 *>(tb.f2i);
-    const h8 *F3r = reinterpret_cast<const h8 *>(tb.f3r), *F3i = reinterpret_cast<const h8 *>(tb.f3i);
-    h8 c1r[4], c1i[4], c2r[2], c2i[2], c3r[4], c3i[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        c1r[t] = F1r[t * 64 + lane];
-        c1i[t] = F1i[t * 64 + lane];
-        c3r[t] = F3r[t * 64 + lane];
-        c3i[t] = F3i[t * 64 + lane];
-    }
+    h8 c2r[2], c2i[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         c2r[t] = F2r[t * 64 + lane];
@@ -151,39 +250,69 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
     _Float16 *zr = s_z[wave][0], *zi = s_z[wave][1];
     const f4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
-    for (int64_t p = p_begin + (int64_t)wg_local * kPairWaves + wave; p < p_end; p += stride) {
-        const int64_t h = p / PB, bp = p % PB;
-        const int64_t ba = 2 * bp, bb = 2 * bp + 1;
-        const bool has_b = bb < B;
-        const int64_t oa = (ba * H + h) * N, ob = (has_b ? bb * H + h : 0) * N;
+    auto offsets = [&](int64_t p, int64_t &h, int64_t &oa, int64_t &ob, bool &has_b) {
+        h = p / PB;
+        const int64_t bp = p - h * PB;
+        has_b = 2 * bp + 1 < B;
+        oa = (2 * bp * H + h) * N;
+        ob = has_b ? oa + H * N : oa;
+    };
 
-        // ---- load x = u * w of both sequences, scatter into the transposed LDS planes
+    // per-pair side data: filter chunks and output-gate chunks
+    struct Side {
+        uint4 k[2][4];
+        float ks;
+    };
+    auto load_side = [&](int64_t pp, Side &sd) {
+        int64_t h, oa, ob;
+        bool hb;
+        offsets(pp, h, oa, ob, hb);
+        const uint4 *krow = kbins + h * 512;
+#pragma unroll
+        for (int mt2 = 0; mt2 < 2; ++mt2)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) sd.k[mt2][nt] = krow[(mt2 * 4 + nt) * 64 + lane];
+        sd.ks = kscale[h];
+    };
+    auto load_in = [&](int64_t pp, PairRaw &raw) {
+        int64_t h, oa, ob;
+        bool hb;
+        offsets(pp, h, oa, ob, hb);
+        load_pair_raw<T>(raw, u, w, oa, ob, hb, lane);
+    };
+
+    // software pipeline: inputs, filter chunks and gate chunks one pair ahead
+    int64_t p = p_begin + (int64_t)wg_local * kPairWaves + wave;
+    PairRaw cur;
+    Side sc;
+    if (p < p_end) {
+        load_in(p, cur);
+        load_side(p, sc);
+    }
+    for (; p < p_end; p += stride) {
+        int64_t h, oa, ob;
+        bool has_b;
+        offsets(p, h, oa, ob, has_b);
+        PairRaw in1;
+        Side sn;
+        if (p + stride < p_end) {
+            load_in(p + stride, in1);
+            load_side(p + stride, sn);
+        }
+        const float ks = sc.ks;
+
+        // ---- x = u * w of both sequences, scattered into the transposed LDS planes
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
             const int m0 = 8 * lane + 512 * r;
-            float xa[8], xb[8], g8[8];
-            io8<T>::load(u + oa + m0, xa);
-            if (w != nullptr) {
-                io8<T>::load(w + oa + m0, g8);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) xa[e] *= g8[e];
-            }
-            if (has_b) {
-                io8<T>::load(u + ob + m0, xb);
-                if (w != nullptr) {
-                    io8<T>::load(w + ob + m0, g8);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) xb[e] *= g8[e];
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) xb[e] = 0.f;
-            }
-            const int ns = m0 >> 5, nf0 = m0 & 31, ks = kslot_of(ns);
+            h8 xa, xb;
+            gate_product<T>(cur.q[r][0], cur.q[r][1], w != nullptr, xa);
+            gate_product<T>(cur.q[r][2], cur.q[r][3], w != nullptr, xb);
+            const int ns = m0 >> 5, nf0 = m0 & 31, kss = kslot_of(ns);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                zr[(nf0 + e) * 32 + ks] = (_Float16)xa[e];
-                zi[(nf0 + e) * 32 + ks] = (_Float16)xb[e];
+                zr[(nf0 + e) * 32 + kss] = xa[e];
+                zi[(nf0 + e) * 32 + kss] = xb[e];
             }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -199,78 +328,67 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         const h8 ndi0 = -di[0], ndi1 = -di[1];
+        const uint8_t *mrow = MASKED ? mask + h * kMaskBlocks : nullptr;
 
-        const float ks = kscale[h];
-        const uint4 *krow = kbins + h * 512;
-        const uint8_t *mrow = mask != nullptr ? mask + h * kMaskBlocks : nullptr;
-
-        // T3 operand planes for S1' : [ks][nt2] (rows f_s of tiles nt = 2ks, 2ks+1)
-        f4 t3r[4][2], t3i[4][2];
+        // S1' operands, fp16: a[ks][nt2] (re, im); rows f_s of tiles nt = 2ks (j < 4), 2ks+1 (j >= 4)
+        h8 a3r[2][2], a3i[2][2];
 
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-            // ---- S1: rows n_f (tiles mt), column tile nt of f_s; then twiddle w2048^{nf fs}
-            f4 t1r[2], t1i[2];
+            // ---- S1: rows n_f (tiles mt), column tile nt of f_s; twiddle w2048^{nf fs} (fp16)
+            h4 t1r[2], t1i[2];
+            const h8 f1r = s_f1[0][nt][lane], f1i = s_f1[1][nt][lane];
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
-                f4 ar = mfma(dr[mt], c1r[nt], zero4);
-                ar = mfma(mt == 0 ? ndi0 : ndi1, c1i[nt], ar);
-                f4 ai = mfma(dr[mt], c1i[nt], zero4);
-                ai = mfma(di[mt], c1r[nt], ai);
-                const float4 *tw = reinterpret_cast<const float4 *>(s_tw1 + ((mt * 4 + nt) * 64 + lane) * 4);
-                const float4 w01 = tw[0], w23 = tw[1];
-                const float wr[4] = {w01.x, w01.z, w23.x, w23.z}, wi[4] = {w01.y, w01.w, w23.y, w23.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float re = ar[i], im = ai[i];
-                    t1r[mt][i] = fmaf(re, wr[i], -im * wi[i]);
-                    t1i[mt][i] = fmaf(re, wi[i], im * wr[i]);
-                }
+                f4 ar = mfma(dr[mt], f1r, zero4);
+                ar = mfma(mt == 0 ? ndi0 : ndi1, f1i, ar);
+                f4 ai = mfma(dr[mt], f1i, zero4);
+                ai = mfma(di[mt], f1r, ai);
+                t1r[mt] = to_h4(ar);
+                t1i[mt] = to_h4(ai);
+                cmul4(t1r[mt], t1i[mt], s_tw1[(mt * 4 + nt) * 64 + lane]);
             }
-            const h8 br = pack8(t1r[0], t1r[1]), bi = pack8(t1i[0], t1i[1]);
+            const h8 br = cat8(t1r[0], t1r[1]), bi = cat8(t1i[0], t1i[1]);
             const h8 nbi = -bi;
-            // ---- S2: rows f_f (tiles mt2), column tile nt; then the filter product
-            f4 yr[2], yi[2];
+            // ---- S2: rows f_f (tiles mt2), column tile nt; filter product (fp16, |K| <= 1)
+            h4 yr[2], yi[2];
 #pragma unroll
             for (int mt2 = 0; mt2 < 2; ++mt2) {
                 f4 ar = mfma(c2r[mt2], br, zero4);
                 ar = mfma(c2i[mt2], nbi, ar);
                 f4 ai = mfma(c2r[mt2], bi, zero4);
                 ai = mfma(c2i[mt2], br, ai);
-                const uint4 kraw = krow[(mt2 * 4 + nt) * 64 + lane];
-                const _Float16 *kh = reinterpret_cast<const _Float16 *>(&kraw);
+                yr[mt2] = to_h4(ar);
+                yi[mt2] = to_h4(ai);
+                h8 kk = *reinterpret_cast<const h8 *>(&sc.k[mt2][nt]);
+                if (MASKED) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float kr = (float)kh[i] * ks, ki = (float)kh[4 + i] * ks;
-                    if (mrow != nullptr) {
+                    for (int i = 0; i < 4; ++i) {
                         const int f = 16 * nt + c + 64 * (16 * mt2 + 4 * g + i);
                         const int fr = f <= N ? f : 2 * N - f;
                         int blk = fr / (N / kMaskBlocks);
                         blk = blk > kMaskBlocks - 1 ? kMaskBlocks - 1 : blk;
-                        if (!mrow[blk]) kr = ki = 0.f;
+                        if (!mrow[blk]) kk[i] = kk[4 + i] = (_Float16)0.f;
                     }
-                    const float re = ar[i], im = ai[i];
-                    yr[mt2][i] = fmaf(re, kr, -im * ki);
-                    yi[mt2][i] = fmaf(re, ki, im * kr);
                 }
+                cmul4(yr[mt2], yi[mt2], kk);
             }
-            const h8 a2r = pack8(yr[0], yr[1]), a2i = pack8(yi[0], yi[1]);
+            const h8 a2r = cat8(yr[0], yr[1]), a2i = cat8(yi[0], yi[1]);
             const h8 na2r = -a2r;
-            // ---- S2': rows f_s (this tile nt), column tiles nt2 of n_f; then conj twiddle
+            // ---- S2': rows f_s (tile nt), column tiles nt2 of n_f; conj twiddle (fp16)
 #pragma unroll
             for (int nt2 = 0; nt2 < 2; ++nt2) {
                 f4 ar = mfma(a2r, c2r[nt2], zero4);
                 ar = mfma(a2i, c2i[nt2], ar);
                 f4 ai = mfma(na2r, c2i[nt2], zero4);
                 ai = mfma(a2i, c2r[nt2], ai);
-                const float4 *tw = reinterpret_cast<const float4 *>(s_tw3 + ((nt * 2 + nt2) * 64 + lane) * 4);
-                const float4 w01 = tw[0], w23 = tw[1];
-                const float wr[4] = {w01.x, w01.z, w23.x, w23.z}, wi[4] = {w01.y, w01.w, w23.y, w23.w};
+                h4 t3r = to_h4(ar), t3i = to_h4(ai);
+                cmul4(t3r, t3i, s_tw3[(nt * 2 + nt2) * 64 + lane]);
+                const int ksi = nt >> 1, half = (nt & 1) * 4;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float re = ar[i], im = ai[i];
-                    t3r[nt][nt2][i] = fmaf(re, wr[i], -im * wi[i]);
-                    t3i[nt][nt2][i] = fmaf(re, wi[i], im * wr[i]);
+                    a3r[ksi][nt2][half + i] = t3r[i];
+                    a3i[ksi][nt2][half + i] = t3i[i];
                 }
             }
         }
@@ -278,37 +396,38 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
         // ---- S1': rows n_f (tiles nt2), columns n_s (tiles nt3, n_s < 32 only), K = f_s
 #pragma unroll
         for (int nt2 = 0; nt2 < 2; ++nt2) {
-            const h8 a0r = pack8(t3r[0][nt2], t3r[1][nt2]), a0i = pack8(t3i[0][nt2], t3i[1][nt2]);
-            const h8 a1r = pack8(t3r[2][nt2], t3r[3][nt2]), a1i = pack8(t3i[2][nt2], t3i[3][nt2]);
-            const h8 na0i = -a0i, na1i = -a1i;
+            const h8 na0i = -a3i[0][nt2], na1i = -a3i[1][nt2];
 #pragma unroll
             for (int nt3 = 0; nt3 < 2; ++nt3) {
-                f4 ar = mfma(a0r, c3r[nt3], zero4);
-                ar = mfma(na0i, c3i[nt3], ar);
-                ar = mfma(a1r, c3r[2 + nt3], ar);
-                ar = mfma(na1i, c3i[2 + nt3], ar);
-                f4 ai = mfma(a0r, c3i[nt3], zero4);
-                ai = mfma(a0i, c3r[nt3], ai);
-                ai = mfma(a1r, c3i[2 + nt3], ai);
-                ai = mfma(a1i, c3r[2 + nt3], ai);
+                const h8 f30r = s_f3[0][nt3][lane], f30i = s_f3[1][nt3][lane];
+                const h8 f31r = s_f3[0][2 + nt3][lane], f31i = s_f3[1][2 + nt3][lane];
+                f4 ar = mfma(a3r[0][nt2], f30r, zero4);
+                ar = mfma(na0i, f30i, ar);
+                ar = mfma(a3r[1][nt2], f31r, ar);
+                ar = mfma(na1i, f31i, ar);
+                f4 ai = mfma(a3r[0][nt2], f30i, zero4);
+                ai = mfma(a3i[0][nt2], f30r, ai);
+                ai = mfma(a3r[1][nt2], f31i, ai);
+                ai = mfma(a3i[1][nt2], f31r, ai);
                 // rows n_f = 16 nt2 + 4g + i, column n_s = 16 nt3 + c: m = n_f + 32 n_s
                 const int m = 16 * nt2 + 4 * g + 32 * (16 * nt3 + c);
-                float ya[4] = {ar[0], ar[1], ar[2], ar[3]}, yb[4] = {ai[0], ai[1], ai[2], ai[3]};
+                float ya[4] = {ar[0] * ks, ar[1] * ks, ar[2] * ks, ar[3] * ks};
+                float yb[4] = {ai[0] * ks, ai[1] * ks, ai[2] * ks, ai[3] * ks};
                 if (v != nullptr) {
                     float g4[4];
                     io8<T>::load4(v + oa + m, g4);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) ya[i] *= g4[i];
-                    if (has_b) {
-                        io8<T>::load4(v + ob + m, g4);
+                    io8<T>::load4(v + ob + m, g4);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) yb[i] *= g4[i];
-                    }
+                    for (int i = 0; i < 4; ++i) yb[i] *= g4[i];
                 }
                 io8<T>::store4(out + oa + m, ya);
                 if (has_b) io8<T>::store4(out + ob + m, yb);
             }
         }
+        cur = in1;
+        sc = sn;
     }
 }
 
@@ -326,18 +445,22 @@ hipError_t launch_pair_conv(int logn, int st, const void *u, const void *w, cons
             cus = v_;
     }
     const int64_t pairs = H * ((B + 1) / 2);
-    int64_t blocks = (int64_t)cus;                           // one resident 4-wave workgroup per CU
+    // two resident 4-wave workgroups per CU (one for the masked variant)
+    int64_t blocks = (int64_t)cus * (mask ? 1 : 2);
     const int64_t need = (pairs + kPairWaves - 1) / kPairWaves;
     if (blocks > need) blocks = need < 8 ? 8 : (need + 7) / 8 * 8;
+    auto go = [&](auto kern, auto *tp) {
+        using TT = std::remove_pointer_t<decltype(tp)>;
+        hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * kPairWaves), 0, stream,
+                           (const TT *)u, (const TT *)w, (const TT *)v, (TT *)out,
+                           (const uint4 *)kbins, kscale, mask, tb, B, H);
+    };
     if (st == ST_F16) {
-        hipLaunchKernelGGL(pair1k_kernel<__half>, dim3((unsigned)blocks), dim3(64 * kPairWaves), 0,
-                           stream, (const __half *)u, (const __half *)w, (const __half *)v,
-                           (__half *)out, (const uint4 *)kbins, kscale, mask, tb, B, H);
+        if (mask) go(pair1k_kernel<__half, true>, (__half *)nullptr);
+        else go(pair1k_kernel<__half, false>, (__half *)nullptr);
     } else {
-        hipLaunchKernelGGL(pair1k_kernel<__hip_bfloat16>, dim3((unsigned)blocks),
-                           dim3(64 * kPairWaves), 0, stream, (const __hip_bfloat16 *)u,
-                           (const __hip_bfloat16 *)w, (const __hip_bfloat16 *)v,
-                           (__hip_bfloat16 *)out, (const uint4 *)kbins, kscale, mask, tb, B, H);
+        if (mask) go(pair1k_kernel<__hip_bfloat16, true>, (__hip_bfloat16 *)nullptr);
+        else go(pair1k_kernel<__hip_bfloat16, false>, (__hip_bfloat16 *)nullptr);
     }
     return hipGetLastError();
 }
