@@ -162,6 +162,16 @@ __device__ __forceinline__ void unpack8<__hip_bfloat16>(const uint4 &q, float *o
     }
 }
 
+// sign flip of eight fp16 values: one integer xor per register
+__device__ __forceinline__ h8 neg8(const h8 &a) {
+    uint4 q = *reinterpret_cast<const uint4 *>(&a);
+    q.x ^= 0x80008000u;
+    q.y ^= 0x80008000u;
+    q.z ^= 0x80008000u;
+    q.w ^= 0x80008000u;
+    return *reinterpret_cast<const h8 *>(&q);
+}
+
 __device__ __forceinline__ h4 to_h4(const f4 &a) {
     h4 r;
 #pragma unroll
@@ -231,7 +241,8 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
     }
     __syncthreads();
 
-    const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
+    // the wave index is uniform: keep pair bookkeeping and addresses scalar
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, c = lane & 15;
     const h8 *F2r = reinterpret_cast<const h8 *>(tb.f2r), *F2i = reinterpret_cast<const h8 *>(tb.f2i);
     h8 c2r[2], c2i[2];
 #pragma unroll
@@ -327,7 +338,7 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const h8 ndi0 = -di[0], ndi1 = -di[1];
+        const h8 ndi0 = neg8(di[0]), ndi1 = neg8(di[1]);
         const uint8_t *mrow = MASKED ? mask + h * kMaskBlocks : nullptr;
 
         // S1' operands, fp16: a[ks][nt2] (re, im); rows f_s of tiles nt = 2ks (j < 4), 2ks+1 (j >= 4)
@@ -349,7 +360,7 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
                 cmul4(t1r[mt], t1i[mt], s_tw1[(mt * 4 + nt) * 64 + lane]);
             }
             const h8 br = cat8(t1r[0], t1r[1]), bi = cat8(t1i[0], t1i[1]);
-            const h8 nbi = -bi;
+            const h8 nbi = neg8(bi);
             // ---- S2: rows f_f (tiles mt2), column tile nt; filter product (fp16, |K| <= 1)
             h4 yr[2], yi[2];
 #pragma unroll
@@ -374,7 +385,7 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
                 cmul4(yr[mt2], yi[mt2], kk);
             }
             const h8 a2r = cat8(yr[0], yr[1]), a2i = cat8(yi[0], yi[1]);
-            const h8 na2r = -a2r;
+            const h8 na2r = neg8(a2r);
             // ---- S2': rows f_s (tile nt), column tiles nt2 of n_f; conj twiddle (fp16)
 #pragma unroll
             for (int nt2 = 0; nt2 < 2; ++nt2) {
@@ -396,7 +407,7 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
         // ---- S1': rows n_f (tiles nt2), columns n_s (tiles nt3, n_s < 32 only), K = f_s
 #pragma unroll
         for (int nt2 = 0; nt2 < 2; ++nt2) {
-            const h8 na0i = -a3i[0][nt2], na1i = -a3i[1][nt2];
+            const h8 na0i = neg8(a3i[0][nt2]), na1i = neg8(a3i[1][nt2]);
 #pragma unroll
             for (int nt3 = 0; nt3 < 2; ++nt3) {
                 const h8 f30r = s_f3[0][nt3][lane], f30i = s_f3[1][nt3][lane];
