@@ -191,6 +191,71 @@ hipError_t get_pair_tables(PairTables *out) {
     return hipSuccess;
 }
 
+namespace {
+std::mutex g_pair3_mu;
+std::map<int, Pair3Tables> g_pair3_tables;
+}  // namespace
+
+hipError_t get_pair3_tables(Pair3Tables *out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lk(g_pair3_mu);
+    auto it = g_pair3_tables.find(dev);
+    if (it != g_pair3_tables.end()) {
+        *out = it->second;
+        return hipSuccess;
+    }
+    const double pi = 3.14159265358979323846264338327950288;
+    const double M2 = 32768.0;
+    std::vector<_Float16> fr(2 * 64 * 8), fi(2 * 64 * 8), tw1(4 * 64 * 8), tw3(4 * 64 * 8),
+        two1((size_t)64 * 2 * 64 * 8), two2((size_t)32 * 4 * 64 * 8);
+    auto put8 = [](std::vector<_Float16> &v, size_t chunk, int i, double ang) {
+        v[chunk * 8 + i] = (_Float16)std::cos(ang);
+        v[chunk * 8 + 4 + i] = (_Float16)std::sin(ang);
+    };
+    for (int l = 0; l < 64; ++l) {
+        const int g = l / 16, c = l % 16;
+        for (int t = 0; t < 2; ++t)
+            for (int j = 0; j < 8; ++j) {   // DFT-32 tile t: w32^{rho(8g+j) (16 t + c)}
+                const double a = -2.0 * pi * (double)rho(8 * g + j) * (16 * t + c) / 32.0;
+                fr[(t * 64 + l) * 8 + j] = (_Float16)std::cos(a);
+                fi[(t * 64 + l) * 8 + j] = (_Float16)std::sin(a);
+            }
+        for (int i = 0; i < 4; ++i) {
+            for (int mt = 0; mt < 2; ++mt)      // rows n_a = 16mt + 4g + i, cols f_b = 16nt + c
+                for (int nt = 0; nt < 2; ++nt)
+                    put8(tw1, (mt * 2 + nt) * 64 + l, i, -2.0 * pi * (double)(16 * mt + 4 * g + i) * (16 * nt + c) / 1024.0);
+            for (int nt = 0; nt < 2; ++nt)      // rows f_b = 16nt + 4g + i, cols n_a = 16nt2 + c (conj)
+                for (int nt2 = 0; nt2 < 2; ++nt2)
+                    put8(tw3, (nt * 2 + nt2) * 64 + l, i, 2.0 * pi * (double)(16 * nt2 + c) * (16 * nt + 4 * g + i) / 1024.0);
+            for (int T = 0; T < 64; ++T)        // rows f_c = 16nt + 4g + i, cols n_ab = 16T + c
+                for (int nt = 0; nt < 2; ++nt) {
+                    const double a = (double)((int64_t)(16 * nt + 4 * g + i) * (16 * T + c) % 32768);
+                    put8(two1, ((size_t)T * 2 + nt) * 64 + l, i, -2.0 * pi * a / M2);
+                }
+            for (int fc = 0; fc < 32; ++fc)     // rows n_b = 16nt3 + 4g + i, cols n_a = 16nt2 + c (conj)
+                for (int nt3 = 0; nt3 < 2; ++nt3)
+                    for (int nt2 = 0; nt2 < 2; ++nt2) {
+                        const int64_t nab = (16 * nt2 + c) + 32 * (16 * nt3 + 4 * g + i);
+                        const double a = (double)((int64_t)fc * nab % 32768);
+                        put8(two2, (((size_t)fc * 2 + nt3) * 2 + nt2) * 64 + l, i, 2.0 * pi * a / M2);
+                    }
+        }
+    }
+    Pair3Tables t{};
+    e = upload_h(fr, &t.fr);
+    if (e == hipSuccess) e = upload_h(fi, &t.fi);
+    if (e == hipSuccess) e = upload_h(tw1, &t.tw1);
+    if (e == hipSuccess) e = upload_h(tw3, &t.tw3);
+    if (e == hipSuccess) e = upload_h(two1, &t.two1);
+    if (e == hipSuccess) e = upload_h(two2, &t.two2);
+    if (e != hipSuccess) return e;
+    g_pair3_tables[dev] = t;
+    *out = t;
+    return hipSuccess;
+}
+
 hipError_t get_mp_tables(int logn, MpTables *out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -342,7 +407,8 @@ fftconv_status_t fftconv_prepare_filter(const void *k, int64_t H, int64_t L, int
     hdr.H = H;
     hdr.L = L;
     hdr.dtype = (int32_t)dtype;
-    hdr.layout = !fused ? KF_ROWS : (use_pair_kernel(l, dtype) ? KF_PAIR : KF_NATURAL);
+    hdr.layout = !fused ? KF_ROWS
+                        : (use_pair_kernel(l, dtype) ? KF_PAIR : (use_pair3_kernel(l, dtype) ? KF_PAIR3 : KF_NATURAL));
     hdr.scale_off = (int64_t)kf_scale_off();
     hdr.bins_off = (int64_t)kf_bins_off(H);
     hdr.n1 = fused ? 0 : (int64_t(1) << sp.log1);
@@ -424,6 +490,8 @@ fftconv_status_t fftconv_fwd(const void *u, const void *K_f, const void *w, cons
     hipError_t e = hipSuccess;
     if (use_pair_kernel(l, dtype)) {
         e = launch_pair_conv(l, dtype, u, w, v, out, kbins, kscale, mask, B, H, stream);
+    } else if (use_pair3_kernel(l, dtype)) {
+        e = launch_pair16k_conv(dtype, u, w, v, out, kbins, kscale, mask, B, H, stream);
     } else if (l <= kFusedMaxLog) {
         Tables tb{};
         e = get_tables(l, &tb);
@@ -479,12 +547,17 @@ fftconv_status_t fftconv_export_filter_rfft(const void *K_f, int64_t H, int64_t 
             *im *= inv_sh;
         };
         double *o = host_out + h * (N + 1) * 2;
-        if (hdr.layout == KF_PAIR) {
+        if (hdr.layout == KF_PAIR || hdr.layout == KF_PAIR3) {
             const _Float16 *p = reinterpret_cast<const _Float16 *>(bins) + h * slots * 2;
             for (int64_t f = 0; f <= N; ++f) {
-                const int64_t a = pair_kf_index(f);
+                int64_t a = hdr.layout == KF_PAIR ? pair_kf_index(f) : pair3_kf_index(f);
+                double sign = 1.0;
+                if (a < 0) {   // row not stored: conjugate of the mirror bin 2N - f
+                    a = pair3_kf_index(2 * N - f);
+                    sign = -1.0;
+                }
                 o[2 * f] = (double)p[a] * inv_sh;
-                o[2 * f + 1] = (double)p[a + 4] * inv_sh;
+                o[2 * f + 1] = sign * (double)p[a + 4] * inv_sh;
             }
             continue;
         }

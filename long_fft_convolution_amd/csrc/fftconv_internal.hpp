@@ -17,7 +17,7 @@ constexpr int kMaxLog = 22;
 constexpr int kMaskBlocks = 128;
 
 enum StorageType : int { ST_F32 = 0, ST_F16 = 1, ST_BF16 = 2 };
-enum KfLayout : int { KF_NATURAL = 0, KF_ROWS = 1, KF_PAIR = 2 };
+enum KfLayout : int { KF_NATURAL = 0, KF_ROWS = 1, KF_PAIR = 2, KF_PAIR3 = 3 };
 
 // Prepared-filter buffer: header at offset 0, per-channel fp32 scales at
 // scale_off, bins at bins_off.  Bin element: float2 (fp32 storage) or
@@ -51,15 +51,34 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // it: 16-byte chunk q = (mt2 * 4 + nt) * 64 + lane, lane = 16 g + c, holds
 // re[0..3] then im[0..3] (fp16) of bins f = 16 nt + c + 64 (16 mt2 + 4 g + i).
 inline bool use_pair_kernel(int logn, int st) { return logn == 10 && st != ST_F32; }
+// The three-stage matrix-core kernel handles N = 16384 in fp16/bf16 storage.
+// Its filter layout (KF_PAIR3) stores the rows f_c = f mod 32 in [0, 16] of
+// the 2N-bin spectrum; chunk ((f_c * 2 + mt2) * 2 + nt) * 64 + lane holds
+// re[0..3], im[0..3] of bins f = f_c + 32 (16 nt + c) + 1024 (16 mt2 + 4 g + i).
+inline bool use_pair3_kernel(int logn, int st) { return logn == 14 && st != ST_F32; }
 inline int64_t kf_slots(int logn, int st) {
-    return use_pair_kernel(logn, st) ? (int64_t(2) << logn) : (int64_t(1) << logn);
+    if (use_pair_kernel(logn, st)) return int64_t(2) << logn;
+    if (use_pair3_kernel(logn, st)) return int64_t(17) * 1024;
+    return int64_t(1) << logn;
 }
 // log2 of the normalisation folded into scale[h]: 4N for the half-length
-// real transform (fused, multi-pass), 2N for the pair kernel.
-inline int kf_norm_log2(int logn, int st) { return use_pair_kernel(logn, st) ? logn + 1 : logn + 2; }
+// real transform (fused, multi-pass), 2N for the pair kernels.
+inline int kf_norm_log2(int logn, int st) {
+    return (use_pair_kernel(logn, st) || use_pair3_kernel(logn, st)) ? logn + 1 : logn + 2;
+}
 // Bound on the stored bins |K| * s_h: 2^14 for the layouts the VALU kernels
-// rescale in fp32, 1 for the pair layout whose product is taken in fp16.
-inline int kf_target_log2(int logn, int st) { return use_pair_kernel(logn, st) ? 0 : 14; }
+// rescale in fp32, 1 for the pair layouts whose product is taken in fp16.
+inline int kf_target_log2(int logn, int st) {
+    return (use_pair_kernel(logn, st) || use_pair3_kernel(logn, st)) ? 0 : 14;
+}
+// fp16 element offset of the real part of bin f in the KF_PAIR3 layout, or -1
+// when the bin's row is not stored (f mod 32 > 16: read the mirror 2N - f).
+__host__ __device__ inline int64_t pair3_kf_index(int64_t f) {
+    const int64_t fc = f & 31, fb = (f >> 5) & 31, fa = f >> 10;
+    if (fc > 16) return -1;
+    const int64_t mt2 = fa >> 4, g = (fa & 15) >> 2, i = fa & 3, nt = fb >> 4, c = fb & 15;
+    return ((((fc * 2 + mt2) * 2 + nt) * 64 + g * 16 + c) * 8) + i;
+}
 // fp16 element offset of the real part of bin f in the pair layout (imag at +4)
 __host__ __device__ inline int64_t pair_kf_index(int64_t f) {
     const int64_t fs = f % 64, ff = f / 64;
@@ -114,6 +133,19 @@ struct PairTables {
     const void *tw3;         // inverse twiddles, [4 nt][2 nt2][64]: cos[4], sin[4] fp16
 };
 hipError_t get_pair_tables(PairTables *out);
+
+// Lane-order constant tables of the three-stage kernel (see pair16k.hip).
+struct Pair3Tables {
+    const void *fr, *fi;     // DFT-32 operand tiles, [2][64 lanes][8] fp16
+    const void *tw1;         // inner twiddles w1024^{n_a f_b}, [mt][nt][lane]: cos[4], sin[4]
+    const void *tw3;         // inner conj twiddles, [nt][nt2][lane]
+    const void *two1;        // outer twiddles wM^{f_c n_ab}, [64 T][2 nt][lane]
+    const void *two2;        // outer conj twiddles, [32 f_c][2 nt3][2 nt2][lane]
+};
+hipError_t get_pair3_tables(Pair3Tables *out);
+hipError_t launch_pair16k_conv(int st, const void *u, const void *w, const void *v, void *out,
+                               const void *kbins, const float *kscale, const uint8_t *mask,
+                               int64_t B, int64_t H, hipStream_t stream);
 hipError_t launch_pair_conv(int logn, int st, const void *u, const void *w, const void *v,
                             void *out, const void *kbins, const float *kscale, const uint8_t *mask,
                             int64_t B, int64_t H, hipStream_t stream);

@@ -227,7 +227,7 @@ fused_conv_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__r
 // partial filter only the loads holding taps are issued), then the real
 // spectrum X[f], f in [0, N], scaled by s_h, stored in natural order with
 // slot 0 = (X[0], X[N]).
-template <int LOGN, typename T, typename TK, bool PAIR>
+template <int LOGN, typename T, typename TK, int LAYOUT>
 __global__ void __launch_bounds__(FusedPlan<LOGN>::THREADS)
 fused_prepare_kernel(const T *__restrict__ k, int64_t L, TK *__restrict__ kbins,
                      const float *__restrict__ kscale, const float2 *__restrict__ tw,
@@ -279,23 +279,32 @@ fused_prepare_kernel(const T *__restrict__ k, int64_t L, TK *__restrict__ kbins,
     dft_inplace<R>(Bv);
     if (!valid) return;
 
+    constexpr bool PAIR = LAYOUT != KF_NATURAL;
     // s_h = 1 / (scale[h] * norm), exact (both powers of two)
     const float sh = 1.0f / (kscale[h] * (float)(PAIR ? 2 * NC : 4 * NC));
-    TK *krow = kbins + h * (int64_t)(PAIR ? 2 * NC : NC);
-    // one real-spectrum bin: natural order, or the pair kernel's lane order
-    // (with the Hermitian mirror 2N - f stored as well)
+    constexpr int64_t kRowSlots = LAYOUT == KF_PAIR3 ? 17 * 1024 : (PAIR ? 2 * NC : NC);
+    TK *krow = kbins + h * kRowSlots;
+    // one real-spectrum bin: natural order, or a matrix-core kernel's lane
+    // order (the Hermitian mirror 2N - f is stored as well where its row is)
+    auto index_of = [](int64_t f) -> int64_t {
+        return LAYOUT == KF_PAIR3 ? pair3_kf_index(f) : pair_kf_index(f);
+    };
     auto put = [&](int f, float2 x) {
         if (!PAIR) {
             kio<TK>::store(krow + f, x);
         } else {
             _Float16 *kh = reinterpret_cast<_Float16 *>(krow);
-            const int64_t a = pair_kf_index(f);
-            kh[a] = (_Float16)x.x;
-            kh[a + 4] = (_Float16)x.y;
+            const int64_t a = index_of(f);
+            if (a >= 0) {
+                kh[a] = (_Float16)x.x;
+                kh[a + 4] = (_Float16)x.y;
+            }
             if (f != 0 && f != NC) {
-                const int64_t b = pair_kf_index(2 * NC - f);
-                kh[b] = (_Float16)x.x;
-                kh[b + 4] = (_Float16)(-x.y);
+                const int64_t b = index_of(2 * NC - f);
+                if (b >= 0) {
+                    kh[b] = (_Float16)x.x;
+                    kh[b + 4] = (_Float16)(-x.y);
+                }
             }
         }
     };
@@ -354,9 +363,10 @@ static hipError_t launch_prep_t(const void *k, int64_t L, void *kbins, const flo
     using Pl = FusedPlan<LOGN>;
     const int64_t blocks = (H + Pl::SPW - 1) / Pl::SPW;
     const size_t lds = (size_t)Pl::SPW * Pl::NC * sizeof(float2);
-    constexpr bool kPair = LOGN == 10 && !std::is_same<T, float>::value;
-    static_assert(!kPair || std::is_same<TK, __half2>::value, "pair layout stores fp16 bins");
-    auto kern = fused_prepare_kernel<LOGN, T, TK, kPair>;
+    constexpr bool kHalf = !std::is_same<T, float>::value;
+    constexpr int kLayout = (LOGN == 10 && kHalf) ? KF_PAIR : ((LOGN == 14 && kHalf) ? KF_PAIR3 : KF_NATURAL);
+    static_assert(kLayout == KF_NATURAL || std::is_same<TK, __half2>::value, "pair layouts store fp16 bins");
+    auto kern = fused_prepare_kernel<LOGN, T, TK, kLayout>;
     hipError_t e = hipFuncSetAttribute((const void *)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;

@@ -1,0 +1,410 @@
+// pair16k.hip -- gated causal FFT convolution for N = 16384 on the MFMA
+// matrix cores (fp16 operands, fp32 accumulation), one sequence pair per
+// workgroup with the whole 32768-point transform on chip.
+//
+// FlashFFTConv summary page, "Approach": order-p Monarch decomposition of the
+// FFT into matrix-matrix products, permutations as on-chip transposes, the
+// whole convolution fused.  Here the order is 3:
+//
+//   two same-channel sequences form z = x_a + i x_b (x = u * w), zero-padded
+//   to M = 32768 = 32 * 32 * 32,  m = n_a + 32 n_b + 1024 n_c,
+//   f = f_c + 32 f_b + 1024 f_a:
+//
+//   Z[f] = sum_{n_a} w32^{n_a f_a} w1024^{n_a f_b} sum_{n_b} w32^{n_b f_b}
+//            [ wM^{(n_a + 32 n_b) f_c} sum_{n_c} w32^{n_c f_c} z[m] ]
+//
+//  phase 1  outer DFT-32 over n_c (only n_c < 16 is non-zero) for all
+//           n_ab = n_a + 32 n_b, twiddle wM^{n_ab f_c}, into LDS rows f_c;
+//  phase 2  per row f_c (each wave owns rows wave + 8 r): the 1024-point
+//           two-stage chain of the N = 1024 kernel (contract n_b, twiddle,
+//           contract n_a), the filter product, the inverse chain, the
+//           conjugate outer twiddle, into LDS laid out by n_ab;
+//  phase 3  outer inverse DFT-32 over f_c producing only n_c < 16 (outputs
+//           t < N), output scale and gate, store.
+//
+// All six stages are complex-as-real v_mfma_f32_16x16x32_f16 products with
+// one shared set of DFT-32 operand tiles (conjugated for the inverse).  The
+// filter spectrum is stored for rows f_c = 0..16 only; a row f_c > 16 reads
+// the Hermitian mirror row 32 - f_c (lane 63 - l, tiles flipped, elements
+// reversed, conjugated).
+#include "fft_device.hpp"
+#include "fftconv_internal.hpp"
+
+#include <type_traits>
+
+namespace fftconv {
+
+namespace p16 {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ h8 neg8(const h8 &a) {
+    uint4 q = *reinterpret_cast<const uint4 *>(&a);
+    q.x ^= 0x80008000u;
+    q.y ^= 0x80008000u;
+    q.z ^= 0x80008000u;
+    q.w ^= 0x80008000u;
+    return *reinterpret_cast<const h8 *>(&q);
+}
+__device__ __forceinline__ h4 to_h4(const f4 &a) {
+    h4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = (_Float16)a[i];
+    return r;
+}
+__device__ __forceinline__ h8 cat8(const h4 &lo, const h4 &hi) {
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ h4 lo4(const h8 &a) { return __builtin_shufflevector(a, a, 0, 1, 2, 3); }
+__device__ __forceinline__ h4 hi4(const h8 &a) { return __builtin_shufflevector(a, a, 4, 5, 6, 7); }
+// (re, im) <- (re, im) * (c + i s); t = {c[0..3], s[0..3]}
+__device__ __forceinline__ void cmul4(h4 &re, h4 &im, const h8 &t) {
+    const h4 c = lo4(t), s = hi4(t);
+    const h4 r = re * c - im * s;
+    im = re * s + im * c;
+    re = r;
+}
+// complex 16x16x32 tile products, (re, im) planes; "data A": C = D F, "const A": C = F D
+__device__ __forceinline__ void cm_dataA(const h8 &dr, const h8 &di, const h8 &ndi, const h8 &fr,
+                                         const h8 &fi, f4 &cr, f4 &ci) {
+    const f4 z = {0.f, 0.f, 0.f, 0.f};
+    cr = mfma(ndi, fi, mfma(dr, fr, z));
+    ci = mfma(di, fr, mfma(dr, fi, z));
+}
+__device__ __forceinline__ void cm_constA(const h8 &fr, const h8 &fi, const h8 &dr, const h8 &di,
+                                          const h8 &ndi, f4 &cr, f4 &ci) {
+    const f4 z = {0.f, 0.f, 0.f, 0.f};
+    cr = mfma(fi, ndi, mfma(fr, dr, z));
+    ci = mfma(fi, dr, mfma(fr, di, z));
+}
+
+// K slot (0..31) of row r (0..31) in a chained operand: rows 4g + j of tile 0
+// -> slot 8g + j, rows 16 + 4g + j -> slot 8g + 4 + j
+__device__ __forceinline__ int kslot(int r) {
+    return 8 * ((r & 15) >> 2) + 4 * (r >> 4) + (r & 3);
+}
+
+// LDS layouts (fp16 element offsets within one plane)
+constexpr int kR1Row = 1032;                 // 1024 + 8: rows f_c padded against bank conflicts
+constexpr int kR1Plane = 32 * kR1Row;        // [f_c][chunk 4][n_a 32][8]
+constexpr int kR2Plane = 32768;              // [chunk 4][n_ab 1024][8]
+__device__ __forceinline__ int r1(int fc, int ks, int na) {
+    return fc * kR1Row + (ks >> 3) * 256 + na * 8 + (ks & 7);
+}
+__device__ __forceinline__ int r2(int ks, int nab) { return (ks >> 3) * 8192 + nab * 8 + (ks & 7); }
+
+template <typename T> struct st;
+template <> struct st<__half> {
+    static __device__ __forceinline__ float ld(const __half *p) { return (float)*reinterpret_cast<const _Float16 *>(p); }
+    static __device__ __forceinline__ void ld4(const __half *p, float *o) {
+        const uint2 raw = *reinterpret_cast<const uint2 *>(p);
+        const _Float16 *hv = reinterpret_cast<const _Float16 *>(&raw);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = (float)hv[i];
+    }
+    static __device__ __forceinline__ void st4(__half *p, const float *v) {
+        _Float16 hv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hv[i] = (_Float16)v[i];
+        *reinterpret_cast<uint2 *>(p) = *reinterpret_cast<const uint2 *>(hv);
+    }
+};
+template <> struct st<__hip_bfloat16> {
+    static __device__ __forceinline__ float ld(const __hip_bfloat16 *p) {
+        return __uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t *>(p)) << 16);
+    }
+    static __device__ __forceinline__ void ld4(const __hip_bfloat16 *p, float *o) {
+        const uint2 raw = *reinterpret_cast<const uint2 *>(p);
+        o[0] = __uint_as_float(raw.x << 16);
+        o[1] = __uint_as_float(raw.x & 0xffff0000u);
+        o[2] = __uint_as_float(raw.y << 16);
+        o[3] = __uint_as_float(raw.y & 0xffff0000u);
+    }
+    static __device__ __forceinline__ void st4(__hip_bfloat16 *p, const float *v) {
+        uint32_t w[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            __hip_bfloat16 a = __float2bfloat16(v[2 * i]), b = __float2bfloat16(v[2 * i + 1]);
+            w[i] = (uint32_t)(*reinterpret_cast<uint16_t *>(&a)) |
+                   ((uint32_t)(*reinterpret_cast<uint16_t *>(&b)) << 16);
+        }
+        *reinterpret_cast<uint2 *>(p) = make_uint2(w[0], w[1]);
+    }
+};
+
+constexpr int kWaves = 8;
+
+}  // namespace p16
+
+using namespace p16;
+
+// grid: persistent, one workgroup (8 waves) per CU; each workgroup walks an
+// XCD-local range of pairs p = h * ceil(B/2) + bp.
+template <typename T, bool MASKED>
+__global__ void __launch_bounds__(64 * kWaves, 1)
+pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restrict__ v,
+               T *__restrict__ out, const uint4 *__restrict__ kbins, const float *__restrict__ kscale,
+               const uint8_t *__restrict__ mask, Pair3Tables tb, int64_t B, int64_t H) {
+    constexpr int N = 16384;
+    constexpr int M2 = 2 * N;
+    extern __shared__ __align__(16) _Float16 smem[];
+    _Float16 *P0 = smem;                    // plane 0 (re) of R1 / R2
+    _Float16 *P1 = smem + kR1Plane;         // plane 1 (im)
+    h8 *s_tw1 = reinterpret_cast<h8 *>(smem + 2 * kR1Plane);   // [mt][nt][lane]
+    h8 *s_tw3 = s_tw1 + 4 * 64;                                 // [nt][nt2][lane]
+
+    const int tid = threadIdx.x;
+    for (int i = tid; i < 256; i += 64 * kWaves) {
+        s_tw1[i] = reinterpret_cast<const h8 *>(tb.tw1)[i];
+        s_tw3[i] = reinterpret_cast<const h8 *>(tb.tw3)[i];
+    }
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, c = lane & 15;
+    h8 Fr[2], Fi[2], nFi[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        Fr[t] = reinterpret_cast<const h8 *>(tb.fr)[t * 64 + lane];
+        Fi[t] = reinterpret_cast<const h8 *>(tb.fi)[t * 64 + lane];
+        nFi[t] = neg8(Fi[t]);
+    }
+    const h8 *twO1 = reinterpret_cast<const h8 *>(tb.two1);   // [T][nt][lane]
+    const h8 *twO2 = reinterpret_cast<const h8 *>(tb.two2);   // [fc][nt3][nt2][lane]
+    __syncthreads();
+
+    const int64_t PB = (B + 1) / 2, P = H * PB;
+    const uint32_t nwg = gridDim.x, xcd = blockIdx.x % 8, wg_local = blockIdx.x / 8;
+    const uint32_t wg_on_xcd = nwg / 8 + (xcd < nwg % 8 ? 1u : 0u);
+    const int64_t p_begin = P * xcd / 8, p_end = P * (xcd + 1) / 8;
+
+    for (int64_t p = p_begin + wg_local; p < p_end; p += wg_on_xcd) {
+        const int64_t h = p / PB, bp = p - h * PB;
+        const bool has_b = 2 * bp + 1 < B;
+        const int64_t oa = (2 * bp * H + h) * N, ob = has_b ? oa + H * N : oa;
+        const float ks = kscale[h];
+
+        // ---- phase 1: outer DFT over n_c for tiles T of n_ab (this wave: T = 8 wave .. 8 wave + 7)
+#pragma unroll 1
+        for (int tt = 0; tt < 8; ++tt) {
+            const int T_ = wave * 8 + tt;
+            h8 br, bi;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                br[j] = (_Float16)0.f;
+                bi[j] = (_Float16)0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t m = 16 * T_ + c + 1024 * (4 * g + j);
+                float xa = st<T>::ld(u + oa + m), xb = has_b ? st<T>::ld(u + ob + m) : 0.f;
+                if (w != nullptr) {
+                    xa *= st<T>::ld(w + oa + m);
+                    xb *= has_b ? st<T>::ld(w + ob + m) : 0.f;
+                }
+                br[j] = (_Float16)xa;
+                bi[j] = (_Float16)xb;
+            }
+            const h8 nbi = neg8(bi);
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                f4 ar, ai;
+                cm_constA(Fr[nt], Fi[nt], br, bi, nbi, ar, ai);   // rows f_c = 16nt + 4g + i, cols n_ab
+                h4 yr = to_h4(ar), yi = to_h4(ai);
+                cmul4(yr, yi, twO1[(T_ * 2 + nt) * 64 + lane]);
+                const int nab = 16 * T_ + c, na = nab & 31, kb = kslot(nab >> 5);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int fc = 16 * nt + 4 * g + i;
+                    P0[r1(fc, kb, na)] = yr[i];
+                    P1[r1(fc, kb, na)] = yi[i];
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- phase 2a: this wave's rows f_c = wave + 8 r into registers (S1 operands)
+        h8 ar_[4][2], ai_[4][2];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int fc = wave + 8 * r;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                ar_[r][mt] = *reinterpret_cast<const h8 *>(P0 + r1(fc, 8 * g, 16 * mt + c));
+                ai_[r][mt] = *reinterpret_cast<const h8 *>(P1 + r1(fc, 8 * g, 16 * mt + c));
+            }
+        }
+        __syncthreads();
+
+        // ---- phase 2b: the 1024-point chain per row, filter product, inverse chain
+#pragma unroll 1
+        for (int r = 0; r < 4; ++r) {
+            const int fc = wave + 8 * r;
+            // filter chunks for (mt2, nt): rows f_c <= 16 stored, others from the mirror row
+            h8 kk[2][2];
+            const uint4 *kch = kbins + h * (int64_t)(17 * 256);
+#pragma unroll
+            for (int mt2 = 0; mt2 < 2; ++mt2)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    if (fc <= 16) {
+                        const uint4 q = kch[((fc * 2 + mt2) * 2 + nt) * 64 + lane];
+                        kk[mt2][nt] = *reinterpret_cast<const h8 *>(&q);
+                    } else {
+                        const uint4 q = kch[(((32 - fc) * 2 + (1 - mt2)) * 2 + (1 - nt)) * 64 + (63 - lane)];
+                        const h8 m8 = *reinterpret_cast<const h8 *>(&q);
+                        h8 t8;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            t8[i] = m8[3 - i];
+                            t8[4 + i] = -m8[7 - i];
+                        }
+                        kk[mt2][nt] = t8;
+                    }
+                }
+            // S1: data A (M = n_a tiles mt, K = n_b), const B F[nt] (N = f_b); twiddle w1024^{n_a f_b}
+            h4 t1r[2][2], t1i[2][2];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const h8 nai = neg8(ai_[r][mt]);
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    f4 cr, ci;
+                    cm_dataA(ar_[r][mt], ai_[r][mt], nai, Fr[nt], Fi[nt], cr, ci);
+                    t1r[mt][nt] = to_h4(cr);
+                    t1i[mt][nt] = to_h4(ci);
+                    cmul4(t1r[mt][nt], t1i[mt][nt], s_tw1[(mt * 2 + nt) * 64 + lane]);
+                }
+            }
+            // S2: const A F[mt2] (M = f_a, K = n_a), data B = T1 (K = n_a, N = f_b); filter product
+            h4 yr[2][2], yi[2][2];
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const h8 br = cat8(t1r[0][nt], t1r[1][nt]), bi = cat8(t1i[0][nt], t1i[1][nt]);
+                const h8 nbi = neg8(bi);
+#pragma unroll
+                for (int mt2 = 0; mt2 < 2; ++mt2) {
+                    f4 cr, ci;
+                    cm_constA(Fr[mt2], Fi[mt2], br, bi, nbi, cr, ci);   // rows f_a, cols f_b
+                    yr[mt2][nt] = to_h4(cr);
+                    yi[mt2][nt] = to_h4(ci);
+                    h8 kq = kk[mt2][nt];
+                    if (MASKED) {
+                        const uint8_t *mrow = mask + h * kMaskBlocks;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int f = fc + 32 * (16 * nt + c) + 1024 * (16 * mt2 + 4 * g + i);
+                            const int fr_ = f <= N ? f : M2 - f;
+                            int blk = fr_ / (N / kMaskBlocks);
+                            blk = blk > kMaskBlocks - 1 ? kMaskBlocks - 1 : blk;
+                            if (!mrow[blk]) kq[i] = kq[4 + i] = (_Float16)0.f;
+                        }
+                    }
+                    cmul4(yr[mt2][nt], yi[mt2][nt], kq);
+                }
+            }
+            // S2': data A = T2^T (M = f_b tiles nt, K = f_a), const B conj F[nt2] (N = n_a); conj twiddle
+            h4 t3r[2][2], t3i[2][2];
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const h8 dr = cat8(yr[0][nt], yr[1][nt]), di = cat8(yi[0][nt], yi[1][nt]);
+                const h8 ndi = neg8(di);
+#pragma unroll
+                for (int nt2 = 0; nt2 < 2; ++nt2) {
+                    f4 cr, ci;
+                    cm_dataA(dr, di, ndi, Fr[nt2], nFi[nt2], cr, ci);   // rows f_b, cols n_a
+                    t3r[nt][nt2] = to_h4(cr);
+                    t3i[nt][nt2] = to_h4(ci);
+                    cmul4(t3r[nt][nt2], t3i[nt][nt2], s_tw3[(nt * 2 + nt2) * 64 + lane]);
+                }
+            }
+            // S1': const A conj F[nt3] (M = n_b, K = f_b), data B = T3 (K = f_b, N = n_a);
+            // conj outer twiddle; into R2 at [kslot(f_c)][n_ab]
+            const int kfc = kslot(fc);
+#pragma unroll
+            for (int nt2 = 0; nt2 < 2; ++nt2) {
+                const h8 br = cat8(t3r[0][nt2], t3r[1][nt2]), bi = cat8(t3i[0][nt2], t3i[1][nt2]);
+                const h8 nbi = neg8(bi);
+#pragma unroll
+                for (int nt3 = 0; nt3 < 2; ++nt3) {
+                    f4 cr, ci;
+                    cm_constA(Fr[nt3], nFi[nt3], br, bi, nbi, cr, ci);   // rows n_b, cols n_a
+                    h4 qr = to_h4(cr), qi = to_h4(ci);
+                    cmul4(qr, qi, twO2[((fc * 2 + nt3) * 2 + nt2) * 64 + lane]);
+                    const int na = 16 * nt2 + c;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int nab = na + 32 * (16 * nt3 + 4 * g + i);
+                        P0[r2(kfc, nab)] = qr[i];
+                        P1[r2(kfc, nab)] = qi[i];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- phase 3: outer inverse over f_c (outputs n_c < 16 only), scale, gate, store
+#pragma unroll 1
+        for (int tt = 0; tt < 8; ++tt) {
+            const int T_ = wave * 8 + tt;
+            const h8 dr = *reinterpret_cast<const h8 *>(P0 + r2(8 * g, 16 * T_ + c));
+            const h8 di = *reinterpret_cast<const h8 *>(P1 + r2(8 * g, 16 * T_ + c));
+            f4 cr, ci;
+            cm_dataA(dr, di, neg8(di), Fr[0], nFi[0], cr, ci);   // rows n_ab = 16T + 4g + i, col n_c = c
+            const int64_t m = 16 * T_ + 4 * g + 1024 * c;
+            float ya[4] = {cr[0] * ks, cr[1] * ks, cr[2] * ks, cr[3] * ks};
+            float yb[4] = {ci[0] * ks, ci[1] * ks, ci[2] * ks, ci[3] * ks};
+            if (v != nullptr) {
+                float g4[4];
+                st<T>::ld4(v + oa + m, g4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ya[i] *= g4[i];
+                if (has_b) {
+                    st<T>::ld4(v + ob + m, g4);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) yb[i] *= g4[i];
+                }
+            }
+            st<T>::st4(out + oa + m, ya);
+            if (has_b) st<T>::st4(out + ob + m, yb);
+        }
+        __syncthreads();
+    }
+}
+
+hipError_t launch_pair16k_conv(int st_, const void *u, const void *w, const void *v, void *out,
+                               const void *kbins, const float *kscale, const uint8_t *mask,
+                               int64_t B, int64_t H, hipStream_t stream) {
+    Pair3Tables tb{};
+    hipError_t e = get_pair3_tables(&tb);
+    if (e != hipSuccess) return e;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+            cus = n;
+    }
+    const int64_t pairs = H * ((B + 1) / 2);
+    int64_t blocks = cus;
+    if (blocks > pairs) blocks = pairs < 8 ? 8 : pairs;
+    const size_t lds = (size_t)2 * kR1Plane * sizeof(_Float16) + 2 * 256 * 16;
+    auto go = [&](auto kern, auto *tp) -> hipError_t {
+        using TT = std::remove_pointer_t<decltype(tp)>;
+        hipError_t err = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)lds);
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * kWaves), lds, stream, (const TT *)u,
+                           (const TT *)w, (const TT *)v, (TT *)out, (const uint4 *)kbins, kscale, mask, tb,
+                           B, H);
+        return hipGetLastError();
+    };
+    if (st_ == ST_F16)
+        return mask ? go(pair16k_kernel<__half, true>, (__half *)nullptr)
+                    : go(pair16k_kernel<__half, false>, (__half *)nullptr);
+    return mask ? go(pair16k_kernel<__hip_bfloat16, true>, (__hip_bfloat16 *)nullptr)
+                : go(pair16k_kernel<__hip_bfloat16, false>, (__hip_bfloat16 *)nullptr);
+}
+
+}  // namespace fftconv

@@ -191,3 +191,28 @@ def test_pair_layout_spectrum(dtype):
         x[:L] = k64[h]
         want = oracle.fft(x)[:N + 1]
         assert np.linalg.norm(got[h] - want) / np.linalg.norm(want) < 2e-3
+
+
+# ---- N = 16384 in fp16 / bf16 storage runs on the three-stage matrix-core kernel
+@pytest.mark.parametrize("gates,dtype,L", [("both", "bf16", 16384), ("none", "f16", 5000),
+                                           ("w", "f16", 16384), ("v", "bf16", 1)])
+def test_pair16k_gates_and_partial(gates, dtype, L):
+    _say(f"pair16k gates={gates} {dtype} L={L}")
+    inp = synth.generate(3, 2, 16384, L, dtype, gated=True, seed=41)
+    if gates in ("none", "v"):
+        inp.w = None
+    if gates in ("none", "w"):
+        inp.v = None
+    y = run_gpu(inp)
+    ref = oracle.fft_conv(inp.f64("u"), inp.f64("k"), inp.f64("w"), inp.f64("v"))
+    assert oracle.rel_l2(y, ref) < TOL[dtype]
+
+
+@pytest.mark.parametrize("kind", ["band", "random"])
+def test_pair16k_mask(kind):
+    _say(f"pair16k mask {kind}")
+    inp = synth.generate(2, 3, 16384, 16384, "f16", gated=True, seed=42)
+    mask = synth.band_mask(3, 27) if kind == "band" else synth.random_mask(3, seed=7)
+    y = run_gpu(inp, mask)
+    ref = oracle_full(inp, mask)
+    assert oracle.rel_l2(y, ref) < TOL["f16"]
