@@ -83,6 +83,20 @@ __device__ __forceinline__ void cm_constA(const h8 &fr, const h8 &fi, const h8 &
     ci = mfma(fi, dr, mfma(fr, di, z));
 }
 
+// the same with conj(F): the negated data plane is the real one
+__device__ __forceinline__ void cm_dataA_conj(const h8 &dr, const h8 &di, const h8 &ndr, const h8 &fr,
+                                              const h8 &fi, f4 &cr, f4 &ci) {
+    const f4 z = {0.f, 0.f, 0.f, 0.f};
+    cr = mfma(di, fi, mfma(dr, fr, z));
+    ci = mfma(ndr, fi, mfma(di, fr, z));
+}
+__device__ __forceinline__ void cm_constA_conj(const h8 &fr, const h8 &fi, const h8 &dr, const h8 &di,
+                                               const h8 &ndr, f4 &cr, f4 &ci) {
+    const f4 z = {0.f, 0.f, 0.f, 0.f};
+    cr = mfma(fi, di, mfma(fr, dr, z));
+    ci = mfma(fi, ndr, mfma(fr, di, z));
+}
+
 // K slot (0..31) of row r (0..31) in a chained operand: rows 4g + j of tile 0
 // -> slot 8g + j, rows 16 + 4g + j -> slot 8g + 4 + j
 __device__ __forceinline__ int kslot(int r) {
@@ -101,8 +115,7 @@ __device__ __forceinline__ int r2(int ks, int nab) { return (ks >> 3) * 8192 + n
 template <typename T> struct st;
 template <> struct st<__half> {
     static __device__ __forceinline__ float ld(const __half *p) { return (float)*reinterpret_cast<const _Float16 *>(p); }
-    static __device__ __forceinline__ void ld4(const __half *p, float *o) {
-        const uint2 raw = *reinterpret_cast<const uint2 *>(p);
+    static __device__ __forceinline__ void unpack4(const uint2 &raw, float *o) {
         const _Float16 *hv = reinterpret_cast<const _Float16 *>(&raw);
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = (float)hv[i];
@@ -118,8 +131,7 @@ template <> struct st<__hip_bfloat16> {
     static __device__ __forceinline__ float ld(const __hip_bfloat16 *p) {
         return __uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t *>(p)) << 16);
     }
-    static __device__ __forceinline__ void ld4(const __hip_bfloat16 *p, float *o) {
-        const uint2 raw = *reinterpret_cast<const uint2 *>(p);
+    static __device__ __forceinline__ void unpack4(const uint2 &raw, float *o) {
         o[0] = __uint_as_float(raw.x << 16);
         o[1] = __uint_as_float(raw.x & 0xffff0000u);
         o[2] = __uint_as_float(raw.y << 16);
@@ -138,14 +150,37 @@ template <> struct st<__hip_bfloat16> {
 };
 
 constexpr int kWaves = 8;
+constexpr int kTilesPerWave = 64 / kWaves;   // 16-column tiles of n_ab in phases 1 and 3
+constexpr int kRowsPerWave = 32 / kWaves;    // rows f_c in phase 2
+static_assert(kWaves == 8, "the LDS address split below assumes 8 waves");
+
+// filter chunk of row fc for (mt2, nt): rows f_c <= 16 as stored, the others from
+// the mirror row 32 - f_c (lane 63 - l, tiles flipped, elements reversed, conjugated)
+__device__ __forceinline__ uint4 k_load(const uint4 *kch, int fc, int mt2, int nt, int lane) {
+    const bool mir = fc > 16;
+    const int row = mir ? 32 - fc : fc, a = mir ? 1 - mt2 : mt2, b = mir ? 1 - nt : nt;
+    return kch[((row * 2 + a) * 2 + b) * 64 + (mir ? 63 - lane : lane)];
+}
+__device__ __forceinline__ h8 k_fix(const uint4 &q, bool mir) {
+    if (!mir) return *reinterpret_cast<const h8 *>(&q);
+    // (e0..e3 | e4..e7) -> (e3, e2, e1, e0 | -e7, -e6, -e5, -e4)
+    uint4 t;
+    t.x = __builtin_amdgcn_alignbit(q.y, q.y, 16);
+    t.y = __builtin_amdgcn_alignbit(q.x, q.x, 16);
+    t.z = __builtin_amdgcn_alignbit(q.w, q.w, 16) ^ 0x80008000u;
+    t.w = __builtin_amdgcn_alignbit(q.z, q.z, 16) ^ 0x80008000u;
+    return *reinterpret_cast<const h8 *>(&t);
+}
 
 }  // namespace p16
 
 using namespace p16;
 
-// grid: persistent, one workgroup (8 waves) per CU; each workgroup walks an
-// XCD-local range of pairs p = h * ceil(B/2) + bp.
-template <typename T, bool MASKED>
+// grid: persistent, one workgroup (kWaves waves) per CU; each workgroup walks an
+// XCD-local range of pairs p = h * ceil(B/2) + bp.  An odd B pairs its last row
+// with zeros: the second row's loads then re-read the first row (always in
+// bounds) and are discarded, so no load sits under a branch.
+template <typename T, bool MASKED, bool HAS_W, bool HAS_V>
 __global__ void __launch_bounds__(64 * kWaves, 1)
 pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restrict__ v,
                T *__restrict__ out, const uint4 *__restrict__ kbins, const float *__restrict__ kscale,
@@ -164,15 +199,25 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
         s_tw3[i] = reinterpret_cast<const h8 *>(tb.tw3)[i];
     }
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, c = lane & 15;
-    h8 Fr[2], Fi[2], nFi[2];
+    h8 Fr[2], Fi[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         Fr[t] = reinterpret_cast<const h8 *>(tb.fr)[t * 64 + lane];
         Fi[t] = reinterpret_cast<const h8 *>(tb.fi)[t * 64 + lane];
-        nFi[t] = neg8(Fi[t]);
     }
-    const h8 *twO1 = reinterpret_cast<const h8 *>(tb.two1);   // [T][nt][lane]
-    const h8 *twO2 = reinterpret_cast<const h8 *>(tb.two2);   // [fc][nt3][nt2][lane]
+    // outer twiddles of this wave's tiles [tq][nt][lane] and rows [r][nt3][nt2][lane]
+    const h8 *twO1 = reinterpret_cast<const h8 *>(tb.two1) + wave * (kTilesPerWave * 2 * 64);
+    const h8 *twO2 = reinterpret_cast<const h8 *>(tb.two2) + wave * (4 * 64);
+    // Every LDS access below is a per-lane base plus a compile-time offset: r1() / r2()
+    // split into lane, wave and constant parts (phase 1 writes, 2a reads, 2b writes, 3 reads).
+    const int b1w = 4 * g * kR1Row + 8 * c + 256 * (wave & 3) + 4 * (wave >> 2);
+    const int b2r = kR1Row * wave + 256 * g + 8 * c;
+    const int b2w = 8192 * (wave >> 2) + (wave & 3) + 8 * c + 1024 * g;
+    const int b3r = 1024 * wave + 8192 * g + 8 * c;
+    _Float16 *const w1r = P0 + b1w, *const w1i = P1 + b1w;
+    const _Float16 *const r2r = P0 + b2r, *const r2i = P1 + b2r;
+    _Float16 *const w2r = P0 + b2w, *const w2i = P1 + b2w;
+    const _Float16 *const r3r = P0 + b3r, *const r3i = P1 + b3r;
     __syncthreads();
 
     const int64_t PB = (B + 1) / 2, P = H * PB;
@@ -185,85 +230,106 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
         const bool has_b = 2 * bp + 1 < B;
         const int64_t oa = (2 * bp * H + h) * N, ob = has_b ? oa + H * N : oa;
         const float ks = kscale[h];
+        // per-lane element offset of phase 1 (n_ab = 16 T + c, n_c = 4 g + j) and phase 3
+        const int m1 = 16 * kTilesPerWave * wave + c + 4096 * g;
+        const int m3 = 16 * kTilesPerWave * wave + 4 * g + 1024 * c;
+        const T *ua = u + oa + m1, *ub = u + ob + m1;
+        const T *wa = HAS_W ? w + oa + m1 : nullptr, *wb = HAS_W ? w + ob + m1 : nullptr;
 
-        // ---- phase 1: outer DFT over n_c for tiles T of n_ab (this wave: T = 8 wave .. 8 wave + 7)
-#pragma unroll 1
-        for (int tt = 0; tt < 8; ++tt) {
-            const int T_ = wave * 8 + tt;
-            h8 br, bi;
+        // ---- phase 1: outer DFT over n_c for this wave's tiles T of n_ab, in two
+        // batches whose strided loads are all issued before any is used
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                br[j] = (_Float16)0.f;
-                bi[j] = (_Float16)0.f;
-            }
+        for (int half = 0; half < 2; ++half) {
+            constexpr int TB = kTilesPerWave / 2;
+            float xa[TB][4], xb[TB][4];
+            h8 tw[TB][2];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t m = 16 * T_ + c + 1024 * (4 * g + j);
-                float xa = st<T>::ld(u + oa + m), xb = has_b ? st<T>::ld(u + ob + m) : 0.f;
-                if (w != nullptr) {
-                    xa *= st<T>::ld(w + oa + m);
-                    xb *= has_b ? st<T>::ld(w + ob + m) : 0.f;
+            for (int tq = 0; tq < TB; ++tq) {
+                const int t = half * TB + tq;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int m = 16 * t + 1024 * j;
+                    xa[tq][j] = st<T>::ld(ua + m);
+                    xb[tq][j] = st<T>::ld(ub + m);
+                    if (HAS_W) {
+                        xa[tq][j] *= st<T>::ld(wa + m);
+                        xb[tq][j] *= st<T>::ld(wb + m);
+                    }
                 }
-                br[j] = (_Float16)xa;
-                bi[j] = (_Float16)xb;
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) tw[tq][nt] = twO1[(t * 2 + nt) * 64 + lane];
             }
-            const h8 nbi = neg8(bi);
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                f4 ar, ai;
-                cm_constA(Fr[nt], Fi[nt], br, bi, nbi, ar, ai);   // rows f_c = 16nt + 4g + i, cols n_ab
-                h4 yr = to_h4(ar), yi = to_h4(ai);
-                cmul4(yr, yi, twO1[(T_ * 2 + nt) * 64 + lane]);
-                const int nab = 16 * T_ + c, na = nab & 31, kb = kslot(nab >> 5);
+            for (int tq = 0; tq < TB; ++tq) {
+                const int t = half * TB + tq;
+                h8 br, bi;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int fc = 16 * nt + 4 * g + i;
-                    P0[r1(fc, kb, na)] = yr[i];
-                    P1[r1(fc, kb, na)] = yi[i];
+                for (int j = 0; j < 4; ++j) {
+                    br[j] = (_Float16)xa[tq][j];
+                    bi[j] = has_b ? (_Float16)xb[tq][j] : (_Float16)0.f;
+                    br[4 + j] = (_Float16)0.f;
+                    bi[4 + j] = (_Float16)0.f;
+                }
+                const h8 nbi = neg8(bi);
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    f4 ar, ai;
+                    cm_constA(Fr[nt], Fi[nt], br, bi, nbi, ar, ai);   // rows f_c = 16nt + 4g + i, cols n_ab
+                    h4 yr = to_h4(ar), yi = to_h4(ai);
+                    cmul4(yr, yi, tw[tq][nt]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {   // r1(16 nt + 4 g + i, kslot(n_ab >> 5), n_ab & 31)
+                        const int o = (16 * nt + i) * kR1Row + 128 * (t & 1) + (t >> 1);
+                        w1r[o] = yr[i];
+                        w1i[o] = yi[i];
+                    }
                 }
             }
         }
         __syncthreads();
 
-        // ---- phase 2a: this wave's rows f_c = wave + 8 r into registers (S1 operands)
-        h8 ar_[4][2], ai_[4][2];
+        // ---- phase 2a: this wave's rows f_c = wave + kWaves r into registers (S1 operands);
+        // R2 below reuses the same LDS
+        h8 ar_[kRowsPerWave][2], ai_[kRowsPerWave][2];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int fc = wave + 8 * r;
+        for (int r = 0; r < kRowsPerWave; ++r) {
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                ar_[r][mt] = *reinterpret_cast<const h8 *>(P0 + r1(fc, 8 * g, 16 * mt + c));
-                ai_[r][mt] = *reinterpret_cast<const h8 *>(P1 + r1(fc, 8 * g, 16 * mt + c));
+            for (int mt = 0; mt < 2; ++mt) {   // r1(wave + 8 r, 8 g, 16 mt + c)
+                const int o = kWaves * kR1Row * r + 128 * mt;
+                ar_[r][mt] = *reinterpret_cast<const h8 *>(r2r + o);
+                ai_[r][mt] = *reinterpret_cast<const h8 *>(r2i + o);
             }
         }
+        const uint4 *kch = kbins + h * (int64_t)(17 * 256);
+        uint4 kq[2][2];
+#pragma unroll
+        for (int mt2 = 0; mt2 < 2; ++mt2)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) kq[mt2][nt] = k_load(kch, wave, mt2, nt, lane);
         __syncthreads();
 
-        // ---- phase 2b: the 1024-point chain per row, filter product, inverse chain
-#pragma unroll 1
-        for (int r = 0; r < 4; ++r) {
-            const int fc = wave + 8 * r;
-            // filter chunks for (mt2, nt): rows f_c <= 16 stored, others from the mirror row
+        // ---- phase 2b: the 1024-point chain per row, filter product, inverse chain;
+        // the next row's filter chunks are fetched while this row computes
+#pragma unroll
+        for (int r = 0; r < kRowsPerWave; ++r) {
+            const int fc = wave + kWaves * r;
             h8 kk[2][2];
-            const uint4 *kch = kbins + h * (int64_t)(17 * 256);
 #pragma unroll
             for (int mt2 = 0; mt2 < 2; ++mt2)
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    if (fc <= 16) {
-                        const uint4 q = kch[((fc * 2 + mt2) * 2 + nt) * 64 + lane];
-                        kk[mt2][nt] = *reinterpret_cast<const h8 *>(&q);
-                    } else {
-                        const uint4 q = kch[(((32 - fc) * 2 + (1 - mt2)) * 2 + (1 - nt)) * 64 + (63 - lane)];
-                        const h8 m8 = *reinterpret_cast<const h8 *>(&q);
-                        h8 t8;
+                for (int nt = 0; nt < 2; ++nt) kk[mt2][nt] = k_fix(kq[mt2][nt], fc > 16);
+            if (r + 1 < kRowsPerWave) {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            t8[i] = m8[3 - i];
-                            t8[4 + i] = -m8[7 - i];
-                        }
-                        kk[mt2][nt] = t8;
-                    }
-                }
+                for (int mt2 = 0; mt2 < 2; ++mt2)
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) kq[mt2][nt] = k_load(kch, fc + kWaves, mt2, nt, lane);
+            }
+            h8 two[2][2];
+#pragma unroll
+            for (int nt3 = 0; nt3 < 2; ++nt3)
+#pragma unroll
+                for (int nt2 = 0; nt2 < 2; ++nt2)
+                    two[nt3][nt2] = twO2[((kWaves * r * 2 + nt3) * 2 + nt2) * 64 + lane];
             // S1: data A (M = n_a tiles mt, K = n_b), const B F[nt] (N = f_b); twiddle w1024^{n_a f_b}
             h4 t1r[2][2], t1i[2][2];
 #pragma unroll
@@ -290,7 +356,7 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                     cm_constA(Fr[mt2], Fi[mt2], br, bi, nbi, cr, ci);   // rows f_a, cols f_b
                     yr[mt2][nt] = to_h4(cr);
                     yi[mt2][nt] = to_h4(ci);
-                    h8 kq = kk[mt2][nt];
+                    h8 kf = kk[mt2][nt];
                     if (MASKED) {
                         const uint8_t *mrow = mask + h * kMaskBlocks;
 #pragma unroll
@@ -299,10 +365,10 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                             const int fr_ = f <= N ? f : M2 - f;
                             int blk = fr_ / (N / kMaskBlocks);
                             blk = blk > kMaskBlocks - 1 ? kMaskBlocks - 1 : blk;
-                            if (!mrow[blk]) kq[i] = kq[4 + i] = (_Float16)0.f;
+                            if (!mrow[blk]) kf[i] = kf[4 + i] = (_Float16)0.f;
                         }
                     }
-                    cmul4(yr[mt2][nt], yi[mt2][nt], kq);
+                    cmul4(yr[mt2][nt], yi[mt2][nt], kf);
                 }
             }
             // S2': data A = T2^T (M = f_b tiles nt, K = f_a), const B conj F[nt2] (N = n_a); conj twiddle
@@ -310,11 +376,11 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
                 const h8 dr = cat8(yr[0][nt], yr[1][nt]), di = cat8(yi[0][nt], yi[1][nt]);
-                const h8 ndi = neg8(di);
+                const h8 ndr = neg8(dr);
 #pragma unroll
                 for (int nt2 = 0; nt2 < 2; ++nt2) {
                     f4 cr, ci;
-                    cm_dataA(dr, di, ndi, Fr[nt2], nFi[nt2], cr, ci);   // rows f_b, cols n_a
+                    cm_dataA_conj(dr, di, ndr, Fr[nt2], Fi[nt2], cr, ci);   // rows f_b, cols n_a
                     t3r[nt][nt2] = to_h4(cr);
                     t3i[nt][nt2] = to_h4(ci);
                     cmul4(t3r[nt][nt2], t3i[nt][nt2], s_tw3[(nt * 2 + nt2) * 64 + lane]);
@@ -322,23 +388,21 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
             }
             // S1': const A conj F[nt3] (M = n_b, K = f_b), data B = T3 (K = f_b, N = n_a);
             // conj outer twiddle; into R2 at [kslot(f_c)][n_ab]
-            const int kfc = kslot(fc);
 #pragma unroll
             for (int nt2 = 0; nt2 < 2; ++nt2) {
                 const h8 br = cat8(t3r[0][nt2], t3r[1][nt2]), bi = cat8(t3i[0][nt2], t3i[1][nt2]);
-                const h8 nbi = neg8(bi);
+                const h8 nbr = neg8(br);
 #pragma unroll
                 for (int nt3 = 0; nt3 < 2; ++nt3) {
                     f4 cr, ci;
-                    cm_constA(Fr[nt3], nFi[nt3], br, bi, nbi, cr, ci);   // rows n_b, cols n_a
+                    cm_constA_conj(Fr[nt3], Fi[nt3], br, bi, nbr, cr, ci);   // rows n_b, cols n_a
                     h4 qr = to_h4(cr), qi = to_h4(ci);
-                    cmul4(qr, qi, twO2[((fc * 2 + nt3) * 2 + nt2) * 64 + lane]);
-                    const int na = 16 * nt2 + c;
+                    cmul4(qr, qi, two[nt3][nt2]);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int nab = na + 32 * (16 * nt3 + 4 * g + i);
-                        P0[r2(kfc, nab)] = qr[i];
-                        P1[r2(kfc, nab)] = qi[i];
+                    for (int i = 0; i < 4; ++i) {   // r2(kslot(f_c), 16 nt2 + c + 32 (16 nt3 + 4 g + i))
+                        const int o = 16384 * (r & 1) + 4 * (r >> 1) + 128 * nt2 + 4096 * nt3 + 256 * i;
+                        w2r[o] = qr[i];
+                        w2i[o] = qi[i];
                     }
                 }
             }
@@ -346,25 +410,32 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
         __syncthreads();
 
         // ---- phase 3: outer inverse over f_c (outputs n_c < 16 only), scale, gate, store
-#pragma unroll 1
-        for (int tt = 0; tt < 8; ++tt) {
-            const int T_ = wave * 8 + tt;
-            const h8 dr = *reinterpret_cast<const h8 *>(P0 + r2(8 * g, 16 * T_ + c));
-            const h8 di = *reinterpret_cast<const h8 *>(P1 + r2(8 * g, 16 * T_ + c));
+        uint2 va[kTilesPerWave], vb[kTilesPerWave];
+        if (HAS_V) {
+#pragma unroll
+            for (int tt = 0; tt < kTilesPerWave; ++tt) {
+                va[tt] = *reinterpret_cast<const uint2 *>(v + oa + m3 + 16 * tt);
+                vb[tt] = *reinterpret_cast<const uint2 *>(v + ob + m3 + 16 * tt);
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < kTilesPerWave; ++tt) {
+            // r2(8 g, 16 T + c)
+            const h8 dr = *reinterpret_cast<const h8 *>(r3r + 128 * tt);
+            const h8 di = *reinterpret_cast<const h8 *>(r3i + 128 * tt);
             f4 cr, ci;
-            cm_dataA(dr, di, neg8(di), Fr[0], nFi[0], cr, ci);   // rows n_ab = 16T + 4g + i, col n_c = c
-            const int64_t m = 16 * T_ + 4 * g + 1024 * c;
+            cm_dataA_conj(dr, di, neg8(dr), Fr[0], Fi[0], cr, ci);   // rows n_ab = 16T + 4g + i, col n_c = c
+            const int m = m3 + 16 * tt;
             float ya[4] = {cr[0] * ks, cr[1] * ks, cr[2] * ks, cr[3] * ks};
             float yb[4] = {ci[0] * ks, ci[1] * ks, ci[2] * ks, ci[3] * ks};
-            if (v != nullptr) {
-                float g4[4];
-                st<T>::ld4(v + oa + m, g4);
+            if (HAS_V) {
+                float ga[4], gb[4];
+                st<T>::unpack4(va[tt], ga);
+                st<T>::unpack4(vb[tt], gb);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) ya[i] *= g4[i];
-                if (has_b) {
-                    st<T>::ld4(v + ob + m, g4);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) yb[i] *= g4[i];
+                for (int i = 0; i < 4; ++i) {
+                    ya[i] *= ga[i];
+                    yb[i] *= gb[i];
                 }
             }
             st<T>::st4(out + oa + m, ya);
@@ -400,11 +471,23 @@ hipError_t launch_pair16k_conv(int st_, const void *u, const void *w, const void
                            B, H);
         return hipGetLastError();
     };
-    if (st_ == ST_F16)
-        return mask ? go(pair16k_kernel<__half, true>, (__half *)nullptr)
-                    : go(pair16k_kernel<__half, false>, (__half *)nullptr);
-    return mask ? go(pair16k_kernel<__hip_bfloat16, true>, (__hip_bfloat16 *)nullptr)
-                : go(pair16k_kernel<__hip_bfloat16, false>, (__hip_bfloat16 *)nullptr);
+    // one instantiation per (storage type, mask, gates) so that no gate test sits in the loops
+    auto pick = [&](auto *tp) -> hipError_t {
+        using TT = std::remove_pointer_t<decltype(tp)>;
+        const int sel = (mask ? 4 : 0) | (w ? 2 : 0) | (v ? 1 : 0);
+        switch (sel) {
+        case 0: return go(pair16k_kernel<TT, false, false, false>, tp);
+        case 1: return go(pair16k_kernel<TT, false, false, true>, tp);
+        case 2: return go(pair16k_kernel<TT, false, true, false>, tp);
+        case 3: return go(pair16k_kernel<TT, false, true, true>, tp);
+        case 4: return go(pair16k_kernel<TT, true, false, false>, tp);
+        case 5: return go(pair16k_kernel<TT, true, false, true>, tp);
+        case 6: return go(pair16k_kernel<TT, true, true, false>, tp);
+        default: return go(pair16k_kernel<TT, true, true, true>, tp);
+        }
+    };
+    if (st_ == ST_F16) return pick((__half *)nullptr);
+    return pick((__hip_bfloat16 *)nullptr);
 }
 
 }  // namespace fftconv
