@@ -229,9 +229,10 @@ hipError_t get_pair3_tables(Pair3Tables *out) {
             for (int nt = 0; nt < 2; ++nt)      // rows f_b = 16nt + 4g + i, cols n_a = 16nt2 + c (conj)
                 for (int nt2 = 0; nt2 < 2; ++nt2)
                     put8(tw3, (nt * 2 + nt2) * 64 + l, i, 2.0 * pi * (double)(16 * nt2 + c) * (16 * nt + 4 * g + i) / 1024.0);
-            for (int T = 0; T < 64; ++T)        // rows f_c = 16nt + 4g + i, cols n_ab = 16T + c
+            for (int T = 0; T < 64; ++T)        // rows f_c = 16nt + 4g + i, cols n_ab = 16(T & ~1) + 2c + (T & 1)
                 for (int nt = 0; nt < 2; ++nt) {
-                    const double a = (double)((int64_t)(16 * nt + 4 * g + i) * (16 * T + c) % 32768);
+                    const int64_t nab = 16 * (T & ~1) + 2 * c + (T & 1);
+                    const double a = (double)((int64_t)(16 * nt + 4 * g + i) * nab % 32768);
                     put8(two1, ((size_t)T * 2 + nt) * 64 + l, i, -2.0 * pi * a / M2);
                 }
             for (int fc = 0; fc < 32; ++fc)     // rows n_b = 16nt3 + 4g + i, cols n_a = 16nt2 + c (conj)

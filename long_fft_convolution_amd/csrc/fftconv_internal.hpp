@@ -139,7 +139,7 @@ struct Pair3Tables {
     const void *fr, *fi;     // DFT-32 operand tiles, [2][64 lanes][8] fp16
     const void *tw1;         // inner twiddles w1024^{n_a f_b}, [mt][nt][lane]: cos[4], sin[4]
     const void *tw3;         // inner conj twiddles, [nt][nt2][lane]
-    const void *two1;        // outer twiddles wM^{f_c n_ab}, [64 T][2 nt][lane]
+    const void *two1;        // outer twiddles wM^{f_c n_ab}, [64 T][2 nt][lane], n_ab = 16(T & ~1) + 2c + (T & 1)
     const void *two2;        // outer conj twiddles, [32 f_c][2 nt3][2 nt2][lane]
 };
 hipError_t get_pair3_tables(Pair3Tables *out);

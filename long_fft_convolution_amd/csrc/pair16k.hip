@@ -105,29 +105,37 @@ __device__ __forceinline__ int kslot(int r) {
 
 // LDS layouts (fp16 element offsets within one plane)
 constexpr int kR1Row = 1032;                 // 1024 + 8: rows f_c padded against bank conflicts
-constexpr int kR1Plane = 32 * kR1Row;        // [f_c][chunk 4][n_a 32][8]
+constexpr int kR1Plane = 32 * kR1Row;        // [f_c][chunk 4][rot(n_a) 32][8]
 constexpr int kR2Plane = 32768;              // [chunk 4][n_ab 1024][8]
+// R1 stores n_a at rot(n_a) = (n_a >> 1) | ((n_a & 1) << 4), so that the phase-1 writes of
+// the 16 lanes holding n_a = 2c + parity fall on 16 distinct bank groups
 __device__ __forceinline__ int r1(int fc, int ks, int na) {
-    return fc * kR1Row + (ks >> 3) * 256 + na * 8 + (ks & 7);
+    return fc * kR1Row + (ks >> 3) * 256 + ((na >> 1) | ((na & 1) << 4)) * 8 + (ks & 7);
 }
 __device__ __forceinline__ int r2(int ks, int nab) { return (ks >> 3) * 8192 + nab * 8 + (ks & 7); }
 
 template <typename T> struct st;
 template <> struct st<__half> {
+    static __device__ __forceinline__ float cvt_half(uint32_t d, int hi) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(hi ? d >> 16 : d));
+    }
     static __device__ __forceinline__ float ld(const __half *p) { return (float)*reinterpret_cast<const _Float16 *>(p); }
     static __device__ __forceinline__ void unpack4(const uint2 &raw, float *o) {
         const _Float16 *hv = reinterpret_cast<const _Float16 *>(&raw);
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = (float)hv[i];
     }
-    static __device__ __forceinline__ void st4(__half *p, const float *v) {
+    static __device__ __forceinline__ uint2 pack4(const float *v) {
         _Float16 hv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) hv[i] = (_Float16)v[i];
-        *reinterpret_cast<uint2 *>(p) = *reinterpret_cast<const uint2 *>(hv);
+        return *reinterpret_cast<const uint2 *>(hv);
     }
 };
 template <> struct st<__hip_bfloat16> {
+    static __device__ __forceinline__ float cvt_half(uint32_t d, int hi) {
+        return __uint_as_float(hi ? d & 0xffff0000u : d << 16);
+    }
     static __device__ __forceinline__ float ld(const __hip_bfloat16 *p) {
         return __uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t *>(p)) << 16);
     }
@@ -137,7 +145,7 @@ template <> struct st<__hip_bfloat16> {
         o[2] = __uint_as_float(raw.y << 16);
         o[3] = __uint_as_float(raw.y & 0xffff0000u);
     }
-    static __device__ __forceinline__ void st4(__hip_bfloat16 *p, const float *v) {
+    static __device__ __forceinline__ uint2 pack4(const float *v) {
         uint32_t w[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -145,7 +153,7 @@ template <> struct st<__hip_bfloat16> {
             w[i] = (uint32_t)(*reinterpret_cast<uint16_t *>(&a)) |
                    ((uint32_t)(*reinterpret_cast<uint16_t *>(&b)) << 16);
         }
-        *reinterpret_cast<uint2 *>(p) = make_uint2(w[0], w[1]);
+        return make_uint2(w[0], w[1]);
     }
 };
 
@@ -156,10 +164,20 @@ static_assert(kWaves == 8, "the LDS address split below assumes 8 waves");
 
 // filter chunk of row fc for (mt2, nt): rows f_c <= 16 as stored, the others from
 // the mirror row 32 - f_c (lane 63 - l, tiles flipped, elements reversed, conjugated)
-__device__ __forceinline__ uint4 k_load(const uint4 *kch, int fc, int mt2, int nt, int lane) {
+// Table and data addresses are a wave-uniform base plus an unsigned 32-bit byte offset,
+// which maps onto the scalar-base global addressing form (no per-lane 64-bit pointers).
+template <typename V, typename P>
+__device__ __forceinline__ V ldu(const P *base, uint32_t byte_off) {
+    return *reinterpret_cast<const V *>(reinterpret_cast<const char *>(base) + byte_off);
+}
+template <typename V, typename P>
+__device__ __forceinline__ void stu(P *base, uint32_t byte_off, const V &x) {
+    *reinterpret_cast<V *>(reinterpret_cast<char *>(base) + byte_off) = x;
+}
+__device__ __forceinline__ uint4 k_load(const uint4 *kch, int fc, int mt2, int nt, uint32_t lane) {
     const bool mir = fc > 16;
-    const int row = mir ? 32 - fc : fc, a = mir ? 1 - mt2 : mt2, b = mir ? 1 - nt : nt;
-    return kch[((row * 2 + a) * 2 + b) * 64 + (mir ? 63 - lane : lane)];
+    const uint32_t row = mir ? 32 - fc : fc, a = mir ? 1 - mt2 : mt2, b = mir ? 1 - nt : nt;
+    return ldu<uint4>(kch + ((row * 2 + a) * 2 + b) * 64, 16u * (mir ? 63 - lane : lane));
 }
 __device__ __forceinline__ h8 k_fix(const uint4 &q, bool mir) {
     if (!mir) return *reinterpret_cast<const h8 *>(&q);
@@ -192,6 +210,7 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
     _Float16 *P1 = smem + kR1Plane;         // plane 1 (im)
     h8 *s_tw1 = reinterpret_cast<h8 *>(smem + 2 * kR1Plane);   // [mt][nt][lane]
     h8 *s_tw3 = s_tw1 + 4 * 64;                                 // [nt][nt2][lane]
+    uint8_t *s_mask = reinterpret_cast<uint8_t *>(s_tw3 + 4 * 64);   // mask row of the pair's channel
 
     const int tid = threadIdx.x;
     for (int i = tid; i < 256; i += 64 * kWaves) {
@@ -211,7 +230,7 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
     // Every LDS access below is a per-lane base plus a compile-time offset: r1() / r2()
     // split into lane, wave and constant parts (phase 1 writes, 2a reads, 2b writes, 3 reads).
     const int b1w = 4 * g * kR1Row + 8 * c + 256 * (wave & 3) + 4 * (wave >> 2);
-    const int b2r = kR1Row * wave + 256 * g + 8 * c;
+    const int b2r = kR1Row * wave + 256 * g + 8 * (c >> 1) + 128 * (c & 1);
     const int b2w = 8192 * (wave >> 2) + (wave & 3) + 8 * c + 1024 * g;
     const int b3r = 1024 * wave + 8192 * g + 8 * c;
     _Float16 *const w1r = P0 + b1w, *const w1i = P1 + b1w;
@@ -225,48 +244,72 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
     const uint32_t wg_on_xcd = nwg / 8 + (xcd < nwg % 8 ? 1u : 0u);
     const int64_t p_begin = P * xcd / 8, p_end = P * (xcd + 1) / 8;
 
-    for (int64_t p = p_begin + wg_local; p < p_end; p += wg_on_xcd) {
-        const int64_t h = p / PB, bp = p - h * PB;
-        const bool has_b = 2 * bp + 1 < B;
-        const int64_t oa = (2 * bp * H + h) * N, ob = has_b ? oa + H * N : oa;
-        const float ks = kscale[h];
-        // per-lane element offset of phase 1 (n_ab = 16 T + c, n_c = 4 g + j) and phase 3
-        const int m1 = 16 * kTilesPerWave * wave + c + 4096 * g;
-        const int m3 = 16 * kTilesPerWave * wave + 4 * g + 1024 * c;
-        const T *ua = u + oa + m1, *ub = u + ob + m1;
-        const T *wa = HAS_W ? w + oa + m1 : nullptr, *wb = HAS_W ? w + ob + m1 : nullptr;
+    // per-lane element offset of phase 1 (n_ab = 128 wave + 2c, n_c = 4 g) and phase 3
+    const uint32_t m1 = 16 * kTilesPerWave * wave + 2 * c + 4096 * g;
+    const uint32_t m3 = 16 * kTilesPerWave * wave + 4 * g + 1024 * c;
 
-        // ---- phase 1: outer DFT over n_c for this wave's tiles T of n_ab, in two
-        // batches whose strided loads are all issued before any is used
+    // The pair loop is software-pipelined: the first phase-1 batch of the next pair and
+    // the output gate of this pair are loaded during the last row of phase 2, the second
+    // batch while the first is transformed.  Raw 16-bit values are held until used.
+    // Phase 1 reads one dword (two adjacent n_ab) per lane and element: lane (g, c) holds
+    // n_ab = 128 wave + 32 q + 2c + par, n_c = 4g + j, for q = 0..3 (two per batch); the
+    // 16-column tiles are (q, par), outer twiddle tables indexed by T = 8 wave + 2q + par.
+    struct Batch {   // [q in batch][j] raw storage bits of two adjacent n_ab
+        uint32_t xa[2][4], xb[2][4], ga[2][4], gb[2][4];
+    };
+    const uint32_t ul = lane;
+    auto pair_base = [&](int64_t pp, int64_t &oa_, int64_t &ob_, bool &hb_) {
+        // pairs < 2^31; the quotient is made wave-uniform so that all pair addresses are scalar
+        const int64_t hh = __builtin_amdgcn_readfirstlane((uint32_t)pp / (uint32_t)PB), bpp = pp - hh * PB;
+        hb_ = 2 * bpp + 1 < B;
+        oa_ = (2 * bpp * H + hh) * N;
+        ob_ = hb_ ? oa_ + H * N : oa_;
+    };
+    auto load_batch = [&](int64_t oa_, int64_t ob_, int half, Batch &x) {
+        const uint32_t *pua = reinterpret_cast<const uint32_t *>(u + oa_);
+        const uint32_t *pub = reinterpret_cast<const uint32_t *>(u + ob_);
+        const uint32_t *pwa = reinterpret_cast<const uint32_t *>(w + oa_);
+        const uint32_t *pwb = reinterpret_cast<const uint32_t *>(w + ob_);
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            constexpr int TB = kTilesPerWave / 2;
-            float xa[TB][4], xb[TB][4];
-            h8 tw[TB][2];
+        for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
-            for (int tq = 0; tq < TB; ++tq) {
-                const int t = half * TB + tq;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int m = 16 * t + 1024 * j;
-                    xa[tq][j] = st<T>::ld(ua + m);
-                    xb[tq][j] = st<T>::ld(ub + m);
-                    if (HAS_W) {
-                        xa[tq][j] *= st<T>::ld(wa + m);
-                        xb[tq][j] *= st<T>::ld(wb + m);
-                    }
+            for (int j = 0; j < 4; ++j) {
+                const int m = (32 * (2 * half + qq) + 1024 * j) / 2;   // in dwords
+                x.xa[qq][j] = ldu<uint32_t>(pua + m, 2 * m1);
+                x.xb[qq][j] = ldu<uint32_t>(pub + m, 2 * m1);
+                if (HAS_W) {
+                    x.ga[qq][j] = ldu<uint32_t>(pwa + m, 2 * m1);
+                    x.gb[qq][j] = ldu<uint32_t>(pwb + m, 2 * m1);
                 }
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) tw[tq][nt] = twO1[(t * 2 + nt) * 64 + lane];
             }
+    };
+    auto load_tw = [&](int half, h8 (&tw)[2][2][2]) {
 #pragma unroll
-            for (int tq = 0; tq < TB; ++tq) {
-                const int t = half * TB + tq;
+        for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+            for (int par = 0; par < 2; ++par)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+                    tw[qq][par][nt] = ldu<h8>(twO1 + ((2 * (2 * half + qq) + par) * 2 + nt) * 64, 16u * ul);
+    };
+    // phase 1 for one batch: outer DFT over n_c, outer twiddle, into R1; the two q of the
+    // batch sit in adjacent K slots, so each (par, nt, i) is one 32-bit write per plane
+    auto phase1_batch = [&](const Batch &x, const h8 (&tw)[2][2][2], int half, bool hb_) {
+        h4 yr[2][2][2], yi[2][2][2];   // [qq][par][nt]
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+            for (int par = 0; par < 2; ++par) {
                 h8 br, bi;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    br[j] = (_Float16)xa[tq][j];
-                    bi[j] = has_b ? (_Float16)xb[tq][j] : (_Float16)0.f;
+                    float xa = st<T>::cvt_half(x.xa[qq][j], par), xb = st<T>::cvt_half(x.xb[qq][j], par);
+                    if (HAS_W) {
+                        xa *= st<T>::cvt_half(x.ga[qq][j], par);
+                        xb *= st<T>::cvt_half(x.gb[qq][j], par);
+                    }
+                    br[j] = (_Float16)xa;
+                    bi[j] = hb_ ? (_Float16)xb : (_Float16)0.f;
                     br[4 + j] = (_Float16)0.f;
                     bi[4 + j] = (_Float16)0.f;
                 }
@@ -275,16 +318,53 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                 for (int nt = 0; nt < 2; ++nt) {
                     f4 ar, ai;
                     cm_constA(Fr[nt], Fi[nt], br, bi, nbi, ar, ai);   // rows f_c = 16nt + 4g + i, cols n_ab
-                    h4 yr = to_h4(ar), yi = to_h4(ai);
-                    cmul4(yr, yi, tw[tq][nt]);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {   // r1(16 nt + 4 g + i, kslot(n_ab >> 5), n_ab & 31)
-                        const int o = (16 * nt + i) * kR1Row + 128 * (t & 1) + (t >> 1);
-                        w1r[o] = yr[i];
-                        w1i[o] = yi[i];
-                    }
+                    yr[qq][par][nt] = to_h4(ar);
+                    yi[qq][par][nt] = to_h4(ai);
+                    cmul4(yr[qq][par][nt], yi[qq][par][nt], tw[qq][par][nt]);
                 }
             }
+#pragma unroll
+        for (int par = 0; par < 2; ++par)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {   // r1(16 nt + 4 g + i, kslot(4 wave + q), 2c + par)
+                    const int o = (16 * nt + i) * kR1Row + 128 * par + 2 * half;
+                    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+                    *reinterpret_cast<h2 *>(w1r + o) = h2{yr[0][par][nt][i], yr[1][par][nt][i]};
+                    *reinterpret_cast<h2 *>(w1i + o) = h2{yi[0][par][nt][i], yi[1][par][nt][i]};
+                }
+    };
+
+    int64_t p = p_begin + wg_local;
+    if (p >= p_end) return;
+    int64_t oa, ob;
+    bool has_b;
+    pair_base(p, oa, ob, has_b);
+    Batch x0;
+    load_batch(oa, ob, 0, x0);
+
+    for (; p < p_end; p += wg_on_xcd) {
+        const int64_t h = __builtin_amdgcn_readfirstlane((uint32_t)p / (uint32_t)PB);
+        const float ks = kscale[h];
+        int64_t p_nx = p + wg_on_xcd, oa_nx, ob_nx;
+        bool hb_nx;
+        pair_base(p_nx < p_end ? p_nx : p, oa_nx, ob_nx, hb_nx);
+
+        // the mask row is read in phase 2 only, after the barrier that ends phase 1
+        if (MASKED && tid < kMaskBlocks / 4)
+            reinterpret_cast<uint32_t *>(s_mask)[tid] = reinterpret_cast<const uint32_t *>(mask + h * kMaskBlocks)[tid];
+
+        // ---- phase 1: outer DFT over n_c for this wave's tiles T of n_ab, two batches
+        // (loads are issued in the order they are consumed: vmcnt waits are in order)
+        {
+            h8 tw0[2][2][2], tw1[2][2][2];
+            load_tw(0, tw0);
+            load_tw(1, tw1);
+            Batch x1;
+            load_batch(oa, ob, 1, x1);
+            phase1_batch(x0, tw0, 0, has_b);
+            phase1_batch(x1, tw1, 1, has_b);
         }
         __syncthreads();
 
@@ -295,7 +375,7 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
         for (int r = 0; r < kRowsPerWave; ++r) {
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {   // r1(wave + 8 r, 8 g, 16 mt + c)
-                const int o = kWaves * kR1Row * r + 128 * mt;
+                const int o = kWaves * kR1Row * r + 64 * mt;
                 ar_[r][mt] = *reinterpret_cast<const h8 *>(r2r + o);
                 ai_[r][mt] = *reinterpret_cast<const h8 *>(r2i + o);
             }
@@ -305,11 +385,12 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
 #pragma unroll
         for (int mt2 = 0; mt2 < 2; ++mt2)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) kq[mt2][nt] = k_load(kch, wave, mt2, nt, lane);
+            for (int nt = 0; nt < 2; ++nt) kq[mt2][nt] = k_load(kch, wave, mt2, nt, ul);
         __syncthreads();
 
         // ---- phase 2b: the 1024-point chain per row, filter product, inverse chain;
         // the next row's filter chunks are fetched while this row computes
+        uint2 va[kTilesPerWave], vb[kTilesPerWave];
 #pragma unroll
         for (int r = 0; r < kRowsPerWave; ++r) {
             const int fc = wave + kWaves * r;
@@ -322,14 +403,27 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
 #pragma unroll
                 for (int mt2 = 0; mt2 < 2; ++mt2)
 #pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) kq[mt2][nt] = k_load(kch, fc + kWaves, mt2, nt, lane);
+                    for (int nt = 0; nt < 2; ++nt) kq[mt2][nt] = k_load(kch, fc + kWaves, mt2, nt, ul);
             }
             h8 two[2][2];
 #pragma unroll
             for (int nt3 = 0; nt3 < 2; ++nt3)
 #pragma unroll
                 for (int nt2 = 0; nt2 < 2; ++nt2)
-                    two[nt3][nt2] = twO2[((kWaves * r * 2 + nt3) * 2 + nt2) * 64 + lane];
+                    two[nt3][nt2] = ldu<h8>(twO2 + ((kWaves * r * 2 + nt3) * 2 + nt2) * 64, 16u * ul);
+            if (r == kRowsPerWave - 1) {   // output gate of this pair, first batch of the next
+                if (HAS_V) {
+#pragma unroll
+                    for (int tt = 0; tt < kTilesPerWave; ++tt) {
+                        va[tt] = ldu<uint2>(v + oa + 16 * tt, 2 * m3);
+                        vb[tt] = ldu<uint2>(v + ob + 16 * tt, 2 * m3);
+                    }
+                }
+                // pinned order: the gate is consumed first, and vmcnt waits are in order
+                __builtin_amdgcn_sched_barrier(0);
+                load_batch(oa_nx, ob_nx, 0, x0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
             // S1: data A (M = n_a tiles mt, K = n_b), const B F[nt] (N = f_b); twiddle w1024^{n_a f_b}
             h4 t1r[2][2], t1i[2][2];
 #pragma unroll
@@ -358,14 +452,17 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                     yi[mt2][nt] = to_h4(ci);
                     h8 kf = kk[mt2][nt];
                     if (MASKED) {
-                        const uint8_t *mrow = mask + h * kMaskBlocks;
+                        // block of bin f (or of its mirror 2N - f); the lane index is laundered
+                        // so that these pair-invariant indices are recomputed, not held
+                        int lc = c, lg = g;
+                        asm volatile("" : "+v"(lc), "+v"(lg));
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            const int f = fc + 32 * (16 * nt + c) + 1024 * (16 * mt2 + 4 * g + i);
+                            const int f = fc + 32 * (16 * nt + lc) + 1024 * (16 * mt2 + 4 * lg + i);
                             const int fr_ = f <= N ? f : M2 - f;
                             int blk = fr_ / (N / kMaskBlocks);
                             blk = blk > kMaskBlocks - 1 ? kMaskBlocks - 1 : blk;
-                            if (!mrow[blk]) kf[i] = kf[4 + i] = (_Float16)0.f;
+                            if (!s_mask[blk]) kf[i] = kf[4 + i] = (_Float16)0.f;
                         }
                     }
                     cmul4(yr[mt2][nt], yi[mt2][nt], kf);
@@ -410,14 +507,6 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
         __syncthreads();
 
         // ---- phase 3: outer inverse over f_c (outputs n_c < 16 only), scale, gate, store
-        uint2 va[kTilesPerWave], vb[kTilesPerWave];
-        if (HAS_V) {
-#pragma unroll
-            for (int tt = 0; tt < kTilesPerWave; ++tt) {
-                va[tt] = *reinterpret_cast<const uint2 *>(v + oa + m3 + 16 * tt);
-                vb[tt] = *reinterpret_cast<const uint2 *>(v + ob + m3 + 16 * tt);
-            }
-        }
 #pragma unroll
         for (int tt = 0; tt < kTilesPerWave; ++tt) {
             // r2(8 g, 16 T + c)
@@ -425,7 +514,6 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
             const h8 di = *reinterpret_cast<const h8 *>(r3i + 128 * tt);
             f4 cr, ci;
             cm_dataA_conj(dr, di, neg8(dr), Fr[0], Fi[0], cr, ci);   // rows n_ab = 16T + 4g + i, col n_c = c
-            const int m = m3 + 16 * tt;
             float ya[4] = {cr[0] * ks, cr[1] * ks, cr[2] * ks, cr[3] * ks};
             float yb[4] = {ci[0] * ks, ci[1] * ks, ci[2] * ks, ci[3] * ks};
             if (HAS_V) {
@@ -438,10 +526,16 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                     yb[i] *= gb[i];
                 }
             }
-            st<T>::st4(out + oa + m, ya);
-            if (has_b) st<T>::st4(out + ob + m, yb);
+            // without a second row (ob == oa) the first row's values are stored twice, so that
+            // no load or store sits under a branch
+            const uint2 pa = st<T>::pack4(ya), pb = st<T>::pack4(yb);
+            stu(out + oa + 16 * tt, 2 * m3, pa);
+            stu(out + ob + 16 * tt, 2 * m3, has_b ? pb : pa);
         }
         __syncthreads();
+        oa = oa_nx;
+        ob = ob_nx;
+        has_b = hb_nx;
     }
 }
 
@@ -458,9 +552,10 @@ hipError_t launch_pair16k_conv(int st_, const void *u, const void *w, const void
             cus = n;
     }
     const int64_t pairs = H * ((B + 1) / 2);
+    if (pairs >= ((int64_t)1 << 31)) return hipErrorInvalidValue;   // pair indices are 32-bit
     int64_t blocks = cus;
     if (blocks > pairs) blocks = pairs < 8 ? 8 : pairs;
-    const size_t lds = (size_t)2 * kR1Plane * sizeof(_Float16) + 2 * 256 * 16;
+    const size_t lds = (size_t)2 * kR1Plane * sizeof(_Float16) + 2 * 256 * 16 + kMaskBlocks;
     auto go = [&](auto kern, auto *tp) -> hipError_t {
         using TT = std::remove_pointer_t<decltype(tp)>;
         hipError_t err = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
