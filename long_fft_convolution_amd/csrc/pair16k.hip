@@ -233,6 +233,13 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
     const int b2r = kR1Row * wave + 256 * g + 8 * (c >> 1) + 128 * (c & 1);
     const int b2w = 8192 * (wave >> 2) + (wave & 3) + 8 * c + 1024 * g;
     const int b3r = 1024 * wave + 8192 * g + 8 * c;
+    // Phase-3 staging: fp32 rows rho = 16 seq + n_c of this wave's 128 n_ab, held in this
+    // wave's own R2 bytes (plane rho >> 4, chunk (rho >> 2) & 3, n_ab 128 wave .. + 127:
+    // 2 KB = four rows per piece); 16-byte units XOR-swizzled by 4 (n_c & 3).
+    const uint32_t st_w = 2 * (8192 * (c >> 2) + 1024 * wave) + 512 * (c & 3) + 16 * g;   // + 64 (tt ^ (c & 3))
+    const uint32_t st_r = 2 * 1024 * wave + 512 * (lane >> 4);
+    const uint32_t st_r0 = st_r + 16 * ((2 * (lane & 15)) ^ (4 * (lane >> 4)));
+    const uint32_t st_r1 = st_r + 16 * ((2 * (lane & 15) + 1) ^ (4 * (lane >> 4)));
     _Float16 *const w1r = P0 + b1w, *const w1i = P1 + b1w;
     const _Float16 *const r2r = P0 + b2r, *const r2i = P1 + b2r;
     _Float16 *const w2r = P0 + b2w, *const w2i = P1 + b2w;
@@ -246,7 +253,9 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
 
     // per-lane element offset of phase 1 (n_ab = 128 wave + 2c, n_c = 4 g) and phase 3
     const uint32_t m1 = 16 * kTilesPerWave * wave + 2 * c + 4096 * g;
-    const uint32_t m3 = 16 * kTilesPerWave * wave + 4 * g + 1024 * c;
+    // phase 3 stores rows of 128 contiguous n_ab: lane l covers n_c = 4k' + (l >> 4),
+    // n_ab = 128 wave + 8 (l & 15) + 0..7
+    const uint32_t m4 = 16 * kTilesPerWave * wave + 8 * (lane & 15) + 1024 * (lane >> 4);
 
     // The pair loop is software-pipelined: the first phase-1 batch of the next pair and
     // the output gate of this pair are loaded during the last row of phase 2, the second
@@ -390,7 +399,7 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
 
         // ---- phase 2b: the 1024-point chain per row, filter product, inverse chain;
         // the next row's filter chunks are fetched while this row computes
-        uint2 va[kTilesPerWave], vb[kTilesPerWave];
+        uint4 vq[8];
 #pragma unroll
         for (int r = 0; r < kRowsPerWave; ++r) {
             const int fc = wave + kWaves * r;
@@ -415,8 +424,7 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                 if (HAS_V) {
 #pragma unroll
                     for (int tt = 0; tt < kTilesPerWave; ++tt) {
-                        va[tt] = ldu<uint2>(v + oa + 16 * tt, 2 * m3);
-                        vb[tt] = ldu<uint2>(v + ob + 16 * tt, 2 * m3);
+                        vq[tt] = ldu<uint4>(v + (tt < 4 ? oa : ob) + 4096 * (tt & 3), 2 * m4);
                     }
                 }
                 // pinned order: the gate is consumed first, and vmcnt waits are in order
@@ -506,31 +514,51 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
         }
         __syncthreads();
 
-        // ---- phase 3: outer inverse over f_c (outputs n_c < 16 only), scale, gate, store
+        // ---- phase 3: outer inverse over f_c (outputs n_c < 16 only) and output scale for all
+        // of this wave's tiles, staged as fp32 in its own R2 bytes once every tile is read,
+        // then gated and stored as contiguous 16-byte rows
+        f4 ya[kTilesPerWave], yb[kTilesPerWave];
 #pragma unroll
         for (int tt = 0; tt < kTilesPerWave; ++tt) {
             // r2(8 g, 16 T + c)
             const h8 dr = *reinterpret_cast<const h8 *>(r3r + 128 * tt);
             const h8 di = *reinterpret_cast<const h8 *>(r3i + 128 * tt);
-            f4 cr, ci;
-            cm_dataA_conj(dr, di, neg8(dr), Fr[0], Fi[0], cr, ci);   // rows n_ab = 16T + 4g + i, col n_c = c
-            float ya[4] = {cr[0] * ks, cr[1] * ks, cr[2] * ks, cr[3] * ks};
-            float yb[4] = {ci[0] * ks, ci[1] * ks, ci[2] * ks, ci[3] * ks};
-            if (HAS_V) {
-                float ga[4], gb[4];
-                st<T>::unpack4(va[tt], ga);
-                st<T>::unpack4(vb[tt], gb);
+            cm_dataA_conj(dr, di, neg8(dr), Fr[0], Fi[0], ya[tt], yb[tt]);   // rows n_ab = 16T + 4g + i, col n_c = c
+            ya[tt] *= ks;
+            yb[tt] *= ks;
+            __builtin_amdgcn_sched_barrier(0);   // (bounds the live R2 operands)
+        }
+        {
+            char *const s8 = reinterpret_cast<char *>(smem);
+            // (re-derived here so that the eight swizzled addresses are not held across pairs)
+            uint32_t stw = st_w, cq = 64 * (c & 3);
+            asm volatile("" : "+v"(stw), "+v"(cq));
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    ya[i] *= ga[i];
-                    yb[i] *= gb[i];
-                }
+            for (int tt = 0; tt < kTilesPerWave; ++tt) {
+                const uint32_t o = stw + ((64 * tt) ^ cq);
+                stu(s8, o, ya[tt]);                                     // row n_c = c of sequence a
+                stu(s8 + 2 * kR1Plane, o, yb[tt]);                      // plane 1: sequence b
             }
-            // without a second row (ob == oa) the first row's values are stored twice, so that
-            // no load or store sits under a branch
-            const uint2 pa = st<T>::pack4(ya), pb = st<T>::pack4(yb);
-            stu(out + oa + 16 * tt, 2 * m3, pa);
-            stu(out + ob + 16 * tt, 2 * m3, has_b ? pb : pa);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                // without a second row (ob == oa) its stores repeat the first row's values
+                const int kk = (k >= 4 && !has_b) ? k - 4 : k;
+                const char *src = s8 + 2 * ((kk >> 2) * kR1Plane + (kk & 3) * 8192);
+                const f4 y0 = ldu<f4>(src, st_r0), y1 = ldu<f4>(src, st_r1);
+                float yv[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+                if (HAS_V) {
+                    float ga[4], gb[4];
+                    st<T>::unpack4(make_uint2(vq[k].x, vq[k].y), ga);
+                    st<T>::unpack4(make_uint2(vq[k].z, vq[k].w), gb);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        yv[i] *= ga[i];
+                        yv[4 + i] *= gb[i];
+                    }
+                }
+                const uint2 lo = st<T>::pack4(yv), hi = st<T>::pack4(yv + 4);
+                stu(out + (k < 4 ? oa : ob) + 4096 * (k & 3), 2 * m4, make_uint4(lo.x, lo.y, hi.x, hi.y));
+            }
         }
         __syncthreads();
         oa = oa_nx;
