@@ -69,32 +69,33 @@ __device__ __forceinline__ void cmul4(h4 &re, h4 &im, const h8 &t) {
     im = re * s + im * c;
     re = r;
 }
-// complex 16x16x32 tile products, (re, im) planes; "data A": C = D F, "const A": C = F D
-__device__ __forceinline__ void cm_dataA(const h8 &dr, const h8 &di, const h8 &ndi, const h8 &fr,
-                                         const h8 &fi, f4 &cr, f4 &ci) {
+// complex 16x16x32 tile products, (re, im) planes; "data A": C = D F, "const A": C = F D.
+// The constant's imaginary plane is also held negated (nfi = -Im F), so that no data plane
+// is ever negated.
+__device__ __forceinline__ void cm_dataA(const h8 &dr, const h8 &di, const h8 &fr, const h8 &fi,
+                                         const h8 &nfi, f4 &cr, f4 &ci) {
     const f4 z = {0.f, 0.f, 0.f, 0.f};
-    cr = mfma(ndi, fi, mfma(dr, fr, z));
+    cr = mfma(di, nfi, mfma(dr, fr, z));
     ci = mfma(di, fr, mfma(dr, fi, z));
 }
-__device__ __forceinline__ void cm_constA(const h8 &fr, const h8 &fi, const h8 &dr, const h8 &di,
-                                          const h8 &ndi, f4 &cr, f4 &ci) {
+__device__ __forceinline__ void cm_constA(const h8 &fr, const h8 &fi, const h8 &nfi, const h8 &dr,
+                                          const h8 &di, f4 &cr, f4 &ci) {
     const f4 z = {0.f, 0.f, 0.f, 0.f};
-    cr = mfma(fi, ndi, mfma(fr, dr, z));
+    cr = mfma(nfi, di, mfma(fr, dr, z));
     ci = mfma(fi, dr, mfma(fr, di, z));
 }
-
-// the same with conj(F): the negated data plane is the real one
-__device__ __forceinline__ void cm_dataA_conj(const h8 &dr, const h8 &di, const h8 &ndr, const h8 &fr,
-                                              const h8 &fi, f4 &cr, f4 &ci) {
+// the same with conj(F)
+__device__ __forceinline__ void cm_dataA_conj(const h8 &dr, const h8 &di, const h8 &fr, const h8 &fi,
+                                              const h8 &nfi, f4 &cr, f4 &ci) {
     const f4 z = {0.f, 0.f, 0.f, 0.f};
     cr = mfma(di, fi, mfma(dr, fr, z));
-    ci = mfma(ndr, fi, mfma(di, fr, z));
+    ci = mfma(dr, nfi, mfma(di, fr, z));
 }
-__device__ __forceinline__ void cm_constA_conj(const h8 &fr, const h8 &fi, const h8 &dr, const h8 &di,
-                                               const h8 &ndr, f4 &cr, f4 &ci) {
+__device__ __forceinline__ void cm_constA_conj(const h8 &fr, const h8 &fi, const h8 &nfi, const h8 &dr,
+                                               const h8 &di, f4 &cr, f4 &ci) {
     const f4 z = {0.f, 0.f, 0.f, 0.f};
     cr = mfma(fi, di, mfma(fr, dr, z));
-    ci = mfma(fi, ndr, mfma(fr, di, z));
+    ci = mfma(nfi, dr, mfma(fr, di, z));
 }
 
 // K slot (0..31) of row r (0..31) in a chained operand: rows 4g + j of tile 0
@@ -218,11 +219,12 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
         s_tw3[i] = reinterpret_cast<const h8 *>(tb.tw3)[i];
     }
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, c = lane & 15;
-    h8 Fr[2], Fi[2];
+    h8 Fr[2], Fi[2], nFi[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         Fr[t] = reinterpret_cast<const h8 *>(tb.fr)[t * 64 + lane];
         Fi[t] = reinterpret_cast<const h8 *>(tb.fi)[t * 64 + lane];
+        nFi[t] = neg8(Fi[t]);
     }
     // outer twiddles of this wave's tiles [tq][nt][lane] and rows [r][nt3][nt2][lane]
     const h8 *twO1 = reinterpret_cast<const h8 *>(tb.two1) + wave * (kTilesPerWave * 2 * 64);
@@ -322,11 +324,10 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                     br[4 + j] = (_Float16)0.f;
                     bi[4 + j] = (_Float16)0.f;
                 }
-                const h8 nbi = neg8(bi);
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
                     f4 ar, ai;
-                    cm_constA(Fr[nt], Fi[nt], br, bi, nbi, ar, ai);   // rows f_c = 16nt + 4g + i, cols n_ab
+                    cm_constA(Fr[nt], Fi[nt], nFi[nt], br, bi, ar, ai);   // rows f_c = 16nt + 4g + i, cols n_ab
                     yr[qq][par][nt] = to_h4(ar);
                     yi[qq][par][nt] = to_h4(ai);
                     cmul4(yr[qq][par][nt], yi[qq][par][nt], tw[qq][par][nt]);
@@ -403,6 +404,10 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
 #pragma unroll
         for (int r = 0; r < kRowsPerWave; ++r) {
             const int fc = wave + kWaves * r;
+            // the lane offset is re-derived per row so that table byte offsets stay 32-bit
+            // values of this block (a hoisted 64-bit address costs two registers per load)
+            uint32_t lx = ul;
+            asm volatile("" : "+v"(lx));
             h8 kk[2][2];
 #pragma unroll
             for (int mt2 = 0; mt2 < 2; ++mt2)
@@ -412,14 +417,14 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
 #pragma unroll
                 for (int mt2 = 0; mt2 < 2; ++mt2)
 #pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) kq[mt2][nt] = k_load(kch, fc + kWaves, mt2, nt, ul);
+                    for (int nt = 0; nt < 2; ++nt) kq[mt2][nt] = k_load(kch, fc + kWaves, mt2, nt, lx);
             }
             h8 two[2][2];
 #pragma unroll
             for (int nt3 = 0; nt3 < 2; ++nt3)
 #pragma unroll
                 for (int nt2 = 0; nt2 < 2; ++nt2)
-                    two[nt3][nt2] = ldu<h8>(twO2 + ((kWaves * r * 2 + nt3) * 2 + nt2) * 64, 16u * ul);
+                    two[nt3][nt2] = ldu<h8>(twO2 + ((kWaves * r * 2 + nt3) * 2 + nt2) * 64, 16u * lx);
             if (r == kRowsPerWave - 1) {   // output gate of this pair, first batch of the next
                 if (HAS_V) {
 #pragma unroll
@@ -436,11 +441,10 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
             h4 t1r[2][2], t1i[2][2];
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
-                const h8 nai = neg8(ai_[r][mt]);
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
                     f4 cr, ci;
-                    cm_dataA(ar_[r][mt], ai_[r][mt], nai, Fr[nt], Fi[nt], cr, ci);
+                    cm_dataA(ar_[r][mt], ai_[r][mt], Fr[nt], Fi[nt], nFi[nt], cr, ci);
                     t1r[mt][nt] = to_h4(cr);
                     t1i[mt][nt] = to_h4(ci);
                     cmul4(t1r[mt][nt], t1i[mt][nt], s_tw1[(mt * 2 + nt) * 64 + lane]);
@@ -451,11 +455,10 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
                 const h8 br = cat8(t1r[0][nt], t1r[1][nt]), bi = cat8(t1i[0][nt], t1i[1][nt]);
-                const h8 nbi = neg8(bi);
 #pragma unroll
                 for (int mt2 = 0; mt2 < 2; ++mt2) {
                     f4 cr, ci;
-                    cm_constA(Fr[mt2], Fi[mt2], br, bi, nbi, cr, ci);   // rows f_a, cols f_b
+                    cm_constA(Fr[mt2], Fi[mt2], nFi[mt2], br, bi, cr, ci);   // rows f_a, cols f_b
                     yr[mt2][nt] = to_h4(cr);
                     yi[mt2][nt] = to_h4(ci);
                     h8 kf = kk[mt2][nt];
@@ -481,11 +484,10 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
                 const h8 dr = cat8(yr[0][nt], yr[1][nt]), di = cat8(yi[0][nt], yi[1][nt]);
-                const h8 ndr = neg8(dr);
 #pragma unroll
                 for (int nt2 = 0; nt2 < 2; ++nt2) {
                     f4 cr, ci;
-                    cm_dataA_conj(dr, di, ndr, Fr[nt2], Fi[nt2], cr, ci);   // rows f_b, cols n_a
+                    cm_dataA_conj(dr, di, Fr[nt2], Fi[nt2], nFi[nt2], cr, ci);   // rows f_b, cols n_a
                     t3r[nt][nt2] = to_h4(cr);
                     t3i[nt][nt2] = to_h4(ci);
                     cmul4(t3r[nt][nt2], t3i[nt][nt2], s_tw3[(nt * 2 + nt2) * 64 + lane]);
@@ -496,11 +498,10 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
 #pragma unroll
             for (int nt2 = 0; nt2 < 2; ++nt2) {
                 const h8 br = cat8(t3r[0][nt2], t3r[1][nt2]), bi = cat8(t3i[0][nt2], t3i[1][nt2]);
-                const h8 nbr = neg8(br);
 #pragma unroll
                 for (int nt3 = 0; nt3 < 2; ++nt3) {
                     f4 cr, ci;
-                    cm_constA_conj(Fr[nt3], Fi[nt3], br, bi, nbr, cr, ci);   // rows n_b, cols n_a
+                    cm_constA_conj(Fr[nt3], Fi[nt3], nFi[nt3], br, bi, cr, ci);   // rows n_b, cols n_a
                     h4 qr = to_h4(cr), qi = to_h4(ci);
                     cmul4(qr, qi, two[nt3][nt2]);
 #pragma unroll
@@ -523,7 +524,7 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
             // r2(8 g, 16 T + c)
             const h8 dr = *reinterpret_cast<const h8 *>(r3r + 128 * tt);
             const h8 di = *reinterpret_cast<const h8 *>(r3i + 128 * tt);
-            cm_dataA_conj(dr, di, neg8(dr), Fr[0], Fi[0], ya[tt], yb[tt]);   // rows n_ab = 16T + 4g + i, col n_c = c
+            cm_dataA_conj(dr, di, Fr[0], Fi[0], nFi[0], ya[tt], yb[tt]);   // rows n_ab = 16T + 4g + i, col n_c = c
             ya[tt] *= ks;
             yb[tt] *= ks;
             __builtin_amdgcn_sched_barrier(0);   // (bounds the live R2 operands)
