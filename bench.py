@@ -33,7 +33,19 @@ from long_fft_convolution_amd import synth  # noqa: E402
 METRIC = "FFT-conv fwd B·H·N elems/s + % HBM peak (rocprof), N=1K..4M, 1 GPU"
 HBM_PEAK_GBS = 8000.0
 ELEM = {"f32": 4, "f16": 2, "bf16": 2}
-KERNEL_SOURCES = ["fused.hip", "multipass.hip", "fft_device.hpp"]
+KERNEL_SOURCES = ["fused.hip", "multipass.hip", "pair_mfma.hip", "pair16k.hip", "fft_device.hpp",
+                  "fftconv_internal.hpp", "api.cpp"]
+
+
+def path_of(w: synth.Workload):
+    """(kernel name, compute dtype, arithmetic) of the path fftconv_fwd takes for w."""
+    if w.dtype in ("f16", "bf16") and w.N == 1024:
+        return "pair1k_kernel", "f16", "fp16 MFMA operands, fp32 accumulation"
+    if w.dtype in ("f16", "bf16") and w.N == 16384:
+        return "pair16k_kernel", "f16", "fp16 MFMA operands, fp32 accumulation"
+    if w.N <= 16384:
+        return "fused_conv_kernel", "f32", "fp32"
+    return "mp_pass1+mp_pass2+mp_pass3 (one call)", "f32", "fp32"
 
 
 def log(*a):
@@ -181,7 +193,7 @@ def main():
         cpu = cpu_baseline(wl, inp)
         log(f"bench: oracle {cpu['value']:.3e} elems/s on {cpu['cores']} threads ({cpu['sample']})")
 
-    dominant = "fused_conv_kernel" if wl.N <= 16384 else "multipass"
+    dominant, cdtype, arith = path_of(wl)
     rec = {
         "metric": METRIC,
         "value": value,
@@ -193,10 +205,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.dtype,
+        "dtype": cdtype,
         "data": "synthetic (seeded N(0,1) activations, decaying random filter)",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "L_filter": wl.L,
-                   "gated": wl.gated, "storage": wl.dtype, "arithmetic": "fp32",
+                   "gated": wl.gated, "storage": wl.dtype, "arithmetic": arith,
                    "mask_keep_blocks": wl.mask_keep_blocks, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
