@@ -68,6 +68,12 @@ template <> struct io8<__half> {
         for (int i = 0; i < 4; ++i) hv[i] = (_Float16)v[i];
         *reinterpret_cast<uint2 *>(p) = *reinterpret_cast<const uint2 *>(hv);
     }
+    static __device__ __forceinline__ uint4 pack8(const float *v) {
+        _Float16 hv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hv[i] = (_Float16)v[i];
+        return *reinterpret_cast<const uint4 *>(hv);
+    }
 };
 template <> struct io8<__hip_bfloat16> {
     static __device__ __forceinline__ void load(const __hip_bfloat16 *p, float *o) {
@@ -102,6 +108,16 @@ template <> struct io8<__hip_bfloat16> {
         }
         *reinterpret_cast<uint2 *>(p) = make_uint2(w[0], w[1]);
     }
+    static __device__ __forceinline__ uint4 pack8(const float *v) {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            __hip_bfloat16 a = __float2bfloat16(v[2 * i]), b = __float2bfloat16(v[2 * i + 1]);
+            w[i] = (uint32_t)(*reinterpret_cast<uint16_t *>(&a)) |
+                   ((uint32_t)(*reinterpret_cast<uint16_t *>(&b)) << 16);
+        }
+        return make_uint4(w[0], w[1], w[2], w[3]);
+    }
 };
 
 // (re, im) fp32 accumulators of two row tiles -> fp16 operand planes
@@ -129,18 +145,20 @@ struct PairRaw {
     uint4 q[2][4];
 };
 
-template <typename T>
+// (without a second row ob == oa: the loads re-read the first row and the caller zeroes
+// the result, so that no load sits under a branch)
+template <typename T, bool HAS_W>
 __device__ __forceinline__ void load_pair_raw(PairRaw &raw, const T *__restrict__ u,
-                                              const T *__restrict__ w, int64_t oa, int64_t ob,
-                                              bool has_b, int lane) {
+                                              const T *__restrict__ w, int64_t oa, int64_t ob, int lane) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
         const int m0 = 8 * lane + 512 * r;
         raw.q[r][0] = *reinterpret_cast<const uint4 *>(u + oa + m0);
-        raw.q[r][1] = w != nullptr ? *reinterpret_cast<const uint4 *>(w + oa + m0) : make_uint4(0, 0, 0, 0);
-        raw.q[r][2] = has_b ? *reinterpret_cast<const uint4 *>(u + ob + m0) : make_uint4(0, 0, 0, 0);
-        raw.q[r][3] = (has_b && w != nullptr) ? *reinterpret_cast<const uint4 *>(w + ob + m0)
-                                              : make_uint4(0, 0, 0, 0);
+        raw.q[r][2] = *reinterpret_cast<const uint4 *>(u + ob + m0);
+        if (HAS_W) {
+            raw.q[r][1] = *reinterpret_cast<const uint4 *>(w + oa + m0);
+            raw.q[r][3] = *reinterpret_cast<const uint4 *>(w + ob + m0);
+        }
     }
 }
 
@@ -216,7 +234,7 @@ __device__ __forceinline__ void gate_product<__hip_bfloat16>(const uint4 &uq, co
     for (int e = 0; e < 8; ++e) x[e] = (_Float16)a[e];
 }
 
-template <typename T, bool MASKED>
+template <typename T, bool MASKED, bool HAS_W, bool HAS_V>
 __global__ void __launch_bounds__(64 * kPairWaves, MASKED ? 1 : 2)
 pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restrict__ v,
               T *__restrict__ out, const uint4 *__restrict__ kbins, const float *__restrict__ kscale,
@@ -224,7 +242,9 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
     constexpr int N = 1024;
     __shared__ h8 s_tw1[2 * 4 * 64];     // per (mt, nt, lane): cos[4], sin[4]
     __shared__ h8 s_tw3[4 * 2 * 64];     // per (nt, nt2, lane)
-    __shared__ _Float16 s_z[kPairWaves][2][kPlane];
+    // per wave: the transposed input planes (2 x kPlane fp16), later the fp32 output rows
+    // of both sequences (2 x 1024 floats)
+    __shared__ __align__(16) float s_z[kPairWaves][2 * 1024];
     __shared__ h8 s_f1[2][4][64];     // S1 DFT blocks (re, im) per column tile nt
     __shared__ h8 s_f3[2][4][64];     // S1' DFT blocks (re, im) per (ks, nt3)
 
@@ -258,7 +278,8 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
     const uint32_t wg_on_xcd = nwg / 8 + (xcd < nwg % 8 ? 1u : 0u);
     const int64_t p_begin = P * xcd / 8, p_end = P * (xcd + 1) / 8;
     const int64_t stride = (int64_t)wg_on_xcd * kPairWaves;
-    _Float16 *zr = s_z[wave][0], *zi = s_z[wave][1];
+    _Float16 *zr = reinterpret_cast<_Float16 *>(s_z[wave]), *zi = zr + kPlane;
+    char *const so = reinterpret_cast<char *>(s_z[wave]);
     const f4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
     auto offsets = [&](int64_t p, int64_t &h, int64_t &oa, int64_t &ob, bool &has_b) {
@@ -269,9 +290,11 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
         ob = has_b ? oa + H * N : oa;
     };
 
-    // per-pair side data: filter chunks and output-gate chunks
+    // per-pair side data: filter chunks, output-gate rows (contiguous 16-byte chunks in the
+    // order the output is stored) and the channel scale
     struct Side {
         uint4 k[2][4];
+        uint4 v[4];
         float ks;
     };
     auto load_side = [&](int64_t pp, Side &sd) {
@@ -283,13 +306,18 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
         for (int mt2 = 0; mt2 < 2; ++mt2)
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) sd.k[mt2][nt] = krow[(mt2 * 4 + nt) * 64 + lane];
+        if (HAS_V) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                sd.v[q] = *reinterpret_cast<const uint4 *>(v + (q < 2 ? oa : ob) + 512 * (q & 1) + 8 * lane);
+        }
         sd.ks = kscale[h];
     };
     auto load_in = [&](int64_t pp, PairRaw &raw) {
         int64_t h, oa, ob;
         bool hb;
         offsets(pp, h, oa, ob, hb);
-        load_pair_raw<T>(raw, u, w, oa, ob, hb, lane);
+        load_pair_raw<T, HAS_W>(raw, u, w, oa, ob, lane);
     };
 
     // software pipeline: inputs, filter chunks and gate chunks one pair ahead
@@ -317,8 +345,9 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
         for (int r = 0; r < 2; ++r) {
             const int m0 = 8 * lane + 512 * r;
             h8 xa, xb;
-            gate_product<T>(cur.q[r][0], cur.q[r][1], w != nullptr, xa);
-            gate_product<T>(cur.q[r][2], cur.q[r][3], w != nullptr, xb);
+            gate_product<T>(cur.q[r][0], cur.q[r][1], HAS_W, xa);
+            gate_product<T>(cur.q[r][2], cur.q[r][3], HAS_W, xb);
+            if (!has_b) xb = h8{};
             const int ns = m0 >> 5, nf0 = m0 & 31, kss = kslot_of(ns);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -420,23 +449,38 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
                 ai = mfma(a3i[0][nt2], f30r, ai);
                 ai = mfma(a3r[1][nt2], f31i, ai);
                 ai = mfma(a3i[1][nt2], f31r, ai);
-                // rows n_f = 16 nt2 + 4g + i, column n_s = 16 nt3 + c: m = n_f + 32 n_s
-                const int m = 16 * nt2 + 4 * g + 32 * (16 * nt3 + c);
-                float ya[4] = {ar[0] * ks, ar[1] * ks, ar[2] * ks, ar[3] * ks};
-                float yb[4] = {ai[0] * ks, ai[1] * ks, ai[2] * ks, ai[3] * ks};
-                if (v != nullptr) {
-                    float g4[4];
-                    io8<T>::load4(v + oa + m, g4);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) ya[i] *= g4[i];
-                    io8<T>::load4(v + ob + m, g4);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) yb[i] *= g4[i];
-                }
-                io8<T>::store4(out + oa + m, ya);
-                if (has_b) io8<T>::store4(out + ob + m, yb);
+                // rows n_f = 16 nt2 + 4g + i, column n_s = 16 nt3 + c: m = n_f + 32 n_s, four
+                // consecutive m per lane; staged as fp32 rows of both sequences in this wave's
+                // LDS (16-byte unit u = m / 4, bit 2 flipped by bit 4 against bank conflicts)
+                const int un = 8 * (16 * nt3 + c) + 4 * nt2 + g;
+                const int us = un ^ (((un >> 4) & 1) << 2);
+                f4 ya = ar * ks, yb = ai * ks;
+                *reinterpret_cast<f4 *>(so + 16 * us) = ya;
+                *reinterpret_cast<f4 *>(so + 4096 + 16 * us) = yb;
             }
         }
+        // ---- output gate and store: rows of 8 contiguous elements per lane, 16-byte accesses;
+        // without a second row its stores repeat the first row's values
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int qq = (q >= 2 && !has_b) ? q - 2 : q;
+            const int u0 = 128 * (qq & 1) + 2 * lane;
+            const int s0 = u0 ^ (((u0 >> 4) & 1) << 2), s1 = (u0 + 1) ^ ((((u0 + 1) >> 4) & 1) << 2);
+            const f4 y0 = *reinterpret_cast<const f4 *>(so + 4096 * (qq >> 1) + 16 * s0);
+            const f4 y1 = *reinterpret_cast<const f4 *>(so + 4096 * (qq >> 1) + 16 * s1);
+            float y[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+            if (HAS_V) {
+                float g8[8];
+                unpack8<T>(sc.v[q], g8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] *= g8[e];
+            }
+            *reinterpret_cast<uint4 *>(out + (q < 2 ? oa : ob) + 512 * (q & 1) + 8 * lane) = io8<T>::pack8(y);
+        }
+        // the next pair's input scatter reuses this wave's LDS: order after the reads above
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         cur = in1;
         sc = sn;
     }
@@ -466,13 +510,23 @@ hipError_t launch_pair_conv(int logn, int st, const void *u, const void *w, cons
                            (const TT *)u, (const TT *)w, (const TT *)v, (TT *)out,
                            (const uint4 *)kbins, kscale, mask, tb, B, H);
     };
-    if (st == ST_F16) {
-        if (mask) go(pair1k_kernel<__half, true>, (__half *)nullptr);
-        else go(pair1k_kernel<__half, false>, (__half *)nullptr);
-    } else {
-        if (mask) go(pair1k_kernel<__hip_bfloat16, true>, (__hip_bfloat16 *)nullptr);
-        else go(pair1k_kernel<__hip_bfloat16, false>, (__hip_bfloat16 *)nullptr);
-    }
+    // one instantiation per (storage type, mask, gates): no gate test sits in the pair loop
+    auto pick = [&](auto *tp) {
+        using TT = std::remove_pointer_t<decltype(tp)>;
+        const int sel = (mask ? 4 : 0) | (w ? 2 : 0) | (v ? 1 : 0);
+        switch (sel) {
+        case 0: go(pair1k_kernel<TT, false, false, false>, tp); break;
+        case 1: go(pair1k_kernel<TT, false, false, true>, tp); break;
+        case 2: go(pair1k_kernel<TT, false, true, false>, tp); break;
+        case 3: go(pair1k_kernel<TT, false, true, true>, tp); break;
+        case 4: go(pair1k_kernel<TT, true, false, false>, tp); break;
+        case 5: go(pair1k_kernel<TT, true, false, true>, tp); break;
+        case 6: go(pair1k_kernel<TT, true, true, false>, tp); break;
+        default: go(pair1k_kernel<TT, true, true, true>, tp); break;
+        }
+    };
+    if (st == ST_F16) pick((__half *)nullptr);
+    else pick((__hip_bfloat16 *)nullptr);
     return hipGetLastError();
 }
 
