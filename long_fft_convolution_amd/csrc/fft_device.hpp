@@ -31,45 +31,70 @@ __device__ __forceinline__ float2 cmul_posi(float2 a) { return make_float2(-a.y,
 __device__ __forceinline__ float2 cscale(float2 a, float s) { return make_float2(a.x * s, a.y * s); }
 
 // ------------------------------------------------------- storage conversions
+// load2/store2 take an optional element offset e (a lane value): the access
+// is then formed as uniform pointer + 32-bit byte offset.
 template <typename T> struct io;
 template <> struct io<float> {
-    static __device__ __forceinline__ float2 load2(const float *p) { return *reinterpret_cast<const float2 *>(p); }
+    static __device__ __forceinline__ float2 load2(const float *p, uint32_t e = 0) {
+        return *reinterpret_cast<const float2 *>(reinterpret_cast<const char *>(p) + 8u * e);
+    }
     static __device__ __forceinline__ void store2(float *p, float2 v) { *reinterpret_cast<float2 *>(p) = v; }
+    static __device__ __forceinline__ void store2(float *p, uint32_t e, float2 v) {
+        *reinterpret_cast<float2 *>(reinterpret_cast<char *>(p) + 8u * e) = v;
+    }
     static __device__ __forceinline__ float load1(const float *p) { return *p; }
 };
 template <> struct io<__half> {
-    static __device__ __forceinline__ float2 load2(const __half *p) {
-        __half2 h = *reinterpret_cast<const __half2 *>(p);
+    static __device__ __forceinline__ float2 load2(const __half *p, uint32_t e = 0) {
+        __half2 h = *reinterpret_cast<const __half2 *>(reinterpret_cast<const char *>(p) + 4u * e);
         return __half22float2(h);
     }
     static __device__ __forceinline__ void store2(__half *p, float2 v) {
         *reinterpret_cast<__half2 *>(p) = __floats2half2_rn(v.x, v.y);
     }
+    static __device__ __forceinline__ void store2(__half *p, uint32_t e, float2 v) {
+        *reinterpret_cast<__half2 *>(reinterpret_cast<char *>(p) + 4u * e) = __floats2half2_rn(v.x, v.y);
+    }
     static __device__ __forceinline__ float load1(const __half *p) { return __half2float(*p); }
 };
 template <> struct io<__hip_bfloat16> {
-    static __device__ __forceinline__ float2 load2(const __hip_bfloat16 *p) {
-        uint32_t bits = *reinterpret_cast<const uint32_t *>(p);
+    static __device__ __forceinline__ float2 load2(const __hip_bfloat16 *p, uint32_t e = 0) {
+        uint32_t bits = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(p) + 4u * e);
         return make_float2(__uint_as_float(bits << 16), __uint_as_float(bits & 0xffff0000u));
     }
-    static __device__ __forceinline__ void store2(__hip_bfloat16 *p, float2 v) {
+    static __device__ __forceinline__ uint32_t pack(float2 v) {
         __hip_bfloat16 a = __float2bfloat16(v.x), b = __float2bfloat16(v.y);
-        uint32_t bits = (uint32_t)(*reinterpret_cast<uint16_t *>(&a)) |
-                        ((uint32_t)(*reinterpret_cast<uint16_t *>(&b)) << 16);
-        *reinterpret_cast<uint32_t *>(p) = bits;
+        return (uint32_t)(*reinterpret_cast<uint16_t *>(&a)) |
+               ((uint32_t)(*reinterpret_cast<uint16_t *>(&b)) << 16);
+    }
+    static __device__ __forceinline__ void store2(__hip_bfloat16 *p, float2 v) {
+        *reinterpret_cast<uint32_t *>(p) = pack(v);
+    }
+    static __device__ __forceinline__ void store2(__hip_bfloat16 *p, uint32_t e, float2 v) {
+        *reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(p) + 4u * e) = pack(v);
     }
     static __device__ __forceinline__ float load1(const __hip_bfloat16 *p) { return __bfloat162float(*p); }
 };
 
-// Filter-spectrum bins: fp32 complex or fp16 complex.
+// Filter-spectrum bins: fp32 complex or fp16 complex (same element-offset forms).
 template <typename TK> struct kio;
 template <> struct kio<float2> {
-    static __device__ __forceinline__ float2 load(const float2 *p) { return *p; }
+    static __device__ __forceinline__ float2 load(const float2 *p, uint32_t e = 0) {
+        return *reinterpret_cast<const float2 *>(reinterpret_cast<const char *>(p) + 8u * e);
+    }
     static __device__ __forceinline__ void store(float2 *p, float2 v) { *p = v; }
+    static __device__ __forceinline__ void store(float2 *p, uint32_t e, float2 v) {
+        *reinterpret_cast<float2 *>(reinterpret_cast<char *>(p) + 8u * e) = v;
+    }
 };
 template <> struct kio<__half2> {
-    static __device__ __forceinline__ float2 load(const __half2 *p) { return __half22float2(*p); }
+    static __device__ __forceinline__ float2 load(const __half2 *p, uint32_t e = 0) {
+        return __half22float2(*reinterpret_cast<const __half2 *>(reinterpret_cast<const char *>(p) + 4u * e));
+    }
     static __device__ __forceinline__ void store(__half2 *p, float2 v) { *p = __floats2half2_rn(v.x, v.y); }
+    static __device__ __forceinline__ void store(__half2 *p, uint32_t e, float2 v) {
+        *reinterpret_cast<__half2 *>(reinterpret_cast<char *>(p) + 4u * e) = __floats2half2_rn(v.x, v.y);
+    }
 };
 
 // ------------------------------------------------ radix-R DFT in registers
@@ -95,9 +120,14 @@ __device__ __forceinline__ float2 w32(int q) {
     }
 }
 
-// Multiply by exp(-2 pi i q / R) with the trivial angles done exactly.
+// Multiply by exp(-2 pi i q / R), 0 <= q < R (R <= 32), with the trivial
+// angles done exactly; q >= R/2 uses exp(-2 pi i q / R) = -exp(-2 pi i (q - R/2) / R).
 template <int R>
 __device__ __forceinline__ float2 twiddle_const(float2 a, int q) {
+    if (2 * q >= R) {
+        a = make_float2(-a.x, -a.y);
+        q -= R / 2;
+    }
     if (q == 0) return a;
     if (4 * q == R) return cmul_negi(a);
     if (8 * q == R) {
@@ -148,6 +178,39 @@ template <> struct Dft<4> {
     }
 };
 
+// In-place DFT of N = P * Q points in two register stages: n = p + P m,
+// k = q + Q s.  Step 1, for each p, a Q-point DFT over m, written back in
+// place and multiplied by omega_N^{pq}; step 2, for each q, a P-point DFT
+// over p.  The result is relabelled into natural order at compile time.
+// The scheduling barriers keep step 2's transforms from being interleaved,
+// which bounds the registers live at once.
+template <int P, int Q>
+__device__ __forceinline__ void dft_pq(float2 *a) {
+    constexpr int N = P * Q;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        float2 t[Q], o[Q];
+#pragma unroll
+        for (int m = 0; m < Q; ++m) t[m] = a[p + P * m];
+        Dft<Q>::run(t, o);
+#pragma unroll
+        for (int q = 0; q < Q; ++q) a[p + P * q] = twiddle_const<N>(o[q], p * q);
+    }
+    float2 out[N];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        __builtin_amdgcn_sched_barrier(0);
+        float2 t[P], o[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) t[p] = a[p + P * q];
+        Dft<P>::run(t, o);
+#pragma unroll
+        for (int s = 0; s < P; ++s) out[q + Q * s] = o[s];
+    }
+#pragma unroll
+    for (int k = 0; k < N; ++k) a[k] = out[k];
+}
+
 // In-place radix-R DFT of a register array.
 template <int R>
 __device__ __forceinline__ void dft_inplace(float2 *a) {
@@ -155,6 +218,25 @@ __device__ __forceinline__ void dft_inplace(float2 *a) {
 #pragma unroll
     for (int i = 0; i < R; ++i) t[i] = a[i];
     Dft<R>::run(t, a);
+}
+
+// ------------------------------------------------------ uniform addressing
+// Global addresses as a wave-uniform base plus an unsigned 32-bit byte
+// offset, which maps onto the scalar-base addressing form of global loads and
+// stores (no per-lane 64-bit pointers to keep live).
+template <typename V, typename P>
+__device__ __forceinline__ V ldu(const P *base, uint32_t byte_off) {
+    return *reinterpret_cast<const V *>(reinterpret_cast<const char *>(base) + byte_off);
+}
+template <typename V, typename P>
+__device__ __forceinline__ void stu(P *base, uint32_t byte_off, const V &x) {
+    *reinterpret_cast<V *>(reinterpret_cast<char *>(base) + byte_off) = x;
+}
+// Hide a lane value from loop-invariant code motion so that addresses built
+// from it are recomputed where they are used instead of being held live.
+__device__ __forceinline__ int launder(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
 }
 
 // ------------------------------------------------------------ XCD mapping

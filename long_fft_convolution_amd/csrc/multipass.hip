@@ -19,7 +19,10 @@
 //   pass 3  per column n2: conjugate twiddle, inverse DFT over f1 keeping only
 //           n1 < N1/2 (outputs t < N), output gate, store.
 //
-// Workspace: one fp32 complex value per point and sequence of the chunk.
+// Every DFT is split once more into radix stages held in the registers of one
+// lane, with padded (bank-conflict-free) LDS transposes between stages.  All
+// arithmetic is fp32.  Workspace: one fp32 complex value per point and
+// sequence of the chunk.
 #include "fft_device.hpp"
 #include "fft_stages.hpp"
 #include "fftconv_internal.hpp"
@@ -27,12 +30,12 @@
 namespace fftconv {
 
 constexpr int kMpLog2 = 13;                // on-chip row length N2 = 8192
-constexpr int kMpThreads = 256;
+constexpr int kMpThreads = 512;
 
 // omega_N^a for a in [0, N): two-level table lookup (a = hi * 2048 + lo)
 __device__ __forceinline__ float2 tw_big(const float2 *__restrict__ lo, const float2 *__restrict__ hi,
                                          uint32_t a) {
-    return cmul(hi[a >> 11], lo[a & 2047u]);
+    return cmul(ldu<float2>(hi, 8u * (a >> 11)), ldu<float2>(lo, 8u * (a & 2047u)));
 }
 
 struct MpArgs {
@@ -44,232 +47,526 @@ struct MpArgs {
     const float2 *big_hi;   // exp(-2 pi i 2048 j / N), j < N / 2048
 };
 
+// ------------------------------------------------------------ small helpers
+// a[j] *= w^j for j < R (R a power of two, at most 32).  w8 must hold w^8
+// (read from a table) when R > 8, so every factor is a product at most four
+// deep and stays within a few ulp of the exact root of unity.
+template <int R>
+__device__ __forceinline__ void apply_pow(float2 *a, float2 w, float2 w8) {
+    constexpr int R1 = R < 8 ? R : 8;
+    float2 p[R1];
+    p[0] = make_float2(1.f, 0.f);
+    if constexpr (R1 > 1) p[1] = w;
+    if constexpr (R1 > 2) p[2] = cmul(w, w);
+    if constexpr (R1 > 3) p[3] = cmul(p[2], w);
+    if constexpr (R1 > 4) {
+        p[4] = cmul(p[2], p[2]);
+        p[5] = cmul(p[4], w);
+        p[6] = cmul(p[4], p[2]);
+        p[7] = cmul(p[4], p[3]);
+    }
+#pragma unroll
+    for (int i = 1; i < R1; ++i) a[i] = cmul(a[i], p[i]);
+    if constexpr (R > 8) {
+        const float2 w16 = cmul(w8, w8);
+#pragma unroll
+        for (int m = 1; m < R / 8; ++m) {
+            const float2 q = m == 1 ? w8 : (m == 2 ? w16 : cmul(w16, w8));
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a[8 * m + i] = cmul(a[8 * m + i], i == 0 ? q : cmul(q, p[i]));
+        }
+    }
+}
+
+// out[q] = sum_{j < R/2} in[j] omega_R^{jq}, q < R: an R-point DFT whose upper
+// half of inputs is zero.  Even outputs are the R/2-point DFT of in, odd ones
+// that of in[j] omega_R^j.
+template <int R>
+__device__ __forceinline__ void dft_halfzero(const float2 *in, float2 *out) {
+    float2 e[R / 2], o[R / 2], E[R / 2], O[R / 2];
+#pragma unroll
+    for (int j = 0; j < R / 2; ++j) {
+        e[j] = in[j];
+        o[j] = twiddle_const<R>(in[j], j);
+    }
+    Dft<R / 2>::run(e, E);
+    Dft<R / 2>::run(o, O);
+#pragma unroll
+    for (int p = 0; p < R / 2; ++p) {
+        out[2 * p] = E[p];
+        out[2 * p + 1] = O[p];
+    }
+}
+
+// out[q] = sum_{j < R} in[j] omega_R^{jq} for q < R/2 only (decimation in time).
+template <int R>
+__device__ __forceinline__ void dft_halfout(const float2 *in, float2 *out) {
+    float2 e[R / 2], o[R / 2], E[R / 2], O[R / 2];
+#pragma unroll
+    for (int j = 0; j < R / 2; ++j) {
+        e[j] = in[2 * j];
+        o[j] = in[2 * j + 1];
+    }
+    Dft<R / 2>::run(e, E);
+    Dft<R / 2>::run(o, O);
+#pragma unroll
+    for (int q = 0; q < R / 2; ++q) out[q] = cadd(E[q], twiddle_const<R>(O[q], q));
+}
+
+// ------------------------------------------------------------ column plan
+// The N1-point column DFT of passes 1 and 3 is split as N1 = RB * RA with
+// n1 = n_a + RA n_b, f1 = f_b + RB f_a.  A workgroup of 512 lanes owns C
+// adjacent columns; lane (col, j) = (tid % C, tid / C), j < RA.  The RB * RA
+// intermediate values per column pass through LDS in NG groups of RA values
+// of f_b, so a workgroup holds at most 64 KiB of LDS and two fit on a CU.
+template <int LOG1> struct ColPlan {
+    static constexpr int N1 = 1 << LOG1;
+    static constexpr int RB = 1 << ((LOG1 + 1) / 2);
+    static constexpr int RA = N1 / RB;
+    static constexpr int C = kMpThreads / RA;
+    static constexpr int NG = RB / RA;
+    static constexpr size_t kLds = (size_t)RA * RA * C * sizeof(float2);
+    static_assert(RA >= 2 && RB <= 32 && (NG == 1 || NG == 2), "column plan");
+};
+
+// a[fa] *= omega_N^{n2 (fb + RB fa)} for fa < RA
+template <int RA, int RB>
+__device__ __forceinline__ void column_twiddle(float2 *a, uint32_t n2, uint32_t fb, uint32_t nmask,
+                                               const MpArgs &ta) {
+    const float2 base = tw_big(ta.big_lo, ta.big_hi, (n2 * fb) & nmask);
+    const float2 step = tw_big(ta.big_lo, ta.big_hi, (n2 * (uint32_t)RB) & nmask);
+    const float2 step8 = tw_big(ta.big_lo, ta.big_hi, (n2 * (uint32_t)(8 * RB)) & nmask);
+#pragma unroll
+    for (int i = 0; i < RA; ++i) a[i] = cmul(a[i], base);
+    apply_pow<RA>(a, step, step8);
+}
+
 // ---------------------------------------------------------------- pass 1
-// grid (N2 / NCOL, nseq); block 256.  SRC_FILTER: input is the filter row
+// grid (N2 / C, nseq); block 512.  SRC_FILTER: input is the filter row
 // k[h, :L] (prepare); else u * w of sequence seq0 + blockIdx.y.
 template <int LOG1, typename T, bool SRC_FILTER>
-__global__ void __launch_bounds__(kMpThreads)
+__global__ void __launch_bounds__(kMpThreads, 4)
 mp_pass1_kernel(const T *__restrict__ src, const T *__restrict__ gate, int64_t L, int64_t seq0,
                 float2 *__restrict__ ws, MpArgs ta) {
-    using Pl = LdsFftPlan<LOG1>;
-    constexpr int N1 = 1 << LOG1, N2 = 1 << kMpLog2;
+    using P = ColPlan<LOG1>;
+    constexpr int N1 = P::N1, RA = P::RA, RB = P::RB, C = P::C, N2 = 1 << kMpLog2;
     constexpr int64_t NC = (int64_t)N1 * N2;
-    constexpr int TS = Pl::TS, NCOL = kMpThreads / TS, STRIDE = N1 + 1;
     extern __shared__ float2 lds[];
     const int tid = threadIdx.x;
-    const int c0 = blockIdx.x * NCOL;
+    const int col = tid % C, j = tid / C;
+    const int c0 = blockIdx.x * C;
+    const uint32_t n2 = (uint32_t)(c0 + col);
     const int64_t s = seq0 + blockIdx.y;
     const T *row = src + s * (SRC_FILTER ? L : NC);
     const T *grow = (!SRC_FILTER && gate != nullptr) ? gate + s * NC : nullptr;
 
-    // load rows n1 < N1/2 (coalesced along n2), zero the rest
-    for (int idx = tid; idx < N1 * NCOL; idx += kMpThreads) {
-        const int n1 = idx / NCOL, col = idx % NCOL;
-        float2 z = make_float2(0.f, 0.f);
-        if (n1 < N1 / 2) {
-            const int64_t m = (int64_t)(c0 + col) + (int64_t)N2 * n1;
+    // stage 1: lane (col, n_a = j), RB-point DFT over n_b (upper half zero).
+    // Element m = n2 + N2 (j + RA n_b): uniform part c0 + N2 RA n_b, lane part
+    // col + N2 j.
+    const uint32_t lo = (uint32_t)(col + N2 * j);
+    float2 y[RB];
+    {
+        float2 z[RB / 2];
+#pragma unroll
+        for (int nb = 0; nb < RB / 2; ++nb) {
+            const int64_t mu = (int64_t)c0 + (int64_t)N2 * RA * nb;
+            float2 t = make_float2(0.f, 0.f);
             if (SRC_FILTER) {
-                if (2 * m < L) z.x = io<T>::load1(row + 2 * m);
-                if (2 * m + 1 < L) z.y = io<T>::load1(row + 2 * m + 1);
+                const int64_t m = mu + lo;
+                if (2 * m < L) t.x = io<T>::load1(row + 2 * m);
+                if (2 * m + 1 < L) t.y = io<T>::load1(row + 2 * m + 1);
             } else {
-                z = io<T>::load2(row + 2 * m);
+                t = io<T>::load2(row + 2 * mu, lo);
                 if (grow != nullptr) {
-                    const float2 g = io<T>::load2(grow + 2 * m);
-                    z = make_float2(z.x * g.x, z.y * g.y);
+                    const float2 g = io<T>::load2(grow + 2 * mu, lo);
+                    t = make_float2(t.x * g.x, t.y * g.y);
                 }
             }
+            z[nb] = t;
         }
-        lds[col * STRIDE + n1] = z;
+        dft_halfzero<RB>(z, y);
     }
-    __syncthreads();
-    fft_lds<LOG1>(lds + (tid / TS) * STRIDE, tid % TS, ta.tw1);
-    float2 *out = ws + blockIdx.y * NC;
-    for (int idx = tid; idx < N1 * NCOL; idx += kMpThreads) {
-        const int f1 = idx / NCOL, col = idx % NCOL;
-        const uint32_t n2 = (uint32_t)(c0 + col);
-        const uint32_t a = (uint32_t)(((uint64_t)n2 * (uint64_t)f1) & (uint64_t)(NC - 1));
-        out[(int64_t)f1 * N2 + n2] = cmul(lds[col * STRIDE + f1], tw_big(ta.big_lo, ta.big_hi, a));
-    }
-}
+    apply_pow<RB>(y, ldu<float2>(ta.tw1, 8u * j), ldu<float2>(ta.tw1, 8u * ((8 * j) & (N1 - 1))));
 
-// ---------------------------------------------------------------- pass 2
-// One work item of the bin-pair step in a row-pair workgroup.  Rows A, B in
-// LDS (natural order after the row FFTs).  Workgroup 0 holds rows 0 and N1/2
-// (each paired with itself); the others rows f1 and N1 - f1.
-struct PairItem {
-    int ia, ib;       // LDS indices of the two bins (ib == ia: single)
-    int64_t f, g;     // bins (g = N - f; f == 0 uses K[N] as partner)
-};
-
-template <int N1, int N2>
-__device__ __forceinline__ bool pair_item(int w, int f1, PairItem &it) {
-    constexpr int64_t NC = (int64_t)N1 * N2;
-    if (f1 != 0) {
-        if (w >= N2) return false;
-        it.ia = w;
-        it.ib = N2 + (N2 - 1 - w);
-        it.f = f1 + (int64_t)N1 * w;
-        it.g = NC - it.f;
-        return true;
-    }
-    if (w < N2 / 2) {                      // row N1/2 (LDS row B): f2 <-> N2 - 1 - f2
-        it.ia = N2 + w;
-        it.ib = N2 + (N2 - 1 - w);
-        it.f = N1 / 2 + (int64_t)N1 * w;
-        it.g = NC - it.f;
-        return true;
-    }
-    if (w < N2) {                          // row 0 (LDS row A): f2 <-> N2 - f2
-        const int f2 = w - N2 / 2;
-        it.ia = f2;
-        it.ib = f2 == 0 ? 0 : N2 - f2;
-        it.f = (int64_t)N1 * f2;
-        it.g = f2 == 0 ? 0 : NC - it.f;
-        return true;
-    }
-    if (w == N2) {                         // f = N/2, paired with itself
-        it.ia = it.ib = N2 / 2;
-        it.f = it.g = NC / 2;
-        return true;
-    }
-    return false;
-}
-
-template <int N1, int N2>
-__device__ __forceinline__ int64_t kslot(int64_t f) {
-    return (f % N1) * N2 + f / N1;       // row-major (f1, f2); f = 0 -> slot 0
-}
-
-template <int N1, int N2>
-__device__ __forceinline__ float2 omega2n(int64_t f, const MpArgs &ta) {
-    return cmul(ta.w2row[f % N1], ta.w2n2[f / N1]);
-}
-
-// grid (N1 / 2, nseq); block 512 (256 lanes per row).  PREPARE: forward only,
-// writes the filter spectrum; else the full filter product and inverse rows.
-template <int LOG1, typename TK, bool PREPARE>
-__global__ void __launch_bounds__(2 * kMpThreads)
-mp_pass2_kernel(float2 *__restrict__ ws, const TK *__restrict__ kbins_in, TK *__restrict__ kbins_out,
-                const float *__restrict__ kscale, const uint8_t *__restrict__ mask, int64_t H,
-                int64_t seq0, MpArgs ta) {
-    constexpr int N1 = 1 << LOG1, N2 = 1 << kMpLog2;
-    constexpr int64_t NC = (int64_t)N1 * N2;
-    constexpr int TS = LdsFftPlan<kMpLog2>::TS;   // 256
-    extern __shared__ float2 lds[];
-    const int tid = threadIdx.x;
-    const int f1 = blockIdx.x;
-    const int rowA = f1, rowB = f1 == 0 ? N1 / 2 : N1 - f1;
-    const int64_t s = seq0 + blockIdx.y;
-    const int64_t h = s % H;
-    float2 *wsq = ws + blockIdx.y * NC;
-
-    for (int i = tid; i < N2; i += 2 * kMpThreads) {
-        lds[i] = wsq[(int64_t)rowA * N2 + i];
-        lds[N2 + i] = wsq[(int64_t)rowB * N2 + i];
-    }
-    __syncthreads();
-    fft_lds<kMpLog2>(lds + (tid / TS) * N2, tid % TS, ta.tw2);
-
-    const float ks = kscale[h];
-    if (PREPARE) {
-        const float sh = 1.0f / (ks * 4.0f * (float)NC);
-        TK *krow = kbins_out + h * NC;
-        for (int w = tid; w <= N2; w += 2 * kMpThreads) {
-            PairItem it;
-            if (!pair_item<N1, N2>(w, f1, it)) continue;
-            const float2 zf = lds[it.ia], zg = lds[it.ib];
-            const float2 bc = cconj(zg);
-            const float2 xe = cadd(zf, bc);
-            const float2 xo = cmul_negi(csub(zf, bc));
-            const float2 wxo = cmul(it.f == 0 ? make_float2(1.f, 0.f) : omega2n<N1, N2>(it.f, ta), xo);
-            const float2 xf = cscale(cadd(xe, wxo), 0.5f * sh);
-            const float2 xg = cscale(cconj(csub(xe, wxo)), 0.5f * sh);
-            if (it.f == 0) {
-                kio<TK>::store(krow, make_float2(xf.x, xg.x));   // (X[0], X[N])
-            } else {
-                kio<TK>::store(krow + kslot<N1, N2>(it.f), xf);
-                if (it.ib != it.ia) kio<TK>::store(krow + kslot<N1, N2>(it.g), xg);
-            }
-        }
-        return;
-    }
-
-    const TK *krow = kbins_in + h * NC;
-    const uint8_t *mrow = mask != nullptr ? mask + h * kMaskBlocks : nullptr;
-    constexpr int64_t G = NC / kMaskBlocks;
-    auto kval = [&](int64_t f) -> float2 {
-        float2 k = cscale(kio<TK>::load(krow + kslot<N1, N2>(f)), ks);
-        if (mrow != nullptr && !mrow[f / G]) k = make_float2(0.f, 0.f);
-        return k;
-    };
-    for (int w = tid; w <= N2; w += 2 * kMpThreads) {
-        PairItem it;
-        if (!pair_item<N1, N2>(w, f1, it)) continue;
-        float2 zf = lds[it.ia], zg = lds[it.ib];
-        float2 Kf, Kg, Wf;
-        if (it.f == 0) {
-            float2 k0 = cscale(kio<TK>::load(krow), ks);
-            float a = k0.x, b = k0.y;
-            if (mrow != nullptr) {
-                if (!mrow[0]) a = 0.f;
-                if (!mrow[kMaskBlocks - 1]) b = 0.f;
-            }
-            Kf = make_float2(a, 0.f);
-            Kg = make_float2(b, 0.f);
-            Wf = make_float2(1.f, 0.f);
-        } else {
-            Kf = kval(it.f);
-            Kg = it.ib == it.ia ? Kf : kval(it.g);
-            Wf = omega2n<N1, N2>(it.f, ta);
-        }
-        middle_pair(zf, zg, Kf, Kg, Wf);
-        lds[it.ia] = zf;
-        if (it.ib != it.ia) lds[it.ib] = zg;
-    }
-    __syncthreads();
-    fft_lds<kMpLog2>(lds + (tid / TS) * N2, tid % TS, ta.tw2);
-    // rows now hold conj of the inverse row transform; pass 3 undoes the conj
-    for (int i = tid; i < N2; i += 2 * kMpThreads) {
-        wsq[(int64_t)rowA * N2 + i] = lds[i];
-        wsq[(int64_t)rowB * N2 + i] = lds[N2 + i];
+    float2 *out = ws + (int64_t)blockIdx.y * NC;
+#pragma unroll
+    for (int g = 0; g < P::NG; ++g) {
+#pragma unroll
+        for (int i = 0; i < RA; ++i) lds[(i * RA + j) * C + col] = y[g * RA + i];
+        __syncthreads();
+        // stage 2: lane (col, f_b = g RA + j), RA-point DFT over n_a
+        float2 a[RA];
+#pragma unroll
+        for (int i = 0; i < RA; ++i) a[i] = lds[(j * RA + i) * C + col];
+        dft_inplace<RA>(a);
+        const uint32_t fb = (uint32_t)(g * RA + j);
+        column_twiddle<RA, RB>(a, n2, fb, (uint32_t)(NC - 1), ta);
+        // row fb + RB f_a: uniform part (g RA + RB f_a) N2 + c0, lane part j N2 + col
+        const uint32_t so = 8u * (uint32_t)(launder(j) * N2 + launder(col));
+#pragma unroll
+        for (int fa = 0; fa < RA; ++fa) stu(out + (int64_t)(g * RA + RB * fa) * N2 + c0, so, a[fa]);
+        if (g + 1 < P::NG) __syncthreads();
     }
 }
 
 // ---------------------------------------------------------------- pass 3
 template <int LOG1, typename T>
-__global__ void __launch_bounds__(kMpThreads)
+__global__ void __launch_bounds__(kMpThreads, 4)
 mp_pass3_kernel(const float2 *__restrict__ ws, const T *__restrict__ v, T *__restrict__ out,
                 int64_t seq0, MpArgs ta) {
-    using Pl = LdsFftPlan<LOG1>;
-    constexpr int N1 = 1 << LOG1, N2 = 1 << kMpLog2;
+    using P = ColPlan<LOG1>;
+    constexpr int N1 = P::N1, RA = P::RA, RB = P::RB, C = P::C, N2 = 1 << kMpLog2;
     constexpr int64_t NC = (int64_t)N1 * N2;
-    constexpr int TS = Pl::TS, NCOL = kMpThreads / TS, STRIDE = N1 + 1;
     extern __shared__ float2 lds[];
     const int tid = threadIdx.x;
-    const int c0 = blockIdx.x * NCOL;
+    const int col = tid % C, j = tid / C;
+    const int c0 = blockIdx.x * C;
+    const uint32_t n2 = (uint32_t)(c0 + col);
     const int64_t s = seq0 + blockIdx.y;
-    const float2 *wsq = ws + blockIdx.y * NC;
-    for (int idx = tid; idx < N1 * NCOL; idx += kMpThreads) {
-        const int f1 = idx / NCOL, col = idx % NCOL;
-        const uint32_t n2 = (uint32_t)(c0 + col);
-        const uint32_t a = (uint32_t)(((uint64_t)n2 * (uint64_t)f1) & (uint64_t)(NC - 1));
-        // stored value is conj(b); conj(b * w^-a) = conj(b) * w^a
-        lds[col * STRIDE + f1] = cmul(wsq[(int64_t)f1 * N2 + n2], tw_big(ta.big_lo, ta.big_hi, a));
+    const float2 *wsq = ws + (int64_t)blockIdx.y * NC;
+    const uint32_t lo = (uint32_t)(col + N2 * j);
+
+    float2 acc[RB];      // lane (col, n_a = j): all f_b
+#pragma unroll
+    for (int g = 0; g < P::NG; ++g) {
+        // stage 1: lane (col, f_b = g RA + j), RA-point DFT over f_a.  The
+        // stored rows are conj(b); conj(b omega^-a) = conj(b) omega^a.
+        const uint32_t fb = (uint32_t)(g * RA + j);
+        float2 a[RA];
+#pragma unroll
+        for (int fa = 0; fa < RA; ++fa) a[fa] = ldu<float2>(wsq + (int64_t)(g * RA + RB * fa) * N2 + c0, 8u * lo);
+        column_twiddle<RA, RB>(a, n2, fb, (uint32_t)(NC - 1), ta);
+        dft_inplace<RA>(a);
+        apply_pow<RA>(a, ldu<float2>(ta.tw1, 8u * fb), ldu<float2>(ta.tw1, 8u * ((8 * fb) & (N1 - 1))));
+        if (g > 0) __syncthreads();
+#pragma unroll
+        for (int i = 0; i < RA; ++i) lds[(j * RA + i) * C + col] = a[i];
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < RA; ++i) acc[g * RA + i] = lds[(i * RA + j) * C + col];
     }
-    __syncthreads();
-    fft_lds<LOG1>(lds + (tid / TS) * STRIDE, tid % TS, ta.tw1);
+    // stage 2: RB-point DFT over f_b, outputs n_b < RB/2 only (t < N)
+    float2 r[RB / 2];
+    dft_halfout<RB>(acc, r);
     const T *vrow = v != nullptr ? v + s * NC : nullptr;
     T *orow = out + s * NC;
-    for (int idx = tid; idx < (N1 / 2) * NCOL; idx += kMpThreads) {
-        const int n1 = idx / NCOL, col = idx % NCOL;
-        const int64_t m = (int64_t)(c0 + col) + (int64_t)N2 * n1;
-        const float2 r = lds[col * STRIDE + n1];
-        float2 y = make_float2(r.x, -r.y);
+    const uint32_t lo2 = (uint32_t)(launder(col) + N2 * launder(j));
+#pragma unroll
+    for (int nb = 0; nb < RB / 2; ++nb) {
+        const int64_t mu = (int64_t)c0 + (int64_t)N2 * RA * nb;
+        float2 y = make_float2(r[nb].x, -r[nb].y);
         if (vrow != nullptr) {
-            const float2 g = io<T>::load2(vrow + 2 * m);
+            const float2 g = io<T>::load2(vrow + 2 * mu, lo2);
             y = make_float2(y.x * g.x, y.y * g.y);
         }
-        io<T>::store2(orow + 2 * m, y);
+        io<T>::store2(orow + 2 * mu, lo2, y);
+    }
+}
+
+// ---------------------------------------------------------------- pass 2
+// One row of N2 = 8192 points: n2 = n_a + 256 n_b, n_a = n_c + 16 n_d and
+// k = k_b + 32 k_d + 512 k_c (k = f2, the in-row bin):
+//   A  per n_a:        32-point DFT over n_b, twiddle omega_8192^{n_a k_b}
+//   B  per (n_c, k_b): 16-point DFT over n_d, twiddle omega_256^{n_c k_d}
+//   C  per (k_b, k_d): 16-point DFT over n_c
+// The inverse runs the same stages in reverse order on conjugated data.
+//
+// Lanes: stage A (row ra = tid >> 8, n_a = tid & 255); stage B
+// (k_b0 = tid & 31, n_c = tid >> 5) holding row A at k_b0 and row B at
+// k_b0 ^ 16; stage C (k_b = tid & 31, k_d = tid >> 5) holding row A at
+// (k_b, k_d) and row B at (31 - k_b, 15 - k_d), so that every bin pair of the
+// bin-pair step sits in one lane.
+//
+// Two rows do not fit in the LDS share of a workgroup (two workgroups per
+// CU), so each transpose runs in two rounds that move half of the data:
+//   T1 round h: k_b in [16h, 16h + 16) of both rows,
+//               slot (r, k_b & 15, n_a) -> (16 r + (k_b & 15)) * 257 + n_a
+//   T2 round h: k_d in [8h, 8h + 8) of both rows,
+//               slot (r, k_b, k_d, n_c) -> (32 r + k_b) * 129 + 16 r + 16 (k_d & 7) + n_c
+// In every round each lane writes 16 values and reads 16, and the odd
+// strides keep the 32 lanes of each half-wave on distinct LDS banks.
+constexpr int kT1Row = 257;
+constexpr int kT2Row = 129;
+constexpr int kP2LdsFloat2 = 64 * kT2Row + 16 + 128;
+constexpr size_t kP2Lds = (size_t)kP2LdsFloat2 * sizeof(float2) + kMaskBlocks;
+static_assert(kP2LdsFloat2 >= 32 * kT1Row && kP2LdsFloat2 >= 8192, "pass-2 LDS");
+
+// Bin pairs of the workgroup that holds rows 0 and N1/2: each row pairs with
+// itself (row 0: f2 <-> N2 - f2; row N1/2: f2 <-> N2 - 1 - f2).  The row
+// sits in LDS in natural order; lanes take the pairs in turn.
+template <int N1, int N2, typename TK, bool PREPARE, bool MASKED>
+__device__ __forceinline__ void self_pairs(float2 *row, bool half_row, const TK *__restrict__ krow,
+                                           TK *__restrict__ kout, const uint8_t *smask, float ks,
+                                           const MpArgs &ta, int tid) {
+    constexpr int64_t NC = (int64_t)N1 * N2;
+    const int rbase = half_row ? N1 / 2 : 0;
+    const float2 wrow = half_row ? ta.w2row[N1 / 2] : make_float2(1.f, 0.f);
+    const float sh = 1.0f / (ks * 4.0f * (float)NC);
+    for (int w = tid; w <= N2 / 2; w += kMpThreads) {
+        if (half_row && w == N2 / 2) break;
+        const int ia = w;
+        const int ib = half_row ? N2 - 1 - w : (w == 0 ? 0 : N2 - w);
+        const int64_t sa = (int64_t)rbase * N2 + ia, sb = (int64_t)rbase * N2 + ib;
+        float2 zf = row[ia], zg = row[ib];
+        const bool dc = !half_row && w == 0;   // f = 0: (K[0], K[N]) share slot 0
+        const float2 Wf = dc ? make_float2(1.f, 0.f) : cmul(wrow, ta.w2n2[w]);
+        if (PREPARE) {
+            const float2 bc = cconj(zg);
+            const float2 xe = cadd(zf, bc);
+            const float2 xo = cmul_negi(csub(zf, bc));
+            const float2 wxo = cmul(Wf, xo);
+            const float2 xf = cscale(cadd(xe, wxo), 0.5f * sh);
+            const float2 xg = cscale(cconj(csub(xe, wxo)), 0.5f * sh);
+            if (dc) {
+                kio<TK>::store(kout, make_float2(xf.x, xg.x));
+            } else {
+                kio<TK>::store(kout + sa, xf);
+                if (ib != ia) kio<TK>::store(kout + sb, xg);
+            }
+            continue;
+        }
+        float2 Kf, Kg;
+        if (dc) {
+            const float2 k0 = cscale(kio<TK>::load(krow), ks);
+            Kf = make_float2(MASKED && !smask[0] ? 0.f : k0.x, 0.f);
+            Kg = make_float2(MASKED && !smask[kMaskBlocks - 1] ? 0.f : k0.y, 0.f);
+        } else {
+            Kf = (MASKED && !smask[ia >> 6]) ? make_float2(0.f, 0.f) : cscale(kio<TK>::load(krow + sa), ks);
+            Kg = (MASKED && !smask[ib >> 6]) ? make_float2(0.f, 0.f) : cscale(kio<TK>::load(krow + sb), ks);
+        }
+        middle_pair(zf, zg, Kf, Kg, Wf);
+        row[ia] = zf;
+        if (ib != ia) row[ib] = zg;
+    }
+}
+
+// grid (N1 / 2, nseq); block 512.  PREPARE: forward only, writes the filter
+// spectrum; else the full filter product and inverse rows.
+template <int LOG1, typename TK, bool PREPARE, bool MASKED>
+__global__ void __launch_bounds__(kMpThreads, 4)
+mp_pass2_kernel(float2 *__restrict__ ws, const TK *__restrict__ kbins_in, TK *__restrict__ kbins_out,
+                const float *__restrict__ kscale, const uint8_t *__restrict__ mask, int64_t H,
+                int64_t seq0, MpArgs ta) {
+    constexpr int N1 = 1 << LOG1, N2 = 1 << kMpLog2;
+    constexpr int64_t NC = (int64_t)N1 * N2;
+    extern __shared__ float2 lds[];
+    uint8_t *smask = reinterpret_cast<uint8_t *>(lds + kP2LdsFloat2);
+    const int tid = threadIdx.x;
+    const int f1 = blockIdx.x;
+    const int rowA = f1, rowB = f1 == 0 ? N1 / 2 : N1 - f1;
+    const int64_t s = seq0 + blockIdx.y;
+    const int64_t h = s % H;
+    float2 *wsq = ws + (int64_t)blockIdx.y * NC;
+    const float2 *tw = ta.tw2;
+    if (MASKED && tid < kMaskBlocks / 4)
+        reinterpret_cast<uint32_t *>(smask)[tid] = reinterpret_cast<const uint32_t *>(mask + h * kMaskBlocks)[tid];
+
+    // ---- stage A: lane (row ra, n_a)
+    const int ra = __builtin_amdgcn_readfirstlane(tid >> 8), na = tid & 255;
+    float2 *rowp = wsq + (int64_t)(ra ? rowB : rowA) * N2;
+    float2 a[32];
+#pragma unroll
+    for (int nb = 0; nb < 32; ++nb) a[nb] = ldu<float2>(rowp + 256 * nb, 8u * na);
+    dft_pq<8, 4>(a);
+    apply_pow<32>(a, ldu<float2>(tw, 8u * na), ldu<float2>(tw, 64u * na));
+
+    // ---- T1, stage B.  p[q] receives, in round q, the row whose k_b lies in
+    // half q: row (q ^ hb0) at k_b = 16 q + kl0.
+    const int kb0 = tid & 31, ncB = tid >> 5, kl0 = kb0 & 15, hb0 = kb0 >> 4;
+    float2 p[2][16];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+#pragma unroll
+        for (int kl = 0; kl < 16; ++kl) lds[(16 * ra + kl) * kT1Row + na] = a[16 * q + kl];
+        __syncthreads();
+        const int r = q ^ hb0;
+#pragma unroll
+        for (int nd = 0; nd < 16; ++nd) p[q][nd] = lds[(16 * r + kl0) * kT1Row + ncB + 16 * nd];
+        __syncthreads();
+    }
+    {
+        const float2 w = ldu<float2>(tw, 256u * ncB), w8 = ldu<float2>(tw, 2048u * ncB);
+        dft_pq<4, 4>(p[0]);
+        dft_pq<4, 4>(p[1]);
+        apply_pow<16>(p[0], w, w8);
+        apply_pow<16>(p[1], w, w8);
+    }
+
+    // ---- T2, stage C.  The lanes of waves 0-3 (hiw = 0) have k_d < 8: they
+    // take row A in round 0 and row B in round 1; waves 4-7 the other way.
+    const int kbC = tid & 31, kdC = tid >> 5, hiw = tid >> 8;
+    const int t2p0 = (32 * hb0 + kl0) * kT2Row + 16 * hb0 + ncB;
+    const int t2p1 = (32 * (1 - hb0) + 16 + kl0) * kT2Row + 16 * (1 - hb0) + ncB;
+    const int t2a = kbC * kT2Row + 16 * (kdC & 7);
+    const int t2b = (63 - kbC) * kT2Row + 16 + 16 * ((15 - kdC) & 7);
+    // (reads go to per-round arrays and are renamed by value afterwards: a
+    // branch that fills cA or cB would be merged into a store through a
+    // selected array pointer, which forces both arrays out of registers)
+    float2 rd[2][16];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            lds[t2p0 + 16 * i] = p[0][8 * q + i];
+            lds[t2p1 + 16 * i] = p[1][8 * q + i];
+        }
+        __syncthreads();
+        const int src = hiw == q ? t2a : t2b;
+#pragma unroll
+        for (int n = 0; n < 16; ++n) rd[q][n] = lds[src + n];
+        __syncthreads();
+    }
+    float2 cA[16], cB[16];
+#pragma unroll
+    for (int n = 0; n < 16; ++n) {
+        cA[n] = hiw ? rd[1][n] : rd[0][n];
+        cB[n] = hiw ? rd[0][n] : rd[1][n];
+    }
+    dft_pq<4, 4>(cA);
+    dft_pq<4, 4>(cB);
+    // cA[kc] = Z of row A at bin kbC + 32 kdC + 512 kc
+    // cB[kc] = Z of row B at bin (31 - kbC) + 32 (15 - kdC) + 512 kc
+
+    // ---- bin-pair step
+    const float ks = kscale[h];
+    const int kq = kbC + 32 * kdC;
+    if (f1 != 0) {
+        // row A bin k pairs with row B bin 8191 - k: both in this lane
+        const float2 wb = cmul(ta.w2row[f1], ldu<float2>(ta.w2n2, 8u * kq));
+        if (PREPARE) {
+            const float sh = 1.0f / (ks * 4.0f * (float)NC);
+            TK *ka = kbins_out + h * NC + (int64_t)rowA * N2;
+            TK *kb = kbins_out + h * NC + (int64_t)rowB * N2;
+#pragma unroll
+            for (int kc = 0; kc < 16; ++kc) {
+                const int k = kq + 512 * kc;
+                const float2 zf = cA[kc], zg = cB[15 - kc];
+                const float2 Wf = twiddle_const<32>(wb, kc);
+                const float2 bc = cconj(zg);
+                const float2 xe = cadd(zf, bc);
+                const float2 xo = cmul_negi(csub(zf, bc));
+                const float2 wxo = cmul(Wf, xo);
+                // bin N2 - 1 - k: uniform part N2 - 512 (kc + 1), lane part 511 - kq
+                kio<TK>::store(ka + 512 * kc, (uint32_t)kq, cscale(cadd(xe, wxo), 0.5f * sh));
+                kio<TK>::store(kb + N2 - 512 * (kc + 1), (uint32_t)(511 - kq),
+                               cscale(cconj(csub(xe, wxo)), 0.5f * sh));
+            }
+            return;
+        }
+        const TK *ka = kbins_in + h * NC + (int64_t)rowA * N2;
+        const TK *kb = kbins_in + h * NC + (int64_t)rowB * N2;
+        // two batches of eight bin pairs; the scheduling barriers keep the
+        // second batch of filter loads from being hoisted over the first
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            float2 Kf[8], Kg[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int kc = 8 * half + i, k = kq + 512 * kc;
+                Kf[i] = make_float2(0.f, 0.f);
+                Kg[i] = make_float2(0.f, 0.f);
+                // the mask block of bin k is k >> 6 (uniform over the wave)
+                if (!MASKED || smask[k >> 6]) Kf[i] = kio<TK>::load(ka + 512 * kc, (uint32_t)kq);
+                if (!MASKED || smask[(N2 - 1 - k) >> 6])
+                    Kg[i] = kio<TK>::load(kb + N2 - 512 * (kc + 1), (uint32_t)(511 - kq));
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int kc = 8 * half + i;
+                float2 zf = cA[kc], zg = cB[15 - kc];
+                middle_pair(zf, zg, cscale(Kf[i], ks), cscale(Kg[i], ks), twiddle_const<32>(wb, kc));
+                cA[kc] = zf;
+                cB[15 - kc] = zg;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+        // rows 0 and N1/2 pair with themselves: one row at a time in LDS
+        const TK *krow = PREPARE ? nullptr : kbins_in + h * NC;
+        TK *kout = PREPARE ? kbins_out + h * NC : nullptr;
+        const int qa = kq, qb = (31 - kbC) + 32 * (15 - kdC);
+#pragma unroll
+        for (int kc = 0; kc < 16; ++kc) lds[qa + 512 * kc] = cA[kc];
+        __syncthreads();
+        self_pairs<N1, N2, TK, PREPARE, MASKED>(lds, false, krow, kout, smask, ks, ta, tid);
+        __syncthreads();
+        if (!PREPARE) {
+#pragma unroll
+            for (int kc = 0; kc < 16; ++kc) cA[kc] = lds[qa + 512 * kc];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kc = 0; kc < 16; ++kc) lds[qb + 512 * kc] = cB[kc];
+        __syncthreads();
+        self_pairs<N1, N2, TK, PREPARE, MASKED>(lds, true, krow, kout, smask, ks, ta, tid);
+        __syncthreads();
+        if (PREPARE) return;
+#pragma unroll
+        for (int kc = 0; kc < 16; ++kc) cB[kc] = lds[qb + 512 * kc];
+        __syncthreads();
+    }
+    // cA, cB now hold conj(Z') in the same layout; the forward transform of
+    // conjugated data is the conjugated inverse transform.  Lane indices are
+    // recomputed from a laundered thread id so that no address is held live
+    // across the bin-pair step.
+    __builtin_amdgcn_sched_barrier(0);
+    {
+    const int tid2 = launder(tid);
+    const int kbC = tid2 & 31, kdC = tid2 >> 5, kb0 = tid2 & 31, ncB = tid2 >> 5, kl0 = kb0 & 15,
+              hb0 = kb0 >> 4, na = tid2 & 255;
+    const int t2p0 = (32 * hb0 + kl0) * kT2Row + 16 * hb0 + ncB;
+    const int t2p1 = (32 * (1 - hb0) + 16 + kl0) * kT2Row + 16 * (1 - hb0) + ncB;
+    const int t2a = kbC * kT2Row + 16 * (kdC & 7);
+    const int t2b = (63 - kbC) * kT2Row + 16 + 16 * ((15 - kdC) & 7);
+
+    // ---- stage C' (over k_c -> n_c), twiddle omega_256^{n_c k_d}
+    dft_pq<4, 4>(cA);
+    dft_pq<4, 4>(cB);
+    apply_pow<16>(cA, ldu<float2>(tw, 256u * kdC), ldu<float2>(tw, 2048u * kdC));
+    apply_pow<16>(cB, ldu<float2>(tw, 256u * (15 - kdC)), ldu<float2>(tw, 2048u * (15 - kdC)));
+
+    // ---- T2' (T2 backwards), stage B' (over k_d -> n_d), twiddle
+    // omega_8192^{(n_c + 16 n_d) k_b}; p[q] is at k_b = 16 q + kl0
+    const int hiw = tid2 >> 8;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int dst = hiw == q ? t2a : t2b;
+#pragma unroll
+        for (int n = 0; n < 16; ++n) lds[dst + n] = hiw == q ? cA[n] : cB[n];
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            p[0][8 * q + i] = lds[t2p0 + 16 * i];
+            p[1][8 * q + i] = lds[t2p1 + 16 * i];
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int kb = 16 * q + kl0;
+        dft_pq<4, 4>(p[q]);
+        const float2 base = ldu<float2>(tw, 8u * (ncB * kb));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) p[q][i] = cmul(p[q][i], base);
+        apply_pow<16>(p[q], ldu<float2>(tw, 128u * kb), ldu<float2>(tw, 1024u * kb));
+    }
+
+    // ---- T1' (T1 backwards), stage A' (over k_b -> n_b), store
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int r = q ^ hb0;
+#pragma unroll
+        for (int nd = 0; nd < 16; ++nd) lds[(16 * r + kl0) * kT1Row + ncB + 16 * nd] = p[q][nd];
+        __syncthreads();
+#pragma unroll
+        for (int kl = 0; kl < 16; ++kl) a[16 * q + kl] = lds[(16 * ra + kl) * kT1Row + na];
+        __syncthreads();
+    }
+    dft_pq<8, 4>(a);
+    // rows now hold conj of the inverse row transform; pass 3 undoes the conj
+    const uint32_t so = 8u * (uint32_t)launder(tid & 255);
+#pragma unroll
+    for (int nb = 0; nb < 32; ++nb) stu(rowp + 256 * nb, so, a[nb]);
     }
 }
 
@@ -292,12 +589,6 @@ static hipError_t mp_args(int logn, MpArgs *a) {
     return hipSuccess;
 }
 
-template <int LOG1>
-static size_t lds_cols() {
-    using Pl = LdsFftPlan<LOG1>;
-    return (size_t)(kMpThreads / Pl::TS) * ((1 << LOG1) + 1) * sizeof(float2);
-}
-
 template <typename K>
 static hipError_t allow_lds(K kern, size_t bytes) {
     return hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -308,25 +599,27 @@ template <int LOG1, typename T, typename TK>
 static hipError_t conv_t(const void *u, const void *w, const void *v, void *out, const void *kbins,
                          const float *kscale, const uint8_t *mask, void *work, int64_t H,
                          int64_t seq0, int64_t nseq, hipStream_t stream) {
-    constexpr int N2 = 1 << kMpLog2, NCOL = kMpThreads / LdsFftPlan<LOG1>::TS;
+    using P = ColPlan<LOG1>;
+    constexpr int N2 = 1 << kMpLog2;
     MpArgs ta{};
     hipError_t e = mp_args(LOG1 + kMpLog2, &ta);
     if (e != hipSuccess) return e;
     float2 *ws = (float2 *)work;
-    const size_t l1 = lds_cols<LOG1>(), l2 = 2 * (size_t)N2 * sizeof(float2);
     auto k1 = mp_pass1_kernel<LOG1, T, false>;
-    auto k2 = mp_pass2_kernel<LOG1, TK, false>;
+    auto k2m = mp_pass2_kernel<LOG1, TK, false, true>;
+    auto k2u = mp_pass2_kernel<LOG1, TK, false, false>;
+    auto k2 = mask != nullptr ? k2m : k2u;
     auto k3 = mp_pass3_kernel<LOG1, T>;
-    if ((e = allow_lds(k1, l1)) != hipSuccess) return e;
-    if ((e = allow_lds(k2, l2)) != hipSuccess) return e;
-    if ((e = allow_lds(k3, l1)) != hipSuccess) return e;
-    hipLaunchKernelGGL(k1, dim3(N2 / NCOL, (unsigned)nseq), dim3(kMpThreads), l1, stream,
+    if ((e = allow_lds(k1, P::kLds)) != hipSuccess) return e;
+    if ((e = allow_lds(k2, kP2Lds)) != hipSuccess) return e;
+    if ((e = allow_lds(k3, P::kLds)) != hipSuccess) return e;
+    hipLaunchKernelGGL(k1, dim3(N2 / P::C, (unsigned)nseq), dim3(kMpThreads), P::kLds, stream,
                        (const T *)u, (const T *)w, (int64_t)0, seq0, ws, ta);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k2, dim3((1 << LOG1) / 2, (unsigned)nseq), dim3(2 * kMpThreads), l2, stream,
+    hipLaunchKernelGGL(k2, dim3((1 << LOG1) / 2, (unsigned)nseq), dim3(kMpThreads), kP2Lds, stream,
                        ws, (const TK *)kbins, (TK *)nullptr, kscale, mask, H, seq0, ta);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k3, dim3(N2 / NCOL, (unsigned)nseq), dim3(kMpThreads), l1, stream,
+    hipLaunchKernelGGL(k3, dim3(N2 / P::C, (unsigned)nseq), dim3(kMpThreads), P::kLds, stream,
                        (const float2 *)ws, (const T *)v, (T *)out, seq0, ta);
     return hipGetLastError();
 }
@@ -334,20 +627,20 @@ static hipError_t conv_t(const void *u, const void *w, const void *v, void *out,
 template <int LOG1, typename T, typename TK>
 static hipError_t prep_t(const void *k, int64_t L, void *kbins, const float *kscale, void *work,
                          int64_t H, int64_t h0, int64_t nseq, hipStream_t stream) {
-    constexpr int N2 = 1 << kMpLog2, NCOL = kMpThreads / LdsFftPlan<LOG1>::TS;
+    using P = ColPlan<LOG1>;
+    constexpr int N2 = 1 << kMpLog2;
     MpArgs ta{};
     hipError_t e = mp_args(LOG1 + kMpLog2, &ta);
     if (e != hipSuccess) return e;
     float2 *ws = (float2 *)work;
-    const size_t l1 = lds_cols<LOG1>(), l2 = 2 * (size_t)N2 * sizeof(float2);
     auto k1 = mp_pass1_kernel<LOG1, T, true>;
-    auto k2 = mp_pass2_kernel<LOG1, TK, true>;
-    if ((e = allow_lds(k1, l1)) != hipSuccess) return e;
-    if ((e = allow_lds(k2, l2)) != hipSuccess) return e;
-    hipLaunchKernelGGL(k1, dim3(N2 / NCOL, (unsigned)nseq), dim3(kMpThreads), l1, stream,
+    auto k2 = mp_pass2_kernel<LOG1, TK, true, false>;
+    if ((e = allow_lds(k1, P::kLds)) != hipSuccess) return e;
+    if ((e = allow_lds(k2, kP2Lds)) != hipSuccess) return e;
+    hipLaunchKernelGGL(k1, dim3(N2 / P::C, (unsigned)nseq), dim3(kMpThreads), P::kLds, stream,
                        (const T *)k, (const T *)nullptr, L, h0, ws, ta);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k2, dim3((1 << LOG1) / 2, (unsigned)nseq), dim3(2 * kMpThreads), l2, stream,
+    hipLaunchKernelGGL(k2, dim3((1 << LOG1) / 2, (unsigned)nseq), dim3(kMpThreads), kP2Lds, stream,
                        ws, (const TK *)nullptr, (TK *)kbins, kscale, (const uint8_t *)nullptr, H,
                        h0, ta);
     return hipGetLastError();

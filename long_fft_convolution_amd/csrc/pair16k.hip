@@ -165,16 +165,6 @@ static_assert(kWaves == 8, "the LDS address split below assumes 8 waves");
 
 // filter chunk of row fc for (mt2, nt): rows f_c <= 16 as stored, the others from
 // the mirror row 32 - f_c (lane 63 - l, tiles flipped, elements reversed, conjugated)
-// Table and data addresses are a wave-uniform base plus an unsigned 32-bit byte offset,
-// which maps onto the scalar-base global addressing form (no per-lane 64-bit pointers).
-template <typename V, typename P>
-__device__ __forceinline__ V ldu(const P *base, uint32_t byte_off) {
-    return *reinterpret_cast<const V *>(reinterpret_cast<const char *>(base) + byte_off);
-}
-template <typename V, typename P>
-__device__ __forceinline__ void stu(P *base, uint32_t byte_off, const V &x) {
-    *reinterpret_cast<V *>(reinterpret_cast<char *>(base) + byte_off) = x;
-}
 __device__ __forceinline__ uint4 k_load(const uint4 *kch, int fc, int mt2, int nt, uint32_t lane) {
     const bool mir = fc > 16;
     const uint32_t row = mir ? 32 - fc : fc, a = mir ? 1 - mt2 : mt2, b = mir ? 1 - nt : nt;
