@@ -321,9 +321,14 @@ MpSplit mp_split(int logn) {
     return s;
 }
 
-int64_t mp_chunk(int logn) {
-    // keep one chunk's fp32 complex intermediate near 128 MiB
-    const int64_t per_seq = (int64_t(8)) << logn;
+int64_t mp_ws_bytes(int st) {
+    // one complex value per point in the storage type
+    return st == ST_F32 ? 8 : 4;
+}
+
+int64_t mp_chunk(int logn, int st) {
+    // keep one chunk's complex intermediate near 128 MiB
+    const int64_t per_seq = mp_ws_bytes(st) << logn;
     int64_t c = (int64_t(128) << 20) / per_seq;
     return c < 1 ? 1 : c;
 }
@@ -363,9 +368,10 @@ size_t fftconv_workspace_bytes(int64_t B, int64_t H, int64_t N, fftconv_dtype_t 
     if (l < kMinLog || l > kMaxLog || B < 0 || H < 0 || !dtype_ok(dtype)) return 0;
     if (l <= kFusedMaxLog) return 0;
     int64_t S = B * H;
-    const int64_t c = mp_chunk(l);
+    const int64_t c = mp_chunk(l, dtype);
     if (S > c) S = c;
-    return (size_t)S * (size_t)N * sizeof(float2);
+    // per sequence: the intermediate, then the fp32 rows 0 and N1/2
+    return (size_t)S * ((size_t)N * (size_t)mp_ws_bytes(dtype) + kMpSelfBytes);
 }
 
 fftconv_status_t fftconv_prepare_filter(const void *k, int64_t H, int64_t L, int64_t N,
@@ -425,7 +431,7 @@ fftconv_status_t fftconv_prepare_filter(const void *k, int64_t H, int64_t L, int
         e = get_tables(l, &tb);
         if (e == hipSuccess) e = launch_fused_prepare(l, dtype, k, L, kbins, kscale, tb, H, stream);
     } else {
-        const int64_t c = mp_chunk(l);
+        const int64_t c = mp_chunk(l, dtype);
         for (int64_t h0 = 0; h0 < H && e == hipSuccess; h0 += c) {
             const int64_t n = H - h0 < c ? H - h0 : c;
             e = launch_multipass_prepare(l, dtype, k, L, kbins, kscale, workspace, H, h0, n, stream);
@@ -499,7 +505,7 @@ fftconv_status_t fftconv_fwd(const void *u, const void *K_f, const void *w, cons
         if (e == hipSuccess)
             e = launch_fused_conv(l, dtype, u, w, v, out, kbins, kscale, mask, tb, B, H, stream);
     } else {
-        const int64_t S = B * H, c = mp_chunk(l);
+        const int64_t S = B * H, c = mp_chunk(l, dtype);
         for (int64_t s0 = 0; s0 < S && e == hipSuccess; s0 += c) {
             const int64_t n = S - s0 < c ? S - s0 : c;
             e = launch_multipass_conv(l, dtype, u, w, v, out, kbins, kscale, mask, workspace, H,

@@ -94,8 +94,12 @@ struct MpSplit {
     int log1, log2;
 };
 MpSplit mp_split(int logn);
-// Sequences processed per multi-pass chunk (bounds the workspace).
-int64_t mp_chunk(int logn);
+// Bytes per workspace point (one complex value in the storage type) and
+// sequences processed per multi-pass chunk (bounds the workspace).
+int64_t mp_ws_bytes(int st);
+// fp32 area per sequence for the two self-paired rows of the row pass
+constexpr size_t kMpSelfBytes = 2 * 8192 * 8;
+int64_t mp_chunk(int logn, int st);
 
 // Per-device, per-size tables (allocated once, read only afterwards).
 struct Tables {

@@ -21,8 +21,11 @@
 //
 // Every DFT is split once more into radix stages held in the registers of one
 // lane, with padded (bank-conflict-free) LDS transposes between stages.  All
-// arithmetic is fp32.  Workspace: one fp32 complex value per point and
-// sequence of the chunk.
+// arithmetic is fp32.  Workspace: one complex value per point and sequence
+// of the chunk, held in the storage type (fp32, fp16 or bf16 pairs), so the
+// two passes through it cost as many bytes per point as the input does;
+// after it, 2 * 8192 fp32 complex values per sequence for the two rows that
+// pair with themselves.
 #include "fft_device.hpp"
 #include "fft_stages.hpp"
 #include "fftconv_internal.hpp"
@@ -147,7 +150,7 @@ __device__ __forceinline__ void column_twiddle(float2 *a, uint32_t n2, uint32_t 
 template <int LOG1, typename T, bool SRC_FILTER>
 __global__ void __launch_bounds__(kMpThreads, 4)
 mp_pass1_kernel(const T *__restrict__ src, const T *__restrict__ gate, int64_t L, int64_t seq0,
-                float2 *__restrict__ ws, MpArgs ta) {
+                T *__restrict__ ws, MpArgs ta) {
     using P = ColPlan<LOG1>;
     constexpr int N1 = P::N1, RA = P::RA, RB = P::RB, C = P::C, N2 = 1 << kMpLog2;
     constexpr int64_t NC = (int64_t)N1 * N2;
@@ -188,7 +191,7 @@ mp_pass1_kernel(const T *__restrict__ src, const T *__restrict__ gate, int64_t L
     }
     apply_pow<RB>(y, ldu<float2>(ta.tw1, 8u * j), ldu<float2>(ta.tw1, 8u * ((8 * j) & (N1 - 1))));
 
-    float2 *out = ws + (int64_t)blockIdx.y * NC;
+    T *out = ws + 2 * (int64_t)blockIdx.y * NC;
 #pragma unroll
     for (int g = 0; g < P::NG; ++g) {
 #pragma unroll
@@ -202,9 +205,9 @@ mp_pass1_kernel(const T *__restrict__ src, const T *__restrict__ gate, int64_t L
         const uint32_t fb = (uint32_t)(g * RA + j);
         column_twiddle<RA, RB>(a, n2, fb, (uint32_t)(NC - 1), ta);
         // row fb + RB f_a: uniform part (g RA + RB f_a) N2 + c0, lane part j N2 + col
-        const uint32_t so = 8u * (uint32_t)(launder(j) * N2 + launder(col));
+        const uint32_t so = (uint32_t)(launder(j) * N2 + launder(col));
 #pragma unroll
-        for (int fa = 0; fa < RA; ++fa) stu(out + (int64_t)(g * RA + RB * fa) * N2 + c0, so, a[fa]);
+        for (int fa = 0; fa < RA; ++fa) io<T>::store2(out + 2 * ((int64_t)(g * RA + RB * fa) * N2 + c0), so, a[fa]);
         if (g + 1 < P::NG) __syncthreads();
     }
 }
@@ -212,7 +215,7 @@ mp_pass1_kernel(const T *__restrict__ src, const T *__restrict__ gate, int64_t L
 // ---------------------------------------------------------------- pass 3
 template <int LOG1, typename T>
 __global__ void __launch_bounds__(kMpThreads, 4)
-mp_pass3_kernel(const float2 *__restrict__ ws, const T *__restrict__ v, T *__restrict__ out,
+mp_pass3_kernel(const T *__restrict__ ws, const T *__restrict__ v, T *__restrict__ out,
                 int64_t seq0, MpArgs ta) {
     using P = ColPlan<LOG1>;
     constexpr int N1 = P::N1, RA = P::RA, RB = P::RB, C = P::C, N2 = 1 << kMpLog2;
@@ -223,7 +226,7 @@ mp_pass3_kernel(const float2 *__restrict__ ws, const T *__restrict__ v, T *__res
     const int c0 = blockIdx.x * C;
     const uint32_t n2 = (uint32_t)(c0 + col);
     const int64_t s = seq0 + blockIdx.y;
-    const float2 *wsq = ws + (int64_t)blockIdx.y * NC;
+    const T *wsq = ws + 2 * (int64_t)blockIdx.y * NC;
     const uint32_t lo = (uint32_t)(col + N2 * j);
 
     float2 acc[RB];      // lane (col, n_a = j): all f_b
@@ -234,7 +237,7 @@ mp_pass3_kernel(const float2 *__restrict__ ws, const T *__restrict__ v, T *__res
         const uint32_t fb = (uint32_t)(g * RA + j);
         float2 a[RA];
 #pragma unroll
-        for (int fa = 0; fa < RA; ++fa) a[fa] = ldu<float2>(wsq + (int64_t)(g * RA + RB * fa) * N2 + c0, 8u * lo);
+        for (int fa = 0; fa < RA; ++fa) a[fa] = io<T>::load2(wsq + 2 * ((int64_t)(g * RA + RB * fa) * N2 + c0), lo);
         column_twiddle<RA, RB>(a, n2, fb, (uint32_t)(NC - 1), ta);
         dft_inplace<RA>(a);
         apply_pow<RA>(a, ldu<float2>(ta.tw1, 8u * fb), ldu<float2>(ta.tw1, 8u * ((8 * fb) & (N1 - 1))));
@@ -288,27 +291,36 @@ mp_pass3_kernel(const float2 *__restrict__ ws, const T *__restrict__ v, T *__res
 constexpr int kT1Row = 257;
 constexpr int kT2Row = 129;
 constexpr int kP2LdsFloat2 = 64 * kT2Row + 16 + 128;
-constexpr size_t kP2Lds = (size_t)kP2LdsFloat2 * sizeof(float2) + kMaskBlocks;
+constexpr size_t kP2Lds = (size_t)kP2LdsFloat2 * sizeof(float2);
+
+// The 128 mask blocks of a channel as two 64-bit words (bit b: block kept).
+struct BlockMask {
+    uint64_t lo, hi;
+    __device__ __forceinline__ bool keep(int b) const { return ((b < 64 ? lo >> b : hi >> (b - 64)) & 1) != 0; }
+};
 static_assert(kP2LdsFloat2 >= 32 * kT1Row && kP2LdsFloat2 >= 8192, "pass-2 LDS");
 
 // Bin pairs of the workgroup that holds rows 0 and N1/2: each row pairs with
-// itself (row 0: f2 <-> N2 - f2; row N1/2: f2 <-> N2 - 1 - f2).  The row
-// sits in LDS in natural order; lanes take the pairs in turn.
+// itself (row 0: f2 <-> N2 - f2; row N1/2: f2 <-> N2 - 1 - f2).  Both rows
+// sit in natural order in an fp32 area of the workspace (row 0, then row
+// N1/2); lanes take the 8193 pairs in turn.
 template <int N1, int N2, typename TK, bool PREPARE, bool MASKED>
-__device__ __forceinline__ void self_pairs(float2 *row, bool half_row, const TK *__restrict__ krow,
-                                           TK *__restrict__ kout, const uint8_t *smask, float ks,
+__device__ __forceinline__ void self_pairs(float2 *area, const TK *__restrict__ krow,
+                                           TK *__restrict__ kout, BlockMask bm, float ks,
                                            const MpArgs &ta, int tid) {
     constexpr int64_t NC = (int64_t)N1 * N2;
-    const int rbase = half_row ? N1 / 2 : 0;
-    const float2 wrow = half_row ? ta.w2row[N1 / 2] : make_float2(1.f, 0.f);
     const float sh = 1.0f / (ks * 4.0f * (float)NC);
-    for (int w = tid; w <= N2 / 2; w += kMpThreads) {
-        if (half_row && w == N2 / 2) break;
+    for (int it = tid; it <= N2; it += kMpThreads) {
+        const bool half_row = it > N2 / 2;             // items 0..N2/2: row 0; the rest: row N1/2
+        const int w = half_row ? it - (N2 / 2 + 1) : it;
+        const int rbase = half_row ? N1 / 2 : 0;
+        float2 *row = area + (half_row ? N2 : 0);
         const int ia = w;
         const int ib = half_row ? N2 - 1 - w : (w == 0 ? 0 : N2 - w);
         const int64_t sa = (int64_t)rbase * N2 + ia, sb = (int64_t)rbase * N2 + ib;
         float2 zf = row[ia], zg = row[ib];
         const bool dc = !half_row && w == 0;   // f = 0: (K[0], K[N]) share slot 0
+        const float2 wrow = half_row ? ta.w2row[N1 / 2] : make_float2(1.f, 0.f);
         const float2 Wf = dc ? make_float2(1.f, 0.f) : cmul(wrow, ta.w2n2[w]);
         if (PREPARE) {
             const float2 bc = cconj(zg);
@@ -328,11 +340,11 @@ __device__ __forceinline__ void self_pairs(float2 *row, bool half_row, const TK 
         float2 Kf, Kg;
         if (dc) {
             const float2 k0 = cscale(kio<TK>::load(krow), ks);
-            Kf = make_float2(MASKED && !smask[0] ? 0.f : k0.x, 0.f);
-            Kg = make_float2(MASKED && !smask[kMaskBlocks - 1] ? 0.f : k0.y, 0.f);
+            Kf = make_float2(MASKED && !bm.keep(0) ? 0.f : k0.x, 0.f);
+            Kg = make_float2(MASKED && !bm.keep(kMaskBlocks - 1) ? 0.f : k0.y, 0.f);
         } else {
-            Kf = (MASKED && !smask[ia >> 6]) ? make_float2(0.f, 0.f) : cscale(kio<TK>::load(krow + sa), ks);
-            Kg = (MASKED && !smask[ib >> 6]) ? make_float2(0.f, 0.f) : cscale(kio<TK>::load(krow + sb), ks);
+            Kf = (MASKED && !bm.keep(ia >> 6)) ? make_float2(0.f, 0.f) : cscale(kio<TK>::load(krow + sa), ks);
+            Kg = (MASKED && !bm.keep(ib >> 6)) ? make_float2(0.f, 0.f) : cscale(kio<TK>::load(krow + sb), ks);
         }
         middle_pair(zf, zg, Kf, Kg, Wf);
         row[ia] = zf;
@@ -342,31 +354,34 @@ __device__ __forceinline__ void self_pairs(float2 *row, bool half_row, const TK 
 
 // grid (N1 / 2, nseq); block 512.  PREPARE: forward only, writes the filter
 // spectrum; else the full filter product and inverse rows.
-template <int LOG1, typename TK, bool PREPARE, bool MASKED>
+template <int LOG1, typename T, typename TK, bool PREPARE, bool MASKED>
 __global__ void __launch_bounds__(kMpThreads, 4)
-mp_pass2_kernel(float2 *__restrict__ ws, const TK *__restrict__ kbins_in, TK *__restrict__ kbins_out,
-                const float *__restrict__ kscale, const uint8_t *__restrict__ mask, int64_t H,
-                int64_t seq0, MpArgs ta) {
+mp_pass2_kernel(T *__restrict__ ws, float2 *__restrict__ self_area, const TK *__restrict__ kbins_in,
+                TK *__restrict__ kbins_out, const float *__restrict__ kscale,
+                const uint8_t *__restrict__ mask, int64_t H, int64_t seq0, MpArgs ta) {
     constexpr int N1 = 1 << LOG1, N2 = 1 << kMpLog2;
     constexpr int64_t NC = (int64_t)N1 * N2;
     extern __shared__ float2 lds[];
-    uint8_t *smask = reinterpret_cast<uint8_t *>(lds + kP2LdsFloat2);
     const int tid = threadIdx.x;
     const int f1 = blockIdx.x;
     const int rowA = f1, rowB = f1 == 0 ? N1 / 2 : N1 - f1;
     const int64_t s = seq0 + blockIdx.y;
     const int64_t h = s % H;
-    float2 *wsq = ws + (int64_t)blockIdx.y * NC;
+    T *wsq = ws + 2 * (int64_t)blockIdx.y * NC;
     const float2 *tw = ta.tw2;
-    if (MASKED && tid < kMaskBlocks / 4)
-        reinterpret_cast<uint32_t *>(smask)[tid] = reinterpret_cast<const uint32_t *>(mask + h * kMaskBlocks)[tid];
+    BlockMask bm{~0ull, ~0ull};
+    if (MASKED) {
+        const uint8_t *mrow = mask + h * kMaskBlocks;
+        bm.lo = __builtin_amdgcn_ballot_w64(mrow[tid & 63] != 0);
+        bm.hi = __builtin_amdgcn_ballot_w64(mrow[64 + (tid & 63)] != 0);
+    }
 
     // ---- stage A: lane (row ra, n_a)
     const int ra = __builtin_amdgcn_readfirstlane(tid >> 8), na = tid & 255;
-    float2 *rowp = wsq + (int64_t)(ra ? rowB : rowA) * N2;
+    T *rowp = wsq + 2 * (int64_t)(ra ? rowB : rowA) * N2;
     float2 a[32];
 #pragma unroll
-    for (int nb = 0; nb < 32; ++nb) a[nb] = ldu<float2>(rowp + 256 * nb, 8u * na);
+    for (int nb = 0; nb < 32; ++nb) a[nb] = io<T>::load2(rowp + 512 * nb, (uint32_t)na);
     dft_pq<8, 4>(a);
     apply_pow<32>(a, ldu<float2>(tw, 8u * na), ldu<float2>(tw, 64u * na));
 
@@ -394,15 +409,13 @@ mp_pass2_kernel(float2 *__restrict__ ws, const TK *__restrict__ kbins_in, TK *__
 
     // ---- T2, stage C.  The lanes of waves 0-3 (hiw = 0) have k_d < 8: they
     // take row A in round 0 and row B in round 1; waves 4-7 the other way.
+    // c[q] is the row received in round q: row A when hiw == q, else row B.
     const int kbC = tid & 31, kdC = tid >> 5, hiw = tid >> 8;
     const int t2p0 = (32 * hb0 + kl0) * kT2Row + 16 * hb0 + ncB;
     const int t2p1 = (32 * (1 - hb0) + 16 + kl0) * kT2Row + 16 * (1 - hb0) + ncB;
     const int t2a = kbC * kT2Row + 16 * (kdC & 7);
     const int t2b = (63 - kbC) * kT2Row + 16 + 16 * ((15 - kdC) & 7);
-    // (reads go to per-round arrays and are renamed by value afterwards: a
-    // branch that fills cA or cB would be merged into a store through a
-    // selected array pointer, which forces both arrays out of registers)
-    float2 rd[2][16];
+    float2 c[2][16];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
 #pragma unroll
@@ -413,99 +426,113 @@ mp_pass2_kernel(float2 *__restrict__ ws, const TK *__restrict__ kbins_in, TK *__
         __syncthreads();
         const int src = hiw == q ? t2a : t2b;
 #pragma unroll
-        for (int n = 0; n < 16; ++n) rd[q][n] = lds[src + n];
+        for (int n = 0; n < 16; ++n) c[q][n] = lds[src + n];
         __syncthreads();
     }
-    float2 cA[16], cB[16];
-#pragma unroll
-    for (int n = 0; n < 16; ++n) {
-        cA[n] = hiw ? rd[1][n] : rd[0][n];
-        cB[n] = hiw ? rd[0][n] : rd[1][n];
-    }
-    dft_pq<4, 4>(cA);
-    dft_pq<4, 4>(cB);
-    // cA[kc] = Z of row A at bin kbC + 32 kdC + 512 kc
-    // cB[kc] = Z of row B at bin (31 - kbC) + 32 (15 - kdC) + 512 kc
+    dft_pq<4, 4>(c[0]);
+    dft_pq<4, 4>(c[1]);
+    // Row A holds bins kq + 512 kc at (kbC, kdC), row B bins
+    // (31 - kbC) + 32 (15 - kdC) + 512 kc = 8191 - (kq + 512 (15 - kc)).
+    // So c[0][j] and c[1][15 - j] are always the two bins of one pair:
+    //   hiw = 0: (A at k, B at 8191 - k),  k = kq + 512 j
+    //   hiw = 1: (B at 8191 - k, A at k),  k = kq + 512 (15 - j)
+    // The bin-pair step is symmetric in its two bins (with omega_2N^{N - f} =
+    // -conj(omega_2N^f)), so every lane runs the same code on (c[0][j],
+    // c[1][15 - j]) with its filter addresses and twiddle chosen per wave.
 
-    // ---- bin-pair step
+    // ---- bin-pair step.  The workgroup of rows 0 and N1/2 (f1 = 0), whose
+    // rows pair with themselves, first saves its spectra to this sequence's
+    // fp32 area (row 0, then row N1/2, natural order), runs the in-lane step
+    // like every other workgroup (its results are discarded: rowB = N1/2
+    // keeps every access in range), then pairs the bins in the area and
+    // reloads.  Keeping the common step outside any branch keeps its register
+    // allocation free of the rare path.
     const float ks = kscale[h];
     const int kq = kbC + 32 * kdC;
-    if (f1 != 0) {
-        // row A bin k pairs with row B bin 8191 - k: both in this lane
-        const float2 wb = cmul(ta.w2row[f1], ldu<float2>(ta.w2n2, 8u * kq));
+    float2 *area = self_area + (int64_t)blockIdx.y * 2 * N2;
+    const int qa = kq, qb = N2 + (31 - kbC) + 32 * (15 - kdC);   // area offsets of rows A, B
+    if (f1 == 0) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            float2 *dst = area + (hiw == q ? qa : qb);
+#pragma unroll
+            for (int kc = 0; kc < 16; ++kc) dst[512 * kc] = c[q][kc];
+        }
+    }
+    {
+        const float2 wb = cmul(ta.w2row[f1], ldu<float2>(ta.w2n2, 8u * kq));   // omega_2N^{f1 + N1 kq}
+        // twiddle of the first bin of pair j is w1 omega_32^j
+        const float2 w1 = hiw ? twiddle_const<32>(cconj(wb), 1) : wb;
+        // in-row bin of the first element: o1 + 512 j; of the second: o2 + 512 (15 - j)
+        const uint32_t o1 = hiw ? 511 - kq : kq, o2 = hiw ? kq : 511 - kq;
         if (PREPARE) {
-            const float sh = 1.0f / (ks * 4.0f * (float)NC);
-            TK *ka = kbins_out + h * NC + (int64_t)rowA * N2;
-            TK *kb = kbins_out + h * NC + (int64_t)rowB * N2;
+            if (f1 != 0) {
+                const float sh = 1.0f / (ks * 4.0f * (float)NC);
+                TK *k1 = kbins_out + h * NC + (int64_t)(hiw ? rowB : rowA) * N2;
+                TK *k2 = kbins_out + h * NC + (int64_t)(hiw ? rowA : rowB) * N2;
 #pragma unroll
-            for (int kc = 0; kc < 16; ++kc) {
-                const int k = kq + 512 * kc;
-                const float2 zf = cA[kc], zg = cB[15 - kc];
-                const float2 Wf = twiddle_const<32>(wb, kc);
-                const float2 bc = cconj(zg);
-                const float2 xe = cadd(zf, bc);
-                const float2 xo = cmul_negi(csub(zf, bc));
-                const float2 wxo = cmul(Wf, xo);
-                // bin N2 - 1 - k: uniform part N2 - 512 (kc + 1), lane part 511 - kq
-                kio<TK>::store(ka + 512 * kc, (uint32_t)kq, cscale(cadd(xe, wxo), 0.5f * sh));
-                kio<TK>::store(kb + N2 - 512 * (kc + 1), (uint32_t)(511 - kq),
-                               cscale(cconj(csub(xe, wxo)), 0.5f * sh));
+                for (int jj = 0; jj < 16; ++jj) {
+                    const float2 zf = c[0][jj], zg = c[1][15 - jj];
+                    const float2 Wf = twiddle_const<32>(w1, jj);
+                    const float2 bc = cconj(zg);
+                    const float2 xe = cadd(zf, bc);
+                    const float2 xo = cmul_negi(csub(zf, bc));
+                    const float2 wxo = cmul(Wf, xo);
+                    kio<TK>::store(k1 + 512 * jj, o1, cscale(cadd(xe, wxo), 0.5f * sh));
+                    kio<TK>::store(k2 + 512 * (15 - jj), o2, cscale(cconj(csub(xe, wxo)), 0.5f * sh));
+                }
+                return;
             }
-            return;
+        } else {
+            const TK *k1 = kbins_in + h * NC + (int64_t)(hiw ? rowB : rowA) * N2;
+            const TK *k2 = kbins_in + h * NC + (int64_t)(hiw ? rowA : rowB) * N2;
+            // the mask block of in-row bin b is b >> 6; o1 >> 6 and o2 >> 6 are
+            // uniform over the wave (kq >> 6 is the wave's index modulo 4)
+            const int b1 = __builtin_amdgcn_readfirstlane((int)(o1 >> 6));
+            const int b2 = __builtin_amdgcn_readfirstlane((int)(o2 >> 6));
+            // two batches of eight bin pairs; the scheduling barriers keep the
+            // second batch of filter loads from being hoisted over the first
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                float2 K1[8], K2[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int jj = 8 * half + i;
+                    K1[i] = make_float2(0.f, 0.f);
+                    K2[i] = make_float2(0.f, 0.f);
+                    if (!MASKED || bm.keep(b1 + 8 * jj)) K1[i] = kio<TK>::load(k1 + 512 * jj, o1);
+                    if (!MASKED || bm.keep(b2 + 8 * (15 - jj))) K2[i] = kio<TK>::load(k2 + 512 * (15 - jj), o2);
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int jj = 8 * half + i;
+                    float2 z1 = c[0][jj], z2 = c[1][15 - jj];
+                    middle_pair(z1, z2, cscale(K1[i], ks), cscale(K2[i], ks), twiddle_const<32>(w1, jj));
+                    c[0][jj] = z1;
+                    c[1][15 - jj] = z2;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-        const TK *ka = kbins_in + h * NC + (int64_t)rowA * N2;
-        const TK *kb = kbins_in + h * NC + (int64_t)rowB * N2;
-        // two batches of eight bin pairs; the scheduling barriers keep the
-        // second batch of filter loads from being hoisted over the first
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            float2 Kf[8], Kg[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int kc = 8 * half + i, k = kq + 512 * kc;
-                Kf[i] = make_float2(0.f, 0.f);
-                Kg[i] = make_float2(0.f, 0.f);
-                // the mask block of bin k is k >> 6 (uniform over the wave)
-                if (!MASKED || smask[k >> 6]) Kf[i] = kio<TK>::load(ka + 512 * kc, (uint32_t)kq);
-                if (!MASKED || smask[(N2 - 1 - k) >> 6])
-                    Kg[i] = kio<TK>::load(kb + N2 - 512 * (kc + 1), (uint32_t)(511 - kq));
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int kc = 8 * half + i;
-                float2 zf = cA[kc], zg = cB[15 - kc];
-                middle_pair(zf, zg, cscale(Kf[i], ks), cscale(Kg[i], ks), twiddle_const<32>(wb, kc));
-                cA[kc] = zf;
-                cB[15 - kc] = zg;
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    } else {
-        // rows 0 and N1/2 pair with themselves: one row at a time in LDS
+    }
+    if (f1 == 0) {
+        // The barriers (workgroup scope) order the area's global writes and
+        // reads across the workgroup's waves, which share one CU's L1.  A
+        // device-scope fence here would write back the whole L2.
         const TK *krow = PREPARE ? nullptr : kbins_in + h * NC;
         TK *kout = PREPARE ? kbins_out + h * NC : nullptr;
-        const int qa = kq, qb = (31 - kbC) + 32 * (15 - kdC);
-#pragma unroll
-        for (int kc = 0; kc < 16; ++kc) lds[qa + 512 * kc] = cA[kc];
         __syncthreads();
-        self_pairs<N1, N2, TK, PREPARE, MASKED>(lds, false, krow, kout, smask, ks, ta, tid);
-        __syncthreads();
-        if (!PREPARE) {
-#pragma unroll
-            for (int kc = 0; kc < 16; ++kc) cA[kc] = lds[qa + 512 * kc];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int kc = 0; kc < 16; ++kc) lds[qb + 512 * kc] = cB[kc];
-        __syncthreads();
-        self_pairs<N1, N2, TK, PREPARE, MASKED>(lds, true, krow, kout, smask, ks, ta, tid);
-        __syncthreads();
+        self_pairs<N1, N2, TK, PREPARE, MASKED>(area, krow, kout, bm, ks, ta, tid);
         if (PREPARE) return;
-#pragma unroll
-        for (int kc = 0; kc < 16; ++kc) cB[kc] = lds[qb + 512 * kc];
         __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const float2 *src = area + (hiw == q ? qa : qb);
+#pragma unroll
+            for (int kc = 0; kc < 16; ++kc) c[q][kc] = src[512 * kc];
+        }
     }
-    // cA, cB now hold conj(Z') in the same layout; the forward transform of
+    // c now holds conj(Z') in the same layout; the forward transform of
     // conjugated data is the conjugated inverse transform.  Lane indices are
     // recomputed from a laundered thread id so that no address is held live
     // across the bin-pair step.
@@ -513,26 +540,28 @@ mp_pass2_kernel(float2 *__restrict__ ws, const TK *__restrict__ kbins_in, TK *__
     {
     const int tid2 = launder(tid);
     const int kbC = tid2 & 31, kdC = tid2 >> 5, kb0 = tid2 & 31, ncB = tid2 >> 5, kl0 = kb0 & 15,
-              hb0 = kb0 >> 4, na = tid2 & 255;
+              hb0 = kb0 >> 4, na = tid2 & 255, hiw = tid2 >> 8;
     const int t2p0 = (32 * hb0 + kl0) * kT2Row + 16 * hb0 + ncB;
     const int t2p1 = (32 * (1 - hb0) + 16 + kl0) * kT2Row + 16 * (1 - hb0) + ncB;
     const int t2a = kbC * kT2Row + 16 * (kdC & 7);
     const int t2b = (63 - kbC) * kT2Row + 16 + 16 * ((15 - kdC) & 7);
 
-    // ---- stage C' (over k_c -> n_c), twiddle omega_256^{n_c k_d}
-    dft_pq<4, 4>(cA);
-    dft_pq<4, 4>(cB);
-    apply_pow<16>(cA, ldu<float2>(tw, 256u * kdC), ldu<float2>(tw, 2048u * kdC));
-    apply_pow<16>(cB, ldu<float2>(tw, 256u * (15 - kdC)), ldu<float2>(tw, 2048u * (15 - kdC)));
+    // ---- stage C' (over k_c -> n_c), twiddle omega_256^{n_c k_d}; c[q] is
+    // row A (k_d = kdC) when hiw == q, else row B (k_d = 15 - kdC)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        dft_pq<4, 4>(c[q]);
+        const int kd = hiw == q ? kdC : 15 - kdC;
+        apply_pow<16>(c[q], ldu<float2>(tw, 256u * kd), ldu<float2>(tw, 2048u * kd));
+    }
 
     // ---- T2' (T2 backwards), stage B' (over k_d -> n_d), twiddle
     // omega_8192^{(n_c + 16 n_d) k_b}; p[q] is at k_b = 16 q + kl0
-    const int hiw = tid2 >> 8;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const int dst = hiw == q ? t2a : t2b;
 #pragma unroll
-        for (int n = 0; n < 16; ++n) lds[dst + n] = hiw == q ? cA[n] : cB[n];
+        for (int n = 0; n < 16; ++n) lds[dst + n] = c[q][n];
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -564,9 +593,9 @@ mp_pass2_kernel(float2 *__restrict__ ws, const TK *__restrict__ kbins_in, TK *__
     }
     dft_pq<8, 4>(a);
     // rows now hold conj of the inverse row transform; pass 3 undoes the conj
-    const uint32_t so = 8u * (uint32_t)launder(tid & 255);
+    const uint32_t so = (uint32_t)launder(tid & 255);
 #pragma unroll
-    for (int nb = 0; nb < 32; ++nb) stu(rowp + 256 * nb, so, a[nb]);
+    for (int nb = 0; nb < 32; ++nb) io<T>::store2(rowp + 512 * nb, so, a[nb]);
     }
 }
 
@@ -604,10 +633,11 @@ static hipError_t conv_t(const void *u, const void *w, const void *v, void *out,
     MpArgs ta{};
     hipError_t e = mp_args(LOG1 + kMpLog2, &ta);
     if (e != hipSuccess) return e;
-    float2 *ws = (float2 *)work;
+    T *ws = (T *)work;
+    float2 *self_area = (float2 *)((char *)work + (size_t)nseq * ((size_t)1 << (LOG1 + kMpLog2)) * 2 * sizeof(T));
     auto k1 = mp_pass1_kernel<LOG1, T, false>;
-    auto k2m = mp_pass2_kernel<LOG1, TK, false, true>;
-    auto k2u = mp_pass2_kernel<LOG1, TK, false, false>;
+    auto k2m = mp_pass2_kernel<LOG1, T, TK, false, true>;
+    auto k2u = mp_pass2_kernel<LOG1, T, TK, false, false>;
     auto k2 = mask != nullptr ? k2m : k2u;
     auto k3 = mp_pass3_kernel<LOG1, T>;
     if ((e = allow_lds(k1, P::kLds)) != hipSuccess) return e;
@@ -617,10 +647,10 @@ static hipError_t conv_t(const void *u, const void *w, const void *v, void *out,
                        (const T *)u, (const T *)w, (int64_t)0, seq0, ws, ta);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k2, dim3((1 << LOG1) / 2, (unsigned)nseq), dim3(kMpThreads), kP2Lds, stream,
-                       ws, (const TK *)kbins, (TK *)nullptr, kscale, mask, H, seq0, ta);
+                       ws, self_area, (const TK *)kbins, (TK *)nullptr, kscale, mask, H, seq0, ta);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k3, dim3(N2 / P::C, (unsigned)nseq), dim3(kMpThreads), P::kLds, stream,
-                       (const float2 *)ws, (const T *)v, (T *)out, seq0, ta);
+                       (const T *)ws, (const T *)v, (T *)out, seq0, ta);
     return hipGetLastError();
 }
 
@@ -632,17 +662,18 @@ static hipError_t prep_t(const void *k, int64_t L, void *kbins, const float *ksc
     MpArgs ta{};
     hipError_t e = mp_args(LOG1 + kMpLog2, &ta);
     if (e != hipSuccess) return e;
-    float2 *ws = (float2 *)work;
+    T *ws = (T *)work;
+    float2 *self_area = (float2 *)((char *)work + (size_t)nseq * ((size_t)1 << (LOG1 + kMpLog2)) * 2 * sizeof(T));
     auto k1 = mp_pass1_kernel<LOG1, T, true>;
-    auto k2 = mp_pass2_kernel<LOG1, TK, true, false>;
+    auto k2 = mp_pass2_kernel<LOG1, T, TK, true, false>;
     if ((e = allow_lds(k1, P::kLds)) != hipSuccess) return e;
     if ((e = allow_lds(k2, kP2Lds)) != hipSuccess) return e;
     hipLaunchKernelGGL(k1, dim3(N2 / P::C, (unsigned)nseq), dim3(kMpThreads), P::kLds, stream,
                        (const T *)k, (const T *)nullptr, L, h0, ws, ta);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k2, dim3((1 << LOG1) / 2, (unsigned)nseq), dim3(kMpThreads), kP2Lds, stream,
-                       ws, (const TK *)nullptr, (TK *)kbins, kscale, (const uint8_t *)nullptr, H,
-                       h0, ta);
+                       ws, self_area, (const TK *)nullptr, (TK *)kbins, kscale, (const uint8_t *)nullptr,
+                       H, h0, ta);
     return hipGetLastError();
 }
 

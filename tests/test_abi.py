@@ -52,9 +52,15 @@ def test_size_helpers():
     assert fc.fftconv_filter_bytes(4, 1024, 7) == 0
     for n in (1024, 16384):
         assert fc.fftconv_workspace_bytes(64, 768, n, F16) == 0
+    # multi-pass workspace per sequence of a chunk: one complex value per point
+    # in the storage type plus 2 * 8192 fp32 complex values; the intermediate
+    # of a chunk takes 128 MiB
+    extra = 2 * 8192 * 8
     ws = fc.fftconv_workspace_bytes(1, 256, 1 << 20, F16)
-    assert ws > 0 and ws % ((1 << 20) * 8) == 0
-    assert fc.fftconv_workspace_bytes(1, 1, 1 << 20, F16) == (1 << 20) * 8
+    assert ws == 32 * ((1 << 20) * 4 + extra)
+    assert fc.fftconv_workspace_bytes(1, 1, 1 << 20, F16) == (1 << 20) * 4 + extra
+    assert fc.fftconv_workspace_bytes(1, 1, 1 << 20, F32) == (1 << 20) * 8 + extra
+    assert fc.fftconv_workspace_bytes(1, 256, 1 << 20, F32) == 16 * ((1 << 20) * 8 + extra)
     assert fc.fftconv_mask_blocks(1 << 22) == 128
     assert fc.fftconv_mask_blocks(1024) == 128
     assert fc.fftconv_mask_blocks(512) == 0

@@ -20,7 +20,10 @@ MUTANTS = {
     "fft_butterfly_sign": ("re[q] = re[s] - br;", "re[q] = re[s] + br;"),
     "direct_drops_last_tap": ("for (int64_t s = 0; s <= smax; ++s) {", "for (int64_t s = 0; s < smax; ++s) {"),
     "direct_gate_swapped": ("double x = u[t - s] * (w ? w[t - s] : 1.0);", "double x = u[t - s] * (v ? v[t - s] : 1.0);"),
-    "points_filter_stride": ("acc += k[h * L + s] * (us[t - s]", "acc += k[h * N + s] * (us[t - s]"),
+    # filter read as the transposed (L, H) array: a wrong-layout mistake that
+    # stays inside the buffer (a wrong stride that reads past it would make
+    # the mutant's output undefined rather than wrong)
+    "points_filter_stride": ("acc += k[h * L + s] * (us[t - s]", "acc += k[s * H + h] * (us[t - s]"),
     "fft_conv_correlation": ("xr[f] = a * kr[f] - bq * ki[f];", "xr[f] = a * kr[f] + bq * ki[f];"),
     "fft_conv_normalisation": ("(xr[t] / (double)M);", "(xr[t] / (double)N);"),
     "fft_conv_circular_input": ("xr[n] = n < N ? us[n] * (ws ? ws[n] : 1.0) : 0.0;",
