@@ -181,6 +181,92 @@ def circular_points(u_row, kp, ts, w_row=None, v_row=None, lib=None):
     return out
 
 
+# ---------------------------------------------------------------- backward
+# Gradients of the scalar sum(dy * y) for y = v * conv(u * w, k) (FlashFFTConv
+# summary page: the convolutions are trained, so the operator's backward pass
+# is part of what a user runs; "Approach" gives the frequency-sparse filter).
+# With x = u * w and g = v * dy:
+#   dv[t] = dy[t] c[t],        c = conv(x, k) (no output gate)
+#   dx[n] = sum_t g[t] k[t - n]            (correlation: the adjoint of conv)
+#   du = dx * w,  dw = dx * u
+#   dk[s] = sum_b sum_t g[t] x[t - s],     s < L
+# With a frequency mask the filter acts as the 2N-periodic kp = Re IFFT(m FFT
+# pad(k)) (see fft_conv); that operator is a real symmetric circulant, so
+# dk = [Re IFFT(m FFT(r))][:L] with r the 2N-point circular correlation of g
+# and x summed over the batch.  Gates that are absent (None) have no gradient.
+
+def direct_bwd(u, k, dy, w=None, v=None):
+    """Route D gradients (du, dk, dw, dv) by the sums above; no mask.
+
+    u, w, v, dy: (B, H, N); k: (H, L).  Returns float64 arrays; dw / dv are
+    None when w / v are absent."""
+    u, k, dy = _f64(u), _f64(k), _f64(dy)
+    w, v = _f64(w), _f64(v)
+    B, H, N = u.shape
+    L = k.shape[1]
+    x = u * w if w is not None else u.copy()
+    g = dy * v if v is not None else dy.copy()
+    dv = None
+    if v is not None:
+        c = direct(u, k, w, None)
+        dv = dy * c
+    dx = np.zeros((B, H, N))
+    dk = np.zeros((H, L))
+    for s in range(L):
+        # dx[n] += k[s] g[n + s] for n + s < N;  dk[s] = sum_b sum_t g[t] x[t - s]
+        dx[:, :, :N - s] += k[None, :, s, None] * g[:, :, s:]
+        dk[:, s] = np.sum(g[:, :, s:] * x[:, :, :N - s], axis=(0, 2))
+    du = dx * w if w is not None else dx
+    dw = dx * u if w is not None else None
+    return du, dk, dw, dv
+
+
+def _bin_keep(mask_row, N: int) -> np.ndarray:
+    """Kept flag of each bin f < 2N: bin f follows its mirror 2N - f; rfft bins
+    [0, N] form 128 blocks of N/128 bins and the Nyquist bin joins block 127."""
+    M = 2 * N
+    f = np.arange(M)
+    fr = np.where(f <= N, f, M - f)
+    blk = np.minimum(fr // (N // 128), 127)
+    return np.asarray(mask_row, dtype=np.uint8)[blk] != 0
+
+
+def fft_bwd(u, k, dy, w=None, v=None, mask=None, lib=None):
+    """Route F gradients through the oracle's FFT (2N points), optional (H, 128) mask."""
+    u, k, dy = _f64(u), _f64(k), _f64(dy)
+    w, v = _f64(w), _f64(v)
+    B, H, N = u.shape
+    L = k.shape[1]
+    M = 2 * N
+    x = u * w if w is not None else u.copy()
+    g = dy * v if v is not None else dy.copy()
+    dx = np.empty((B, H, N))
+    c = np.empty((B, H, N))
+    dk = np.empty((H, L))
+    for h in range(H):
+        kpad = np.zeros(M)
+        kpad[:L] = k[h]
+        K = fft(kpad, -1, lib)
+        keep = np.ones(M, dtype=bool) if mask is None else _bin_keep(mask[h], N)
+        K = np.where(keep, K, 0.0)
+        R = np.zeros(M, dtype=np.complex128)
+        for b in range(B):
+            xp = np.zeros(M)
+            xp[:N] = x[b, h]
+            gp = np.zeros(M)
+            gp[:N] = g[b, h]
+            X = fft(xp, -1, lib)
+            G = fft(gp, -1, lib)
+            c[b, h] = fft(X * K, +1, lib).real[:N] / M
+            dx[b, h] = fft(G * np.conj(K), +1, lib).real[:N] / M
+            R += G * np.conj(X)
+        dk[h] = fft(np.where(keep, R, 0.0), +1, lib).real[:L] / M
+    du = dx * w if w is not None else dx
+    dw = dx * u if w is not None else None
+    dv = dy * c if v is not None else None
+    return du, dk, dw, dv
+
+
 def rel_l2(a, b) -> float:
     """||a - b||_2 / ||b||_2 in float64 (b is the oracle's value)."""
     a = np.asarray(a, dtype=np.float64)
