@@ -116,6 +116,31 @@ fftconv_status_t fftconv_fwd(const void *u, const void *K_f, const void *w, cons
                              const uint8_t *sparsity_mask, fftconv_dtype_t dtype,
                              void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Device scratch bytes fftconv_bwd needs for this shape (0 for unsupported
+ * N or dtype).  It holds the conjugated spectrum, u*w, the spectra of the
+ * B*H sequences u*w, their correlations with v*dy, and the forward
+ * workspace. */
+size_t fftconv_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, fftconv_dtype_t dtype);
+
+/* Backward pass of fftconv_fwd: the gradients of sum(dy * out) (the
+ * convolutions are trained, FlashFFTConv summary page, "Key results"), with
+ * x = u*w and g = v*dy:
+ *   dv = dy * conv(x, k)                       (needs v; NULL = skip)
+ *   du = w * corr(g, k),  dw = u * corr(g, k)  (dw needs w; NULL = skip)
+ *   dk[h, s] = sum_b sum_t g[b,h,t] x[b,h,t-s], s < L_filter  (NULL = skip)
+ * where corr(g, k)[t] = sum_s k[s] g[t+s] is the adjoint of the causal
+ * convolution: the forward kernels run on the conjugated spectrum of K_f.
+ * With a sparsity mask the gradients are those of the masked forward pass.
+ *   dy, u, w, v  (B, H, N) device arrays as in fftconv_fwd (w, v may be NULL)
+ *   K_f          the spectrum fftconv_fwd used (same H, L_filter, N, dtype)
+ *   du, dw, dv   (B, H, N) outputs; dk (H, L_filter) output, all in dtype
+ *   workspace    at least fftconv_bwd_workspace_bytes(B, H, N, dtype) bytes
+ * Asynchronous on stream; outputs must not overlap inputs. */
+fftconv_status_t fftconv_bwd(const void *dy, const void *u, const void *K_f, const void *w, const void *v,
+                             void *du, void *dk, void *dw, void *dv, int64_t B, int64_t H, int64_t N,
+                             int64_t L_filter, const uint8_t *sparsity_mask, fftconv_dtype_t dtype,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Static text for a status code. */
 const char *fftconv_status_string(fftconv_status_t status);
 

@@ -55,6 +55,10 @@ def _load():
     lib.fftconv_prepare_filter.restype = ctypes.c_int
     lib.fftconv_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, ctypes.c_int, vp, sz, vp]
     lib.fftconv_fwd.restype = ctypes.c_int
+    lib.fftconv_bwd_workspace_bytes.argtypes = [i64, i64, i64, ctypes.c_int]
+    lib.fftconv_bwd_workspace_bytes.restype = sz
+    lib.fftconv_bwd.argtypes = [vp] * 9 + [i64, i64, i64, i64, vp, ctypes.c_int, vp, sz, vp]
+    lib.fftconv_bwd.restype = ctypes.c_int
     lib.fftconv_status_string.argtypes = [ctypes.c_int]
     lib.fftconv_status_string.restype = ctypes.c_char_p
     lib.fftconv_last_error.argtypes = []
@@ -150,6 +154,28 @@ def fftconv_fwd(u: torch.Tensor, K_f: torch.Tensor, w: torch.Tensor | None,
         _stream(stream, u.device)))
 
 
+def fftconv_bwd_workspace_bytes(B: int, H: int, N: int, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    return int(_load().fftconv_bwd_workspace_bytes(B, H, N, code))
+
+
+def fftconv_bwd(dy: torch.Tensor, u: torch.Tensor, K_f: torch.Tensor, w: torch.Tensor | None,
+                v: torch.Tensor | None, du: torch.Tensor | None, dk: torch.Tensor | None,
+                dw: torch.Tensor | None, dv: torch.Tensor | None, L_filter: int,
+                sparsity_mask: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                stream=None) -> None:
+    """Gradients of sum(dy * fftconv_fwd(u, K_f, w, v)) into du, dk, dw, dv (None = skip)."""
+    for name, t in (("dy", dy), ("u", u), ("K_f", K_f), ("w", w), ("v", v), ("du", du), ("dk", dk),
+                    ("dw", dw), ("dv", dv), ("sparsity_mask", sparsity_mask), ("workspace", workspace)):
+        _dev_tensor(t, name)
+    B, H, N = u.shape
+    _check(_load().fftconv_bwd(
+        _ptr(dy), _ptr(u), _ptr(K_f), _ptr(w), _ptr(v), _ptr(du), _ptr(dk), _ptr(dw), _ptr(dv),
+        B, H, N, L_filter, _ptr(sparsity_mask), dtype_code(u.dtype), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(stream, u.device)))
+
+
 def fftconv_export_filter_rfft(K_f: torch.Tensor, H: int, N: int, dtype, stream=None) -> np.ndarray:
     """Synchronous: natural-order rfft bins (H, N+1) complex128 decoded from K_f."""
     _dev_tensor(K_f, "K_f")
@@ -183,3 +209,19 @@ def causal_conv(u, k, w=None, v=None, sparsity_mask=None, stream=None):
     out = torch.empty_like(u)
     fftconv_fwd(u, K_f, w, v, out, L, sparsity_mask, ws, stream)
     return out
+
+
+def causal_conv_bwd(u, k, dy, w=None, v=None, sparsity_mask=None, stream=None):
+    """Prepare k and run one backward call; returns (du, dk, dw, dv), None for absent gates."""
+    B, H, N = u.shape
+    L = k.shape[1]
+    K_f = alloc_filter(H, N, u.dtype, u.device)
+    ws_p = alloc_workspace(1, H, N, u.dtype, u.device)
+    fftconv_prepare_filter(k, N, K_f, ws_p, stream)
+    ws = torch.empty(fftconv_bwd_workspace_bytes(B, H, N, u.dtype), dtype=torch.uint8, device=u.device)
+    du = torch.empty_like(u)
+    dk = torch.empty((H, L), dtype=u.dtype, device=u.device)
+    dw = torch.empty_like(u) if w is not None else None
+    dv = torch.empty_like(u) if v is not None else None
+    fftconv_bwd(dy, u, K_f, w, v, du, dk, dw, dv, L, sparsity_mask, ws, stream)
+    return du, dk, dw, dv

@@ -516,6 +516,151 @@ fftconv_status_t fftconv_fwd(const void *u, const void *K_f, const void *w, cons
     return ok();
 }
 
+// ---- backward pass ---------------------------------------------------------
+// Workspace regions, each 256-byte aligned: the conjugated spectrum of K_f;
+// x = u w; the spectra of the sequences x as filters of their own channel;
+// the per-sequence correlations; the repeated mask rows; the forward
+// workspace (the same size serves the B*H-channel prepare and forward).
+struct BwdLayout {
+    size_t kc, x, kx, part, mrep, fws, total;
+};
+
+static BwdLayout bwd_layout(int64_t B, int64_t H, int64_t N, fftconv_dtype_t dtype) {
+    BwdLayout o{};
+    const int64_t S = B * H;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align_up(off + bytes, 256);
+        return at;
+    };
+    o.kc = take(fftconv_filter_bytes(H, N, dtype));
+    o.x = take((size_t)S * (size_t)N * elem_bytes(dtype));
+    o.kx = take(S > 0 ? fftconv_filter_bytes(S, N, dtype) : 0);
+    o.part = take((size_t)S * (size_t)N * elem_bytes(dtype));
+    o.mrep = take((size_t)S * kMaskBlocks);
+    o.fws = take(fftconv_workspace_bytes(1, S, N, dtype));
+    o.total = off;
+    return o;
+}
+
+size_t fftconv_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, fftconv_dtype_t dtype) {
+    const int l = log2_exact(N);
+    if (l < kMinLog || l > kMaxLog || B < 0 || H < 1 || !dtype_ok(dtype)) return 0;
+    return bwd_layout(B, H, N, dtype).total;
+}
+
+// Conjugate every stored bin of a prepared spectrum of H channels (src may be dst).
+static hipError_t conj_spectrum(const void *src, void *dst, int64_t H, int64_t N, fftconv_dtype_t dtype,
+                                hipStream_t stream) {
+    const int l = log2_exact(N);
+    const size_t boff = kf_bins_off(H);
+    hipError_t e = hipSuccess;
+    if (src != dst) e = hipMemcpyAsync(dst, src, boff, hipMemcpyDeviceToDevice, stream);
+    if (e != hipSuccess) return e;
+    const bool pair = l <= kFusedMaxLog && (use_pair_kernel(l, dtype) || use_pair3_kernel(l, dtype));
+    const int kind = pair ? 0 : (dtype == FFTCONV_F32 ? 2 : 1);
+    const int64_t per_channel = kf_slots(l, dtype) * (int64_t)bin_bytes(dtype);
+    return launch_conj_bins(static_cast<const char *>(src) + boff, static_cast<char *>(dst) + boff, H,
+                            per_channel, kind, stream);
+}
+
+fftconv_status_t fftconv_bwd(const void *dy, const void *u, const void *K_f, const void *w, const void *v,
+                             void *du, void *dk, void *dw, void *dv, int64_t B, int64_t H, int64_t N,
+                             int64_t L, const uint8_t *mask, fftconv_dtype_t dtype, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+    g_last_error.clear();
+    if (!dtype_ok(dtype)) return fail(FFTCONV_ERR_UNSUPPORTED, "dtype %d is not supported", (int)dtype);
+    const int l = log2_exact(N);
+    if (l < kMinLog || l > kMaxLog)
+        return fail(FFTCONV_ERR_UNSUPPORTED, "N=%lld must be a power of two in [2^%d, 2^%d]",
+                    (long long)N, kMinLog, kMaxLog);
+    if (B < 0 || H < 0)
+        return fail(FFTCONV_ERR_INVALID_ARGUMENT, "B=%lld and H=%lld must be >= 0", (long long)B,
+                    (long long)H);
+    if (L < 1 || L > N)
+        return fail(FFTCONV_ERR_INVALID_ARGUMENT, "L_filter=%lld must be in [1, N=%lld]",
+                    (long long)L, (long long)N);
+    if (H == 0) return ok();
+    if (dw && !w) return fail(FFTCONV_ERR_INVALID_ARGUMENT, "dw needs the input gate w");
+    if (dv && !v) return fail(FFTCONV_ERR_INVALID_ARGUMENT, "dv needs the output gate v");
+    if (!K_f || (B > 0 && (!dy || !u)))
+        return fail(FFTCONV_ERR_INVALID_ARGUMENT, "dy, u and K_f must be non-null");
+    const void *ptrs[] = {dy, u, K_f, w, v, du, dk, dw, dv, mask};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return fail(FFTCONV_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+    const size_t nbytes = (size_t)B * (size_t)H * (size_t)N * elem_bytes(dtype);
+    const size_t kbytes = (size_t)H * (size_t)L * elem_bytes(dtype);
+    const void *ins[] = {dy, u, w, v};
+    for (const void *o : {(const void *)du, (const void *)dw, (const void *)dv})
+        for (const void *i : ins)
+            if (o && i && overlap(o, nbytes, i, nbytes))
+                return fail(FFTCONV_ERR_INVALID_ARGUMENT, "a gradient overlaps an input");
+    if (dk)
+        for (const void *i : ins)
+            if (i && overlap(dk, kbytes, i, nbytes))
+                return fail(FFTCONV_ERR_INVALID_ARGUMENT, "dk overlaps an input");
+    const BwdLayout lay = bwd_layout(B, H, N, dtype);
+    if (!workspace || workspace_bytes < lay.total)
+        return fail(FFTCONV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, lay.total);
+    if (!aligned16(workspace)) return fail(FFTCONV_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+
+    char *ws = static_cast<char *>(workspace);
+    void *fws = ws + lay.fws;
+    const size_t fws_bytes = lay.total - lay.fws;
+    fftconv_status_t st = FFTCONV_OK;
+    // dv = dy * conv(u w, k): the forward pass with dy as the output gate
+    if (dv && B > 0) {
+        st = fftconv_fwd(u, K_f, w, dy, dv, B, H, N, L, mask, dtype, fws, fws_bytes, stream);
+        if (st != FFTCONV_OK) return st;
+    }
+    // du = w * corr(v dy, k), dw = u * corr(v dy, k): conjugated spectrum
+    if ((du || dw) && B > 0) {
+        hipError_t e = conj_spectrum(K_f, ws + lay.kc, H, N, dtype, stream);
+        if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "conjugating K_f: %s", hipGetErrorString(e));
+        if (du) {
+            st = fftconv_fwd(dy, ws + lay.kc, v, w, du, B, H, N, L, mask, dtype, fws, fws_bytes, stream);
+            if (st != FFTCONV_OK) return st;
+        }
+        if (dw) {
+            st = fftconv_fwd(dy, ws + lay.kc, v, u, dw, B, H, N, L, mask, dtype, fws, fws_bytes, stream);
+            if (st != FFTCONV_OK) return st;
+        }
+    }
+    // dk[h, s] = sum_b corr(v dy, u w)[b, h, s]: each x = u w is the filter of
+    // its own channel b H + h; the mask rows repeat per batch row
+    if (dk) {
+        const int64_t S = B * H;
+        hipError_t e = hipSuccess;
+        if (S > 0) {
+            const void *x = u;
+            if (w) {
+                e = launch_gate_product(dtype, u, w, ws + lay.x, S * N, stream);
+                if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "gate product: %s", hipGetErrorString(e));
+                x = ws + lay.x;
+            }
+            st = fftconv_prepare_filter(x, S, N, N, dtype, ws + lay.kx, fftconv_filter_bytes(S, N, dtype), fws,
+                                        fws_bytes, stream);
+            if (st != FFTCONV_OK) return st;
+            e = conj_spectrum(ws + lay.kx, ws + lay.kx, S, N, dtype, stream);
+            if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "conjugating spectra: %s", hipGetErrorString(e));
+            const uint8_t *mrep = nullptr;
+            if (mask) {
+                e = launch_mask_repeat(mask, reinterpret_cast<uint8_t *>(ws + lay.mrep), H, S, stream);
+                if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "mask rows: %s", hipGetErrorString(e));
+                mrep = reinterpret_cast<const uint8_t *>(ws + lay.mrep);
+            }
+            st = fftconv_fwd(dy, ws + lay.kx, v, nullptr, ws + lay.part, 1, S, N, N, mrep, dtype, fws, fws_bytes,
+                             stream);
+            if (st != FFTCONV_OK) return st;
+        }
+        e = launch_dk_reduce(dtype, ws + lay.part, dk, B, H, N, L, stream);
+        if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "dk reduction: %s", hipGetErrorString(e));
+    }
+    g_last_error.clear();
+    return ok();
+}
+
 fftconv_status_t fftconv_export_filter_rfft(const void *K_f, int64_t H, int64_t N,
                                             fftconv_dtype_t dtype, double *host_out,
                                             hipStream_t stream) {

@@ -1,0 +1,136 @@
+// bwd.hip -- small kernels of the backward pass.  The transforms themselves
+// run on the forward kernels (the host side in api.cpp wires them):
+//
+//   dv = dy * conv(u w, k)            forward call with dy as the output gate
+//   du = w * corr(v dy, k)            forward call on the conjugated spectrum
+//   dw = u * corr(v dy, k)            (correlation = product with conj K)
+//   dk[h, s] = sum_b corr(v dy, u w)[b, h, s],  s < L
+//
+// For dk every sequence x = u w is prepared as a filter of its own channel
+// (b, h), its spectrum conjugated, and the forward kernels correlate v dy with
+// it; a reduction over b follows.  With a frequency mask, the mask multiplies
+// the conjugated spectra as it multiplies K in the forward pass, which is the
+// adjoint because the mask is real.
+#include "fft_device.hpp"
+#include "fftconv_internal.hpp"
+
+#include <type_traits>
+
+namespace fftconv {
+
+// Conjugate the stored bins of a prepared spectrum (dst may equal src).  The
+// bins are viewed as 32-bit words; `words_per_channel` words per channel.
+//   PAIR layouts: 16-byte chunks re[4], im[4] (fp16): words 2 and 3 of each
+//     chunk hold the imaginary parts.
+//   NATURAL / ROWS: slot 0 holds (K[0], K[N]), both real, and stays; every
+//     other slot is one complex bin whose imaginary part is its upper half
+//     (fp16 pair: the high 16 bits of the word; fp32 pair: the second word).
+__global__ void __launch_bounds__(256)
+conj_bins_kernel(const uint32_t *__restrict__ src, uint32_t *__restrict__ dst, int64_t nwords,
+                 int64_t words_per_channel, int kind) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nwords; i += (int64_t)gridDim.x * 256) {
+        const int64_t j = i % words_per_channel;
+        uint32_t m = 0;
+        if (kind == 0) {                       // PAIR / PAIR3 chunks
+            m = (j & 3) >= 2 ? 0x80008000u : 0u;
+        } else if (kind == 1) {                // fp16 complex slots
+            m = j != 0 ? 0x80000000u : 0u;
+        } else {                               // fp32 complex slots
+            m = (j >= 2 && (j & 1)) ? 0x80000000u : 0u;
+        }
+        dst[i] = src[i] ^ m;
+    }
+}
+
+// x = u * w elementwise (the product formed in fp32, rounded once to T).
+template <typename T>
+__global__ void __launch_bounds__(256)
+gate_product_kernel(const T *__restrict__ u, const T *__restrict__ w, T *__restrict__ x, int64_t npairs) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < npairs; i += (int64_t)gridDim.x * 256) {
+        const float2 a = io<T>::load2(u + 2 * i), b = io<T>::load2(w + 2 * i);
+        io<T>::store2(x + 2 * i, make_float2(a.x * b.x, a.y * b.y));
+    }
+}
+
+// mask rows of the per-sequence channels: dst[c] = mask[c mod H]
+__global__ void __launch_bounds__(128)
+mask_repeat_kernel(const uint8_t *__restrict__ mask, uint8_t *__restrict__ dst, int64_t H) {
+    const int64_t c = blockIdx.x;
+    dst[c * kMaskBlocks + threadIdx.x] = mask[(c % H) * kMaskBlocks + threadIdx.x];
+}
+
+// dk[h, s] = sum_b part[b H + h, s] for s < L (fp32 sum, rounded once to T)
+template <typename T>
+__global__ void __launch_bounds__(256)
+dk_reduce_kernel(const T *__restrict__ part, T *__restrict__ dk, int64_t B, int64_t H, int64_t N,
+                 int64_t L) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < H * L; i += (int64_t)gridDim.x * 256) {
+        const int64_t h = i / L, s = i - h * L;
+        float acc = 0.f;
+        for (int64_t b = 0; b < B; ++b) acc += io<T>::load1(part + (b * H + h) * N + s);
+        if constexpr (std::is_same<T, float>::value) {
+            dk[i] = acc;
+        } else if constexpr (std::is_same<T, __half>::value) {
+            dk[i] = __float2half_rn(acc);
+        } else {
+            dk[i] = __float2bfloat16(acc);
+        }
+    }
+}
+
+static unsigned grid_for(int64_t n) {
+    int64_t g = (n + 255) / 256;
+    return (unsigned)(g > 65536 ? 65536 : (g < 1 ? 1 : g));
+}
+
+hipError_t launch_conj_bins(const void *src, void *dst, int64_t H, int64_t bytes_per_channel, int kind,
+                            hipStream_t stream) {
+    const int64_t wpc = bytes_per_channel / 4, nwords = H * wpc;
+    hipLaunchKernelGGL(conj_bins_kernel, dim3(grid_for(nwords)), dim3(256), 0, stream,
+                       (const uint32_t *)src, (uint32_t *)dst, nwords, wpc, kind);
+    return hipGetLastError();
+}
+
+hipError_t launch_gate_product(int st, const void *u, const void *w, void *x, int64_t n, hipStream_t stream) {
+    const int64_t npairs = n / 2;
+    switch (st) {
+    case ST_F32:
+        hipLaunchKernelGGL(gate_product_kernel<float>, dim3(grid_for(npairs)), dim3(256), 0, stream,
+                           (const float *)u, (const float *)w, (float *)x, npairs);
+        break;
+    case ST_F16:
+        hipLaunchKernelGGL(gate_product_kernel<__half>, dim3(grid_for(npairs)), dim3(256), 0, stream,
+                           (const __half *)u, (const __half *)w, (__half *)x, npairs);
+        break;
+    default:
+        hipLaunchKernelGGL(gate_product_kernel<__hip_bfloat16>, dim3(grid_for(npairs)), dim3(256), 0, stream,
+                           (const __hip_bfloat16 *)u, (const __hip_bfloat16 *)w, (__hip_bfloat16 *)x, npairs);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_mask_repeat(const uint8_t *mask, uint8_t *dst, int64_t H, int64_t C, hipStream_t stream) {
+    hipLaunchKernelGGL(mask_repeat_kernel, dim3((unsigned)C), dim3(kMaskBlocks), 0, stream, mask, dst, H);
+    return hipGetLastError();
+}
+
+hipError_t launch_dk_reduce(int st, const void *part, void *dk, int64_t B, int64_t H, int64_t N, int64_t L,
+                            hipStream_t stream) {
+    const dim3 grid(grid_for(H * L));
+    switch (st) {
+    case ST_F32:
+        hipLaunchKernelGGL(dk_reduce_kernel<float>, grid, dim3(256), 0, stream, (const float *)part,
+                           (float *)dk, B, H, N, L);
+        break;
+    case ST_F16:
+        hipLaunchKernelGGL(dk_reduce_kernel<__half>, grid, dim3(256), 0, stream, (const __half *)part,
+                           (__half *)dk, B, H, N, L);
+        break;
+    default:
+        hipLaunchKernelGGL(dk_reduce_kernel<__hip_bfloat16>, grid, dim3(256), 0, stream,
+                           (const __hip_bfloat16 *)part, (__hip_bfloat16 *)dk, B, H, N, L);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace fftconv

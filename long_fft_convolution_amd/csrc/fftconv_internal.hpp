@@ -125,6 +125,13 @@ hipError_t launch_fused_conv(int logn, int st, const void *u,
 hipError_t launch_fused_prepare(int logn, int st, const void *k, int64_t L, void *kbins,
                                 const float *kscale, const Tables &tb, int64_t H,
                                 hipStream_t stream);
+// backward-pass helpers (bwd.hip); kind: 0 PAIR chunks, 1 fp16 slots, 2 fp32 slots
+hipError_t launch_conj_bins(const void *src, void *dst, int64_t H, int64_t bytes_per_channel, int kind,
+                            hipStream_t stream);
+hipError_t launch_gate_product(int st, const void *u, const void *w, void *x, int64_t n, hipStream_t stream);
+hipError_t launch_mask_repeat(const uint8_t *mask, uint8_t *dst, int64_t H, int64_t C, hipStream_t stream);
+hipError_t launch_dk_reduce(int st, const void *part, void *dk, int64_t B, int64_t H, int64_t N, int64_t L,
+                            hipStream_t stream);
 hipError_t launch_filter_scale(int st, const void *k, int64_t H, int64_t L, int norm_log2,
                                int target_log2, float *kscale, hipStream_t stream);
 

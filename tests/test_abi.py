@@ -121,3 +121,47 @@ def test_prepare_validation():
     assert call(k=0x10002) == 1
     assert call(K_f=0x10000 + 256) == 1 and "overlaps" in fc.fftconv_last_error()
     assert call(N=1 << 20, L=5, kb=1 << 30) == 3
+
+
+def test_bwd_workspace_bytes():
+    F16, F32 = fc.FFTCONV_F16, fc.FFTCONV_F32
+    # conjugated K_f + u*w + the B*H sequence spectra + correlations + mask rows
+    # + the forward workspace, each region rounded up to 256 bytes
+    B, H, N = 2, 3, 1024
+
+    def up(x):
+        return (x + 255) // 256 * 256
+
+    S = B * H
+    want = (up(fc.fftconv_filter_bytes(H, N, F16)) + up(S * N * 2) + up(fc.fftconv_filter_bytes(S, N, F16))
+            + up(S * N * 2) + up(S * 128) + up(fc.fftconv_workspace_bytes(1, S, N, F16)))
+    assert fc.fftconv_bwd_workspace_bytes(B, H, N, F16) == want
+    assert fc.fftconv_bwd_workspace_bytes(B, H, 1 << 20, F32) > 0
+    assert fc.fftconv_bwd_workspace_bytes(B, H, 1000, F16) == 0
+    assert fc.fftconv_bwd_workspace_bytes(B, 0, N, F16) == 0
+
+
+def test_bwd_validation():
+    lib = fc.lib()
+    N = 1024
+    good = dict(dy=0x10000, u=0x20000, K_f=0x30000, w=0x40000, v=0x50000, du=0x60000, dk=0x70000,
+                dw=0x80000, dv=0x90000, B=1, H=2, N=N, L=N, m=None, dt=0, ws=0x1000000, wsb=1 << 40)
+
+    def call(**kw):
+        a = dict(good)
+        a.update(kw)
+        return lib.fftconv_bwd(a["dy"], a["u"], a["K_f"], a["w"], a["v"], a["du"], a["dk"], a["dw"], a["dv"],
+                               a["B"], a["H"], a["N"], a["L"], a["m"], a["dt"], a["ws"], a["wsb"], None)
+
+    assert call(dt=7) == 2
+    assert call(N=1000) == 2
+    assert call(L=0) == 1
+    assert call(B=-1) == 1
+    assert call(H=0) == 0
+    assert call(w=None) == 1 and "dw needs" in fc.fftconv_last_error()
+    assert call(v=None) == 1 and "dv needs" in fc.fftconv_last_error()
+    assert call(dy=None) == 1
+    assert call(du=0x60004) == 1 and "aligned" in fc.fftconv_last_error()
+    assert call(du=0x20000 + 256) == 1 and "overlaps" in fc.fftconv_last_error()
+    assert call(ws=None) == 3
+    assert call(wsb=16) == 3
