@@ -1,6 +1,6 @@
 """Benchmark: one step = one fftconv_fwd call over a whole synthetic batch.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass fwd|bwd]
 
 Prints ONE JSON line (stdout).  The default workload is gated_fp16_n1k
 (B=64, H=768, N=1024, fp16 storage, gated, filter as long as the sequence).
@@ -11,6 +11,9 @@ algorithmic HBM bytes of one forward call divided by the average duration of
 the dominant kernel, timed with HIP events on the stream it runs on.  The
 cpu_baseline object times the CPU oracle (route F) on a bounded sample of the
 same workload on this host's cores.
+
+With --pass bwd one step is one fftconv_bwd call (du, dk, dw, dv) instead;
+that line names its own metric and carries no CPU baseline.
 """
 from __future__ import annotations
 
@@ -124,6 +127,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gated_fp16_n1k", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd",
+                    help="time the forward call (default) or the backward call")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain device copy of the activation bytes (counter scale)")
     args = ap.parse_args()
@@ -150,6 +155,9 @@ def main():
 
     def step():
         fc.fftconv_fwd(u, K_f, w, v, out, wl.L, mask, ws)
+
+    if args.which == "bwd":
+        return bench_bwd(args, wl, dev, u, K_f, w, v, mask)
 
     for _ in range(args.warmup):
         step()
@@ -215,6 +223,62 @@ def main():
                      "traffic": measured_traffic(wl.name), "algorithmic_bytes": alg,
                      "kernel_ms": kern_ms},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def bench_bwd(args, wl, dev, u, K_f, w, v, mask):
+    """One step = one fftconv_bwd call producing du, dk, dw, dv."""
+    g = torch.Generator().manual_seed(4242)
+    dy = torch.randn(u.shape, generator=g, dtype=torch.float32).to(u.dtype).to(dev)
+    du = torch.empty_like(u)
+    dk = torch.empty((wl.H, wl.L), dtype=u.dtype, device=dev)
+    dw = torch.empty_like(u) if w is not None else None
+    dv = torch.empty_like(u) if v is not None else None
+    ws = torch.empty(fc.fftconv_bwd_workspace_bytes(wl.B, wl.H, wl.N, u.dtype), dtype=torch.uint8, device=dev)
+
+    def step():
+        fc.fftconv_bwd(dy, u, K_f, w, v, du, dk, dw, dv, wl.L, mask, ws)
+
+    for _ in range(args.warmup):
+        step()
+    stream = torch.cuda.current_stream(dev)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    elems = wl.B * wl.H * wl.N
+    e = ELEM[wl.dtype]
+    # what the backward must move: dy, u (+ w, v) read, du (+ dw, dv) written,
+    # dk written, the spectrum read once per channel
+    nact = 2 + (2 if w is not None else 0) + (2 if v is not None else 0)
+    alg = elems * e * nact + wl.H * wl.L * e + wl.H * (wl.N + 1) * (8 if wl.dtype == "f32" else 4)
+    achieved = alg / (ms_per_step / 1e3) / 1e9
+    log(f"bench: bwd {ms_per_step * 1e3:.1f} us/step, {elems / (ms_per_step / 1e3):.3e} elems/s")
+    rec = {
+        "metric": "FFT-conv bwd (du, dk, dw, dv) B·H·N elems/s, 1 GPU",
+        "value": elems / (ms_per_step / 1e3),
+        "unit": "elems/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": path_of(wl)[1],
+        "data": "synthetic (seeded N(0,1) activations and output gradient, decaying random filter)",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "L_filter": wl.L,
+                   "gated": wl.gated, "storage": wl.dtype, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "fftconv_bwd (several launches)", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes": alg, "kernel_ms": ms_per_step},
+        "cpu_baseline": None,
     }
     print(json.dumps(rec), flush=True)
 

@@ -374,11 +374,23 @@ size_t fftconv_workspace_bytes(int64_t B, int64_t H, int64_t N, fftconv_dtype_t 
     return (size_t)S * ((size_t)N * (size_t)mp_ws_bytes(dtype) + kMpSelfBytes);
 }
 
+// The prepare steps; conj = true stores the conjugated spectrum (backward pass).
+static fftconv_status_t prepare_impl(const void *k, int64_t H, int64_t L, int64_t N, fftconv_dtype_t dtype,
+                                     void *K_f, size_t K_f_bytes, void *workspace, size_t workspace_bytes,
+                                     bool conj, hipStream_t stream);
+
 fftconv_status_t fftconv_prepare_filter(const void *k, int64_t H, int64_t L, int64_t N,
                                         fftconv_dtype_t dtype, void *K_f, size_t K_f_bytes,
                                         void *workspace, size_t workspace_bytes,
                                         hipStream_t stream) {
+    return prepare_impl(k, H, L, N, dtype, K_f, K_f_bytes, workspace, workspace_bytes, false, stream);
+}
+
+static fftconv_status_t prepare_impl(const void *k, int64_t H, int64_t L, int64_t N, fftconv_dtype_t dtype,
+                                     void *K_f, size_t K_f_bytes, void *workspace, size_t workspace_bytes,
+                                     bool conj, hipStream_t stream) {
     g_last_error.clear();
+    const float ysgn = conj ? -1.0f : 1.0f;
     if (!dtype_ok(dtype)) return fail(FFTCONV_ERR_UNSUPPORTED, "dtype %d is not supported", (int)dtype);
     const int l = log2_exact(N);
     if (l < kMinLog || l > kMaxLog)
@@ -429,12 +441,12 @@ fftconv_status_t fftconv_prepare_filter(const void *k, int64_t H, int64_t L, int
     if (fused) {
         Tables tb{};
         e = get_tables(l, &tb);
-        if (e == hipSuccess) e = launch_fused_prepare(l, dtype, k, L, kbins, kscale, tb, H, stream);
+        if (e == hipSuccess) e = launch_fused_prepare(l, dtype, k, L, kbins, kscale, tb, H, ysgn, stream);
     } else {
         const int64_t c = mp_chunk(l, dtype);
         for (int64_t h0 = 0; h0 < H && e == hipSuccess; h0 += c) {
             const int64_t n = H - h0 < c ? H - h0 : c;
-            e = launch_multipass_prepare(l, dtype, k, L, kbins, kscale, workspace, H, h0, n, stream);
+            e = launch_multipass_prepare(l, dtype, k, L, kbins, kscale, workspace, H, h0, n, ysgn, stream);
         }
     }
     if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "prepare launch: %s", hipGetErrorString(e));
@@ -639,11 +651,10 @@ fftconv_status_t fftconv_bwd(const void *dy, const void *u, const void *K_f, con
                 if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "gate product: %s", hipGetErrorString(e));
                 x = ws + lay.x;
             }
-            st = fftconv_prepare_filter(x, S, N, N, dtype, ws + lay.kx, fftconv_filter_bytes(S, N, dtype), fws,
-                                        fws_bytes, stream);
+            // the sequences' spectra, stored conjugated
+            st = prepare_impl(x, S, N, N, dtype, ws + lay.kx, fftconv_filter_bytes(S, N, dtype), fws, fws_bytes,
+                              true, stream);
             if (st != FFTCONV_OK) return st;
-            e = conj_spectrum(ws + lay.kx, ws + lay.kx, S, N, dtype, stream);
-            if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "conjugating spectra: %s", hipGetErrorString(e));
             const uint8_t *mrep = nullptr;
             if (mask) {
                 e = launch_mask_repeat(mask, reinterpret_cast<uint8_t *>(ws + lay.mrep), H, S, stream);

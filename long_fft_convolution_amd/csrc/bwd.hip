@@ -18,27 +18,31 @@
 
 namespace fftconv {
 
-// Conjugate the stored bins of a prepared spectrum (dst may equal src).  The
-// bins are viewed as 32-bit words; `words_per_channel` words per channel.
-//   PAIR layouts: 16-byte chunks re[4], im[4] (fp16): words 2 and 3 of each
-//     chunk hold the imaginary parts.
+// Conjugate the stored bins of a prepared spectrum (dst may equal src).  A
+// channel's bins are viewed as 16-byte units (q4_per_channel of them).
+//   PAIR layouts: each unit is a chunk re[4], im[4] (fp16): words z, w hold
+//     the imaginary parts.
 //   NATURAL / ROWS: slot 0 holds (K[0], K[N]), both real, and stays; every
 //     other slot is one complex bin whose imaginary part is its upper half
-//     (fp16 pair: the high 16 bits of the word; fp32 pair: the second word).
+//     (fp16 pair: the high 16 bits of a word; fp32 pair: the odd words).
+// grid (units / 256, channel stride); lanes index units of one channel.
 __global__ void __launch_bounds__(256)
-conj_bins_kernel(const uint32_t *__restrict__ src, uint32_t *__restrict__ dst, int64_t nwords,
-                 int64_t words_per_channel, int kind) {
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nwords; i += (int64_t)gridDim.x * 256) {
-        const int64_t j = i % words_per_channel;
-        uint32_t m = 0;
-        if (kind == 0) {                       // PAIR / PAIR3 chunks
-            m = (j & 3) >= 2 ? 0x80008000u : 0u;
-        } else if (kind == 1) {                // fp16 complex slots
-            m = j != 0 ? 0x80000000u : 0u;
-        } else {                               // fp32 complex slots
-            m = (j >= 2 && (j & 1)) ? 0x80000000u : 0u;
-        }
-        dst[i] = src[i] ^ m;
+conj_bins_kernel(const uint4 *__restrict__ src, uint4 *__restrict__ dst, int64_t H, uint32_t q4_per_channel,
+                 int kind) {
+    const uint32_t q = blockIdx.x * 256u + threadIdx.x;
+    if (q >= q4_per_channel) return;
+    uint4 m;
+    if (kind == 0) {
+        m = make_uint4(0u, 0u, 0x80008000u, 0x80008000u);
+    } else if (kind == 1) {
+        m = make_uint4(q == 0 ? 0u : 0x80000000u, 0x80000000u, 0x80000000u, 0x80000000u);
+    } else {
+        m = make_uint4(0u, q == 0 ? 0u : 0x80000000u, 0u, 0x80000000u);
+    }
+    for (int64_t c = blockIdx.y; c < H; c += gridDim.y) {
+        const int64_t i = c * q4_per_channel + q;
+        const uint4 x = src[i];
+        dst[i] = make_uint4(x.x ^ m.x, x.y ^ m.y, x.z ^ m.z, x.w ^ m.w);
     }
 }
 
@@ -67,6 +71,7 @@ dk_reduce_kernel(const T *__restrict__ part, T *__restrict__ dk, int64_t B, int6
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < H * L; i += (int64_t)gridDim.x * 256) {
         const int64_t h = i / L, s = i - h * L;
         float acc = 0.f;
+#pragma unroll 8
         for (int64_t b = 0; b < B; ++b) acc += io<T>::load1(part + (b * H + h) * N + s);
         if constexpr (std::is_same<T, float>::value) {
             dk[i] = acc;
@@ -85,9 +90,10 @@ static unsigned grid_for(int64_t n) {
 
 hipError_t launch_conj_bins(const void *src, void *dst, int64_t H, int64_t bytes_per_channel, int kind,
                             hipStream_t stream) {
-    const int64_t wpc = bytes_per_channel / 4, nwords = H * wpc;
-    hipLaunchKernelGGL(conj_bins_kernel, dim3(grid_for(nwords)), dim3(256), 0, stream,
-                       (const uint32_t *)src, (uint32_t *)dst, nwords, wpc, kind);
+    const uint32_t q4 = (uint32_t)(bytes_per_channel / 16);
+    const dim3 grid((q4 + 255) / 256, (unsigned)(H < 4096 ? H : 4096));
+    hipLaunchKernelGGL(conj_bins_kernel, grid, dim3(256), 0, stream, (const uint4 *)src, (uint4 *)dst, H, q4,
+                       kind);
     return hipGetLastError();
 }
 

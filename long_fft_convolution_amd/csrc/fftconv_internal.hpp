@@ -122,9 +122,10 @@ hipError_t launch_fused_conv(int logn, int st, const void *u,
                              const void *w, const void *v, void *out, const void *kbins,
                              const float *kscale, const uint8_t *mask, const Tables &tb,
                              int64_t B, int64_t H, hipStream_t stream);
+// ysgn = -1 stores the conjugated spectrum (used by the backward pass)
 hipError_t launch_fused_prepare(int logn, int st, const void *k, int64_t L, void *kbins,
                                 const float *kscale, const Tables &tb, int64_t H,
-                                hipStream_t stream);
+                                float ysgn, hipStream_t stream);
 // backward-pass helpers (bwd.hip); kind: 0 PAIR chunks, 1 fp16 slots, 2 fp32 slots
 hipError_t launch_conj_bins(const void *src, void *dst, int64_t H, int64_t bytes_per_channel, int kind,
                             hipStream_t stream);
@@ -168,6 +169,6 @@ hipError_t launch_multipass_conv(int logn, int st, const void *u, const void *w,
                                  int64_t nseq, hipStream_t stream);
 hipError_t launch_multipass_prepare(int logn, int st, const void *k, int64_t L, void *kbins,
                                     const float *kscale, void *work, int64_t H, int64_t h0,
-                                    int64_t nseq, hipStream_t stream);
+                                    int64_t nseq, float ysgn, hipStream_t stream);
 
 }  // namespace fftconv

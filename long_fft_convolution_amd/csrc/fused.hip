@@ -231,7 +231,7 @@ template <int LOGN, typename T, typename TK, int LAYOUT>
 __global__ void __launch_bounds__(FusedPlan<LOGN>::THREADS)
 fused_prepare_kernel(const T *__restrict__ k, int64_t L, TK *__restrict__ kbins,
                      const float *__restrict__ kscale, const float2 *__restrict__ tw,
-                     const float2 *__restrict__ tw2, int64_t H) {
+                     const float2 *__restrict__ tw2, int64_t H, float ysgn) {
     using Pl = FusedPlan<LOGN>;
     constexpr int NC = Pl::NC, R = Pl::R, P = Pl::P, TS = Pl::TS, R1 = Pl::R1;
     extern __shared__ float2 lds[];
@@ -289,7 +289,9 @@ fused_prepare_kernel(const T *__restrict__ k, int64_t L, TK *__restrict__ kbins,
     auto index_of = [](int64_t f) -> int64_t {
         return LAYOUT == KF_PAIR3 ? pair3_kf_index(f) : pair_kf_index(f);
     };
+    // ysgn = -1 stores the conjugated spectrum (the correlation of the backward pass)
     auto put = [&](int f, float2 x) {
+        x.y *= ysgn;
         if (!PAIR) {
             kio<TK>::store(krow + f, x);
         } else {
@@ -359,7 +361,7 @@ static hipError_t launch_conv_t(const void *u, const void *w,
 
 template <int LOGN, typename T, typename TK>
 static hipError_t launch_prep_t(const void *k, int64_t L, void *kbins, const float *kscale,
-                                const Tables &tb, int64_t H, hipStream_t stream) {
+                                const Tables &tb, int64_t H, float ysgn, hipStream_t stream) {
     using Pl = FusedPlan<LOGN>;
     const int64_t blocks = (H + Pl::SPW - 1) / Pl::SPW;
     const size_t lds = (size_t)Pl::SPW * Pl::NC * sizeof(float2);
@@ -371,7 +373,7 @@ static hipError_t launch_prep_t(const void *k, int64_t L, void *kbins, const flo
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(Pl::THREADS), lds, stream,
-                       (const T *)k, L, (TK *)kbins, kscale, tb.tw, tb.tw2, H);
+                       (const T *)k, L, (TK *)kbins, kscale, tb.tw, tb.tw2, H, ysgn);
     return hipGetLastError();
 }
 
@@ -395,12 +397,12 @@ static hipError_t conv_by_type(int st, const void *u, const void *w,
 
 template <int LOGN>
 static hipError_t prep_by_type(int st, const void *k, int64_t L, void *kbins, const float *kscale,
-                               const Tables &tb, int64_t H, hipStream_t stream) {
+                               const Tables &tb, int64_t H, float ysgn, hipStream_t stream) {
     switch (st) {
-    case ST_F32: return launch_prep_t<LOGN, float, float2>(k, L, kbins, kscale, tb, H, stream);
-    case ST_F16: return launch_prep_t<LOGN, __half, __half2>(k, L, kbins, kscale, tb, H, stream);
+    case ST_F32: return launch_prep_t<LOGN, float, float2>(k, L, kbins, kscale, tb, H, ysgn, stream);
+    case ST_F16: return launch_prep_t<LOGN, __half, __half2>(k, L, kbins, kscale, tb, H, ysgn, stream);
     default:
-        return launch_prep_t<LOGN, __hip_bfloat16, __half2>(k, L, kbins, kscale, tb, H, stream);
+        return launch_prep_t<LOGN, __hip_bfloat16, __half2>(k, L, kbins, kscale, tb, H, ysgn, stream);
     }
 }
 
@@ -420,13 +422,13 @@ hipError_t launch_fused_conv(int logn, int st, const void *u,
 
 hipError_t launch_fused_prepare(int logn, int st, const void *k, int64_t L, void *kbins,
                                 const float *kscale, const Tables &tb, int64_t H,
-                                hipStream_t stream) {
+                                float ysgn, hipStream_t stream) {
     switch (logn) {
-    case 10: return prep_by_type<10>(st, k, L, kbins, kscale, tb, H, stream);
-    case 11: return prep_by_type<11>(st, k, L, kbins, kscale, tb, H, stream);
-    case 12: return prep_by_type<12>(st, k, L, kbins, kscale, tb, H, stream);
-    case 13: return prep_by_type<13>(st, k, L, kbins, kscale, tb, H, stream);
-    case 14: return prep_by_type<14>(st, k, L, kbins, kscale, tb, H, stream);
+    case 10: return prep_by_type<10>(st, k, L, kbins, kscale, tb, H, ysgn, stream);
+    case 11: return prep_by_type<11>(st, k, L, kbins, kscale, tb, H, ysgn, stream);
+    case 12: return prep_by_type<12>(st, k, L, kbins, kscale, tb, H, ysgn, stream);
+    case 13: return prep_by_type<13>(st, k, L, kbins, kscale, tb, H, ysgn, stream);
+    case 14: return prep_by_type<14>(st, k, L, kbins, kscale, tb, H, ysgn, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -307,7 +307,7 @@ static_assert(kP2LdsFloat2 >= 32 * kT1Row && kP2LdsFloat2 >= 8192, "pass-2 LDS")
 template <int N1, int N2, typename TK, bool PREPARE, bool MASKED>
 __device__ __forceinline__ void self_pairs(float2 *area, const TK *__restrict__ krow,
                                            TK *__restrict__ kout, BlockMask bm, float ks,
-                                           const MpArgs &ta, int tid) {
+                                           const MpArgs &ta, int tid, float ysgn) {
     constexpr int64_t NC = (int64_t)N1 * N2;
     const float sh = 1.0f / (ks * 4.0f * (float)NC);
     for (int it = tid; it <= N2; it += kMpThreads) {
@@ -327,8 +327,10 @@ __device__ __forceinline__ void self_pairs(float2 *area, const TK *__restrict__ 
             const float2 xe = cadd(zf, bc);
             const float2 xo = cmul_negi(csub(zf, bc));
             const float2 wxo = cmul(Wf, xo);
-            const float2 xf = cscale(cadd(xe, wxo), 0.5f * sh);
-            const float2 xg = cscale(cconj(csub(xe, wxo)), 0.5f * sh);
+            float2 xf = cscale(cadd(xe, wxo), 0.5f * sh);
+            float2 xg = cscale(cconj(csub(xe, wxo)), 0.5f * sh);
+            xf.y *= ysgn;
+            xg.y *= ysgn;
             if (dc) {
                 kio<TK>::store(kout, make_float2(xf.x, xg.x));
             } else {
@@ -358,7 +360,7 @@ template <int LOG1, typename T, typename TK, bool PREPARE, bool MASKED>
 __global__ void __launch_bounds__(kMpThreads, 4)
 mp_pass2_kernel(T *__restrict__ ws, float2 *__restrict__ self_area, const TK *__restrict__ kbins_in,
                 TK *__restrict__ kbins_out, const float *__restrict__ kscale,
-                const uint8_t *__restrict__ mask, int64_t H, int64_t seq0, MpArgs ta) {
+                const uint8_t *__restrict__ mask, int64_t H, int64_t seq0, MpArgs ta, float ysgn) {
     constexpr int N1 = 1 << LOG1, N2 = 1 << kMpLog2;
     constexpr int64_t NC = (int64_t)N1 * N2;
     extern __shared__ float2 lds[];
@@ -478,8 +480,11 @@ mp_pass2_kernel(T *__restrict__ ws, float2 *__restrict__ self_area, const TK *__
                     const float2 xe = cadd(zf, bc);
                     const float2 xo = cmul_negi(csub(zf, bc));
                     const float2 wxo = cmul(Wf, xo);
-                    kio<TK>::store(k1 + 512 * jj, o1, cscale(cadd(xe, wxo), 0.5f * sh));
-                    kio<TK>::store(k2 + 512 * (15 - jj), o2, cscale(cconj(csub(xe, wxo)), 0.5f * sh));
+                    float2 x1 = cscale(cadd(xe, wxo), 0.5f * sh), x2 = cscale(cconj(csub(xe, wxo)), 0.5f * sh);
+                    x1.y *= ysgn;   // ysgn = -1: conjugated spectrum
+                    x2.y *= ysgn;
+                    kio<TK>::store(k1 + 512 * jj, o1, x1);
+                    kio<TK>::store(k2 + 512 * (15 - jj), o2, x2);
                 }
                 return;
             }
@@ -522,7 +527,7 @@ mp_pass2_kernel(T *__restrict__ ws, float2 *__restrict__ self_area, const TK *__
         const TK *krow = PREPARE ? nullptr : kbins_in + h * NC;
         TK *kout = PREPARE ? kbins_out + h * NC : nullptr;
         __syncthreads();
-        self_pairs<N1, N2, TK, PREPARE, MASKED>(area, krow, kout, bm, ks, ta, tid);
+        self_pairs<N1, N2, TK, PREPARE, MASKED>(area, krow, kout, bm, ks, ta, tid, ysgn);
         if (PREPARE) return;
         __syncthreads();
 #pragma unroll
@@ -647,7 +652,7 @@ static hipError_t conv_t(const void *u, const void *w, const void *v, void *out,
                        (const T *)u, (const T *)w, (int64_t)0, seq0, ws, ta);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k2, dim3((1 << LOG1) / 2, (unsigned)nseq), dim3(kMpThreads), kP2Lds, stream,
-                       ws, self_area, (const TK *)kbins, (TK *)nullptr, kscale, mask, H, seq0, ta);
+                       ws, self_area, (const TK *)kbins, (TK *)nullptr, kscale, mask, H, seq0, ta, 1.0f);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k3, dim3(N2 / P::C, (unsigned)nseq), dim3(kMpThreads), P::kLds, stream,
                        (const T *)ws, (const T *)v, (T *)out, seq0, ta);
@@ -656,7 +661,7 @@ static hipError_t conv_t(const void *u, const void *w, const void *v, void *out,
 
 template <int LOG1, typename T, typename TK>
 static hipError_t prep_t(const void *k, int64_t L, void *kbins, const float *kscale, void *work,
-                         int64_t H, int64_t h0, int64_t nseq, hipStream_t stream) {
+                         int64_t H, int64_t h0, int64_t nseq, float ysgn, hipStream_t stream) {
     using P = ColPlan<LOG1>;
     constexpr int N2 = 1 << kMpLog2;
     MpArgs ta{};
@@ -673,7 +678,7 @@ static hipError_t prep_t(const void *k, int64_t L, void *kbins, const float *ksc
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k2, dim3((1 << LOG1) / 2, (unsigned)nseq), dim3(kMpThreads), kP2Lds, stream,
                        ws, self_area, (const TK *)nullptr, (TK *)kbins, kscale, (const uint8_t *)nullptr,
-                       H, h0, ta);
+                       H, h0, ta, ysgn);
     return hipGetLastError();
 }
 
@@ -694,12 +699,12 @@ static hipError_t conv_st(int st, const void *u, const void *w, const void *v, v
 
 template <int LOG1>
 static hipError_t prep_st(int st, const void *k, int64_t L, void *kbins, const float *kscale,
-                          void *work, int64_t H, int64_t h0, int64_t nseq, hipStream_t stream) {
+                          void *work, int64_t H, int64_t h0, int64_t nseq, float ysgn, hipStream_t stream) {
     switch (st) {
-    case ST_F32: return prep_t<LOG1, float, float2>(k, L, kbins, kscale, work, H, h0, nseq, stream);
-    case ST_F16: return prep_t<LOG1, __half, __half2>(k, L, kbins, kscale, work, H, h0, nseq, stream);
+    case ST_F32: return prep_t<LOG1, float, float2>(k, L, kbins, kscale, work, H, h0, nseq, ysgn, stream);
+    case ST_F16: return prep_t<LOG1, __half, __half2>(k, L, kbins, kscale, work, H, h0, nseq, ysgn, stream);
     default:
-        return prep_t<LOG1, __hip_bfloat16, __half2>(k, L, kbins, kscale, work, H, h0, nseq, stream);
+        return prep_t<LOG1, __hip_bfloat16, __half2>(k, L, kbins, kscale, work, H, h0, nseq, ysgn, stream);
     }
 }
 
@@ -722,16 +727,16 @@ hipError_t launch_multipass_conv(int logn, int st, const void *u, const void *w,
 
 hipError_t launch_multipass_prepare(int logn, int st, const void *k, int64_t L, void *kbins,
                                     const float *kscale, void *work, int64_t H, int64_t h0,
-                                    int64_t nseq, hipStream_t stream) {
+                                    int64_t nseq, float ysgn, hipStream_t stream) {
     switch (logn - kMpLog2) {
-    case 2: return prep_st<2>(st, k, L, kbins, kscale, work, H, h0, nseq, stream);
-    case 3: return prep_st<3>(st, k, L, kbins, kscale, work, H, h0, nseq, stream);
-    case 4: return prep_st<4>(st, k, L, kbins, kscale, work, H, h0, nseq, stream);
-    case 5: return prep_st<5>(st, k, L, kbins, kscale, work, H, h0, nseq, stream);
-    case 6: return prep_st<6>(st, k, L, kbins, kscale, work, H, h0, nseq, stream);
-    case 7: return prep_st<7>(st, k, L, kbins, kscale, work, H, h0, nseq, stream);
-    case 8: return prep_st<8>(st, k, L, kbins, kscale, work, H, h0, nseq, stream);
-    case 9: return prep_st<9>(st, k, L, kbins, kscale, work, H, h0, nseq, stream);
+    case 2: return prep_st<2>(st, k, L, kbins, kscale, work, H, h0, nseq, ysgn, stream);
+    case 3: return prep_st<3>(st, k, L, kbins, kscale, work, H, h0, nseq, ysgn, stream);
+    case 4: return prep_st<4>(st, k, L, kbins, kscale, work, H, h0, nseq, ysgn, stream);
+    case 5: return prep_st<5>(st, k, L, kbins, kscale, work, H, h0, nseq, ysgn, stream);
+    case 6: return prep_st<6>(st, k, L, kbins, kscale, work, H, h0, nseq, ysgn, stream);
+    case 7: return prep_st<7>(st, k, L, kbins, kscale, work, H, h0, nseq, ysgn, stream);
+    case 8: return prep_st<8>(st, k, L, kbins, kscale, work, H, h0, nseq, ysgn, stream);
+    case 9: return prep_st<9>(st, k, L, kbins, kscale, work, H, h0, nseq, ysgn, stream);
     default: return hipErrorInvalidValue;
     }
 }
