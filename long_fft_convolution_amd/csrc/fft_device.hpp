@@ -76,11 +76,25 @@ template <> struct io<__hip_bfloat16> {
     static __device__ __forceinline__ float load1(const __hip_bfloat16 *p) { return __bfloat162float(*p); }
 };
 
+// A raw buffer view of `bytes` bytes at p (wave-uniform).  A buffer load
+// whose offset lies past the end returns zero without touching memory (the
+// buffer unit's range check), so an offset of kBufferSkip reads a zero at no
+// HBM cost and without a branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_view(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kBufferSkip = 0x80000000u;
+
 // Filter-spectrum bins: fp32 complex or fp16 complex (same element-offset forms).
 template <typename TK> struct kio;
 template <> struct kio<float2> {
     static __device__ __forceinline__ float2 load(const float2 *p, uint32_t e = 0) {
         return *reinterpret_cast<const float2 *>(reinterpret_cast<const char *>(p) + 8u * e);
+    }
+    // bin at byte offset off of a buffer view (zero past its end)
+    static __device__ __forceinline__ float2 load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        return make_float2(__uint_as_float(v[0]), __uint_as_float(v[1]));
     }
     static __device__ __forceinline__ void store(float2 *p, float2 v) { *p = v; }
     static __device__ __forceinline__ void store(float2 *p, uint32_t e, float2 v) {
@@ -90,6 +104,10 @@ template <> struct kio<float2> {
 template <> struct kio<__half2> {
     static __device__ __forceinline__ float2 load(const __half2 *p, uint32_t e = 0) {
         return __half22float2(*reinterpret_cast<const __half2 *>(reinterpret_cast<const char *>(p) + 4u * e));
+    }
+    static __device__ __forceinline__ float2 load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+        const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+        return __half22float2(*reinterpret_cast<const __half2 *>(&v));
     }
     static __device__ __forceinline__ void store(__half2 *p, float2 v) { *p = __floats2half2_rn(v.x, v.y); }
     static __device__ __forceinline__ void store(__half2 *p, uint32_t e, float2 v) {

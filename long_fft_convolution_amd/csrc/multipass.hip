@@ -229,7 +229,13 @@ mp_pass3_kernel(const T *__restrict__ ws, const T *__restrict__ v, T *__restrict
     const T *wsq = ws + 2 * (int64_t)blockIdx.y * NC;
     const uint32_t lo = (uint32_t)(col + N2 * j);
 
-    float2 acc[RB];      // lane (col, n_a = j): all f_b
+    // stage 2 needs, per lane, the RB-point DFT over f_b at outputs n_b < RB/2.
+    // With NG = 2 it is split by decimation in frequency: the two halves of
+    // f_b arrive one after the other and are folded at once into
+    //   e[f] = x[f] + x[f + RA]          -> outputs n_b = 2m
+    //   d[f] = (x[f] - x[f + RA]) w_RB^f -> outputs n_b = 2m + 1
+    // so at most RB values (not RB plus the transform's temporaries) are live.
+    float2 e[RA], d[RA];
 #pragma unroll
     for (int g = 0; g < P::NG; ++g) {
         // stage 1: lane (col, f_b = g RA + j), RA-point DFT over f_a.  The
@@ -245,24 +251,49 @@ mp_pass3_kernel(const T *__restrict__ ws, const T *__restrict__ v, T *__restrict
 #pragma unroll
         for (int i = 0; i < RA; ++i) lds[(j * RA + i) * C + col] = a[i];
         __syncthreads();
+        if (g == 0) {
 #pragma unroll
-        for (int i = 0; i < RA; ++i) acc[g * RA + i] = lds[(i * RA + j) * C + col];
+            for (int i = 0; i < RA; ++i) e[i] = lds[(i * RA + j) * C + col];
+        } else {
+#pragma unroll
+            for (int i = 0; i < RA; ++i) {
+                const float2 t = lds[(i * RA + j) * C + col];
+                d[i] = twiddle_const<RB>(csub(e[i], t), i);
+                e[i] = cadd(e[i], t);
+            }
+        }
     }
-    // stage 2: RB-point DFT over f_b, outputs n_b < RB/2 only (t < N)
     float2 r[RB / 2];
-    dft_halfout<RB>(acc, r);
-    const T *vrow = v != nullptr ? v + s * NC : nullptr;
+    if constexpr (P::NG == 2) {
+        float2 re[RA / 2], ro[RA / 2];
+        dft_halfout<RA>(e, re);
+        dft_halfout<RA>(d, ro);
+#pragma unroll
+        for (int m = 0; m < RA / 2; ++m) {
+            r[2 * m] = re[m];
+            r[2 * m + 1] = ro[m];
+        }
+    } else {
+        dft_halfout<RB>(e, r);
+    }
     T *orow = out + s * NC;
     const uint32_t lo2 = (uint32_t)(launder(col) + N2 * launder(j));
+    // one branch around the whole store loop (not one per store), so that the
+    // final butterflies are not sunk into it with their inputs held live
+    if (v != nullptr) {
+        const T *vrow = v + s * NC;
 #pragma unroll
-    for (int nb = 0; nb < RB / 2; ++nb) {
-        const int64_t mu = (int64_t)c0 + (int64_t)N2 * RA * nb;
-        float2 y = make_float2(r[nb].x, -r[nb].y);
-        if (vrow != nullptr) {
+        for (int nb = 0; nb < RB / 2; ++nb) {
+            const int64_t mu = (int64_t)c0 + (int64_t)N2 * RA * nb;
             const float2 g = io<T>::load2(vrow + 2 * mu, lo2);
-            y = make_float2(y.x * g.x, y.y * g.y);
+            io<T>::store2(orow + 2 * mu, lo2, make_float2(r[nb].x * g.x, -r[nb].y * g.y));
         }
-        io<T>::store2(orow + 2 * mu, lo2, y);
+    } else {
+#pragma unroll
+        for (int nb = 0; nb < RB / 2; ++nb) {
+            const int64_t mu = (int64_t)c0 + (int64_t)N2 * RA * nb;
+            io<T>::store2(orow + 2 * mu, lo2, make_float2(r[nb].x, -r[nb].y));
+        }
     }
 }
 
@@ -489,28 +520,40 @@ mp_pass2_kernel(T *__restrict__ ws, float2 *__restrict__ self_area, const TK *__
                 return;
             }
         } else {
-            const TK *k1 = kbins_in + h * NC + (int64_t)(hiw ? rowB : rowA) * N2;
-            const TK *k2 = kbins_in + h * NC + (int64_t)(hiw ? rowA : rowB) * N2;
+            const int hw = __builtin_amdgcn_readfirstlane(hiw);
+            const TK *k1 = kbins_in + h * NC + (int64_t)(hw ? rowB : rowA) * N2;
+            const TK *k2 = kbins_in + h * NC + (int64_t)(hw ? rowA : rowB) * N2;
             // the mask block of in-row bin b is b >> 6; o1 >> 6 and o2 >> 6 are
-            // uniform over the wave (kq >> 6 is the wave's index modulo 4)
+            // uniform over the wave (kq >> 6 is the wave's index modulo 4).
+            // Masked filter bins are read through buffer views of the two rows:
+            // a dropped block takes an offset past the view and reads zero
+            // without a branch and without its HBM traffic.
             const int b1 = __builtin_amdgcn_readfirstlane((int)(o1 >> 6));
             const int b2 = __builtin_amdgcn_readfirstlane((int)(o2 >> 6));
-            // two batches of eight bin pairs; the scheduling barriers keep the
+            const __amdgpu_buffer_rsrc_t r1 = buffer_view(k1, N2 * (uint32_t)sizeof(TK));
+            const __amdgpu_buffer_rsrc_t r2 = buffer_view(k2, N2 * (uint32_t)sizeof(TK));
+            // two batches of KB = 8 bin pairs; the scheduling barriers keep the
             // second batch of filter loads from being hoisted over the first
+            constexpr int KB = 8;
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                float2 K1[8], K2[8];
+            for (int bt = 0; bt < 16 / KB; ++bt) {
+                float2 K1[KB], K2[KB];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int jj = 8 * half + i;
-                    K1[i] = make_float2(0.f, 0.f);
-                    K2[i] = make_float2(0.f, 0.f);
-                    if (!MASKED || bm.keep(b1 + 8 * jj)) K1[i] = kio<TK>::load(k1 + 512 * jj, o1);
-                    if (!MASKED || bm.keep(b2 + 8 * (15 - jj))) K2[i] = kio<TK>::load(k2 + 512 * (15 - jj), o2);
+                for (int i = 0; i < KB; ++i) {
+                    const int jj = KB * bt + i;
+                    if (MASKED) {
+                        const uint32_t e1 = (uint32_t)sizeof(TK) * (512u * jj + o1);
+                        const uint32_t e2 = (uint32_t)sizeof(TK) * (512u * (15 - jj) + o2);
+                        K1[i] = kio<TK>::load(r1, bm.keep(b1 + 8 * jj) ? e1 : kBufferSkip);
+                        K2[i] = kio<TK>::load(r2, bm.keep(b2 + 8 * (15 - jj)) ? e2 : kBufferSkip);
+                    } else {
+                        K1[i] = kio<TK>::load(k1 + 512 * jj, o1);
+                        K2[i] = kio<TK>::load(k2 + 512 * (15 - jj), o2);
+                    }
                 }
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int jj = 8 * half + i;
+                for (int i = 0; i < KB; ++i) {
+                    const int jj = KB * bt + i;
                     float2 z1 = c[0][jj], z2 = c[1][15 - jj];
                     middle_pair(z1, z2, cscale(K1[i], ks), cscale(K2[i], ks), twiddle_const<32>(w1, jj));
                     c[0][jj] = z1;

@@ -341,8 +341,9 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
     int64_t oa, ob;
     bool has_b;
     pair_base(p, oa, ob, has_b);
-    Batch x0;
+    Batch x0, x1;
     load_batch(oa, ob, 0, x0);
+    load_batch(oa, ob, 1, x1);
 
     for (; p < p_end; p += wg_on_xcd) {
         const int64_t h = __builtin_amdgcn_readfirstlane((uint32_t)p / (uint32_t)PB);
@@ -361,8 +362,6 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
             h8 tw0[2][2][2], tw1[2][2][2];
             load_tw(0, tw0);
             load_tw(1, tw1);
-            Batch x1;
-            load_batch(oa, ob, 1, x1);
             phase1_batch(x0, tw0, 0, has_b);
             phase1_batch(x1, tw1, 1, has_b);
         }
@@ -530,6 +529,8 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                 stu(s8, o, ya[tt]);                                     // row n_c = c of sequence a
                 stu(s8 + 2 * kR1Plane, o, yb[tt]);                      // plane 1: sequence b
             }
+            // the second input batch of the next pair is fetched while the outputs are stored
+            load_batch(oa_nx, ob_nx, 1, x1);
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 // without a second row (ob == oa) its stores repeat the first row's values
