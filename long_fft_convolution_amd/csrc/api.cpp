@@ -731,9 +731,10 @@ fftconv_status_t fftconv_export_filter_rfft(const void *K_f, int64_t H, int64_t 
         for (int64_t f = 1; f < N; ++f) {
             int64_t slot = f;
             if (hdr.layout == KF_ROWS) {
-                // bin f = f1 + n1 f2 lives at row f1, column f2
+                // bin f = f1 + n1 f2 lives in row f1 at column f2 (fp32) or at the
+                // matrix-core position of f2 (half precision)
                 const int64_t f1 = f % n1, f2 = f / n1;
-                slot = f1 * n2 + f2;
+                slot = f1 * n2 + (dtype == FFTCONV_F32 ? f2 : (int64_t)mp_chain_pos((uint32_t)f2));
             }
             get(slot, &o[2 * f], &o[2 * f + 1]);
         }

@@ -41,7 +41,7 @@ struct KfHeader {
     int64_t n2;   // multi-pass inner size
 };
 constexpr uint32_t kKfMagic = 0x4b544646u;  // "FFTK"
-constexpr uint32_t kKfVersion = 1;
+constexpr uint32_t kKfVersion = 2;
 constexpr size_t kKfHeaderBytes = 256;
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -100,6 +100,18 @@ int64_t mp_ws_bytes(int st);
 // fp32 area per sequence for the two self-paired rows of the row pass
 constexpr size_t kMpSelfBytes = 2 * 8192 * 8;
 int64_t mp_chunk(int logn, int st);
+// Position of in-row bin f2 (row length 8192) in a multi-pass spectrum stored
+// in half precision.  Such spectra are kept in the order the matrix-core row
+// pass produces them: f2 = f_c + 8 f_b + 256 f_a with f_b = 16 nt + c and
+// f_a = 16 mt2 + 4 g + i sits at f_c * 1024 + (2 mt2 + nt) * 256 +
+// (16 g + c) * 4 + i, so that lane 16 g + c of the wave that owns chain f_c
+// reads the four bins i of tile (mt2, nt) as one 16-byte word.  Bin 0 stays at
+// position 0.  fp32 spectra keep the natural order.
+__host__ __device__ inline uint32_t mp_chain_pos(uint32_t f2) {
+    const uint32_t fc = f2 & 7u, fb = (f2 >> 3) & 31u, fa = f2 >> 8;
+    return fc * 1024u + ((fa >> 4) * 2u + (fb >> 4)) * 256u + (16u * ((fa >> 2) & 3u) + (fb & 15u)) * 4u +
+           (fa & 3u);
+}
 
 // Per-device, per-size tables (allocated once, read only afterwards).
 struct Tables {

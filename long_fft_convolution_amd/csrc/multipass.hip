@@ -29,6 +29,9 @@
 #include "fft_device.hpp"
 #include "fft_stages.hpp"
 #include "fftconv_internal.hpp"
+#include "cmfma.hpp"
+
+#include <type_traits>
 
 namespace fftconv {
 
@@ -331,6 +334,12 @@ struct BlockMask {
 };
 static_assert(kP2LdsFloat2 >= 32 * kT1Row && kP2LdsFloat2 >= 8192, "pass-2 LDS");
 
+// Position of in-row bin f2 in a stored filter row: natural order for fp32
+// spectra, the matrix-core order (mp_chain_pos) for half-precision ones.
+template <typename TK> __device__ __forceinline__ uint32_t kpos(uint32_t f2);
+template <> __device__ __forceinline__ uint32_t kpos<float2>(uint32_t f2) { return f2; }
+template <> __device__ __forceinline__ uint32_t kpos<__half2>(uint32_t f2) { return mp_chain_pos(f2); }
+
 // Bin pairs of the workgroup that holds rows 0 and N1/2: each row pairs with
 // itself (row 0: f2 <-> N2 - f2; row N1/2: f2 <-> N2 - 1 - f2).  Both rows
 // sit in natural order in an fp32 area of the workspace (row 0, then row
@@ -348,7 +357,8 @@ __device__ __forceinline__ void self_pairs(float2 *area, const TK *__restrict__ 
         float2 *row = area + (half_row ? N2 : 0);
         const int ia = w;
         const int ib = half_row ? N2 - 1 - w : (w == 0 ? 0 : N2 - w);
-        const int64_t sa = (int64_t)rbase * N2 + ia, sb = (int64_t)rbase * N2 + ib;
+        const int64_t rb = (int64_t)rbase * N2;
+        const uint32_t pa = kpos<TK>((uint32_t)ia), pb = kpos<TK>((uint32_t)ib);
         float2 zf = row[ia], zg = row[ib];
         const bool dc = !half_row && w == 0;   // f = 0: (K[0], K[N]) share slot 0
         const float2 wrow = half_row ? ta.w2row[N1 / 2] : make_float2(1.f, 0.f);
@@ -365,8 +375,8 @@ __device__ __forceinline__ void self_pairs(float2 *area, const TK *__restrict__ 
             if (dc) {
                 kio<TK>::store(kout, make_float2(xf.x, xg.x));
             } else {
-                kio<TK>::store(kout + sa, xf);
-                if (ib != ia) kio<TK>::store(kout + sb, xg);
+                kio<TK>::store(kout + rb, pa, xf);
+                if (ib != ia) kio<TK>::store(kout + rb, pb, xg);
             }
             continue;
         }
@@ -376,8 +386,8 @@ __device__ __forceinline__ void self_pairs(float2 *area, const TK *__restrict__ 
             Kf = make_float2(MASKED && !bm.keep(0) ? 0.f : k0.x, 0.f);
             Kg = make_float2(MASKED && !bm.keep(kMaskBlocks - 1) ? 0.f : k0.y, 0.f);
         } else {
-            Kf = (MASKED && !bm.keep(ia >> 6)) ? make_float2(0.f, 0.f) : cscale(kio<TK>::load(krow + sa), ks);
-            Kg = (MASKED && !bm.keep(ib >> 6)) ? make_float2(0.f, 0.f) : cscale(kio<TK>::load(krow + sb), ks);
+            Kf = (MASKED && !bm.keep(ia >> 6)) ? make_float2(0.f, 0.f) : cscale(kio<TK>::load(krow + rb, pa), ks);
+            Kg = (MASKED && !bm.keep(ib >> 6)) ? make_float2(0.f, 0.f) : cscale(kio<TK>::load(krow + rb, pb), ks);
         }
         middle_pair(zf, zg, Kf, Kg, Wf);
         row[ia] = zf;
@@ -514,8 +524,8 @@ mp_pass2_kernel(T *__restrict__ ws, float2 *__restrict__ self_area, const TK *__
                     float2 x1 = cscale(cadd(xe, wxo), 0.5f * sh), x2 = cscale(cconj(csub(xe, wxo)), 0.5f * sh);
                     x1.y *= ysgn;   // ysgn = -1: conjugated spectrum
                     x2.y *= ysgn;
-                    kio<TK>::store(k1 + 512 * jj, o1, x1);
-                    kio<TK>::store(k2 + 512 * (15 - jj), o2, x2);
+                    kio<TK>::store(k1, kpos<TK>(512u * jj + o1), x1);
+                    kio<TK>::store(k2, kpos<TK>(512u * (15 - jj) + o2), x2);
                 }
                 return;
             }
@@ -542,13 +552,13 @@ mp_pass2_kernel(T *__restrict__ ws, float2 *__restrict__ self_area, const TK *__
                 for (int i = 0; i < KB; ++i) {
                     const int jj = KB * bt + i;
                     if (MASKED) {
-                        const uint32_t e1 = (uint32_t)sizeof(TK) * (512u * jj + o1);
-                        const uint32_t e2 = (uint32_t)sizeof(TK) * (512u * (15 - jj) + o2);
+                        const uint32_t e1 = (uint32_t)sizeof(TK) * kpos<TK>(512u * jj + o1);
+                        const uint32_t e2 = (uint32_t)sizeof(TK) * kpos<TK>(512u * (15 - jj) + o2);
                         K1[i] = kio<TK>::load(r1, bm.keep(b1 + 8 * jj) ? e1 : kBufferSkip);
                         K2[i] = kio<TK>::load(r2, bm.keep(b2 + 8 * (15 - jj)) ? e2 : kBufferSkip);
                     } else {
-                        K1[i] = kio<TK>::load(k1 + 512 * jj, o1);
-                        K2[i] = kio<TK>::load(k2 + 512 * (15 - jj), o2);
+                        K1[i] = kio<TK>::load(k1, kpos<TK>(512u * jj + o1));
+                        K2[i] = kio<TK>::load(k2, kpos<TK>(512u * (15 - jj) + o2));
                     }
                 }
 #pragma unroll
@@ -647,6 +657,404 @@ mp_pass2_kernel(T *__restrict__ ws, float2 *__restrict__ self_area, const TK *__
     }
 }
 
+// ---------------------------------------------------------------- pass 2 on the matrix cores
+// Half-precision storage runs the row pass on the MFMA matrix cores (fp16
+// operands, fp32 accumulation; FlashFFTConv summary page, "Approach": the DFT
+// as an order-p chain of matrix products).  A row of 8192 points is split as
+// n = n_ab + 1024 n_c, n_ab = n_a + 32 n_b, and bin f2 = f_c + 8 f_b + 256 f_a:
+//
+//   X[f2] = sum_{n_a} w32^{n_a f_a} w1024^{n_a f_b} sum_{n_b} w32^{n_b f_b}
+//             [ w8192^{n_ab f_c} sum_{n_c} w8^{n_c f_c} x[n] ]
+//
+//   phase 1 (VALU)  per column n_ab: the 8-point DFT over n_c and the twiddle,
+//                   into LDS as the fp16 operand rows of the chains (row, f_c);
+//   phase 2 (MFMA)  per chain: S1 contracts n_b, twiddle, S2 contracts n_a;
+//                   the bin-pair step (filter product and repacking); then the
+//                   same stages in the forward direction on conj(Z'), which
+//                   gives conj of the inverse transform (S2'' contracts f_a,
+//                   twiddle, S1'' contracts f_b, outer twiddle), into LDS;
+//   phase 3 (VALU)  per column: the 8-point DFT over f_c, store.
+//
+// Wave w owns the chains (A, f_c = w) and (B, f_c = 7 - w).  Bin f2 of row A
+// pairs with bin 8191 - f2 of row B, which is bin (7 - f_c, 31 - f_b, 31 - f_a)
+// of chain (B, 7 - w): tile (1 - mt2, 1 - nt), lane 63 - l, element 3 - i, so
+// one lane permutation (ds_bpermute) brings every pair into one lane.  The
+// filter rows are stored in the same order (mp_chain_pos): each lane reads the
+// four bins of a tile as one 16-byte word.
+namespace mm {
+using namespace cmfma;
+constexpr int kR2Stride = 34;                          // complex values per (chain, n_a) row of R2
+constexpr size_t kR1Bytes = (size_t)2 * 16 * 1024 * 2;  // two fp16 planes of 16 chains x 1024
+constexpr size_t kR2Bytes = (size_t)16 * 32 * kR2Stride * 4;
+constexpr size_t kLds = kR1Bytes > kR2Bytes ? kR1Bytes : kR2Bytes;
+
+__device__ __forceinline__ uint32_t bperm(uint32_t addr, uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_ds_bpermute((int)addr, (int)v);
+}
+__device__ __forceinline__ float2 h2f(uint32_t d) {
+    const __half2 v = *reinterpret_cast<const __half2 *>(&d);
+    return __half22float2(v);
+}
+__device__ __forceinline__ uint32_t f2h(float2 v) {
+    const __half2 h = __floats2half2_rn(v.x, v.y);
+    return *reinterpret_cast<const uint32_t *>(&h);
+}
+// exp(-2 pi i e / 64), e < 4, and exp(-2 pi i / 128)
+__device__ __forceinline__ float2 w64(int e) {
+    switch (e) {
+    case 0: return make_float2(1.0f, 0.0f);
+    case 1: return make_float2(9.951847267e-01f, -9.801714033e-02f);
+    case 2: return make_float2(9.807852804e-01f, -1.950903220e-01f);
+    default: return make_float2(9.569403357e-01f, -2.902846773e-01f);
+    }
+}
+constexpr float kW128c = 9.987954562e-01f, kW128s = -4.906767433e-02f;
+}  // namespace mm
+
+struct MmTables {
+    const void *fr, *fi;   // DFT-32 operand tiles [2][64 lanes] x 8 fp16
+    const void *tw1;       // w1024^{n_a f_b} in the S1 output layout [mt][nt][lane]: cos[4], sin[4]
+    const void *tw3;       // conj of w1024^{n_a f_b} in the S2'' output layout [nt][nt2][lane]
+};
+
+// grid (N1 / 2, nseq); block 512; dynamic LDS mm::kLds.
+template <int LOG1, typename T, bool MASKED>
+__global__ void __launch_bounds__(kMpThreads, 4)
+mp_pass2m_kernel(T *__restrict__ ws, float2 *__restrict__ self_area, const __half2 *__restrict__ kbins,
+                 const float *__restrict__ kscale, const uint8_t *__restrict__ mask, int64_t H, int64_t seq0,
+                 MpArgs ta, MmTables mt) {
+    using namespace mm;
+    constexpr int N1 = 1 << LOG1, N2 = 1 << kMpLog2;
+    constexpr int64_t NC = (int64_t)N1 * N2;
+    extern __shared__ __align__(16) _Float16 smem[];
+    _Float16 *const P0 = smem;                   // R1 plane re: [chain 16][chunk 4][n_a 32][8]
+    _Float16 *const P1 = smem + 16 * 1024;       // R1 plane im
+    char *const R2 = reinterpret_cast<char *>(smem);   // [chain 16][n_a 32][kR2Stride] half2
+    const int tid = threadIdx.x;
+    // Workgroup order: the nseq workgroups of the self-paired rows (f1 = 0), which
+    // take about three times as long, come first and spread over the XCDs; then
+    // f1 = 1 .. N1/2 - 1 of every sequence.
+    const uint32_t wg = blockIdx.x + gridDim.x * blockIdx.y, nseq = gridDim.y;
+    int f1;
+    uint32_t sq;
+    if (wg < nseq) {
+        f1 = 0;
+        sq = wg;
+    } else {
+        const uint32_t j = wg - nseq;
+        f1 = 1 + (int)(j % (uint32_t)(N1 / 2 - 1));
+        sq = j / (uint32_t)(N1 / 2 - 1);
+    }
+    f1 = __builtin_amdgcn_readfirstlane(f1);
+    sq = __builtin_amdgcn_readfirstlane(sq);
+    const int rowA = f1, rowB = f1 == 0 ? N1 / 2 : N1 - f1;
+    const int64_t s = seq0 + sq;
+    const int64_t h = s % H;
+    T *const wsq = ws + 2 * (int64_t)sq * NC;
+    BlockMask bm{~0ull, ~0ull};
+    if (MASKED) {
+        const uint8_t *mrow = mask + h * kMaskBlocks;
+        bm.lo = __builtin_amdgcn_ballot_w64(mrow[tid & 63] != 0);
+        bm.hi = __builtin_amdgcn_ballot_w64(mrow[64 + (tid & 63)] != 0);
+    }
+
+    // ---- phase 1: lane (row r, quad q, n_a) holds columns n_ab = n_a + 32 (4 q + k), k < 4
+    {
+        const int r = __builtin_amdgcn_readfirstlane(tid >> 8), q = (tid >> 5) & 7, na = tid & 31;
+        const T *rowp = wsq + 2 * (int64_t)(r ? rowB : rowA) * N2;
+        const uint32_t lo = (uint32_t)(na + 128 * q);
+        float2 y[4][8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int nc = 0; nc < 8; ++nc) y[k][nc] = io<T>::load2(rowp + 2 * (32 * k + 1024 * nc), lo);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            dft_inplace<8>(y[k]);
+            const uint32_t nab = (uint32_t)(na + 32 * (4 * q + k));
+            apply_pow<8>(y[k], ldu<float2>(ta.tw2, 8u * nab), make_float2(1.f, 0.f));
+        }
+        // n_b = 4q + k sits in K slot kslot(n_b): chunk q & 3, slot 4 (q >> 2) + k
+        const uint32_t o = (uint32_t)((q & 3) * 256 + na * 8 + 4 * (q >> 2));
+#pragma unroll
+        for (int fc = 0; fc < 8; ++fc) {
+            const uint32_t oc = (uint32_t)((r * 8 + fc) * 1024) + o;
+            const h4 re = {(_Float16)y[0][fc].x, (_Float16)y[1][fc].x, (_Float16)y[2][fc].x, (_Float16)y[3][fc].x};
+            const h4 im = {(_Float16)y[0][fc].y, (_Float16)y[1][fc].y, (_Float16)y[2][fc].y, (_Float16)y[3][fc].y};
+            *reinterpret_cast<h4 *>(P0 + oc) = re;
+            *reinterpret_cast<h4 *>(P1 + oc) = im;
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 2
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, c = lane & 15;
+    const int fcA = wave, fcB = 7 - wave;
+    const uint32_t ul = (uint32_t)lane;
+    h8 ar[2][2], ai[2][2];   // [chain A / B][mt]: rows n_a = 16 mt + c, K slots 8g..8g+7
+#pragma unroll
+    for (int qc = 0; qc < 2; ++qc) {
+        const int ch = qc ? 8 + fcB : fcA;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int o = ch * 1024 + g * 256 + (16 * m + c) * 8;
+            ar[qc][m] = *reinterpret_cast<const h8 *>(P0 + o);
+            ai[qc][m] = *reinterpret_cast<const h8 *>(P1 + o);
+        }
+    }
+    // every wave has its operands; R1 becomes R2 below
+    __syncthreads();
+
+    // the DFT-32 operand tiles (the negated imaginary plane is formed where it is used)
+    h8 Fr[2], Fi[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        Fr[t] = ldu<h8>(mt.fr, 16u * (t * 64 + ul));
+        Fi[t] = ldu<h8>(mt.fi, 16u * (t * 64 + ul));
+    }
+
+    // S1 (data A: rows n_a, K = n_b; const B: F, N = f_b) and the twiddle w1024^{n_a f_b}
+    h4 t1r[2][2][2], t1i[2][2][2];   // [chain][mt][nt]
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const h8 tw = ldu<h8>(mt.tw1, 16u * ((m * 2 + n) * 64 + ul));
+#pragma unroll
+            for (int qc = 0; qc < 2; ++qc) {
+                f4 cr, ci;
+                cm_dataA(ar[qc][m], ai[qc][m], Fr[n], Fi[n], neg8(Fi[n]), cr, ci);
+                t1r[qc][m][n] = to_h4(cr);
+                t1i[qc][m][n] = to_h4(ci);
+                cmul4(t1r[qc][m][n], t1i[qc][m][n], tw);
+            }
+        }
+
+    // S2 (const A: F rows f_a; data B: T1, K = n_a) tile pair by tile pair, the
+    // bin-pair step on (A tile (m2, n), mirrored B tile (1 - m2, 1 - n))
+    const float ks = kscale[h];
+    const __half2 *kA = kbins + h * NC + (int64_t)rowA * N2 + fcA * 1024;
+    const __half2 *kB = kbins + h * NC + (int64_t)rowB * N2 + fcB * 1024;
+    const uint32_t maddr = 4u * (63u - ul);
+    // keep bits of this lane's 16 bins of row A (bit 4 (2 m2 + n) + e) and of their
+    // row-B partners (bit 16 + the same); the block of A's bin is
+    // 64 m2 + 16 g + 4 e + 2 n + (c >> 3), its partner's 127 minus that
+    uint32_t kbits = 0xffffffffu;
+    if (MASKED) {
+        kbits = 0;
+#pragma unroll
+        for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int b = 64 * m2 + 16 * g + 4 * e + 2 * n + (c >> 3);
+                    const int bit = 4 * (2 * m2 + n) + e;
+                    kbits |= (bm.keep(b) ? 1u : 0u) << bit;
+                    kbits |= (bm.keep(127 - b) ? 1u : 0u) << (16 + bit);
+                }
+    }
+    // twiddle of A's bin f2 = f_c + 8 (16 n + c) + 256 (16 m2 + 4 g + e):
+    // omega_2N^{rowA + N1 f2} = w2row[rowA] omega_{2 N2}^{f2}
+    const float2 wbase = cmul(ta.w2row[rowA], ldu<float2>(ta.w2n2, 8u * (uint32_t)(fcA + 8 * c + 1024 * g)));
+    float2 *const area = self_area + (int64_t)sq * 2 * N2;
+    // conj(Z') of the wave's two chains as fp16 tiles in LDS (the R2 region, free
+    // until the barrier below): [wave][chain][m2][n][lane] x (re h4, im h4)
+    char *const Yw = reinterpret_cast<char *>(smem) + wave * 8192;
+    auto yput = [&](int qc, int m2, int n, uint32_t ln, const h4 &re, const h4 &im) {
+        stu(Yw, 16u * (((qc * 2 + m2) * 2 + n) * 64 + ln), cat8(re, im));
+    };
+    if (f1 == 0) {
+        // rows 0 and N1/2 pair with themselves: their spectra go to the area in
+        // natural order (the products are formed once more below)
+#pragma unroll
+        for (int qc = 0; qc < 2; ++qc)
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const h8 br = cat8(t1r[qc][0][n], t1r[qc][1][n]), bi = cat8(t1i[qc][0][n], t1i[qc][1][n]);
+#pragma unroll
+                for (int m2 = 0; m2 < 2; ++m2) {
+                    f4 zr, zi;
+                    cm_constA(Fr[m2], Fi[m2], neg8(Fi[m2]), br, bi, zr, zi);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int f = (qc ? fcB : fcA) + 8 * (16 * n + c) + 256 * (16 * m2 + 4 * g + e);
+                        area[qc * N2 + f] = make_float2(zr[e], zi[e]);
+                    }
+                }
+            }
+        // The barriers (workgroup scope) order the area's global writes and reads
+        // across the waves, which share one CU's L1.
+        __syncthreads();
+        self_pairs<N1, N2, __half2, false, MASKED>(area, kbins + h * NC, nullptr, bm, ks, ta, tid, 1.0f);
+        __syncthreads();
+#pragma unroll
+        for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                f4 ra, ia, rb, ib;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int fA = fcA + 8 * (16 * n + c) + 256 * (16 * m2 + 4 * g + e);
+                    const int fB = fcB + 8 * (16 * n + c) + 256 * (16 * m2 + 4 * g + e);
+                    const float2 va = area[fA], vb = area[N2 + fB];
+                    ra[e] = va.x;
+                    ia[e] = va.y;
+                    rb[e] = vb.x;
+                    ib[e] = vb.y;
+                }
+                yput(0, m2, n, ul, to_h4(ra), to_h4(ia));
+                yput(1, m2, n, ul, to_h4(rb), to_h4(ib));
+            }
+    } else {
+        // (n outer: the S1 results of A's column tile n and B's 1 - n die after two tile pairs)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int m2 = 0; m2 < 2; ++m2) {
+                // (a scheduling fence per tile pair keeps the next pair's products and
+                // loads from being hoisted here, which would exceed the register budget)
+                __builtin_amdgcn_sched_barrier(0);
+                const int mb = 1 - m2, nb = 1 - n;
+                // filter bins: A's tile (m2, n) and B's tile (mb, nb) read from lane 63 - l
+                uint4 qa, qb;
+                const uint32_t ea = 16u * ((m2 * 2 + n) * 64 + ul), eb = 16u * ((mb * 2 + nb) * 64 + (63u - ul));
+                const int kb0 = 4 * (2 * m2 + n);
+                if (MASKED) {
+                    const bool anyA = ((kbits >> kb0) & 15u) != 0, anyB = ((kbits >> (16 + kb0)) & 15u) != 0;
+                    qa = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       buffer_view(kA, 4096u), anyA ? ea : kBufferSkip, 0, 0));
+                    qb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       buffer_view(kB, 4096u), anyB ? eb : kBufferSkip, 0, 0));
+                } else {
+                    qa = ldu<uint4>(kA, ea);
+                    qb = ldu<uint4>(kB, eb);
+                }
+                f4 zr, zi, mr, mi;
+                {
+                    const h8 br = cat8(t1r[0][0][n], t1r[0][1][n]), bi = cat8(t1i[0][0][n], t1i[0][1][n]);
+                    cm_constA(Fr[m2], Fi[m2], neg8(Fi[m2]), br, bi, zr, zi);
+                }
+                {
+                    f4 pr, pi;
+                    const h8 br = cat8(t1r[1][0][nb], t1r[1][1][nb]), bi = cat8(t1i[1][0][nb], t1i[1][1][nb]);
+                    cm_constA(Fr[mb], Fi[mb], neg8(Fi[mb]), br, bi, pr, pi);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        mr[e] = __uint_as_float(bperm(maddr, __float_as_uint(pr[3 - e])));
+                        mi[e] = __uint_as_float(bperm(maddr, __float_as_uint(pi[3 - e])));
+                    }
+                }
+                uint32_t ka[4] = {qa.x, qa.y, qa.z, qa.w}, kb[4] = {qb.w, qb.z, qb.y, qb.x};
+                if (MASKED) {
+                    // a dropped bin reads as zero (the whole word: both halves of the value)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        ka[e] &= 0u - ((kbits >> (kb0 + e)) & 1u);
+                        kb[e] &= 0u - ((kbits >> (16 + kb0 + e)) & 1u);
+                    }
+                }
+                float2 wt = cmul(wbase, make_float2(n ? kW128c : 1.f, n ? kW128s : 0.f));
+                if (m2) wt = cmul_negi(wt);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float2 Ka = cscale(h2f(ka[e]), ks), Kb = cscale(h2f(kb[e]), ks);
+                    float2 zf = make_float2(zr[e], zi[e]), zg = make_float2(mr[e], mi[e]);
+                    middle_pair(zf, zg, Ka, Kb, cmul(wt, w64(e)));
+                    zr[e] = zf.x;
+                    zi[e] = zf.y;
+                    mr[e] = zg.x;
+                    mi[e] = zg.y;
+                }
+                yput(0, m2, n, ul, to_h4(zr), to_h4(zi));
+                // B's values go to lane 63 - l of its own layout, elements reversed
+                const h4 qr = to_h4(mr), qi = to_h4(mi);
+                yput(1, mb, nb, 63u - ul, h4{qr[3], qr[2], qr[1], qr[0]}, h4{qi[3], qi[2], qi[1], qi[0]});
+            }
+    }
+    // forward-direction stages on conj(Z'): S2'' (data A: rows f_b, K = f_a;
+    // const B: F, N = n_a), twiddle w1024^{n_a f_b}; S1'' (const A: F rows n_b;
+    // data B: K = f_b), outer twiddle w8192^{n_ab f_c}; into R2 as half2
+    h4 t3r[2][2][2], t3i[2][2][2];   // [chain][n (f_b tile)][n2 (n_a tile)]
+#pragma unroll
+    for (int qc = 0; qc < 2; ++qc)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const h8 y0 = ldu<h8>(Yw, 16u * (((qc * 2 + 0) * 2 + n) * 64 + ul));
+            const h8 y1 = ldu<h8>(Yw, 16u * (((qc * 2 + 1) * 2 + n) * 64 + ul));
+            const h8 dr = cat8(lo4(y0), lo4(y1)), di = cat8(hi4(y0), hi4(y1));
+#pragma unroll
+            for (int n2 = 0; n2 < 2; ++n2) {
+                f4 cr, ci;
+                cm_dataA(dr, di, Fr[n2], Fi[n2], neg8(Fi[n2]), cr, ci);
+                t3r[qc][n][n2] = to_h4(cr);
+                t3i[qc][n][n2] = to_h4(ci);
+                h8 tw = ldu<h8>(mt.tw3, 16u * ((n * 2 + n2) * 64 + ul));
+                tw = cat8(lo4(tw), -hi4(tw));   // the table holds the conjugate
+                cmul4(t3r[qc][n][n2], t3i[qc][n][n2], tw);
+            }
+        }
+    // every wave has read its tiles: the region becomes R2
+    __syncthreads();
+#pragma unroll
+    for (int qc = 0; qc < 2; ++qc) {
+        const int fc = qc ? fcB : fcA;
+        // outer twiddle of (n_a = 16 n2 + c, n_b = 16 n3 + 4 g + e):
+        // w8192^{f_c (c + 128 g)} (w8192^{16 f_c})^{n2} (w8192^{512 f_c})^{n3} (w8192^{32 f_c})^e
+        const float2 b0 = ldu<float2>(ta.tw2, 8u * ((uint32_t)(fc * (c + 128 * g)) & (N2 - 1)));
+        const float2 s16 = ta.tw2[16 * fc], s512 = ta.tw2[(512 * fc) & (N2 - 1)], s32 = ta.tw2[32 * fc];
+        const float2 s32_2 = cmul(s32, s32), s32_3 = cmul(s32_2, s32);
+#pragma unroll
+        for (int n2 = 0; n2 < 2; ++n2) {
+            const h8 br = cat8(t3r[qc][0][n2], t3r[qc][1][n2]), bi = cat8(t3i[qc][0][n2], t3i[qc][1][n2]);
+#pragma unroll
+            for (int n3 = 0; n3 < 2; ++n3) {
+                f4 cr, ci;
+                cm_constA(Fr[n3], Fi[n3], neg8(Fi[n3]), br, bi, cr, ci);   // rows n_b = 16 n3 + 4g + e, col n_a
+                float2 bt = b0;
+                if (n2) bt = cmul(bt, s16);
+                if (n3) bt = cmul(bt, s512);
+                uint32_t d[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float2 we = e == 0 ? bt : cmul(bt, e == 1 ? s32 : (e == 2 ? s32_2 : s32_3));
+                    d[e] = f2h(cmul(make_float2(cr[e], ci[e]), we));
+                }
+                // R2[chain][n_a][n_b]: n_b = 16 n3 + 4 g + e are consecutive
+                const uint32_t o = (uint32_t)((((qc * 8 + fc) * 32 + 16 * n2 + c) * kR2Stride + 16 * n3 + 4 * g) * 4);
+                stu(R2, o, make_uint2(d[0], d[1]));
+                stu(R2, o + 8u, make_uint2(d[2], d[3]));
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 3: lane (row r, quad q, n_a): the 8-point DFT over f_c of columns
+    // n_ab = n_a + 32 (4 q + k), outputs n_c; store
+    {
+        const int tid2 = launder(tid);
+        const int r = __builtin_amdgcn_readfirstlane(tid2 >> 8), q = (tid2 >> 5) & 7, na = tid2 & 31;
+        T *rowp = wsq + 2 * (int64_t)(r ? rowB : rowA) * N2;
+        float2 y[4][8];
+#pragma unroll
+        for (int fc = 0; fc < 8; ++fc) {
+            const uint32_t o = (uint32_t)((((r * 8 + fc) * 32 + na) * kR2Stride + 4 * q) * 4);
+            const uint2 a = ldu<uint2>(R2, o), b = ldu<uint2>(R2, o + 8u);
+            y[0][fc] = h2f(a.x);
+            y[1][fc] = h2f(a.y);
+            y[2][fc] = h2f(b.x);
+            y[3][fc] = h2f(b.y);
+        }
+        const uint32_t lo = (uint32_t)(na + 128 * q);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            dft_inplace<8>(y[k]);
+#pragma unroll
+            for (int nc = 0; nc < 8; ++nc) io<T>::store2(rowp + 2 * (32 * k + 1024 * nc), lo, y[k][nc]);
+        }
+    }
+}
+
 // ---------------------------------------------------------------- tables
 static hipError_t mp_args(int logn, MpArgs *a) {
     Tables t1{}, t2{};
@@ -684,18 +1092,29 @@ static hipError_t conv_t(const void *u, const void *w, const void *v, void *out,
     T *ws = (T *)work;
     float2 *self_area = (float2 *)((char *)work + (size_t)nseq * ((size_t)1 << (LOG1 + kMpLog2)) * 2 * sizeof(T));
     auto k1 = mp_pass1_kernel<LOG1, T, false>;
-    auto k2m = mp_pass2_kernel<LOG1, T, TK, false, true>;
-    auto k2u = mp_pass2_kernel<LOG1, T, TK, false, false>;
-    auto k2 = mask != nullptr ? k2m : k2u;
     auto k3 = mp_pass3_kernel<LOG1, T>;
     if ((e = allow_lds(k1, P::kLds)) != hipSuccess) return e;
-    if ((e = allow_lds(k2, kP2Lds)) != hipSuccess) return e;
     if ((e = allow_lds(k3, P::kLds)) != hipSuccess) return e;
     hipLaunchKernelGGL(k1, dim3(N2 / P::C, (unsigned)nseq), dim3(kMpThreads), P::kLds, stream,
                        (const T *)u, (const T *)w, (int64_t)0, seq0, ws, ta);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k2, dim3((1 << LOG1) / 2, (unsigned)nseq), dim3(kMpThreads), kP2Lds, stream,
-                       ws, self_area, (const TK *)kbins, (TK *)nullptr, kscale, mask, H, seq0, ta, 1.0f);
+    const dim3 g2((1 << LOG1) / 2, (unsigned)nseq);
+    if constexpr (std::is_same<TK, __half2>::value) {
+        // half-precision storage: the row pass on the matrix cores
+        Pair3Tables p3{};
+        if ((e = get_pair3_tables(&p3)) != hipSuccess) return e;
+        const MmTables mt{p3.fr, p3.fi, p3.tw1, p3.tw3};
+        auto k2 = mask != nullptr ? mp_pass2m_kernel<LOG1, T, true> : mp_pass2m_kernel<LOG1, T, false>;
+        if ((e = allow_lds(k2, mm::kLds)) != hipSuccess) return e;
+        hipLaunchKernelGGL(k2, g2, dim3(kMpThreads), mm::kLds, stream, ws, self_area, (const __half2 *)kbins,
+                           kscale, mask, H, seq0, ta, mt);
+    } else {
+        auto k2 = mask != nullptr ? mp_pass2_kernel<LOG1, T, TK, false, true>
+                                  : mp_pass2_kernel<LOG1, T, TK, false, false>;
+        if ((e = allow_lds(k2, kP2Lds)) != hipSuccess) return e;
+        hipLaunchKernelGGL(k2, g2, dim3(kMpThreads), kP2Lds, stream, ws, self_area, (const TK *)kbins,
+                           (TK *)nullptr, kscale, mask, H, seq0, ta, 1.0f);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k3, dim3(N2 / P::C, (unsigned)nseq), dim3(kMpThreads), P::kLds, stream,
                        (const T *)ws, (const T *)v, (T *)out, seq0, ta);

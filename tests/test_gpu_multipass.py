@@ -55,6 +55,42 @@ def test_multipass_half_dtypes(dtype):
     assert oracle.rel_l2(y, ref) < TOL[dtype]
 
 
+@pytest.mark.parametrize("logn", [15, 16, 17, 18, 19, 20])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_multipass_sizes_half(logn, dtype):
+    # half-precision storage runs the row pass on the matrix cores: every outer
+    # length N1 = 4 .. 128, gated
+    N = 1 << logn
+    _say(f"multipass {dtype} N={N}")
+    inp = synth.generate(1, 3, N, N, dtype, gated=True, seed=100 + logn)
+    y = run_gpu(inp)
+    ref = oracle.fft_conv(inp.f64("u"), inp.f64("k"), inp.f64("w"), inp.f64("v"))
+    assert oracle.rel_l2(y, ref) < TOL[dtype]
+
+
+@pytest.mark.parametrize("kind", ["band", "random"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_multipass_mask_half(kind, dtype):
+    N = 1 << 18
+    _say(f"multipass mask {kind} {dtype}")
+    inp = synth.generate(1, 3, N, 1 << 16, dtype, gated=False, seed=19)
+    mask = synth.band_mask(3, 27) if kind == "band" else synth.random_mask(3, seed=15)
+    y = run_gpu(inp, mask)
+    ref = oracle.fft_conv(inp.f64("u"), inp.f64("k"), mask=mask)
+    assert oracle.rel_l2(y, ref) < TOL[dtype]
+
+
+def test_multipass_chunks_half_ragged():
+    # 2^16 points per sequence in fp16: 512 sequences per 128 MiB chunk; 515 -> a ragged chunk
+    N = 1 << 16
+    assert fc.fftconv_workspace_bytes(1, 515, N, torch.float16) == 512 * (N * 4 + 2 * 8192 * 8)
+    _say("multipass chunking f16 B=1 H=515")
+    inp = synth.generate(1, 515, N, 2048, "f16", gated=False, seed=24)
+    y = run_gpu(inp)
+    ref = oracle.fft_conv(inp.f64("u"), inp.f64("k"))
+    assert oracle.rel_l2(y, ref) < TOL["f16"]
+
+
 def test_multipass_chunks_and_ragged_tail():
     # 2^17 points per sequence in fp32: 128 sequences per 128 MiB chunk;
     # 131 sequences -> a ragged chunk
