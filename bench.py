@@ -42,6 +42,8 @@ KERNEL_SOURCES = ["fused.hip", "multipass.hip", "pair_mfma.hip", "pair16k.hip", 
 
 def path_of(w: synth.Workload):
     """(kernel name, compute dtype, arithmetic) of the path fftconv_fwd takes for w."""
+    if w.short:
+        return "pair1k_kernel (windows of 1024)", "f16", "fp16 MFMA operands, fp32 accumulation"
     if w.dtype in ("f16", "bf16") and w.N == 1024:
         return "pair1k_kernel", "f16", "fp16 MFMA operands, fp32 accumulation"
     if w.dtype in ("f16", "bf16") and w.N == 16384:
@@ -60,6 +62,8 @@ def algorithmic_bytes(w: synth.Workload) -> int:
     per channel (only the kept blocks when the mask zeroes some)."""
     e = ELEM[w.dtype]
     act = w.B * w.H * w.N * e * (4 if w.gated else 2)
+    if w.short:   # the spectrum of a 1024-sample window: 2048 bins per channel
+        return int(act + w.H * 2048 * 4)
     bin_bytes = 8 if w.dtype == "f32" else 4
     keep = 1.0 if w.mask_keep_blocks is None else w.mask_keep_blocks / 128.0
     return int(act + w.H * w.N * bin_bytes * keep)
@@ -147,16 +151,27 @@ def main():
     v = None if inp.v is None else inp.v.to(dev)
     mask = None if inp.mask is None else torch.from_numpy(inp.mask).to(dev)
     out = torch.empty_like(u)
-    K_f = fc.alloc_filter(wl.H, wl.N, u.dtype, dev)
-    ws_p = fc.alloc_workspace(1, wl.H, wl.N, u.dtype, dev)
-    fc.fftconv_prepare_filter(k, wl.N, K_f, ws_p)
-    ws = fc.alloc_workspace(wl.B, wl.H, wl.N, u.dtype, dev)
+    if wl.short:
+        K_f = torch.empty(fc.fftconv_short_filter_bytes(wl.H, u.dtype), dtype=torch.uint8, device=dev)
+        fc.fftconv_prepare_short_filter(k, K_f)
+        ws = None
+    else:
+        K_f = fc.alloc_filter(wl.H, wl.N, u.dtype, dev)
+        ws_p = fc.alloc_workspace(1, wl.H, wl.N, u.dtype, dev)
+        fc.fftconv_prepare_filter(k, wl.N, K_f, ws_p)
+        ws = fc.alloc_workspace(wl.B, wl.H, wl.N, u.dtype, dev)
     torch.cuda.synchronize(dev)
 
     def step():
-        fc.fftconv_fwd(u, K_f, w, v, out, wl.L, mask, ws)
+        if wl.short:
+            fc.fftconv_fwd_short(u, K_f, w, v, out, wl.L)
+        else:
+            fc.fftconv_fwd(u, K_f, w, v, out, wl.L, mask, ws)
 
     if args.which == "bwd":
+        if wl.short:
+            log("bench: the short-filter path has no backward pass")
+            return 2
         return bench_bwd(args, wl, dev, u, K_f, w, v, mask)
 
     for _ in range(args.warmup):

@@ -66,6 +66,12 @@ def _load():
     lib.fftconv_export_filter_rfft.argtypes = [vp, i64, i64, ctypes.c_int,
                                                ctypes.POINTER(ctypes.c_double), vp]
     lib.fftconv_export_filter_rfft.restype = ctypes.c_int
+    lib.fftconv_short_filter_bytes.argtypes = [i64, ctypes.c_int]
+    lib.fftconv_short_filter_bytes.restype = sz
+    lib.fftconv_prepare_short_filter.argtypes = [vp, i64, i64, ctypes.c_int, vp, sz, vp]
+    lib.fftconv_prepare_short_filter.restype = ctypes.c_int
+    lib.fftconv_fwd_short.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, vp]
+    lib.fftconv_fwd_short.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -188,6 +194,42 @@ def fftconv_export_filter_rfft(K_f: torch.Tensor, H: int, N: int, dtype, stream=
 
 
 # ---------------------------------------------------------------- plumbing
+def fftconv_short_filter_bytes(H: int, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    return int(_load().fftconv_short_filter_bytes(H, code))
+
+
+def fftconv_prepare_short_filter(k: torch.Tensor, K_s: torch.Tensor, stream=None) -> None:
+    """K_s <- spectrum of the (H, L) filter k, L <= 512, for the chunked short-filter path."""
+    _dev_tensor(k, "k")
+    _dev_tensor(K_s, "K_s")
+    H, L = k.shape
+    _check(_load().fftconv_prepare_short_filter(
+        _ptr(k), H, L, dtype_code(k.dtype), _ptr(K_s), K_s.numel() * K_s.element_size(),
+        _stream(stream, k.device)))
+
+
+def fftconv_fwd_short(u: torch.Tensor, K_s: torch.Tensor, w: torch.Tensor | None, v: torch.Tensor | None,
+                      out: torch.Tensor, L_filter: int, stream=None) -> None:
+    """out <- v * causal_conv(u * w, k) through the short-filter spectrum K_s (N a multiple of 1024)."""
+    for name, t in (("u", u), ("K_s", K_s), ("w", w), ("v", v), ("out", out)):
+        _dev_tensor(t, name)
+    B, H, N = u.shape
+    _check(_load().fftconv_fwd_short(
+        _ptr(u), _ptr(K_s), _ptr(w), _ptr(v), _ptr(out), B, H, N, L_filter, dtype_code(u.dtype),
+        _stream(stream, u.device)))
+
+
+def causal_conv_short(u, k, w=None, v=None, stream=None):
+    """Prepare a short filter k (L <= 512) and run one chunked forward call."""
+    H, L = k.shape
+    K_s = torch.empty(fftconv_short_filter_bytes(H, u.dtype), dtype=torch.uint8, device=u.device)
+    fftconv_prepare_short_filter(k, K_s, stream)
+    out = torch.empty_like(u)
+    fftconv_fwd_short(u, K_s, w, v, out, L, stream)
+    return out
+
+
 def alloc_filter(H: int, N: int, dtype: torch.dtype, device="cuda") -> torch.Tensor:
     """Device buffer for K_f (torch allocation; the library never allocates it)."""
     return torch.empty(fftconv_filter_bytes(H, N, dtype), dtype=torch.uint8, device=device)

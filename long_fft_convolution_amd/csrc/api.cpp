@@ -672,6 +672,55 @@ fftconv_status_t fftconv_bwd(const void *dy, const void *u, const void *K_f, con
     return ok();
 }
 
+// ---- chunked short-filter path ---------------------------------------------
+constexpr int64_t kShortWindow = 1024;   // window length; the filter spans at most half of it
+
+size_t fftconv_short_filter_bytes(int64_t H, fftconv_dtype_t dtype) {
+    if (dtype != FFTCONV_F16 && dtype != FFTCONV_BF16) return 0;
+    return fftconv_filter_bytes(H, kShortWindow, dtype);
+}
+
+fftconv_status_t fftconv_prepare_short_filter(const void *k, int64_t H, int64_t L, fftconv_dtype_t dtype,
+                                              void *K_s, size_t K_s_bytes, hipStream_t stream) {
+    g_last_error.clear();
+    if (dtype != FFTCONV_F16 && dtype != FFTCONV_BF16)
+        return fail(FFTCONV_ERR_UNSUPPORTED, "the short-filter path needs fp16 or bf16 storage");
+    if (L < 1 || L > kShortWindow / 2)
+        return fail(FFTCONV_ERR_INVALID_ARGUMENT, "L_filter=%lld must be in [1, %lld]", (long long)L,
+                    (long long)(kShortWindow / 2));
+    // the spectrum of the filter zero-padded to the window's transform size
+    return prepare_impl(k, H, L, kShortWindow, dtype, K_s, K_s_bytes, nullptr, 0, false, stream);
+}
+
+fftconv_status_t fftconv_fwd_short(const void *u, const void *K_s, const void *w, const void *v, void *out,
+                                   int64_t B, int64_t H, int64_t N, int64_t L, fftconv_dtype_t dtype,
+                                   hipStream_t stream) {
+    g_last_error.clear();
+    if (dtype != FFTCONV_F16 && dtype != FFTCONV_BF16)
+        return fail(FFTCONV_ERR_UNSUPPORTED, "the short-filter path needs fp16 or bf16 storage");
+    if (N < kShortWindow || N % kShortWindow != 0)
+        return fail(FFTCONV_ERR_UNSUPPORTED, "N=%lld must be a positive multiple of %lld", (long long)N,
+                    (long long)kShortWindow);
+    if (B < 0 || H < 0) return fail(FFTCONV_ERR_INVALID_ARGUMENT, "B and H must be >= 0");
+    if (L < 1 || L > kShortWindow / 2)
+        return fail(FFTCONV_ERR_INVALID_ARGUMENT, "L_filter=%lld must be in [1, %lld]", (long long)L,
+                    (long long)(kShortWindow / 2));
+    if (B * H == 0) return ok();
+    if (!u || !K_s || !out) return fail(FFTCONV_ERR_INVALID_ARGUMENT, "u, K_s and out must be non-null");
+    if (!aligned16(u) || !aligned16(K_s) || !aligned16(out) || (w && !aligned16(w)) || (v && !aligned16(v)))
+        return fail(FFTCONV_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+    const size_t nbytes = (size_t)B * (size_t)H * (size_t)N * elem_bytes(dtype);
+    if (overlap(out, nbytes, u, nbytes) || overlap(out, nbytes, w, nbytes) || overlap(out, nbytes, v, nbytes) ||
+        overlap(out, nbytes, K_s, fftconv_short_filter_bytes(H, dtype)))
+        return fail(FFTCONV_ERR_INVALID_ARGUMENT, "out overlaps an input");
+    const char *base = static_cast<const char *>(K_s);
+    const float *kscale = reinterpret_cast<const float *>(base + kf_scale_off());
+    const void *kbins = base + kf_bins_off(H);
+    const hipError_t e = launch_pair_conv_win(dtype, u, w, v, out, kbins, kscale, B, H, N, stream);
+    if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "fwd_short launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 fftconv_status_t fftconv_export_filter_rfft(const void *K_f, int64_t H, int64_t N,
                                             fftconv_dtype_t dtype, double *host_out,
                                             hipStream_t stream) {

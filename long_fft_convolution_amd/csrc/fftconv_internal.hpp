@@ -173,6 +173,11 @@ hipError_t launch_pair16k_conv(int st, const void *u, const void *w, const void 
 hipError_t launch_pair_conv(int logn, int st, const void *u, const void *w, const void *v,
                             void *out, const void *kbins, const float *kscale, const uint8_t *mask,
                             int64_t B, int64_t H, hipStream_t stream);
+// Chunked short-filter path: (B, H, NS) sequences, NS a multiple of 1024, as
+// half-overlapping windows of 1024 through the N = 1024 matrix-core kernel.
+hipError_t launch_pair_conv_win(int st, const void *u, const void *w, const void *v, void *out,
+                                const void *kbins, const float *kscale, int64_t B, int64_t H, int64_t NS,
+                                hipStream_t stream);
 hipError_t launch_write_header(const KfHeader &hdr, void *K_f, hipStream_t stream);
 
 hipError_t launch_multipass_conv(int logn, int st, const void *u, const void *w, const void *v,

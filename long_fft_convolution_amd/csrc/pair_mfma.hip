@@ -234,11 +234,19 @@ __device__ __forceinline__ void gate_product<__hip_bfloat16>(const uint4 &uq, co
     for (int e = 0; e < 8; ++e) x[e] = (_Float16)a[e];
 }
 
-template <typename T, bool MASKED, bool HAS_W, bool HAS_V>
+// WIN: the chunked short-filter path (overlap-save).  The (B, H, NS) sequences,
+// NS a multiple of 1024, are covered by windows of 1024 samples that overlap by
+// half: window j starts at (j - 1) 512 (zeros before the sequence start) and
+// keeps its outputs 512 .. 1023, the outputs j 512 .. j 512 + 511 of the
+// sequence; with a filter of at most 512 taps those depend only on the
+// window.  A pair is windows (2 jp, 2 jp + 1) of one sequence, so three
+// 512-sample blocks feed it and only the second halves are stored.
+template <typename T, bool MASKED, bool HAS_W, bool HAS_V, bool WIN = false>
 __global__ void __launch_bounds__(64 * kPairWaves, MASKED ? 1 : 2)
 pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restrict__ v,
               T *__restrict__ out, const uint4 *__restrict__ kbins, const float *__restrict__ kscale,
-              const uint8_t *__restrict__ mask, PairTables tb, int64_t B, int64_t H) {
+              const uint8_t *__restrict__ mask, PairTables tb, int64_t B, int64_t H, int64_t NS) {
+    static_assert(!(WIN && MASKED), "the windowed path has no frequency mask");
     constexpr int N = 1024;
     __shared__ h8 s_tw1[2 * 4 * 64];     // per (mt, nt, lane): cos[4], sin[4]
     __shared__ h8 s_tw3[4 * 2 * 64];     // per (nt, nt2, lane)
@@ -272,7 +280,7 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
     }
 
     // pair p = h * PB + bp (batch fastest); each XCD walks one contiguous range
-    const int64_t PB = (B + 1) / 2;
+    const int64_t PB = WIN ? B * (NS / 1024) : (B + 1) / 2;   // pairs per channel
     const int64_t P = H * PB;
     const uint32_t nwg = gridDim.x, xcd = blockIdx.x % 8, wg_local = blockIdx.x / 8;
     const uint32_t wg_on_xcd = nwg / 8 + (xcd < nwg % 8 ? 1u : 0u);
@@ -285,9 +293,17 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
     auto offsets = [&](int64_t p, int64_t &h, int64_t &oa, int64_t &ob, bool &has_b) {
         h = p / PB;
         const int64_t bp = p - h * PB;
-        has_b = 2 * bp + 1 < B;
-        oa = (2 * bp * H + h) * N;
-        ob = has_b ? oa + H * N : oa;
+        if (WIN) {
+            // window pair jp of batch row b: windows start at (2 jp - 1) 512 and 2 jp 512
+            const int64_t jpb = NS / 1024, b = bp / jpb, jp = bp - b * jpb;
+            has_b = true;
+            oa = (b * H + h) * NS + (2 * jp - 1) * 512;
+            ob = oa + 512;
+        } else {
+            has_b = 2 * bp + 1 < B;
+            oa = (2 * bp * H + h) * N;
+            ob = has_b ? oa + H * N : oa;
+        }
     };
 
     // per-pair side data: filter chunks, output-gate rows (contiguous 16-byte chunks in the
@@ -309,7 +325,8 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
         if (HAS_V) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                sd.v[q] = *reinterpret_cast<const uint4 *>(v + (q < 2 ? oa : ob) + 512 * (q & 1) + 8 * lane);
+                if (!WIN || (q & 1))   // windows store their second halves only
+                    sd.v[q] = *reinterpret_cast<const uint4 *>(v + (q < 2 ? oa : ob) + 512 * (q & 1) + 8 * lane);
         }
         sd.ks = kscale[h];
     };
@@ -317,7 +334,28 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
         int64_t h, oa, ob;
         bool hb;
         offsets(pp, h, oa, ob, hb);
-        load_pair_raw<T, HAS_W>(raw, u, w, oa, ob, lane);
+        if (WIN) {
+            // blocks b0 = [oa, oa + 512) (before the sequence for the first window: the
+            // load re-reads b1 and is zeroed), b1 = [oa + 512, ...), b2 = [oa + 1024, ...);
+            // window a = (b0, b1), window b = (b1, b2)
+            const int64_t base = oa + 512 - (oa + 512) % NS;
+            const bool first = oa < base;
+            const int64_t o0 = first ? oa + 512 : oa;
+            const int m = 8 * lane;
+            raw.q[0][0] = *reinterpret_cast<const uint4 *>(u + o0 + m);
+            raw.q[1][0] = *reinterpret_cast<const uint4 *>(u + oa + 512 + m);
+            raw.q[1][2] = *reinterpret_cast<const uint4 *>(u + oa + 1024 + m);
+            if (HAS_W) {
+                raw.q[0][1] = *reinterpret_cast<const uint4 *>(w + o0 + m);
+                raw.q[1][1] = *reinterpret_cast<const uint4 *>(w + oa + 512 + m);
+                raw.q[1][3] = *reinterpret_cast<const uint4 *>(w + oa + 1024 + m);
+            }
+            if (first) raw.q[0][0] = make_uint4(0u, 0u, 0u, 0u);
+            raw.q[0][2] = raw.q[1][0];
+            raw.q[0][3] = raw.q[1][1];
+        } else {
+            load_pair_raw<T, HAS_W>(raw, u, w, oa, ob, lane);
+        }
     };
 
     // software pipeline: inputs, filter chunks and gate chunks one pair ahead
@@ -463,6 +501,7 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
         // without a second row its stores repeat the first row's values
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
+            if (WIN && !(q & 1)) continue;   // windows store their second halves only
             const int qq = (q >= 2 && !has_b) ? q - 2 : q;
             const int u0 = 128 * (qq & 1) + 2 * lane;
             const int s0 = u0 ^ (((u0 >> 4) & 1) << 2), s1 = (u0 + 1) ^ ((((u0 + 1) >> 4) & 1) << 2);
@@ -508,7 +547,7 @@ hipError_t launch_pair_conv(int logn, int st, const void *u, const void *w, cons
         using TT = std::remove_pointer_t<decltype(tp)>;
         hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * kPairWaves), 0, stream,
                            (const TT *)u, (const TT *)w, (const TT *)v, (TT *)out,
-                           (const uint4 *)kbins, kscale, mask, tb, B, H);
+                           (const uint4 *)kbins, kscale, mask, tb, B, H, (int64_t)1024);
     };
     // one instantiation per (storage type, mask, gates): no gate test sits in the pair loop
     auto pick = [&](auto *tp) {
@@ -523,6 +562,44 @@ hipError_t launch_pair_conv(int logn, int st, const void *u, const void *w, cons
         case 5: go(pair1k_kernel<TT, true, false, true>, tp); break;
         case 6: go(pair1k_kernel<TT, true, true, false>, tp); break;
         default: go(pair1k_kernel<TT, true, true, true>, tp); break;
+        }
+    };
+    if (st == ST_F16) pick((__half *)nullptr);
+    else pick((__hip_bfloat16 *)nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_pair_conv_win(int st, const void *u, const void *w, const void *v, void *out,
+                                const void *kbins, const float *kscale, int64_t B, int64_t H, int64_t NS,
+                                hipStream_t stream) {
+    if (st == ST_F32 || NS < 1024 || NS % 1024 != 0) return hipErrorInvalidValue;
+    PairTables tb{};
+    hipError_t e = get_pair_tables(&tb);
+    if (e != hipSuccess) return e;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v_ = 0;
+        if (hipDeviceGetAttribute(&v_, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v_ > 0)
+            cus = v_;
+    }
+    const int64_t pairs = H * B * (NS / 1024);
+    int64_t blocks = (int64_t)cus * 2;
+    const int64_t need = (pairs + kPairWaves - 1) / kPairWaves;
+    if (blocks > need) blocks = need < 8 ? 8 : (need + 7) / 8 * 8;
+    auto go = [&](auto kern, auto *tp) {
+        using TT = std::remove_pointer_t<decltype(tp)>;
+        hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * kPairWaves), 0, stream,
+                           (const TT *)u, (const TT *)w, (const TT *)v, (TT *)out,
+                           (const uint4 *)kbins, kscale, (const uint8_t *)nullptr, tb, B, H, NS);
+    };
+    auto pick = [&](auto *tp) {
+        using TT = std::remove_pointer_t<decltype(tp)>;
+        const int sel = (w ? 2 : 0) | (v ? 1 : 0);
+        switch (sel) {
+        case 0: go(pair1k_kernel<TT, false, false, false, true>, tp); break;
+        case 1: go(pair1k_kernel<TT, false, false, true, true>, tp); break;
+        case 2: go(pair1k_kernel<TT, false, true, false, true>, tp); break;
+        default: go(pair1k_kernel<TT, false, true, true, true>, tp); break;
         }
     };
     if (st == ST_F16) pick((__half *)nullptr);

@@ -51,6 +51,7 @@ class Workload:
     decay: str = "loguniform"     # or "fixed0.01"
     mask_keep_blocks: int | None = None  # blocks [0, keep) kept, the rest zeroed
     seed: int = 1000
+    short: bool = False                  # run through the chunked short-filter path (L <= 512)
 
     @property
     def elems(self) -> int:
@@ -64,6 +65,8 @@ WORKLOADS = {
         Workload("gated_bf16_n16k", 4, 2560, 16384, 16384, "bf16", True, "loguniform", None, 1002),
         Workload("ungated_fp16_n1m", 1, 256, 1 << 20, 1 << 20, "f16", False, "loguniform", None, 1003),
         Workload("partial_sparse_n4m", 1, 128, 1 << 22, 1 << 20, "f16", False, "loguniform", 27, 1004),
+        # the chunked short-filter path: a 512-tap filter on the 1M-point sequences
+        Workload("short_fp16_n1m_l512", 1, 256, 1 << 20, 512, "f16", False, "loguniform", None, 1005, True),
     ]
 }
 

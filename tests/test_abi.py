@@ -165,3 +165,37 @@ def test_bwd_validation():
     assert call(du=0x20000 + 256) == 1 and "overlaps" in fc.fftconv_last_error()
     assert call(ws=None) == 3
     assert call(wsb=16) == 3
+
+
+def test_short_filter_abi():
+    lib = fc.lib()
+    F16, F32 = fc.FFTCONV_F16, fc.FFTCONV_F32
+    # the spectrum of a 1024-sample window: header, scales, 2048 bins of 4 bytes per channel
+    assert fc.fftconv_short_filter_bytes(3, F16) == fc.fftconv_filter_bytes(3, 1024, F16)
+    assert fc.fftconv_short_filter_bytes(3, F32) == 0
+
+    def prep(**kw):
+        a = dict(k=0x10000, H=2, L=100, dt=F16, K=0x100000, kb=1 << 20)
+        a.update(kw)
+        return lib.fftconv_prepare_short_filter(a["k"], a["H"], a["L"], a["dt"], a["K"], a["kb"], None)
+
+    assert prep(dt=F32) == 2
+    assert prep(L=513) == 1 and "L_filter" in fc.fftconv_last_error()
+    assert prep(L=0) == 1
+    assert prep(kb=16) == 1
+
+    def fwd(**kw):
+        a = dict(u=0x10000, K=0x20000, w=None, v=None, out=0x30000, B=1, H=1, N=2048, L=100, dt=F16)
+        a.update(kw)
+        return lib.fftconv_fwd_short(a["u"], a["K"], a["w"], a["v"], a["out"], a["B"], a["H"], a["N"],
+                                     a["L"], a["dt"], None)
+
+    assert fwd(dt=F32) == 2
+    assert fwd(N=1000) == 2 and "multiple of 1024" in fc.fftconv_last_error()
+    assert fwd(N=512) == 2
+    assert fwd(L=600) == 1
+    assert fwd(B=-1) == 1
+    assert fwd(u=None) == 1
+    assert fwd(out=0x30008) == 1 and "aligned" in fc.fftconv_last_error()
+    assert fwd(out=0x10000 + 16) == 1 and "overlaps" in fc.fftconv_last_error()
+    assert fwd(B=0, u=None, out=None, K=None) == 0
