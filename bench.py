@@ -36,7 +36,8 @@ from long_fft_convolution_amd import synth  # noqa: E402
 METRIC = "FFT-conv fwd B·H·N elems/s + % HBM peak (rocprof), N=1K..4M, 1 GPU"
 HBM_PEAK_GBS = 8000.0
 ELEM = {"f32": 4, "f16": 2, "bf16": 2}
-KERNEL_SOURCES = ["fused.hip", "multipass.hip", "pair_mfma.hip", "pair16k.hip", "fft_device.hpp",
+KERNEL_SOURCES = ["fused.hip", "multipass.hip", "pair_mfma.hip", "pair16k.hip", "eqlinear.hip", "cmfma.hpp",
+                  "fft_device.hpp",
                   "fftconv_internal.hpp", "api.cpp"]
 
 
@@ -129,7 +130,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gated_fp16_n1k", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--workload", default="gated_fp16_n1k",
+                    choices=sorted(synth.WORKLOADS) + sorted(synth.EQ_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd",
                     help="time the forward call (default) or the backward call")
@@ -137,10 +139,12 @@ def main():
                     help="also run one plain device copy of the activation bytes (counter scale)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(sequences are independent: shard (b, h) across devices, see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py: runs on one GPU; --gpus {args.gpus} is not supported "
+              "(sequences are independent: (b, h) would be sharded across devices)", file=sys.stderr)
         sys.exit(2)
 
+    if args.workload in synth.EQ_WORKLOADS:
+        return bench_eqlinear(args)
     wl = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     log(f"bench: generating {wl.name} (B={wl.B} H={wl.H} N={wl.N} L={wl.L} {wl.dtype})")
@@ -238,6 +242,70 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+def bench_eqlinear(args):
+    """One step = one fftconv_eqlinear_fwd call (the group-axis circular convolution)."""
+    wl = synth.EQ_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    log(f"bench: generating {wl.name} (N={wl.N} T={wl.T} C_in={wl.C_in} C_out={wl.C_out} {wl.dtype})")
+    x_h, W_h = synth.generate_eq(wl.name)
+    x, W = x_h.to(dev), W_h.to(dev)
+    W_f = torch.empty(fc.fftconv_eqlinear_weight_bytes(wl.T, wl.C_out, wl.C_in), dtype=torch.uint8, device=dev)
+    fc.fftconv_eqlinear_prepare(W, W_f)
+    y = torch.empty((wl.N, wl.T, wl.C_out), dtype=x.dtype, device=dev)
+    for _ in range(args.warmup):
+        fc.fftconv_eqlinear_fwd(x, W_f, y)
+    torch.cuda.synchronize(dev)
+    stream = torch.cuda.current_stream(dev)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        fc.fftconv_eqlinear_fwd(x, W_f, y)
+    t1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = t0.elapsed_time(t1) / args.steps
+    e = ELEM[wl.dtype]
+    alg = wl.N * wl.T * (wl.C_in + wl.C_out) * e + W_f.numel()
+    # matrix-core work: per token, f = 0 and T/2 are real products, the T/2 - 1 others complex (4 real)
+    flops = 2.0 * wl.N * wl.C_in * wl.C_out * (2 + 4 * (wl.T // 2 - 1))
+    value = wl.N * wl.T * wl.C_in / (ms / 1e3)
+    achieved = alg / (ms / 1e3) / 1e9
+    log(f"bench: {ms * 1e3:.1f} us/step, {value:.3e} elems/s, {achieved:.0f} GB/s algorithmic "
+        f"({achieved / HBM_PEAK_GBS:.1%} of 8 TB/s), MFMA {flops / (ms / 1e3) / 1e12:.1f} TFLOP/s")
+    if args.calibrate_copy:
+        n = (alg // 2) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize(dev)
+        log(f"bench: calibration copy kernel moved {n * 4} bytes each way")
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle.eqlinear import eqlinear_tokens
+        n = 256
+        xx, WW = x_h[:n].double().numpy(), W_h.double().numpy()
+        t = time.perf_counter()
+        eqlinear_tokens(xx, WW, np.arange(n))
+        dt = time.perf_counter() - t
+        cpu = {"value": n * wl.T * wl.C_in / dt, "unit": "elems/s", "cores": torch.get_num_threads(),
+               "kind": "oracle", "sample": f"{n} of {wl.N} tokens of {wl.name}, float64 numpy, {dt:.2f} s"}
+    rec = {
+        "metric": "group-axis circular conv fwd N*T*C_in elems/s + % HBM peak, 1 GPU",
+        "value": value, "unit": "elems/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (seeded N(0,1) activations, N(0, 1/(T C_in)) weights)",
+        "config": {"workload": wl.name, "N": wl.N, "T": wl.T, "C_in": wl.C_in, "C_out": wl.C_out,
+                   "storage": wl.dtype, "arithmetic": "fp16 MFMA operands, fp32 accumulation",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "eqlinear_kernel", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name),
+                     "algorithmic_bytes": int(alg), "kernel_ms": ms, "mfma_tflops": flops / (ms / 1e3) / 1e12},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
 
 
 def bench_bwd(args, wl, dev, u, K_f, w, v, mask):

@@ -170,6 +170,32 @@ fftconv_status_t fftconv_fwd_short(const void *u, const void *K_s, const void *w
                                    void *out, int64_t B, int64_t H, int64_t N, int64_t L_filter,
                                    fftconv_dtype_t dtype, hipStream_t stream);
 
+/* ---- Group-axis circular convolution (Flash EQ-Linear) ------------------
+ * The Flash EQ-Linear abstract page: an equivariant linear layer is a
+ * circular convolution along the group dimension composed with a linear map
+ * along the channels, computed through the Fourier convolution theorem along
+ * the group axis with the real DFT's conjugate symmetry.  Here, for a cyclic
+ * group of order T:
+ *   y[n, t, d] = sum_{s < T} sum_{c < C_in} W[s, d, c] x[n, (t - s) mod T, c]
+ * x (N, T, C_in), W (T, C_out, C_in), y (N, T, C_out), contiguous, fp16 or
+ * bf16 storage; T in {4, 8, 16}; C_in and C_out positive multiples of 32.
+ * The per-frequency channel products run on the matrix cores with fp16
+ * operands and fp32 accumulation. */
+
+/* Bytes of the transformed weights (T/2 + 1 complex fp16 matrices); 0 when unsupported. */
+size_t fftconv_eqlinear_weight_bytes(int64_t T, int64_t C_out, int64_t C_in);
+
+/* W (T, C_out, C_in) device array -> W_f (W_f_bytes >= fftconv_eqlinear_weight_bytes).
+ * Asynchronous on stream. */
+fftconv_status_t fftconv_eqlinear_prepare(const void *W, int64_t T, int64_t C_out, int64_t C_in,
+                                          fftconv_dtype_t dtype, void *W_f, size_t W_f_bytes,
+                                          hipStream_t stream);
+
+/* y = the group convolution of x with the prepared weights W_f.  Asynchronous on
+ * stream; y must not overlap x or W_f. */
+fftconv_status_t fftconv_eqlinear_fwd(const void *x, const void *W_f, void *y, int64_t N, int64_t T,
+                                      int64_t C_in, int64_t C_out, fftconv_dtype_t dtype, hipStream_t stream);
+
 /* Static text for a status code. */
 const char *fftconv_status_string(fftconv_status_t status);
 

@@ -72,6 +72,12 @@ def _load():
     lib.fftconv_prepare_short_filter.restype = ctypes.c_int
     lib.fftconv_fwd_short.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, vp]
     lib.fftconv_fwd_short.restype = ctypes.c_int
+    lib.fftconv_eqlinear_weight_bytes.argtypes = [i64, i64, i64]
+    lib.fftconv_eqlinear_weight_bytes.restype = sz
+    lib.fftconv_eqlinear_prepare.argtypes = [vp, i64, i64, i64, ctypes.c_int, vp, sz, vp]
+    lib.fftconv_eqlinear_prepare.restype = ctypes.c_int
+    lib.fftconv_eqlinear_fwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, vp]
+    lib.fftconv_eqlinear_fwd.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -228,6 +234,40 @@ def causal_conv_short(u, k, w=None, v=None, stream=None):
     out = torch.empty_like(u)
     fftconv_fwd_short(u, K_s, w, v, out, L, stream)
     return out
+
+
+def fftconv_eqlinear_weight_bytes(T: int, C_out: int, C_in: int) -> int:
+    return int(_load().fftconv_eqlinear_weight_bytes(T, C_out, C_in))
+
+
+def fftconv_eqlinear_prepare(W: torch.Tensor, W_f: torch.Tensor, stream=None) -> None:
+    """W_f <- the group-axis real DFT of W (T, C_out, C_in)."""
+    _dev_tensor(W, "W")
+    _dev_tensor(W_f, "W_f")
+    T, C_out, C_in = W.shape
+    _check(_load().fftconv_eqlinear_prepare(
+        _ptr(W), T, C_out, C_in, dtype_code(W.dtype), _ptr(W_f), W_f.numel() * W_f.element_size(),
+        _stream(stream, W.device)))
+
+
+def fftconv_eqlinear_fwd(x: torch.Tensor, W_f: torch.Tensor, y: torch.Tensor, stream=None) -> None:
+    """y (N, T, C_out) <- group circular convolution of x (N, T, C_in) with the prepared W_f."""
+    for name, t in (("x", x), ("W_f", W_f), ("y", y)):
+        _dev_tensor(t, name)
+    N, T, C_in = x.shape
+    C_out = y.shape[2]
+    _check(_load().fftconv_eqlinear_fwd(
+        _ptr(x), _ptr(W_f), _ptr(y), N, T, C_in, C_out, dtype_code(x.dtype), _stream(stream, x.device)))
+
+
+def eqlinear(x, W, stream=None):
+    """Prepare W and run the group convolution once (allocations by torch)."""
+    T, C_out, C_in = W.shape
+    W_f = torch.empty(fftconv_eqlinear_weight_bytes(T, C_out, C_in), dtype=torch.uint8, device=x.device)
+    fftconv_eqlinear_prepare(W, W_f, stream)
+    y = torch.empty((x.shape[0], T, C_out), dtype=x.dtype, device=x.device)
+    fftconv_eqlinear_fwd(x, W_f, y, stream)
+    return y
 
 
 def alloc_filter(H: int, N: int, dtype: torch.dtype, device="cuda") -> torch.Tensor:

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libfftconv.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["api.cpp", "bwd.hip", "filter.hip", "fused.hip", "multipass.hip", "pair_mfma.hip", "pair16k.hip"]
+SOURCES = ["api.cpp", "bwd.hip", "eqlinear.hip", "filter.hip", "fused.hip", "multipass.hip", "pair_mfma.hip", "pair16k.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

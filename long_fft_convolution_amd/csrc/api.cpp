@@ -721,6 +721,59 @@ fftconv_status_t fftconv_fwd_short(const void *u, const void *K_s, const void *w
     return ok();
 }
 
+// ---- group-axis circular convolution ----------------------------------------
+static bool eq_group_ok(int64_t T) { return T == 4 || T == 8 || T == 16; }
+
+size_t fftconv_eqlinear_weight_bytes(int64_t T, int64_t C_out, int64_t C_in) {
+    if (!eq_group_ok(T) || C_out < 1 || C_in < 1) return 0;
+    return (size_t)(T / 2 + 1) * 2 * (size_t)C_out * (size_t)C_in * 2;
+}
+
+fftconv_status_t fftconv_eqlinear_prepare(const void *W, int64_t T, int64_t C_out, int64_t C_in,
+                                          fftconv_dtype_t dtype, void *W_f, size_t W_f_bytes,
+                                          hipStream_t stream) {
+    g_last_error.clear();
+    if (dtype != FFTCONV_F16 && dtype != FFTCONV_BF16)
+        return fail(FFTCONV_ERR_UNSUPPORTED, "the group convolution needs fp16 or bf16 storage");
+    if (!eq_group_ok(T)) return fail(FFTCONV_ERR_UNSUPPORTED, "group order T=%lld must be 4, 8 or 16", (long long)T);
+    if (C_in < 32 || C_in % 32 != 0 || C_out < 32 || C_out % 32 != 0)
+        return fail(FFTCONV_ERR_UNSUPPORTED, "C_in=%lld and C_out=%lld must be positive multiples of 32",
+                    (long long)C_in, (long long)C_out);
+    if (!W || !W_f) return fail(FFTCONV_ERR_INVALID_ARGUMENT, "W and W_f must be non-null");
+    if (!aligned16(W) || !aligned16(W_f))
+        return fail(FFTCONV_ERR_INVALID_ARGUMENT, "W and W_f must be 16-byte aligned");
+    const size_t need = fftconv_eqlinear_weight_bytes(T, C_out, C_in);
+    if (W_f_bytes < need) return fail(FFTCONV_ERR_INVALID_ARGUMENT, "W_f has %zu bytes, needs %zu", W_f_bytes, need);
+    if (overlap(W, (size_t)T * C_out * C_in * elem_bytes(dtype), W_f, need))
+        return fail(FFTCONV_ERR_INVALID_ARGUMENT, "W overlaps W_f");
+    const hipError_t e = launch_eqlinear_prepare(dtype, (int)T, W, W_f, C_out, C_in, stream);
+    if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "eqlinear prepare launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+fftconv_status_t fftconv_eqlinear_fwd(const void *x, const void *W_f, void *y, int64_t N, int64_t T,
+                                      int64_t C_in, int64_t C_out, fftconv_dtype_t dtype, hipStream_t stream) {
+    g_last_error.clear();
+    if (dtype != FFTCONV_F16 && dtype != FFTCONV_BF16)
+        return fail(FFTCONV_ERR_UNSUPPORTED, "the group convolution needs fp16 or bf16 storage");
+    if (!eq_group_ok(T)) return fail(FFTCONV_ERR_UNSUPPORTED, "group order T=%lld must be 4, 8 or 16", (long long)T);
+    if (C_in < 32 || C_in % 32 != 0 || C_out < 32 || C_out % 32 != 0)
+        return fail(FFTCONV_ERR_UNSUPPORTED, "C_in=%lld and C_out=%lld must be positive multiples of 32",
+                    (long long)C_in, (long long)C_out);
+    if (N < 0) return fail(FFTCONV_ERR_INVALID_ARGUMENT, "N must be >= 0");
+    if (N == 0) return ok();
+    if (!x || !W_f || !y) return fail(FFTCONV_ERR_INVALID_ARGUMENT, "x, W_f and y must be non-null");
+    if (!aligned16(x) || !aligned16(W_f) || !aligned16(y))
+        return fail(FFTCONV_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+    const size_t ybytes = (size_t)N * T * C_out * elem_bytes(dtype);
+    if (overlap(y, ybytes, x, (size_t)N * T * C_in * elem_bytes(dtype)) ||
+        overlap(y, ybytes, W_f, fftconv_eqlinear_weight_bytes(T, C_out, C_in)))
+        return fail(FFTCONV_ERR_INVALID_ARGUMENT, "y overlaps an input");
+    const hipError_t e = launch_eqlinear(dtype, (int)T, x, W_f, y, N, C_in, C_out, stream);
+    if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "eqlinear launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 fftconv_status_t fftconv_export_filter_rfft(const void *K_f, int64_t H, int64_t N,
                                             fftconv_dtype_t dtype, double *host_out,
                                             hipStream_t stream) {

@@ -178,6 +178,12 @@ hipError_t launch_pair_conv(int logn, int st, const void *u, const void *w, cons
 hipError_t launch_pair_conv_win(int st, const void *u, const void *w, const void *v, void *out,
                                 const void *kbins, const float *kscale, int64_t B, int64_t H, int64_t NS,
                                 hipStream_t stream);
+// Group-axis circular convolution composed with a channel map (eqlinear.hip).
+int eqlinear_span(int T);   // output channels per workgroup (C_out must be a multiple of span / 4)
+hipError_t launch_eqlinear_prepare(int st, int T, const void *W, void *Wf, int64_t Cout, int64_t Cin,
+                                   hipStream_t stream);
+hipError_t launch_eqlinear(int st, int T, const void *x, const void *Wf, void *y, int64_t Ntok, int64_t Cin,
+                           int64_t Cout, hipStream_t stream);
 hipError_t launch_write_header(const KfHeader &hdr, void *K_f, hipStream_t stream);
 
 hipError_t launch_multipass_conv(int logn, int st, const void *u, const void *w, const void *v,

@@ -147,3 +147,33 @@ def generate_workload(name: str, seed: int | None = None) -> Inputs:
     w = WORKLOADS[name]
     return generate(w.B, w.H, w.N, w.L, w.dtype, w.gated, w.decay,
                     w.seed if seed is None else seed, w.mask_keep_blocks)
+
+
+# ---- group-axis circular convolution (the Flash EQ-Linear operator) ----------
+@dataclass(frozen=True)
+class EqWorkload:
+    name: str
+    N: int        # tokens
+    T: int        # cyclic group order
+    C_in: int
+    C_out: int
+    dtype: str
+    seed: int
+
+
+EQ_WORKLOADS = {
+    w.name: w for w in [
+        # a vision-transformer-sized equivariant linear layer: 64K tokens, C8 rotations, 128 channels
+        EqWorkload("eqlinear_fp16_t8", 65536, 8, 128, 128, "f16", 1006),
+    ]
+}
+
+
+def generate_eq(name: str):
+    """x (N, T, C_in) ~ N(0, 1) and W (T, C_out, C_in) ~ N(0, 1 / (T C_in)), rounded to the dtype."""
+    w = EQ_WORKLOADS[name]
+    g = torch.Generator().manual_seed(w.seed)
+    dt = {"f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    x = torch.randn((w.N, w.T, w.C_in), generator=g).to(dt)
+    W = (torch.randn((w.T, w.C_out, w.C_in), generator=g) / float(np.sqrt(w.T * w.C_in))).to(dt)
+    return x, W

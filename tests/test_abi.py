@@ -199,3 +199,35 @@ def test_short_filter_abi():
     assert fwd(out=0x30008) == 1 and "aligned" in fc.fftconv_last_error()
     assert fwd(out=0x10000 + 16) == 1 and "overlaps" in fc.fftconv_last_error()
     assert fwd(B=0, u=None, out=None, K=None) == 0
+
+
+def test_eqlinear_abi():
+    lib = fc.lib()
+    F16, F32 = fc.FFTCONV_F16, fc.FFTCONV_F32
+    # T/2 + 1 frequencies, two fp16 planes each
+    assert fc.fftconv_eqlinear_weight_bytes(8, 64, 32) == 5 * 2 * 64 * 32 * 2
+    assert fc.fftconv_eqlinear_weight_bytes(6, 64, 32) == 0
+
+    def prep(**kw):
+        a = dict(W=0x10000, T=8, Co=64, Ci=32, dt=F16, Wf=0x100000, b=1 << 20)
+        a.update(kw)
+        return lib.fftconv_eqlinear_prepare(a["W"], a["T"], a["Co"], a["Ci"], a["dt"], a["Wf"], a["b"], None)
+
+    assert prep(dt=F32) == 2
+    assert prep(T=6) == 2 and "4, 8 or 16" in fc.fftconv_last_error()
+    assert prep(Ci=48) == 2
+    assert prep(Co=16) == 2
+    assert prep(b=100) == 1
+    assert prep(W=None) == 1
+
+    def fwd(**kw):
+        a = dict(x=0x10000, Wf=0x200000, y=0x400000, N=10, T=8, Ci=32, Co=64, dt=F16)
+        a.update(kw)
+        return lib.fftconv_eqlinear_fwd(a["x"], a["Wf"], a["y"], a["N"], a["T"], a["Ci"], a["Co"], a["dt"], None)
+
+    assert fwd(T=12) == 2
+    assert fwd(dt=F32) == 2
+    assert fwd(N=-1) == 1
+    assert fwd(N=0, x=None, y=None) == 0
+    assert fwd(y=0x400008) == 1 and "aligned" in fc.fftconv_last_error()
+    assert fwd(y=0x10000 + 64) == 1 and "overlaps" in fc.fftconv_last_error()
