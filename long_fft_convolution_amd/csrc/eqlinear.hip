@@ -114,22 +114,32 @@ eqlinear_kernel(const S *__restrict__ x, const _Float16 *__restrict__ Wf, S *__r
     const int tok = tid >> 4, cp = tid & 15;
     const int64_t n = n0 + tok;
     const int64_t nsafe = n < Ntok ? n : Ntok - 1;
-    auto stage_a = [&](int kc, int b) {
+    // raw input of one chunk (two channels per lane, T group elements), loaded a
+    // chunk ahead so that the loads overlap the previous chunk's products
+    typedef uint32_t Raw[T];
+    auto load_a = [&](int kc, Raw &raw) {
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+            raw[t] = *reinterpret_cast<const uint32_t *>(x + (nsafe * T + t) * Cin + 32 * kc + 2 * cp);
+    };
+    auto stage_a = [&](const Raw &raw, int b) {
         float2 xv[T];
 #pragma unroll
-        for (int t = 0; t < T; ++t) xv[t] = st<S>::ld2(x + (nsafe * T + t) * Cin + 32 * kc + 2 * cp);
+        for (int t = 0; t < T; ++t) xv[t] = st<S>::ld2(reinterpret_cast<const S *>(&raw[t]));
         if (n >= Ntok) {
 #pragma unroll
             for (int t = 0; t < T; ++t) xv[t] = make_float2(0.f, 0.f);
         }
+        // the two channels as one complex sequence z = x0 + i x1: one T-point DFT,
+        // then X0[f] = (Z[f] + conj Z[T-f]) / 2, X1[f] = (Z[f] - conj Z[T-f]) / 2i
+        float2 zf[T];
+        Dft<T>::run(xv, zf);
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
-            float2 a0 = make_float2(0.f, 0.f), a1 = make_float2(0.f, 0.f);
-#pragma unroll
-            for (int t = 0; t < T; ++t) {
-                a0 = cadd(a0, rot<T>(make_float2(xv[t].x, 0.f), t * f));
-                a1 = cadd(a1, rot<T>(make_float2(xv[t].y, 0.f), t * f));
-            }
+            const float2 za = zf[f], zb = cconj(zf[(T - f) % T]);
+            const float2 a0 = cscale(cadd(za, zb), 0.5f);
+            const float2 dd = csub(za, zb);
+            const float2 a1 = make_float2(0.5f * dd.y, -0.5f * dd.x);
             _Float16 *pr = smem + (((b * NF + f) * 2 + 0) * 16 + tok) * 32 + 2 * cp;
             _Float16 *pi = smem + (((b * NF + f) * 2 + 1) * 16 + tok) * 32 + 2 * cp;
             typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -147,11 +157,13 @@ eqlinear_kernel(const S *__restrict__ x, const _Float16 *__restrict__ Wf, S *__r
             acci[f][j] = f4{0.f, 0.f, 0.f, 0.f};
         }
 
-    stage_a(0, 0);
+    Raw raw;
+    load_a(0, raw);
+    stage_a(raw, 0);
     __syncthreads();
     for (int kc = 0; kc < nchunk; ++kc) {
         const int b = kc & 1;
-        if (kc + 1 < nchunk) stage_a(kc + 1, b ^ 1);
+        if (kc + 1 < nchunk) load_a(kc + 1, raw);
         if (active) {
             // ---- B: per frequency, rows = tokens (A from LDS), columns = output channels
 #pragma unroll
@@ -175,6 +187,9 @@ eqlinear_kernel(const S *__restrict__ x, const _Float16 *__restrict__ Wf, S *__r
                 }
             }
         }
+        // the next chunk's transform goes to the other buffer, which every wave
+        // finished reading before the previous barrier
+        if (kc + 1 < nchunk) stage_a(raw, b ^ 1);
         __syncthreads();
     }
 
