@@ -96,7 +96,7 @@ eqlinear_prepare_kernel(const S *__restrict__ W, _Float16 *__restrict__ Wf, int6
     }
 }
 
-// grid (ceil(C_out / DSPAN), ceil(N / 16)); block 256; dynamic LDS Plan<T>::kLds
+// grid: 8 D ceil(N / 128) workgroups (D = ceil(C_out / DSPAN)); block 256; dynamic LDS Plan<T>::kLds
 template <int T, typename S>
 __global__ void __launch_bounds__(256)
 eqlinear_kernel(const S *__restrict__ x, const _Float16 *__restrict__ Wf, S *__restrict__ y, int64_t Ntok,
@@ -107,8 +107,14 @@ eqlinear_kernel(const S *__restrict__ x, const _Float16 *__restrict__ Wf, S *__r
     extern __shared__ __align__(16) _Float16 smem[];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, c = lane & 15;
-    const int64_t n0 = (int64_t)blockIdx.y * 16;
-    const int64_t d0 = (int64_t)blockIdx.x * DSPAN;
+    // 1-D grid: workgroup L runs on XCD L % 8; the D output-channel spans of one
+    // token tile are L, L + 8, ..., so they share an XCD and its L2 and x is
+    // read from HBM once per tile
+    const uint32_t L = blockIdx.x, q = L / 8, D = (uint32_t)((Cout + DSPAN - 1) / DSPAN);
+    const int64_t tt = (int64_t)(q / D) * 8 + (L % 8);
+    if (tt * 16 >= Ntok) return;   // (whole workgroup: before any barrier)
+    const int64_t n0 = tt * 16;
+    const int64_t d0 = (int64_t)(q % D) * DSPAN;
     const int64_t dw = d0 + 16 * NT * wave;              // this wave's first output channel
     const bool active = dw < Cout;                       // (C_out is a multiple of 16 NT)
     const int64_t DC = Cout * Cin;
@@ -242,7 +248,8 @@ static hipError_t eq_launch(const void *x, const void *Wf, void *y, int64_t Ntok
     auto k = eqlinear_kernel<T, S>;
     hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)P::kLds);
     if (e != hipSuccess) return e;
-    const dim3 grid((unsigned)((Cout + P::DSPAN - 1) / P::DSPAN), (unsigned)((Ntok + 15) / 16));
+    const int64_t D = (Cout + P::DSPAN - 1) / P::DSPAN, tiles = (Ntok + 15) / 16;
+    const dim3 grid((unsigned)(((tiles + 7) / 8) * 8 * D));
     hipLaunchKernelGGL(k, grid, dim3(256), P::kLds, stream, (const S *)x, (const _Float16 *)Wf, (S *)y, Ntok,
                        Cin, Cout);
     return hipGetLastError();
