@@ -279,23 +279,48 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
         c2i[t] = F2i[t * 64 + lane];
     }
 
-    // pair p = h * PB + bp (batch fastest); each XCD walks one contiguous range
+    // Pair index spaces.  Windows: p = h PB + bp (window pairs of one sequence fastest:
+    // neighbouring waves read neighbouring memory); each XCD walks one contiguous range.
+    // Batch-row pairs: with H >= 8 each XCD owns the channels [h0, h0 + Hx) and walks
+    // p = bp Hx + (h - h0), the channel fastest, so that the waves in flight read the
+    // contiguous rows of neighbouring channels while the XCD's filter spectra stay in its
+    // L2 (with the batch fastest, neighbouring waves read rows 2 H N elements apart and
+    // the HBM pages are poorly used); with H < 8 the XCDs split p = bp H + h.
     const int64_t PB = WIN ? B * (NS / 1024) : (B + 1) / 2;   // pairs per channel
     const int64_t P = H * PB;
     const uint32_t nwg = gridDim.x, xcd = blockIdx.x % 8, wg_local = blockIdx.x / 8;
     const uint32_t wg_on_xcd = nwg / 8 + (xcd < nwg % 8 ? 1u : 0u);
-    const int64_t p_begin = P * xcd / 8, p_end = P * (xcd + 1) / 8;
+    int64_t p_begin, p_end, h0 = 0, Hx = H;
+    if (!WIN && H >= 8) {
+        h0 = H * xcd / 8;
+        Hx = H * (xcd + 1) / 8 - h0;
+        p_begin = 0;
+        p_end = Hx * PB;
+    } else {
+        p_begin = P * xcd / 8;
+        p_end = P * (xcd + 1) / 8;
+    }
     const int64_t stride = (int64_t)wg_on_xcd * kPairWaves;
     _Float16 *zr = reinterpret_cast<_Float16 *>(s_z[wave]), *zi = zr + kPlane;
     char *const so = reinterpret_cast<char *>(s_z[wave]);
     const f4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
+    // (the host keeps the pair count below 2^31: 32-bit divisions)
     auto offsets = [&](int64_t p, int64_t &h, int64_t &oa, int64_t &ob, bool &has_b) {
-        h = p / PB;
-        const int64_t bp = p - h * PB;
+        int64_t bp;
+        if (WIN) {
+            const uint32_t h32 = (uint32_t)p / (uint32_t)PB;
+            h = h32;
+            bp = (uint32_t)p - h32 * (uint32_t)PB;
+        } else {
+            const uint32_t b32 = (uint32_t)p / (uint32_t)Hx;
+            bp = b32;
+            h = h0 + ((uint32_t)p - b32 * (uint32_t)Hx);
+        }
         if (WIN) {
             // window pair jp of batch row b: windows start at (2 jp - 1) 512 and 2 jp 512
-            const int64_t jpb = NS / 1024, b = bp / jpb, jp = bp - b * jpb;
+            const uint32_t jpb = (uint32_t)(NS / 1024), b32 = (uint32_t)bp / jpb;
+            const int64_t b = b32, jp = (uint32_t)bp - b32 * jpb;
             has_b = true;
             oa = (b * H + h) * NS + (2 * jp - 1) * 512;
             ob = oa + 512;
@@ -306,14 +331,13 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
         }
     };
 
-    // per-pair side data: filter chunks, output-gate rows (contiguous 16-byte chunks in the
-    // order the output is stored) and the channel scale
-    struct Side {
+    // per-pair side data: the filter chunks with the channel scale, and the output-gate rows
+    // (contiguous 16-byte chunks in the order the output is stored)
+    struct Filt {
         uint4 k[2][4];
-        uint4 v[4];
         float ks;
     };
-    auto load_side = [&](int64_t pp, Side &sd) {
+    auto load_filt = [&](int64_t pp, Filt &fk) {
         int64_t h, oa, ob;
         bool hb;
         offsets(pp, h, oa, ob, hb);
@@ -321,14 +345,14 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
 #pragma unroll
         for (int mt2 = 0; mt2 < 2; ++mt2)
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) sd.k[mt2][nt] = krow[(mt2 * 4 + nt) * 64 + lane];
-        if (HAS_V) {
+            for (int nt = 0; nt < 4; ++nt) fk.k[mt2][nt] = krow[(mt2 * 4 + nt) * 64 + lane];
+        fk.ks = kscale[h];
+    };
+    auto load_gate = [&](int64_t oa, int64_t ob, uint4 (&vg)[4]) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                if (!WIN || (q & 1))   // windows store their second halves only
-                    sd.v[q] = *reinterpret_cast<const uint4 *>(v + (q < 2 ? oa : ob) + 512 * (q & 1) + 8 * lane);
-        }
-        sd.ks = kscale[h];
+        for (int q = 0; q < 4; ++q)
+            if (!WIN || (q & 1))   // windows store their second halves only
+                vg[q] = *reinterpret_cast<const uint4 *>(v + (q < 2 ? oa : ob) + 512 * (q & 1) + 8 * lane);
     };
     auto load_in = [&](int64_t pp, PairRaw &raw) {
         int64_t h, oa, ob;
@@ -358,25 +382,32 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
         }
     };
 
-    // software pipeline: inputs, filter chunks and gate chunks one pair ahead
+    // software pipeline: the next pair's inputs are loaded into the registers of this pair's
+    // inputs once these are scattered to LDS, its filter chunks into this pair's once S2 has
+    // used them (no register copies: a copy of a prefetched set would make the compiler wait
+    // for its loads in the middle of the current pair); the gate rows are loaded at the top
+    // of their own pair and used at its end
+    //   The prefetch loads are issued on every path (the last one re-reads the current pair,
+    // a wave with no pair reads its first pair): with a branch around them the compiler has to
+    // assume that they may be absent, and each later wait for an older load then waits for
+    // the prefetch as well.
     int64_t p = p_begin + (int64_t)wg_local * kPairWaves + wave;
     PairRaw cur;
-    Side sc;
-    if (p < p_end) {
-        load_in(p, cur);
-        load_side(p, sc);
-    }
+    Filt fc;
+    // (the same load order as in the loop, so that the waits at the loop head hold for both
+    // ways into it)
+    load_in(p < p_end ? p : 0, cur);
+    __builtin_amdgcn_sched_barrier(0);
+    load_filt(p < p_end ? p : 0, fc);
+    __builtin_amdgcn_sched_barrier(0);
     for (; p < p_end; p += stride) {
         int64_t h, oa, ob;
         bool has_b;
         offsets(p, h, oa, ob, has_b);
-        PairRaw in1;
-        Side sn;
-        if (p + stride < p_end) {
-            load_in(p + stride, in1);
-            load_side(p + stride, sn);
-        }
-        const float ks = sc.ks;
+        const int64_t pn = p + stride < p_end ? p + stride : p;
+        uint4 vg[4];
+        if (HAS_V) load_gate(oa, ob, vg);
+        const float ks = fc.ks;
 
         // ---- x = u * w of both sequences, scattered into the transposed LDS planes
 #pragma unroll
@@ -405,6 +436,9 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        __builtin_amdgcn_sched_barrier(0);   // (keep the prefetch loads where they are)
+        load_in(pn, cur);
+        __builtin_amdgcn_sched_barrier(0);
         const h8 ndi0 = neg8(di[0]), ndi1 = neg8(di[1]);
         const uint8_t *mrow = MASKED ? mask + h * kMaskBlocks : nullptr;
 
@@ -438,7 +472,7 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
                 ai = mfma(c2i[mt2], br, ai);
                 yr[mt2] = to_h4(ar);
                 yi[mt2] = to_h4(ai);
-                h8 kk = *reinterpret_cast<const h8 *>(&sc.k[mt2][nt]);
+                h8 kk = *reinterpret_cast<const h8 *>(&fc.k[mt2][nt]);
                 if (MASKED) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -470,6 +504,10 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
                 }
             }
         }
+
+        __builtin_amdgcn_sched_barrier(0);
+        load_filt(pn, fc);
+        __builtin_amdgcn_sched_barrier(0);
 
         // ---- S1': rows n_f (tiles nt2), columns n_s (tiles nt3, n_s < 32 only), K = f_s
 #pragma unroll
@@ -510,7 +548,7 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
             float y[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
             if (HAS_V) {
                 float g8[8];
-                unpack8<T>(sc.v[q], g8);
+                unpack8<T>(vg[q], g8);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) y[e] *= g8[e];
             }
@@ -520,8 +558,6 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        cur = in1;
-        sc = sn;
     }
 }
 
@@ -539,6 +575,8 @@ hipError_t launch_pair_conv(int logn, int st, const void *u, const void *w, cons
             cus = v_;
     }
     const int64_t pairs = H * ((B + 1) / 2);
+    if (pairs >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    if (pairs == 0) return hipSuccess;
     // two resident 4-wave workgroups per CU (one for the masked variant)
     int64_t blocks = (int64_t)cus * (mask ? 1 : 2);
     const int64_t need = (pairs + kPairWaves - 1) / kPairWaves;
@@ -583,6 +621,8 @@ hipError_t launch_pair_conv_win(int st, const void *u, const void *w, const void
             cus = v_;
     }
     const int64_t pairs = H * B * (NS / 1024);
+    if (pairs >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    if (pairs == 0) return hipSuccess;
     int64_t blocks = (int64_t)cus * 2;
     const int64_t need = (pairs + kPairWaves - 1) / kPairWaves;
     if (blocks > need) blocks = need < 8 ? 8 : (need + 7) / 8 * 8;

@@ -143,7 +143,8 @@ def test_prepared_filter_matches_oracle_spectrum(dtype, logn, L):
 
 
 # ---- N = 1024 in fp16 / bf16 storage runs on the matrix-core pair kernel
-@pytest.mark.parametrize("B,H", [(1, 1), (2, 1), (3, 5), (1, 7), (64, 3)])
+# (H >= 8: each XCD owns a channel range, ragged when 8 does not divide H)
+@pytest.mark.parametrize("B,H", [(1, 1), (2, 1), (3, 5), (1, 7), (64, 3), (2, 8), (1, 9), (5, 13), (7, 50)])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_pair_kernel_batches(B, H, dtype):
     _say(f"pair kernel B={B} H={H} {dtype}")
@@ -169,8 +170,8 @@ def test_pair_kernel_gates(gates):
 @pytest.mark.parametrize("kind", ["band", "random"])
 def test_pair_kernel_mask(kind):
     _say(f"pair kernel mask {kind}")
-    inp = synth.generate(3, 4, 1024, 1024, "f16", gated=True, seed=32)
-    mask = synth.band_mask(4, 27) if kind == "band" else synth.random_mask(4, seed=3)
+    inp = synth.generate(3, 12, 1024, 1024, "f16", gated=True, seed=32)
+    mask = synth.band_mask(12, 27) if kind == "band" else synth.random_mask(12, seed=3)
     y = run_gpu(inp, mask)
     ref = oracle_full(inp, mask)
     assert oracle.rel_l2(y, ref) < TOL["f16"]
