@@ -35,6 +35,28 @@ from long_fft_convolution_amd import synth  # noqa: E402
 
 METRIC = "FFT-conv fwd B·H·N elems/s + % HBM peak (rocprof), N=1K..4M, 1 GPU"
 HBM_PEAK_GBS = 8000.0
+
+
+# The GPU's clock ramps up over several milliseconds of sustained work: calls right after an
+# idle period run 10-20 % slower.  Warm-up therefore runs the requested W steps and, beyond
+# them, keeps stepping (untimed) until at least this much wall time has passed, so that the
+# K timed steps see the steady clock.
+MIN_WARMUP_S = 0.2
+
+
+def warm_up(step, warmup: int, dev) -> int:
+    """Run `warmup` steps, then more until MIN_WARMUP_S has passed; return the count run."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or time.perf_counter() - t0 < MIN_WARMUP_S:
+        step()
+        n += 1
+        if n >= warmup and n % 8 == 0:
+            torch.cuda.synchronize(dev)
+    torch.cuda.synchronize(dev)
+    return n
+
+
 ELEM = {"f32": 4, "f16": 2, "bf16": 2}
 KERNEL_SOURCES = ["fused.hip", "multipass.hip", "pair_mfma.hip", "pair16k.hip", "eqlinear.hip", "cmfma.hpp",
                   "fft_device.hpp",
@@ -178,9 +200,8 @@ def main():
             return 2
         return bench_bwd(args, wl, dev, u, K_f, w, v, mask)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize(dev)
+    n_warm = warm_up(step, args.warmup, dev)
+    log(f"bench: {n_warm} warm-up steps")
     stream = torch.cuda.current_stream(dev)
     # HIP events on the stream the library launches on (torch's current stream), around the
     # K back-to-back calls only: an event between calls would add its own gap to every call
@@ -254,9 +275,7 @@ def bench_eqlinear(args):
     W_f = torch.empty(fc.fftconv_eqlinear_weight_bytes(wl.T, wl.C_out, wl.C_in), dtype=torch.uint8, device=dev)
     fc.fftconv_eqlinear_prepare(W, W_f)
     y = torch.empty((wl.N, wl.T, wl.C_out), dtype=x.dtype, device=dev)
-    for _ in range(args.warmup):
-        fc.fftconv_eqlinear_fwd(x, W_f, y)
-    torch.cuda.synchronize(dev)
+    warm_up(lambda: fc.fftconv_eqlinear_fwd(x, W_f, y), args.warmup, dev)
     stream = torch.cuda.current_stream(dev)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -321,8 +340,7 @@ def bench_bwd(args, wl, dev, u, K_f, w, v, mask):
     def step():
         fc.fftconv_bwd(dy, u, K_f, w, v, du, dk, dw, dv, wl.L, mask, ws)
 
-    for _ in range(args.warmup):
-        step()
+    warm_up(step, args.warmup, dev)
     stream = torch.cuda.current_stream(dev)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
