@@ -66,7 +66,7 @@ KERNEL_SOURCES = ["fused.hip", "multipass.hip", "pair_mfma.hip", "pair16k.hip", 
 def path_of(w: synth.Workload):
     """(kernel name, compute dtype, arithmetic) of the path fftconv_fwd takes for w."""
     if w.short:
-        return "pair1k_kernel (windows of 1024)", "f16", "fp16 MFMA operands, fp32 accumulation"
+        return "pair1k_kernel (windows of 2048, hop 1024)", "f16", "fp16 MFMA operands, fp32 accumulation"
     if w.dtype in ("f16", "bf16") and w.N == 1024:
         return "pair1k_kernel", "f16", "fp16 MFMA operands, fp32 accumulation"
     if w.dtype in ("f16", "bf16") and w.N == 16384:

@@ -142,20 +142,21 @@ fftconv_status_t fftconv_bwd(const void *dy, const void *u, const void *K_f, con
                              void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---- Chunked short-filter path (overlap-save) --------------------------
- * For a filter of at most 512 taps (the FlashFFTConv summary page, table of
+ * For a filter of at most 1024 taps (the FlashFFTConv summary page, table of
  * measured effects: filters shortened to 2K keep model quality) the
  * convolution needs no transform of the whole sequence.  The sequence is
- * covered by windows of 1024 samples overlapping by half; each window runs
- * through the N = 1024 matrix-core kernel (FFT size 2048) and keeps the
- * second half of its outputs, which depend only on the window.  The result
- * is the same causal convolution as fftconv_fwd with this filter.  fp16 and
- * bf16 storage only; no frequency mask (the spectrum is that of a 1024-sample
- * window).  The backward pass is not provided for this path. */
+ * covered by windows of 2048 samples overlapping by half (zeros before the
+ * sequence start); each window's 2048-point circular convolution with the
+ * filter runs on the matrix cores and keeps the second half of its outputs,
+ * which no filter tap wraps around to.  The result is the same causal
+ * convolution as fftconv_fwd with this filter.  fp16 and bf16 storage only;
+ * no frequency mask (the spectrum is the 2048-point one of the filter).  The
+ * backward pass is not provided for this path. */
 
 /* Bytes of a short-filter spectrum for H channels (0 for fp32 or H < 1). */
 size_t fftconv_short_filter_bytes(int64_t H, fftconv_dtype_t dtype);
 
-/* k (H, L_filter) device array, 1 <= L_filter <= 512, fp16 or bf16 ->
+/* k (H, L_filter) device array, 1 <= L_filter <= 1024, fp16 or bf16 ->
  * K_s, K_s_bytes >= fftconv_short_filter_bytes(H, dtype).  Asynchronous. */
 fftconv_status_t fftconv_prepare_short_filter(const void *k, int64_t H, int64_t L_filter,
                                               fftconv_dtype_t dtype, void *K_s, size_t K_s_bytes,
@@ -164,7 +165,7 @@ fftconv_status_t fftconv_prepare_short_filter(const void *k, int64_t H, int64_t 
 /* out = v * causal_conv(u * w, k) with the prepared short filter K_s.
  *   u, w, v, out  (B, H, N) device arrays, N a positive multiple of 1024
  *                 (not necessarily a power of two); w, v may be NULL
- *   L_filter      the filter length K_s was prepared with (<= 512)
+ *   L_filter      the filter length K_s was prepared with (<= 1024)
  * Asynchronous on stream; no workspace; out must not overlap the inputs. */
 fftconv_status_t fftconv_fwd_short(const void *u, const void *K_s, const void *w, const void *v,
                                    void *out, int64_t B, int64_t H, int64_t N, int64_t L_filter,

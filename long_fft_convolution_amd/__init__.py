@@ -206,7 +206,7 @@ def fftconv_short_filter_bytes(H: int, dtype) -> int:
 
 
 def fftconv_prepare_short_filter(k: torch.Tensor, K_s: torch.Tensor, stream=None) -> None:
-    """K_s <- spectrum of the (H, L) filter k, L <= 512, for the chunked short-filter path."""
+    """K_s <- spectrum of the (H, L) filter k, L <= 1024, for the chunked short-filter path."""
     _dev_tensor(k, "k")
     _dev_tensor(K_s, "K_s")
     H, L = k.shape
@@ -227,7 +227,7 @@ def fftconv_fwd_short(u: torch.Tensor, K_s: torch.Tensor, w: torch.Tensor | None
 
 
 def causal_conv_short(u, k, w=None, v=None, stream=None):
-    """Prepare a short filter k (L <= 512) and run one chunked forward call."""
+    """Prepare a short filter k (L <= 1024) and run one chunked forward call."""
     H, L = k.shape
     K_s = torch.empty(fftconv_short_filter_bytes(H, u.dtype), dtype=torch.uint8, device=u.device)
     fftconv_prepare_short_filter(k, K_s, stream)

@@ -673,11 +673,14 @@ fftconv_status_t fftconv_bwd(const void *dy, const void *u, const void *K_f, con
 }
 
 // ---- chunked short-filter path ---------------------------------------------
-constexpr int64_t kShortWindow = 1024;   // window length; the filter spans at most half of it
+// The short path covers a sequence with windows of 2 kShortBlock samples at a hop of
+// kShortBlock (the transform of the N = kShortBlock kernels, 2048 points); a filter of at
+// most kShortBlock taps leaves the window's second half free of wrap-around.
+constexpr int64_t kShortBlock = 1024;
 
 size_t fftconv_short_filter_bytes(int64_t H, fftconv_dtype_t dtype) {
     if (dtype != FFTCONV_F16 && dtype != FFTCONV_BF16) return 0;
-    return fftconv_filter_bytes(H, kShortWindow, dtype);
+    return fftconv_filter_bytes(H, kShortBlock, dtype);
 }
 
 fftconv_status_t fftconv_prepare_short_filter(const void *k, int64_t H, int64_t L, fftconv_dtype_t dtype,
@@ -685,11 +688,11 @@ fftconv_status_t fftconv_prepare_short_filter(const void *k, int64_t H, int64_t 
     g_last_error.clear();
     if (dtype != FFTCONV_F16 && dtype != FFTCONV_BF16)
         return fail(FFTCONV_ERR_UNSUPPORTED, "the short-filter path needs fp16 or bf16 storage");
-    if (L < 1 || L > kShortWindow / 2)
+    if (L < 1 || L > kShortBlock)
         return fail(FFTCONV_ERR_INVALID_ARGUMENT, "L_filter=%lld must be in [1, %lld]", (long long)L,
-                    (long long)(kShortWindow / 2));
-    // the spectrum of the filter zero-padded to the window's transform size
-    return prepare_impl(k, H, L, kShortWindow, dtype, K_s, K_s_bytes, nullptr, 0, false, stream);
+                    (long long)(kShortBlock));
+    // the spectrum of the filter zero-padded to the window (2048 points)
+    return prepare_impl(k, H, L, kShortBlock, dtype, K_s, K_s_bytes, nullptr, 0, false, stream);
 }
 
 fftconv_status_t fftconv_fwd_short(const void *u, const void *K_s, const void *w, const void *v, void *out,
@@ -698,13 +701,13 @@ fftconv_status_t fftconv_fwd_short(const void *u, const void *K_s, const void *w
     g_last_error.clear();
     if (dtype != FFTCONV_F16 && dtype != FFTCONV_BF16)
         return fail(FFTCONV_ERR_UNSUPPORTED, "the short-filter path needs fp16 or bf16 storage");
-    if (N < kShortWindow || N % kShortWindow != 0)
+    if (N < kShortBlock || N % kShortBlock != 0)
         return fail(FFTCONV_ERR_UNSUPPORTED, "N=%lld must be a positive multiple of %lld", (long long)N,
-                    (long long)kShortWindow);
+                    (long long)kShortBlock);
     if (B < 0 || H < 0) return fail(FFTCONV_ERR_INVALID_ARGUMENT, "B and H must be >= 0");
-    if (L < 1 || L > kShortWindow / 2)
+    if (L < 1 || L > kShortBlock)
         return fail(FFTCONV_ERR_INVALID_ARGUMENT, "L_filter=%lld must be in [1, %lld]", (long long)L,
-                    (long long)(kShortWindow / 2));
+                    (long long)(kShortBlock));
     if (B * H == 0) return ok();
     if (!u || !K_s || !out) return fail(FFTCONV_ERR_INVALID_ARGUMENT, "u, K_s and out must be non-null");
     if (!aligned16(u) || !aligned16(K_s) || !aligned16(out) || (w && !aligned16(w)) || (v && !aligned16(v)))

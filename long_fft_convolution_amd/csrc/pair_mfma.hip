@@ -144,6 +144,10 @@ constexpr int kPlane = 32 * 32;     // fp16 elements per LDS plane (rows n_f, K 
 struct PairRaw {
     uint4 q[2][4];
 };
+// windowed pair: [block A, B, C] x [r = 0, 1] x [u, w]
+struct WinRaw {
+    uint4 q[3][2][2];
+};
 
 // (without a second row ob == oa: the loads re-read the first row and the caller zeroes
 // the result, so that no load sits under a branch)
@@ -178,6 +182,16 @@ __device__ __forceinline__ void unpack8<__hip_bfloat16>(const uint4 &q, float *o
         o[2 * i] = __uint_as_float(w[i] << 16);
         o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
+}
+
+// xor of each 32-bit word of eight fp16 values with m (a sign pattern)
+__device__ __forceinline__ h8 xor8(const h8 &a, uint32_t m) {
+    uint4 q = *reinterpret_cast<const uint4 *>(&a);
+    q.x ^= m;
+    q.y ^= m;
+    q.z ^= m;
+    q.w ^= m;
+    return *reinterpret_cast<const h8 *>(&q);
 }
 
 // sign flip of eight fp16 values: one integer xor per register
@@ -234,13 +248,20 @@ __device__ __forceinline__ void gate_product<__hip_bfloat16>(const uint4 &uq, co
     for (int e = 0; e < 8; ++e) x[e] = (_Float16)a[e];
 }
 
-// WIN: the chunked short-filter path (overlap-save).  The (B, H, NS) sequences,
-// NS a multiple of 1024, are covered by windows of 1024 samples that overlap by
-// half: window j starts at (j - 1) 512 (zeros before the sequence start) and
-// keeps its outputs 512 .. 1023, the outputs j 512 .. j 512 + 511 of the
-// sequence; with a filter of at most 512 taps those depend only on the
-// window.  A pair is windows (2 jp, 2 jp + 1) of one sequence, so three
-// 512-sample blocks feed it and only the second halves are stored.
+// WIN: the chunked short-filter path (overlap-save with the transform's own
+// length as the window).  The (B, H, NS) sequences, NS a multiple of 1024, are
+// covered by windows of 2048 samples that overlap by half: window j holds the
+// samples (j - 1) 1024 .. (j + 1) 1024 - 1 (zeros before the sequence start).
+// Its 2048-point circular convolution with a filter of at most 1024 taps equals
+// the linear one at the window's outputs 1024 .. 2047 (no tap reaches around
+// the window), which are the outputs j 1024 .. j 1024 + 1023 of the sequence.
+// The filter spectrum is the same 2048-point one as for N = 1024.  A pair is
+// windows (2 jp, 2 jp + 1) of one sequence: three 1024-sample blocks A, B, C
+// feed it (window a = A B, window b = B C; an odd last window has no b).
+//   Relative to the N = 1024 path, S1 contracts all 64 values of n_s (the
+// input fills the window: two K blocks, the second with DFT entries
+// w64^{(n_s + 32) f_s} = (-1)^{f_s} w64^{n_s f_s}) and S1' produces n_s = 32 .. 63
+// (entries conj w64^{f_s (n_s + 32)} = (-1)^{f_s} conj w64^{f_s n_s}).
 template <typename T, bool MASKED, bool HAS_W, bool HAS_V, bool WIN = false>
 __global__ void __launch_bounds__(64 * kPairWaves, MASKED ? 1 : 2)
 pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restrict__ v,
@@ -253,6 +274,8 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
     // per wave: the transposed input planes (2 x kPlane fp16), later the fp32 output rows
     // of both sequences (2 x 1024 floats)
     __shared__ __align__(16) float s_z[kPairWaves][2 * 1024];
+    // input planes: rows n_f, K slots (two blocks of 32 in a window)
+    constexpr int kRow = WIN ? 64 : 32, kPl = 32 * kRow;
     __shared__ h8 s_f1[2][4][64];     // S1 DFT blocks (re, im) per column tile nt
     __shared__ h8 s_f3[2][4][64];     // S1' DFT blocks (re, im) per (ks, nt3)
 
@@ -264,8 +287,15 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
     for (int i = tid; i < 256; i += 64 * kPairWaves) {
         s_f1[0][i / 64][i % 64] = reinterpret_cast<const h8 *>(tb.f1r)[i];
         s_f1[1][i / 64][i % 64] = reinterpret_cast<const h8 *>(tb.f1i)[i];
-        s_f3[0][i / 64][i % 64] = reinterpret_cast<const h8 *>(tb.f3r)[i];
-        s_f3[1][i / 64][i % 64] = reinterpret_cast<const h8 *>(tb.f3i)[i];
+        // windows: S1' produces n_s + 32, i.e. the entries of the odd K slots (odd f_s:
+        // element j odd, the upper half of each 32-bit word) change sign
+        uint4 a = reinterpret_cast<const uint4 *>(tb.f3r)[i], b = reinterpret_cast<const uint4 *>(tb.f3i)[i];
+        if (WIN) {
+            a = make_uint4(a.x ^ 0x80000000u, a.y ^ 0x80000000u, a.z ^ 0x80000000u, a.w ^ 0x80000000u);
+            b = make_uint4(b.x ^ 0x80000000u, b.y ^ 0x80000000u, b.z ^ 0x80000000u, b.w ^ 0x80000000u);
+        }
+        s_f3[0][i / 64][i % 64] = *reinterpret_cast<const h8 *>(&a);
+        s_f3[1][i / 64][i % 64] = *reinterpret_cast<const h8 *>(&b);
     }
     __syncthreads();
 
@@ -286,7 +316,8 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
     // contiguous rows of neighbouring channels while the XCD's filter spectra stay in its
     // L2 (with the batch fastest, neighbouring waves read rows 2 H N elements apart and
     // the HBM pages are poorly used); with H < 8 the XCDs split p = bp H + h.
-    const int64_t PB = WIN ? B * (NS / 1024) : (B + 1) / 2;   // pairs per channel
+    const int64_t NW = NS / 1024, JP = (NW + 1) / 2;            // windows, window pairs per sequence
+    const int64_t PB = WIN ? B * JP : (B + 1) / 2;               // pairs per channel
     const int64_t P = H * PB;
     const uint32_t nwg = gridDim.x, xcd = blockIdx.x % 8, wg_local = blockIdx.x / 8;
     const uint32_t wg_on_xcd = nwg / 8 + (xcd < nwg % 8 ? 1u : 0u);
@@ -301,12 +332,14 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
         p_end = P * (xcd + 1) / 8;
     }
     const int64_t stride = (int64_t)wg_on_xcd * kPairWaves;
-    _Float16 *zr = reinterpret_cast<_Float16 *>(s_z[wave]), *zi = zr + kPlane;
+    _Float16 *zr = reinterpret_cast<_Float16 *>(s_z[wave]), *zi = zr + kPl;
     char *const so = reinterpret_cast<char *>(s_z[wave]);
     const f4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
-    // (the host keeps the pair count below 2^31: 32-bit divisions)
-    auto offsets = [&](int64_t p, int64_t &h, int64_t &oa, int64_t &ob, bool &has_b) {
+    // (the host keeps the pair count below 2^31: 32-bit divisions).  oa, ob: where the
+    // outputs (and output gates) of sequence / window a and b start; without b, ob == oa.
+    // first: a window pair at the sequence start (its block A lies before it)
+    auto offsets = [&](int64_t p, int64_t &h, int64_t &oa, int64_t &ob, bool &has_b, bool &first) {
         int64_t bp;
         if (WIN) {
             const uint32_t h32 = (uint32_t)p / (uint32_t)PB;
@@ -318,14 +351,17 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
             h = h0 + ((uint32_t)p - b32 * (uint32_t)Hx);
         }
         if (WIN) {
-            // window pair jp of batch row b: windows start at (2 jp - 1) 512 and 2 jp 512
-            const uint32_t jpb = (uint32_t)(NS / 1024), b32 = (uint32_t)bp / jpb;
-            const int64_t b = b32, jp = (uint32_t)bp - b32 * jpb;
-            has_b = true;
-            oa = (b * H + h) * NS + (2 * jp - 1) * 512;
-            ob = oa + 512;
+            // window pair jp of batch row b: windows 2 jp and 2 jp + 1, outputs at 2 jp 1024
+            // and (2 jp + 1) 1024
+            const uint32_t b32 = (uint32_t)bp / (uint32_t)JP;
+            const int64_t b = b32, jp = (uint32_t)bp - b32 * (uint32_t)JP;
+            has_b = 2 * jp + 1 < NW;
+            first = jp == 0;
+            oa = (b * H + h) * NS + 2 * jp * 1024;
+            ob = has_b ? oa + 1024 : oa;
         } else {
             has_b = 2 * bp + 1 < B;
+            first = false;
             oa = (2 * bp * H + h) * N;
             ob = has_b ? oa + H * N : oa;
         }
@@ -339,8 +375,8 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
     };
     auto load_filt = [&](int64_t pp, Filt &fk) {
         int64_t h, oa, ob;
-        bool hb;
-        offsets(pp, h, oa, ob, hb);
+        bool hb, fst;
+        offsets(pp, h, oa, ob, hb, fst);
         const uint4 *krow = kbins + h * 512;
 #pragma unroll
         for (int mt2 = 0; mt2 < 2; ++mt2)
@@ -351,32 +387,34 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
     auto load_gate = [&](int64_t oa, int64_t ob, uint4 (&vg)[4]) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            if (!WIN || (q & 1))   // windows store their second halves only
-                vg[q] = *reinterpret_cast<const uint4 *>(v + (q < 2 ? oa : ob) + 512 * (q & 1) + 8 * lane);
+            vg[q] = *reinterpret_cast<const uint4 *>(v + (q < 2 ? oa : ob) + 512 * (q & 1) + 8 * lane);
     };
-    auto load_in = [&](int64_t pp, PairRaw &raw) {
+    using Raw = std::conditional_t<WIN, WinRaw, PairRaw>;
+    auto load_in = [&](int64_t pp, Raw &raw) {
         int64_t h, oa, ob;
-        bool hb;
-        offsets(pp, h, oa, ob, hb);
-        if (WIN) {
-            // blocks b0 = [oa, oa + 512) (before the sequence for the first window: the
-            // load re-reads b1 and is zeroed), b1 = [oa + 512, ...), b2 = [oa + 1024, ...);
-            // window a = (b0, b1), window b = (b1, b2)
-            const int64_t base = oa + 512 - (oa + 512) % NS;
-            const bool first = oa < base;
-            const int64_t o0 = first ? oa + 512 : oa;
+        bool hb, fst;
+        offsets(pp, h, oa, ob, hb, fst);
+        if constexpr (WIN) {
+            // blocks A = [oa - 1024, oa) (before the sequence start for the first pair: the
+            // load re-reads B and is zeroed), B = [oa, oa + 1024), C = [oa + 1024, oa + 2048):
+            // without window b, C re-reads B (its results are not stored)
+            const int64_t oA = fst ? oa : oa - 1024, oC = hb ? oa + 1024 : oa;
             const int m = 8 * lane;
-            raw.q[0][0] = *reinterpret_cast<const uint4 *>(u + o0 + m);
-            raw.q[1][0] = *reinterpret_cast<const uint4 *>(u + oa + 512 + m);
-            raw.q[1][2] = *reinterpret_cast<const uint4 *>(u + oa + 1024 + m);
-            if (HAS_W) {
-                raw.q[0][1] = *reinterpret_cast<const uint4 *>(w + o0 + m);
-                raw.q[1][1] = *reinterpret_cast<const uint4 *>(w + oa + 512 + m);
-                raw.q[1][3] = *reinterpret_cast<const uint4 *>(w + oa + 1024 + m);
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                raw.q[0][r][0] = *reinterpret_cast<const uint4 *>(u + oA + 512 * r + m);
+                raw.q[1][r][0] = *reinterpret_cast<const uint4 *>(u + oa + 512 * r + m);
+                raw.q[2][r][0] = *reinterpret_cast<const uint4 *>(u + oC + 512 * r + m);
+                if (HAS_W) {
+                    raw.q[0][r][1] = *reinterpret_cast<const uint4 *>(w + oA + 512 * r + m);
+                    raw.q[1][r][1] = *reinterpret_cast<const uint4 *>(w + oa + 512 * r + m);
+                    raw.q[2][r][1] = *reinterpret_cast<const uint4 *>(w + oC + 512 * r + m);
+                }
             }
-            if (first) raw.q[0][0] = make_uint4(0u, 0u, 0u, 0u);
-            raw.q[0][2] = raw.q[1][0];
-            raw.q[0][3] = raw.q[1][1];
+            if (fst) {
+                raw.q[0][0][0] = make_uint4(0u, 0u, 0u, 0u);
+                raw.q[0][1][0] = make_uint4(0u, 0u, 0u, 0u);
+            }
         } else {
             load_pair_raw<T, HAS_W>(raw, u, w, oa, ob, lane);
         }
@@ -392,7 +430,7 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
     // assume that they may be absent, and each later wait for an older load then waits for
     // the prefetch as well.
     int64_t p = p_begin + (int64_t)wg_local * kPairWaves + wave;
-    PairRaw cur;
+    Raw cur;
     Filt fc;
     // (the same load order as in the loop, so that the waits at the loop head hold for both
     // ways into it)
@@ -403,43 +441,73 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
     for (; p < p_end; p += stride) {
         int64_t h, oa, ob;
         bool has_b;
-        offsets(p, h, oa, ob, has_b);
+        bool first;
+        offsets(p, h, oa, ob, has_b, first);
         const int64_t pn = p + stride < p_end ? p + stride : p;
         uint4 vg[4];
         if (HAS_V) load_gate(oa, ob, vg);
         const float ks = fc.ks;
 
-        // ---- x = u * w of both sequences, scattered into the transposed LDS planes
+        // ---- x = u * w of both sequences (windows), scattered into the transposed LDS
+        // planes: element m = n_f + 32 n_s at row n_f, K block n_s / 32, slot kslot(n_s % 32)
+        if constexpr (WIN) {
+            h8 xb3[3][2];   // blocks A, B, C
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int m0 = 8 * lane + 512 * r;
-            h8 xa, xb;
-            gate_product<T>(cur.q[r][0], cur.q[r][1], HAS_W, xa);
-            gate_product<T>(cur.q[r][2], cur.q[r][3], HAS_W, xb);
-            if (!has_b) xb = h8{};
-            const int ns = m0 >> 5, nf0 = m0 & 31, kss = kslot_of(ns);
+            for (int k = 0; k < 3; ++k)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                zr[(nf0 + e) * 32 + kss] = xa[e];
-                zi[(nf0 + e) * 32 + kss] = xb[e];
+                for (int r = 0; r < 2; ++r) gate_product<T>(cur.q[k][r][0], cur.q[k][r][1], HAS_W, xb3[k][r]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {   // window a = (A, B), window b = (B, C)
+                const int m0 = 8 * lane + 512 * r;
+                const h8 xa = xb3[r >> 1][r & 1], xb = xb3[1 + (r >> 1)][r & 1];
+                const int ns = m0 >> 5, nf0 = m0 & 31, kss = 32 * (ns >> 5) + kslot_of(ns & 31);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    zr[(nf0 + e) * kRow + kss] = xa[e];
+                    zi[(nf0 + e) * kRow + kss] = xb[e];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int m0 = 8 * lane + 512 * r;
+                h8 xa, xb;
+                gate_product<T>(cur.q[r][0], cur.q[r][1], HAS_W, xa);
+                gate_product<T>(cur.q[r][2], cur.q[r][3], HAS_W, xb);
+                if (!has_b) xb = h8{};
+                const int ns = m0 >> 5, nf0 = m0 & 31, kss = kslot_of(ns);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    zr[(nf0 + e) * kRow + kss] = xa[e];
+                    zi[(nf0 + e) * kRow + kss] = xb[e];
+                }
             }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        h8 dr[2], di[2];
+        constexpr int KB = WIN ? 2 : 1;   // K blocks of S1
+        h8 dr[KB][2], di[KB][2];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            dr[mt] = *reinterpret_cast<const h8 *>(zr + (16 * mt + c) * 32 + 8 * g);
-            di[mt] = *reinterpret_cast<const h8 *>(zi + (16 * mt + c) * 32 + 8 * g);
-        }
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                dr[kb][mt] = *reinterpret_cast<const h8 *>(zr + (16 * mt + c) * kRow + 32 * kb + 8 * g);
+                di[kb][mt] = *reinterpret_cast<const h8 *>(zi + (16 * mt + c) * kRow + 32 * kb + 8 * g);
+            }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         __builtin_amdgcn_sched_barrier(0);   // (keep the prefetch loads where they are)
         load_in(pn, cur);
         __builtin_amdgcn_sched_barrier(0);
-        const h8 ndi0 = neg8(di[0]), ndi1 = neg8(di[1]);
+        h8 ndi[KB][2];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) ndi[kb][mt] = neg8(di[kb][mt]);
+        // second K block (windows): column f_s = 16 nt + c of the DFT changes sign for odd c
+        const uint32_t sgn1 = (c & 1) ? 0x80008000u : 0u;
         const uint8_t *mrow = MASKED ? mask + h * kMaskBlocks : nullptr;
 
         // S1' operands, fp16: a[ks][nt2] (re, im); rows f_s of tiles nt = 2ks (j < 4), 2ks+1 (j >= 4)
@@ -449,13 +517,23 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
         for (int nt = 0; nt < 4; ++nt) {
             // ---- S1: rows n_f (tiles mt), column tile nt of f_s; twiddle w2048^{nf fs} (fp16)
             h4 t1r[2], t1i[2];
-            const h8 f1r = s_f1[0][nt][lane], f1i = s_f1[1][nt][lane];
+            h8 f1r[KB], f1i[KB];
+            f1r[0] = s_f1[0][nt][lane];
+            f1i[0] = s_f1[1][nt][lane];
+            if constexpr (WIN) {
+                f1r[1] = xor8(f1r[0], sgn1);
+                f1i[1] = xor8(f1i[0], sgn1);
+            }
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
-                f4 ar = mfma(dr[mt], f1r, zero4);
-                ar = mfma(mt == 0 ? ndi0 : ndi1, f1i, ar);
-                f4 ai = mfma(dr[mt], f1i, zero4);
-                ai = mfma(di[mt], f1r, ai);
+                f4 ar = zero4, ai = zero4;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    ar = mfma(dr[kb][mt], f1r[kb], ar);
+                    ar = mfma(ndi[kb][mt], f1i[kb], ar);
+                    ai = mfma(dr[kb][mt], f1i[kb], ai);
+                    ai = mfma(di[kb][mt], f1r[kb], ai);
+                }
                 t1r[mt] = to_h4(ar);
                 t1i[mt] = to_h4(ai);
                 cmul4(t1r[mt], t1i[mt], s_tw1[(mt * 4 + nt) * 64 + lane]);
@@ -509,7 +587,8 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
         load_filt(pn, fc);
         __builtin_amdgcn_sched_barrier(0);
 
-        // ---- S1': rows n_f (tiles nt2), columns n_s (tiles nt3, n_s < 32 only), K = f_s
+        // ---- S1': rows n_f (tiles nt2), columns n_s (tiles nt3; n_s < 32 only, or n_s - 32 for
+        // windows: the outputs m - 1024), K = f_s
 #pragma unroll
         for (int nt2 = 0; nt2 < 2; ++nt2) {
             const h8 na0i = neg8(a3i[0][nt2]), na1i = neg8(a3i[1][nt2]);
@@ -536,10 +615,9 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
             }
         }
         // ---- output gate and store: rows of 8 contiguous elements per lane, 16-byte accesses;
-        // without a second row its stores repeat the first row's values
+        // without a second row (window) its stores repeat the first one's values
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            if (WIN && !(q & 1)) continue;   // windows store their second halves only
             const int qq = (q >= 2 && !has_b) ? q - 2 : q;
             const int u0 = 128 * (qq & 1) + 2 * lane;
             const int s0 = u0 ^ (((u0 >> 4) & 1) << 2), s1 = (u0 + 1) ^ ((((u0 + 1) >> 4) & 1) << 2);
@@ -620,7 +698,7 @@ hipError_t launch_pair_conv_win(int st, const void *u, const void *w, const void
         if (hipDeviceGetAttribute(&v_, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v_ > 0)
             cus = v_;
     }
-    const int64_t pairs = H * B * (NS / 1024);
+    const int64_t pairs = H * B * ((NS / 1024 + 1) / 2);
     if (pairs >= (int64_t(1) << 31)) return hipErrorInvalidValue;
     if (pairs == 0) return hipSuccess;
     int64_t blocks = (int64_t)cus * 2;

@@ -170,7 +170,7 @@ def test_bwd_validation():
 def test_short_filter_abi():
     lib = fc.lib()
     F16, F32 = fc.FFTCONV_F16, fc.FFTCONV_F32
-    # the spectrum of a 1024-sample window: header, scales, 2048 bins of 4 bytes per channel
+    # the 2048-point spectrum of the window: header, scales, 2048 bins of 4 bytes per channel
     assert fc.fftconv_short_filter_bytes(3, F16) == fc.fftconv_filter_bytes(3, 1024, F16)
     assert fc.fftconv_short_filter_bytes(3, F32) == 0
 
@@ -180,7 +180,7 @@ def test_short_filter_abi():
         return lib.fftconv_prepare_short_filter(a["k"], a["H"], a["L"], a["dt"], a["K"], a["kb"], None)
 
     assert prep(dt=F32) == 2
-    assert prep(L=513) == 1 and "L_filter" in fc.fftconv_last_error()
+    assert prep(L=1025) == 1 and "L_filter" in fc.fftconv_last_error()
     assert prep(L=0) == 1
     assert prep(kb=16) == 1
 
@@ -193,7 +193,7 @@ def test_short_filter_abi():
     assert fwd(dt=F32) == 2
     assert fwd(N=1000) == 2 and "multiple of 1024" in fc.fftconv_last_error()
     assert fwd(N=512) == 2
-    assert fwd(L=600) == 1
+    assert fwd(L=1025) == 1
     assert fwd(B=-1) == 1
     assert fwd(u=None) == 1
     assert fwd(out=0x30008) == 1 and "aligned" in fc.fftconv_last_error()

@@ -1,11 +1,14 @@
 """GPU parity of the chunked short-filter path (fftconv_prepare_short_filter +
-fftconv_fwd_short, overlap-save windows of 1024 through the N = 1024 matrix-core
-kernel) against the CPU oracle's exact causal convolution with the same filter.
+fftconv_fwd_short: overlap-save windows of 2048 samples at a hop of 1024, each a
+2048-point circular convolution on the matrix cores) against the CPU oracle's
+exact causal convolution with the same filter.
 
-The windows' outputs depend only on the window when the filter has at most 512
-taps, so the result is the full causal convolution; the cases cover the first
-window (zeros before the sequence), sequence lengths that are multiples of 1024
-but not powers of two, both gates, several channels and batch rows.
+The second half of a window's circular convolution is free of wrap-around when
+the filter has at most 1024 taps, so the result is the full causal convolution;
+the cases cover the first window (zeros before the sequence), the longest filter,
+an odd number of windows (the last window pair has one window), sequence lengths
+that are multiples of 1024 but not powers of two, both gates, several channels
+and batch rows.
 """
 import sys
 
@@ -48,8 +51,8 @@ def _ref(inp):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("N,L", [(1024, 512), (2048, 1), (3072, 100), (8192, 511), (8192, 512),
-                                 (5 * 1024, 257)])
+@pytest.mark.parametrize("N,L", [(1024, 512), (1024, 1024), (2048, 1), (3072, 100), (3072, 1024),
+                                 (8192, 511), (8192, 1023), (5 * 1024, 257), (7 * 1024, 1000)])
 def test_short_filter_sizes(dtype, N, L):
     _say(f"short {dtype} N={N} L={L}")
     inp = synth.generate(3, 2, N, L, dtype, gated=True, seed=N + L)
@@ -65,13 +68,13 @@ def test_short_filter_gates_and_batch(gated):
     ref = _ref(inp)
     assert oracle.rel_l2(y, ref) < TOL["f16"]
     # every window boundary is exact: the error is flat along the sequence
-    err = np.abs(y - ref).reshape(5, 3, N // 512, 512).max(axis=(0, 1, 3))
+    err = np.abs(y - ref).reshape(5, 3, N // 1024, 1024).max(axis=(0, 1, 3))
     scale = np.abs(ref).max()
     assert err.max() < 2e-2 * scale
 
 
 def test_short_filter_long_sequence():
-    N, L = 1 << 20, 512
+    N, L = 1 << 20, 1024
     _say(f"short N={N} L={L} H=2")
     inp = synth.generate(1, 2, N, L, "f16", gated=False, seed=21)
     assert oracle.rel_l2(_run(inp), _ref(inp)) < TOL["f16"]
