@@ -639,6 +639,298 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
     }
 }
 
+// ---- dk of the backward pass at N = 1024 -------------------------------------
+// dk[h, s] = sum_b corr(g, x)[b, h, s], s < L, with g = v dy and x = u w (the gradient
+// of sum(dy out) with respect to the filter).  With the rows of a batch pair packed as
+// z_g = g_a + i g_b and z_x = x_a + i x_b (the forward kernel's packing), the spectra
+// of the single rows follow from Z(f) and conj Z(M - f), and
+//   G_a conj X_a + G_b conj X_b = (P(f) + conj P(M - f)) / 2,  P = Z_g conj Z_x,
+// so with S = sum over the channel's pairs of P, DK = (S(f) + conj S(M - f)) / 2 and
+// dk = IFFT(DK) = Re IFFT(S) (1/M included).  Per channel: the two forward chains
+// (S1, twiddle, S2) of every pair on the matrix cores, P accumulated in fp32 registers,
+// a sum over the waves in LDS, and one inverse chain (S2', twiddle, S1', real part).
+// An odd last row pairs with zeros, which adds G_a conj X_a exactly (a real row's
+// spectrum is Hermitian).  One 8-wave workgroup per CU walks channels
+// h = blockIdx.x + k gridDim.x; within a channel wave w takes pairs w, w + 8, ...
+constexpr int kDkWaves = 8;
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ __half from_f32<__half>(float x) { return __float2half_rn(x); }
+template <> __device__ __forceinline__ __hip_bfloat16 from_f32<__hip_bfloat16>(float x) {
+    return __float2bfloat16(x);
+}
+
+template <typename T, bool HAS_W, bool HAS_V>
+__global__ void __launch_bounds__(64 * kDkWaves, 1)
+pair1k_dk_kernel(const T *__restrict__ dy, const T *__restrict__ u, const T *__restrict__ w,
+                 const T *__restrict__ v, T *__restrict__ dk, PairTables tb, int64_t B, int64_t H,
+                 int64_t L) {
+    constexpr int N = 1024, M = 2048, W = kDkWaves;
+    __shared__ h8 s_tw1[2 * 4 * 64];
+    __shared__ h8 s_tw3[4 * 2 * 64];
+    __shared__ h8 s_f1[3][4][64];   // re, im, -im: S1 takes no negated data operand
+    __shared__ h8 s_f3[2][4][64];
+    // per wave: the input planes of g and x (4 x kPlane fp16), later wave 0's output row
+    __shared__ __align__(16) _Float16 s_z[W][4 * kPlane];
+    // the channel's sum S in the S2 accumulator layout: [nt][mt2][re / im][lane][4]
+    __shared__ __align__(16) float s_S[4 * 2 * 2 * 64 * 4];
+
+    const int tid = threadIdx.x;
+    for (int i = tid; i < 512; i += 64 * W) {
+        s_tw1[i] = reinterpret_cast<const h8 *>(tb.tw1)[i];
+        s_tw3[i] = reinterpret_cast<const h8 *>(tb.tw3)[i];
+    }
+    for (int i = tid; i < 256; i += 64 * W) {
+        s_f1[0][i / 64][i % 64] = reinterpret_cast<const h8 *>(tb.f1r)[i];
+        s_f1[1][i / 64][i % 64] = reinterpret_cast<const h8 *>(tb.f1i)[i];
+        s_f1[2][i / 64][i % 64] = neg8(reinterpret_cast<const h8 *>(tb.f1i)[i]);
+        s_f3[0][i / 64][i % 64] = reinterpret_cast<const h8 *>(tb.f3r)[i];
+        s_f3[1][i / 64][i % 64] = reinterpret_cast<const h8 *>(tb.f3i)[i];
+    }
+    for (int i = tid; i < 4 * 2 * 2 * 64 * 4; i += 64 * W) s_S[i] = 0.f;
+    __syncthreads();
+
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, c = lane & 15;
+    const h8 *F2r = reinterpret_cast<const h8 *>(tb.f2r), *F2i = reinterpret_cast<const h8 *>(tb.f2i);
+    h8 c2r[2], c2i[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        c2r[t] = F2r[t * 64 + lane];
+        c2i[t] = F2i[t * 64 + lane];
+    }
+    _Float16 *const zgr = s_z[wave], *const zgi = zgr + kPlane, *const zxr = zgi + kPlane, *const zxi = zxr + kPlane;
+    const f4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+    // work items of this wave: channel slot ci, pair slot j -> h = blockIdx.x + ci gridDim.x,
+    // bp = wave + W j; slots past the channel's pairs (bp >= PB) add nothing
+    const int64_t PB = (B + 1) / 2, PPW = (PB + W - 1) / W;
+    const int64_t NCH = ((int64_t)H - blockIdx.x + gridDim.x - 1) / gridDim.x;   // channels of this workgroup
+    const int64_t NI = NCH * PPW;
+    // raw 16-byte chunks of one pair: [r][dy_a, v_a, dy_b, v_b, u_a, w_a, u_b, w_b]
+    struct Raw {
+        uint4 q[2][8];
+    };
+    auto locate = [&](int64_t i, int64_t &h, int64_t &bp, int64_t &oa, int64_t &ob, bool &has_b, bool &real) {
+        const int64_t ci = i / PPW, j = i - ci * PPW;
+        h = blockIdx.x + ci * (int64_t)gridDim.x;
+        bp = wave + W * j;
+        real = bp < PB;
+        const int64_t bq = real ? bp : PB - 1;   // (a slot without a pair reads the last pair)
+        has_b = 2 * bq + 1 < B;
+        oa = (2 * bq * H + h) * N;
+        ob = has_b ? oa + H * N : oa;
+    };
+    auto load_raw = [&](int64_t i, Raw &raw) {
+        int64_t h, bp, oa, ob;
+        bool hb, real;
+        locate(i < NI ? i : NI - 1, h, bp, oa, ob, hb, real);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int m0 = 8 * lane + 512 * r;
+            raw.q[r][0] = *reinterpret_cast<const uint4 *>(dy + oa + m0);
+            raw.q[r][2] = *reinterpret_cast<const uint4 *>(dy + ob + m0);
+            raw.q[r][4] = *reinterpret_cast<const uint4 *>(u + oa + m0);
+            raw.q[r][6] = *reinterpret_cast<const uint4 *>(u + ob + m0);
+            if (HAS_V) {
+                raw.q[r][1] = *reinterpret_cast<const uint4 *>(v + oa + m0);
+                raw.q[r][3] = *reinterpret_cast<const uint4 *>(v + ob + m0);
+            }
+            if (HAS_W) {
+                raw.q[r][5] = *reinterpret_cast<const uint4 *>(w + oa + m0);
+                raw.q[r][7] = *reinterpret_cast<const uint4 *>(w + ob + m0);
+            }
+        }
+    };
+    auto wave_sync = [&]() {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
+    Raw cur;
+    load_raw(0, cur);   // (pinned before the loop in the loop's order, as in the forward kernel)
+    __builtin_amdgcn_sched_barrier(0);
+    int64_t i = 0;
+    for (int64_t ci = 0; ci < NCH; ++ci) {
+      f4 Sr[4][2], Si[4][2];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int mt2 = 0; mt2 < 2; ++mt2) Sr[nt][mt2] = Si[nt][mt2] = zero4;
+      int64_t h = 0;
+      for (int64_t j = 0; j < PPW; ++j, ++i) {
+        int64_t bp, oa, ob;
+        bool has_b, real;
+        locate(i, h, bp, oa, ob, has_b, real);
+        if (real) {
+            // ---- g = v dy and x = u w of both rows, scattered into the transposed planes
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int m0 = 8 * lane + 512 * r;
+                h8 ga, gb, xa, xb;
+                gate_product<T>(cur.q[r][0], cur.q[r][1], HAS_V, ga);
+                gate_product<T>(cur.q[r][2], cur.q[r][3], HAS_V, gb);
+                gate_product<T>(cur.q[r][4], cur.q[r][5], HAS_W, xa);
+                gate_product<T>(cur.q[r][6], cur.q[r][7], HAS_W, xb);
+                if (!has_b) {
+                    gb = h8{};
+                    xb = h8{};
+                }
+                const int ns = m0 >> 5, nf0 = m0 & 31, kss = kslot_of(ns);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    zgr[(nf0 + e) * 32 + kss] = ga[e];
+                    zgi[(nf0 + e) * 32 + kss] = gb[e];
+                    zxr[(nf0 + e) * 32 + kss] = xa[e];
+                    zxi[(nf0 + e) * 32 + kss] = xb[e];
+                }
+            }
+        }
+        wave_sync();
+        h8 dgr[2], dgi[2], dxr[2], dxi[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const int o = (16 * mt + c) * 32 + 8 * g;
+            dgr[mt] = *reinterpret_cast<const h8 *>(zgr + o);
+            dgi[mt] = *reinterpret_cast<const h8 *>(zgi + o);
+            dxr[mt] = *reinterpret_cast<const h8 *>(zxr + o);
+            dxi[mt] = *reinterpret_cast<const h8 *>(zxi + o);
+        }
+        wave_sync();
+        __builtin_amdgcn_sched_barrier(0);
+        load_raw(i + 1, cur);   // the next item (clamped: issued on every path)
+        __builtin_amdgcn_sched_barrier(0);
+        if (real) {
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                __builtin_amdgcn_sched_barrier(0);   // (one column tile at a time: bounds the live operands)
+                const h8 f1r = s_f1[0][nt][lane], f1i = s_f1[1][nt][lane], nf1i = s_f1[2][nt][lane];
+                f4 zr_[2][2], zi_[2][2];   // [g / x][mt2]: the S2 accumulators of both chains
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const h8 *dr = q ? dxr : dgr, *di = q ? dxi : dgi;
+                    // S1 with twiddle w2048^{nf fs}, then S2 (as in the forward kernel)
+                    h4 t1r[2], t1i[2];
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt) {
+                        f4 ar = mfma(dr[mt], f1r, zero4);
+                        ar = mfma(di[mt], nf1i, ar);
+                        f4 ai = mfma(dr[mt], f1i, zero4);
+                        ai = mfma(di[mt], f1r, ai);
+                        t1r[mt] = to_h4(ar);
+                        t1i[mt] = to_h4(ai);
+                        cmul4(t1r[mt], t1i[mt], s_tw1[(mt * 4 + nt) * 64 + lane]);
+                    }
+                    const h8 br = cat8(t1r[0], t1r[1]), bi = cat8(t1i[0], t1i[1]);
+                    const h8 nbi = neg8(bi);
+#pragma unroll
+                    for (int mt2 = 0; mt2 < 2; ++mt2) {
+                        f4 ar = mfma(c2r[mt2], br, zero4);
+                        ar = mfma(c2i[mt2], nbi, ar);
+                        f4 ai = mfma(c2r[mt2], bi, zero4);
+                        ai = mfma(c2i[mt2], br, ai);
+                        zr_[q][mt2] = ar;
+                        zi_[q][mt2] = ai;
+                    }
+                }
+                // S += Z_g conj(Z_x)
+#pragma unroll
+                for (int mt2 = 0; mt2 < 2; ++mt2) {
+                    Sr[nt][mt2] += zr_[0][mt2] * zr_[1][mt2] + zi_[0][mt2] * zi_[1][mt2];
+                    Si[nt][mt2] += zi_[0][mt2] * zr_[1][mt2] - zr_[0][mt2] * zi_[1][mt2];
+                }
+            }
+        }
+      }
+
+        // ---- end of the channel: sum over the waves, then the inverse by wave 0
+        __syncthreads();   // (wave 0 has read and cleared the previous channel's sum)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int mt2 = 0; mt2 < 2; ++mt2)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    atomicAdd(&s_S[(((nt * 2 + mt2) * 2 + 0) * 64 + lane) * 4 + e], Sr[nt][mt2][e]);
+                    atomicAdd(&s_S[(((nt * 2 + mt2) * 2 + 1) * 64 + lane) * 4 + e], Si[nt][mt2][e]);
+                }
+        __syncthreads();
+        if (wave != 0) continue;
+        f4 Tr[4][2], Ti[4][2];
+        float mx = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int mt2 = 0; mt2 < 2; ++mt2) {
+                float *pr = &s_S[(((nt * 2 + mt2) * 2 + 0) * 64 + lane) * 4];
+                float *pi = &s_S[(((nt * 2 + mt2) * 2 + 1) * 64 + lane) * 4];
+                Tr[nt][mt2] = *reinterpret_cast<const f4 *>(pr);
+                Ti[nt][mt2] = *reinterpret_cast<const f4 *>(pi);
+                *reinterpret_cast<f4 *>(pr) = zero4;
+                *reinterpret_cast<f4 *>(pi) = zero4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fmaxf(fabsf(Tr[nt][mt2][e]), fabsf(Ti[nt][mt2][e])));
+            }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        // scale 2^-e with max |S| 2^-e <= 1: the fp16 operands of the inverse chain
+        const int ex = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx) : 0;
+        const float sc = __builtin_ldexpf(1.f, -ex), back = __builtin_ldexpf(1.f, ex) / (float)M;
+        // S2': rows f_s (tile nt), column tiles nt2 of n_f; conj twiddle (as in the forward kernel)
+        h8 a3r[2][2], a3i[2][2];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            const h8 a2r = cat8(to_h4(Tr[nt][0] * sc), to_h4(Tr[nt][1] * sc));
+            const h8 a2i = cat8(to_h4(Ti[nt][0] * sc), to_h4(Ti[nt][1] * sc));
+            const h8 na2r = neg8(a2r);
+#pragma unroll
+            for (int nt2 = 0; nt2 < 2; ++nt2) {
+                f4 ar = mfma(a2r, c2r[nt2], zero4);
+                ar = mfma(a2i, c2i[nt2], ar);
+                f4 ai = mfma(na2r, c2i[nt2], zero4);
+                ai = mfma(a2i, c2r[nt2], ai);
+                h4 t3r = to_h4(ar), t3i = to_h4(ai);
+                cmul4(t3r, t3i, s_tw3[(nt * 2 + nt2) * 64 + lane]);
+                const int ksi = nt >> 1, half = (nt & 1) * 4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    a3r[ksi][nt2][half + e] = t3r[e];
+                    a3i[ksi][nt2][half + e] = t3i[e];
+                }
+            }
+        }
+        // S1': the real part only (rows n_f, columns n_s < 32), staged as one fp32 row of
+        // 1024 outputs in wave 0's planes (16-byte unit m / 4, bit 2 flipped by bit 4)
+        char *const so = reinterpret_cast<char *>(s_z[0]);
+#pragma unroll
+        for (int nt2 = 0; nt2 < 2; ++nt2) {
+            const h8 na0i = neg8(a3i[0][nt2]), na1i = neg8(a3i[1][nt2]);
+#pragma unroll
+            for (int nt3 = 0; nt3 < 2; ++nt3) {
+                const h8 f30r = s_f3[0][nt3][lane], f30i = s_f3[1][nt3][lane];
+                const h8 f31r = s_f3[0][2 + nt3][lane], f31i = s_f3[1][2 + nt3][lane];
+                f4 ar = mfma(a3r[0][nt2], f30r, zero4);
+                ar = mfma(na0i, f30i, ar);
+                ar = mfma(a3r[1][nt2], f31r, ar);
+                ar = mfma(na1i, f31i, ar);
+                const int un = 8 * (16 * nt3 + c) + 4 * nt2 + g;
+                const int us = un ^ (((un >> 4) & 1) << 2);
+                *reinterpret_cast<f4 *>(so + 16 * us) = ar * back;
+            }
+        }
+        wave_sync();
+        const float *sf = reinterpret_cast<const float *>(so);
+        T *drow = dk + h * L;
+#pragma unroll
+        for (int k = 0; k < N / 64; ++k) {
+            const int s = lane + 64 * k;
+            const int un = s >> 2, us = un ^ (((un >> 4) & 1) << 2);
+            if (s < L) drow[s] = from_f32<T>(sf[4 * us + (s & 3)]);
+        }
+        wave_sync();   // (the next pair's scatter reuses these planes)
+    }
+}
+
 hipError_t launch_pair_conv(int logn, int st, const void *u, const void *w, const void *v,
                             void *out, const void *kbins, const float *kscale, const uint8_t *mask,
                             int64_t B, int64_t H, hipStream_t stream) {
@@ -718,6 +1010,41 @@ hipError_t launch_pair_conv_win(int st, const void *u, const void *w, const void
         case 1: go(pair1k_kernel<TT, false, false, true, true>, tp); break;
         case 2: go(pair1k_kernel<TT, false, true, false, true>, tp); break;
         default: go(pair1k_kernel<TT, false, true, true, true>, tp); break;
+        }
+    };
+    if (st == ST_F16) pick((__half *)nullptr);
+    else pick((__hip_bfloat16 *)nullptr);
+    return hipGetLastError();
+}
+
+
+hipError_t launch_pair_dk(int st, const void *dy, const void *u, const void *w, const void *v, void *dk,
+                          int64_t B, int64_t H, int64_t L, hipStream_t stream) {
+    if (st == ST_F32) return hipErrorInvalidValue;
+    if (B <= 0 || H <= 0) return hipSuccess;
+    PairTables tb{};
+    hipError_t e = get_pair_tables(&tb);
+    if (e != hipSuccess) return e;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v_ = 0;
+        if (hipDeviceGetAttribute(&v_, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v_ > 0)
+            cus = v_;
+    }
+    const int64_t blocks = H < cus ? H : cus;   // one 8-wave workgroup per CU, channels strided
+    auto go = [&](auto kern, auto *tp) {
+        using TT = std::remove_pointer_t<decltype(tp)>;
+        hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * kDkWaves), 0, stream, (const TT *)dy,
+                           (const TT *)u, (const TT *)w, (const TT *)v, (TT *)dk, tb, B, H, L);
+    };
+    auto pick = [&](auto *tp) {
+        using TT = std::remove_pointer_t<decltype(tp)>;
+        const int sel = (w ? 2 : 0) | (v ? 1 : 0);
+        switch (sel) {
+        case 0: go(pair1k_dk_kernel<TT, false, false>, tp); break;
+        case 1: go(pair1k_dk_kernel<TT, false, true>, tp); break;
+        case 2: go(pair1k_dk_kernel<TT, true, false>, tp); break;
+        default: go(pair1k_dk_kernel<TT, true, true>, tp); break;
         }
     };
     if (st == ST_F16) pick((__half *)nullptr);

@@ -101,3 +101,15 @@ def test_bwd_odd_batch_and_one_sequence():
         got = _run(inp, dy)
         want = oracle.direct_bwd(inp.f64("u"), inp.f64("k"), dy.double().numpy(), inp.f64("w"), inp.f64("v"))
         _check(got, want, TOL["f16"])
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_bwd_n1024_many_channels(dtype):
+    # N = 1024: dk comes from one kernel per channel; more channels than CUs (a workgroup
+    # walks several), an odd batch, a filter shorter than the sequence
+    B, H, N, L = 5, 300, 1024, 700
+    _say(f"bwd N={N} B={B} H={H} L={L} {dtype}")
+    inp, dy = _case(B, H, N, L, dtype, "both", seed=301)
+    got = _run(inp, dy)
+    want = oracle.fft_bwd(inp.f64("u"), inp.f64("k"), dy.double().numpy(), inp.f64("w"), inp.f64("v"))
+    _check(got, want, TOL[dtype])
