@@ -670,10 +670,9 @@ pair1k_dk_kernel(const T *__restrict__ dy, const T *__restrict__ u, const T *__r
     __shared__ h8 s_tw3[4 * 2 * 64];
     __shared__ h8 s_f1[3][4][64];   // re, im, -im: S1 takes no negated data operand
     __shared__ h8 s_f3[2][4][64];
-    // per wave: the input planes of g and x (4 x kPlane fp16), later wave 0's output row
+    // per wave: the input planes of g and x (4 x kPlane fp16), later wave 0's output row;
+    // at a channel's end the whole 64 KB holds four 16 KB slots of the sum over the waves
     __shared__ __align__(16) _Float16 s_z[W][4 * kPlane];
-    // the channel's sum S in the S2 accumulator layout: [nt][mt2][re / im][lane][4]
-    __shared__ __align__(16) float s_S[4 * 2 * 2 * 64 * 4];
 
     const int tid = threadIdx.x;
     for (int i = tid; i < 512; i += 64 * W) {
@@ -687,7 +686,6 @@ pair1k_dk_kernel(const T *__restrict__ dy, const T *__restrict__ u, const T *__r
         s_f3[0][i / 64][i % 64] = reinterpret_cast<const h8 *>(tb.f3r)[i];
         s_f3[1][i / 64][i % 64] = reinterpret_cast<const h8 *>(tb.f3i)[i];
     }
-    for (int i = tid; i < 4 * 2 * 2 * 64 * 4; i += 64 * W) s_S[i] = 0.f;
     __syncthreads();
 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, c = lane & 15;
@@ -843,18 +841,41 @@ pair1k_dk_kernel(const T *__restrict__ dy, const T *__restrict__ u, const T *__r
         }
       }
 
-        // ---- end of the channel: sum over the waves, then the inverse by wave 0
-        __syncthreads();   // (wave 0 has read and cleared the previous channel's sum)
+        // ---- end of the channel: pairwise sum over the waves (8 -> 4 -> 2 -> 1) through
+        // 16 KB slots of the planes region ([nt][mt2][re / im][lane] f4), then the inverse
+        // by wave 0 on the sum in its registers
+        f4 *const slot = reinterpret_cast<f4 *>(&s_z[0][0]);
+        auto put = [&](int k) {
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
+            for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-            for (int mt2 = 0; mt2 < 2; ++mt2)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    atomicAdd(&s_S[(((nt * 2 + mt2) * 2 + 0) * 64 + lane) * 4 + e], Sr[nt][mt2][e]);
-                    atomicAdd(&s_S[(((nt * 2 + mt2) * 2 + 1) * 64 + lane) * 4 + e], Si[nt][mt2][e]);
+                for (int mt2 = 0; mt2 < 2; ++mt2) {
+                    slot[k * 1024 + ((nt * 2 + mt2) * 2 + 0) * 64 + lane] = Sr[nt][mt2];
+                    slot[k * 1024 + ((nt * 2 + mt2) * 2 + 1) * 64 + lane] = Si[nt][mt2];
                 }
+        };
+        auto add = [&](int k) {
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+                for (int mt2 = 0; mt2 < 2; ++mt2) {
+                    Sr[nt][mt2] += slot[k * 1024 + ((nt * 2 + mt2) * 2 + 0) * 64 + lane];
+                    Si[nt][mt2] += slot[k * 1024 + ((nt * 2 + mt2) * 2 + 1) * 64 + lane];
+                }
+        };
+        __syncthreads();   // every wave is past its last pair: the planes are free
+        if (wave >= 4) put(wave - 4);
         __syncthreads();
+        if (wave < 4) add(wave);
+        __syncthreads();
+        if (wave == 2 || wave == 3) put(wave - 2);
+        __syncthreads();
+        if (wave < 2) add(wave);
+        __syncthreads();
+        if (wave == 1) put(0);
+        __syncthreads();
+        if (wave == 0) add(0);
+        __syncthreads();   // (the next pairs' scatters reuse the planes)
         if (wave != 0) continue;
         f4 Tr[4][2], Ti[4][2];
         float mx = 0.f;
@@ -862,12 +883,8 @@ pair1k_dk_kernel(const T *__restrict__ dy, const T *__restrict__ u, const T *__r
         for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
             for (int mt2 = 0; mt2 < 2; ++mt2) {
-                float *pr = &s_S[(((nt * 2 + mt2) * 2 + 0) * 64 + lane) * 4];
-                float *pi = &s_S[(((nt * 2 + mt2) * 2 + 1) * 64 + lane) * 4];
-                Tr[nt][mt2] = *reinterpret_cast<const f4 *>(pr);
-                Ti[nt][mt2] = *reinterpret_cast<const f4 *>(pi);
-                *reinterpret_cast<f4 *>(pr) = zero4;
-                *reinterpret_cast<f4 *>(pi) = zero4;
+                Tr[nt][mt2] = Sr[nt][mt2];
+                Ti[nt][mt2] = Si[nt][mt2];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fmaxf(fabsf(Tr[nt][mt2][e]), fabsf(Ti[nt][mt2][e])));
             }
