@@ -630,13 +630,21 @@ fftconv_status_t fftconv_bwd(const void *dy, const void *u, const void *K_f, con
     if ((du || dw) && B > 0) {
         hipError_t e = conj_spectrum(K_f, ws + lay.kc, H, N, dtype, stream);
         if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "conjugating K_f: %s", hipGetErrorString(e));
-        if (du) {
-            st = fftconv_fwd(dy, ws + lay.kc, v, w, du, B, H, N, L, mask, dtype, fws, fws_bytes, stream);
-            if (st != FFTCONV_OK) return st;
-        }
-        if (dw) {
-            st = fftconv_fwd(dy, ws + lay.kc, v, u, dw, B, H, N, L, mask, dtype, fws, fws_bytes, stream);
-            if (st != FFTCONV_OK) return st;
+        if (du && dw && use_pair_kernel(l, dtype)) {
+            // N = 1024: one call forms both from the same transforms
+            const char *kb = ws + lay.kc;
+            e = launch_pair_conv(l, dtype, dy, v, w, du, kb + kf_bins_off(H),
+                                 reinterpret_cast<const float *>(kb + kf_scale_off()), mask, B, H, stream, u, dw);
+            if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "du, dw: %s", hipGetErrorString(e));
+        } else {
+            if (du) {
+                st = fftconv_fwd(dy, ws + lay.kc, v, w, du, B, H, N, L, mask, dtype, fws, fws_bytes, stream);
+                if (st != FFTCONV_OK) return st;
+            }
+            if (dw) {
+                st = fftconv_fwd(dy, ws + lay.kc, v, u, dw, B, H, N, L, mask, dtype, fws, fws_bytes, stream);
+                if (st != FFTCONV_OK) return st;
+            }
         }
     }
     // dk[h, s] = sum_b corr(v dy, u w)[b, h, s].  N = 1024 (fp16 / bf16, no mask): one

@@ -170,9 +170,11 @@ hipError_t get_pair3_tables(Pair3Tables *out);
 hipError_t launch_pair16k_conv(int st, const void *u, const void *w, const void *v, void *out,
                                const void *kbins, const float *kscale, const uint8_t *mask,
                                int64_t B, int64_t H, hipStream_t stream);
+// with out2: also out2 = v2 * conv(u w, k) from the same transforms (v and v2 non-null)
 hipError_t launch_pair_conv(int logn, int st, const void *u, const void *w, const void *v,
                             void *out, const void *kbins, const float *kscale, const uint8_t *mask,
-                            int64_t B, int64_t H, hipStream_t stream);
+                            int64_t B, int64_t H, hipStream_t stream, const void *v2 = nullptr,
+                            void *out2 = nullptr);
 // Chunked short-filter path: (B, H, NS) sequences, NS a multiple of 1024, as
 // half-overlapping windows of 1024 through the N = 1024 matrix-core kernel.
 // dk of the backward pass at N = 1024 (fp16 / bf16, no mask): dk (H, L) <- sum over b of

@@ -262,12 +262,16 @@ __device__ __forceinline__ void gate_product<__hip_bfloat16>(const uint4 &uq, co
 // input fills the window: two K blocks, the second with DFT entries
 // w64^{(n_s + 32) f_s} = (-1)^{f_s} w64^{n_s f_s}) and S1' produces n_s = 32 .. 63
 // (entries conj w64^{f_s (n_s + 32)} = (-1)^{f_s} conj w64^{f_s n_s}).
-template <typename T, bool MASKED, bool HAS_W, bool HAS_V, bool WIN = false>
+// DUAL: a second output out2 = v2 * conv(u w, k) of the same convolution (the backward
+// pass forms du = w corr(v dy, k) and dw = u corr(v dy, k) in one call).
+template <typename T, bool MASKED, bool HAS_W, bool HAS_V, bool WIN = false, bool DUAL = false>
 __global__ void __launch_bounds__(64 * kPairWaves, MASKED ? 1 : 2)
 pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restrict__ v,
               T *__restrict__ out, const uint4 *__restrict__ kbins, const float *__restrict__ kscale,
-              const uint8_t *__restrict__ mask, PairTables tb, int64_t B, int64_t H, int64_t NS) {
+              const uint8_t *__restrict__ mask, PairTables tb, int64_t B, int64_t H, int64_t NS,
+              const T *__restrict__ v2, T *__restrict__ out2) {
     static_assert(!(WIN && MASKED), "the windowed path has no frequency mask");
+    static_assert(!DUAL || (HAS_V && !WIN), "a second output has an output gate of its own");
     constexpr int N = 1024;
     __shared__ h8 s_tw1[2 * 4 * 64];     // per (mt, nt, lane): cos[4], sin[4]
     __shared__ h8 s_tw3[4 * 2 * 64];     // per (nt, nt2, lane)
@@ -384,10 +388,10 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
             for (int nt = 0; nt < 4; ++nt) fk.k[mt2][nt] = krow[(mt2 * 4 + nt) * 64 + lane];
         fk.ks = kscale[h];
     };
-    auto load_gate = [&](int64_t oa, int64_t ob, uint4 (&vg)[4]) {
+    auto load_gate = [&](const T *gp, int64_t oa, int64_t ob, uint4 (&vg)[4]) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            vg[q] = *reinterpret_cast<const uint4 *>(v + (q < 2 ? oa : ob) + 512 * (q & 1) + 8 * lane);
+            vg[q] = *reinterpret_cast<const uint4 *>(gp + (q < 2 ? oa : ob) + 512 * (q & 1) + 8 * lane);
     };
     using Raw = std::conditional_t<WIN, WinRaw, PairRaw>;
     auto load_in = [&](int64_t pp, Raw &raw) {
@@ -444,8 +448,9 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
         bool first;
         offsets(p, h, oa, ob, has_b, first);
         const int64_t pn = p + stride < p_end ? p + stride : p;
-        uint4 vg[4];
-        if (HAS_V) load_gate(oa, ob, vg);
+        uint4 vg[4], vg2[4];
+        if (HAS_V) load_gate(v, oa, ob, vg);
+        if (DUAL) load_gate(v2, oa, ob, vg2);
         const float ks = fc.ks;
 
         // ---- x = u * w of both sequences (windows), scattered into the transposed LDS
@@ -624,13 +629,21 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
             const f4 y0 = *reinterpret_cast<const f4 *>(so + 4096 * (qq >> 1) + 16 * s0);
             const f4 y1 = *reinterpret_cast<const f4 *>(so + 4096 * (qq >> 1) + 16 * s1);
             float y[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+            const int64_t oq = (q < 2 ? oa : ob) + 512 * (q & 1) + 8 * lane;
+            if (DUAL) {
+                float g8[8], y2[8];
+                unpack8<T>(vg2[q], g8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y2[e] = y[e] * g8[e];
+                *reinterpret_cast<uint4 *>(out2 + oq) = io8<T>::pack8(y2);
+            }
             if (HAS_V) {
                 float g8[8];
                 unpack8<T>(vg[q], g8);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) y[e] *= g8[e];
             }
-            *reinterpret_cast<uint4 *>(out + (q < 2 ? oa : ob) + 512 * (q & 1) + 8 * lane) = io8<T>::pack8(y);
+            *reinterpret_cast<uint4 *>(out + oq) = io8<T>::pack8(y);
         }
         // the next pair's input scatter reuses this wave's LDS: order after the reads above
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -950,8 +963,9 @@ pair1k_dk_kernel(const T *__restrict__ dy, const T *__restrict__ u, const T *__r
 
 hipError_t launch_pair_conv(int logn, int st, const void *u, const void *w, const void *v,
                             void *out, const void *kbins, const float *kscale, const uint8_t *mask,
-                            int64_t B, int64_t H, hipStream_t stream) {
+                            int64_t B, int64_t H, hipStream_t stream, const void *v2, void *out2) {
     if (logn != 10 || st == ST_F32) return hipErrorInvalidValue;
+    if (out2 != nullptr && (v == nullptr || v2 == nullptr)) return hipErrorInvalidValue;
     PairTables tb{};
     hipError_t e = get_pair_tables(&tb);
     if (e != hipSuccess) return e;
@@ -972,11 +986,21 @@ hipError_t launch_pair_conv(int logn, int st, const void *u, const void *w, cons
         using TT = std::remove_pointer_t<decltype(tp)>;
         hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * kPairWaves), 0, stream,
                            (const TT *)u, (const TT *)w, (const TT *)v, (TT *)out,
-                           (const uint4 *)kbins, kscale, mask, tb, B, H, (int64_t)1024);
+                           (const uint4 *)kbins, kscale, mask, tb, B, H, (int64_t)1024, (const TT *)v2,
+                           (TT *)out2);
     };
     // one instantiation per (storage type, mask, gates): no gate test sits in the pair loop
     auto pick = [&](auto *tp) {
         using TT = std::remove_pointer_t<decltype(tp)>;
+        if (out2 != nullptr) {   // two outputs: both output gates present
+            switch ((mask ? 2 : 0) | (w ? 1 : 0)) {
+            case 0: go(pair1k_kernel<TT, false, false, true, false, true>, tp); break;
+            case 1: go(pair1k_kernel<TT, false, true, true, false, true>, tp); break;
+            case 2: go(pair1k_kernel<TT, true, false, true, false, true>, tp); break;
+            default: go(pair1k_kernel<TT, true, true, true, false, true>, tp); break;
+            }
+            return;
+        }
         const int sel = (mask ? 4 : 0) | (w ? 2 : 0) | (v ? 1 : 0);
         switch (sel) {
         case 0: go(pair1k_kernel<TT, false, false, false>, tp); break;
@@ -1017,7 +1041,8 @@ hipError_t launch_pair_conv_win(int st, const void *u, const void *w, const void
         using TT = std::remove_pointer_t<decltype(tp)>;
         hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * kPairWaves), 0, stream,
                            (const TT *)u, (const TT *)w, (const TT *)v, (TT *)out,
-                           (const uint4 *)kbins, kscale, (const uint8_t *)nullptr, tb, B, H, NS);
+                           (const uint4 *)kbins, kscale, (const uint8_t *)nullptr, tb, B, H, NS,
+                           (const TT *)nullptr, (TT *)nullptr);
     };
     auto pick = [&](auto *tp) {
         using TT = std::remove_pointer_t<decltype(tp)>;
