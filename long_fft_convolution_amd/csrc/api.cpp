@@ -647,10 +647,10 @@ fftconv_status_t fftconv_bwd(const void *dy, const void *u, const void *K_f, con
             }
         }
     }
-    // dk[h, s] = sum_b corr(v dy, u w)[b, h, s].  N = 1024 (fp16 / bf16, no mask): one
-    // kernel accumulates the pairs' spectrum products per channel on chip.
-    if (dk && B > 0 && use_pair_kernel(l, dtype) && !mask) {
-        hipError_t e = launch_pair_dk(dtype, dy, u, w, v, dk, B, H, L, stream);
+    // dk[h, s] = sum_b corr(v dy, u w)[b, h, s].  N = 1024 (fp16 / bf16): one kernel
+    // accumulates the pairs' spectrum products per channel on chip.
+    if (dk && B > 0 && use_pair_kernel(l, dtype)) {
+        hipError_t e = launch_pair_dk(dtype, dy, u, w, v, dk, mask, B, H, L, stream);
         if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "dk: %s", hipGetErrorString(e));
     } else if (dk) {
         // otherwise each x = u w is the filter of its own channel b H + h; the mask rows

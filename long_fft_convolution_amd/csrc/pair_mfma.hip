@@ -673,11 +673,14 @@ template <> __device__ __forceinline__ __hip_bfloat16 from_f32<__hip_bfloat16>(f
     return __float2bfloat16(x);
 }
 
-template <typename T, bool HAS_W, bool HAS_V>
+// With a frequency mask the dropped bins of S are zeroed before the inverse (the mask
+// multiplies the spectrum product as it multiplies K in the forward pass, and it is
+// symmetric in f, so it commutes with taking the Hermitian part).
+template <typename T, bool HAS_W, bool HAS_V, bool MASKED>
 __global__ void __launch_bounds__(64 * kDkWaves, 1)
 pair1k_dk_kernel(const T *__restrict__ dy, const T *__restrict__ u, const T *__restrict__ w,
-                 const T *__restrict__ v, T *__restrict__ dk, PairTables tb, int64_t B, int64_t H,
-                 int64_t L) {
+                 const T *__restrict__ v, T *__restrict__ dk, const uint8_t *__restrict__ mask,
+                 PairTables tb, int64_t B, int64_t H, int64_t L) {
     constexpr int N = 1024, M = 2048, W = kDkWaves;
     __shared__ h8 s_tw1[2 * 4 * 64];
     __shared__ h8 s_tw3[4 * 2 * 64];
@@ -898,6 +901,20 @@ pair1k_dk_kernel(const T *__restrict__ dy, const T *__restrict__ u, const T *__r
             for (int mt2 = 0; mt2 < 2; ++mt2) {
                 Tr[nt][mt2] = Sr[nt][mt2];
                 Ti[nt][mt2] = Si[nt][mt2];
+                if (MASKED) {
+                    // (the lane index is laundered so that these channel-invariant indices are
+                    // recomputed here, not held in registers across the pair loop)
+                    int lc = c, lg = g;
+                    asm volatile("" : "+v"(lc), "+v"(lg));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {   // bin f = f_s + 64 f_f of this element
+                        const int f = 16 * nt + lc + 64 * (16 * mt2 + 4 * lg + e);
+                        const int fr = f <= N ? f : M - f;
+                        int blk = fr / (N / kMaskBlocks);
+                        blk = blk > kMaskBlocks - 1 ? kMaskBlocks - 1 : blk;
+                        if (!mask[h * kMaskBlocks + blk]) Tr[nt][mt2][e] = Ti[nt][mt2][e] = 0.f;
+                    }
+                }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fmaxf(fabsf(Tr[nt][mt2][e]), fabsf(Ti[nt][mt2][e])));
             }
@@ -1061,7 +1078,7 @@ hipError_t launch_pair_conv_win(int st, const void *u, const void *w, const void
 
 
 hipError_t launch_pair_dk(int st, const void *dy, const void *u, const void *w, const void *v, void *dk,
-                          int64_t B, int64_t H, int64_t L, hipStream_t stream) {
+                          const uint8_t *mask, int64_t B, int64_t H, int64_t L, hipStream_t stream) {
     if (st == ST_F32) return hipErrorInvalidValue;
     if (B <= 0 || H <= 0) return hipSuccess;
     PairTables tb{};
@@ -1077,16 +1094,20 @@ hipError_t launch_pair_dk(int st, const void *dy, const void *u, const void *w, 
     auto go = [&](auto kern, auto *tp) {
         using TT = std::remove_pointer_t<decltype(tp)>;
         hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * kDkWaves), 0, stream, (const TT *)dy,
-                           (const TT *)u, (const TT *)w, (const TT *)v, (TT *)dk, tb, B, H, L);
+                           (const TT *)u, (const TT *)w, (const TT *)v, (TT *)dk, mask, tb, B, H, L);
     };
     auto pick = [&](auto *tp) {
         using TT = std::remove_pointer_t<decltype(tp)>;
-        const int sel = (w ? 2 : 0) | (v ? 1 : 0);
+        const int sel = (mask ? 4 : 0) | (w ? 2 : 0) | (v ? 1 : 0);
         switch (sel) {
-        case 0: go(pair1k_dk_kernel<TT, false, false>, tp); break;
-        case 1: go(pair1k_dk_kernel<TT, false, true>, tp); break;
-        case 2: go(pair1k_dk_kernel<TT, true, false>, tp); break;
-        default: go(pair1k_dk_kernel<TT, true, true>, tp); break;
+        case 0: go(pair1k_dk_kernel<TT, false, false, false>, tp); break;
+        case 1: go(pair1k_dk_kernel<TT, false, true, false>, tp); break;
+        case 2: go(pair1k_dk_kernel<TT, true, false, false>, tp); break;
+        case 3: go(pair1k_dk_kernel<TT, true, true, false>, tp); break;
+        case 4: go(pair1k_dk_kernel<TT, false, false, true>, tp); break;
+        case 5: go(pair1k_dk_kernel<TT, false, true, true>, tp); break;
+        case 6: go(pair1k_dk_kernel<TT, true, false, true>, tp); break;
+        default: go(pair1k_dk_kernel<TT, true, true, true>, tp); break;
         }
     };
     if (st == ST_F16) pick((__half *)nullptr);
