@@ -250,6 +250,36 @@ template <typename V, typename P>
 __device__ __forceinline__ void stu(P *base, uint32_t byte_off, const V &x) {
     *reinterpret_cast<V *>(reinterpret_cast<char *>(base) + byte_off) = x;
 }
+// Streaming (non-temporal) forms for data that is read or written once: they do not
+// keep the stream in L2 ahead of data that is reused (filter spectra, tables).
+template <typename V>
+__device__ __forceinline__ V ldnt(const void *p) {
+    static_assert(sizeof(V) % 4 == 0 && sizeof(V) <= 16, "32-bit words");
+    if constexpr (sizeof(V) == 4) {
+        return __builtin_bit_cast(V, __builtin_nontemporal_load(reinterpret_cast<const unsigned int *>(p)));
+    } else {
+        typedef unsigned int w_t __attribute__((ext_vector_type(sizeof(V) / 4)));
+        return __builtin_bit_cast(V, __builtin_nontemporal_load(reinterpret_cast<const w_t *>(p)));
+    }
+}
+template <typename V>
+__device__ __forceinline__ void stnt(void *p, const V &x) {
+    static_assert(sizeof(V) % 4 == 0 && sizeof(V) <= 16, "32-bit words");
+    if constexpr (sizeof(V) == 4) {
+        __builtin_nontemporal_store(__builtin_bit_cast(unsigned int, x), reinterpret_cast<unsigned int *>(p));
+    } else {
+        typedef unsigned int w_t __attribute__((ext_vector_type(sizeof(V) / 4)));
+        __builtin_nontemporal_store(__builtin_bit_cast(w_t, x), reinterpret_cast<w_t *>(p));
+    }
+}
+template <typename V, typename P>
+__device__ __forceinline__ V ldu_nt(const P *base, uint32_t byte_off) {
+    return ldnt<V>(reinterpret_cast<const char *>(base) + byte_off);
+}
+template <typename V, typename P>
+__device__ __forceinline__ void stu_nt(P *base, uint32_t byte_off, const V &x) {
+    stnt<V>(reinterpret_cast<char *>(base) + byte_off, x);
+}
 // Hide a lane value from loop-invariant code motion so that addresses built
 // from it are recomputed where they are used instead of being held live.
 __device__ __forceinline__ int launder(int x) {

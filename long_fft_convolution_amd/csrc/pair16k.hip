@@ -353,7 +353,7 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                 if (HAS_V) {
 #pragma unroll
                     for (int tt = 0; tt < kTilesPerWave; ++tt) {
-                        vq[tt] = ldu<uint4>(v + (tt < 4 ? oa : ob) + 4096 * (tt & 3), 2 * m4);
+                        vq[tt] = ldu_nt<uint4>(v + (tt < 4 ? oa : ob) + 4096 * (tt & 3), 2 * m4);
                     }
                 }
                 // pinned order: the gate is consumed first, and vmcnt waits are in order
@@ -484,7 +484,7 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                     }
                 }
                 const uint2 lo = st<T>::pack4(yv), hi = st<T>::pack4(yv + 4);
-                stu(out + (k < 4 ? oa : ob) + 4096 * (k & 3), 2 * m4, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                stu_nt(out + (k < 4 ? oa : ob) + 4096 * (k & 3), 2 * m4, make_uint4(lo.x, lo.y, hi.x, hi.y));
             }
         }
         __syncthreads();

@@ -157,11 +157,11 @@ __device__ __forceinline__ void load_pair_raw(PairRaw &raw, const T *__restrict_
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
         const int m0 = 8 * lane + 512 * r;
-        raw.q[r][0] = *reinterpret_cast<const uint4 *>(u + oa + m0);
-        raw.q[r][2] = *reinterpret_cast<const uint4 *>(u + ob + m0);
+        raw.q[r][0] = ldnt<uint4>(u + oa + m0);
+        raw.q[r][2] = ldnt<uint4>(u + ob + m0);
         if (HAS_W) {
-            raw.q[r][1] = *reinterpret_cast<const uint4 *>(w + oa + m0);
-            raw.q[r][3] = *reinterpret_cast<const uint4 *>(w + ob + m0);
+            raw.q[r][1] = ldnt<uint4>(w + oa + m0);
+            raw.q[r][3] = ldnt<uint4>(w + ob + m0);
         }
     }
 }
@@ -391,7 +391,7 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
     auto load_gate = [&](const T *gp, int64_t oa, int64_t ob, uint4 (&vg)[4]) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            vg[q] = *reinterpret_cast<const uint4 *>(gp + (q < 2 ? oa : ob) + 512 * (q & 1) + 8 * lane);
+            vg[q] = ldnt<uint4>(gp + (q < 2 ? oa : ob) + 512 * (q & 1) + 8 * lane);   // (read once: streaming)
     };
     using Raw = std::conditional_t<WIN, WinRaw, PairRaw>;
     auto load_in = [&](int64_t pp, Raw &raw) {
@@ -635,7 +635,7 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
                 unpack8<T>(vg2[q], g8);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) y2[e] = y[e] * g8[e];
-                *reinterpret_cast<uint4 *>(out2 + oq) = io8<T>::pack8(y2);
+                stnt<uint4>(out2 + oq, io8<T>::pack8(y2));
             }
             if (HAS_V) {
                 float g8[8];
@@ -643,7 +643,7 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
 #pragma unroll
                 for (int e = 0; e < 8; ++e) y[e] *= g8[e];
             }
-            *reinterpret_cast<uint4 *>(out + oq) = io8<T>::pack8(y);
+            stnt<uint4>(out + oq, io8<T>::pack8(y));   // (written once: streaming)
         }
         // the next pair's input scatter reuses this wave's LDS: order after the reads above
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -741,17 +741,17 @@ pair1k_dk_kernel(const T *__restrict__ dy, const T *__restrict__ u, const T *__r
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
             const int m0 = 8 * lane + 512 * r;
-            raw.q[r][0] = *reinterpret_cast<const uint4 *>(dy + oa + m0);
-            raw.q[r][2] = *reinterpret_cast<const uint4 *>(dy + ob + m0);
-            raw.q[r][4] = *reinterpret_cast<const uint4 *>(u + oa + m0);
-            raw.q[r][6] = *reinterpret_cast<const uint4 *>(u + ob + m0);
+            raw.q[r][0] = ldnt<uint4>(dy + oa + m0);
+            raw.q[r][2] = ldnt<uint4>(dy + ob + m0);
+            raw.q[r][4] = ldnt<uint4>(u + oa + m0);
+            raw.q[r][6] = ldnt<uint4>(u + ob + m0);
             if (HAS_V) {
-                raw.q[r][1] = *reinterpret_cast<const uint4 *>(v + oa + m0);
-                raw.q[r][3] = *reinterpret_cast<const uint4 *>(v + ob + m0);
+                raw.q[r][1] = ldnt<uint4>(v + oa + m0);
+                raw.q[r][3] = ldnt<uint4>(v + ob + m0);
             }
             if (HAS_W) {
-                raw.q[r][5] = *reinterpret_cast<const uint4 *>(w + oa + m0);
-                raw.q[r][7] = *reinterpret_cast<const uint4 *>(w + ob + m0);
+                raw.q[r][5] = ldnt<uint4>(w + oa + m0);
+                raw.q[r][7] = ldnt<uint4>(w + ob + m0);
             }
         }
     };
