@@ -236,7 +236,7 @@ eqlinear_kernel(const S *__restrict__ x, const _Float16 *__restrict__ Wf, S *__r
         const int64_t nn = n0 + tk;
         if (nn < Ntok && dl < dvalid) {
             const uint4 q = *reinterpret_cast<const uint4 *>(sy + r * DSPAN + dl);
-            *reinterpret_cast<uint4 *>(y + (nn * T + t) * Cout + d0 + dl) = q;
+            stnt<uint4>(y + (nn * T + t) * Cout + d0 + dl, q);   // (written once: streaming)
         }
     }
 }
