@@ -175,13 +175,14 @@ hipError_t launch_pair_conv(int logn, int st, const void *u, const void *w, cons
                             void *out, const void *kbins, const float *kscale, const uint8_t *mask,
                             int64_t B, int64_t H, hipStream_t stream, const void *v2 = nullptr,
                             void *out2 = nullptr);
-// Chunked short-filter path: (B, H, NS) sequences, NS a multiple of 1024, as
-// half-overlapping windows of 1024 through the N = 1024 matrix-core kernel.
 // dk of the backward pass at N = 1024 (fp16 / bf16): dk (H, L) <- sum over b of
 // corr(v dy, u w), the spectrum product masked like K when mask is given (w, v, mask
 // may be null)
 hipError_t launch_pair_dk(int st, const void *dy, const void *u, const void *w, const void *v, void *dk,
                           const uint8_t *mask, int64_t B, int64_t H, int64_t L, hipStream_t stream);
+// Chunked short-filter path: (B, H, NS) sequences, NS a multiple of 1024, as
+// half-overlapping windows of 2048 samples, each a 2048-point circular convolution on
+// the N = 1024 matrix-core kernel (filters of at most 1024 taps).
 hipError_t launch_pair_conv_win(int st, const void *u, const void *w, const void *v, void *out,
                                 const void *kbins, const float *kscale, int64_t B, int64_t H, int64_t NS,
                                 hipStream_t stream);

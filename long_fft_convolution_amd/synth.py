@@ -51,7 +51,7 @@ class Workload:
     decay: str = "loguniform"     # or "fixed0.01"
     mask_keep_blocks: int | None = None  # blocks [0, keep) kept, the rest zeroed
     seed: int = 1000
-    short: bool = False                  # run through the chunked short-filter path (L <= 512)
+    short: bool = False                  # run through the chunked short-filter path (L <= 1024)
 
     @property
     def elems(self) -> int:
