@@ -400,7 +400,7 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
         offsets(pp, h, oa, ob, hb, fst);
         if constexpr (WIN) {
             // blocks A = [oa - 1024, oa) (before the sequence start for the first pair: the
-            // load re-reads B and is zeroed), B = [oa, oa + 1024), C = [oa + 1024, oa + 2048):
+            // load re-reads B and its product is zeroed), B = [oa, oa + 1024), C = [oa + 1024, oa + 2048):
             // without window b, C re-reads B (its results are not stored)
             const int64_t oA = fst ? oa : oa - 1024, oC = hb ? oa + 1024 : oa;
             const int m = 8 * lane;
@@ -414,10 +414,6 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
                     raw.q[1][r][1] = *reinterpret_cast<const uint4 *>(w + oa + 512 * r + m);
                     raw.q[2][r][1] = *reinterpret_cast<const uint4 *>(w + oC + 512 * r + m);
                 }
-            }
-            if (fst) {
-                raw.q[0][0][0] = make_uint4(0u, 0u, 0u, 0u);
-                raw.q[0][1][0] = make_uint4(0u, 0u, 0u, 0u);
             }
         } else {
             load_pair_raw<T, HAS_W>(raw, u, w, oa, ob, lane);
@@ -461,6 +457,7 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
             for (int k = 0; k < 3; ++k)
 #pragma unroll
                 for (int r = 0; r < 2; ++r) gate_product<T>(cur.q[k][r][0], cur.q[k][r][1], HAS_W, xb3[k][r]);
+            if (first) xb3[0][0] = xb3[0][1] = h8{};   // zeros before the sequence start
 #pragma unroll
             for (int r = 0; r < 4; ++r) {   // window a = (A, B), window b = (B, C)
                 const int m0 = 8 * lane + 512 * r;

@@ -98,3 +98,4 @@ def test_short_filter_empty_batch():
     k = torch.randn(3, 64).to(torch.float16).cuda()
     out = fc.causal_conv_short(u, k)
     assert out.shape == u.shape
+
