@@ -113,3 +113,16 @@ def test_bwd_n1024_many_channels(dtype):
     got = _run(inp, dy)
     want = oracle.fft_bwd(inp.f64("u"), inp.f64("k"), dy.double().numpy(), inp.f64("w"), inp.f64("v"))
     _check(got, want, TOL[dtype])
+
+
+def test_bwd_workload_full_size():
+    # the backward benchmark's configuration (gated_fp16_n1k: B = 64, H = 768, N = 1024,
+    # the same dy recipe), every gradient compared whole against the oracle
+    wl = synth.WORKLOADS["gated_fp16_n1k"]
+    _say(f"bwd {wl.name} full size")
+    inp = synth.generate_workload(wl.name)
+    g = torch.Generator().manual_seed(4242)
+    dy = torch.randn(inp.u.shape, generator=g, dtype=torch.float32).to(inp.u.dtype)
+    got = _run(inp, dy)
+    want = oracle.fft_bwd(inp.f64("u"), inp.f64("k"), dy.double().numpy(), inp.f64("w"), inp.f64("v"))
+    _check(got, want, TOL["f16"])
