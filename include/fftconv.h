@@ -119,7 +119,8 @@ fftconv_status_t fftconv_fwd(const void *u, const void *K_f, const void *w, cons
 /* Device scratch bytes fftconv_bwd needs for this shape (0 for unsupported
  * N or dtype).  It holds the conjugated spectrum, u*w, the spectra of the
  * B*H sequences u*w, their correlations with v*dy, and the forward
- * workspace. */
+ * workspace; at N = 1024 with fp16 or bf16 storage only the conjugated
+ * spectrum (dk is accumulated on chip there). */
 size_t fftconv_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, fftconv_dtype_t dtype);
 
 /* Backward pass of fftconv_fwd: the gradients of sum(dy * out) (the

@@ -547,11 +547,14 @@ static BwdLayout bwd_layout(int64_t B, int64_t H, int64_t N, fftconv_dtype_t dty
         return at;
     };
     o.kc = take(fftconv_filter_bytes(H, N, dtype));
-    o.x = take((size_t)S * (size_t)N * elem_bytes(dtype));
-    o.kx = take(S > 0 ? fftconv_filter_bytes(S, N, dtype) : 0);
-    o.part = take((size_t)S * (size_t)N * elem_bytes(dtype));
-    o.mrep = take((size_t)S * kMaskBlocks);
-    o.fws = take(fftconv_workspace_bytes(1, S, N, dtype));
+    // N = 1024 (fp16 / bf16): du, dw and dk come from kernels that need no scratch beyond
+    // the conjugated spectrum (the dk chain's areas below are then empty)
+    const bool chain = !use_pair_kernel(log2_exact(N), dtype);
+    o.x = take(chain ? (size_t)S * (size_t)N * elem_bytes(dtype) : 0);
+    o.kx = take(chain && S > 0 ? fftconv_filter_bytes(S, N, dtype) : 0);
+    o.part = take(chain ? (size_t)S * (size_t)N * elem_bytes(dtype) : 0);
+    o.mrep = take(chain ? (size_t)S * kMaskBlocks : 0);
+    o.fws = take(chain ? fftconv_workspace_bytes(1, S, N, dtype) : fftconv_workspace_bytes(B, H, N, dtype));
     o.total = off;
     return o;
 }

@@ -124,10 +124,10 @@ def test_prepare_validation():
 
 
 def test_bwd_workspace_bytes():
-    F16, F32 = fc.FFTCONV_F16, fc.FFTCONV_F32
+    F16, BF16, F32 = fc.FFTCONV_F16, fc.FFTCONV_BF16, fc.FFTCONV_F32
     # conjugated K_f + u*w + the B*H sequence spectra + correlations + mask rows
     # + the forward workspace, each region rounded up to 256 bytes
-    B, H, N = 2, 3, 1024
+    B, H, N = 2, 3, 2048
 
     def up(x):
         return (x + 255) // 256 * 256
@@ -136,6 +136,11 @@ def test_bwd_workspace_bytes():
     want = (up(fc.fftconv_filter_bytes(H, N, F16)) + up(S * N * 2) + up(fc.fftconv_filter_bytes(S, N, F16))
             + up(S * N * 2) + up(S * 128) + up(fc.fftconv_workspace_bytes(1, S, N, F16)))
     assert fc.fftconv_bwd_workspace_bytes(B, H, N, F16) == want
+    # N = 1024 in fp16 / bf16: only the conjugated K_f (the gradients come from kernels
+    # that need no other scratch); fp32 keeps the whole layout
+    for dt in (F16, BF16):
+        assert fc.fftconv_bwd_workspace_bytes(B, H, 1024, dt) == up(fc.fftconv_filter_bytes(H, 1024, dt))
+    assert fc.fftconv_bwd_workspace_bytes(B, H, 1024, F32) > up(fc.fftconv_filter_bytes(H, 1024, F32)) + B * H * 1024 * 4
     assert fc.fftconv_bwd_workspace_bytes(B, H, 1 << 20, F32) > 0
     assert fc.fftconv_bwd_workspace_bytes(B, H, 1000, F16) == 0
     assert fc.fftconv_bwd_workspace_bytes(B, 0, N, F16) == 0
