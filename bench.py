@@ -59,7 +59,7 @@ def warm_up(step, warmup: int, dev) -> int:
 
 ELEM = {"f32": 4, "f16": 2, "bf16": 2}
 KERNEL_SOURCES = ["fused.hip", "multipass.hip", "pair_mfma.hip", "pair16k.hip", "eqlinear.hip", "cmfma.hpp",
-                  "fft_device.hpp",
+                  "fft_device.hpp", "fft_stages.hpp",
                   "fftconv_internal.hpp", "api.cpp"]
 
 
