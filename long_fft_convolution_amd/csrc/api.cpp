@@ -633,11 +633,13 @@ fftconv_status_t fftconv_bwd(const void *dy, const void *u, const void *K_f, con
     if ((du || dw) && B > 0) {
         hipError_t e = conj_spectrum(K_f, ws + lay.kc, H, N, dtype, stream);
         if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "conjugating K_f: %s", hipGetErrorString(e));
-        if (du && dw && use_pair_kernel(l, dtype)) {
-            // N = 1024: one call forms both from the same transforms
+        if (du && dw && (use_pair_kernel(l, dtype) || use_pair3_kernel(l, dtype))) {
+            // N = 1024, 16384: one call forms both from the same transforms
             const char *kb = ws + lay.kc;
-            e = launch_pair_conv(l, dtype, dy, v, w, du, kb + kf_bins_off(H),
-                                 reinterpret_cast<const float *>(kb + kf_scale_off()), mask, B, H, stream, u, dw);
+            const float *ksc = reinterpret_cast<const float *>(kb + kf_scale_off());
+            e = use_pair_kernel(l, dtype)
+                    ? launch_pair_conv(l, dtype, dy, v, w, du, kb + kf_bins_off(H), ksc, mask, B, H, stream, u, dw)
+                    : launch_pair16k_conv(dtype, dy, v, w, du, kb + kf_bins_off(H), ksc, mask, B, H, stream, u, dw);
             if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "du, dw: %s", hipGetErrorString(e));
         } else {
             if (du) {

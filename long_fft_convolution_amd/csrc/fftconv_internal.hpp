@@ -167,9 +167,11 @@ struct Pair3Tables {
     const void *two2;        // outer conj twiddles, [32 f_c][2 nt3][2 nt2][lane]
 };
 hipError_t get_pair3_tables(Pair3Tables *out);
+// with out2: also out2 = v2 * conv(u w, k) from the same transforms (v and v2 non-null)
 hipError_t launch_pair16k_conv(int st, const void *u, const void *w, const void *v, void *out,
                                const void *kbins, const float *kscale, const uint8_t *mask,
-                               int64_t B, int64_t H, hipStream_t stream);
+                               int64_t B, int64_t H, hipStream_t stream, const void *v2 = nullptr,
+                               void *out2 = nullptr);
 // with out2: also out2 = v2 * conv(u w, k) from the same transforms (v and v2 non-null)
 hipError_t launch_pair_conv(int logn, int st, const void *u, const void *w, const void *v,
                             void *out, const void *kbins, const float *kscale, const uint8_t *mask,

@@ -124,11 +124,16 @@ using namespace p16;
 // XCD-local range of pairs p = h * ceil(B/2) + bp.  An odd B pairs its last row
 // with zeros: the second row's loads then re-read the first row (always in
 // bounds) and are discarded, so no load sits under a branch.
-template <typename T, bool MASKED, bool HAS_W, bool HAS_V>
+// DUAL: a second output out2 = v2 * conv(u w, k) from the same transforms (the backward
+// pass forms du and dw in one call); the second gate's rows are loaded once the staged
+// outputs have freed their registers.
+template <typename T, bool MASKED, bool HAS_W, bool HAS_V, bool DUAL = false>
 __global__ void __launch_bounds__(64 * kWaves, 1)
 pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restrict__ v,
                T *__restrict__ out, const uint4 *__restrict__ kbins, const float *__restrict__ kscale,
-               const uint8_t *__restrict__ mask, Pair3Tables tb, int64_t B, int64_t H) {
+               const uint8_t *__restrict__ mask, Pair3Tables tb, int64_t B, int64_t H,
+               const T *__restrict__ v2, T *__restrict__ out2) {
+    static_assert(!DUAL || HAS_V, "a second output has an output gate of its own");
     constexpr int N = 16384;
     constexpr int M2 = 2 * N;
     extern __shared__ __align__(16) _Float16 smem[];
@@ -464,8 +469,16 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                 stu(s8, o, ya[tt]);                                     // row n_c = c of sequence a
                 stu(s8 + 2 * kR1Plane, o, yb[tt]);                      // plane 1: sequence b
             }
+            uint4 vq2[8];
+            if (DUAL) {   // (issued before the next input batch: vmcnt waits are in order)
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    vq2[k] = ldu_nt<uint4>(v2 + (k < 4 ? oa : ob) + 4096 * (k & 3), 2 * m4);
+            }
+            __builtin_amdgcn_sched_barrier(0);
             // the second input batch of the next pair is fetched while the outputs are stored
             load_batch(oa_nx, ob_nx, 1, x1);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 // without a second row (ob == oa) its stores repeat the first row's values
@@ -473,6 +486,18 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                 const char *src = s8 + 2 * ((kk >> 2) * kR1Plane + (kk & 3) * 8192);
                 const f4 y0 = ldu<f4>(src, st_r0), y1 = ldu<f4>(src, st_r1);
                 float yv[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+                if (DUAL) {
+                    float ga[4], gb[4], y2[8];
+                    st<T>::unpack4(make_uint2(vq2[k].x, vq2[k].y), ga);
+                    st<T>::unpack4(make_uint2(vq2[k].z, vq2[k].w), gb);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        y2[i] = yv[i] * ga[i];
+                        y2[4 + i] = yv[4 + i] * gb[i];
+                    }
+                    const uint2 lo2 = st<T>::pack4(y2), hi2 = st<T>::pack4(y2 + 4);
+                    stu_nt(out2 + (k < 4 ? oa : ob) + 4096 * (k & 3), 2 * m4, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
+                }
                 if (HAS_V) {
                     float ga[4], gb[4];
                     st<T>::unpack4(make_uint2(vq[k].x, vq[k].y), ga);
@@ -496,7 +521,8 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
 
 hipError_t launch_pair16k_conv(int st_, const void *u, const void *w, const void *v, void *out,
                                const void *kbins, const float *kscale, const uint8_t *mask,
-                               int64_t B, int64_t H, hipStream_t stream) {
+                               int64_t B, int64_t H, hipStream_t stream, const void *v2, void *out2) {
+    if (out2 != nullptr && (v == nullptr || v2 == nullptr)) return hipErrorInvalidValue;
     Pair3Tables tb{};
     hipError_t e = get_pair3_tables(&tb);
     if (e != hipSuccess) return e;
@@ -518,12 +544,20 @@ hipError_t launch_pair16k_conv(int st_, const void *u, const void *w, const void
         if (err != hipSuccess) return err;
         hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * kWaves), lds, stream, (const TT *)u,
                            (const TT *)w, (const TT *)v, (TT *)out, (const uint4 *)kbins, kscale, mask, tb,
-                           B, H);
+                           B, H, (const TT *)v2, (TT *)out2);
         return hipGetLastError();
     };
     // one instantiation per (storage type, mask, gates) so that no gate test sits in the loops
     auto pick = [&](auto *tp) -> hipError_t {
         using TT = std::remove_pointer_t<decltype(tp)>;
+        if (out2 != nullptr) {   // two outputs: both output gates present
+            switch ((mask ? 2 : 0) | (w ? 1 : 0)) {
+            case 0: return go(pair16k_kernel<TT, false, false, true, true>, tp);
+            case 1: return go(pair16k_kernel<TT, false, true, true, true>, tp);
+            case 2: return go(pair16k_kernel<TT, true, false, true, true>, tp);
+            default: return go(pair16k_kernel<TT, true, true, true, true>, tp);
+            }
+        }
         const int sel = (mask ? 4 : 0) | (w ? 2 : 0) | (v ? 1 : 0);
         switch (sel) {
         case 0: return go(pair16k_kernel<TT, false, false, false>, tp);

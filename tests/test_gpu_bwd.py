@@ -115,6 +115,19 @@ def test_bwd_n1024_many_channels(dtype):
     _check(got, want, TOL[dtype])
 
 
+@pytest.mark.parametrize("gates", ["w", "both"])
+def test_bwd_n16384_channels(gates):
+    # N = 16384: du and dw come from one kernel call; an odd batch (the last pair has one
+    # sequence), enough channels for the per-XCD channel split, with and without the
+    # input gate v
+    B, H, N = 3, 9, 16384
+    _say(f"bwd N={N} B={B} H={H} gates={gates}")
+    inp, dy = _case(B, H, N, N, "f16", gates, seed=163)
+    got = _run(inp, dy)
+    want = oracle.fft_bwd(inp.f64("u"), inp.f64("k"), dy.double().numpy(), inp.f64("w"), inp.f64("v"))
+    _check(got, want, TOL["f16"])
+
+
 def test_bwd_workload_full_size():
     # the backward benchmark's configuration (gated_fp16_n1k: B = 64, H = 768, N = 1024,
     # the same dy recipe), every gradient compared whole against the oracle
