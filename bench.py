@@ -1,6 +1,6 @@
 """Benchmark: one step = one fftconv_fwd call over a whole synthetic batch.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass fwd|bwd]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass fwd|bwd|taps]
 
 Prints ONE JSON line (stdout).  The default workload is gated_fp16_n1k
 (B=64, H=768, N=1024, fp16 storage, gated, filter as long as the sequence).
@@ -13,7 +13,9 @@ cpu_baseline object times the CPU oracle (route F) on a bounded sample of the
 same workload on this host's cores.
 
 With --pass bwd one step is one fftconv_bwd call (du, dk, dw, dv) instead;
-that line names its own metric and carries no CPU baseline.
+with --pass taps one fftconv_fwd_taps call (the filter transformed from its L
+time-domain taps inside the call).  Those lines name their own metric and carry
+no CPU baseline.
 """
 from __future__ import annotations
 
@@ -155,8 +157,9 @@ def main():
     ap.add_argument("--workload", default="gated_fp16_n1k",
                     choices=sorted(synth.WORKLOADS) + sorted(synth.EQ_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd",
-                    help="time the forward call (default) or the backward call")
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd", "taps"], default="fwd",
+                    help="time the forward call (default), the backward call, or the forward "
+                         "call from time-domain taps")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain device copy of the activation bytes (counter scale)")
     args = ap.parse_args()
@@ -199,6 +202,11 @@ def main():
             log("bench: the short-filter path has no backward pass")
             return 2
         return bench_bwd(args, wl, dev, u, K_f, w, v, mask)
+    if args.which == "taps":
+        if wl.short:
+            log("bench: the short-filter path takes its taps' spectrum from its own prepare")
+            return 2
+        return bench_taps(args, wl, dev, u, k, w, v, mask)
 
     n_warm = warm_up(step, args.warmup, dev)
     log(f"bench: {n_warm} warm-up steps")
@@ -377,6 +385,59 @@ def bench_bwd(args, wl, dev, u, K_f, w, v, mask):
         "roofline": {"bound": "hbm", "kernel": "fftconv_bwd (several launches)", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": None, "algorithmic_bytes": alg, "kernel_ms": ms_per_step},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def bench_taps(args, wl, dev, u, k, w, v, mask):
+    """One step = one fftconv_fwd_taps call: the spectrum of the L taps is formed inside
+    the call (into its workspace), then the forward kernels run on it."""
+    out = torch.empty_like(u)
+    ws = torch.empty(fc.fftconv_fwd_taps_workspace_bytes(wl.B, wl.H, wl.N, u.dtype), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        fc.fftconv_fwd_taps(u, k, w, v, out, ws, mask)
+
+    n_warm = warm_up(step, args.warmup, dev)
+    log(f"bench: {n_warm} warm-up steps")
+    stream = torch.cuda.current_stream(dev)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    elems = wl.B * wl.H * wl.N
+    e = ELEM[wl.dtype]
+    # the forward call's bytes with the L taps read in place of the spectrum
+    alg = wl.B * wl.H * wl.N * e * (4 if wl.gated else 2) + wl.H * wl.L * e
+    achieved = alg / (ms_per_step / 1e3) / 1e9
+    log(f"bench: taps {ms_per_step * 1e3:.1f} us/step, {elems / (ms_per_step / 1e3):.3e} elems/s")
+    rec = {
+        "metric": "FFT-conv fwd from time-domain taps B·H·N elems/s, 1 GPU",
+        "value": elems / (ms_per_step / 1e3),
+        "unit": "elems/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": path_of(wl)[1],
+        "data": "synthetic (seeded N(0,1) activations, decaying random filter)",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "L_filter": wl.L,
+                   "gated": wl.gated, "storage": wl.dtype,
+                   "mask_keep_blocks": wl.mask_keep_blocks, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "fftconv_fwd_taps (prepare and forward launches)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes": alg,
+                     "kernel_ms": ms_per_step},
         "cpu_baseline": None,
     }
     print(json.dumps(rec), flush=True)

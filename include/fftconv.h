@@ -116,6 +116,33 @@ fftconv_status_t fftconv_fwd(const void *u, const void *K_f, const void *w, cons
                              const uint8_t *sparsity_mask, fftconv_dtype_t dtype,
                              void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Device scratch bytes fftconv_fwd_taps needs: the prepared spectrum of the
+ * H filters (fftconv_filter_bytes, rounded up to 256 bytes) followed by the
+ * larger of the prepare's and the forward call's scratch.  0 for unsupported
+ * N or dtype, H < 1 or B < 0. */
+size_t fftconv_fwd_taps_workspace_bytes(int64_t B, int64_t H, int64_t N, fftconv_dtype_t dtype);
+
+/* Forward call from the time-domain filter ("Approach", FlashFFTConv summary
+ * page: a partial convolution's filter has fewer taps than the sequence, and
+ * only the blocks that hold taps are transformed).  Equivalent to
+ * fftconv_prepare_filter(k -> a spectrum in the workspace) followed by
+ * fftconv_fwd on it, both enqueued on `stream` by this one call, so the
+ * caller keeps no prepared filter; the results equal that pair of calls bit
+ * for bit.
+ *   k         (H, L_filter) device array of taps, same dtype as u, read only
+ *   u, w, v, out, sparsity_mask  as in fftconv_fwd; w, v may be NULL
+ *   workspace device scratch of fftconv_fwd_taps_workspace_bytes bytes,
+ *             16-byte aligned, overlapping no argument; it holds the spectrum
+ *             until the forward kernels have read it, so it must not be reused
+ *             by another stream before this call's work completes
+ * Errors as fftconv_prepare_filter and fftconv_fwd, plus
+ * FFTCONV_ERR_WORKSPACE for a short workspace.  B = 0 or H = 0: nothing is
+ * enqueued. */
+fftconv_status_t fftconv_fwd_taps(const void *u, const void *k, const void *w, const void *v,
+                                  void *out, int64_t B, int64_t H, int64_t N, int64_t L_filter,
+                                  const uint8_t *sparsity_mask, fftconv_dtype_t dtype,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Device scratch bytes fftconv_bwd needs for this shape (0 for unsupported
  * N or dtype).  It holds the conjugated spectrum, u*w, the spectra of the
  * B*H sequences u*w, their correlations with v*dy, and the forward

@@ -55,6 +55,10 @@ def _load():
     lib.fftconv_prepare_filter.restype = ctypes.c_int
     lib.fftconv_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, ctypes.c_int, vp, sz, vp]
     lib.fftconv_fwd.restype = ctypes.c_int
+    lib.fftconv_fwd_taps_workspace_bytes.argtypes = [i64, i64, i64, ctypes.c_int]
+    lib.fftconv_fwd_taps_workspace_bytes.restype = sz
+    lib.fftconv_fwd_taps.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, ctypes.c_int, vp, sz, vp]
+    lib.fftconv_fwd_taps.restype = ctypes.c_int
     lib.fftconv_bwd_workspace_bytes.argtypes = [i64, i64, i64, ctypes.c_int]
     lib.fftconv_bwd_workspace_bytes.restype = sz
     lib.fftconv_bwd.argtypes = [vp] * 9 + [i64, i64, i64, i64, vp, ctypes.c_int, vp, sz, vp]
@@ -161,6 +165,26 @@ def fftconv_fwd(u: torch.Tensor, K_f: torch.Tensor, w: torch.Tensor | None,
     B, H, N = u.shape
     _check(_load().fftconv_fwd(
         _ptr(u), _ptr(K_f), _ptr(w), _ptr(v), _ptr(out), B, H, N, L_filter, _ptr(sparsity_mask),
+        dtype_code(u.dtype), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(stream, u.device)))
+
+
+def fftconv_fwd_taps_workspace_bytes(B: int, H: int, N: int, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    return int(_load().fftconv_fwd_taps_workspace_bytes(B, H, N, code))
+
+
+def fftconv_fwd_taps(u: torch.Tensor, k: torch.Tensor, w: torch.Tensor | None,
+                     v: torch.Tensor | None, out: torch.Tensor, workspace: torch.Tensor,
+                     sparsity_mask: torch.Tensor | None = None, stream=None) -> None:
+    """out <- v * causal_conv(u * w, k) from the (H, L) taps k, transformed within the call."""
+    for name, t in (("u", u), ("k", k), ("w", w), ("v", v), ("out", out),
+                    ("sparsity_mask", sparsity_mask), ("workspace", workspace)):
+        _dev_tensor(t, name)
+    B, H, N = u.shape
+    _check(_load().fftconv_fwd_taps(
+        _ptr(u), _ptr(k), _ptr(w), _ptr(v), _ptr(out), B, H, N, k.shape[1], _ptr(sparsity_mask),
         dtype_code(u.dtype), _ptr(workspace),
         0 if workspace is None else workspace.numel() * workspace.element_size(),
         _stream(stream, u.device)))

@@ -453,11 +453,12 @@ static fftconv_status_t prepare_impl(const void *k, int64_t H, int64_t L, int64_
     return ok();
 }
 
-fftconv_status_t fftconv_fwd(const void *u, const void *K_f, const void *w, const void *v,
-                             void *out, int64_t B, int64_t H, int64_t N, int64_t L,
-                             const uint8_t *mask, fftconv_dtype_t dtype, void *workspace,
-                             size_t workspace_bytes, hipStream_t stream) {
-    g_last_error.clear();
+// The forward call's argument checks; FFTCONV_OK with an empty g_last_error when the call
+// has work to enqueue, FFTCONV_OK with `*empty` set when B * H = 0.
+static fftconv_status_t fwd_args(const void *u, const void *K_f, const void *w, const void *v, void *out,
+                                 int64_t B, int64_t H, int64_t N, int64_t L, const uint8_t *mask,
+                                 fftconv_dtype_t dtype, void *workspace, size_t workspace_bytes, bool *empty) {
+    *empty = false;
     if (!dtype_ok(dtype)) return fail(FFTCONV_ERR_UNSUPPORTED, "dtype %d is not supported", (int)dtype);
     const int l = log2_exact(N);
     if (l < kMinLog || l > kMaxLog)
@@ -469,7 +470,10 @@ fftconv_status_t fftconv_fwd(const void *u, const void *K_f, const void *w, cons
     if (L < 1 || L > N)
         return fail(FFTCONV_ERR_INVALID_ARGUMENT, "L_filter=%lld must be in [1, N=%lld]",
                     (long long)L, (long long)N);
-    if (B * H == 0) return ok();
+    if (B * H == 0) {
+        *empty = true;
+        return ok();
+    }
     if (!u || !K_f || !out) return fail(FFTCONV_ERR_INVALID_ARGUMENT, "u, K_f and out must be non-null");
     if (!aligned16(u) || !aligned16(K_f) || !aligned16(out) || (w && !aligned16(w)) ||
         (v && !aligned16(v)) || (mask && !aligned16(mask)))
@@ -487,6 +491,20 @@ fftconv_status_t fftconv_fwd(const void *u, const void *K_f, const void *w, cons
         return fail(FFTCONV_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
     if (wneed > 0 && (overlap(workspace, wneed, out, nbytes) || overlap(workspace, wneed, u, nbytes)))
         return fail(FFTCONV_ERR_INVALID_ARGUMENT, "workspace overlaps a tensor");
+    return FFTCONV_OK;
+}
+
+fftconv_status_t fftconv_fwd(const void *u, const void *K_f, const void *w, const void *v,
+                             void *out, int64_t B, int64_t H, int64_t N, int64_t L,
+                             const uint8_t *mask, fftconv_dtype_t dtype, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+    g_last_error.clear();
+    bool empty = false;
+    const fftconv_status_t chk_st =
+        fwd_args(u, K_f, w, v, out, B, H, N, L, mask, dtype, workspace, workspace_bytes, &empty);
+    if (chk_st != FFTCONV_OK || empty) return chk_st;
+    const int l = log2_exact(N);
+    const size_t kfb = fftconv_filter_bytes(H, N, dtype);
 
     const char *chk = std::getenv("FFTCONV_CHECK");
     if (chk && chk[0] == '1') {
@@ -688,6 +706,61 @@ fftconv_status_t fftconv_bwd(const void *dy, const void *u, const void *K_f, con
     }
     g_last_error.clear();
     return ok();
+}
+
+// ---- forward from time-domain taps ------------------------------------------
+// The spectrum is prepared into the head of the workspace on the call's stream, then
+// the forward call reads it; the remaining workspace serves both as scratch (they run
+// one after the other on the stream).
+static size_t round_up256(size_t n) { return (n + 255) & ~size_t(255); }
+
+size_t fftconv_fwd_taps_workspace_bytes(int64_t B, int64_t H, int64_t N, fftconv_dtype_t dtype) {
+    const size_t kf = fftconv_filter_bytes(H, N, dtype);
+    if (kf == 0 || B < 0) return 0;
+    const size_t a = fftconv_workspace_bytes(1, H, N, dtype), b = fftconv_workspace_bytes(B, H, N, dtype);
+    return round_up256(kf) + (a > b ? a : b);
+}
+
+fftconv_status_t fftconv_fwd_taps(const void *u, const void *k, const void *w, const void *v, void *out,
+                                  int64_t B, int64_t H, int64_t N, int64_t L, const uint8_t *mask,
+                                  fftconv_dtype_t dtype, void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+    g_last_error.clear();
+    if (!dtype_ok(dtype)) return fail(FFTCONV_ERR_UNSUPPORTED, "dtype %d is not supported", (int)dtype);
+    const int l = log2_exact(N);
+    if (l < kMinLog || l > kMaxLog)
+        return fail(FFTCONV_ERR_UNSUPPORTED, "N=%lld must be a power of two in [2^%d, 2^%d]",
+                    (long long)N, kMinLog, kMaxLog);
+    if (B < 0 || H < 0)
+        return fail(FFTCONV_ERR_INVALID_ARGUMENT, "B=%lld and H=%lld must be >= 0", (long long)B,
+                    (long long)H);
+    if (L < 1 || L > N)
+        return fail(FFTCONV_ERR_INVALID_ARGUMENT, "L_filter=%lld must be in [1, N=%lld]",
+                    (long long)L, (long long)N);
+    if (B * H == 0) return ok();
+    if (!k) return fail(FFTCONV_ERR_INVALID_ARGUMENT, "k must be non-null");
+    const size_t need = fftconv_fwd_taps_workspace_bytes(B, H, N, dtype);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(FFTCONV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    if (!aligned16(workspace) || !aligned16(k))
+        return fail(FFTCONV_ERR_INVALID_ARGUMENT, "k and workspace must be 16-byte aligned");
+    const size_t nbytes = (size_t)B * (size_t)H * (size_t)N * elem_bytes(dtype);
+    const size_t kbytes = (size_t)H * (size_t)L * elem_bytes(dtype);
+    if (overlap(workspace, need, k, kbytes) || overlap(workspace, need, u, nbytes) ||
+        overlap(workspace, need, w, nbytes) || overlap(workspace, need, v, nbytes) ||
+        overlap(workspace, need, out, nbytes) || overlap(workspace, need, mask, (size_t)H * kMaskBlocks))
+        return fail(FFTCONV_ERR_INVALID_ARGUMENT, "workspace overlaps an argument");
+    if (overlap(out, nbytes, k, kbytes)) return fail(FFTCONV_ERR_INVALID_ARGUMENT, "out overlaps k");
+    char *ws = static_cast<char *>(workspace);
+    const size_t kf = round_up256(fftconv_filter_bytes(H, N, dtype));
+    bool empty = false;
+    fftconv_status_t chk_st =
+        fwd_args(u, ws, w, v, out, B, H, N, L, mask, dtype, ws + kf, workspace_bytes - kf, &empty);
+    if (chk_st != FFTCONV_OK) return chk_st;
+    const fftconv_status_t st =
+        prepare_impl(k, H, L, N, dtype, ws, kf, ws + kf, workspace_bytes - kf, false, stream);
+    if (st != FFTCONV_OK) return st;
+    return fftconv_fwd(u, ws, w, v, out, B, H, N, L, mask, dtype, ws + kf, workspace_bytes - kf, stream);
 }
 
 // ---- chunked short-filter path ---------------------------------------------

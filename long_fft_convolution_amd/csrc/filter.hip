@@ -15,26 +15,60 @@
 
 namespace fftconv {
 
+// sum of |x| over the 16 / sizeof(T) values of one 16-byte word
+template <typename T> __device__ __forceinline__ float sum_abs16(const uint4 &q) {
+    const T *e = reinterpret_cast<const T *>(&q);
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < (int)(16 / sizeof(T)); ++j) s += fabsf(io<T>::load1(e + j));
+    return s;
+}
+
+constexpr int kScaleThreads = 1024;
+
+// One workgroup per channel.  The row is read as 16-byte words from its first 16-byte
+// boundary (rows of odd length start unaligned), four words in flight per thread; the
+// few values before that boundary and after the last whole word are read one by one.
+// The summation order is fixed, so the scale does not vary from call to call.
 template <typename T>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kScaleThreads)
 filter_scale_kernel(const T *__restrict__ k, int64_t L, int norm_log2, int target_log2, bool unit,
                     float *__restrict__ kscale) {
-    __shared__ float part[256];
+    __shared__ float part[kScaleThreads / 64];
     const int64_t h = blockIdx.x;
-    float s = 0.f;
+    const int tid = threadIdx.x;
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
     if (!unit) {
+        constexpr int E = 16 / sizeof(T);
         const T *row = k + h * L;
-        for (int64_t t = threadIdx.x; t < L; t += 256) s += fabsf(io<T>::load1(row + t));
+        // rows start at multiples of sizeof(T): the head holds fewer than E values
+        int64_t head = (int64_t)(((16u - (uint32_t)(reinterpret_cast<uintptr_t>(row) & 15u)) & 15u) / sizeof(T));
+        if (head > L) head = L;
+        const int64_t nv = (L - head) / E;
+        const uint4 *vec = reinterpret_cast<const uint4 *>(row + head);
+        int64_t i = tid;
+        for (; i + 3 * kScaleThreads < nv; i += 4 * kScaleThreads) {
+            const uint4 q0 = vec[i], q1 = vec[i + kScaleThreads], q2 = vec[i + 2 * kScaleThreads],
+                        q3 = vec[i + 3 * kScaleThreads];
+            s0 += sum_abs16<T>(q0);
+            s1 += sum_abs16<T>(q1);
+            s2 += sum_abs16<T>(q2);
+            s3 += sum_abs16<T>(q3);
+        }
+        for (; i < nv; i += kScaleThreads) s0 += sum_abs16<T>(vec[i]);
+        if (tid < head) s1 += fabsf(io<T>::load1(row + tid));
+        const int64_t t1 = head + nv * E + tid;   // the tail: fewer than E values
+        if (t1 < L) s2 += fabsf(io<T>::load1(row + t1));
     }
-    part[threadIdx.x] = s;
+    float s = (s0 + s1) + (s2 + s3);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    if ((tid & 63) == 0) part[tid >> 6] = s;
     __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-        if ((int)threadIdx.x < o) part[threadIdx.x] += part[threadIdx.x + o];
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) {
+    if (tid == 0) {
+        float tot = 0.f;
+        for (int j = 0; j < kScaleThreads / 64; ++j) tot += part[j];
         int e = 0;
-        const float tot = part[0];
         if (!unit && tot > 0.f && isfinite(tot)) {
             e = (int)floorf(log2f(ldexpf(1.0f, target_log2) / tot));
             e = e < -60 ? -60 : (e > 60 ? 60 : e);
@@ -53,15 +87,15 @@ hipError_t launch_filter_scale(int st, const void *k, int64_t H, int64_t L, int 
     const bool unit = st == ST_F32;
     switch (st) {
     case ST_F32:
-        hipLaunchKernelGGL(filter_scale_kernel<float>, dim3((unsigned)H), dim3(256), 0, stream,
+        hipLaunchKernelGGL(filter_scale_kernel<float>, dim3((unsigned)H), dim3(kScaleThreads), 0, stream,
                            (const float *)k, L, norm_log2, target_log2, unit, kscale);
         break;
     case ST_F16:
-        hipLaunchKernelGGL(filter_scale_kernel<__half>, dim3((unsigned)H), dim3(256), 0, stream,
+        hipLaunchKernelGGL(filter_scale_kernel<__half>, dim3((unsigned)H), dim3(kScaleThreads), 0, stream,
                            (const __half *)k, L, norm_log2, target_log2, unit, kscale);
         break;
     default:
-        hipLaunchKernelGGL(filter_scale_kernel<__hip_bfloat16>, dim3((unsigned)H), dim3(256), 0,
+        hipLaunchKernelGGL(filter_scale_kernel<__hip_bfloat16>, dim3((unsigned)H), dim3(kScaleThreads), 0,
                            stream, (const __hip_bfloat16 *)k, L, norm_log2, target_log2, unit, kscale);
     }
     return hipGetLastError();

@@ -236,3 +236,40 @@ def test_eqlinear_abi():
     assert fwd(N=0, x=None, y=None) == 0
     assert fwd(y=0x400008) == 1 and "aligned" in fc.fftconv_last_error()
     assert fwd(y=0x10000 + 64) == 1 and "overlaps" in fc.fftconv_last_error()
+
+
+def test_fwd_taps_abi():
+    # forward from time-domain taps: the workspace holds the spectrum and the scratch;
+    # every rejection below happens before anything is enqueued
+    lib = fc.lib()
+    F16 = fc.FFTCONV_F16
+    H, N = 3, 1 << 20
+    kf = (fc.fftconv_filter_bytes(H, N, F16) + 255) // 256 * 256
+    need = fc.fftconv_fwd_taps_workspace_bytes(2, H, N, F16)
+    assert need == kf + max(fc.fftconv_workspace_bytes(1, H, N, F16), fc.fftconv_workspace_bytes(2, H, N, F16))
+    assert fc.fftconv_fwd_taps_workspace_bytes(2, H, 1024, F16) == (fc.fftconv_filter_bytes(H, 1024, F16) + 255) // 256 * 256
+    assert fc.fftconv_fwd_taps_workspace_bytes(2, H, 1000, F16) == 0
+    assert fc.fftconv_fwd_taps_workspace_bytes(-1, H, N, F16) == 0
+    assert fc.fftconv_fwd_taps_workspace_bytes(2, 0, N, F16) == 0
+    good = dict(u=0x100000, k=0x200000, w=None, v=None, out=0x40000000, B=2, H=H, N=N, L=1000, m=None,
+                dt=F16, ws=0x80000000, wsb=need)
+
+    def call(**kw):
+        a = dict(good)
+        a.update(kw)
+        return lib.fftconv_fwd_taps(a["u"], a["k"], a["w"], a["v"], a["out"], a["B"], a["H"], a["N"], a["L"],
+                                    a["m"], a["dt"], a["ws"], a["wsb"], None)
+
+    assert call(dt=7) == 2
+    assert call(N=1000) == 2
+    assert call(L=0) == 1 and call(L=N + 1) == 1
+    assert call(B=-1) == 1
+    assert call(B=0) == 0 and call(H=0) == 0
+    assert call(k=None) == 1
+    assert call(ws=None) == 3 and call(wsb=need - 1) == 3
+    assert call(ws=0x80000004) == 1 and "aligned" in fc.fftconv_last_error()
+    assert call(k=0x80000000 + 4096) == 1 and "overlaps" in fc.fftconv_last_error()
+    assert call(out=0x200000 + 64) == 1 and "overlaps" in fc.fftconv_last_error()
+    # the forward call's own checks also run before the prepare is enqueued
+    assert call(u=0x100004) == 1 and "aligned" in fc.fftconv_last_error()
+    assert call(u=None) == 1
