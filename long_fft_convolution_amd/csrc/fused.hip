@@ -279,11 +279,19 @@ fused_prepare_kernel(const T *__restrict__ k, int64_t L, TK *__restrict__ kbins,
     dft_inplace<R>(Bv);
     if (!valid) return;
 
+    // N = 16384: the fp16 row (every slot of it is written below) is assembled in the
+    // LDS buffer, which is free once every lane holds its A, Bv, and stored as 16-byte
+    // words; stored directly, each bin would take four scattered 2-byte stores
+    constexpr bool STAGE = LAYOUT == KF_PAIR3;
+    static_assert(!STAGE || (Pl::SPW == 1 && 17 * 1024 * 4 <= Pl::NC * (int)sizeof(float2)),
+                  "one sequence per workgroup, its row fits the LDS buffer");
+    if (STAGE) __syncthreads();
     constexpr bool PAIR = LAYOUT != KF_NATURAL;
     // s_h = 1 / (scale[h] * norm), exact (both powers of two)
     const float sh = 1.0f / (kscale[h] * (float)(PAIR ? 2 * NC : 4 * NC));
     constexpr int64_t kRowSlots = LAYOUT == KF_PAIR3 ? 17 * 1024 : (PAIR ? 2 * NC : NC);
     TK *krow = kbins + h * kRowSlots;
+    _Float16 *const row16 = STAGE ? reinterpret_cast<_Float16 *>(lds) : reinterpret_cast<_Float16 *>(krow);
     // one real-spectrum bin: natural order, or a matrix-core kernel's lane
     // order (the Hermitian mirror 2N - f is stored as well where its row is)
     auto index_of = [](int64_t f) -> int64_t {
@@ -295,7 +303,7 @@ fused_prepare_kernel(const T *__restrict__ k, int64_t L, TK *__restrict__ kbins,
         if (!PAIR) {
             kio<TK>::store(krow + f, x);
         } else {
-            _Float16 *kh = reinterpret_cast<_Float16 *>(krow);
+            _Float16 *kh = row16;
             const int64_t a = index_of(f);
             if (a >= 0) {
                 kh[a] = (_Float16)x.x;
@@ -336,6 +344,12 @@ fused_prepare_kernel(const T *__restrict__ k, int64_t L, TK *__restrict__ kbins,
         for (int q = 1; q < R / 2; ++q) emit(A[q], A[R - q], q * P, true);
 #pragma unroll
         for (int q = 0; q < R / 2; ++q) emit(Bv[q], Bv[R - 1 - q], P / 2 + q * P, true);
+    }
+    if (STAGE) {
+        __syncthreads();
+        const uint4 *src = reinterpret_cast<const uint4 *>(lds);
+        uint4 *dst = reinterpret_cast<uint4 *>(krow);
+        for (int i = tid; i < (int)(kRowSlots * sizeof(TK) / 16); i += Pl::THREADS) dst[i] = src[i];
     }
 }
 
