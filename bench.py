@@ -348,7 +348,8 @@ def bench_bwd(args, wl, dev, u, K_f, w, v, mask):
     def step():
         fc.fftconv_bwd(dy, u, K_f, w, v, du, dk, dw, dv, wl.L, mask, ws)
 
-    warm_up(step, args.warmup, dev)
+    n_warm = warm_up(step, args.warmup, dev)
+    log(f"bench: {n_warm} warm-up steps")
     stream = torch.cuda.current_stream(dev)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
