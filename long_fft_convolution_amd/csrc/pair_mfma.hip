@@ -27,6 +27,7 @@
 // (persistent), prefetching the next pair's inputs, filter and gate chunks;
 // twiddles and two of the three DFT block sets live in LDS so that two
 // workgroups of four waves fit per CU.
+#include "cmfma.hpp"
 #include "fft_device.hpp"
 #include "fftconv_internal.hpp"
 
@@ -34,13 +35,16 @@
 
 namespace fftconv {
 
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-typedef float f4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
+using cmfma::f4;
+using cmfma::h4;
+using cmfma::h8;
+using cmfma::cat8;
+using cmfma::cmul4;
+using cmfma::hi4;
+using cmfma::lo4;
+using cmfma::mfma;
+using cmfma::neg8;
+using cmfma::to_h4;
 
 // 8 consecutive storage elements -> fp32
 template <typename T> struct io8;
@@ -192,36 +196,6 @@ __device__ __forceinline__ h8 xor8(const h8 &a, uint32_t m) {
     q.z ^= m;
     q.w ^= m;
     return *reinterpret_cast<const h8 *>(&q);
-}
-
-// sign flip of eight fp16 values: one integer xor per register
-__device__ __forceinline__ h8 neg8(const h8 &a) {
-    uint4 q = *reinterpret_cast<const uint4 *>(&a);
-    q.x ^= 0x80008000u;
-    q.y ^= 0x80008000u;
-    q.z ^= 0x80008000u;
-    q.w ^= 0x80008000u;
-    return *reinterpret_cast<const h8 *>(&q);
-}
-
-__device__ __forceinline__ h4 to_h4(const f4 &a) {
-    h4 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = (_Float16)a[i];
-    return r;
-}
-__device__ __forceinline__ h8 cat8(const h4 &lo, const h4 &hi) {
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-__device__ __forceinline__ h4 lo4(const h8 &a) { return __builtin_shufflevector(a, a, 0, 1, 2, 3); }
-__device__ __forceinline__ h4 hi4(const h8 &a) { return __builtin_shufflevector(a, a, 4, 5, 6, 7); }
-
-// (re, im) <- (re, im) * (c + i s), four values, packed fp16; t = {c[0..3], s[0..3]}
-__device__ __forceinline__ void cmul4(h4 &re, h4 &im, const h8 &t) {
-    const h4 c = lo4(t), s = hi4(t);
-    const h4 r = re * c - im * s;
-    im = re * s + im * c;
-    re = r;
 }
 
 // x = u * w as eight fp16 values (w absent: x = u).  fp16 storage: one packed

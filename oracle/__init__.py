@@ -268,9 +268,35 @@ def fft_bwd(u, k, dy, w=None, v=None, mask=None, lib=None):
 
 
 def rel_l2(a, b) -> float:
-    """||a - b||_2 / ||b||_2 in float64 (b is the oracle's value)."""
+    """||a - b||_2 / ||b||_2 in float64 (b is the oracle's value); ||a - b||_2
+    when b is all zero."""
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
     den = np.sqrt(np.sum(b * b))
     num = np.sqrt(np.sum((a - b) ** 2))
     return float(num / den) if den > 0 else float(num)
+
+
+def seq_rel_l2(a, b) -> np.ndarray:
+    """rel_l2 of every sequence: the last axis is the sequence, the leading axes
+    (for a (B, H, N) tensor: b and h) are flattened.  One value per sequence, in
+    row-major order of the leading axes; a 1-D input is one sequence."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    if a.shape != b.shape:
+        raise ValueError(f"shape mismatch {a.shape} vs {b.shape}")
+    n = a.shape[-1] if a.ndim else 1
+    a2 = a.reshape(-1, n)
+    b2 = b.reshape(-1, n)
+    den = np.sqrt(np.sum(b2 * b2, axis=1))
+    num = np.sqrt(np.sum((a2 - b2) ** 2, axis=1))
+    return np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
+
+
+def max_abs(a, b) -> float:
+    """max |a - b| over all elements (0 for empty inputs)."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    if a.shape != b.shape:
+        raise ValueError(f"shape mismatch {a.shape} vs {b.shape}")
+    return float(np.max(np.abs(a - b))) if a.size else 0.0

@@ -10,8 +10,8 @@ import pytest
 import torch
 
 import long_fft_convolution_amd as fc
-from oracle import rel_l2
 from oracle.eqlinear import eqlinear, eqlinear_tokens
+from parity import check
 
 pytestmark = pytest.mark.gpu
 
@@ -39,7 +39,7 @@ def test_eqlinear_parity(dtype, T, Ci, Co, N):
     y = fc.eqlinear(x.cuda(), W.cuda())
     torch.cuda.synchronize()
     ref = eqlinear(x.double().numpy(), W.double().numpy())
-    assert rel_l2(y.float().cpu().double().numpy(), ref) < TOL[dtype]
+    check(y.float().cpu().double().numpy(), ref, TOL[dtype])
 
 
 def test_eqlinear_equivariance_on_gpu():
@@ -49,7 +49,7 @@ def test_eqlinear_equivariance_on_gpu():
     xs = torch.roll(x, 3, dims=1)
     y = fc.eqlinear(x.cuda(), W.cuda()).float().cpu()
     ys = fc.eqlinear(xs.cuda(), W.cuda()).float().cpu()
-    assert rel_l2(ys.numpy(), torch.roll(y, 3, dims=1).numpy()) < 5e-3
+    check(ys.numpy(), torch.roll(y, 3, dims=1).numpy(), 5e-3)
 
 
 def test_eqlinear_bench_shape_sampled():
@@ -61,7 +61,7 @@ def test_eqlinear_bench_shape_sampled():
     toks = np.random.default_rng(0).choice(N, 300, replace=False)
     toks = np.concatenate([toks, [0, N - 1]])
     ref = eqlinear_tokens(x.double().numpy(), W.double().numpy(), toks)
-    assert rel_l2(y[toks], ref) < 5e-3
+    check(y[toks], ref, 5e-3)
 
 
 def test_eqlinear_empty():

@@ -15,6 +15,7 @@ import torch
 import oracle
 import long_fft_convolution_amd as fc
 from long_fft_convolution_amd import synth
+from parity import check
 
 pytestmark = pytest.mark.gpu
 
@@ -51,7 +52,7 @@ def test_fused_sizes_dtypes_ragged(logn, dtype):
     inp = synth.generate(B, H, N, N, dtype, gated=True, seed=logn * 10 + len(dtype))
     y = run_gpu(inp)
     ref = oracle_full(inp)
-    assert oracle.rel_l2(y, ref) < TOL[dtype]
+    check(y, ref, TOL[dtype])
 
 
 @pytest.mark.parametrize("L", [1, 17, 1000, 1024])
@@ -60,7 +61,7 @@ def test_fused_partial_filters_fp32(L):
     inp = synth.generate(2, 3, 1024, L, "f32", gated=False, decay="fixed0.01", seed=L)
     y = run_gpu(inp)
     ref = oracle.direct(inp.f64("u"), inp.f64("k"))
-    assert oracle.rel_l2(y, ref) < 1e-5
+    check(y, ref, 1e-5)
 
 
 def test_small_fp32_workload_full():
@@ -68,7 +69,7 @@ def test_small_fp32_workload_full():
     inp = synth.generate_workload("ungated_fp32_n1k")
     y = run_gpu(inp)
     ref = oracle.direct(inp.f64("u"), inp.f64("k"))
-    assert oracle.rel_l2(y, ref) < 1e-5
+    check(y, ref, 1e-5)
     assert np.max(np.abs(y - ref)) < 1e-4 * np.max(np.abs(ref))
 
 
@@ -82,7 +83,7 @@ def test_one_sided_gate(side):
         inp.w = None
     y = run_gpu(inp)
     ref = oracle.direct(inp.f64("u"), inp.f64("k"), inp.f64("w"), inp.f64("v"))
-    assert oracle.rel_l2(y, ref) < 1e-5
+    check(y, ref, 1e-5)
 
 
 @pytest.mark.parametrize("logn", [10, 14])
@@ -94,7 +95,7 @@ def test_fused_frequency_mask(logn, kind):
     mask = synth.band_mask(3, 27) if kind == "band" else synth.random_mask(3, seed=logn)
     y = run_gpu(inp, mask)
     ref = oracle_full(inp, mask)
-    assert oracle.rel_l2(y, ref) < 1e-5
+    check(y, ref, 1e-5)
 
 
 def test_delta_filter_is_identity_times_gates():
@@ -103,7 +104,7 @@ def test_delta_filter_is_identity_times_gates():
     inp.k = torch.ones_like(inp.k)
     y = run_gpu(inp)
     ref = inp.f64("v") * (inp.f64("u") * inp.f64("w"))
-    assert oracle.rel_l2(y, ref) < 1e-6
+    check(y, ref, 1e-6)
 
 
 def test_causality_on_gpu():
@@ -151,7 +152,7 @@ def test_pair_kernel_batches(B, H, dtype):
     inp = synth.generate(B, H, 1024, 1024, dtype, gated=True, seed=B * 100 + H)
     y = run_gpu(inp)
     ref = oracle_full(inp)
-    assert oracle.rel_l2(y, ref) < TOL[dtype]
+    check(y, ref, TOL[dtype])
 
 
 @pytest.mark.parametrize("gates", ["none", "w", "v"])
@@ -164,7 +165,7 @@ def test_pair_kernel_gates(gates):
         inp.v = None
     y = run_gpu(inp)
     ref = oracle.direct(inp.f64("u"), inp.f64("k"), inp.f64("w"), inp.f64("v"))
-    assert oracle.rel_l2(y, ref) < TOL["f16"]
+    check(y, ref, TOL["f16"])
 
 
 @pytest.mark.parametrize("kind", ["band", "random"])
@@ -174,7 +175,7 @@ def test_pair_kernel_mask(kind):
     mask = synth.band_mask(12, 27) if kind == "band" else synth.random_mask(12, seed=3)
     y = run_gpu(inp, mask)
     ref = oracle_full(inp, mask)
-    assert oracle.rel_l2(y, ref) < TOL["f16"]
+    check(y, ref, TOL["f16"])
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
@@ -206,7 +207,7 @@ def test_pair16k_gates_and_partial(gates, dtype, L):
         inp.v = None
     y = run_gpu(inp)
     ref = oracle.fft_conv(inp.f64("u"), inp.f64("k"), inp.f64("w"), inp.f64("v"))
-    assert oracle.rel_l2(y, ref) < TOL[dtype]
+    check(y, ref, TOL[dtype])
 
 
 @pytest.mark.parametrize("kind", ["band", "random"])
@@ -216,4 +217,4 @@ def test_pair16k_mask(kind):
     mask = synth.band_mask(3, 27) if kind == "band" else synth.random_mask(3, seed=7)
     y = run_gpu(inp, mask)
     ref = oracle_full(inp, mask)
-    assert oracle.rel_l2(y, ref) < TOL["f16"]
+    check(y, ref, TOL["f16"])

@@ -13,6 +13,7 @@ import torch
 import oracle
 import long_fft_convolution_amd as fc
 from long_fft_convolution_amd import synth
+from parity import check
 
 pytestmark = pytest.mark.gpu
 
@@ -42,7 +43,7 @@ def test_multipass_sizes_fp32(logn):
     inp = synth.generate(1, 2, N, N, "f32", gated=True, seed=logn)
     y = run_gpu(inp)
     ref = oracle.fft_conv(inp.f64("u"), inp.f64("k"), inp.f64("w"), inp.f64("v"))
-    assert oracle.rel_l2(y, ref) < TOL["f32"]
+    check(y, ref, TOL["f32"])
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
@@ -52,7 +53,7 @@ def test_multipass_half_dtypes(dtype):
     inp = synth.generate(2, 3, N, N, dtype, gated=True, seed=3)
     y = run_gpu(inp)
     ref = oracle.fft_conv(inp.f64("u"), inp.f64("k"), inp.f64("w"), inp.f64("v"))
-    assert oracle.rel_l2(y, ref) < TOL[dtype]
+    check(y, ref, TOL[dtype])
 
 
 @pytest.mark.parametrize("logn", [15, 16, 17, 18, 19, 20])
@@ -65,7 +66,7 @@ def test_multipass_sizes_half(logn, dtype):
     inp = synth.generate(1, 3, N, N, dtype, gated=True, seed=100 + logn)
     y = run_gpu(inp)
     ref = oracle.fft_conv(inp.f64("u"), inp.f64("k"), inp.f64("w"), inp.f64("v"))
-    assert oracle.rel_l2(y, ref) < TOL[dtype]
+    check(y, ref, TOL[dtype])
 
 
 @pytest.mark.parametrize("kind", ["band", "random"])
@@ -77,7 +78,7 @@ def test_multipass_mask_half(kind, dtype):
     mask = synth.band_mask(3, 27) if kind == "band" else synth.random_mask(3, seed=15)
     y = run_gpu(inp, mask)
     ref = oracle.fft_conv(inp.f64("u"), inp.f64("k"), mask=mask)
-    assert oracle.rel_l2(y, ref) < TOL[dtype]
+    check(y, ref, TOL[dtype])
 
 
 def test_multipass_chunks_half_ragged():
@@ -88,7 +89,7 @@ def test_multipass_chunks_half_ragged():
     inp = synth.generate(1, 515, N, 2048, "f16", gated=False, seed=24)
     y = run_gpu(inp)
     ref = oracle.fft_conv(inp.f64("u"), inp.f64("k"))
-    assert oracle.rel_l2(y, ref) < TOL["f16"]
+    check(y, ref, TOL["f16"])
 
 
 def test_multipass_chunks_and_ragged_tail():
@@ -100,7 +101,7 @@ def test_multipass_chunks_and_ragged_tail():
     inp = synth.generate(1, 131, N, 4096, "f32", gated=False, seed=4)
     y = run_gpu(inp)
     ref = oracle.fft_conv(inp.f64("u"), inp.f64("k"))
-    assert oracle.rel_l2(y, ref) < TOL["f32"]
+    check(y, ref, TOL["f32"])
 
 
 @pytest.mark.parametrize("L", [1, 777, 1 << 15])
@@ -110,7 +111,7 @@ def test_multipass_partial_filter(L):
     inp = synth.generate(1, 2, N, L, "f32", gated=False, seed=L)
     y = run_gpu(inp)
     ref = oracle.fft_conv(inp.f64("u"), inp.f64("k"))
-    assert oracle.rel_l2(y, ref) < TOL["f32"]
+    check(y, ref, TOL["f32"])
 
 
 @pytest.mark.parametrize("kind", ["band", "random"])
@@ -121,7 +122,7 @@ def test_multipass_mask(kind):
     mask = synth.band_mask(3, 27) if kind == "band" else synth.random_mask(3, seed=5)
     y = run_gpu(inp, mask)
     ref = oracle.fft_conv(inp.f64("u"), inp.f64("k"), mask=mask)
-    assert oracle.rel_l2(y, ref) < TOL["f32"]
+    check(y, ref, TOL["f32"])
 
 
 def test_multipass_prepared_spectrum():
@@ -147,4 +148,4 @@ def test_multipass_largest_size_masked_partial():
     inp = synth.generate(1, 2, N, 1 << 20, "f16", gated=False, seed=11, mask_keep_blocks=27)
     y = run_gpu(inp, inp.mask)
     ref = oracle.fft_conv(inp.f64("u"), inp.f64("k"), mask=inp.mask)
-    assert oracle.rel_l2(y, ref) < TOL["f16"]
+    check(y, ref, TOL["f16"])

@@ -19,6 +19,7 @@ import torch
 import oracle
 import long_fft_convolution_amd as fc
 from long_fft_convolution_amd import synth
+from parity import check
 
 pytestmark = pytest.mark.gpu
 
@@ -56,7 +57,7 @@ def _ref(inp):
 def test_short_filter_sizes(dtype, N, L):
     _say(f"short {dtype} N={N} L={L}")
     inp = synth.generate(3, 2, N, L, dtype, gated=True, seed=N + L)
-    assert oracle.rel_l2(_run(inp), _ref(inp)) < TOL[dtype]
+    check(_run(inp), _ref(inp), TOL[dtype])
 
 
 @pytest.mark.parametrize("gated", [False, True])
@@ -66,7 +67,7 @@ def test_short_filter_gates_and_batch(gated):
     inp = synth.generate(5, 3, N, L, "f16", gated=gated, seed=7)
     y = _run(inp)
     ref = _ref(inp)
-    assert oracle.rel_l2(y, ref) < TOL["f16"]
+    check(y, ref, TOL["f16"])
     # every window boundary is exact: the error is flat along the sequence
     err = np.abs(y - ref).reshape(5, 3, N // 1024, 1024).max(axis=(0, 1, 3))
     scale = np.abs(ref).max()
@@ -77,7 +78,7 @@ def test_short_filter_long_sequence():
     N, L = 1 << 20, 1024
     _say(f"short N={N} L={L} H=2")
     inp = synth.generate(1, 2, N, L, "f16", gated=False, seed=21)
-    assert oracle.rel_l2(_run(inp), _ref(inp)) < TOL["f16"]
+    check(_run(inp), _ref(inp), TOL["f16"])
 
 
 def test_short_filter_matches_full_path():
@@ -88,9 +89,9 @@ def test_short_filter_matches_full_path():
     y_short = _run(inp)
     y_full = fc.causal_conv(_dev(inp.u), _dev(inp.k), _dev(inp.w), _dev(inp.v)).float().cpu().double().numpy()
     ref = _ref(inp)
-    assert oracle.rel_l2(y_short, ref) < TOL["f16"]
-    assert oracle.rel_l2(y_full, ref) < TOL["f16"]
-    assert oracle.rel_l2(y_short, y_full) < 2 * TOL["f16"]
+    check(y_short, ref, TOL["f16"])
+    check(y_full, ref, TOL["f16"])
+    check(y_short, y_full, 2 * TOL["f16"])
 
 
 def test_short_filter_empty_batch():

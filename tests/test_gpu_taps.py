@@ -16,6 +16,7 @@ import torch
 import oracle
 import long_fft_convolution_amd as fc
 from long_fft_convolution_amd import synth
+from parity import check
 
 pytestmark = pytest.mark.gpu
 
@@ -55,7 +56,7 @@ def test_taps_matches_prepared_and_oracle(dtype, B, H, N, L, gated):
     torch.cuda.synchronize()
     assert torch.equal(got, want_gpu)
     ref = oracle.fft_conv(inp.f64("u"), inp.f64("k"), inp.f64("w"), inp.f64("v"))
-    assert oracle.rel_l2(got.float().cpu().double().numpy(), ref) < TOL[dtype]
+    check(got.float().cpu().double().numpy(), ref, TOL[dtype])
 
 
 @pytest.mark.parametrize("dtype,N", [("f16", 1024), ("bf16", 16384), ("f16", 1 << 18)])
@@ -71,7 +72,7 @@ def test_taps_masked(dtype, N):
     torch.cuda.synchronize()
     assert torch.equal(got, want_gpu)
     ref = oracle.fft_conv(inp.f64("u"), inp.f64("k"), mask=mask)
-    assert oracle.rel_l2(got.float().cpu().double().numpy(), ref) < TOL[dtype]
+    check(got.float().cpu().double().numpy(), ref, TOL[dtype])
 
 
 def test_taps_repeated_calls_share_a_workspace():
@@ -89,4 +90,4 @@ def test_taps_repeated_calls_share_a_workspace():
     torch.cuda.synchronize()
     for inp, out in zip((a, b), outs):
         ref = oracle.fft_conv(inp.f64("u"), inp.f64("k"), inp.f64("w"), inp.f64("v"))
-        assert oracle.rel_l2(out.float().cpu().double().numpy(), ref) < TOL["f16"]
+        check(out.float().cpu().double().numpy(), ref, TOL["f16"])

@@ -1,11 +1,18 @@
 """Full-size workloads on the GPU, in the launch configuration the benchmark
-times, checked on sampled outputs the oracle computes one by one.
+times, checked against the oracle sequence by sequence.
 
-The five workloads (long_fft_convolution_amd.synth.WORKLOADS) are run whole on
-the GPU; the oracle evaluates the exact definition at seeded sample positions
-(the direct sum for dense filters, the circular form with the masked filter
-for the frequency-sparse one) plus the first and last positions of sampled
-sequences.  The tolerance applies to the relative L2 error over the samples.
+The five workloads (long_fft_convolution_amd.synth.WORKLOADS) run whole on the
+GPU.  The oracle then recomputes
+  - every sequence where its FFT route finishes in seconds (the 1024- and
+    16384-point workloads: 4, 49,152 and 10,240 sequences), or
+  - a seeded set of whole sequences, the first and last included (the 1M and
+    4M-point workloads: its FFT route takes seconds per sequence there),
+    plus the exact definition at seeded sample positions spread over every
+    sequence (the direct sum for dense filters, the circular form with the
+    masked filter for the frequency-sparse one).
+Each comparison goes through tests/parity.check: whole relL2, the worst
+per-sequence relL2 and the max-abs error are printed ([parity] lines) and the
+first two are held to the workload's tolerance.
 """
 import sys
 
@@ -16,6 +23,7 @@ import torch
 import oracle
 import long_fft_convolution_amd as fc
 from long_fft_convolution_amd import synth
+from parity import check
 
 pytestmark = pytest.mark.gpu
 
@@ -52,46 +60,57 @@ def _run_full(inp, wl):
     return out
 
 
-@pytest.mark.parametrize("name", ["ungated_fp32_n1k", "gated_fp16_n1k", "gated_bf16_n16k",
-                                  "ungated_fp16_n1m"])
-def test_dense_workload_sampled(name):
+def _sequences(inp, wl, seqs):
+    """Oracle (route F) for the given flat sequence indices b * H + h, each as its own channel."""
+    b = torch.from_numpy(seqs // wl.H)
+    h = torch.from_numpy(seqs % wl.H)
+    g = lambda t: None if t is None else t[b, h].to(torch.float64).numpy()[None]
+    mask = None if inp.mask is None else inp.mask[h.numpy()]
+    return oracle.fft_conv(g(inp.u), inp.k[h].to(torch.float64).numpy(), g(inp.w), g(inp.v), mask=mask)[0]
+
+
+@pytest.mark.parametrize("name", ["ungated_fp32_n1k", "gated_fp16_n1k", "gated_bf16_n16k"])
+def test_on_chip_workload_every_sequence(name):
     wl = synth.WORKLOADS[name]
-    _say(f"workload {name}")
+    _say(f"workload {name}: every sequence")
     inp = synth.generate_workload(name)
     out = _run_full(inp, wl)
-    pts = _sample_points(wl, 256 if wl.N <= 16384 else 48, seed=1)
-    got = out[pts[:, 0], pts[:, 1], pts[:, 2]].double().cpu().numpy()
-    # the oracle only needs the sampled sequences
-    seqs = np.unique(pts[:, 0] * wl.H + pts[:, 1])
+    got = out.double().cpu().numpy()
+    del out
+    ref = oracle.fft_conv(inp.f64("u"), inp.f64("k"), inp.f64("w"), inp.f64("v"))
+    check(got, ref, TOL[wl.dtype], f"{name} (all {wl.B * wl.H} sequences)")
+    if wl.N <= 1024:
+        # the direct sums agree with route F on this size; compare them too
+        pts = _sample_points(wl, 256, seed=1)
+        ref_d = oracle.direct_points(inp.f64("u"), inp.f64("k"), pts, inp.f64("w"), inp.f64("v"))
+        check(got[pts[:, 0], pts[:, 1], pts[:, 2]], ref_d, TOL[wl.dtype], f"{name} (direct sums at samples)")
+
+
+@pytest.mark.parametrize("name,nseq", [("ungated_fp16_n1m", 16), ("partial_sparse_n4m", 4)])
+def test_long_workload_sequences_and_samples(name, nseq):
+    wl = synth.WORKLOADS[name]
+    _say(f"workload {name}: {nseq} whole sequences and samples")
+    inp = synth.generate_workload(name)
+    out = _run_full(inp, wl)
+    assert torch.isfinite(out).all()
+    S = wl.B * wl.H
+    rng = np.random.default_rng(3)
+    seqs = np.concatenate([[0, S - 1], rng.choice(np.arange(1, S - 1), nseq - 2, replace=False)])
+    got = out.view(S, wl.N)[torch.from_numpy(seqs).cuda()].double().cpu().numpy()
+    check(got, _sequences(inp, wl, seqs), TOL[wl.dtype], f"{name} ({nseq} whole sequences)")
+    # samples spread over every sequence
+    pts = _sample_points(wl, 64, seed=1)
+    gotp = out[pts[:, 0], pts[:, 1], pts[:, 2]].double().cpu().numpy()
     ref = np.empty(len(pts))
-    for s in seqs:
+    for s in np.unique(pts[:, 0] * wl.H + pts[:, 1]):
         b, h = divmod(int(s), wl.H)
         sel = (pts[:, 0] == b) & (pts[:, 1] == h)
-        f64 = lambda t: None if t is None else t[b:b + 1, h:h + 1].to(torch.float64).numpy()
-        kk = inp.k[h:h + 1].to(torch.float64).numpy()
-        q = np.stack([np.zeros(sel.sum(), np.int64), np.zeros(sel.sum(), np.int64), pts[sel, 2]], 1)
-        ref[sel] = oracle.direct_points(f64(inp.u), kk, q, f64(inp.w), f64(inp.v))
-    err = oracle.rel_l2(got, ref)
-    print(f"{name}: sampled relL2 {err:.3e} over {len(pts)} points", flush=True)
-    assert err < TOL[wl.dtype]
-    assert torch.isfinite(out).all()
-
-
-def test_partial_sparse_workload_sampled():
-    name = "partial_sparse_n4m"
-    wl = synth.WORKLOADS[name]
-    _say(f"workload {name}")
-    inp = synth.generate_workload(name)
-    out = _run_full(inp, wl)
-    rng = np.random.default_rng(2)
-    hs = [0, wl.H - 1] + list(rng.integers(1, wl.H - 1, 2))
-    got, ref = [], []
-    for h in hs:
-        ts = np.concatenate([[0, 1, wl.L - 1, wl.L, wl.N - 1], rng.integers(0, wl.N, 12)])
-        kp = oracle.masked_filter(inp.k[h].to(torch.float64).numpy(), wl.N, inp.mask[h])
-        ref.append(oracle.circular_points(inp.u[0, h].to(torch.float64).numpy(), kp, ts))
-        got.append(out[0, h, torch.from_numpy(ts).cuda()].double().cpu().numpy())
-    err = oracle.rel_l2(np.concatenate(got), np.concatenate(ref))
-    print(f"{name}: sampled relL2 {err:.3e}", flush=True)
-    assert err < TOL[wl.dtype]
-    assert torch.isfinite(out).all()
+        if inp.mask is None:
+            f64 = lambda t: None if t is None else t[b:b + 1, h:h + 1].to(torch.float64).numpy()
+            q = np.stack([np.zeros(sel.sum(), np.int64), np.zeros(sel.sum(), np.int64), pts[sel, 2]], 1)
+            ref[sel] = oracle.direct_points(f64(inp.u), inp.k[h:h + 1].to(torch.float64).numpy(), q,
+                                            f64(inp.w), f64(inp.v))
+        else:
+            kp = oracle.masked_filter(inp.k[h].to(torch.float64).numpy(), wl.N, inp.mask[h])
+            ref[sel] = oracle.circular_points(inp.u[b, h].to(torch.float64).numpy(), kp, pts[sel, 2])
+    check(gotp, ref, TOL[wl.dtype], f"{name} (samples over all sequences)")
