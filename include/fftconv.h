@@ -46,7 +46,15 @@
  *    was launched.  fftconv_last_error() gives the detail of the calling
  *    thread's last non-OK status.  Calls on different streams may run
  *    concurrently; the library's only shared state is a per-device cache of
- *    twiddle tables guarded by a mutex.
+ *    constant tables (twiddles, DFT operand tiles) guarded by a mutex.
+ *  - The constant tables of a device are built once, by fftconv_init() or by
+ *    the first fftconv_prepare_filter / fftconv_prepare_short_filter on that
+ *    device: that one call allocates device memory and copies synchronously.
+ *    After it, no call of this library allocates device memory or waits for
+ *    the GPU (apart from the functions marked SYNCHRONOUS), so the forward
+ *    and backward calls may be captured into a HIP graph.  A forward or
+ *    backward call on a device where neither ran builds the tables itself,
+ *    allocating and blocking like fftconv_init.
  */
 #ifndef FFTCONV_H
 #define FFTCONV_H
@@ -224,6 +232,12 @@ fftconv_status_t fftconv_eqlinear_prepare(const void *W, int64_t T, int64_t C_ou
  * stream; y must not overlap x or W_f. */
 fftconv_status_t fftconv_eqlinear_fwd(const void *x, const void *W_f, void *y, int64_t N, int64_t T,
                                       int64_t C_in, int64_t C_out, fftconv_dtype_t dtype, hipStream_t stream);
+
+/* Set-up of the calling thread's current device, SYNCHRONOUS: builds every
+ * constant table the kernels read (device memory owned by the library until
+ * the process ends).  Idempotent: later calls on the same device return at
+ * once.  Returns FFTCONV_ERR_HIP when an allocation or copy fails. */
+fftconv_status_t fftconv_init(void);
 
 /* Static text for a status code. */
 const char *fftconv_status_string(fftconv_status_t status);

@@ -63,6 +63,8 @@ def _load():
     lib.fftconv_bwd_workspace_bytes.restype = sz
     lib.fftconv_bwd.argtypes = [vp] * 9 + [i64, i64, i64, i64, vp, ctypes.c_int, vp, sz, vp]
     lib.fftconv_bwd.restype = ctypes.c_int
+    lib.fftconv_init.argtypes = []
+    lib.fftconv_init.restype = ctypes.c_int
     lib.fftconv_status_string.argtypes = [ctypes.c_int]
     lib.fftconv_status_string.restype = ctypes.c_char_p
     lib.fftconv_last_error.argtypes = []
@@ -131,6 +133,12 @@ def fftconv_workspace_bytes(B: int, H: int, N: int, dtype) -> int:
 
 def fftconv_mask_blocks(N: int) -> int:
     return int(_load().fftconv_mask_blocks(N))
+
+
+def fftconv_init(device=None) -> None:
+    """Build the library's constant tables on `device` (default: the current one); synchronous."""
+    with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+        _check(_load().fftconv_init())
 
 
 def fftconv_status_string(status: int) -> str:

@@ -313,6 +313,38 @@ hipError_t get_tables(int logn, Tables *out) {
     return hipSuccess;
 }
 
+namespace {
+std::mutex g_ready_mu;
+std::map<int, bool> g_ready;   // devices whose every table is built
+}  // namespace
+
+hipError_t init_device_tables() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lk(g_ready_mu);
+    if (g_ready.count(dev)) return hipSuccess;
+    Tables t{};
+    // twiddles of every on-chip size (2^10 .. 2^14), of every multi-pass outer
+    // size (2^2 .. 2^9) and of the multi-pass row (2^13)
+    for (int l = 2; l <= kFusedMaxLog && e == hipSuccess; ++l) e = get_tables(l, &t);
+    MpTables m{};
+    for (int l = kFusedMaxLog + 1; l <= kMaxLog && e == hipSuccess; ++l) e = get_mp_tables(l, &m);
+    PairTables p{};
+    if (e == hipSuccess) e = get_pair_tables(&p);
+    Pair3Tables p3{};
+    if (e == hipSuccess) e = get_pair3_tables(&p3);
+    if (e == hipSuccess) g_ready[dev] = true;
+    return e;
+}
+
+bool device_tables_ready() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    std::lock_guard<std::mutex> lk(g_ready_mu);
+    return g_ready.count(dev) != 0;
+}
+
 MpSplit mp_split(int logn) {
     // inner (on-chip) transform of 2^log2 points, outer of 2^log1 points
     MpSplit s;
@@ -351,6 +383,13 @@ const char *fftconv_status_string(fftconv_status_t s) {
 }
 
 const char *fftconv_last_error(void) { return g_last_error.c_str(); }
+
+fftconv_status_t fftconv_init(void) {
+    g_last_error.clear();
+    const hipError_t e = init_device_tables();
+    if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "building the constant tables: %s", hipGetErrorString(e));
+    return ok();
+}
 
 int64_t fftconv_mask_blocks(int64_t N) {
     const int l = log2_exact(N);
@@ -414,6 +453,11 @@ static fftconv_status_t prepare_impl(const void *k, int64_t H, int64_t L, int64_
     if (wneed > 0 && !aligned16(workspace))
         return fail(FFTCONV_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
 
+    // the first prepare on a device builds every constant table of the library
+    // (synchronous), so that the forward calls that follow neither allocate nor block
+    hipError_t e = init_device_tables();
+    if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "building the constant tables: %s", hipGetErrorString(e));
+
     char *base = static_cast<char *>(K_f);
     float *kscale = reinterpret_cast<float *>(base + kf_scale_off());
     void *kbins = base + kf_bins_off(H);
@@ -433,7 +477,7 @@ static fftconv_status_t prepare_impl(const void *k, int64_t H, int64_t L, int64_
     hdr.n1 = fused ? 0 : (int64_t(1) << sp.log1);
     hdr.n2 = fused ? N : (int64_t(1) << sp.log2);
 
-    hipError_t e = launch_write_header(hdr, K_f, stream);
+    e = launch_write_header(hdr, K_f, stream);
     if (e == hipSuccess)
         e = launch_filter_scale(dtype, k, H, L, kf_norm_log2(l, dtype), kf_target_log2(l, dtype), kscale,
                                 stream);
@@ -457,7 +501,8 @@ static fftconv_status_t prepare_impl(const void *k, int64_t H, int64_t L, int64_
 // has work to enqueue, FFTCONV_OK with `*empty` set when B * H = 0.
 static fftconv_status_t fwd_args(const void *u, const void *K_f, const void *w, const void *v, void *out,
                                  int64_t B, int64_t H, int64_t N, int64_t L, const uint8_t *mask,
-                                 fftconv_dtype_t dtype, void *workspace, size_t workspace_bytes, bool *empty) {
+                                 fftconv_dtype_t dtype, void *workspace, size_t workspace_bytes, bool *empty,
+                                 bool check_workspace = true) {
     *empty = false;
     if (!dtype_ok(dtype)) return fail(FFTCONV_ERR_UNSUPPORTED, "dtype %d is not supported", (int)dtype);
     const int l = log2_exact(N);
@@ -484,6 +529,7 @@ static fftconv_status_t fwd_args(const void *u, const void *K_f, const void *w, 
         overlap(out, nbytes, v, nbytes) || overlap(out, nbytes, K_f, kfb) ||
         overlap(out, nbytes, mask, (size_t)H * kMaskBlocks))
         return fail(FFTCONV_ERR_INVALID_ARGUMENT, "out overlaps an input");
+    if (!check_workspace) return FFTCONV_OK;
     const size_t wneed = fftconv_workspace_bytes(B, H, N, dtype);
     if (wneed > 0 && (workspace == nullptr || workspace_bytes < wneed))
         return fail(FFTCONV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, wneed);
@@ -494,18 +540,13 @@ static fftconv_status_t fwd_args(const void *u, const void *K_f, const void *w, 
     return FFTCONV_OK;
 }
 
-fftconv_status_t fftconv_fwd(const void *u, const void *K_f, const void *w, const void *v,
-                             void *out, int64_t B, int64_t H, int64_t N, int64_t L,
-                             const uint8_t *mask, fftconv_dtype_t dtype, void *workspace,
-                             size_t workspace_bytes, hipStream_t stream) {
-    g_last_error.clear();
-    bool empty = false;
-    const fftconv_status_t chk_st =
-        fwd_args(u, K_f, w, v, out, B, H, N, L, mask, dtype, workspace, workspace_bytes, &empty);
-    if (chk_st != FFTCONV_OK || empty) return chk_st;
+// The forward call's launches, after fwd_args accepted the arguments.  The
+// three-pass path runs `chunk` sequences at a time through the workspace,
+// which holds chunk * (N complex values + the two self-paired rows).
+static fftconv_status_t fwd_enqueue(const void *u, const void *K_f, const void *w, const void *v, void *out,
+                                    int64_t B, int64_t H, int64_t N, int64_t L, const uint8_t *mask,
+                                    fftconv_dtype_t dtype, void *workspace, int64_t chunk, hipStream_t stream) {
     const int l = log2_exact(N);
-    const size_t kfb = fftconv_filter_bytes(H, N, dtype);
-
     const char *chk = std::getenv("FFTCONV_CHECK");
     if (chk && chk[0] == '1') {
         KfHeader hdr{};
@@ -535,15 +576,29 @@ fftconv_status_t fftconv_fwd(const void *u, const void *K_f, const void *w, cons
         if (e == hipSuccess)
             e = launch_fused_conv(l, dtype, u, w, v, out, kbins, kscale, mask, tb, B, H, stream);
     } else {
-        const int64_t S = B * H, c = mp_chunk(l, dtype);
-        for (int64_t s0 = 0; s0 < S && e == hipSuccess; s0 += c) {
-            const int64_t n = S - s0 < c ? S - s0 : c;
+        const int64_t S = B * H;
+        for (int64_t s0 = 0; s0 < S && e == hipSuccess; s0 += chunk) {
+            const int64_t n = S - s0 < chunk ? S - s0 : chunk;
             e = launch_multipass_conv(l, dtype, u, w, v, out, kbins, kscale, mask, workspace, H,
                                       s0, n, stream);
         }
     }
     if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "fwd launch: %s", hipGetErrorString(e));
     return ok();
+}
+
+fftconv_status_t fftconv_fwd(const void *u, const void *K_f, const void *w, const void *v,
+                             void *out, int64_t B, int64_t H, int64_t N, int64_t L,
+                             const uint8_t *mask, fftconv_dtype_t dtype, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+    g_last_error.clear();
+    bool empty = false;
+    const fftconv_status_t chk_st =
+        fwd_args(u, K_f, w, v, out, B, H, N, L, mask, dtype, workspace, workspace_bytes, &empty);
+    if (chk_st != FFTCONV_OK || empty) return chk_st;
+    const int l = log2_exact(N);
+    return fwd_enqueue(u, K_f, w, v, out, B, H, N, L, mask, dtype, workspace,
+                       l > kFusedMaxLog ? mp_chunk(l, dtype) : 0, stream);
 }
 
 // ---- backward pass ---------------------------------------------------------

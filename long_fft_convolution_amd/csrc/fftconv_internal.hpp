@@ -128,6 +128,10 @@ struct MpTables {
     const float2 *big_hi;  // exp(-2 pi i 2048 j / N),   j < N / 2048
 };
 hipError_t get_mp_tables(int logn, MpTables *out);
+// Builds every table of the current device once (hipMalloc and synchronous
+// copies); later calls return at once.  device_tables_ready: already built.
+hipError_t init_device_tables();
+bool device_tables_ready();
 
 // ---- launchers (return the launch status) --------------------------------
 hipError_t launch_fused_conv(int logn, int st, const void *u,
