@@ -1,16 +1,25 @@
 """Benchmark: one step = one fftconv_fwd call over a whole synthetic batch.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass fwd|bwd|taps]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|all] [--pass fwd|bwd|taps]
 
-Prints ONE JSON line (stdout).  The default workload is gated_fp16_n1k
-(B=64, H=768, N=1024, fp16 storage, gated, filter as long as the sequence).
+Prints ONE JSON line (stdout).  By default (--workload all) every one of the
+five configurations the metric spans (N = 1K .. 4M) is measured in turn:
+ungated_fp32_n1k, gated_fp16_n1k, gated_bf16_n16k, ungated_fp16_n1m and
+partial_sparse_n4m.  The line's headline (value, ms_per_step, config,
+roofline, cpu_baseline) is the largest, partial_sparse_n4m; the list
+"workloads" holds the same figures for all five, and "target_n16k" compares
+the N = 16K configuration with half of the HBM peak.
+
 Inputs are seeded synthetic data already resident in HBM; the filter is
 prepared once before timing (it depends only on k).  `value` is B*H*N
-elements per second over the timed steps.  The roofline object reports the
-algorithmic HBM bytes of one forward call divided by the average duration of
-the dominant kernel, timed with HIP events on the stream it runs on.  The
-cpu_baseline object times the CPU oracle (route F) on a bounded sample of the
-same workload on this host's cores.
+elements per second over the K timed steps.  The roofline object reports the
+algorithmic HBM bytes of one forward call divided by the call's average
+duration, timed with HIP events on the stream the library launches on; the
+HBM traffic and matrix-core utilisation come from the committed rocprofv3
+counter summaries (profiles/) when they were taken on the current kernel
+sources.  The cpu_baseline object times the CPU oracle (route F) on a bounded
+sample of the same workload on this host's cores, and compares the GPU's
+output with it on that sample (relL2, worst sequence, max-abs).
 
 With --pass bwd one step is one fftconv_bwd call (du, dk, dw, dv) instead;
 with --pass taps one fftconv_fwd_taps call (the filter transformed from its L
@@ -67,15 +76,20 @@ KERNEL_SOURCES = ["fused.hip", "multipass.hip", "pair_mfma.hip", "pair16k.hip", 
 
 def path_of(w: synth.Workload):
     """(kernel name, compute dtype, arithmetic) of the path fftconv_fwd takes for w."""
+    mm = "fp16 MFMA operands, fp32 accumulation"
     if w.short:
-        return "pair1k_kernel (windows of 2048, hop 1024)", "f16", "fp16 MFMA operands, fp32 accumulation"
+        return "pair1k_kernel (windows of 2048, hop 1024)", "f16", mm
     if w.dtype in ("f16", "bf16") and w.N == 1024:
-        return "pair1k_kernel", "f16", "fp16 MFMA operands, fp32 accumulation"
+        return "pair1k_kernel", "f16", mm
     if w.dtype in ("f16", "bf16") and w.N == 16384:
-        return "pair16k_kernel", "f16", "fp16 MFMA operands, fp32 accumulation"
+        return "pair16k_kernel", "f16", mm
     if w.N <= 16384:
-        return "fused_conv_kernel", "f32", "fp32"
-    return "mp_pass1+mp_pass2+mp_pass3 (one call)", "f32", "fp32"
+        return "fused_conv_kernel", "f32", "fp32 (VALU)"
+    if w.dtype == "f32":
+        return "mp_pass1+mp_pass2+mp_pass3 (one call)", "f32", "fp32 (VALU)"
+    return ("mp_pass1+mp_pass2m+mp_pass3 (one call)", "f16",
+            "column passes fp32 (VALU); row pass fp16 MFMA operands, fp32 accumulation; "
+            f"{w.dtype} intermediate")
 
 
 def log(*a):
@@ -103,23 +117,55 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
-    taken on the current kernel sources (else None)."""
-    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+def _profile_json(name: str):
+    p = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(p):
         return None
     try:
         d = json.load(open(p))
     except Exception:
         return None
-    if d.get("kernel_source_hash") != kernel_source_hash():
+    return d if d.get("kernel_source_hash") == kernel_source_hash() else None
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per call from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel sources (else None)."""
+    d = _profile_json(f"traffic_{workload}.json")
+    return None if d is None else d.get("hbm_bytes_per_launch")
+
+
+def measured_mfma(workload: str, ms_per_call: float):
+    """Matrix-core figures per call from the committed rocprofv3 SQ counters of the
+    current kernel sources (else None): fp16 MFMA flops (SQ_INSTS_VALU_MFMA_MOPS_F16,
+    512 flops per unit) over the timed call duration against the 2.5 PFLOP/s dense
+    fp16 peak, and the counters' busy fraction SQ_VALU_MFMA_BUSY_CYCLES /
+    (GRBM_GUI_ACTIVE x 256 CUs)."""
+    d = _profile_json(f"counters_{workload}.json")
+    if d is None:
         return None
-    return d.get("hbm_bytes_per_launch")
+    flops = d.get("mfma_f16_flops_per_call")
+    out = {"peak_tflops": 2500.0, "flops_per_call": flops, "busy_frac": d.get("mfma_busy_frac")}
+    if flops is not None:
+        out["achieved_tflops"] = flops / (ms_per_call / 1e3) / 1e12
+        out["frac"] = out["achieved_tflops"] / 2500.0
+    return out
 
 
-def cpu_baseline(wl: synth.Workload, inp: synth.Inputs, budget_s: float = 10.0):
-    """Time oracle.fft_conv on leading batch rows (or channels when B = 1)."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl: synth.Workload, inp: synth.Inputs, out: torch.Tensor, budget_s: float = 8.0):
+    """Time oracle.fft_conv (route F, float64) on leading batch rows (or channels when
+    B = 1), sized to about budget_s of work on this host's threads, and compare the
+    GPU's output `out` with the oracle's on that sample."""
     import oracle
 
     def sample(n):
@@ -130,48 +176,57 @@ def cpu_baseline(wl: synth.Workload, inp: synth.Inputs, budget_s: float = 10.0):
             sl = (slice(None), slice(0, n))
             kk, mm = inp.k[:n], None if inp.mask is None else inp.mask[:n]
         f64 = lambda t: None if t is None else t[sl].to(torch.float64).numpy()
-        return f64(inp.u), kk.to(torch.float64).numpy(), f64(inp.w), f64(inp.v), mm
+        return sl, (f64(inp.u), kk.to(torch.float64).numpy(), f64(inp.w), f64(inp.v), mm)
 
     def run(n):
-        uu, kk, ww, vv, mm = sample(n)
+        sl, (uu, kk, ww, vv, mm) = sample(n)
         t0 = time.perf_counter()
-        oracle.fft_conv(uu, kk, ww, vv, mask=mm)
-        return time.perf_counter() - t0, uu.shape[0] * uu.shape[1]
+        y = oracle.fft_conv(uu, kk, ww, vv, mask=mm)
+        return time.perf_counter() - t0, uu.shape[0] * uu.shape[1], sl, y
 
     units = wl.B if wl.B > 1 else wl.H
-    dt, nseq = run(1)
-    n = int(min(units, max(1, budget_s / max(dt, 1e-9))))
-    dt, nseq = run(n)
+    cores = oracle.max_threads()
+    per_unit = wl.H if wl.B > 1 else 1            # sequences per sampled unit
+    n = min(units, max(1, -(-cores // per_unit)))   # fill the threads once
+    dt, nseq, sl, y = run(n)
+    if dt < 0.5 * budget_s and n < units:
+        n = int(min(units, max(n + 1, n * budget_s / max(dt, 1e-9))))
+        dt, nseq, sl, y = run(n)
+    got = out[sl].double().cpu().numpy()
+    seq = oracle.seq_rel_l2(got, y)
+    mabs = oracle.max_abs(got, y)
     what = "batch rows" if wl.B > 1 else "channels"
-    return {"value": nseq * wl.N / dt, "unit": "elems/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
-            "sample": f"{n} of {units} {what} ({nseq} sequences) of {wl.name}, route F float64, "
-                      f"{dt:.1f} s"}
+    return {"value": nseq * wl.N / dt, "unit": "elems/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"{n} of {units} {what} ({nseq} sequences) of {wl.name}, route F float64, {dt:.1f} s",
+            "parity_on_sample": {"rel_l2": oracle.rel_l2(got, y), "worst_seq_rel_l2": float(seq.max()),
+                                 "max_abs": mabs, "max_abs_rel": mabs / float(np.abs(y).max()),
+                                 "sequences": int(seq.size)}}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gated_fp16_n1k",
-                    choices=sorted(synth.WORKLOADS) + sorted(synth.EQ_WORKLOADS))
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd", "taps"], default="fwd",
-                    help="time the forward call (default), the backward call, or the forward "
-                         "call from time-domain taps")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="also run one plain device copy of the activation bytes (counter scale)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py: runs on one GPU; --gpus {args.gpus} is not supported "
-              "(sequences are independent: (b, h) would be sharded across devices)", file=sys.stderr)
-        sys.exit(2)
+FIVE = ["ungated_fp32_n1k", "gated_fp16_n1k", "gated_bf16_n16k", "ungated_fp16_n1m", "partial_sparse_n4m"]
+HEADLINE = "partial_sparse_n4m"
+TARGET_N16K = "gated_bf16_n16k"
 
-    if args.workload in synth.EQ_WORKLOADS:
-        return bench_eqlinear(args)
-    wl = synth.WORKLOADS[args.workload]
-    dev = torch.device("cuda:0")
+
+def time_steps(step, steps: int, dev) -> float:
+    """ms per step over `steps` back-to-back calls between two HIP events on the
+    stream the library launches on (torch's current stream); no event between calls,
+    which would add its own gap to every call."""
+    stream = torch.cuda.current_stream(dev)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    t0.record(stream)
+    for _ in range(steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize(dev)
+    return t0.elapsed_time(t1) / steps
+
+
+def measure_fwd(wl: synth.Workload, args, dev, with_cpu: bool):
+    """One workload's forward figures (a dict of the bench line's fields)."""
     log(f"bench: generating {wl.name} (B={wl.B} H={wl.H} N={wl.N} L={wl.L} {wl.dtype})")
     inp = synth.generate_workload(wl.name)
     u = inp.u.to(dev)
@@ -186,8 +241,7 @@ def main():
         ws = None
     else:
         K_f = fc.alloc_filter(wl.H, wl.N, u.dtype, dev)
-        ws_p = fc.alloc_workspace(1, wl.H, wl.N, u.dtype, dev)
-        fc.fftconv_prepare_filter(k, wl.N, K_f, ws_p)
+        fc.fftconv_prepare_filter(k, wl.N, K_f, fc.alloc_workspace(1, wl.H, wl.N, u.dtype, dev))
         ws = fc.alloc_workspace(wl.B, wl.H, wl.N, u.dtype, dev)
     torch.cuda.synchronize(dev)
 
@@ -197,41 +251,14 @@ def main():
         else:
             fc.fftconv_fwd(u, K_f, w, v, out, wl.L, mask, ws)
 
-    if args.which == "bwd":
-        if wl.short:
-            log("bench: the short-filter path has no backward pass")
-            return 2
-        return bench_bwd(args, wl, dev, u, K_f, w, v, mask)
-    if args.which == "taps":
-        if wl.short:
-            log("bench: the short-filter path takes its taps' spectrum from its own prepare")
-            return 2
-        return bench_taps(args, wl, dev, u, k, w, v, mask)
-
     n_warm = warm_up(step, args.warmup, dev)
-    log(f"bench: {n_warm} warm-up steps")
-    stream = torch.cuda.current_stream(dev)
-    # HIP events on the stream the library launches on (torch's current stream), around the
-    # K back-to-back calls only: an event between calls would add its own gap to every call
-    t_all0 = torch.cuda.Event(enable_timing=True)
-    t_all1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize(dev)
-    t_all0.record(stream)
-    for i in range(args.steps):
-        step()
-    t_all1.record(stream)
-    torch.cuda.synchronize(dev)
-    total_ms = t_all0.elapsed_time(t_all1)
-    ms_per_step = total_ms / args.steps
+    ms = time_steps(step, args.steps, dev)
     elems = wl.B * wl.H * wl.N
-    value = elems / (ms_per_step / 1e3)
     alg = algorithmic_bytes(wl)
-    # one fwd call per step: the mean call duration is the step time
-    kern_ms = ms_per_step
-    achieved = alg / (kern_ms / 1e3) / 1e9
-    log(f"bench: {ms_per_step * 1e3:.1f} us/step, "
-        f"{value:.3e} elems/s, {achieved:.0f} GB/s algorithmic ({achieved / HBM_PEAK_GBS:.1%} of 8 TB/s)")
-
+    achieved = alg / (ms / 1e3) / 1e9
+    kernel, cdtype, arith = path_of(wl)
+    log(f"bench: {wl.name}: {n_warm} warm-up steps, {ms * 1e3:.1f} us/step, {elems / (ms / 1e3):.3e} elems/s, "
+        f"{achieved:.0f} GB/s algorithmic ({achieved / HBM_PEAK_GBS:.1%} of 8 TB/s)")
     if args.calibrate_copy:
         # a plain elementwise copy kernel of known size: reads and writes n*4 bytes
         n = (alg // 2) // 4
@@ -240,37 +267,107 @@ def main():
         torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize(dev)
         log(f"bench: calibration copy kernel moved {n * 4} bytes each way")
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("bench: timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(wl, inp)
-        log(f"bench: oracle {cpu['value']:.3e} elems/s on {cpu['cores']} threads ({cpu['sample']})")
-
-    dominant, cdtype, arith = path_of(wl)
+        del src, dst
+    traffic = measured_traffic(wl.name)
     rec = {
+        "workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "L_filter": wl.L, "gated": wl.gated,
+        "storage": wl.dtype, "dtype": cdtype, "arithmetic": arith, "mask_keep_blocks": wl.mask_keep_blocks,
+        "ms_per_step": ms, "value": elems / (ms / 1e3), "unit": "elems/s", "warmup_steps_run": n_warm,
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "traffic_over_algorithmic": None if traffic is None else traffic / alg,
+                     "algorithmic_bytes": alg, "kernel_ms": ms, "mfma": measured_mfma(wl.name, ms)},
+        "cpu_baseline": None,
+    }
+    if with_cpu:
+        log(f"bench: {wl.name}: timing the CPU oracle on a bounded sample")
+        rec["cpu_baseline"] = cpu_baseline(wl, inp, out)
+        c = rec["cpu_baseline"]
+        log(f"bench: {wl.name}: oracle {c['value']:.3e} elems/s on {c['cores']} threads ({c['sample']}); "
+            f"sample relL2 {c['parity_on_sample']['rel_l2']:.2e}, worst sequence "
+            f"{c['parity_on_sample']['worst_seq_rel_l2']:.2e}")
+    del u, k, w, v, mask, out, K_f, ws, inp
+    torch.cuda.empty_cache()
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5,
+                    help="minimum untimed steps; more run until 0.2 s has passed (the count run is reported)")
+    ap.add_argument("--workload", default="all",
+                    choices=["all"] + sorted(synth.WORKLOADS) + sorted(synth.EQ_WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd", "taps"], default="fwd",
+                    help="time the forward call (default), the backward call, or the forward "
+                         "call from time-domain taps")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain device copy of the activation bytes (counter scale)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: runs on one GPU; --gpus {args.gpus} is not supported "
+              "(sequences are independent: (b, h) would be sharded across devices)", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+
+    if args.workload in synth.EQ_WORKLOADS:
+        return bench_eqlinear(args)
+    if args.which != "fwd":
+        wl = synth.WORKLOADS[HEADLINE if args.workload == "all" else args.workload]
+        if wl.short:
+            log("bench: the short-filter path has only the forward call")
+            return 2
+        return bench_other(args, wl, dev)
+
+    names = FIVE if args.workload == "all" else [args.workload]
+    recs = [measure_fwd(synth.WORKLOADS[n], args, dev, not args.no_cpu_baseline) for n in names]
+    head = next((r for r in recs if r["workload"] == HEADLINE), recs[-1])
+    line = {
         "metric": METRIC,
-        "value": value,
+        "value": head["value"],
         "unit": "elems/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "warmup": head["warmup_steps_run"],
+        "warmup_min": args.warmup,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cdtype,
+        "dtype": head["dtype"],
         "data": "synthetic (seeded N(0,1) activations, decaying random filter)",
-        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "L_filter": wl.L,
-                   "gated": wl.gated, "storage": wl.dtype, "arithmetic": arith,
-                   "mask_keep_blocks": wl.mask_keep_blocks, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(wl.name), "algorithmic_bytes": alg,
-                     "kernel_ms": kern_ms},
-        "cpu_baseline": cpu,
+        "config": {"workload": head["workload"], "B": head["B"], "H": head["H"], "N": head["N"],
+                   "L_filter": head["L_filter"], "gated": head["gated"], "storage": head["storage"],
+                   "arithmetic": head["arithmetic"], "mask_keep_blocks": head["mask_keep_blocks"],
+                   "parallelism": "single GPU"},
+        "roofline": head["roofline"],
+        "cpu_baseline": head["cpu_baseline"],
+        "workloads": recs,
     }
-    print(json.dumps(rec), flush=True)
+    t = next((r for r in recs if r["workload"] == TARGET_N16K), None)
+    if t is not None:
+        line["target_n16k"] = {"workload": TARGET_N16K, "frac": t["roofline"]["frac"], "target_frac": 0.5,
+                               "met": t["roofline"]["frac"] >= 0.5,
+                               "elems_per_s": t["value"], "target_elems_per_s": 4.44e11}
+    print(json.dumps(line), flush=True)
+
+
+def bench_other(args, wl, dev):
+    """--pass bwd / taps on one workload."""
+    inp = synth.generate_workload(wl.name)
+    u = inp.u.to(dev)
+    k = inp.k.to(dev)
+    w = None if inp.w is None else inp.w.to(dev)
+    v = None if inp.v is None else inp.v.to(dev)
+    mask = None if inp.mask is None else torch.from_numpy(inp.mask).to(dev)
+    K_f = fc.alloc_filter(wl.H, wl.N, u.dtype, dev)
+    fc.fftconv_prepare_filter(k, wl.N, K_f, fc.alloc_workspace(1, wl.H, wl.N, u.dtype, dev))
+    torch.cuda.synchronize(dev)
+    if args.which == "bwd":
+        return bench_bwd(args, wl, dev, u, K_f, w, v, mask)
+    return bench_taps(args, wl, dev, u, k, w, v, mask)
 
 
 def bench_eqlinear(args):
@@ -283,16 +380,8 @@ def bench_eqlinear(args):
     W_f = torch.empty(fc.fftconv_eqlinear_weight_bytes(wl.T, wl.C_out, wl.C_in), dtype=torch.uint8, device=dev)
     fc.fftconv_eqlinear_prepare(W, W_f)
     y = torch.empty((wl.N, wl.T, wl.C_out), dtype=x.dtype, device=dev)
-    warm_up(lambda: fc.fftconv_eqlinear_fwd(x, W_f, y), args.warmup, dev)
-    stream = torch.cuda.current_stream(dev)
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(args.steps):
-        fc.fftconv_eqlinear_fwd(x, W_f, y)
-    t1.record(stream)
-    torch.cuda.synchronize(dev)
-    ms = t0.elapsed_time(t1) / args.steps
+    n_warm = warm_up(lambda: fc.fftconv_eqlinear_fwd(x, W_f, y), args.warmup, dev)
+    ms = time_steps(lambda: fc.fftconv_eqlinear_fwd(x, W_f, y), args.steps, dev)
     e = ELEM[wl.dtype]
     alg = wl.N * wl.T * (wl.C_in + wl.C_out) * e + W_f.numel()
     # matrix-core work: per token, f = 0 and T/2 are real products, the T/2 - 1 others complex (4 real)
@@ -320,7 +409,8 @@ def bench_eqlinear(args):
                "kind": "oracle", "sample": f"{n} of {wl.N} tokens of {wl.name}, float64 numpy, {dt:.2f} s"}
     rec = {
         "metric": "group-axis circular conv fwd N*T*C_in elems/s + % HBM peak, 1 GPU",
-        "value": value, "unit": "elems/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "value": value, "unit": "elems/s", "n_gpus": 1, "steps": args.steps, "warmup": n_warm,
+        "warmup_min": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic (seeded N(0,1) activations, N(0, 1/(T C_in)) weights)",
         "config": {"workload": wl.name, "N": wl.N, "T": wl.T, "C_in": wl.C_in, "C_out": wl.C_out,
@@ -350,16 +440,7 @@ def bench_bwd(args, wl, dev, u, K_f, w, v, mask):
 
     n_warm = warm_up(step, args.warmup, dev)
     log(f"bench: {n_warm} warm-up steps")
-    stream = torch.cuda.current_stream(dev)
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize(dev)
-    t0.record(stream)
-    for _ in range(args.steps):
-        step()
-    t1.record(stream)
-    torch.cuda.synchronize(dev)
-    ms_per_step = t0.elapsed_time(t1) / args.steps
+    ms_per_step = time_steps(step, args.steps, dev)
     elems = wl.B * wl.H * wl.N
     e = ELEM[wl.dtype]
     # what the backward must move: dy, u (+ w, v) read, du (+ dw, dv) written,
@@ -374,7 +455,8 @@ def bench_bwd(args, wl, dev, u, K_f, w, v, mask):
         "unit": "elems/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": n_warm,
+        "warmup_min": args.warmup,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -403,16 +485,7 @@ def bench_taps(args, wl, dev, u, k, w, v, mask):
 
     n_warm = warm_up(step, args.warmup, dev)
     log(f"bench: {n_warm} warm-up steps")
-    stream = torch.cuda.current_stream(dev)
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize(dev)
-    t0.record(stream)
-    for _ in range(args.steps):
-        step()
-    t1.record(stream)
-    torch.cuda.synchronize(dev)
-    ms_per_step = t0.elapsed_time(t1) / args.steps
+    ms_per_step = time_steps(step, args.steps, dev)
     elems = wl.B * wl.H * wl.N
     e = ELEM[wl.dtype]
     # the forward call's bytes with the L taps read in place of the spectrum
@@ -425,7 +498,8 @@ def bench_taps(args, wl, dev, u, k, w, v, mask):
         "unit": "elems/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": n_warm,
+        "warmup_min": args.warmup,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",

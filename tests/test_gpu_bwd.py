@@ -17,6 +17,7 @@ import torch
 import oracle
 import long_fft_convolution_amd as fc
 from long_fft_convolution_amd import synth
+from parity import check
 
 pytestmark = pytest.mark.gpu
 

@@ -14,6 +14,7 @@ Each comparison goes through tests/parity.check: whole relL2, the worst
 per-sequence relL2 and the max-abs error are printed ([parity] lines) and the
 first two are held to the workload's tolerance.
 """
+import concurrent.futures
 import sys
 
 import numpy as np
@@ -98,11 +99,18 @@ def test_long_workload_sequences_and_samples(name, nseq):
     seqs = np.concatenate([[0, S - 1], rng.choice(np.arange(1, S - 1), nseq - 2, replace=False)])
     got = out.view(S, wl.N)[torch.from_numpy(seqs).cuda()].double().cpu().numpy()
     check(got, _sequences(inp, wl, seqs), TOL[wl.dtype], f"{name} ({nseq} whole sequences)")
-    # samples spread over every sequence
+    # samples spread over the sequences: every sequence for a dense filter (the direct
+    # sum costs O(t) per output); for the masked one 16 channels, since each needs its
+    # masked filter through two 2N-point FFTs (run in parallel threads)
     pts = _sample_points(wl, 64, seed=1)
+    if inp.mask is not None:
+        hs = np.concatenate([[0, wl.H - 1], rng.choice(np.arange(1, wl.H - 1), 14, replace=False)])
+        pts[:64, 1] = hs[np.arange(64) % 16]
     gotp = out[pts[:, 0], pts[:, 1], pts[:, 2]].double().cpu().numpy()
     ref = np.empty(len(pts))
-    for s in np.unique(pts[:, 0] * wl.H + pts[:, 1]):
+    keys = np.unique(pts[:, 0] * wl.H + pts[:, 1])
+
+    def one(s):
         b, h = divmod(int(s), wl.H)
         sel = (pts[:, 0] == b) & (pts[:, 1] == h)
         if inp.mask is None:
@@ -113,4 +121,7 @@ def test_long_workload_sequences_and_samples(name, nseq):
         else:
             kp = oracle.masked_filter(inp.k[h].to(torch.float64).numpy(), wl.N, inp.mask[h])
             ref[sel] = oracle.circular_points(inp.u[b, h].to(torch.float64).numpy(), kp, pts[sel, 2])
-    check(gotp, ref, TOL[wl.dtype], f"{name} (samples over all sequences)")
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=16) as ex:
+        list(ex.map(one, keys))
+    check(gotp, ref, TOL[wl.dtype], f"{name} (samples over {len(keys)} sequences)")
