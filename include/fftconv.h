@@ -124,6 +124,26 @@ fftconv_status_t fftconv_fwd(const void *u, const void *K_f, const void *w, cons
                              const uint8_t *sparsity_mask, fftconv_dtype_t dtype,
                              void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): fftconv_fwd
+ * with the same arguments except the workspace, which comes from a static
+ * device array of the library (fftconv_fwd_noalloc_scratch_bytes() bytes,
+ * one copy per device, held until the process ends).  fftconv_init() must
+ * have run on the calling thread's current device (else
+ * FFTCONV_ERR_INVALID_ARGUMENT); the call then allocates nothing.  Sequences
+ * longer than the on-chip size run through the scratch in chunks of as many
+ * sequences as it holds (every supported N fits one sequence); the results are
+ * those of fftconv_fwd bit for bit.  Every call on one device shares that
+ * device's scratch, which keeps the last call's contents (nothing in it needs
+ * to start at zero): calls that may overlap in time on one device (other
+ * streams, other threads) race and must be serialised by the caller. */
+fftconv_status_t fftconv_fwd_noalloc(const void *u, const void *K_f, const void *w, const void *v,
+                                     void *out, int64_t B, int64_t H, int64_t N, int64_t L_filter,
+                                     const uint8_t *sparsity_mask, fftconv_dtype_t dtype, hipStream_t stream);
+
+/* Bytes of the static scratch of fftconv_fwd_noalloc (72 MiB). */
+size_t fftconv_fwd_noalloc_scratch_bytes(void);
+
 /* Device scratch bytes fftconv_fwd_taps needs: the prepared spectrum of the
  * H filters (fftconv_filter_bytes, rounded up to 256 bytes) followed by the
  * larger of the prepare's and the forward call's scratch.  0 for unsupported

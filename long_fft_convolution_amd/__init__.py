@@ -55,6 +55,10 @@ def _load():
     lib.fftconv_prepare_filter.restype = ctypes.c_int
     lib.fftconv_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, ctypes.c_int, vp, sz, vp]
     lib.fftconv_fwd.restype = ctypes.c_int
+    lib.fftconv_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, ctypes.c_int, vp]
+    lib.fftconv_fwd_noalloc.restype = ctypes.c_int
+    lib.fftconv_fwd_noalloc_scratch_bytes.argtypes = []
+    lib.fftconv_fwd_noalloc_scratch_bytes.restype = sz
     lib.fftconv_fwd_taps_workspace_bytes.argtypes = [i64, i64, i64, ctypes.c_int]
     lib.fftconv_fwd_taps_workspace_bytes.restype = sz
     lib.fftconv_fwd_taps.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, ctypes.c_int, vp, sz, vp]
@@ -176,6 +180,23 @@ def fftconv_fwd(u: torch.Tensor, K_f: torch.Tensor, w: torch.Tensor | None,
         dtype_code(u.dtype), _ptr(workspace),
         0 if workspace is None else workspace.numel() * workspace.element_size(),
         _stream(stream, u.device)))
+
+
+def fftconv_fwd_noalloc(u: torch.Tensor, K_f: torch.Tensor, w: torch.Tensor | None,
+                        v: torch.Tensor | None, out: torch.Tensor, L_filter: int,
+                        sparsity_mask: torch.Tensor | None = None, stream=None) -> None:
+    """fftconv_fwd with the library's static scratch instead of a workspace (after fftconv_init)."""
+    for name, t in (("u", u), ("K_f", K_f), ("w", w), ("v", v), ("out", out),
+                    ("sparsity_mask", sparsity_mask)):
+        _dev_tensor(t, name)
+    B, H, N = u.shape
+    _check(_load().fftconv_fwd_noalloc(
+        _ptr(u), _ptr(K_f), _ptr(w), _ptr(v), _ptr(out), B, H, N, L_filter, _ptr(sparsity_mask),
+        dtype_code(u.dtype), _stream(stream, u.device)))
+
+
+def fftconv_fwd_noalloc_scratch_bytes() -> int:
+    return int(_load().fftconv_fwd_noalloc_scratch_bytes())
 
 
 def fftconv_fwd_taps_workspace_bytes(B: int, H: int, N: int, dtype) -> int:

@@ -318,6 +318,41 @@ std::mutex g_ready_mu;
 std::map<int, bool> g_ready;   // devices whose every table is built
 }  // namespace
 
+// Scratch of fftconv_fwd_noalloc (the three-pass intermediate of a chunk of
+// sequences): a file-scope device array, one copy per device, held until the
+// process ends.  On the host its name is only a stand-in: the device address
+// is looked up per device by scratch_address() and only that address is ever
+// handed to kernels.
+constexpr size_t kScratchBytes = size_t(72) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+std::map<int, void *> g_scratch;   // device -> address of its copy of `scratch`
+}  // namespace
+
+// Looks the current device's address of `scratch` up (first call per device)
+// or returns the one found before.
+static hipError_t scratch_address(bool lookup, void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    auto it = g_scratch.find(dev);
+    if (it != g_scratch.end()) {
+        *out = it->second;
+        return hipSuccess;
+    }
+    *out = nullptr;
+    if (!lookup) return hipSuccess;
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = ptr;
+    *out = ptr;
+    return hipSuccess;
+}
+
 hipError_t init_device_tables() {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -386,8 +421,11 @@ const char *fftconv_last_error(void) { return g_last_error.c_str(); }
 
 fftconv_status_t fftconv_init(void) {
     g_last_error.clear();
-    const hipError_t e = init_device_tables();
+    hipError_t e = init_device_tables();
     if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "building the constant tables: %s", hipGetErrorString(e));
+    void *sp = nullptr;
+    e = scratch_address(true, &sp);
+    if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "scratch address: %s", hipGetErrorString(e));
     return ok();
 }
 
@@ -599,6 +637,38 @@ fftconv_status_t fftconv_fwd(const void *u, const void *K_f, const void *w, cons
     const int l = log2_exact(N);
     return fwd_enqueue(u, K_f, w, v, out, B, H, N, L, mask, dtype, workspace,
                        l > kFusedMaxLog ? mp_chunk(l, dtype) : 0, stream);
+}
+
+size_t fftconv_fwd_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+fftconv_status_t fftconv_fwd_noalloc(const void *u, const void *K_f, const void *w, const void *v, void *out,
+                                     int64_t B, int64_t H, int64_t N, int64_t L, const uint8_t *mask,
+                                     fftconv_dtype_t dtype, hipStream_t stream) {
+    g_last_error.clear();
+    bool empty = false;
+    const fftconv_status_t chk_st =
+        fwd_args(u, K_f, w, v, out, B, H, N, L, mask, dtype, nullptr, 0, &empty, false);
+    if (chk_st != FFTCONV_OK || empty) return chk_st;
+    void *sp = nullptr;
+    hipError_t e = scratch_address(false, &sp);
+    if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "scratch address: %s", hipGetErrorString(e));
+    if (sp == nullptr || !device_tables_ready())
+        return fail(FFTCONV_ERR_INVALID_ARGUMENT, "fftconv_init() has not run on this device");
+    const int l = log2_exact(N);
+    int64_t chunk = 0;
+    if (l > kFusedMaxLog) {
+        // as many sequences per chunk as the scratch holds (at most the usual chunk)
+        const size_t per_seq = ((size_t)N * (size_t)mp_ws_bytes(dtype) + kMpSelfBytes);
+        if (per_seq > kScratchBytes)
+            return fail(FFTCONV_ERR_UNSUPPORTED, "one sequence of N=%lld needs %zu scratch bytes, the maximum is %zu",
+                        (long long)N, per_seq, kScratchBytes);
+        chunk = (int64_t)(kScratchBytes / per_seq);
+        const int64_t usual = mp_chunk(l, dtype);
+        if (chunk > usual) chunk = usual;
+        if (overlap(sp, kScratchBytes, out, (size_t)B * H * N * elem_bytes(dtype)))
+            return fail(FFTCONV_ERR_INVALID_ARGUMENT, "out overlaps the library's scratch");
+    }
+    return fwd_enqueue(u, K_f, w, v, out, B, H, N, L, mask, dtype, sp, chunk, stream);
 }
 
 // ---- backward pass ---------------------------------------------------------
