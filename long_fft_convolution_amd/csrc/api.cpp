@@ -144,21 +144,21 @@ hipError_t get_pair_tables(PairTables *out) {
         const int g = l / 16, c = l % 16;
         for (int j = 0; j < 8; ++j) {
             const int r = rho(8 * g + j);
-            for (int nt = 0; nt < 4; ++nt) {   // S1: F64[n_s = r][f_s = 16 nt + c]
+            for (int nt = 0; nt < 4; ++nt) {   // S1: F64[n_s = r][f_s = 16 nt + c] 2^-kPairS1Log2
                 const double a = -ang((double)r * (16 * nt + c), 64);
-                f1r[(nt * 64 + l) * 8 + j] = (_Float16)std::cos(a);
-                f1i[(nt * 64 + l) * 8 + j] = (_Float16)std::sin(a);
+                f1r[(nt * 64 + l) * 8 + j] = (_Float16)std::ldexp(std::cos(a), -kPairS1Log2);
+                f1i[(nt * 64 + l) * 8 + j] = (_Float16)std::ldexp(std::sin(a), -kPairS1Log2);
             }
-            for (int mt = 0; mt < 2; ++mt) {   // S2: F32[f_f = 16 mt + c][n_f = r]
+            for (int mt = 0; mt < 2; ++mt) {   // S2: F32[f_f = 16 mt + c][n_f = r] 2^-kPairS2Log2
                 const double a = -ang((double)(16 * mt + c) * r, 32);
-                f2r[(mt * 64 + l) * 8 + j] = (_Float16)std::cos(a);
-                f2i[(mt * 64 + l) * 8 + j] = (_Float16)std::sin(a);
+                f2r[(mt * 64 + l) * 8 + j] = (_Float16)std::ldexp(std::cos(a), -kPairS2Log2);
+                f2i[(mt * 64 + l) * 8 + j] = (_Float16)std::ldexp(std::sin(a), -kPairS2Log2);
             }
-            for (int ks = 0; ks < 2; ++ks)     // S1': conj F64[f_s = 32 ks + r][n_s = 16 nt + c]
+            for (int ks = 0; ks < 2; ++ks)     // S1': conj F64[f_s = 32 ks + r][n_s = 16 nt + c] 2^-kPairS1Log2
                 for (int nt = 0; nt < 2; ++nt) {
                     const double a = ang((double)(32 * ks + r) * (16 * nt + c), 64);
-                    f3r[((ks * 2 + nt) * 64 + l) * 8 + j] = (_Float16)std::cos(a);
-                    f3i[((ks * 2 + nt) * 64 + l) * 8 + j] = (_Float16)std::sin(a);
+                    f3r[((ks * 2 + nt) * 64 + l) * 8 + j] = (_Float16)std::ldexp(std::cos(a), -kPairS1Log2);
+                    f3i[((ks * 2 + nt) * 64 + l) * 8 + j] = (_Float16)std::ldexp(std::sin(a), -kPairS1Log2);
                 }
         }
         for (int i = 0; i < 4; ++i) {
@@ -217,10 +217,10 @@ hipError_t get_pair3_tables(Pair3Tables *out) {
     for (int l = 0; l < 64; ++l) {
         const int g = l / 16, c = l % 16;
         for (int t = 0; t < 2; ++t)
-            for (int j = 0; j < 8; ++j) {   // DFT-32 tile t: w32^{rho(8g+j) (16 t + c)}
+            for (int j = 0; j < 8; ++j) {   // DFT-32 tile t: w32^{rho(8g+j) (16 t + c)} 2^-kDft32Log2
                 const double a = -2.0 * pi * (double)rho(8 * g + j) * (16 * t + c) / 32.0;
-                fr[(t * 64 + l) * 8 + j] = (_Float16)std::cos(a);
-                fi[(t * 64 + l) * 8 + j] = (_Float16)std::sin(a);
+                fr[(t * 64 + l) * 8 + j] = (_Float16)std::ldexp(std::cos(a), -kDft32Log2);
+                fi[(t * 64 + l) * 8 + j] = (_Float16)std::ldexp(std::sin(a), -kDft32Log2);
             }
         for (int i = 0; i < 4; ++i) {
             for (int mt = 0; mt < 2; ++mt)      // rows n_a = 16mt + 4g + i, cols f_b = 16nt + c

@@ -85,6 +85,22 @@ __host__ __device__ inline int64_t pair_kf_index(int64_t f) {
     const int64_t mt2 = ff / 16, g = (ff % 16) / 4, i = ff % 4, nt = fs / 16, c = fs % 16;
     return (((mt2 * 4 + nt) * 64 + g * 16 + c) * 8) + i;
 }
+// Power-of-two factors 2^-k folded into the fp16 DFT operand tables of the
+// matrix-core kernels.  With them each fp16 stage result stays within a small
+// factor of its input's magnitude (unnormalised stages would grow the
+// zero-frequency bin of a sequence with mean m to N * m, past the fp16 range
+// for m above a few units); every kernel multiplies its fp32 output scale by
+// 2^k for each stage it ran.
+constexpr int kPairS1Log2 = 3;   // DFT-64 blocks (S1, S1') of the N = 1024 kernel
+constexpr int kPairS2Log2 = 2;   // DFT-32 blocks (S2, S2') of the N = 1024 kernel
+constexpr int kDft32Log2 = 2;    // DFT-32 tiles of the N = 16384 kernel and of the multi-pass row pass
+// The multi-pass row pass multiplies stored filter bins (|K s_h| <= 2^14 for
+// that layout) by 2^-kRowKLog2 in its product, so |product| <= |spectrum|; the
+// rest of the channel scale is applied by the last pass in fp32.
+constexpr int kRowKLog2 = 14;
+// Column-pass factor of the half-precision three-pass path: 2^-p1 with
+// p1 = floor((log2 N1 - 1) / 2) + 1 (about 1/sqrt of the N1/2 summed terms)
+inline __host__ __device__ constexpr int mp_p1_log2(int log1) { return (log1 - 1) / 2 + 1; }
 inline size_t bin_bytes(int st) { return st == ST_F32 ? 8 : 4; }
 inline size_t kf_scale_off() { return kKfHeaderBytes; }
 inline size_t kf_bins_off(int64_t H) { return kKfHeaderBytes + align_up((size_t)H * 4, 256); }

@@ -165,6 +165,10 @@ mp_pass1_kernel(const T *__restrict__ src, const T *__restrict__ gate, int64_t L
     const int64_t s = seq0 + blockIdx.y;
     const T *row = src + s * (SRC_FILTER ? L : NC);
     const T *grow = (!SRC_FILTER && gate != nullptr) ? gate + s * NC : nullptr;
+    // the half-precision convolution path stores the column transform scaled by
+    // 2^-p1 (about 1/sqrt of the N1/2 summed terms), undone by pass 3
+    constexpr bool kHalfConv = !SRC_FILTER && sizeof(T) == 2;
+    const float p1 = kHalfConv ? __builtin_ldexpf(1.f, -mp_p1_log2(LOG1)) : 1.f;
 
     // stage 1: lane (col, n_a = j), RB-point DFT over n_b (upper half zero).
     // Element m = n2 + N2 (j + RA n_b): uniform part c0 + N2 RA n_b, lane part
@@ -187,6 +191,7 @@ mp_pass1_kernel(const T *__restrict__ src, const T *__restrict__ gate, int64_t L
                     const float2 g = io<T>::load2(grow + 2 * mu, lo);
                     t = make_float2(t.x * g.x, t.y * g.y);
                 }
+                if (kHalfConv) t = make_float2(t.x * p1, t.y * p1);
             }
             z[nb] = t;
         }
@@ -216,10 +221,13 @@ mp_pass1_kernel(const T *__restrict__ src, const T *__restrict__ gate, int64_t L
 }
 
 // ---------------------------------------------------------------- pass 3
-template <int LOG1, typename T>
+// SCALED (half-precision storage): the outputs are multiplied by the part of the
+// channel scale the row pass left out and the inverse of the column-pass and
+// table factors: kscale[h] 2^(kRowKLog2 + 4 kDft32Log2 + p1).
+template <int LOG1, typename T, bool SCALED>
 __global__ void __launch_bounds__(kMpThreads, 4)
 mp_pass3_kernel(const T *__restrict__ ws, const T *__restrict__ v, T *__restrict__ out,
-                int64_t seq0, MpArgs ta) {
+                int64_t seq0, MpArgs ta, const float *__restrict__ kscale, int64_t H) {
     using P = ColPlan<LOG1>;
     constexpr int N1 = P::N1, RA = P::RA, RB = P::RB, C = P::C, N2 = 1 << kMpLog2;
     constexpr int64_t NC = (int64_t)N1 * N2;
@@ -278,6 +286,11 @@ mp_pass3_kernel(const T *__restrict__ ws, const T *__restrict__ v, T *__restrict
         }
     } else {
         dft_halfout<RB>(e, r);
+    }
+    if (SCALED) {
+        const float comp = __builtin_ldexpf(kscale[s % H], kRowKLog2 + 4 * kDft32Log2 + mp_p1_log2(LOG1));
+#pragma unroll
+        for (int nb = 0; nb < RB / 2; ++nb) r[nb] = make_float2(r[nb].x * comp, r[nb].y * comp);
     }
     T *orow = out + s * NC;
     const uint32_t lo2 = (uint32_t)(launder(col) + N2 * launder(j));
@@ -831,8 +844,10 @@ mp_pass2m_kernel(T *__restrict__ ws, float2 *__restrict__ self_area, const __hal
         }
 
     // S2 (const A: F rows f_a; data B: T1, K = n_a) tile pair by tile pair, the
-    // bin-pair step on (A tile (m2, n), mirrored B tile (1 - m2, 1 - n))
-    const float ks = kscale[h];
+    // bin-pair step on (A tile (m2, n), mirrored B tile (1 - m2, 1 - n)).  The
+    // stored bins (|K s_h| <= 2^14) enter the product times 2^-kRowKLog2; pass 3
+    // applies the channel scale.
+    const float ks = __builtin_ldexpf(1.f, -kRowKLog2);
     const __half2 *kA = kbins + h * NC + (int64_t)rowA * N2 + fcA * 1024;
     const __half2 *kB = kbins + h * NC + (int64_t)rowB * N2 + fcB * 1024;
     const uint32_t maddr = 4u * (63u - ul);
@@ -1092,7 +1107,8 @@ static hipError_t conv_t(const void *u, const void *w, const void *v, void *out,
     T *ws = (T *)work;
     float2 *self_area = (float2 *)((char *)work + (size_t)nseq * ((size_t)1 << (LOG1 + kMpLog2)) * 2 * sizeof(T));
     auto k1 = mp_pass1_kernel<LOG1, T, false>;
-    auto k3 = mp_pass3_kernel<LOG1, T>;
+    constexpr bool kHalf = std::is_same<TK, __half2>::value;
+    auto k3 = mp_pass3_kernel<LOG1, T, kHalf>;
     if ((e = allow_lds(k1, P::kLds)) != hipSuccess) return e;
     if ((e = allow_lds(k3, P::kLds)) != hipSuccess) return e;
     hipLaunchKernelGGL(k1, dim3(N2 / P::C, (unsigned)nseq), dim3(kMpThreads), P::kLds, stream,
@@ -1117,7 +1133,7 @@ static hipError_t conv_t(const void *u, const void *w, const void *v, void *out,
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k3, dim3(N2 / P::C, (unsigned)nseq), dim3(kMpThreads), P::kLds, stream,
-                       (const T *)ws, (const T *)v, (T *)out, seq0, ta);
+                       (const T *)ws, (const T *)v, (T *)out, seq0, ta, kscale, H);
     return hipGetLastError();
 }
 

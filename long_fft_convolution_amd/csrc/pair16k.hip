@@ -287,7 +287,8 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
 
     for (; p < p_end; p += wg_on_xcd) {
         const int64_t h = __builtin_amdgcn_readfirstlane((uint32_t)p / (uint32_t)PB);
-        const float ks = kscale[h];
+        // (the six stages' table factors are undone with the channel scale)
+        const float ks = __builtin_ldexpf(kscale[h], 6 * kDft32Log2);
         int64_t p_nx = p + wg_on_xcd, oa_nx, ob_nx;
         bool hb_nx;
         pair_base(p_nx < p_end ? p_nx : p, oa_nx, ob_nx, hb_nx);

@@ -360,7 +360,8 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
         for (int mt2 = 0; mt2 < 2; ++mt2)
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) fk.k[mt2][nt] = krow[(mt2 * 4 + nt) * 64 + lane];
-        fk.ks = kscale[h];
+        // (the four stages' table factors are undone with the channel scale)
+        fk.ks = __builtin_ldexpf(kscale[h], 2 * (kPairS1Log2 + kPairS2Log2));
     };
     auto load_gate = [&](const T *gp, int64_t oa, int64_t ob, uint4 (&vg)[4]) {
 #pragma unroll
@@ -893,7 +894,9 @@ pair1k_dk_kernel(const T *__restrict__ dy, const T *__restrict__ u, const T *__r
         for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
         // scale 2^-e with max |S| 2^-e <= 1: the fp16 operands of the inverse chain
         const int ex = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx) : 0;
-        const float sc = __builtin_ldexpf(1.f, -ex), back = __builtin_ldexpf(1.f, ex) / (float)M;
+        // (back also undoes the table factors of the two forward chains and the inverse one)
+        const float sc = __builtin_ldexpf(1.f, -ex),
+                    back = __builtin_ldexpf(1.f, ex + 3 * (kPairS1Log2 + kPairS2Log2)) / (float)M;
         // S2': rows f_s (tile nt), column tiles nt2 of n_f; conj twiddle (as in the forward kernel)
         h8 a3r[2][2], a3i[2][2];
 #pragma unroll
