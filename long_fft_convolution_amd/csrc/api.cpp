@@ -209,7 +209,8 @@ hipError_t get_pair3_tables(Pair3Tables *out) {
     const double pi = 3.14159265358979323846264338327950288;
     const double M2 = 32768.0;
     std::vector<_Float16> fr(2 * 64 * 8), fi(2 * 64 * 8), tw1(4 * 64 * 8), tw3(4 * 64 * 8),
-        two1((size_t)64 * 2 * 64 * 8), two2((size_t)32 * 4 * 64 * 8);
+        two1((size_t)64 * 2 * 64 * 8), two2((size_t)32 * 4 * 64 * 8), far_(2 * 64 * 8), fai_(2 * 64 * 8),
+        fbr_(2 * 64 * 8), fbi_(2 * 64 * 8);
     auto put8 = [](std::vector<_Float16> &v, size_t chunk, int i, double ang) {
         v[chunk * 8 + i] = (_Float16)std::cos(ang);
         v[chunk * 8 + 4 + i] = (_Float16)std::sin(ang);
@@ -221,6 +222,13 @@ hipError_t get_pair3_tables(Pair3Tables *out) {
                 const double a = -2.0 * pi * (double)rho(8 * g + j) * (16 * t + c) / 32.0;
                 fr[(t * 64 + l) * 8 + j] = (_Float16)std::ldexp(std::cos(a), -kDft32Log2);
                 fi[(t * 64 + l) * 8 + j] = (_Float16)std::ldexp(std::sin(a), -kDft32Log2);
+                // row-pass tiles with f_a in the order row_fa (A: rows; B: K slots)
+                const double aa = -2.0 * pi * (double)rho(8 * g + j) * row_fa(t, c) / 32.0;
+                far_[(t * 64 + l) * 8 + j] = (_Float16)std::ldexp(std::cos(aa), -kDft32Log2);
+                fai_[(t * 64 + l) * 8 + j] = (_Float16)std::ldexp(std::sin(aa), -kDft32Log2);
+                const double ab = -2.0 * pi * (double)row_fa(j / 4, 4 * g + j % 4) * (16 * t + c) / 32.0;
+                fbr_[(t * 64 + l) * 8 + j] = (_Float16)std::ldexp(std::cos(ab), -kDft32Log2);
+                fbi_[(t * 64 + l) * 8 + j] = (_Float16)std::ldexp(std::sin(ab), -kDft32Log2);
             }
         for (int i = 0; i < 4; ++i) {
             for (int mt = 0; mt < 2; ++mt)      // rows n_a = 16mt + 4g + i, cols f_b = 16nt + c
@@ -251,6 +259,10 @@ hipError_t get_pair3_tables(Pair3Tables *out) {
     if (e == hipSuccess) e = upload_h(tw3, &t.tw3);
     if (e == hipSuccess) e = upload_h(two1, &t.two1);
     if (e == hipSuccess) e = upload_h(two2, &t.two2);
+    if (e == hipSuccess) e = upload_h(far_, &t.far_);
+    if (e == hipSuccess) e = upload_h(fai_, &t.fai_);
+    if (e == hipSuccess) e = upload_h(fbr_, &t.fbr_);
+    if (e == hipSuccess) e = upload_h(fbi_, &t.fbi_);
     if (e != hipSuccess) return e;
     g_pair3_tables[dev] = t;
     *out = t;

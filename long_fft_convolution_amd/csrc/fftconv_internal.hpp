@@ -41,7 +41,7 @@ struct KfHeader {
     int64_t n2;   // multi-pass inner size
 };
 constexpr uint32_t kKfMagic = 0x4b544646u;  // "FFTK"
-constexpr uint32_t kKfVersion = 2;
+constexpr uint32_t kKfVersion = 3;
 constexpr size_t kKfHeaderBytes = 256;
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -116,17 +116,27 @@ int64_t mp_ws_bytes(int st);
 // fp32 area per sequence for the two self-paired rows of the row pass
 constexpr size_t kMpSelfBytes = 2 * 8192 * 8;
 int64_t mp_chunk(int logn, int st);
+// The row pass of the half-precision multi-pass path computes the last forward
+// stage (over n_a, producing the most significant digit f_a of the in-row bin)
+// as two 16-row matrix tiles; tile m2, row r (r < 16) holds
+//   f_a = row_fa(m2, r):  m2 = 0: 0..7 and 24..31,   m2 = 1: 8..23,
+// so that the middle frequencies of a row (which a low-pass frequency mask
+// drops for both bins of every bin pair) fill one whole tile.  The partner of
+// f_a, 31 - f_a, is row 15 - r of the same tile.
+__host__ __device__ inline int row_fa(int m2, int r) { return m2 ? 8 + r : (r < 8 ? r : 16 + r); }
+__host__ __device__ inline int row_tile_of(int fa) { return (fa >= 8 && fa < 24) ? 1 : 0; }
+__host__ __device__ inline int row_r_of(int fa) { return fa < 8 ? fa : (fa < 24 ? fa - 8 : fa - 16); }
 // Position of in-row bin f2 (row length 8192) in a multi-pass spectrum stored
 // in half precision.  Such spectra are kept in the order the matrix-core row
 // pass produces them: f2 = f_c + 8 f_b + 256 f_a with f_b = 16 nt + c and
-// f_a = 16 mt2 + 4 g + i sits at f_c * 1024 + (2 mt2 + nt) * 256 +
+// f_a = row_fa(mt2, 4 g + i) sits at f_c * 1024 + (2 mt2 + nt) * 256 +
 // (16 g + c) * 4 + i, so that lane 16 g + c of the wave that owns chain f_c
 // reads the four bins i of tile (mt2, nt) as one 16-byte word.  Bin 0 stays at
 // position 0.  fp32 spectra keep the natural order.
 __host__ __device__ inline uint32_t mp_chain_pos(uint32_t f2) {
     const uint32_t fc = f2 & 7u, fb = (f2 >> 3) & 31u, fa = f2 >> 8;
-    return fc * 1024u + ((fa >> 4) * 2u + (fb >> 4)) * 256u + (16u * ((fa >> 2) & 3u) + (fb & 15u)) * 4u +
-           (fa & 3u);
+    const uint32_t mt2 = (uint32_t)row_tile_of((int)fa), r = (uint32_t)row_r_of((int)fa);
+    return fc * 1024u + (mt2 * 2u + (fb >> 4)) * 256u + (16u * (r >> 2) + (fb & 15u)) * 4u + (r & 3u);
 }
 
 // Per-device, per-size tables (allocated once, read only afterwards).
@@ -185,6 +195,11 @@ struct Pair3Tables {
     const void *tw3;         // inner conj twiddles, [nt][nt2][lane]
     const void *two1;        // outer twiddles wM^{f_c n_ab}, [64 T][2 nt][lane], n_ab = 16(T & ~1) + 2c + (T & 1)
     const void *two2;        // outer conj twiddles, [32 f_c][2 nt3][2 nt2][lane]
+    // the multi-pass row pass's last forward stage and first inverse stage, with
+    // f_a in the tile order row_fa: A operand [m2][64 lanes][8] (row f_a = row_fa(m2, c),
+    // K slot 8g + j <-> n_a = rho(8g + j)) and B operand [n2][64][8] (column
+    // n_a = 16 n2 + c, K slot 8g + j <-> f_a = row_fa(j / 4, 4g + j % 4))
+    const void *far_, *fai_, *fbr_, *fbi_;
 };
 hipError_t get_pair3_tables(Pair3Tables *out);
 // with out2: also out2 = v2 * conv(u w, k) from the same transforms (v and v2 non-null)

@@ -728,6 +728,9 @@ struct MmTables {
     const void *fr, *fi;   // DFT-32 operand tiles [2][64 lanes] x 8 fp16
     const void *tw1;       // w1024^{n_a f_b} in the S1 output layout [mt][nt][lane]: cos[4], sin[4]
     const void *tw3;       // conj of w1024^{n_a f_b} in the S2'' output layout [nt][nt2][lane]
+    // S2 (A operand, rows f_a in the tile order row_fa) and S2'' (B operand, K slots
+    // f_a in that order): DFT-32 tiles [2][64 lanes] x 8 fp16 (re, im)
+    const void *far_, *fai_, *fbr_, *fbi_;
 };
 
 // grid (N1 / 2, nseq); block 512; dynamic LDS mm::kLds.
@@ -818,16 +821,19 @@ mp_pass2m_kernel(T *__restrict__ ws, float2 *__restrict__ self_area, const __hal
     // every wave has its operands; R1 becomes R2 below
     __syncthreads();
 
-    // the DFT-32 operand tiles (the negated imaginary plane is formed where it is used)
-    h8 Fr[2], Fi[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        Fr[t] = ldu<h8>(mt.fr, 16u * (t * 64 + ul));
-        Fi[t] = ldu<h8>(mt.fi, 16u * (t * 64 + ul));
-    }
+    // the DFT-32 operand tiles are read (from the L1 cache) where each stage uses them,
+    // so that none is held across the bin-pair step; the negated imaginary plane is
+    // formed where it is used
+    auto ftile = [&](const void *tab, int t) { return ldu<h8>(tab, 16u * (t * 64 + ul)); };
 
     // S1 (data A: rows n_a, K = n_b; const B: F, N = f_b) and the twiddle w1024^{n_a f_b}
     h4 t1r[2][2][2], t1i[2][2][2];   // [chain][mt][nt]
+    h8 Fr[2], Fi[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        Fr[t] = ftile(mt.fr, t);
+        Fi[t] = ftile(mt.fi, t);
+    }
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -853,8 +859,13 @@ mp_pass2m_kernel(T *__restrict__ ws, float2 *__restrict__ self_area, const __hal
     const uint32_t maddr = 4u * (63u - ul);
     // keep bits of this lane's 16 bins of row A (bit 4 (2 m2 + n) + e) and of their
     // row-B partners (bit 16 + the same); the block of A's bin is
-    // 64 m2 + 16 g + 4 e + 2 n + (c >> 3), its partner's 127 minus that
+    // 4 f_a + 2 n + (c >> 3) with f_a = row_fa(m2, 4 g + e), its partner's 127 minus that
     uint32_t kbits = 0xffffffffu;
+    // skip[m2]: no bin of tile m2 (row A) nor of its partners (row B) is kept by the
+    // mask, in any lane: the pair's products are zero, so the tile's S2 products,
+    // filter loads and bin-pair step are skipped (the same for every wave: a bin's
+    // block does not depend on f_c)
+    bool skip[2] = {false, false};
     if (MASKED) {
         kbits = 0;
 #pragma unroll
@@ -863,14 +874,18 @@ mp_pass2m_kernel(T *__restrict__ ws, float2 *__restrict__ self_area, const __hal
             for (int n = 0; n < 2; ++n)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int b = 64 * m2 + 16 * g + 4 * e + 2 * n + (c >> 3);
+                    const int b = 4 * row_fa(m2, 4 * g + e) + 2 * n + (c >> 3);
                     const int bit = 4 * (2 * m2 + n) + e;
                     kbits |= (bm.keep(b) ? 1u : 0u) << bit;
                     kbits |= (bm.keep(127 - b) ? 1u : 0u) << (16 + bit);
                 }
+#pragma unroll
+        for (int m2 = 0; m2 < 2; ++m2)
+            skip[m2] = __builtin_amdgcn_ballot_w64((((kbits >> (8 * m2)) | (kbits >> (16 + 8 * m2))) & 0xffu) != 0) == 0;
     }
-    // twiddle of A's bin f2 = f_c + 8 (16 n + c) + 256 (16 m2 + 4 g + e):
-    // omega_2N^{rowA + N1 f2} = w2row[rowA] omega_{2 N2}^{f2}
+    // twiddle of A's bin f2 = f_c + 8 (16 n + c) + 256 f_a, f_a = row_fa(m2, 4 g + e):
+    // omega_2N^{rowA + N1 f2} = w2row[rowA] omega_{2 N2}^{f2}; row_fa adds 16 to 4 g + e
+    // in tile 0 for g >= 2 (omega_{2 N2}^{4096} = -i) and 8 in tile 1 (omega_{2 N2}^{2048})
     const float2 wbase = cmul(ta.w2row[rowA], ldu<float2>(ta.w2n2, 8u * (uint32_t)(fcA + 8 * c + 1024 * g)));
     float2 *const area = self_area + (int64_t)sq * 2 * N2;
     // conj(Z') of the wave's two chains as fp16 tiles in LDS (the R2 region, free
@@ -890,10 +905,11 @@ mp_pass2m_kernel(T *__restrict__ ws, float2 *__restrict__ self_area, const __hal
 #pragma unroll
                 for (int m2 = 0; m2 < 2; ++m2) {
                     f4 zr, zi;
-                    cm_constA(Fr[m2], Fi[m2], neg8(Fi[m2]), br, bi, zr, zi);
+                    const h8 far_ = ftile(mt.far_, m2), fai_ = ftile(mt.fai_, m2);
+                    cm_constA(far_, fai_, neg8(fai_), br, bi, zr, zi);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const int f = (qc ? fcB : fcA) + 8 * (16 * n + c) + 256 * (16 * m2 + 4 * g + e);
+                        const int f = (qc ? fcB : fcA) + 8 * (16 * n + c) + 256 * row_fa(m2, 4 * g + e);
                         area[qc * N2 + f] = make_float2(zr[e], zi[e]);
                     }
                 }
@@ -910,8 +926,8 @@ mp_pass2m_kernel(T *__restrict__ ws, float2 *__restrict__ self_area, const __hal
                 f4 ra, ia, rb, ib;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int fA = fcA + 8 * (16 * n + c) + 256 * (16 * m2 + 4 * g + e);
-                    const int fB = fcB + 8 * (16 * n + c) + 256 * (16 * m2 + 4 * g + e);
+                    const int fA = fcA + 8 * (16 * n + c) + 256 * row_fa(m2, 4 * g + e);
+                    const int fB = fcB + 8 * (16 * n + c) + 256 * row_fa(m2, 4 * g + e);
                     const float2 va = area[fA], vb = area[N2 + fB];
                     ra[e] = va.x;
                     ia[e] = va.y;
@@ -930,7 +946,18 @@ mp_pass2m_kernel(T *__restrict__ ws, float2 *__restrict__ self_area, const __hal
                 // (a scheduling fence per tile pair keeps the next pair's products and
                 // loads from being hoisted here, which would exceed the register budget)
                 __builtin_amdgcn_sched_barrier(0);
-                const int mb = 1 - m2, nb = 1 - n;
+                // A's tile (m2, n) pairs with B's tile (m2, 1 - n): f_a -> 31 - f_a stays in
+                // its tile (row_fa), f_b -> 31 - f_b flips the column tile
+                const int mb = m2, nb = 1 - n;
+                if (MASKED && skip[m2]) {
+                    // every product of this tile pair is zero: its S2 products, filter loads
+                    // and bin-pair step are skipped (frequency-sparse filter)
+                    const h4 z4 = {(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
+                    yput(0, m2, n, ul, z4, z4);
+                    yput(1, mb, nb, ul, z4, z4);
+                    continue;
+                }
+                const h8 far_ = ftile(mt.far_, m2), fai_ = ftile(mt.fai_, m2);
                 // filter bins: A's tile (m2, n) and B's tile (mb, nb) read from lane 63 - l
                 uint4 qa, qb;
                 const uint32_t ea = 16u * ((m2 * 2 + n) * 64 + ul), eb = 16u * ((mb * 2 + nb) * 64 + (63u - ul));
@@ -948,12 +975,12 @@ mp_pass2m_kernel(T *__restrict__ ws, float2 *__restrict__ self_area, const __hal
                 f4 zr, zi, mr, mi;
                 {
                     const h8 br = cat8(t1r[0][0][n], t1r[0][1][n]), bi = cat8(t1i[0][0][n], t1i[0][1][n]);
-                    cm_constA(Fr[m2], Fi[m2], neg8(Fi[m2]), br, bi, zr, zi);
+                    cm_constA(far_, fai_, neg8(fai_), br, bi, zr, zi);
                 }
                 {
                     f4 pr, pi;
                     const h8 br = cat8(t1r[1][0][nb], t1r[1][1][nb]), bi = cat8(t1i[1][0][nb], t1i[1][1][nb]);
-                    cm_constA(Fr[mb], Fi[mb], neg8(Fi[mb]), br, bi, pr, pi);
+                    cm_constA(far_, fai_, neg8(fai_), br, bi, pr, pi);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         mr[e] = __uint_as_float(bperm(maddr, __float_as_uint(pr[3 - e])));
@@ -969,8 +996,9 @@ mp_pass2m_kernel(T *__restrict__ ws, float2 *__restrict__ self_area, const __hal
                         kb[e] &= 0u - ((kbits >> (16 + kb0 + e)) & 1u);
                     }
                 }
-                float2 wt = cmul(wbase, make_float2(n ? kW128c : 1.f, n ? kW128s : 0.f));
-                if (m2) wt = cmul_negi(wt);
+                const float2 wm = m2 ? cmul(wbase, make_float2(7.071067812e-01f, -7.071067812e-01f))
+                                     : (g >= 2 ? cmul_negi(wbase) : wbase);
+                const float2 wt = cmul(wm, make_float2(n ? kW128c : 1.f, n ? kW128s : 0.f));
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float2 Ka = cscale(h2f(ka[e]), ks), Kb = cscale(h2f(kb[e]), ks);
@@ -1001,7 +1029,9 @@ mp_pass2m_kernel(T *__restrict__ ws, float2 *__restrict__ self_area, const __hal
 #pragma unroll
             for (int n2 = 0; n2 < 2; ++n2) {
                 f4 cr, ci;
-                cm_dataA(dr, di, Fr[n2], Fi[n2], neg8(Fi[n2]), cr, ci);
+                // K slots 8g + j: f_a = row_fa(j / 4, 4g + j % 4), the order of the Y tiles
+                const h8 fbr = ftile(mt.fbr_, n2), fbi = ftile(mt.fbi_, n2);
+                cm_dataA(dr, di, fbr, fbi, neg8(fbi), cr, ci);
                 t3r[qc][n][n2] = to_h4(cr);
                 t3i[qc][n][n2] = to_h4(ci);
                 h8 tw = ldu<h8>(mt.tw3, 16u * ((n * 2 + n2) * 64 + ul));
@@ -1025,7 +1055,8 @@ mp_pass2m_kernel(T *__restrict__ ws, float2 *__restrict__ self_area, const __hal
 #pragma unroll
             for (int n3 = 0; n3 < 2; ++n3) {
                 f4 cr, ci;
-                cm_constA(Fr[n3], Fi[n3], neg8(Fi[n3]), br, bi, cr, ci);   // rows n_b = 16 n3 + 4g + e, col n_a
+                const h8 fr3 = ftile(mt.fr, n3), fi3 = ftile(mt.fi, n3);
+                cm_constA(fr3, fi3, neg8(fi3), br, bi, cr, ci);   // rows n_b = 16 n3 + 4g + e, col n_a
                 float2 bt = b0;
                 if (n2) bt = cmul(bt, s16);
                 if (n3) bt = cmul(bt, s512);
@@ -1119,7 +1150,7 @@ static hipError_t conv_t(const void *u, const void *w, const void *v, void *out,
         // half-precision storage: the row pass on the matrix cores
         Pair3Tables p3{};
         if ((e = get_pair3_tables(&p3)) != hipSuccess) return e;
-        const MmTables mt{p3.fr, p3.fi, p3.tw1, p3.tw3};
+        const MmTables mt{p3.fr, p3.fi, p3.tw1, p3.tw3, p3.far_, p3.fai_, p3.fbr_, p3.fbi_};
         auto k2 = mask != nullptr ? mp_pass2m_kernel<LOG1, T, true> : mp_pass2m_kernel<LOG1, T, false>;
         if ((e = allow_lds(k2, mm::kLds)) != hipSuccess) return e;
         hipLaunchKernelGGL(k2, g2, dim3(kMpThreads), mm::kLds, stream, ws, self_area, (const __half2 *)kbins,

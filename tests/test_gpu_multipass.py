@@ -149,3 +149,19 @@ def test_multipass_largest_size_masked_partial():
     y = run_gpu(inp, inp.mask)
     ref = oracle.fft_conv(inp.f64("u"), inp.f64("k"), mask=inp.mask)
     check(y, ref, TOL["f16"])
+
+
+@pytest.mark.parametrize("keep", [(0, 27), (40, 88), (0, 128), (100, 128)])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_multipass_band_masks_half(keep, dtype):
+    # contiguous kept bands: low (the 79 % mask: the row pass skips its middle-frequency
+    # tile), middle (it skips the other tile), all (nothing skipped), high
+    N, H = 1 << 19, 3
+    lo, hi = keep
+    _say(f"multipass band mask {lo}..{hi} {dtype}")
+    inp = synth.generate(1, H, N, 1 << 17, dtype, gated=False, seed=lo + hi)
+    mask = np.zeros((H, 128), dtype=np.uint8)
+    mask[:, lo:hi] = 1
+    y = run_gpu(inp, mask)
+    ref = oracle.fft_conv(inp.f64("u"), inp.f64("k"), mask=mask)
+    check(y, ref, TOL[dtype])
