@@ -377,7 +377,8 @@ def bench_eqlinear(args):
     log(f"bench: generating {wl.name} (N={wl.N} T={wl.T} C_in={wl.C_in} C_out={wl.C_out} {wl.dtype})")
     x_h, W_h = synth.generate_eq(wl.name)
     x, W = x_h.to(dev), W_h.to(dev)
-    W_f = torch.empty(fc.fftconv_eqlinear_weight_bytes(wl.T, wl.C_out, wl.C_in), dtype=torch.uint8, device=dev)
+    W_f = torch.empty(fc.fftconv_eqlinear_weight_bytes(wl.T, wl.C_out, wl.C_in, x.dtype), dtype=torch.uint8,
+                      device=dev)
     fc.fftconv_eqlinear_prepare(W, W_f)
     y = torch.empty((wl.N, wl.T, wl.C_out), dtype=x.dtype, device=dev)
     n_warm = warm_up(lambda: fc.fftconv_eqlinear_fwd(x, W_f, y), args.warmup, dev)
@@ -388,8 +389,13 @@ def bench_eqlinear(args):
     flops = 2.0 * wl.N * wl.C_in * wl.C_out * (2 + 4 * (wl.T // 2 - 1))
     value = wl.N * wl.T * wl.C_in / (ms / 1e3)
     achieved = alg / (ms / 1e3) / 1e9
+    tflops = flops / (ms / 1e3) / 1e12
+    # the bound: HBM for fp16 operands (dense fp16 peak 2.5 PFLOP/s), the fp32 matrix cores
+    # (157.3 TFLOP/s dense) for fp32, whichever takes longer at its peak
+    mfma_peak = 157.3 if wl.dtype == "f32" else 2500.0
+    bound = "mfma" if flops / (mfma_peak * 1e12) > alg / (HBM_PEAK_GBS * 1e9) else "hbm"
     log(f"bench: {ms * 1e3:.1f} us/step, {value:.3e} elems/s, {achieved:.0f} GB/s algorithmic "
-        f"({achieved / HBM_PEAK_GBS:.1%} of 8 TB/s), MFMA {flops / (ms / 1e3) / 1e12:.1f} TFLOP/s")
+        f"({achieved / HBM_PEAK_GBS:.1%} of 8 TB/s), MFMA {tflops:.1f} TFLOP/s ({tflops / mfma_peak:.1%} of {mfma_peak})")
     if args.calibrate_copy:
         n = (alg // 2) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -411,14 +417,22 @@ def bench_eqlinear(args):
         "metric": "group-axis circular conv fwd N*T*C_in elems/s + % HBM peak, 1 GPU",
         "value": value, "unit": "elems/s", "n_gpus": 1, "steps": args.steps, "warmup": n_warm,
         "warmup_min": args.warmup,
-        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32" if wl.dtype == "f32" else "f16",
         "data": "synthetic (seeded N(0,1) activations, N(0, 1/(T C_in)) weights)",
         "config": {"workload": wl.name, "N": wl.N, "T": wl.T, "C_in": wl.C_in, "C_out": wl.C_out,
-                   "storage": wl.dtype, "arithmetic": "fp16 MFMA operands, fp32 accumulation",
+                   "storage": wl.dtype,
+                   "arithmetic": ("fp32 MFMA operands, fp32 accumulation" if wl.dtype == "f32"
+                                  else "fp16 MFMA operands, fp32 accumulation"),
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "eqlinear_kernel", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name),
-                     "algorithmic_bytes": int(alg), "kernel_ms": ms, "mfma_tflops": flops / (ms / 1e3) / 1e12},
+        "roofline": ({"bound": "hbm", "kernel": "eqlinear_kernel", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name),
+                      "algorithmic_bytes": int(alg), "kernel_ms": ms, "mfma_tflops": tflops}
+                     if bound == "hbm" else
+                     {"bound": "mfma", "kernel": "eqlinear32_kernel", "achieved": tflops, "peak": mfma_peak,
+                      "unit": "TFLOP/s", "frac": tflops / mfma_peak, "traffic": measured_traffic(wl.name),
+                      "algorithmic_flops": flops, "algorithmic_bytes": int(alg), "kernel_ms": ms,
+                      "hbm_gbs": achieved}),
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

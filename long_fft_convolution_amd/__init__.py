@@ -82,7 +82,7 @@ def _load():
     lib.fftconv_prepare_short_filter.restype = ctypes.c_int
     lib.fftconv_fwd_short.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, vp]
     lib.fftconv_fwd_short.restype = ctypes.c_int
-    lib.fftconv_eqlinear_weight_bytes.argtypes = [i64, i64, i64]
+    lib.fftconv_eqlinear_weight_bytes.argtypes = [i64, i64, i64, ctypes.c_int]
     lib.fftconv_eqlinear_weight_bytes.restype = sz
     lib.fftconv_eqlinear_prepare.argtypes = [vp, i64, i64, i64, ctypes.c_int, vp, sz, vp]
     lib.fftconv_eqlinear_prepare.restype = ctypes.c_int
@@ -289,8 +289,9 @@ def causal_conv_short(u, k, w=None, v=None, stream=None):
     return out
 
 
-def fftconv_eqlinear_weight_bytes(T: int, C_out: int, C_in: int) -> int:
-    return int(_load().fftconv_eqlinear_weight_bytes(T, C_out, C_in))
+def fftconv_eqlinear_weight_bytes(T: int, C_out: int, C_in: int, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    return int(_load().fftconv_eqlinear_weight_bytes(T, C_out, C_in, code))
 
 
 def fftconv_eqlinear_prepare(W: torch.Tensor, W_f: torch.Tensor, stream=None) -> None:
@@ -316,7 +317,7 @@ def fftconv_eqlinear_fwd(x: torch.Tensor, W_f: torch.Tensor, y: torch.Tensor, st
 def eqlinear(x, W, stream=None):
     """Prepare W and run the group convolution once (allocations by torch)."""
     T, C_out, C_in = W.shape
-    W_f = torch.empty(fftconv_eqlinear_weight_bytes(T, C_out, C_in), dtype=torch.uint8, device=x.device)
+    W_f = torch.empty(fftconv_eqlinear_weight_bytes(T, C_out, C_in, W.dtype), dtype=torch.uint8, device=x.device)
     fftconv_eqlinear_prepare(W, W_f, stream)
     y = torch.empty((x.shape[0], T, C_out), dtype=x.dtype, device=x.device)
     fftconv_eqlinear_fwd(x, W_f, y, stream)

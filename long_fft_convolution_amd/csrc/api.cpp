@@ -955,17 +955,17 @@ fftconv_status_t fftconv_fwd_short(const void *u, const void *K_s, const void *w
 // ---- group-axis circular convolution ----------------------------------------
 static bool eq_group_ok(int64_t T) { return T == 4 || T == 8 || T == 16; }
 
-size_t fftconv_eqlinear_weight_bytes(int64_t T, int64_t C_out, int64_t C_in) {
-    if (!eq_group_ok(T) || C_out < 1 || C_in < 1) return 0;
-    return (size_t)(T / 2 + 1) * 2 * (size_t)C_out * (size_t)C_in * 2;
+size_t fftconv_eqlinear_weight_bytes(int64_t T, int64_t C_out, int64_t C_in, fftconv_dtype_t dtype) {
+    if (!eq_group_ok(T) || C_out < 1 || C_in < 1 || !dtype_ok(dtype)) return 0;
+    // (T/2 + 1) complex matrices: fp32 for fp32 storage, fp16 otherwise
+    return (size_t)(T / 2 + 1) * 2 * (size_t)C_out * (size_t)C_in * (dtype == FFTCONV_F32 ? 4 : 2);
 }
 
 fftconv_status_t fftconv_eqlinear_prepare(const void *W, int64_t T, int64_t C_out, int64_t C_in,
                                           fftconv_dtype_t dtype, void *W_f, size_t W_f_bytes,
                                           hipStream_t stream) {
     g_last_error.clear();
-    if (dtype != FFTCONV_F16 && dtype != FFTCONV_BF16)
-        return fail(FFTCONV_ERR_UNSUPPORTED, "the group convolution needs fp16 or bf16 storage");
+    if (!dtype_ok(dtype)) return fail(FFTCONV_ERR_UNSUPPORTED, "dtype %d is not supported", (int)dtype);
     if (!eq_group_ok(T)) return fail(FFTCONV_ERR_UNSUPPORTED, "group order T=%lld must be 4, 8 or 16", (long long)T);
     if (C_in < 32 || C_in % 32 != 0 || C_out < 32 || C_out % 32 != 0)
         return fail(FFTCONV_ERR_UNSUPPORTED, "C_in=%lld and C_out=%lld must be positive multiples of 32",
@@ -973,7 +973,7 @@ fftconv_status_t fftconv_eqlinear_prepare(const void *W, int64_t T, int64_t C_ou
     if (!W || !W_f) return fail(FFTCONV_ERR_INVALID_ARGUMENT, "W and W_f must be non-null");
     if (!aligned16(W) || !aligned16(W_f))
         return fail(FFTCONV_ERR_INVALID_ARGUMENT, "W and W_f must be 16-byte aligned");
-    const size_t need = fftconv_eqlinear_weight_bytes(T, C_out, C_in);
+    const size_t need = fftconv_eqlinear_weight_bytes(T, C_out, C_in, dtype);
     if (W_f_bytes < need) return fail(FFTCONV_ERR_INVALID_ARGUMENT, "W_f has %zu bytes, needs %zu", W_f_bytes, need);
     if (overlap(W, (size_t)T * C_out * C_in * elem_bytes(dtype), W_f, need))
         return fail(FFTCONV_ERR_INVALID_ARGUMENT, "W overlaps W_f");
@@ -985,8 +985,7 @@ fftconv_status_t fftconv_eqlinear_prepare(const void *W, int64_t T, int64_t C_ou
 fftconv_status_t fftconv_eqlinear_fwd(const void *x, const void *W_f, void *y, int64_t N, int64_t T,
                                       int64_t C_in, int64_t C_out, fftconv_dtype_t dtype, hipStream_t stream) {
     g_last_error.clear();
-    if (dtype != FFTCONV_F16 && dtype != FFTCONV_BF16)
-        return fail(FFTCONV_ERR_UNSUPPORTED, "the group convolution needs fp16 or bf16 storage");
+    if (!dtype_ok(dtype)) return fail(FFTCONV_ERR_UNSUPPORTED, "dtype %d is not supported", (int)dtype);
     if (!eq_group_ok(T)) return fail(FFTCONV_ERR_UNSUPPORTED, "group order T=%lld must be 4, 8 or 16", (long long)T);
     if (C_in < 32 || C_in % 32 != 0 || C_out < 32 || C_out % 32 != 0)
         return fail(FFTCONV_ERR_UNSUPPORTED, "C_in=%lld and C_out=%lld must be positive multiples of 32",
@@ -998,7 +997,7 @@ fftconv_status_t fftconv_eqlinear_fwd(const void *x, const void *W_f, void *y, i
         return fail(FFTCONV_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
     const size_t ybytes = (size_t)N * T * C_out * elem_bytes(dtype);
     if (overlap(y, ybytes, x, (size_t)N * T * C_in * elem_bytes(dtype)) ||
-        overlap(y, ybytes, W_f, fftconv_eqlinear_weight_bytes(T, C_out, C_in)))
+        overlap(y, ybytes, W_f, fftconv_eqlinear_weight_bytes(T, C_out, C_in, dtype)))
         return fail(FFTCONV_ERR_INVALID_ARGUMENT, "y overlaps an input");
     const hipError_t e = launch_eqlinear(dtype, (int)T, x, W_f, y, N, C_in, C_out, stream);
     if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "eqlinear launch: %s", hipGetErrorString(e));

@@ -15,7 +15,7 @@ from parity import check
 
 pytestmark = pytest.mark.gpu
 
-TOL = {torch.float16: 5e-3, torch.bfloat16: 2e-2}
+TOL = {torch.float32: 1e-5, torch.float16: 5e-3, torch.bfloat16: 2e-2}
 
 
 def _say(msg):
@@ -30,7 +30,7 @@ def _inputs(N, T, Ci, Co, dtype, seed):
     return x, W
 
 
-@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("T,Ci,Co,N", [(8, 32, 32, 16), (8, 64, 96, 50), (4, 128, 64, 37),
                                        (8, 128, 256, 300), (16, 96, 32, 17), (16, 32, 64, 33)])
 def test_eqlinear_parity(dtype, T, Ci, Co, N):
@@ -68,3 +68,18 @@ def test_eqlinear_empty():
     x = torch.empty((0, 8, 32), dtype=torch.float16, device="cuda")
     W = torch.randn(8, 32, 32).to(torch.float16).cuda()
     assert fc.eqlinear(x, W).shape == (0, 8, 32)
+
+
+def test_eqlinear_fp32_equivariance_and_bench_shape():
+    # fp32 storage and arithmetic: the shift equivariance to fp32 rounding, and the
+    # benchmark shape on sampled tokens
+    x, W = _inputs(64, 8, 64, 96, torch.float32, seed=5)
+    y = fc.eqlinear(x.cuda(), W.cuda()).cpu()
+    ys = fc.eqlinear(torch.roll(x, 3, dims=1).cuda(), W.cuda()).cpu()
+    check(ys.double().numpy(), torch.roll(y, 3, dims=1).double().numpy(), 1e-6)
+    N, T, Ci, Co = 65536, 8, 128, 128
+    _say(f"eqlinear fp32 N={N} sampled")
+    x, W = _inputs(N, T, Ci, Co, torch.float32, seed=12)
+    y = fc.eqlinear(x.cuda(), W.cuda()).cpu().double().numpy()
+    toks = np.concatenate([np.random.default_rng(1).choice(N, 300, replace=False), [0, N - 1]])
+    check(y[toks], eqlinear_tokens(x.double().numpy(), W.double().numpy(), toks), 1e-5)
