@@ -140,3 +140,27 @@ def test_bwd_workload_full_size():
     got = _run(inp, dy)
     want = oracle.fft_bwd(inp.f64("u"), inp.f64("k"), dy.double().numpy(), inp.f64("w"), inp.f64("v"))
     _check(got, want, TOL["f16"])
+
+
+@pytest.mark.parametrize("kind", ["band", "random"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_bwd_mask_multipass_half(kind, dtype):
+    # the three-pass path in half precision with a frequency mask (the row pass skips
+    # the dropped tiles under the band mask), gated, an odd batch
+    B, H, N = 3, 2, 1 << 17
+    _say(f"bwd mask {kind} N={N} {dtype}")
+    inp, dy = _case(B, H, N, 5000, dtype, "both", seed=N + 11)
+    mask = synth.band_mask(H, 27) if kind == "band" else synth.random_mask(H, seed=N + 1)
+    got = _run(inp, dy, mask)
+    want = oracle.fft_bwd(inp.f64("u"), inp.f64("k"), dy.double().numpy(), inp.f64("w"), inp.f64("v"), mask)
+    _check(got, want, TOL[dtype])
+
+
+def test_bwd_n2_20():
+    # N = 2^20 (the 1M workload's length): all four gradients of two whole channels
+    B, H, N = 1, 2, 1 << 20
+    _say(f"bwd N={N} f16 B={B} H={H}")
+    inp, dy = _case(B, H, N, N, "f16", "both", seed=2020)
+    got = _run(inp, dy)
+    want = oracle.fft_bwd(inp.f64("u"), inp.f64("k"), dy.double().numpy(), inp.f64("w"), inp.f64("v"))
+    _check(got, want, TOL["f16"])
