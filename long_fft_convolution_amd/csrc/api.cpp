@@ -688,8 +688,10 @@ fftconv_status_t fftconv_fwd_noalloc(const void *u, const void *K_f, const void 
 // x = u w; the spectra of the sequences x as filters of their own channel;
 // the per-sequence correlations; the repeated mask rows; the forward
 // workspace (the same size serves the B*H-channel prepare and forward).
+// N = 16384 (fp16 / bf16) instead: the batch-row pairs' spectra of u w and
+// their scales, and the per-pair correlations.
 struct BwdLayout {
-    size_t kc, x, kx, part, mrep, fws, total;
+    size_t kc, x, kx, part, mrep, fws, spec, pscale, total;
 };
 
 static BwdLayout bwd_layout(int64_t B, int64_t H, int64_t N, fftconv_dtype_t dtype) {
@@ -704,10 +706,15 @@ static BwdLayout bwd_layout(int64_t B, int64_t H, int64_t N, fftconv_dtype_t dty
     o.kc = take(fftconv_filter_bytes(H, N, dtype));
     // N = 1024 (fp16 / bf16): du, dw and dk come from kernels that need no scratch beyond
     // the conjugated spectrum (the dk chain's areas below are then empty)
-    const bool chain = !use_pair_kernel(log2_exact(N), dtype);
+    const bool p16 = use_pair3_kernel(log2_exact(N), dtype);
+    const bool chain = !use_pair_kernel(log2_exact(N), dtype) && !p16;
+    const int64_t P = H * ((B + 1) / 2);
+    o.spec = take(p16 ? (size_t)P * kP16SpecBytes : 0);
+    o.pscale = take(p16 ? (size_t)P * sizeof(float) : 0);
+    o.part = take(p16 ? (size_t)P * (size_t)N * elem_bytes(dtype) : 0);
     o.x = take(chain ? (size_t)S * (size_t)N * elem_bytes(dtype) : 0);
     o.kx = take(chain && S > 0 ? fftconv_filter_bytes(S, N, dtype) : 0);
-    o.part = take(chain ? (size_t)S * (size_t)N * elem_bytes(dtype) : 0);
+    if (chain) o.part = take((size_t)S * (size_t)N * elem_bytes(dtype));
     o.mrep = take(chain ? (size_t)S * kMaskBlocks : 0);
     o.fws = take(chain ? fftconv_workspace_bytes(1, S, N, dtype) : fftconv_workspace_bytes(B, H, N, dtype));
     o.total = off;
@@ -812,6 +819,13 @@ fftconv_status_t fftconv_bwd(const void *dy, const void *u, const void *K_f, con
     if (dk && B > 0 && use_pair_kernel(l, dtype)) {
         hipError_t e = launch_pair_dk(dtype, dy, u, w, v, dk, mask, B, H, L, stream);
         if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "dk: %s", hipGetErrorString(e));
+    } else if (dk && B > 0 && use_pair3_kernel(l, dtype)) {
+        // N = 16384 (fp16 / bf16): the pairs' spectra of u w, then one correlation per pair
+        hipError_t e = launch_pair16k_dk(dtype, dy, u, w, v, ws + lay.part, ws + lay.spec,
+                                         reinterpret_cast<float *>(ws + lay.pscale), mask, B, H, stream);
+        if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "dk pairs: %s", hipGetErrorString(e));
+        e = launch_dk_reduce(dtype, ws + lay.part, dk, (B + 1) / 2, H, N, L, stream);
+        if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "dk reduction: %s", hipGetErrorString(e));
     } else if (dk) {
         // otherwise each x = u w is the filter of its own channel b H + h; the mask rows
         // repeat per batch row

@@ -98,9 +98,21 @@ constexpr int kTilesPerWave = 64 / kWaves;   // 16-column tiles of n_ab in phase
 constexpr int kRowsPerWave = 32 / kWaves;    // rows f_c in phase 2
 static_assert(kWaves == 8, "the LDS address split below assumes 8 waves");
 
+// Kernel modes.  kConv: the convolution.  kSpec: the forward transform of the pair only;
+// the spectrum is stored conjugated and scaled, as a complex "filter" of all 32 rows f_c,
+// in the order in which the product step reads it.  kCorr: the convolution with such a
+// per-pair spectrum in place of K_f, keeping only the real part of the result (the
+// backward pass's filter gradient: with z_x = x_a + i x_b and z_g = g_a + i g_b,
+// Re IDFT(conj(Z_x) Z_g) = corr(g_a, x_a) + corr(g_b, x_b)).
+constexpr int kConv = 0, kSpec = 1, kCorr = 2;
+constexpr int kSpecRows = 32 * 2 * 2 * 64;   // uint4 per pair spectrum (all rows f_c)
+
 // filter chunk of row fc for (mt2, nt): rows f_c <= 16 as stored, the others from
-// the mirror row 32 - f_c (lane 63 - l, tiles flipped, elements reversed, conjugated)
+// the mirror row 32 - f_c (lane 63 - l, tiles flipped, elements reversed, conjugated);
+// FULL: a per-pair spectrum with every row stored
+template <bool FULL = false>
 __device__ __forceinline__ uint4 k_load(const uint4 *kch, int fc, int mt2, int nt, uint32_t lane) {
+    if constexpr (FULL) return ldu<uint4>(kch + ((fc * 2 + mt2) * 2 + nt) * 64, 16u * lane);
     const bool mir = fc > 16;
     const uint32_t row = mir ? 32 - fc : fc, a = mir ? 1 - mt2 : mt2, b = mir ? 1 - nt : nt;
     return ldu<uint4>(kch + ((row * 2 + a) * 2 + b) * 64, 16u * (mir ? 63 - lane : lane));
@@ -127,13 +139,19 @@ using namespace p16;
 // DUAL: a second output out2 = v2 * conv(u w, k) from the same transforms (the backward
 // pass forms du and dw in one call); the second gate's rows are loaded once the staged
 // outputs have freed their registers.
-template <typename T, bool MASKED, bool HAS_W, bool HAS_V, bool DUAL = false>
+// MODE (kConv, kSpec, kCorr) above.  kSpec writes spec_out[p] and scale_out[p] for pair p;
+// kCorr reads them through kbins and kscale and writes row bp H + h of out.
+template <typename T, bool MASKED, bool HAS_W, bool HAS_V, bool DUAL = false, int MODE = kConv>
 __global__ void __launch_bounds__(64 * kWaves, 1)
 pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restrict__ v,
                T *__restrict__ out, const uint4 *__restrict__ kbins, const float *__restrict__ kscale,
                const uint8_t *__restrict__ mask, Pair3Tables tb, int64_t B, int64_t H,
-               const T *__restrict__ v2, T *__restrict__ out2) {
+               const T *__restrict__ v2, T *__restrict__ out2, uint4 *__restrict__ spec_out,
+               float *__restrict__ scale_out) {
     static_assert(!DUAL || HAS_V, "a second output has an output gate of its own");
+    static_assert(MODE == kConv || (!DUAL && !HAS_V), "the spectrum and correlation modes have no output gate");
+    static_assert(MODE != kSpec || !MASKED, "the spectrum mode stores every bin");
+    constexpr bool SPEC = MODE == kSpec, CORR = MODE == kCorr;
     constexpr int N = 16384;
     constexpr int M2 = 2 * N;
     extern __shared__ __align__(16) _Float16 smem[];
@@ -206,6 +224,8 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
         oa_ = (2 * bpp * H + hh) * N;
         ob_ = hb_ ? oa_ + H * N : oa_;
     };
+    // kSpec: sum of |x| over the pair's transformed values (this lane's share)
+    float l1 = 0.f;
     auto load_batch = [&](int64_t oa_, int64_t ob_, int half, Batch &x) {
         const uint32_t *pua = reinterpret_cast<const uint32_t *>(u + oa_);
         const uint32_t *pub = reinterpret_cast<const uint32_t *>(u + ob_);
@@ -253,6 +273,7 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                     bi[j] = hb_ ? (_Float16)xb : (_Float16)0.f;
                     br[4 + j] = (_Float16)0.f;
                     bi[4 + j] = (_Float16)0.f;
+                    if (SPEC) l1 += fabsf((float)br[j]) + fabsf((float)bi[j]);
                 }
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
@@ -287,8 +308,9 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
 
     for (; p < p_end; p += wg_on_xcd) {
         const int64_t h = __builtin_amdgcn_readfirstlane((uint32_t)p / (uint32_t)PB);
-        // (the six stages' table factors are undone with the channel scale)
-        const float ks = __builtin_ldexpf(kscale[h], 6 * kDft32Log2);
+        // (the six stages' table factors are undone with the channel scale; kCorr: the pair's)
+        const float ks = SPEC ? 1.f : __builtin_ldexpf(kscale[CORR ? p : h], 6 * kDft32Log2);
+        const int64_t oo = CORR ? ((p - h * PB) * H + h) * N : 0;   // kCorr output row
         int64_t p_nx = p + wg_on_xcd, oa_nx, ob_nx;
         bool hb_nx;
         pair_base(p_nx < p_end ? p_nx : p, oa_nx, ob_nx, hb_nx);
@@ -306,7 +328,30 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
             phase1_batch(x0, tw0, 0, has_b);
             phase1_batch(x1, tw1, 1, has_b);
         }
+        float *const s_part = reinterpret_cast<float *>(s_mask);   // kSpec: per-wave sums of |x|
+        if (SPEC) {
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) l1 += __shfl_xor(l1, o);
+            if (lane == 0) s_part[wave] = l1;
+            l1 = 0.f;
+        }
         __syncthreads();
+        // kSpec: |Z[f]| <= sum |z| bounds every bin, so the stored spectrum, scaled by the
+        // power of two 2^e <= 64 / sum |z|, stays within |.| <= 1 after the three stages'
+        // 2^-6; the pair's scale is 1 / (2^(e - 6) 2N), the filter scale of that spectrum
+        float sc = 1.f;
+        if (SPEC) {
+            float tot = 0.f;
+#pragma unroll
+            for (int j = 0; j < kWaves; ++j) tot += s_part[j];
+            int e = 0;
+            if (tot > 0.f && isfinite(tot)) {
+                e = (int)floorf(log2f(64.f / tot));
+                e = e < -60 ? -60 : (e > 60 ? 60 : e);
+            }
+            sc = __builtin_ldexpf(1.f, e);
+            if (tid == 0) scale_out[p] = __builtin_ldexpf(1.f, 6 - e - 15);
+        }
 
         // ---- phase 2a: this wave's rows f_c = wave + kWaves r into registers (S1 operands);
         // R2 below reuses the same LDS
@@ -320,12 +365,14 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                 ai_[r][mt] = *reinterpret_cast<const h8 *>(r2i + o);
             }
         }
-        const uint4 *kch = kbins + h * (int64_t)(17 * 256);
+        const uint4 *kch = kbins + (CORR ? p * (int64_t)kSpecRows : h * (int64_t)(17 * 256));
         uint4 kq[2][2];
+        if (!SPEC) {
 #pragma unroll
-        for (int mt2 = 0; mt2 < 2; ++mt2)
+            for (int mt2 = 0; mt2 < 2; ++mt2)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) kq[mt2][nt] = k_load(kch, wave, mt2, nt, ul);
+                for (int nt = 0; nt < 2; ++nt) kq[mt2][nt] = k_load<CORR>(kch, wave, mt2, nt, ul);
+        }
         __syncthreads();
 
         // ---- phase 2b: the 1024-point chain per row, filter product, inverse chain;
@@ -338,23 +385,24 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
             // values of this block (a hoisted 64-bit address costs two registers per load)
             uint32_t lx = ul;
             asm volatile("" : "+v"(lx));
-            h8 kk[2][2];
-#pragma unroll
-            for (int mt2 = 0; mt2 < 2; ++mt2)
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) kk[mt2][nt] = k_fix(kq[mt2][nt], fc > 16);
-            if (r + 1 < kRowsPerWave) {
+            h8 kk[2][2], two[2][2];
+            if (!SPEC) {
 #pragma unroll
                 for (int mt2 = 0; mt2 < 2; ++mt2)
 #pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) kq[mt2][nt] = k_load(kch, fc + kWaves, mt2, nt, lx);
+                    for (int nt = 0; nt < 2; ++nt) kk[mt2][nt] = k_fix(kq[mt2][nt], !CORR && fc > 16);
+                if (r + 1 < kRowsPerWave) {
+#pragma unroll
+                    for (int mt2 = 0; mt2 < 2; ++mt2)
+#pragma unroll
+                        for (int nt = 0; nt < 2; ++nt) kq[mt2][nt] = k_load<CORR>(kch, fc + kWaves, mt2, nt, lx);
+                }
+#pragma unroll
+                for (int nt3 = 0; nt3 < 2; ++nt3)
+#pragma unroll
+                    for (int nt2 = 0; nt2 < 2; ++nt2)
+                        two[nt3][nt2] = ldu<h8>(twO2 + ((kWaves * r * 2 + nt3) * 2 + nt2) * 64, 16u * lx);
             }
-            h8 two[2][2];
-#pragma unroll
-            for (int nt3 = 0; nt3 < 2; ++nt3)
-#pragma unroll
-                for (int nt2 = 0; nt2 < 2; ++nt2)
-                    two[nt3][nt2] = ldu<h8>(twO2 + ((kWaves * r * 2 + nt3) * 2 + nt2) * 64, 16u * lx);
             if (r == kRowsPerWave - 1) {   // output gate of this pair, first batch of the next
                 if (HAS_V) {
 #pragma unroll
@@ -389,6 +437,11 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                 for (int mt2 = 0; mt2 < 2; ++mt2) {
                     f4 cr, ci;
                     cm_constA(Fr[mt2], Fi[mt2], nFi[mt2], br, bi, cr, ci);   // rows f_a, cols f_b
+                    if (SPEC) {   // conj(Z) 2^e in the order the product step reads it
+                        const h8 q = cat8(to_h4(cr * sc), to_h4(ci * -sc));
+                        stu(spec_out + p * (int64_t)kSpecRows + ((fc * 2 + mt2) * 2 + nt) * 64, 16u * lx, q);
+                        continue;
+                    }
                     yr[mt2][nt] = to_h4(cr);
                     yi[mt2][nt] = to_h4(ci);
                     h8 kf = kk[mt2][nt];
@@ -409,6 +462,7 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                     cmul4(yr[mt2][nt], yi[mt2][nt], kf);
                 }
             }
+            if (SPEC) continue;
             // S2': data A = T2^T (M = f_b tiles nt, K = f_a), const B conj F[nt2] (N = n_a); conj twiddle
             h4 t3r[2][2], t3i[2][2];
 #pragma unroll
@@ -442,6 +496,14 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                     }
                 }
             }
+        }
+        if (SPEC) {   // no inverse: the next pair's second input batch, then the next pair
+            load_batch(oa_nx, ob_nx, 1, x1);
+            __syncthreads();
+            oa = oa_nx;
+            ob = ob_nx;
+            has_b = hb_nx;
+            continue;
         }
         __syncthreads();
 
@@ -482,6 +544,7 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
+                if (CORR && k >= 4) break;   // the real part only
                 // without a second row (ob == oa) its stores repeat the first row's values
                 const int kk = (k >= 4 && !has_b) ? k - 4 : k;
                 const char *src = s8 + 2 * ((kk >> 2) * kR1Plane + (kk & 3) * 8192);
@@ -510,7 +573,8 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                     }
                 }
                 const uint2 lo = st<T>::pack4(yv), hi = st<T>::pack4(yv + 4);
-                stu_nt(out + (k < 4 ? oa : ob) + 4096 * (k & 3), 2 * m4, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                stu_nt(out + (CORR ? oo : (k < 4 ? oa : ob)) + 4096 * (k & 3), 2 * m4,
+                       make_uint4(lo.x, lo.y, hi.x, hi.y));
             }
         }
         __syncthreads();
@@ -520,13 +584,8 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
     }
 }
 
-hipError_t launch_pair16k_conv(int st_, const void *u, const void *w, const void *v, void *out,
-                               const void *kbins, const float *kscale, const uint8_t *mask,
-                               int64_t B, int64_t H, hipStream_t stream, const void *v2, void *out2) {
-    if (out2 != nullptr && (v == nullptr || v2 == nullptr)) return hipErrorInvalidValue;
-    Pair3Tables tb{};
-    hipError_t e = get_pair3_tables(&tb);
-    if (e != hipSuccess) return e;
+// persistent grid: one workgroup per CU, at most one per pair (and at least 8, one per XCD)
+static hipError_t p16_grid(int64_t B, int64_t H, int64_t *blocks) {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) {
         int n = 0;
@@ -535,9 +594,23 @@ hipError_t launch_pair16k_conv(int st_, const void *u, const void *w, const void
     }
     const int64_t pairs = H * ((B + 1) / 2);
     if (pairs >= ((int64_t)1 << 31)) return hipErrorInvalidValue;   // pair indices are 32-bit
-    int64_t blocks = cus;
-    if (blocks > pairs) blocks = pairs < 8 ? 8 : pairs;
-    const size_t lds = (size_t)2 * kR1Plane * sizeof(_Float16) + 2 * 256 * 16 + kMaskBlocks;
+    *blocks = cus;
+    if (*blocks > pairs) *blocks = pairs < 8 ? 8 : pairs;
+    return hipSuccess;
+}
+
+static constexpr size_t kP16Lds = (size_t)2 * kR1Plane * sizeof(_Float16) + 2 * 256 * 16 + kMaskBlocks;
+
+hipError_t launch_pair16k_conv(int st_, const void *u, const void *w, const void *v, void *out,
+                               const void *kbins, const float *kscale, const uint8_t *mask,
+                               int64_t B, int64_t H, hipStream_t stream, const void *v2, void *out2) {
+    if (out2 != nullptr && (v == nullptr || v2 == nullptr)) return hipErrorInvalidValue;
+    Pair3Tables tb{};
+    hipError_t e = get_pair3_tables(&tb);
+    if (e != hipSuccess) return e;
+    int64_t blocks = 0;
+    if ((e = p16_grid(B, H, &blocks)) != hipSuccess) return e;
+    const size_t lds = kP16Lds;
     auto go = [&](auto kern, auto *tp) -> hipError_t {
         using TT = std::remove_pointer_t<decltype(tp)>;
         hipError_t err = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -545,7 +618,7 @@ hipError_t launch_pair16k_conv(int st_, const void *u, const void *w, const void
         if (err != hipSuccess) return err;
         hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * kWaves), lds, stream, (const TT *)u,
                            (const TT *)w, (const TT *)v, (TT *)out, (const uint4 *)kbins, kscale, mask, tb,
-                           B, H, (const TT *)v2, (TT *)out2);
+                           B, H, (const TT *)v2, (TT *)out2, (uint4 *)nullptr, (float *)nullptr);
         return hipGetLastError();
     };
     // one instantiation per (storage type, mask, gates) so that no gate test sits in the loops
@@ -569,6 +642,47 @@ hipError_t launch_pair16k_conv(int st_, const void *u, const void *w, const void
         case 5: return go(pair16k_kernel<TT, true, false, true>, tp);
         case 6: return go(pair16k_kernel<TT, true, true, false>, tp);
         default: return go(pair16k_kernel<TT, true, true, true>, tp);
+        }
+    };
+    if (st_ == ST_F16) return pick((__half *)nullptr);
+    return pick((__hip_bfloat16 *)nullptr);
+}
+
+// Filter gradient partials at N = 16384: for every pair p = h ceil(B/2) + bp of batch rows
+// (2 bp, 2 bp + 1) of channel h, part[bp H + h] = corr(dy v, u w) summed over the two rows.
+// spec (ceil(B/2) H * 128 KiB) and pscale (ceil(B/2) H floats) hold the pairs' conjugated
+// spectra of u w between the two launches.
+hipError_t launch_pair16k_dk(int st_, const void *dy, const void *u, const void *w, const void *v,
+                             void *part, void *spec, float *pscale, const uint8_t *mask, int64_t B,
+                             int64_t H, hipStream_t stream) {
+    Pair3Tables tb{};
+    hipError_t e = get_pair3_tables(&tb);
+    if (e != hipSuccess) return e;
+    int64_t blocks = 0;
+    if ((e = p16_grid(B, H, &blocks)) != hipSuccess) return e;
+    auto go = [&](auto kern, auto *tp, const void *in, const void *gate, void *o, const void *kb,
+                  const float *ksc, const uint8_t *m) -> hipError_t {
+        using TT = std::remove_pointer_t<decltype(tp)>;
+        hipError_t err = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)kP16Lds);
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * kWaves), kP16Lds, stream, (const TT *)in,
+                           (const TT *)gate, (const TT *)nullptr, (TT *)o, (const uint4 *)kb, ksc, m, tb, B, H,
+                           (const TT *)nullptr, (TT *)nullptr, (uint4 *)spec, pscale);
+        return hipGetLastError();
+    };
+    auto pick = [&](auto *tp) -> hipError_t {
+        using TT = std::remove_pointer_t<decltype(tp)>;
+        hipError_t err = w ? go(pair16k_kernel<TT, false, true, false, false, kSpec>, tp, u, w, nullptr, nullptr,
+                                nullptr, nullptr)
+                           : go(pair16k_kernel<TT, false, false, false, false, kSpec>, tp, u, nullptr, nullptr,
+                                nullptr, nullptr, nullptr);
+        if (err != hipSuccess) return err;
+        switch ((mask ? 2 : 0) | (v ? 1 : 0)) {
+        case 0: return go(pair16k_kernel<TT, false, false, false, false, kCorr>, tp, dy, nullptr, part, spec, pscale, mask);
+        case 1: return go(pair16k_kernel<TT, false, true, false, false, kCorr>, tp, dy, v, part, spec, pscale, mask);
+        case 2: return go(pair16k_kernel<TT, true, false, false, false, kCorr>, tp, dy, nullptr, part, spec, pscale, mask);
+        default: return go(pair16k_kernel<TT, true, true, false, false, kCorr>, tp, dy, v, part, spec, pscale, mask);
         }
     };
     if (st_ == ST_F16) return pick((__half *)nullptr);

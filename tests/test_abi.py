@@ -140,6 +140,13 @@ def test_bwd_workspace_bytes():
     # that need no other scratch); fp32 keeps the whole layout
     for dt in (F16, BF16):
         assert fc.fftconv_bwd_workspace_bytes(B, H, 1024, dt) == up(fc.fftconv_filter_bytes(H, 1024, dt))
+    # N = 16384 in fp16 / bf16: the conjugated K_f, then per pair of batch rows its
+    # spectrum of u*w (32 rows x 1024 bins x fp16 re/im), its scale and its correlation
+    for Bq in (1, 2, 3):
+        P = H * ((Bq + 1) // 2)
+        want = (up(fc.fftconv_filter_bytes(H, 16384, BF16)) + up(P * 32 * 1024 * 4) + up(P * 4)
+                + up(P * 16384 * 2))
+        assert fc.fftconv_bwd_workspace_bytes(Bq, H, 16384, BF16) == want
     assert fc.fftconv_bwd_workspace_bytes(B, H, 1024, F32) > up(fc.fftconv_filter_bytes(H, 1024, F32)) + B * H * 1024 * 4
     assert fc.fftconv_bwd_workspace_bytes(B, H, 1 << 20, F32) > 0
     assert fc.fftconv_bwd_workspace_bytes(B, H, 1000, F16) == 0

@@ -116,11 +116,11 @@ def test_bwd_n1024_many_channels(dtype):
     _check(got, want, TOL[dtype])
 
 
-@pytest.mark.parametrize("gates", ["w", "both"])
+@pytest.mark.parametrize("gates", ["w", "both", "none", "v"])
 def test_bwd_n16384_channels(gates):
-    # N = 16384: du and dw come from one kernel call; an odd batch (the last pair has one
-    # sequence), enough channels for the per-XCD channel split, with and without the
-    # input gate v
+    # N = 16384: du and dw come from one kernel call, dk from the pairs' spectra of u w and
+    # one correlation per pair; an odd batch (the last pair has one sequence), enough
+    # channels for the per-XCD channel split, every combination of the gates
     B, H, N = 3, 9, 16384
     _say(f"bwd N={N} B={B} H={H} gates={gates}")
     inp, dy = _case(B, H, N, N, "f16", gates, seed=163)
@@ -164,3 +164,49 @@ def test_bwd_n2_20():
     got = _run(inp, dy)
     want = oracle.fft_bwd(inp.f64("u"), inp.f64("k"), dy.double().numpy(), inp.f64("w"), inp.f64("v"))
     _check(got, want, TOL["f16"])
+
+
+@pytest.mark.parametrize("B", [1, 2, 4])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_bwd_n16384_batches(B, dtype):
+    # N = 16384: one pair of batch rows per channel (B = 2), a lone row (B = 1) and two
+    # pairs summed by the reduction (B = 4); a filter shorter than the sequence
+    H, N, L = 5, 16384, 9000
+    _say(f"bwd N={N} B={B} H={H} L={L} {dtype}")
+    inp, dy = _case(B, H, N, L, dtype, "both", seed=900 + B)
+    got = _run(inp, dy)
+    want = oracle.fft_bwd(inp.f64("u"), inp.f64("k"), dy.double().numpy(), inp.f64("w"), inp.f64("v"))
+    _check(got, want, TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype,loc,dscale", [("bf16", 2.0, 1e3), ("f16", 4.0, 1.0), ("bf16", 0.0, 1e-3)])
+def test_bwd_n16384_range(dtype, loc, dscale):
+    # the filter gradient's per-pair spectrum scale: u, w ~ N(loc, 1) (a large zero bin),
+    # and dy scaled far from unit size
+    B, H, N = 2, 3, 16384
+    _say(f"bwd range N={N} {dtype} loc={loc} dy x{dscale}")
+    inp, dy = _case(B, H, N, N, dtype, "both", seed=1600 + int(loc))
+    inp.u = (inp.u.double() + loc).to(inp.u.dtype)
+    inp.w = (inp.w.double() + loc).to(inp.w.dtype)
+    dy = (dy.double() * dscale).to(dy.dtype)
+    got = _run(inp, dy)
+    want = oracle.fft_bwd(inp.f64("u"), inp.f64("k"), dy.double().numpy(), inp.f64("w"), inp.f64("v"))
+    _check(got, want, TOL[dtype])
+
+
+def test_bwd_gated_bf16_n16k_full_size():
+    # the N = 16384 benchmark configuration (gated_bf16_n16k: B = 4, H = 2560, bf16) run
+    # whole; every gradient of 12 channels spread over the range (all their batch rows,
+    # their dk rows) compared with the oracle run on those channels alone
+    wl = synth.WORKLOADS["gated_bf16_n16k"]
+    _say(f"bwd {wl.name} full size")
+    inp = synth.generate_workload(wl.name)
+    g = torch.Generator().manual_seed(4243)
+    dy = torch.randn(inp.u.shape, generator=g, dtype=torch.float32).to(inp.u.dtype)
+    got = _run(inp, dy)
+    hs = np.array([0, 1, 7, 255, 256, 1023, 1280, 1281, 2047, 2300, 2558, 2559])
+    sub = lambda t: t[:, hs]
+    want = oracle.fft_bwd(sub(inp.f64("u")), inp.f64("k")[hs], sub(dy.double().numpy()), sub(inp.f64("w")),
+                          sub(inp.f64("v")))
+    for name, a, b in zip(("du", "dk", "dw", "dv"), got, want):
+        check(a[hs] if name == "dk" else a[:, hs], b, TOL["bf16"], f"{name} channels {list(hs)}")
