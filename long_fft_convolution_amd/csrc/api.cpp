@@ -300,6 +300,41 @@ hipError_t get_mp_tables(int logn, MpTables *out) {
     e = upload(w2row, &t.w2row);
     if (e == hipSuccess) e = upload(lo, &t.big_lo);
     if (e == hipSuccess) e = upload(hi, &t.big_hi);
+    if (e == hipSuccess && sp.log1 >= kMpColMinLog1) {
+        // Operand tiles of the matrix-core column passes (A operands of the complex
+        // 16x16x32 products: lane l holds row l % 16, K slots 8 (l / 16) .. + 7), each tile
+        // three planes (re, im, -im) of 64 lanes x 8 fp16.  Entries outside a tile's
+        // rows or K range are zero.  Order: pass-1 stage 1 (RB / 16 tiles of the RB-point
+        // DFT over n_b < RB/2, rows f_b), pass-1 stage 2 (one tile per f_b: the RA-point
+        // DFT over n_a times omega_N1^{n_a f_b}, rows f_a), pass-3 stage 1 (the RA-point
+        // DFT over f_a, rows n_a, times 2^-mp_c3_log2), pass-3 stage 2 (one tile per n_a:
+        // the RB-point DFT over f_b times omega_N1^{n_a f_b}, rows n_b < RB/2).
+        const int rb = 1 << mp_col_rb_log2(sp.log1), ra = (int)n1 / rb, t1 = rb / 16;
+        const int ntiles = t1 + rb + 1 + ra;
+        std::vector<_Float16> col((size_t)ntiles * 3 * 64 * 8, (_Float16)0.f);
+        auto put = [&](int tile, int l, int j, int64_t num, int64_t den, double scale) {
+            const double a = -2.0 * pi * (double)(num % den) / (double)den;
+            const size_t o = ((size_t)tile * 3 * 64 + l) * 8 + j;
+            col[o] = (_Float16)(scale * std::cos(a));
+            col[o + 64 * 8] = (_Float16)(scale * std::sin(a));
+            col[o + 2 * 64 * 8] = (_Float16)(-scale * std::sin(a));
+        };
+        const double s3 = std::ldexp(1.0, -mp_c3_log2(sp.log1));
+        for (int l = 0; l < 64; ++l) {
+            const int r = l % 16;
+            for (int j = 0; j < 8; ++j) {
+                const int k = 8 * (l / 16) + j;
+                for (int m = 0; m < t1; ++m)        // rows f_b = 16 m + r, K = n_b
+                    if (k < rb / 2) put(m, l, j, (int64_t)k * (16 * m + r), rb, 1.0);
+                for (int fb = 0; fb < rb; ++fb)      // rows f_a = r, K = n_a
+                    if (k < ra && r < ra) put(t1 + fb, l, j, (int64_t)k * (r * rb + fb), n1, 1.0);
+                if (k < ra && r < ra) put(t1 + rb, l, j, (int64_t)k * r, ra, s3);   // rows n_a, K = f_a
+                for (int na = 0; na < ra; ++na)      // rows n_b = r, K = f_b
+                    if (k < rb && r < rb / 2) put(t1 + rb + 1 + na, l, j, (int64_t)k * (r * ra + na), n1, 1.0);
+            }
+        }
+        e = upload_h(col, &t.col);
+    }
     if (e != hipSuccess) return e;
     g_mp_tables[key] = t;
     *out = t;

@@ -152,7 +152,19 @@ struct MpTables {
     const float2 *w2row;   // exp(-pi i j / N),          j < N1
     const float2 *big_lo;  // exp(-2 pi i j / N),        j < 2048
     const float2 *big_hi;  // exp(-2 pi i 2048 j / N),   j < N / 2048
+    const void *col;       // matrix-core column-pass operand tiles (N1 >= 2^kMpColMinLog1), else null
 };
+// The column transforms of the three-pass path split N1 = 2^log1 = RA * RB with
+// RB = 2^mp_col_rb_log2(log1) (the first stage of the forward column DFT, over the
+// coarse input digit) and RA = N1 / RB.
+inline __host__ __device__ constexpr int mp_col_rb_log2(int log1) { return (log1 + 1) / 2; }
+// Half-precision storage with N1 >= 2^kMpColMinLog1 runs both column passes on the
+// matrix cores; the first stage of the inverse column pass (RA points) has its
+// table scaled by 2^-mp_c3_log2 (undone with the output scale).
+constexpr int kMpColMinLog1 = 8;
+inline __host__ __device__ constexpr int mp_c3_log2(int log1) {
+    return (log1 - mp_col_rb_log2(log1) + 1) / 2;
+}
 hipError_t get_mp_tables(int logn, MpTables *out);
 // Builds every table of the current device once (hipMalloc and synchronous
 // copies); later calls return at once.  device_tables_ready: already built.

@@ -51,6 +51,7 @@ struct MpArgs {
     const float2 *w2row;    // exp(-pi i j / N),    j < N1   (omega_{2N}^{f1})
     const float2 *big_lo;   // exp(-2 pi i j / N),  j < 2048
     const float2 *big_hi;   // exp(-2 pi i 2048 j / N), j < N / 2048
+    const uint4 *col;       // matrix-core column-pass operand tiles (or null)
 };
 
 // ------------------------------------------------------------ small helpers
@@ -127,7 +128,7 @@ __device__ __forceinline__ void dft_halfout(const float2 *in, float2 *out) {
 // of f_b, so a workgroup holds at most 64 KiB of LDS and two fit on a CU.
 template <int LOG1> struct ColPlan {
     static constexpr int N1 = 1 << LOG1;
-    static constexpr int RB = 1 << ((LOG1 + 1) / 2);
+    static constexpr int RB = 1 << mp_col_rb_log2(LOG1);
     static constexpr int RA = N1 / RB;
     static constexpr int C = kMpThreads / RA;
     static constexpr int NG = RB / RA;
@@ -309,6 +310,402 @@ mp_pass3_kernel(const T *__restrict__ ws, const T *__restrict__ v, T *__restrict
         for (int nb = 0; nb < RB / 2; ++nb) {
             const int64_t mu = (int64_t)c0 + (int64_t)N2 * RA * nb;
             io<T>::store2(orow + 2 * mu, lo2, make_float2(r[nb].x, -r[nb].y));
+        }
+    }
+}
+
+// ------------------------------------------- matrix-core column passes (half storage)
+// For fp16 / bf16 storage with N1 = RA RB >= 2^kMpColMinLog1 both column passes run
+// as two complex-as-real v_mfma_f32_16x16x32_f16 stages (cmfma.hpp) instead of the
+// fp32 register DFTs above; same index splits (n1 = n_a + RA n_b, f1 = f_b + RB f_a),
+// same results up to fp16 rounding of the stage operands.  A workgroup owns 32
+// columns n2 = c0 .. c0 + 31 as two column tiles ct of the products (column 2c + ct
+// at lane column c = l % 16, so a lane stores two adjacent columns at once).  The
+// stage operands pass through LDS as fp16 planes [ct][re / im][c][row][slot], the
+// slot (the contraction index) contiguous: a lane's eight K slots are one 16-byte
+// read; lanes whose K slots lie past the transform read a 16-byte zero word.  The
+// twiddle between the two stages is folded into the second stage's operand tile
+// (one tile per digit), so only the four-step twiddle omega_N^{n2 f1} stays on the
+// VALU (fp32, from the two-level table).
+namespace colmm {
+using cmfma::h8;
+using cmfma::f4;
+using cmfma::cm_constA;
+}  // namespace colmm
+using namespace colmm;
+
+template <int LOG1> struct ColMm {
+    using P = ColPlan<LOG1>;
+    static constexpr int RA = P::RA, RB = P::RB, N1 = P::N1;
+    static constexpr int T1 = RB / 16;                  // pass-1 stage-1 tiles (rows f_b)
+    static_assert(RB >= 16 && RB <= 32 && RA >= 8 && RA <= 16, "matrix-core column split");
+    // per-c strides (bytes) of the LDS planes, 16 bytes of padding against bank conflicts
+    static constexpr int C11 = RA * (RB / 2) * 2 + 16;   // pass 1 stage 1: rows n_a, slots n_b
+    static constexpr int C12 = RB * RA * 2 + 16;         // pass 1 stage 2: rows f_b, slots n_a
+    static constexpr int C31 = RB * RA * 2 + 16;         // pass 3 stage 1: rows f_b, slots f_a
+    static constexpr int C32 = RA * RB * 2 + 16;         // pass 3 stage 2: rows n_a, slots f_b
+    static constexpr int kRegion = 64 * C12;             // the largest of the four
+    static_assert(C11 <= C12 && C31 == C12 && C32 == C12, "LDS regions");
+    static constexpr int kZero = kRegion;                // 16 zero bytes
+    static constexpr size_t kLds = (size_t)kRegion + 16;
+    static constexpr int kTile = 3 * 64;                 // uint4 per operand tile (re, im, -im)
+    static constexpr int kC1S1 = 0, kC1S2 = T1 * kTile, kC3S1 = (T1 + RB) * kTile,
+                         kC3S2 = (T1 + RB + 1) * kTile;
+};
+
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, h2v{(_Float16)a, (_Float16)b});
+}
+template <typename T> __device__ __forceinline__ float2 t2f(uint32_t w);
+template <> __device__ __forceinline__ float2 t2f<__half>(uint32_t w) {
+    const h2v h = __builtin_bit_cast(h2v, w);
+    return make_float2((float)h[0], (float)h[1]);
+}
+template <> __device__ __forceinline__ float2 t2f<__hip_bfloat16>(uint32_t w) {
+    return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+}
+template <typename T> __device__ __forceinline__ uint32_t f2t(float2 v);
+template <> __device__ __forceinline__ uint32_t f2t<__half>(float2 v) { return pack_h2(v.x, v.y); }
+template <> __device__ __forceinline__ uint32_t f2t<__hip_bfloat16>(float2 v) { return io<__hip_bfloat16>::pack(v); }
+
+// one operand tile (three planes) of the table
+__device__ __forceinline__ void col_tile(const uint4 *tabs, int base, int lane, h8 &fr, h8 &fi, h8 &nfi) {
+    fr = ldu<h8>(tabs + base, 16u * lane);
+    fi = ldu<h8>(tabs + base + 64, 16u * lane);
+    nfi = ldu<h8>(tabs + base + 128, 16u * lane);
+}
+// the B operand (re, im planes) at byte offset off of plane 0 (plane 1 is 16 c-strides on),
+// or zeros
+__device__ __forceinline__ void col_operand(const char *lds, int off, int cstride, bool in, int zero, h8 &br,
+                                            h8 &bi) {
+    br = *reinterpret_cast<const h8 *>(lds + (in ? off : zero));
+    bi = *reinterpret_cast<const h8 *>(lds + (in ? off + 16 * cstride : zero));
+}
+
+// pass 1 on the matrix cores: grid (N2 / 32, nseq); block 512.  Input u * w of sequence
+// seq0 + blockIdx.y, scaled by 2^-p1 as in mp_pass1_kernel; output the twiddled column
+// transform in rows f1 of the workspace.
+template <int LOG1, typename T>
+__global__ void __launch_bounds__(kMpThreads, 4)
+mp_pass1c_kernel(const T *__restrict__ src, const T *__restrict__ gate, int64_t seq0, T *__restrict__ ws,
+                 MpArgs ta) {
+    using M = ColMm<LOG1>;
+    constexpr int RA = M::RA, RB = M::RB, N1 = M::N1, N2 = 1 << kMpLog2;
+    constexpr int64_t NC = (int64_t)N1 * N2;
+    constexpr uint32_t NM = (uint32_t)(NC - 1);
+    extern __shared__ float2 lds[];
+    char *const L = reinterpret_cast<char *>(lds);
+    const int tid = threadIdx.x, lane = tid & 63, c = lane & 15, g = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c0 = blockIdx.x * 32;
+    const int64_t s = seq0 + blockIdx.y;
+    const T *row = src + s * NC;
+    const T *grow = gate != nullptr ? gate + s * NC : nullptr;
+    const float p1 = __builtin_ldexpf(1.f, -mp_p1_log2(LOG1));
+    const uint4 *tabs = ta.col;
+    if (tid == 0) *reinterpret_cast<uint4 *>(L + M::kZero) = make_uint4(0u, 0u, 0u, 0u);
+
+    // ---- inputs z[n1][c0 .. c0 + 31], n1 < N1/2, in row pairs (n_a + 2k RA, n_a + (2k+1) RA):
+    // both rows' values of column 2cp + ct form one 32-bit word at slots n_b = 2k, 2k + 1.
+    // Every load is issued before the first is used.
+    constexpr int R1 = N1 / 128;
+    {
+        const int cp = tid & 15;
+        uint2 qa[R1], qb[R1], ga[R1], gb[R1];
+#pragma unroll
+        for (int r = 0; r < R1; ++r) {
+            const int rp = (tid >> 4) + 32 * r;
+            const uint32_t ea = 4u * (uint32_t)((rp % RA + 2 * RA * (rp / RA)) * N2 + c0 + 2 * cp);   // bytes
+            qa[r] = ldu<uint2>(row, ea);
+            qb[r] = ldu<uint2>(row, ea + 4u * (uint32_t)(RA * N2));
+        }
+        if (grow != nullptr) {
+#pragma unroll
+            for (int r = 0; r < R1; ++r) {
+                const int rp = (tid >> 4) + 32 * r;
+                const uint32_t ea = 4u * (uint32_t)((rp % RA + 2 * RA * (rp / RA)) * N2 + c0 + 2 * cp);
+                ga[r] = ldu<uint2>(grow, ea);
+                gb[r] = ldu<uint2>(grow, ea + 4u * (uint32_t)(RA * N2));
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R1; ++r) {
+            const int rp = (tid >> 4) + 32 * r;
+            const int na = rp % RA, k = rp / RA;
+            float2 va[2] = {t2f<T>(qa[r].x), t2f<T>(qa[r].y)}, vb[2] = {t2f<T>(qb[r].x), t2f<T>(qb[r].y)};
+            if (grow != nullptr) {
+                const float2 wa[2] = {t2f<T>(ga[r].x), t2f<T>(ga[r].y)}, wb[2] = {t2f<T>(gb[r].x), t2f<T>(gb[r].y)};
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    va[ct] = make_float2(va[ct].x * wa[ct].x, va[ct].y * wa[ct].y);
+                    vb[ct] = make_float2(vb[ct].x * wb[ct].x, vb[ct].y * wb[ct].y);
+                }
+            }
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                const int o = (ct * 32 + cp) * M::C11 + (na * (RB / 2) + 2 * k) * 2;
+                *reinterpret_cast<uint32_t *>(L + o) = pack_h2(va[ct].x * p1, vb[ct].x * p1);
+                *reinterpret_cast<uint32_t *>(L + o + 16 * M::C11) = pack_h2(va[ct].y * p1, vb[ct].y * p1);
+            }
+        }
+    }
+    h8 Fr[M::T1], Fi[M::T1], nFi[M::T1];
+#pragma unroll
+    for (int m = 0; m < M::T1; ++m) col_tile(tabs, M::kC1S1 + m * M::kTile, lane, Fr[m], Fi[m], nFi[m]);
+    __syncthreads();
+
+    // ---- stage 1: per (n_a, ct) the RB-point DFT over n_b < RB/2, rows f_b = 16 m + 4 g + i.
+    // A wave takes n_a pairs (2p, 2p + 1) so that both values of a slot pair are its own;
+    // the results are held until every wave has read its operands (the next planes
+    // overwrite these).
+    constexpr int NPU = RA / 8;   // (n_a pair, ct) units per wave
+    uint32_t hold[NPU][M::T1][2][4];
+    {
+        const bool in = g < RB / 16;
+#pragma unroll
+        for (int t = 0; t < NPU; ++t) {
+            const int u = wave * NPU + t, p = u >> 1, ct = u & 1;
+            f4 cr[2][M::T1], ci[2][M::T1];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                h8 br, bi;
+                col_operand(L, (ct * 32 + c) * M::C11 + ((2 * p + h) * (RB / 2) + 8 * g) * 2, M::C11, in,
+                            M::kZero, br, bi);
+#pragma unroll
+                for (int m = 0; m < M::T1; ++m) cm_constA(Fr[m], Fi[m], nFi[m], br, bi, cr[h][m], ci[h][m]);
+            }
+#pragma unroll
+            for (int m = 0; m < M::T1; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    hold[t][m][0][i] = pack_h2(cr[0][m][i], cr[1][m][i]);
+                    hold[t][m][1][i] = pack_h2(ci[0][m][i], ci[1][m][i]);
+                }
+        }
+    }
+    // stage-2 operand tile of the first unit and the four-step twiddle factors, fetched
+    // across the barriers: for column n2 (ct) and rows f1 = f_b + RB (4 g + i) with
+    // f_b = wave + 8 t, omega_N^{n2 f1} = P (S8)^t (SR)^i
+    h8 Ar, Ai, nAi;
+    col_tile(tabs, M::kC1S2 + wave * M::kTile, lane, Ar, Ai, nAi);
+    float2 P[2], S8[2], SR[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        const uint32_t n2 = (uint32_t)(c0 + 2 * c + ct);
+        P[ct] = tw_big(ta.big_lo, ta.big_hi, (n2 * (uint32_t)(wave + 4 * g * RB)) & NM);
+        S8[ct] = tw_big(ta.big_lo, ta.big_hi, (n2 * 8u) & NM);
+        SR[ct] = tw_big(ta.big_lo, ta.big_hi, (n2 * (uint32_t)RB) & NM);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NPU; ++t) {
+        const int u = wave * NPU + t, p = u >> 1, ct = u & 1;
+#pragma unroll
+        for (int m = 0; m < M::T1; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int o = (ct * 32 + c) * M::C12 + ((16 * m + 4 * g + i) * RA + 2 * p) * 2;
+                *reinterpret_cast<uint32_t *>(L + o) = hold[t][m][0][i];
+                *reinterpret_cast<uint32_t *>(L + o + 16 * M::C12) = hold[t][m][1][i];
+            }
+    }
+    __syncthreads();
+
+    // ---- stage 2: per f_b the RA-point DFT over n_a with omega_N1^{n_a f_b} (its table
+    // tile), rows f_a = 4 g + i < RA; the four-step twiddle; store rows f1 = f_b + RB f_a
+    T *out = ws + 2 * (int64_t)blockIdx.y * NC;
+    const bool in = g < RA / 8;
+    float2 SR2[2], SR3[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        SR2[ct] = cmul(SR[ct], SR[ct]);
+        SR3[ct] = cmul(SR2[ct], SR[ct]);
+    }
+#pragma unroll
+    for (int t = 0; t < RB / 8; ++t) {
+        const int fb = wave + 8 * t;
+        f4 cr[2], ci[2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            h8 br, bi;
+            col_operand(L, (ct * 32 + c) * M::C12 + (fb * RA + 8 * g) * 2, M::C12, in, M::kZero, br, bi);
+            cm_constA(Ar, Ai, nAi, br, bi, cr[ct], ci[ct]);
+        }
+        if (t + 1 < RB / 8) col_tile(tabs, M::kC1S2 + (fb + 8) * M::kTile, lane, Ar, Ai, nAi);
+        if (4 * g < RA) {
+            const uint32_t n2 = (uint32_t)(c0 + 2 * c);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t f1 = (uint32_t)(fb + RB * (4 * g + i));
+                float2 y[2];
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    const float2 tw = i == 0 ? P[ct] : cmul(P[ct], i == 1 ? SR[ct] : (i == 2 ? SR2[ct] : SR3[ct]));
+                    y[ct] = cmul(make_float2(cr[ct][i], ci[ct][i]), tw);
+                }
+                stu(out, 4u * (f1 * (uint32_t)N2 + n2), make_uint2(f2t<T>(y[0]), f2t<T>(y[1])));
+            }
+        }
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) P[ct] = cmul(P[ct], S8[ct]);
+    }
+}
+
+// pass 3 on the matrix cores: grid (N2 / 32, nseq); block 512.  The same outputs as
+// mp_pass3_kernel<LOG1, T, true> (conjugate, channel and table scales, output gate).
+template <int LOG1, typename T>
+__global__ void __launch_bounds__(kMpThreads, 4)
+mp_pass3c_kernel(const T *__restrict__ ws, const T *__restrict__ v, T *__restrict__ out, int64_t seq0,
+                 MpArgs ta, const float *__restrict__ kscale, int64_t H) {
+    using M = ColMm<LOG1>;
+    constexpr int RA = M::RA, RB = M::RB, N1 = M::N1, N2 = 1 << kMpLog2;
+    constexpr int64_t NC = (int64_t)N1 * N2;
+    constexpr uint32_t NM = (uint32_t)(NC - 1);
+    extern __shared__ float2 lds[];
+    char *const L = reinterpret_cast<char *>(lds);
+    const int tid = threadIdx.x, lane = tid & 63, c = lane & 15, g = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c0 = blockIdx.x * 32;
+    const int64_t s = seq0 + blockIdx.y;
+    const T *wsq = ws + 2 * (int64_t)blockIdx.y * NC;
+    const uint4 *tabs = ta.col;
+    if (tid == 0) *reinterpret_cast<uint4 *>(L + M::kZero) = make_uint4(0u, 0u, 0u, 0u);
+
+    // ---- inputs y[f1][c0 .. c0 + 31], all rows, in pairs (f_b + 2k RB, f_b + (2k+1) RB) ->
+    // slots f_a = 2k, 2k + 1, times omega_N^{n2 f1} (the stored rows are conj(b), and
+    // conj(b omega^-a) = conj(b) omega^a).  Round r reads rows f1 = f0 + 64 r and
+    // f0 + 64 r + RB, so the twiddles follow from three table values per column.
+    constexpr int R3 = N1 / 64;
+    {
+        const int cp = tid & 15;
+        const uint32_t n2 = (uint32_t)(c0 + 2 * cp);
+        const int fb = (tid >> 4) % RB, k0 = (tid >> 4) / RB;
+        const uint32_t f0 = (uint32_t)(fb + 2 * RB * k0);
+        uint2 qa[R3], qb[R3];
+#pragma unroll
+        for (int r = 0; r < R3; ++r) {
+            qa[r] = ldu<uint2>(wsq, 4u * ((f0 + 64u * r) * (uint32_t)N2 + n2));
+            qb[r] = ldu<uint2>(wsq, 4u * ((f0 + 64u * r + RB) * (uint32_t)N2 + n2));
+        }
+        float2 cur[2], S64[2], SR[2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            const uint32_t n = n2 + (uint32_t)ct;
+            cur[ct] = tw_big(ta.big_lo, ta.big_hi, (n * f0) & NM);
+            S64[ct] = tw_big(ta.big_lo, ta.big_hi, (n * 64u) & NM);
+            SR[ct] = tw_big(ta.big_lo, ta.big_hi, (n * (uint32_t)RB) & NM);
+        }
+#pragma unroll
+        for (int r = 0; r < R3; ++r) {
+            const int k = k0 + r * (32 / RB);
+            const float2 qa2[2] = {t2f<T>(qa[r].x), t2f<T>(qa[r].y)}, qb2[2] = {t2f<T>(qb[r].x), t2f<T>(qb[r].y)};
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                const float2 va = cmul(qa2[ct], cur[ct]), vb = cmul(qb2[ct], cmul(cur[ct], SR[ct]));
+                const int o = (ct * 32 + cp) * M::C31 + (fb * RA + 2 * k) * 2;
+                *reinterpret_cast<uint32_t *>(L + o) = pack_h2(va.x, vb.x);
+                *reinterpret_cast<uint32_t *>(L + o + 16 * M::C31) = pack_h2(va.y, vb.y);
+                cur[ct] = cmul(cur[ct], S64[ct]);
+            }
+        }
+    }
+    h8 Fr, Fi, nFi;
+    col_tile(tabs, M::kC3S1, lane, Fr, Fi, nFi);
+    __syncthreads();
+
+    // ---- stage 1: per (f_b, ct) the RA-point DFT over f_a, rows n_a = 4 g + i < RA; a
+    // wave takes f_b pairs (2p, 2p + 1); results held until every wave has read its operands
+    constexpr int NPU = RB / 8;
+    uint32_t hold[NPU][2][4];
+    {
+        const bool in = g < RA / 8;
+#pragma unroll
+        for (int t = 0; t < NPU; ++t) {
+            const int u = wave * NPU + t, p = u >> 1, ct = u & 1;
+            f4 cr[2], ci[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                h8 br, bi;
+                col_operand(L, (ct * 32 + c) * M::C31 + ((2 * p + h) * RA + 8 * g) * 2, M::C31, in, M::kZero,
+                            br, bi);
+                cm_constA(Fr, Fi, nFi, br, bi, cr[h], ci[h]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                hold[t][0][i] = pack_h2(cr[0][i], cr[1][i]);
+                hold[t][1][i] = pack_h2(ci[0][i], ci[1][i]);
+            }
+        }
+    }
+    // the first stage-2 tile and output gate, fetched across the barriers
+    h8 Ar, Ai, nAi;
+    col_tile(tabs, M::kC3S2 + wave * M::kTile, lane, Ar, Ai, nAi);
+    T *orow = out + s * NC;
+    const T *vrow = v != nullptr ? v + s * NC : nullptr;
+    auto out_off = [&](int na, int i) {
+        return 4u * ((uint32_t)(na + RA * (4 * g + i)) * (uint32_t)N2 + (uint32_t)(c0 + 2 * c));
+    };
+    uint2 gq[4];
+    if (vrow != nullptr && 4 * g < RB / 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gq[i] = ldu<uint2>(vrow, out_off(wave, i));
+    }
+    __syncthreads();
+    if (4 * g < RA) {
+#pragma unroll
+        for (int t = 0; t < NPU; ++t) {
+            const int u = wave * NPU + t, p = u >> 1, ct = u & 1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int o = (ct * 32 + c) * M::C32 + ((4 * g + i) * RB + 2 * p) * 2;
+                *reinterpret_cast<uint32_t *>(L + o) = hold[t][0][i];
+                *reinterpret_cast<uint32_t *>(L + o + 16 * M::C32) = hold[t][1][i];
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- stage 2: per n_a the RB-point DFT over f_b with omega_N1^{n_a f_b} (its table
+    // tile), rows n_b = 4 g + i < RB/2: outputs n1 = n_a + RA n_b (t < N); conjugate,
+    // scale, gate, store
+    const float comp = __builtin_ldexpf(kscale[s % H], kRowKLog2 + 4 * kDft32Log2 + mp_p1_log2(LOG1) +
+                                                           mp_c3_log2(LOG1));
+    const bool in = g < RB / 8;
+#pragma unroll
+    for (int t = 0; t < RA / 8; ++t) {
+        const int na = wave + 8 * t;
+        f4 cr[2], ci[2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            h8 br, bi;
+            col_operand(L, (ct * 32 + c) * M::C32 + (na * RB + 8 * g) * 2, M::C32, in, M::kZero, br, bi);
+            cm_constA(Ar, Ai, nAi, br, bi, cr[ct], ci[ct]);
+        }
+        uint2 gn[4];
+        if (t + 1 < RA / 8) {
+            col_tile(tabs, M::kC3S2 + (na + 8) * M::kTile, lane, Ar, Ai, nAi);
+            if (vrow != nullptr && 4 * g < RB / 2) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) gn[i] = ldu<uint2>(vrow, out_off(na + 8, i));
+            }
+        }
+        if (4 * g < RB / 2) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float2 y0 = make_float2(cr[0][i] * comp, -ci[0][i] * comp);
+                float2 y1 = make_float2(cr[1][i] * comp, -ci[1][i] * comp);
+                if (vrow != nullptr) {
+                    const float2 g0 = t2f<T>(gq[i].x), g1 = t2f<T>(gq[i].y);
+                    y0 = make_float2(y0.x * g0.x, y0.y * g0.y);
+                    y1 = make_float2(y1.x * g1.x, y1.y * g1.y);
+                }
+                stu(orow, out_off(na, i), make_uint2(f2t<T>(y0), f2t<T>(y1)));
+            }
+        }
+        if (t + 1 < RA / 8) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gq[i] = gn[i];
         }
     }
 }
@@ -1117,6 +1514,7 @@ static hipError_t mp_args(int logn, MpArgs *a) {
     a->w2row = mt.w2row;
     a->big_lo = mt.big_lo;
     a->big_hi = mt.big_hi;
+    a->col = static_cast<const uint4 *>(mt.col);
     return hipSuccess;
 }
 
@@ -1137,13 +1535,21 @@ static hipError_t conv_t(const void *u, const void *w, const void *v, void *out,
     if (e != hipSuccess) return e;
     T *ws = (T *)work;
     float2 *self_area = (float2 *)((char *)work + (size_t)nseq * ((size_t)1 << (LOG1 + kMpLog2)) * 2 * sizeof(T));
-    auto k1 = mp_pass1_kernel<LOG1, T, false>;
     constexpr bool kHalf = std::is_same<TK, __half2>::value;
-    auto k3 = mp_pass3_kernel<LOG1, T, kHalf>;
-    if ((e = allow_lds(k1, P::kLds)) != hipSuccess) return e;
-    if ((e = allow_lds(k3, P::kLds)) != hipSuccess) return e;
-    hipLaunchKernelGGL(k1, dim3(N2 / P::C, (unsigned)nseq), dim3(kMpThreads), P::kLds, stream,
-                       (const T *)u, (const T *)w, (int64_t)0, seq0, ws, ta);
+    // half-precision storage and N1 >= 2^kMpColMinLog1: column passes on the matrix cores
+    constexpr bool kColMm = kHalf && LOG1 >= kMpColMinLog1;
+    if constexpr (kColMm) {
+        if (ta.col == nullptr) return hipErrorNotInitialized;
+        auto k1 = mp_pass1c_kernel<LOG1, T>;
+        if ((e = allow_lds(k1, ColMm<LOG1>::kLds)) != hipSuccess) return e;
+        hipLaunchKernelGGL(k1, dim3(N2 / 32, (unsigned)nseq), dim3(kMpThreads), ColMm<LOG1>::kLds, stream,
+                           (const T *)u, (const T *)w, seq0, ws, ta);
+    } else {
+        auto k1 = mp_pass1_kernel<LOG1, T, false>;
+        if ((e = allow_lds(k1, P::kLds)) != hipSuccess) return e;
+        hipLaunchKernelGGL(k1, dim3(N2 / P::C, (unsigned)nseq), dim3(kMpThreads), P::kLds, stream,
+                           (const T *)u, (const T *)w, (int64_t)0, seq0, ws, ta);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const dim3 g2((1 << LOG1) / 2, (unsigned)nseq);
     if constexpr (std::is_same<TK, __half2>::value) {
@@ -1163,8 +1569,17 @@ static hipError_t conv_t(const void *u, const void *w, const void *v, void *out,
                            (TK *)nullptr, kscale, mask, H, seq0, ta, 1.0f);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k3, dim3(N2 / P::C, (unsigned)nseq), dim3(kMpThreads), P::kLds, stream,
-                       (const T *)ws, (const T *)v, (T *)out, seq0, ta, kscale, H);
+    if constexpr (kColMm) {
+        auto k3 = mp_pass3c_kernel<LOG1, T>;
+        if ((e = allow_lds(k3, ColMm<LOG1>::kLds)) != hipSuccess) return e;
+        hipLaunchKernelGGL(k3, dim3(N2 / 32, (unsigned)nseq), dim3(kMpThreads), ColMm<LOG1>::kLds, stream,
+                           (const T *)ws, (const T *)v, (T *)out, seq0, ta, kscale, H);
+    } else {
+        auto k3 = mp_pass3_kernel<LOG1, T, kHalf>;
+        if ((e = allow_lds(k3, P::kLds)) != hipSuccess) return e;
+        hipLaunchKernelGGL(k3, dim3(N2 / P::C, (unsigned)nseq), dim3(kMpThreads), P::kLds, stream,
+                           (const T *)ws, (const T *)v, (T *)out, seq0, ta, kscale, H);
+    }
     return hipGetLastError();
 }
 

@@ -69,6 +69,19 @@ def test_multipass_sizes_half(logn, dtype):
     check(y, ref, TOL[dtype])
 
 
+@pytest.mark.parametrize("logn,H", [(21, 2), (22, 2), (21, 17)])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_multipass_matrix_core_columns(logn, H, dtype):
+    # N1 = 256 and 512: both column passes on the matrix cores, gated, every sequence
+    # compared whole; H = 17 at N = 2^21 leaves a ragged last chunk (16 sequences per chunk)
+    N = 1 << logn
+    _say(f"multipass columns {dtype} N={N} H={H}")
+    inp = synth.generate(1, H, N, N if H == 2 else 1 << 12, dtype, gated=True, seed=200 + logn + H)
+    y = run_gpu(inp)
+    ref = oracle.fft_conv(inp.f64("u"), inp.f64("k"), inp.f64("w"), inp.f64("v"))
+    check(y, ref, TOL[dtype])
+
+
 @pytest.mark.parametrize("kind", ["band", "random"])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_multipass_mask_half(kind, dtype):
