@@ -210,7 +210,7 @@ hipError_t get_pair3_tables(Pair3Tables *out) {
     const double M2 = 32768.0;
     std::vector<_Float16> fr(2 * 64 * 8), fi(2 * 64 * 8), tw1(4 * 64 * 8), tw3(4 * 64 * 8),
         two1((size_t)64 * 2 * 64 * 8), two2((size_t)32 * 4 * 64 * 8), far_(2 * 64 * 8), fai_(2 * 64 * 8),
-        fbr_(2 * 64 * 8), fbi_(2 * 64 * 8);
+        fbr_(2 * 64 * 8), fbi_(2 * 64 * 8), rtw((size_t)8 * 8 * 32 * 8);
     auto put8 = [](std::vector<_Float16> &v, size_t chunk, int i, double ang) {
         v[chunk * 8 + i] = (_Float16)std::cos(ang);
         v[chunk * 8 + 4 + i] = (_Float16)std::sin(ang);
@@ -252,6 +252,12 @@ hipError_t get_pair3_tables(Pair3Tables *out) {
                     }
         }
     }
+    for (int fc = 0; fc < 8; ++fc)   // row pass outer twiddle omega_8192^{f_c (n_a + 32 (4 q + k))}
+        for (int q = 0; q < 8; ++q)
+            for (int na = 0; na < 32; ++na)
+                for (int k = 0; k < 4; ++k)
+                    put8(rtw, ((size_t)fc * 8 + q) * 32 + na, k,
+                         -2.0 * pi * (double)((fc * (na + 32 * (4 * q + k))) % 8192) / 8192.0);
     Pair3Tables t{};
     e = upload_h(fr, &t.fr);
     if (e == hipSuccess) e = upload_h(fi, &t.fi);
@@ -263,6 +269,7 @@ hipError_t get_pair3_tables(Pair3Tables *out) {
     if (e == hipSuccess) e = upload_h(fai_, &t.fai_);
     if (e == hipSuccess) e = upload_h(fbr_, &t.fbr_);
     if (e == hipSuccess) e = upload_h(fbi_, &t.fbi_);
+    if (e == hipSuccess) e = upload_h(rtw, &t.rtw);
     if (e != hipSuccess) return e;
     g_pair3_tables[dev] = t;
     *out = t;

@@ -212,6 +212,9 @@ struct Pair3Tables {
     // K slot 8g + j <-> n_a = rho(8g + j)) and B operand [n2][64][8] (column
     // n_a = 16 n2 + c, K slot 8g + j <-> f_a = row_fa(j / 4, 4g + j % 4))
     const void *far_, *fai_, *fbr_, *fbi_;
+    // the row pass's outer twiddle omega_8192^{f_c n_ab}, n_ab = n_a + 32 (4 q + k):
+    // [f_c 8][q 8][n_a 32] x (cos[k], sin[k]) fp16, k < 4
+    const void *rtw;
 };
 hipError_t get_pair3_tables(Pair3Tables *out);
 // with out2: also out2 = v2 * conv(u w, k) from the same transforms (v and v2 non-null)

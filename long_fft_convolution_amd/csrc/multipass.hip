@@ -741,6 +741,10 @@ constexpr size_t kP2Lds = (size_t)kP2LdsFloat2 * sizeof(float2);
 struct BlockMask {
     uint64_t lo, hi;
     __device__ __forceinline__ bool keep(int b) const { return ((b < 64 ? lo >> b : hi >> (b - 64)) & 1) != 0; }
+    // keep bits of blocks 4 j .. 4 j + 3 (bit i of the result: block 4 j + i), j < 32
+    __device__ __forceinline__ uint32_t nibble(int j) const {
+        return (uint32_t)((j < 16 ? lo >> (4 * j) : hi >> (4 * j - 64)) & 15u);
+    }
 };
 static_assert(kP2LdsFloat2 >= 32 * kT1Row && kP2LdsFloat2 >= 8192, "pass-2 LDS");
 
@@ -1128,6 +1132,7 @@ struct MmTables {
     // S2 (A operand, rows f_a in the tile order row_fa) and S2'' (B operand, K slots
     // f_a in that order): DFT-32 tiles [2][64 lanes] x 8 fp16 (re, im)
     const void *far_, *fai_, *fbr_, *fbi_;
+    const void *rtw;       // outer twiddle omega_8192^{f_c n_ab}: [f_c][q][n_a] x (cos[4], sin[4])
 };
 
 // grid (N1 / 2, nseq); block 512; dynamic LDS mm::kLds.
@@ -1182,18 +1187,17 @@ mp_pass2m_kernel(T *__restrict__ ws, float2 *__restrict__ self_area, const __hal
 #pragma unroll
             for (int nc = 0; nc < 8; ++nc) y[k][nc] = io<T>::load2(rowp + 2 * (32 * k + 1024 * nc), lo);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            dft_inplace<8>(y[k]);
-            const uint32_t nab = (uint32_t)(na + 32 * (4 * q + k));
-            apply_pow<8>(y[k], ldu<float2>(ta.tw2, 8u * nab), make_float2(1.f, 0.f));
-        }
-        // n_b = 4q + k sits in K slot kslot(n_b): chunk q & 3, slot 4 (q >> 2) + k
+        for (int k = 0; k < 4; ++k) dft_inplace<8>(y[k]);
+        // n_b = 4q + k sits in K slot kslot(n_b): chunk q & 3, slot 4 (q >> 2) + k.  The
+        // twiddle omega_8192^{n_ab f_c} of the four columns is one fp16 table word
+        // (the same table as the inverse chain's outer twiddle), applied to the fp16 planes.
         const uint32_t o = (uint32_t)((q & 3) * 256 + na * 8 + 4 * (q >> 2));
 #pragma unroll
         for (int fc = 0; fc < 8; ++fc) {
             const uint32_t oc = (uint32_t)((r * 8 + fc) * 1024) + o;
-            const h4 re = {(_Float16)y[0][fc].x, (_Float16)y[1][fc].x, (_Float16)y[2][fc].x, (_Float16)y[3][fc].x};
-            const h4 im = {(_Float16)y[0][fc].y, (_Float16)y[1][fc].y, (_Float16)y[2][fc].y, (_Float16)y[3][fc].y};
+            h4 re = {(_Float16)y[0][fc].x, (_Float16)y[1][fc].x, (_Float16)y[2][fc].x, (_Float16)y[3][fc].x};
+            h4 im = {(_Float16)y[0][fc].y, (_Float16)y[1][fc].y, (_Float16)y[2][fc].y, (_Float16)y[3][fc].y};
+            if (fc > 0) cmul4(re, im, ldu<h8>(mt.rtw, 16u * (uint32_t)((fc * 8 + q) * 32 + na)));
             *reinterpret_cast<h4 *>(P0 + oc) = re;
             *reinterpret_cast<h4 *>(P1 + oc) = im;
         }
@@ -1265,17 +1269,22 @@ mp_pass2m_kernel(T *__restrict__ ws, float2 *__restrict__ self_area, const __hal
     bool skip[2] = {false, false};
     if (MASKED) {
         kbits = 0;
+        // the blocks 4 f_a + 2 n + (c >> 3) of A's bins are bits 2 n + (c >> 3) of mask
+        // nibble f_a; their partners 127 minus that are bits 3 - 2 n - (c >> 3) of nibble 31 - f_a
+        const uint32_t cb = (uint32_t)(c >> 3);
 #pragma unroll
         for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
-            for (int n = 0; n < 2; ++n)
+            for (int e = 0; e < 4; ++e) {
+                const int fa = row_fa(m2, 4 * g + e);
+                const uint32_t na_ = bm.nibble(fa) >> cb, nb_ = bm.nibble(31 - fa) << cb;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int b = 4 * row_fa(m2, 4 * g + e) + 2 * n + (c >> 3);
+                for (int n = 0; n < 2; ++n) {
                     const int bit = 4 * (2 * m2 + n) + e;
-                    kbits |= (bm.keep(b) ? 1u : 0u) << bit;
-                    kbits |= (bm.keep(127 - b) ? 1u : 0u) << (16 + bit);
+                    kbits |= ((na_ >> (2 * n)) & 1u) << bit;
+                    kbits |= ((nb_ >> (3 - 2 * n)) & 1u) << (16 + bit);
                 }
+            }
 #pragma unroll
         for (int m2 = 0; m2 < 2; ++m2)
             skip[m2] = __builtin_amdgcn_ballot_w64((((kbits >> (8 * m2)) | (kbits >> (16 + 8 * m2))) & 0xffu) != 0) == 0;
@@ -1441,11 +1450,6 @@ mp_pass2m_kernel(T *__restrict__ ws, float2 *__restrict__ self_area, const __hal
 #pragma unroll
     for (int qc = 0; qc < 2; ++qc) {
         const int fc = qc ? fcB : fcA;
-        // outer twiddle of (n_a = 16 n2 + c, n_b = 16 n3 + 4 g + e):
-        // w8192^{f_c (c + 128 g)} (w8192^{16 f_c})^{n2} (w8192^{512 f_c})^{n3} (w8192^{32 f_c})^e
-        const float2 b0 = ldu<float2>(ta.tw2, 8u * ((uint32_t)(fc * (c + 128 * g)) & (N2 - 1)));
-        const float2 s16 = ta.tw2[16 * fc], s512 = ta.tw2[(512 * fc) & (N2 - 1)], s32 = ta.tw2[32 * fc];
-        const float2 s32_2 = cmul(s32, s32), s32_3 = cmul(s32_2, s32);
 #pragma unroll
         for (int n2 = 0; n2 < 2; ++n2) {
             const h8 br = cat8(t3r[qc][0][n2], t3r[qc][1][n2]), bi = cat8(t3i[qc][0][n2], t3i[qc][1][n2]);
@@ -1454,15 +1458,13 @@ mp_pass2m_kernel(T *__restrict__ ws, float2 *__restrict__ self_area, const __hal
                 f4 cr, ci;
                 const h8 fr3 = ftile(mt.fr, n3), fi3 = ftile(mt.fi, n3);
                 cm_constA(fr3, fi3, neg8(fi3), br, bi, cr, ci);   // rows n_b = 16 n3 + 4g + e, col n_a
-                float2 bt = b0;
-                if (n2) bt = cmul(bt, s16);
-                if (n3) bt = cmul(bt, s512);
+                // outer twiddle omega_8192^{f_c n_ab} of (n_a = 16 n2 + c, n_b = 4 (4 n3 + g) + e):
+                // the table word (f_c, q = 4 n3 + g, n_a), applied to the fp16 planes
+                h4 tr = to_h4(cr), ti = to_h4(ci);
+                cmul4(tr, ti, ldu<h8>(mt.rtw, 16u * (uint32_t)((fc * 8 + 4 * n3 + g) * 32 + 16 * n2 + c)));
                 uint32_t d[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float2 we = e == 0 ? bt : cmul(bt, e == 1 ? s32 : (e == 2 ? s32_2 : s32_3));
-                    d[e] = f2h(cmul(make_float2(cr[e], ci[e]), we));
-                }
+                for (int e = 0; e < 4; ++e) d[e] = __builtin_bit_cast(uint32_t, h2v{tr[e], ti[e]});
                 // R2[chain][n_a][n_b]: n_b = 16 n3 + 4 g + e are consecutive
                 const uint32_t o = (uint32_t)((((qc * 8 + fc) * 32 + 16 * n2 + c) * kR2Stride + 16 * n3 + 4 * g) * 4);
                 stu(R2, o, make_uint2(d[0], d[1]));
@@ -1556,7 +1558,7 @@ static hipError_t conv_t(const void *u, const void *w, const void *v, void *out,
         // half-precision storage: the row pass on the matrix cores
         Pair3Tables p3{};
         if ((e = get_pair3_tables(&p3)) != hipSuccess) return e;
-        const MmTables mt{p3.fr, p3.fi, p3.tw1, p3.tw3, p3.far_, p3.fai_, p3.fbr_, p3.fbi_};
+        const MmTables mt{p3.fr, p3.fi, p3.tw1, p3.tw3, p3.far_, p3.fai_, p3.fbr_, p3.fbi_, p3.rtw};
         auto k2 = mask != nullptr ? mp_pass2m_kernel<LOG1, T, true> : mp_pass2m_kernel<LOG1, T, false>;
         if ((e = allow_lds(k2, mm::kLds)) != hipSuccess) return e;
         hipLaunchKernelGGL(k2, g2, dim3(kMpThreads), mm::kLds, stream, ws, self_area, (const __half2 *)kbins,
