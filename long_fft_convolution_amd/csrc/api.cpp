@@ -270,6 +270,57 @@ hipError_t get_pair3_tables(Pair3Tables *out) {
     if (e == hipSuccess) e = upload_h(fbr_, &t.fbr_);
     if (e == hipSuccess) e = upload_h(fbi_, &t.fbi_);
     if (e == hipSuccess) e = upload_h(rtw, &t.rtw);
+    // outer stages for R = 4, 8, 16 (M = 1024 R): 32 / R sub-pairs share one workgroup
+    for (int i = 0; i < 3 && e == hipSuccess; ++i) {
+        const int logr = 2 + i, R = 1 << logr, nch = R / 2;
+        const double M = 1024.0 * R, sc = std::ldexp(1.0, -p16_outer_log2(logr));
+        std::vector<_Float16> o1r(2 * 64 * 8, (_Float16)0.f), o1i(2 * 64 * 8, (_Float16)0.f),
+            o3r(64 * 8, (_Float16)0.f), o3i(64 * 8, (_Float16)0.f), ot1((size_t)64 * 2 * 64 * 8),
+            ot2((size_t)32 * 4 * 64 * 8);
+        for (int l = 0; l < 64; ++l) {
+            const int g = l / 16, c = l % 16;
+            for (int j = 0; j < 8; ++j) {
+                // phase 1: rows rho = 16 nt + c, K slots 4 g + j (j < 4)
+                for (int nt = 0; nt < 2; ++nt) {
+                    const int rw = 16 * nt + c, k = 4 * g + j;
+                    if (j < 4 && rw / R == k / nch) {
+                        const double a = -2.0 * pi * (double)((rw % R) * (k % nch) % R) / R;
+                        o1r[(nt * 64 + l) * 8 + j] = (_Float16)(sc * std::cos(a));
+                        o1i[(nt * 64 + l) * 8 + j] = (_Float16)(sc * std::sin(a));
+                    }
+                }
+                // phase 3: column c = (sub-pair c / nch, n_c = c mod nch), K slot row rho(8 g + j)
+                const int rw = rho(8 * g + j);
+                if (rw / R == c / nch) {
+                    const double a = -2.0 * pi * (double)((rw % R) * (c % nch) % R) / R;
+                    o3r[l * 8 + j] = (_Float16)(sc * std::cos(a));
+                    o3i[l * 8 + j] = (_Float16)(sc * std::sin(a));
+                }
+            }
+            for (int ii = 0; ii < 4; ++ii) {
+                for (int T = 0; T < 64; ++T)        // rows rho = 16 nt + 4 g + i (f_c = rho mod R), cols n_ab
+                    for (int nt = 0; nt < 2; ++nt) {
+                        const int64_t nab = 16 * (T & ~1) + 2 * c + (T & 1);
+                        const int64_t fcv = (16 * nt + 4 * g + ii) % R;
+                        put8(ot1, ((size_t)T * 2 + nt) * 64 + l, ii, -2.0 * pi * (double)(fcv * nab % (int64_t)M) / M);
+                    }
+                for (int rw2 = 0; rw2 < 32; ++rw2)  // row rho (f_c = rho mod R); rows n_b = 16nt3 + 4g + i, cols n_a
+                    for (int nt3 = 0; nt3 < 2; ++nt3)
+                        for (int nt2 = 0; nt2 < 2; ++nt2) {
+                            const int64_t nab = (16 * nt2 + c) + 32 * (16 * nt3 + 4 * g + ii);
+                            const int64_t fcv = rw2 % R;
+                            put8(ot2, (((size_t)rw2 * 2 + nt3) * 2 + nt2) * 64 + l, ii,
+                                 2.0 * pi * (double)(fcv * nab % (int64_t)M) / M);
+                        }
+            }
+        }
+        e = upload_h(o1r, &t.o1r[i]);
+        if (e == hipSuccess) e = upload_h(o1i, &t.o1i[i]);
+        if (e == hipSuccess) e = upload_h(o3r, &t.o3r[i]);
+        if (e == hipSuccess) e = upload_h(o3i, &t.o3i[i]);
+        if (e == hipSuccess) e = upload_h(ot1, &t.ot1[i]);
+        if (e == hipSuccess) e = upload_h(ot2, &t.ot2[i]);
+    }
     if (e != hipSuccess) return e;
     g_pair3_tables[dev] = t;
     *out = t;
@@ -661,7 +712,7 @@ static fftconv_status_t fwd_enqueue(const void *u, const void *K_f, const void *
     if (use_pair_kernel(l, dtype)) {
         e = launch_pair_conv(l, dtype, u, w, v, out, kbins, kscale, mask, B, H, stream);
     } else if (use_pair3_kernel(l, dtype)) {
-        e = launch_pair16k_conv(dtype, u, w, v, out, kbins, kscale, mask, B, H, stream);
+        e = launch_pair16k_conv(l, dtype, u, w, v, out, kbins, kscale, mask, B, H, stream);
     } else if (l <= kFusedMaxLog) {
         Tables tb{};
         e = get_tables(l, &tb);
@@ -748,7 +799,7 @@ static BwdLayout bwd_layout(int64_t B, int64_t H, int64_t N, fftconv_dtype_t dty
     o.kc = take(fftconv_filter_bytes(H, N, dtype));
     // N = 1024 (fp16 / bf16): du, dw and dk come from kernels that need no scratch beyond
     // the conjugated spectrum (the dk chain's areas below are then empty)
-    const bool p16 = use_pair3_kernel(log2_exact(N), dtype);
+    const bool p16 = log2_exact(N) == 14 && use_pair3_kernel(14, dtype);
     const bool chain = !use_pair_kernel(log2_exact(N), dtype) && !p16;
     const int64_t P = H * ((B + 1) / 2);
     o.spec = take(p16 ? (size_t)P * kP16SpecBytes : 0);
@@ -843,7 +894,7 @@ fftconv_status_t fftconv_bwd(const void *dy, const void *u, const void *K_f, con
             const float *ksc = reinterpret_cast<const float *>(kb + kf_scale_off());
             e = use_pair_kernel(l, dtype)
                     ? launch_pair_conv(l, dtype, dy, v, w, du, kb + kf_bins_off(H), ksc, mask, B, H, stream, u, dw)
-                    : launch_pair16k_conv(dtype, dy, v, w, du, kb + kf_bins_off(H), ksc, mask, B, H, stream, u, dw);
+                    : launch_pair16k_conv(l, dtype, dy, v, w, du, kb + kf_bins_off(H), ksc, mask, B, H, stream, u, dw);
             if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "du, dw: %s", hipGetErrorString(e));
         } else {
             if (du) {
@@ -861,7 +912,7 @@ fftconv_status_t fftconv_bwd(const void *dy, const void *u, const void *K_f, con
     if (dk && B > 0 && use_pair_kernel(l, dtype)) {
         hipError_t e = launch_pair_dk(dtype, dy, u, w, v, dk, mask, B, H, L, stream);
         if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "dk: %s", hipGetErrorString(e));
-    } else if (dk && B > 0 && use_pair3_kernel(l, dtype)) {
+    } else if (dk && B > 0 && l == 14 && use_pair3_kernel(l, dtype)) {
         // N = 16384 (fp16 / bf16): the pairs' spectra of u w, then one correlation per pair
         hipError_t e = launch_pair16k_dk(dtype, dy, u, w, v, ws + lay.part, ws + lay.spec,
                                          reinterpret_cast<float *>(ws + lay.pscale), mask, B, H, stream);
@@ -1101,10 +1152,11 @@ fftconv_status_t fftconv_export_filter_rfft(const void *K_f, int64_t H, int64_t 
         if (hdr.layout == KF_PAIR || hdr.layout == KF_PAIR3) {
             const _Float16 *p = reinterpret_cast<const _Float16 *>(bins) + h * slots * 2;
             for (int64_t f = 0; f <= N; ++f) {
-                int64_t a = hdr.layout == KF_PAIR ? pair_kf_index(f) : pair3_kf_index(f);
+                const int logr = log2_exact(N) - 9;
+                int64_t a = hdr.layout == KF_PAIR ? pair_kf_index(f) : pair3_kf_index(f, logr);
                 double sign = 1.0;
                 if (a < 0) {   // row not stored: conjugate of the mirror bin 2N - f
-                    a = pair3_kf_index(2 * N - f);
+                    a = pair3_kf_index(2 * N - f, logr);
                     sign = -1.0;
                 }
                 o[2 * f] = (double)p[a] * inv_sh;

@@ -51,14 +51,16 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // it: 16-byte chunk q = (mt2 * 4 + nt) * 64 + lane, lane = 16 g + c, holds
 // re[0..3] then im[0..3] (fp16) of bins f = 16 nt + c + 64 (16 mt2 + 4 g + i).
 inline bool use_pair_kernel(int logn, int st) { return logn == 10 && st != ST_F32; }
-// The three-stage matrix-core kernel handles N = 16384 in fp16/bf16 storage.
-// Its filter layout (KF_PAIR3) stores the rows f_c = f mod 32 in [0, 16] of
-// the 2N-bin spectrum; chunk ((f_c * 2 + mt2) * 2 + nt) * 64 + lane holds
-// re[0..3], im[0..3] of bins f = f_c + 32 (16 nt + c) + 1024 (16 mt2 + 4 g + i).
-inline bool use_pair3_kernel(int logn, int st) { return logn == 14 && st != ST_F32; }
+// The three-stage matrix-core kernel handles N = 2048 .. 16384 in fp16/bf16
+// storage: the 2N-point transform is M = 1024 R points with R = 2N / 1024 =
+// 2^logr (logr = logn - 9 = 2 .. 5) outer rows of 1024.  Its filter layout
+// (KF_PAIR3) stores the rows f_c = f mod R in [0, R/2] of the 2N-bin spectrum;
+// chunk ((f_c * 2 + mt2) * 2 + nt) * 64 + lane holds re[0..3], im[0..3] of bins
+// f = f_c + R (16 nt + c) + 32 R (16 mt2 + 4 g + i).
+inline bool use_pair3_kernel(int logn, int st) { return logn >= 11 && logn <= 14 && st != ST_F32; }
 inline int64_t kf_slots(int logn, int st) {
     if (use_pair_kernel(logn, st)) return int64_t(2) << logn;
-    if (use_pair3_kernel(logn, st)) return int64_t(17) * 1024;
+    if (use_pair3_kernel(logn, st)) return ((int64_t(1) << (logn - 10)) + 1) * 1024;
     return int64_t(1) << logn;
 }
 // log2 of the normalisation folded into scale[h]: 4N for the half-length
@@ -71,11 +73,13 @@ inline int kf_norm_log2(int logn, int st) {
 inline int kf_target_log2(int logn, int st) {
     return (use_pair_kernel(logn, st) || use_pair3_kernel(logn, st)) ? 0 : 14;
 }
-// fp16 element offset of the real part of bin f in the KF_PAIR3 layout, or -1
-// when the bin's row is not stored (f mod 32 > 16: read the mirror 2N - f).
-__host__ __device__ inline int64_t pair3_kf_index(int64_t f) {
-    const int64_t fc = f & 31, fb = (f >> 5) & 31, fa = f >> 10;
-    if (fc > 16) return -1;
+// fp16 element offset of the real part of bin f in the KF_PAIR3 layout with
+// R = 2^logr outer rows, or -1 when the bin's row is not stored (f mod R > R/2:
+// read the mirror 2N - f).
+__host__ __device__ inline int64_t pair3_kf_index(int64_t f, int logr = 5) {
+    const int64_t R = int64_t(1) << logr;
+    const int64_t fc = f & (R - 1), fb = (f >> logr) & 31, fa = f >> (logr + 5);
+    if (fc > R / 2) return -1;
     const int64_t mt2 = fa >> 4, g = (fa & 15) >> 2, i = fa & 3, nt = fb >> 4, c = fb & 15;
     return ((((fc * 2 + mt2) * 2 + nt) * 64 + g * 16 + c) * 8) + i;
 }
@@ -215,10 +219,24 @@ struct Pair3Tables {
     // the row pass's outer twiddle omega_8192^{f_c n_ab}, n_ab = n_a + 32 (4 q + k):
     // [f_c 8][q 8][n_a 32] x (cos[k], sin[k]) fp16, k < 4
     const void *rtw;
+    // outer stages of the three-stage kernel for R = 2^(2 + i) < 32 (i < 3), see
+    // P16Outer; for R = 32 the DFT-32 tiles fr, fi and two1, two2 above serve
+    const void *o1r[3], *o1i[3], *o3r[3], *o3i[3], *ot1[3], *ot2[3];
 };
+// Outer-stage tables of the three-stage kernel for one R: the phase-1 DFT (A
+// operand, two row tiles: row rho = 16 nt + c is (sub-pair rho / R, f_c = rho mod R),
+// K slot 8 g + j (j < 4) is (sub-pair k / (R/2), n_c = k mod (R/2)) with k = 4 g + j;
+// zero across sub-pairs), the phase-3 inverse DFT (B operand, one tile: column
+// c = (sub-pair, n_c), K slot 8 g + j = row rho(8 g + j)), and the outer twiddles
+// omega_M^{f_c n_ab} in the layouts of two1, two2 (row rho standing for f_c = rho mod R).
+struct P16Outer {
+    const void *o1r, *o1i, *o3r, *o3i, *two1, *two2;
+};
+// power-of-two factor 2^-p16_outer_log2(logr) folded into each outer-stage table
+inline __host__ __device__ constexpr int p16_outer_log2(int logr) { return logr >= 4 ? 2 : 1; }
 hipError_t get_pair3_tables(Pair3Tables *out);
 // with out2: also out2 = v2 * conv(u w, k) from the same transforms (v and v2 non-null)
-hipError_t launch_pair16k_conv(int st, const void *u, const void *w, const void *v, void *out,
+hipError_t launch_pair16k_conv(int logn, int st, const void *u, const void *w, const void *v, void *out,
                                const void *kbins, const float *kscale, const uint8_t *mask,
                                int64_t B, int64_t H, hipStream_t stream, const void *v2 = nullptr,
                                void *out2 = nullptr);

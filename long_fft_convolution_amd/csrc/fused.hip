@@ -282,20 +282,20 @@ fused_prepare_kernel(const T *__restrict__ k, int64_t L, TK *__restrict__ kbins,
     // N = 16384: the fp16 row (every slot of it is written below) is assembled in the
     // LDS buffer, which is free once every lane holds its A, Bv, and stored as 16-byte
     // words; stored directly, each bin would take four scattered 2-byte stores
-    constexpr bool STAGE = LAYOUT == KF_PAIR3;
+    constexpr bool STAGE = LAYOUT == KF_PAIR3 && LOGN == 14;
     static_assert(!STAGE || (Pl::SPW == 1 && 17 * 1024 * 4 <= Pl::NC * (int)sizeof(float2)),
                   "one sequence per workgroup, its row fits the LDS buffer");
     if (STAGE) __syncthreads();
     constexpr bool PAIR = LAYOUT != KF_NATURAL;
     // s_h = 1 / (scale[h] * norm), exact (both powers of two)
     const float sh = 1.0f / (kscale[h] * (float)(PAIR ? 2 * NC : 4 * NC));
-    constexpr int64_t kRowSlots = LAYOUT == KF_PAIR3 ? 17 * 1024 : (PAIR ? 2 * NC : NC);
+    constexpr int64_t kRowSlots = LAYOUT == KF_PAIR3 ? ((1 << (LOGN - 10)) + 1) * 1024 : (PAIR ? 2 * NC : NC);
     TK *krow = kbins + h * kRowSlots;
     _Float16 *const row16 = STAGE ? reinterpret_cast<_Float16 *>(lds) : reinterpret_cast<_Float16 *>(krow);
     // one real-spectrum bin: natural order, or a matrix-core kernel's lane
     // order (the Hermitian mirror 2N - f is stored as well where its row is)
     auto index_of = [](int64_t f) -> int64_t {
-        return LAYOUT == KF_PAIR3 ? pair3_kf_index(f) : pair_kf_index(f);
+        return LAYOUT == KF_PAIR3 ? pair3_kf_index(f, LOGN - 9) : pair_kf_index(f);
     };
     // ysgn = -1 stores the conjugated spectrum (the correlation of the backward pass)
     auto put = [&](int f, float2 x) {
@@ -380,7 +380,8 @@ static hipError_t launch_prep_t(const void *k, int64_t L, void *kbins, const flo
     const int64_t blocks = (H + Pl::SPW - 1) / Pl::SPW;
     const size_t lds = (size_t)Pl::SPW * Pl::NC * sizeof(float2);
     constexpr bool kHalf = !std::is_same<T, float>::value;
-    constexpr int kLayout = (LOGN == 10 && kHalf) ? KF_PAIR : ((LOGN == 14 && kHalf) ? KF_PAIR3 : KF_NATURAL);
+    constexpr int kLayout =
+        (LOGN == 10 && kHalf) ? KF_PAIR : ((LOGN >= 11 && LOGN <= 14 && kHalf) ? KF_PAIR3 : KF_NATURAL);
     static_assert(kLayout == KF_NATURAL || std::is_same<TK, __half2>::value, "pair layouts store fp16 bins");
     auto kern = fused_prepare_kernel<LOGN, T, TK, kLayout>;
     hipError_t e = hipFuncSetAttribute((const void *)kern,

@@ -107,14 +107,15 @@ static_assert(kWaves == 8, "the LDS address split below assumes 8 waves");
 constexpr int kConv = 0, kSpec = 1, kCorr = 2;
 constexpr int kSpecRows = 32 * 2 * 2 * 64;   // uint4 per pair spectrum (all rows f_c)
 
-// filter chunk of row fc for (mt2, nt): rows f_c <= 16 as stored, the others from
-// the mirror row 32 - f_c (lane 63 - l, tiles flipped, elements reversed, conjugated);
-// FULL: a per-pair spectrum with every row stored
-template <bool FULL = false>
+// filter chunk of row fc (of R = 2^LOGR) for (mt2, nt): rows f_c <= R/2 as stored, the
+// others from the mirror row R - f_c (lane 63 - l, tiles flipped, elements reversed,
+// conjugated); FULL: a per-pair spectrum with every row stored
+template <bool FULL = false, int LOGR = 5>
 __device__ __forceinline__ uint4 k_load(const uint4 *kch, int fc, int mt2, int nt, uint32_t lane) {
     if constexpr (FULL) return ldu<uint4>(kch + ((fc * 2 + mt2) * 2 + nt) * 64, 16u * lane);
-    const bool mir = fc > 16;
-    const uint32_t row = mir ? 32 - fc : fc, a = mir ? 1 - mt2 : mt2, b = mir ? 1 - nt : nt;
+    constexpr int R = 1 << LOGR;
+    const bool mir = fc > R / 2;
+    const uint32_t row = mir ? R - fc : fc, a = mir ? 1 - mt2 : mt2, b = mir ? 1 - nt : nt;
     return ldu<uint4>(kch + ((row * 2 + a) * 2 + b) * 64, 16u * (mir ? 63 - lane : lane));
 }
 __device__ __forceinline__ h8 k_fix(const uint4 &q, bool mir) {
@@ -141,30 +142,51 @@ using namespace p16;
 // outputs have freed their registers.
 // MODE (kConv, kSpec, kCorr) above.  kSpec writes spec_out[p] and scale_out[p] for pair p;
 // kCorr reads them through kbins and kscale and writes row bp H + h of out.
-template <typename T, bool MASKED, bool HAS_W, bool HAS_V, bool DUAL = false, int MODE = kConv>
+// LOGR < 5 (N = 512 R = 2048, 4096, 8192): the 2N-point transform is R = 2^LOGR outer
+// rows of 1024; P = 32 / R pairs of P consecutive channels (the same batch rows) share a
+// workgroup's 32 rows (sub-pair p = row / R, f_c = row mod R), so phase 2 is unchanged.
+// The P channels' rows are adjacent in memory (channel h + p at p N), so every input and
+// output offset of the N = 16384 layout (1024 * slot + column) addresses sub-pair p's
+// values; past the last channel the loads re-read sub-pair 0 and the stores are skipped.
+template <typename T, bool MASKED, bool HAS_W, bool HAS_V, bool DUAL = false, int MODE = kConv, int LOGR = 5>
 __global__ void __launch_bounds__(64 * kWaves, 1)
 pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restrict__ v,
                T *__restrict__ out, const uint4 *__restrict__ kbins, const float *__restrict__ kscale,
                const uint8_t *__restrict__ mask, Pair3Tables tb, int64_t B, int64_t H,
                const T *__restrict__ v2, T *__restrict__ out2, uint4 *__restrict__ spec_out,
-               float *__restrict__ scale_out) {
+               float *__restrict__ scale_out, P16Outer ot) {
     static_assert(!DUAL || HAS_V, "a second output has an output gate of its own");
     static_assert(MODE == kConv || (!DUAL && !HAS_V), "the spectrum and correlation modes have no output gate");
     static_assert(MODE != kSpec || !MASKED, "the spectrum mode stores every bin");
+    static_assert(MODE == kConv || LOGR == 5, "the spectrum and correlation modes are N = 16384 only");
+    static_assert(LOGR >= 2 && LOGR <= 5, "R = 4 .. 32");
     constexpr bool SPEC = MODE == kSpec, CORR = MODE == kCorr;
-    constexpr int N = 16384;
+    constexpr int R = 1 << LOGR, P = 32 / R, NCH = R / 2;   // outer rows, sub-pairs, non-zero n_c
+    constexpr int N = 512 * R;
     constexpr int M2 = 2 * N;
+    constexpr int kKRows = (R / 2 + 1) * 256;                  // uint4 per channel of K_f
     extern __shared__ __align__(16) _Float16 smem[];
     _Float16 *P0 = smem;                    // plane 0 (re) of R1 / R2
     _Float16 *P1 = smem + kR1Plane;         // plane 1 (im)
     h8 *s_tw1 = reinterpret_cast<h8 *>(smem + 2 * kR1Plane);   // [mt][nt][lane]
     h8 *s_tw3 = s_tw1 + 4 * 64;                                 // [nt][nt2][lane]
-    uint8_t *s_mask = reinterpret_cast<uint8_t *>(s_tw3 + 4 * 64);   // mask row of the pair's channel
+    uint8_t *s_mask = reinterpret_cast<uint8_t *>(s_tw3 + 4 * 64);   // mask rows of the P channels
+    // R < 32: the outer DFT tiles, [phase-1 re t0, t1, im t0, t1, phase-3 re, im][lane]
+    h8 *s_out = reinterpret_cast<h8 *>(s_mask + 8 * kMaskBlocks);
 
     const int tid = threadIdx.x;
     for (int i = tid; i < 256; i += 64 * kWaves) {
         s_tw1[i] = reinterpret_cast<const h8 *>(tb.tw1)[i];
         s_tw3[i] = reinterpret_cast<const h8 *>(tb.tw3)[i];
+    }
+    if constexpr (R < 32) {
+        if (tid < 128) {
+            s_out[tid] = reinterpret_cast<const h8 *>(ot.o1r)[tid];
+            s_out[128 + tid] = reinterpret_cast<const h8 *>(ot.o1i)[tid];
+        } else if (tid < 192) {
+            s_out[256 + tid - 128] = reinterpret_cast<const h8 *>(ot.o3r)[tid - 128];
+            s_out[320 + tid - 128] = reinterpret_cast<const h8 *>(ot.o3i)[tid - 128];
+        }
     }
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, c = lane & 15;
     h8 Fr[2], Fi[2], nFi[2];
@@ -175,8 +197,8 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
         nFi[t] = neg8(Fi[t]);
     }
     // outer twiddles of this wave's tiles [tq][nt][lane] and rows [r][nt3][nt2][lane]
-    const h8 *twO1 = reinterpret_cast<const h8 *>(tb.two1) + wave * (kTilesPerWave * 2 * 64);
-    const h8 *twO2 = reinterpret_cast<const h8 *>(tb.two2) + wave * (4 * 64);
+    const h8 *twO1 = reinterpret_cast<const h8 *>(ot.two1) + wave * (kTilesPerWave * 2 * 64);
+    const h8 *twO2 = reinterpret_cast<const h8 *>(ot.two2) + wave * (4 * 64);
     // Every LDS access below is a per-lane base plus a compile-time offset: r1() / r2()
     // split into lane, wave and constant parts (phase 1 writes, 2a reads, 2b writes, 3 reads).
     const int b1w = 4 * g * kR1Row + 8 * c + 256 * (wave & 3) + 4 * (wave >> 2);
@@ -196,10 +218,11 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
     const _Float16 *const r3r = P0 + b3r, *const r3i = P1 + b3r;
     __syncthreads();
 
-    const int64_t PB = (B + 1) / 2, P = H * PB;
+    // groups q = hg PB + bp: channels hg P .. hg P + P - 1, batch rows 2 bp, 2 bp + 1
+    const int64_t PB = (B + 1) / 2, HG = (H + P - 1) / P, NQ = HG * PB;
     const uint32_t nwg = gridDim.x, xcd = blockIdx.x % 8, wg_local = blockIdx.x / 8;
     const uint32_t wg_on_xcd = nwg / 8 + (xcd < nwg % 8 ? 1u : 0u);
-    const int64_t p_begin = P * xcd / 8, p_end = P * (xcd + 1) / 8;
+    const int64_t p_begin = NQ * xcd / 8, p_end = NQ * (xcd + 1) / 8;
 
     // per-lane element offset of phase 1 (n_ab = 128 wave + 2c, n_c = 4 g) and phase 3
     const uint32_t m1 = 16 * kTilesPerWave * wave + 2 * c + 4096 * g;
@@ -218,31 +241,49 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
     };
     const uint32_t ul = lane;
     auto pair_base = [&](int64_t pp, int64_t &oa_, int64_t &ob_, bool &hb_) {
-        // pairs < 2^31; the quotient is made wave-uniform so that all pair addresses are scalar
+        // groups < 2^31; the quotient is made wave-uniform so that all pair addresses are scalar
         const int64_t hh = __builtin_amdgcn_readfirstlane((uint32_t)pp / (uint32_t)PB), bpp = pp - hh * PB;
         hb_ = 2 * bpp + 1 < B;
-        oa_ = (2 * bpp * H + hh) * N;
+        oa_ = (2 * bpp * H + hh * P) * N;
         ob_ = hb_ ? oa_ + H * N : oa_;
+    };
+    // channels of group pp (P, or fewer in the last channel group)
+    auto group_nv = [&](int64_t pp) -> int {
+        if constexpr (P == 1) return 1;
+        const int64_t hh = __builtin_amdgcn_readfirstlane((uint32_t)pp / (uint32_t)PB);
+        const int64_t r = H - hh * P;
+        return (int)(r < P ? r : P);
     };
     // kSpec: sum of |x| over the pair's transformed values (this lane's share)
     float l1 = 0.f;
-    auto load_batch = [&](int64_t oa_, int64_t ob_, int half, Batch &x) {
+    auto load_batch = [&](int64_t oa_, int64_t ob_, int half, Batch &x, int nv_) {
         const uint32_t *pua = reinterpret_cast<const uint32_t *>(u + oa_);
         const uint32_t *pub = reinterpret_cast<const uint32_t *>(u + ob_);
         const uint32_t *pwa = reinterpret_cast<const uint32_t *>(w + oa_);
         const uint32_t *pwb = reinterpret_cast<const uint32_t *>(w + ob_);
 #pragma unroll
-        for (int qq = 0; qq < 2; ++qq)
+        for (int j = 0; j < 4; ++j) {
+            // element m1 + 1024 j is slot 4 g + j of sub-pair (4 g + j) / NCH (channel offset
+            // included); past the group's channels, sub-pair 0.  P > 1 takes the j term into
+            // the lane offset, so that the correction applies to the whole offset.
+            uint32_t lo = 2 * m1;
+            int mj = 1024 * j;
+            if constexpr (P > 1) {
+                const int sp = (4 * g + j) / NCH;
+                lo = 2u * (uint32_t)(m1 + 1024 * j - (sp >= nv_ ? sp * N : 0));
+                mj = 0;
+            }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int m = (32 * (2 * half + qq) + 1024 * j) / 2;   // in dwords
-                x.xa[qq][j] = ldu<uint32_t>(pua + m, 2 * m1);
-                x.xb[qq][j] = ldu<uint32_t>(pub + m, 2 * m1);
+            for (int qq = 0; qq < 2; ++qq) {
+                const int m = (32 * (2 * half + qq) + mj) / 2;   // in dwords
+                x.xa[qq][j] = ldu<uint32_t>(pua + m, lo);
+                x.xb[qq][j] = ldu<uint32_t>(pub + m, lo);
                 if (HAS_W) {
-                    x.ga[qq][j] = ldu<uint32_t>(pwa + m, 2 * m1);
-                    x.gb[qq][j] = ldu<uint32_t>(pwb + m, 2 * m1);
+                    x.ga[qq][j] = ldu<uint32_t>(pwa + m, lo);
+                    x.gb[qq][j] = ldu<uint32_t>(pwb + m, lo);
                 }
             }
+        }
     };
     auto load_tw = [&](int half, h8 (&tw)[2][2][2]) {
 #pragma unroll
@@ -278,7 +319,12 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
                     f4 ar, ai;
-                    cm_constA(Fr[nt], Fi[nt], nFi[nt], br, bi, ar, ai);   // rows f_c = 16nt + 4g + i, cols n_ab
+                    if constexpr (R == 32) {
+                        cm_constA(Fr[nt], Fi[nt], nFi[nt], br, bi, ar, ai);   // rows f_c = 16nt + 4g + i, cols n_ab
+                    } else {   // block-diagonal DFT-R tile (rows: sub-pair, f_c), read at use
+                        const h8 o_r = s_out[nt * 64 + lane], o_i = s_out[128 + nt * 64 + lane];
+                        cm_constA(o_r, o_i, neg8(o_i), br, bi, ar, ai);
+                    }
                     yr[qq][par][nt] = to_h4(ar);
                     yi[qq][par][nt] = to_h4(ai);
                     cmul4(yr[qq][par][nt], yi[qq][par][nt], tw[qq][par][nt]);
@@ -302,22 +348,39 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
     int64_t oa, ob;
     bool has_b;
     pair_base(p, oa, ob, has_b);
+    int nv = group_nv(p);
     Batch x0, x1;
-    load_batch(oa, ob, 0, x0);
-    load_batch(oa, ob, 1, x1);
+    load_batch(oa, ob, 0, x0, nv);
+    load_batch(oa, ob, 1, x1, nv);
+    // channel of sub-pair sp of the current group (past the last channel: the group's first)
+    auto chan = [&](int64_t hg, int sp) -> int64_t { return hg * P + (sp < nv ? sp : 0); };
+    // P > 1: element offset correction of an access of sub-pair sp (sub-pair 0 past the last
+    // channel); rows gamma = (sp, n_c) of the outputs are 1024 gamma apart
+    auto past = [&](int gamma) -> bool { return P > 1 && (gamma / NCH) >= nv; };
+    // 16 output-gate values of rows gamma = 4 kq + (lane >> 4) of the row at element row_:
+    // P > 1 moves the row term into the lane offset, corrected past the last channel
+    auto gate_ld = [&](const T *gp, int64_t row_, int kq) -> uint4 {
+        if constexpr (P == 1) return ldu_nt<uint4>(gp + row_ + 4096 * kq, 2 * m4);
+        const int gm = 4 * kq + (lane >> 4);
+        return ldu_nt<uint4>(gp + row_, 2u * (uint32_t)(4096 * kq + m4 - (past(gm) ? (gm / NCH) * N : 0)));
+    };
 
     for (; p < p_end; p += wg_on_xcd) {
-        const int64_t h = __builtin_amdgcn_readfirstlane((uint32_t)p / (uint32_t)PB);
+        const int64_t h = __builtin_amdgcn_readfirstlane((uint32_t)p / (uint32_t)PB);   // channel group
         // (the six stages' table factors are undone with the channel scale; kCorr: the pair's)
         const float ks = SPEC ? 1.f : __builtin_ldexpf(kscale[CORR ? p : h], 6 * kDft32Log2);
         const int64_t oo = CORR ? ((p - h * PB) * H + h) * N : 0;   // kCorr output row
         int64_t p_nx = p + wg_on_xcd, oa_nx, ob_nx;
         bool hb_nx;
         pair_base(p_nx < p_end ? p_nx : p, oa_nx, ob_nx, hb_nx);
+        const int nv_nx = group_nv(p_nx < p_end ? p_nx : p);
 
-        // the mask row is read in phase 2 only, after the barrier that ends phase 1
-        if (MASKED && tid < kMaskBlocks / 4)
-            reinterpret_cast<uint32_t *>(s_mask)[tid] = reinterpret_cast<const uint32_t *>(mask + h * kMaskBlocks)[tid];
+        // the mask rows are read in phase 2 only, after the barrier that ends phase 1
+        if (MASKED && tid < P * kMaskBlocks / 4) {
+            const int64_t mc = P == 1 ? h : chan(h, tid / (kMaskBlocks / 4));
+            reinterpret_cast<uint32_t *>(s_mask)[tid] =
+                reinterpret_cast<const uint32_t *>(mask + mc * kMaskBlocks)[tid % (kMaskBlocks / 4)];
+        }
 
         // ---- phase 1: outer DFT over n_c for this wave's tiles T of n_ab, two batches
         // (loads are issued in the order they are consumed: vmcnt waits are in order)
@@ -365,13 +428,20 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                 ai_[r][mt] = *reinterpret_cast<const h8 *>(r2i + o);
             }
         }
-        const uint4 *kch = kbins + (CORR ? p * (int64_t)kSpecRows : h * (int64_t)(17 * 256));
+        // filter rows: row rho = wave + 8 r is f_c = rho mod R of sub-pair rho / R
+        auto kchan = [&](int rho) -> const uint4 * {
+            if constexpr (R == 32) return kbins + (CORR ? p * (int64_t)kSpecRows : h * (int64_t)kKRows);
+            return kbins + chan(h, rho >> LOGR) * (int64_t)kKRows;
+        };
+        // f_c of row rho (rho < 32)
+        auto rowfc = [&](int rho) -> int { return R == 32 ? rho : (rho & (R - 1)); };
         uint4 kq[2][2];
         if (!SPEC) {
 #pragma unroll
             for (int mt2 = 0; mt2 < 2; ++mt2)
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) kq[mt2][nt] = k_load<CORR>(kch, wave, mt2, nt, ul);
+                for (int nt = 0; nt < 2; ++nt)
+                    kq[mt2][nt] = k_load<CORR, LOGR>(kchan(wave), rowfc(wave), mt2, nt, ul);
         }
         __syncthreads();
 
@@ -390,12 +460,13 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
 #pragma unroll
                 for (int mt2 = 0; mt2 < 2; ++mt2)
 #pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) kk[mt2][nt] = k_fix(kq[mt2][nt], !CORR && fc > 16);
+                    for (int nt = 0; nt < 2; ++nt) kk[mt2][nt] = k_fix(kq[mt2][nt], !CORR && rowfc(fc) > R / 2);
                 if (r + 1 < kRowsPerWave) {
 #pragma unroll
                     for (int mt2 = 0; mt2 < 2; ++mt2)
 #pragma unroll
-                        for (int nt = 0; nt < 2; ++nt) kq[mt2][nt] = k_load<CORR>(kch, fc + kWaves, mt2, nt, lx);
+                        for (int nt = 0; nt < 2; ++nt)
+                            kq[mt2][nt] = k_load<CORR, LOGR>(kchan(fc + kWaves), rowfc(fc + kWaves), mt2, nt, lx);
                 }
 #pragma unroll
                 for (int nt3 = 0; nt3 < 2; ++nt3)
@@ -407,12 +478,12 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                 if (HAS_V) {
 #pragma unroll
                     for (int tt = 0; tt < kTilesPerWave; ++tt) {
-                        vq[tt] = ldu_nt<uint4>(v + (tt < 4 ? oa : ob) + 4096 * (tt & 3), 2 * m4);
+                        vq[tt] = gate_ld(v, tt < 4 ? oa : ob, tt & 3);
                     }
                 }
                 // pinned order: the gate is consumed first, and vmcnt waits are in order
                 __builtin_amdgcn_sched_barrier(0);
-                load_batch(oa_nx, ob_nx, 0, x0);
+                load_batch(oa_nx, ob_nx, 0, x0, nv_nx);
                 __builtin_amdgcn_sched_barrier(0);
             }
             // S1: data A (M = n_a tiles mt, K = n_b), const B F[nt] (N = f_b); twiddle w1024^{n_a f_b}
@@ -452,10 +523,11 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                         asm volatile("" : "+v"(lc), "+v"(lg));
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            const int f = fc + 32 * (16 * nt + lc) + 1024 * (16 * mt2 + 4 * lg + i);
+                            const int f = rowfc(fc) + R * (16 * nt + lc) + 32 * R * (16 * mt2 + 4 * lg + i);
                             const int fr_ = f <= N ? f : M2 - f;
                             int blk = fr_ / (N / kMaskBlocks);
                             blk = blk > kMaskBlocks - 1 ? kMaskBlocks - 1 : blk;
+                            if (R < 32) blk += (fc >> LOGR) * kMaskBlocks;
                             if (!s_mask[blk]) kf[i] = kf[4 + i] = (_Float16)0.f;
                         }
                     }
@@ -498,11 +570,12 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
             }
         }
         if (SPEC) {   // no inverse: the next pair's second input batch, then the next pair
-            load_batch(oa_nx, ob_nx, 1, x1);
+            load_batch(oa_nx, ob_nx, 1, x1, nv_nx);
             __syncthreads();
             oa = oa_nx;
             ob = ob_nx;
             has_b = hb_nx;
+            nv = nv_nx;
             continue;
         }
         __syncthreads();
@@ -511,14 +584,24 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
         // of this wave's tiles, staged as fp32 in its own R2 bytes once every tile is read,
         // then gated and stored as contiguous 16-byte rows
         f4 ya[kTilesPerWave], yb[kTilesPerWave];
+        // R < 32: the block-diagonal inverse DFT-R tile, and column c = (sub-pair, n_c)
+        // takes its channel's scale
+        float ksl = ks;
+        if constexpr (R < 32)
+            ksl = __builtin_ldexpf(kscale[chan(h, c / NCH)], 4 * kDft32Log2 + 2 * p16_outer_log2(LOGR));
 #pragma unroll
         for (int tt = 0; tt < kTilesPerWave; ++tt) {
             // r2(8 g, 16 T + c)
             const h8 dr = *reinterpret_cast<const h8 *>(r3r + 128 * tt);
             const h8 di = *reinterpret_cast<const h8 *>(r3i + 128 * tt);
-            cm_dataA_conj(dr, di, Fr[0], Fi[0], nFi[0], ya[tt], yb[tt]);   // rows n_ab = 16T + 4g + i, col n_c = c
-            ya[tt] *= ks;
-            yb[tt] *= ks;
+            if constexpr (R == 32) {
+                cm_dataA_conj(dr, di, Fr[0], Fi[0], nFi[0], ya[tt], yb[tt]);   // rows n_ab = 16T + 4g + i, col n_c = c
+            } else {   // the block-diagonal inverse DFT-R tile, read at use
+                const h8 f3r = s_out[256 + lane], f3i = s_out[320 + lane];
+                cm_dataA_conj(dr, di, f3r, f3i, neg8(f3i), ya[tt], yb[tt]);
+            }
+            ya[tt] *= ksl;
+            yb[tt] *= ksl;
             __builtin_amdgcn_sched_barrier(0);   // (bounds the live R2 operands)
         }
         {
@@ -535,16 +618,17 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
             uint4 vq2[8];
             if (DUAL) {   // (issued before the next input batch: vmcnt waits are in order)
 #pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    vq2[k] = ldu_nt<uint4>(v2 + (k < 4 ? oa : ob) + 4096 * (k & 3), 2 * m4);
+                for (int k = 0; k < 8; ++k) vq2[k] = gate_ld(v2, k < 4 ? oa : ob, k & 3);
             }
             __builtin_amdgcn_sched_barrier(0);
             // the second input batch of the next pair is fetched while the outputs are stored
-            load_batch(oa_nx, ob_nx, 1, x1);
+            load_batch(oa_nx, ob_nx, 1, x1, nv_nx);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 if (CORR && k >= 4) break;   // the real part only
+                // rows of sub-pairs past the group's last channel are not stored
+                const bool skip = past(4 * (k & 3) + (lane >> 4));
                 // without a second row (ob == oa) its stores repeat the first row's values
                 const int kk = (k >= 4 && !has_b) ? k - 4 : k;
                 const char *src = s8 + 2 * ((kk >> 2) * kR1Plane + (kk & 3) * 8192);
@@ -560,7 +644,8 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                         y2[4 + i] = yv[4 + i] * gb[i];
                     }
                     const uint2 lo2 = st<T>::pack4(y2), hi2 = st<T>::pack4(y2 + 4);
-                    stu_nt(out2 + (k < 4 ? oa : ob) + 4096 * (k & 3), 2 * m4, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
+                    if (!skip)
+                        stu_nt(out2 + (k < 4 ? oa : ob) + 4096 * (k & 3), 2 * m4, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
                 }
                 if (HAS_V) {
                     float ga[4], gb[4];
@@ -573,43 +658,58 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                     }
                 }
                 const uint2 lo = st<T>::pack4(yv), hi = st<T>::pack4(yv + 4);
-                stu_nt(out + (CORR ? oo : (k < 4 ? oa : ob)) + 4096 * (k & 3), 2 * m4,
-                       make_uint4(lo.x, lo.y, hi.x, hi.y));
+                if (!skip)
+                    stu_nt(out + (CORR ? oo : (k < 4 ? oa : ob)) + 4096 * (k & 3), 2 * m4,
+                           make_uint4(lo.x, lo.y, hi.x, hi.y));
             }
         }
         __syncthreads();
         oa = oa_nx;
         ob = ob_nx;
         has_b = hb_nx;
+        nv = nv_nx;
     }
 }
 
-// persistent grid: one workgroup per CU, at most one per pair (and at least 8, one per XCD)
-static hipError_t p16_grid(int64_t B, int64_t H, int64_t *blocks) {
+// persistent grid: one workgroup per CU, at most one per group of pairs (and at least 8, one
+// per XCD); a group is 32 / R pairs of consecutive channels
+static hipError_t p16_grid(int64_t B, int64_t H, int64_t *blocks, int logr = 5) {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) {
         int n = 0;
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
             cus = n;
     }
-    const int64_t pairs = H * ((B + 1) / 2);
+    const int64_t P = 32 >> logr;
+    const int64_t pairs = (H + P - 1) / P * ((B + 1) / 2);
     if (pairs >= ((int64_t)1 << 31)) return hipErrorInvalidValue;   // pair indices are 32-bit
     *blocks = cus;
     if (*blocks > pairs) *blocks = pairs < 8 ? 8 : pairs;
     return hipSuccess;
 }
 
-static constexpr size_t kP16Lds = (size_t)2 * kR1Plane * sizeof(_Float16) + 2 * 256 * 16 + kMaskBlocks;
+// LDS: the two planes, the inner twiddle tables, the mask rows of up to 8 channels, the
+// outer DFT tiles of R < 32 (six planes of 64 lanes x 16 bytes)
+static constexpr size_t kP16Lds =
+    (size_t)2 * kR1Plane * sizeof(_Float16) + 2 * 256 * 16 + 8 * kMaskBlocks + 6 * 64 * 16;
+static_assert(kP16Lds <= 160 * 1024, "LDS of one workgroup");
 
-hipError_t launch_pair16k_conv(int st_, const void *u, const void *w, const void *v, void *out,
-                               const void *kbins, const float *kscale, const uint8_t *mask,
-                               int64_t B, int64_t H, hipStream_t stream, const void *v2, void *out2) {
-    if (out2 != nullptr && (v == nullptr || v2 == nullptr)) return hipErrorInvalidValue;
+static P16Outer p16_outer(const Pair3Tables &tb, int logr) {
+    if (logr == 5) return P16Outer{tb.fr, tb.fi, tb.fr, tb.fi, tb.two1, tb.two2};
+    const int i = logr - 2;
+    return P16Outer{tb.o1r[i], tb.o1i[i], tb.o3r[i], tb.o3i[i], tb.ot1[i], tb.ot2[i]};
+}
+
+template <int LOGR>
+static hipError_t pair16k_conv_r(int st_, const void *u, const void *w, const void *v, void *out,
+                                 const void *kbins, const float *kscale, const uint8_t *mask, int64_t B,
+                                 int64_t H, hipStream_t stream, const void *v2, void *out2) {
     Pair3Tables tb{};
     hipError_t e = get_pair3_tables(&tb);
     if (e != hipSuccess) return e;
     int64_t blocks = 0;
-    if ((e = p16_grid(B, H, &blocks)) != hipSuccess) return e;
+    if ((e = p16_grid(B, H, &blocks, LOGR)) != hipSuccess) return e;
+    const P16Outer ot = p16_outer(tb, LOGR);
     const size_t lds = kP16Lds;
     auto go = [&](auto kern, auto *tp) -> hipError_t {
         using TT = std::remove_pointer_t<decltype(tp)>;
@@ -618,7 +718,7 @@ hipError_t launch_pair16k_conv(int st_, const void *u, const void *w, const void
         if (err != hipSuccess) return err;
         hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * kWaves), lds, stream, (const TT *)u,
                            (const TT *)w, (const TT *)v, (TT *)out, (const uint4 *)kbins, kscale, mask, tb,
-                           B, H, (const TT *)v2, (TT *)out2, (uint4 *)nullptr, (float *)nullptr);
+                           B, H, (const TT *)v2, (TT *)out2, (uint4 *)nullptr, (float *)nullptr, ot);
         return hipGetLastError();
     };
     // one instantiation per (storage type, mask, gates) so that no gate test sits in the loops
@@ -626,26 +726,39 @@ hipError_t launch_pair16k_conv(int st_, const void *u, const void *w, const void
         using TT = std::remove_pointer_t<decltype(tp)>;
         if (out2 != nullptr) {   // two outputs: both output gates present
             switch ((mask ? 2 : 0) | (w ? 1 : 0)) {
-            case 0: return go(pair16k_kernel<TT, false, false, true, true>, tp);
-            case 1: return go(pair16k_kernel<TT, false, true, true, true>, tp);
-            case 2: return go(pair16k_kernel<TT, true, false, true, true>, tp);
-            default: return go(pair16k_kernel<TT, true, true, true, true>, tp);
+            case 0: return go(pair16k_kernel<TT, false, false, true, true, kConv, LOGR>, tp);
+            case 1: return go(pair16k_kernel<TT, false, true, true, true, kConv, LOGR>, tp);
+            case 2: return go(pair16k_kernel<TT, true, false, true, true, kConv, LOGR>, tp);
+            default: return go(pair16k_kernel<TT, true, true, true, true, kConv, LOGR>, tp);
             }
         }
         const int sel = (mask ? 4 : 0) | (w ? 2 : 0) | (v ? 1 : 0);
         switch (sel) {
-        case 0: return go(pair16k_kernel<TT, false, false, false>, tp);
-        case 1: return go(pair16k_kernel<TT, false, false, true>, tp);
-        case 2: return go(pair16k_kernel<TT, false, true, false>, tp);
-        case 3: return go(pair16k_kernel<TT, false, true, true>, tp);
-        case 4: return go(pair16k_kernel<TT, true, false, false>, tp);
-        case 5: return go(pair16k_kernel<TT, true, false, true>, tp);
-        case 6: return go(pair16k_kernel<TT, true, true, false>, tp);
-        default: return go(pair16k_kernel<TT, true, true, true>, tp);
+        case 0: return go(pair16k_kernel<TT, false, false, false, false, kConv, LOGR>, tp);
+        case 1: return go(pair16k_kernel<TT, false, false, true, false, kConv, LOGR>, tp);
+        case 2: return go(pair16k_kernel<TT, false, true, false, false, kConv, LOGR>, tp);
+        case 3: return go(pair16k_kernel<TT, false, true, true, false, kConv, LOGR>, tp);
+        case 4: return go(pair16k_kernel<TT, true, false, false, false, kConv, LOGR>, tp);
+        case 5: return go(pair16k_kernel<TT, true, false, true, false, kConv, LOGR>, tp);
+        case 6: return go(pair16k_kernel<TT, true, true, false, false, kConv, LOGR>, tp);
+        default: return go(pair16k_kernel<TT, true, true, true, false, kConv, LOGR>, tp);
         }
     };
     if (st_ == ST_F16) return pick((__half *)nullptr);
     return pick((__hip_bfloat16 *)nullptr);
+}
+
+hipError_t launch_pair16k_conv(int logn, int st_, const void *u, const void *w, const void *v, void *out,
+                               const void *kbins, const float *kscale, const uint8_t *mask,
+                               int64_t B, int64_t H, hipStream_t stream, const void *v2, void *out2) {
+    if (out2 != nullptr && (v == nullptr || v2 == nullptr)) return hipErrorInvalidValue;
+    switch (logn) {
+    case 11: return pair16k_conv_r<2>(st_, u, w, v, out, kbins, kscale, mask, B, H, stream, v2, out2);
+    case 12: return pair16k_conv_r<3>(st_, u, w, v, out, kbins, kscale, mask, B, H, stream, v2, out2);
+    case 13: return pair16k_conv_r<4>(st_, u, w, v, out, kbins, kscale, mask, B, H, stream, v2, out2);
+    case 14: return pair16k_conv_r<5>(st_, u, w, v, out, kbins, kscale, mask, B, H, stream, v2, out2);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 // Filter gradient partials at N = 16384: for every pair p = h ceil(B/2) + bp of batch rows
@@ -660,6 +773,7 @@ hipError_t launch_pair16k_dk(int st_, const void *dy, const void *u, const void 
     if (e != hipSuccess) return e;
     int64_t blocks = 0;
     if ((e = p16_grid(B, H, &blocks)) != hipSuccess) return e;
+    const P16Outer ot = p16_outer(tb, 5);
     auto go = [&](auto kern, auto *tp, const void *in, const void *gate, void *o, const void *kb,
                   const float *ksc, const uint8_t *m) -> hipError_t {
         using TT = std::remove_pointer_t<decltype(tp)>;
@@ -668,7 +782,7 @@ hipError_t launch_pair16k_dk(int st_, const void *dy, const void *u, const void 
         if (err != hipSuccess) return err;
         hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * kWaves), kP16Lds, stream, (const TT *)in,
                            (const TT *)gate, (const TT *)nullptr, (TT *)o, (const uint4 *)kb, ksc, m, tb, B, H,
-                           (const TT *)nullptr, (TT *)nullptr, (uint4 *)spec, pscale);
+                           (const TT *)nullptr, (TT *)nullptr, (uint4 *)spec, pscale, ot);
         return hipGetLastError();
     };
     auto pick = [&](auto *tp) -> hipError_t {

@@ -40,10 +40,12 @@ def test_size_helpers():
     F32, F16, BF16 = fc.FFTCONV_F32, fc.FFTCONV_F16, fc.FFTCONV_BF16
     # header 256 B + scales rounded to 256 B + H*N bins of 8 B (fp32) or 4 B (fp16);
     # the matrix-core kernel for N = 1024 (fp16/bf16) keeps all 2N bins of the spectrum;
-    # the one for N = 16384 keeps rows f_c = 0..16 of the 32 x 1024 bin grid (17 * 1024 bins)
+    # the one for N = 2048 .. 16384 keeps rows f_c = 0 .. R/2 of the R x 1024 bin grid,
+    # R = 2N / 1024 (at N = 16384: 17 * 1024 bins)
     assert fc.fftconv_filter_bytes(4, 1024, F32) == 256 + 256 + 4 * 1024 * 8
     assert fc.fftconv_filter_bytes(768, 1024, F16) == 256 + 3072 + 768 * 2048 * 4
-    assert fc.fftconv_filter_bytes(768, 2048, F16) == 256 + 3072 + 768 * 2048 * 4
+    assert fc.fftconv_filter_bytes(768, 2048, F16) == 256 + 3072 + 768 * 3 * 1024 * 4   # rows f mod 4 in [0, 2]
+    assert fc.fftconv_filter_bytes(768, 8192, BF16) == 256 + 3072 + 768 * 9 * 1024 * 4  # rows f mod 16 in [0, 8]
     assert fc.fftconv_filter_bytes(2560, 16384, BF16) == 256 + 10240 + 2560 * 17 * 1024 * 4
     assert fc.fftconv_filter_bytes(2560, 16384, F32) == 256 + 10240 + 2560 * 16384 * 8
     assert fc.fftconv_filter_bytes(0, 1024, F32) == 0

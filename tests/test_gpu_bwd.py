@@ -70,7 +70,8 @@ def test_bwd_n1024(dtype, gates):
     _check(got, want, TOL[dtype])
 
 
-@pytest.mark.parametrize("dtype,N,L", [("f32", 2048, 2048), ("f16", 4096, 1000), ("bf16", 16384, 16384),
+@pytest.mark.parametrize("dtype,N,L", [("f32", 2048, 2048), ("f16", 4096, 1000), ("bf16", 2048, 2048),
+                                       ("f16", 8192, 8192), ("bf16", 16384, 16384),
                                        ("f16", 16384, 3000), ("f32", 1 << 15, 1 << 15),
                                        ("f16", 1 << 15, 5000), ("bf16", 1 << 16, 1 << 16)])
 def test_bwd_sizes(dtype, N, L):

@@ -218,3 +218,64 @@ def test_pair16k_mask(kind):
     y = run_gpu(inp, mask)
     ref = oracle_full(inp, mask)
     check(y, ref, TOL["f16"])
+
+
+# ---- N = 2048, 4096, 8192 in fp16 / bf16 storage run on the same kernel with R = 4, 8, 16
+# outer rows: 32 / R pairs of consecutive channels share a workgroup, so H not a multiple
+# of 32 / R leaves a partial last group of channels
+@pytest.mark.parametrize("logn", [11, 12, 13])
+@pytest.mark.parametrize("B,H", [(1, 1), (2, 9), (4, 16), (5, 3), (1, 37)])
+def test_pair_r_groups(logn, B, H):
+    N = 1 << logn
+    dtype = "f16" if (B + H) % 2 else "bf16"
+    _say(f"pair R kernel N={N} B={B} H={H} {dtype}")
+    inp = synth.generate(B, H, N, N, dtype, gated=True, seed=logn * 1000 + B * 100 + H)
+    y = run_gpu(inp)
+    ref = oracle_full(inp)
+    check(y, ref, TOL[dtype])
+
+
+@pytest.mark.parametrize("logn", [11, 12, 13])
+@pytest.mark.parametrize("gates", ["none", "w", "v"])
+def test_pair_r_gates_and_partial(logn, gates):
+    N = 1 << logn
+    _say(f"pair R kernel N={N} gates={gates}")
+    inp = synth.generate(3, 7, N, N // 3, "f16", gated=True, seed=logn * 10 + len(gates))
+    if gates in ("none", "v"):
+        inp.w = None
+    if gates in ("none", "w"):
+        inp.v = None
+    y = run_gpu(inp)
+    ref = oracle.fft_conv(inp.f64("u"), inp.f64("k"), inp.f64("w"), inp.f64("v"))
+    check(y, ref, TOL["f16"])
+
+
+@pytest.mark.parametrize("logn", [11, 12, 13])
+@pytest.mark.parametrize("kind", ["band", "random"])
+def test_pair_r_mask(logn, kind):
+    N = 1 << logn
+    _say(f"pair R kernel N={N} mask {kind}")
+    H = 11
+    inp = synth.generate(2, H, N, N, "bf16", gated=True, seed=logn + 50)
+    mask = synth.band_mask(H, 27) if kind == "band" else synth.random_mask(H, seed=logn)
+    y = run_gpu(inp, mask)
+    ref = oracle_full(inp, mask)
+    check(y, ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("logn", [11, 13])
+def test_pair_r_layout_spectrum(logn):
+    # the exported spectrum of the R-row layout matches the oracle's FFT of the taps
+    N, L = 1 << logn, 777
+    _say(f"pair R layout export N={N}")
+    inp = synth.generate(1, 5, N, L, "f16", seed=logn + 60)
+    k = inp.k.cuda()
+    K_f = fc.alloc_filter(5, N, k.dtype)
+    fc.fftconv_prepare_filter(k, N, K_f)
+    got = fc.fftconv_export_filter_rfft(K_f, 5, N, k.dtype)
+    k64 = inp.f64("k")
+    for h in range(5):
+        x = np.zeros(2 * N, complex)
+        x[:L] = k64[h]
+        want = oracle.fft(x)[:N + 1]
+        assert np.linalg.norm(got[h] - want) / np.linalg.norm(want) < 2e-3
