@@ -41,7 +41,7 @@ struct KfHeader {
     int64_t n2;   // multi-pass inner size
 };
 constexpr uint32_t kKfMagic = 0x4b544646u;  // "FFTK"
-constexpr uint32_t kKfVersion = 3;
+constexpr uint32_t kKfVersion = 4;
 constexpr size_t kKfHeaderBytes = 256;
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
