@@ -81,12 +81,15 @@ def path_of(w: synth.Workload):
         return "pair1k_kernel (windows of 2048, hop 1024)", "f16", mm
     if w.dtype in ("f16", "bf16") and w.N == 1024:
         return "pair1k_kernel", "f16", mm
-    if w.dtype in ("f16", "bf16") and w.N == 16384:
+    if w.dtype in ("f16", "bf16") and 2048 <= w.N <= 16384:
         return "pair16k_kernel", "f16", mm
     if w.N <= 16384:
         return "fused_conv_kernel", "f32", "fp32 (VALU)"
     if w.dtype == "f32":
         return "mp_pass1+mp_pass2+mp_pass3 (one call)", "f32", "fp32 (VALU)"
+    if w.N >= 1 << 21:   # N1 = N / 8192 >= 256: column passes on the matrix cores too
+        return ("mp_pass1c+mp_pass2m+mp_pass3c (one call)", "f16",
+                f"fp16 MFMA operands, fp32 accumulation; {w.dtype} intermediate")
     return ("mp_pass1+mp_pass2m+mp_pass3 (one call)", "f16",
             "column passes fp32 (VALU); row pass fp16 MFMA operands, fp32 accumulation; "
             f"{w.dtype} intermediate")
