@@ -47,16 +47,17 @@
  *    thread's last non-OK status.  Calls on different streams may run
  *    concurrently; the library's only shared state is a per-device cache of
  *    constant tables (twiddles, DFT operand tiles) guarded by a mutex.
- *  - Range (fp16 and bf16 storage).  The matrix-core kernels (N = 1024 and
- *    N = 16384, and the row pass of N > 16384) round every transform stage to
- *    fp16 (fp32 accumulation); power-of-two factors folded into their DFT
- *    tables keep the stage results within a small factor of the input (about
+ *  - Range (fp16 and bf16 storage).  Every size runs on the matrix-core
+ *    kernels (N = 1024; N = 2048 .. 16384; the row pass of N > 16384, and its
+ *    column passes for N >= 2^21), which round every transform stage to fp16
+ *    (fp32 accumulation); power-of-two factors folded into their DFT tables
+ *    keep the stage results within a small factor of the input (about
  *    rms(u*w) for a zero-mean input).  Overflow needs |u*w| near the fp16
  *    maximum 65504 (bf16 magnitudes beyond it are not representable on these
  *    paths), or a mean m of u*w whose zero-frequency bin passes it: 32 m at
- *    N = 1024, 256 m at N = 16384, at most 4096 m for N > 16384 (|m| < 15 is
- *    safe at every N).  Nothing is clamped: an overflow gives inf / NaN.
- *    fp32 storage and the fp32 kernels (N = 2048 .. 8192) have fp32 range.
+ *    N = 1024, 64 m to 256 m at N = 2048 .. 16384, at most 4096 m for
+ *    N > 16384 (|m| < 15 is safe at every N).  Nothing is clamped: an
+ *    overflow gives inf / NaN.  fp32 storage has fp32 range.
  *  - The constant tables of a device are built once, by fftconv_init() or by
  *    the first fftconv_prepare_filter / fftconv_prepare_short_filter on that
  *    device: that one call allocates device memory and copies synchronously.
