@@ -217,8 +217,8 @@ fftconv_status_t fftconv_bwd(const void *dy, const void *u, const void *K_f, con
  * filter runs on the matrix cores and keeps the second half of its outputs,
  * which no filter tap wraps around to.  The result is the same causal
  * convolution as fftconv_fwd with this filter.  fp16 and bf16 storage only;
- * no frequency mask (the spectrum is the 2048-point one of the filter).  The
- * backward pass is not provided for this path. */
+ * no frequency mask (the spectrum is the 2048-point one of the filter).  Its
+ * backward pass is fftconv_bwd_short. */
 
 /* Bytes of a short-filter spectrum for H channels (0 for fp32 or H < 1). */
 size_t fftconv_short_filter_bytes(int64_t H, fftconv_dtype_t dtype);
@@ -237,6 +237,31 @@ fftconv_status_t fftconv_prepare_short_filter(const void *k, int64_t H, int64_t 
 fftconv_status_t fftconv_fwd_short(const void *u, const void *K_s, const void *w, const void *v,
                                    void *out, int64_t B, int64_t H, int64_t N, int64_t L_filter,
                                    fftconv_dtype_t dtype, hipStream_t stream);
+
+/* Backward pass of fftconv_fwd_short (the convolutions are trained,
+ * FlashFFTConv summary page, "Key results"): the gradients of sum(dy * out)
+ * with x = u*w and g = v*dy,
+ *   dv = dy * conv(x, k)                       (needs v; NULL = skip)
+ *   du = w * corr(g, k),  dw = u * corr(g, k)  (dw needs w; NULL = skip)
+ *   dk[h, s] = sum_b sum_t g[b,h,t+s] x[b,h,t], s < L_filter  (NULL = skip)
+ * with corr(g, k)[t] = sum_s k[s] g[t+s] (zero past the sequence end), the
+ * same quantities as fftconv_bwd.  dv runs the windowed forward kernel with
+ * dy as the output gate; corr takes, for the outputs of block j, the window
+ * of blocks j and j+1 and its 2048-point circular correlation with the
+ * filter (the conjugated spectrum, first half of the outputs: no
+ * wrap-around); dk accumulates, per channel on chip, the spectrum products
+ * of those windows of g with the zero-padded blocks of x.
+ *   dy, u, w, v   (B, H, N) device arrays, N a positive multiple of 1024;
+ *                 w, v may be NULL (absent gates, as in the forward call)
+ *   K_s           the short-filter spectrum of the forward call
+ *   du, dw, dv    (B, H, N) outputs, dk (H, L_filter) output, all in dtype;
+ *                 each may be NULL; none may overlap an input
+ * No workspace.  B = 0: dk is set to zero, nothing else is written.
+ * Asynchronous on stream. */
+fftconv_status_t fftconv_bwd_short(const void *dy, const void *u, const void *K_s, const void *w,
+                                   const void *v, void *du, void *dk, void *dw, void *dv, int64_t B,
+                                   int64_t H, int64_t N, int64_t L_filter, fftconv_dtype_t dtype,
+                                   hipStream_t stream);
 
 /* ---- Group-axis circular convolution (Flash EQ-Linear) ------------------
  * The Flash EQ-Linear abstract page: an equivariant linear layer is a

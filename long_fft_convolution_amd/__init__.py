@@ -82,6 +82,8 @@ def _load():
     lib.fftconv_prepare_short_filter.restype = ctypes.c_int
     lib.fftconv_fwd_short.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, vp]
     lib.fftconv_fwd_short.restype = ctypes.c_int
+    lib.fftconv_bwd_short.argtypes = [vp] * 9 + [i64, i64, i64, i64, ctypes.c_int, vp]
+    lib.fftconv_bwd_short.restype = ctypes.c_int
     lib.fftconv_eqlinear_weight_bytes.argtypes = [i64, i64, i64, ctypes.c_int]
     lib.fftconv_eqlinear_weight_bytes.restype = sz
     lib.fftconv_eqlinear_prepare.argtypes = [vp, i64, i64, i64, ctypes.c_int, vp, sz, vp]
@@ -279,6 +281,19 @@ def fftconv_fwd_short(u: torch.Tensor, K_s: torch.Tensor, w: torch.Tensor | None
         _stream(stream, u.device)))
 
 
+def fftconv_bwd_short(dy: torch.Tensor, u: torch.Tensor, K_s: torch.Tensor, w: torch.Tensor | None,
+                      v: torch.Tensor | None, du: torch.Tensor | None, dk: torch.Tensor | None,
+                      dw: torch.Tensor | None, dv: torch.Tensor | None, L_filter: int, stream=None) -> None:
+    """Gradients of sum(dy * fftconv_fwd_short(u, K_s, w, v)) into du, dk, dw, dv (None = skip)."""
+    for name, t in (("dy", dy), ("u", u), ("K_s", K_s), ("w", w), ("v", v), ("du", du), ("dk", dk),
+                    ("dw", dw), ("dv", dv)):
+        _dev_tensor(t, name)
+    B, H, N = u.shape
+    _check(_load().fftconv_bwd_short(
+        _ptr(dy), _ptr(u), _ptr(K_s), _ptr(w), _ptr(v), _ptr(du), _ptr(dk), _ptr(dw), _ptr(dv),
+        B, H, N, L_filter, dtype_code(u.dtype), _stream(stream, u.device)))
+
+
 def causal_conv_short(u, k, w=None, v=None, stream=None):
     """Prepare a short filter k (L <= 1024) and run one chunked forward call."""
     H, L = k.shape
@@ -287,6 +302,19 @@ def causal_conv_short(u, k, w=None, v=None, stream=None):
     out = torch.empty_like(u)
     fftconv_fwd_short(u, K_s, w, v, out, L, stream)
     return out
+
+
+def causal_conv_short_bwd(u, k, dy, w=None, v=None, stream=None):
+    """Prepare a short filter k and run one backward call; returns (du, dk, dw, dv)."""
+    H, L = k.shape
+    K_s = torch.empty(fftconv_short_filter_bytes(H, u.dtype), dtype=torch.uint8, device=u.device)
+    fftconv_prepare_short_filter(k, K_s, stream)
+    du = torch.empty_like(u)
+    dk = torch.empty((H, L), dtype=u.dtype, device=u.device)
+    dw = torch.empty_like(u) if w is not None else None
+    dv = torch.empty_like(u) if v is not None else None
+    fftconv_bwd_short(dy, u, K_s, w, v, du, dk, dw, dv, L, stream)
+    return du, dk, dw, dv
 
 
 def fftconv_eqlinear_weight_bytes(T: int, C_out: int, C_in: int, dtype) -> int:

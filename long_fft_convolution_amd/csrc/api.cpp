@@ -1059,6 +1059,73 @@ fftconv_status_t fftconv_fwd_short(const void *u, const void *K_s, const void *w
     return ok();
 }
 
+fftconv_status_t fftconv_bwd_short(const void *dy, const void *u, const void *K_s, const void *w, const void *v,
+                                   void *du, void *dk, void *dw, void *dv, int64_t B, int64_t H, int64_t N,
+                                   int64_t L, fftconv_dtype_t dtype, hipStream_t stream) {
+    g_last_error.clear();
+    if (dtype != FFTCONV_F16 && dtype != FFTCONV_BF16)
+        return fail(FFTCONV_ERR_UNSUPPORTED, "the short-filter path needs fp16 or bf16 storage");
+    if (N < kShortBlock || N % kShortBlock != 0)
+        return fail(FFTCONV_ERR_UNSUPPORTED, "N=%lld must be a positive multiple of %lld", (long long)N,
+                    (long long)kShortBlock);
+    if (B < 0 || H < 0) return fail(FFTCONV_ERR_INVALID_ARGUMENT, "B and H must be >= 0");
+    if (L < 1 || L > kShortBlock)
+        return fail(FFTCONV_ERR_INVALID_ARGUMENT, "L_filter=%lld must be in [1, %lld]", (long long)L,
+                    (long long)(kShortBlock));
+    if (H == 0) return ok();
+    if (dw && !w) return fail(FFTCONV_ERR_INVALID_ARGUMENT, "dw needs the input gate w");
+    if (dv && !v) return fail(FFTCONV_ERR_INVALID_ARGUMENT, "dv needs the output gate v");
+    if (!K_s || (B > 0 && (!dy || !u)))
+        return fail(FFTCONV_ERR_INVALID_ARGUMENT, "dy, u and K_s must be non-null");
+    const void *ptrs[] = {dy, u, K_s, w, v, du, dk, dw, dv};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return fail(FFTCONV_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+    const size_t nbytes = (size_t)B * (size_t)H * (size_t)N * elem_bytes(dtype);
+    const size_t kbytes = (size_t)H * (size_t)L * elem_bytes(dtype);
+    const size_t ksb = fftconv_short_filter_bytes(H, dtype);
+    const void *ins[] = {dy, u, w, v};
+    for (const void *o : {(const void *)du, (const void *)dw, (const void *)dv}) {
+        if (!o) continue;
+        for (const void *i : ins)
+            if (i && overlap(o, nbytes, i, nbytes))
+                return fail(FFTCONV_ERR_INVALID_ARGUMENT, "a gradient overlaps an input");
+        if (overlap(o, nbytes, K_s, ksb)) return fail(FFTCONV_ERR_INVALID_ARGUMENT, "a gradient overlaps K_s");
+    }
+    if (dk) {
+        for (const void *i : ins)
+            if (i && overlap(dk, kbytes, i, nbytes))
+                return fail(FFTCONV_ERR_INVALID_ARGUMENT, "dk overlaps an input");
+        if (overlap(dk, kbytes, K_s, ksb)) return fail(FFTCONV_ERR_INVALID_ARGUMENT, "dk overlaps K_s");
+    }
+    const char *base = static_cast<const char *>(K_s);
+    const float *kscale = reinterpret_cast<const float *>(base + kf_scale_off());
+    const void *kbins = base + kf_bins_off(H);
+    hipError_t e = hipSuccess;
+    if (B > 0) {
+        // dv = dy * conv(u w, k): the windowed forward kernel with dy as the output gate
+        if (dv) {
+            e = launch_pair_conv_win(dtype, u, w, dy, dv, kbins, kscale, B, H, N, stream);
+            if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "dv: %s", hipGetErrorString(e));
+        }
+        // du = w * corr(v dy, k), dw = u * corr(v dy, k): the correlation kernel, both from
+        // one call when both are asked for
+        if (du && dw) {
+            e = launch_pair_conv_win(dtype, dy, v, w, du, kbins, kscale, B, H, N, stream, true, u, dw);
+        } else if (du) {
+            e = launch_pair_conv_win(dtype, dy, v, w, du, kbins, kscale, B, H, N, stream, true);
+        } else if (dw) {
+            e = launch_pair_conv_win(dtype, dy, v, u, dw, kbins, kscale, B, H, N, stream, true);
+        }
+        if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "du, dw: %s", hipGetErrorString(e));
+    }
+    if (dk) {
+        e = B > 0 ? launch_pair_dk(dtype, dy, u, w, v, dk, nullptr, B, H, L, stream, N)
+                  : launch_dk_reduce(dtype, nullptr, dk, 0, H, N, L, stream);   // (no rows: zeros)
+        if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "dk: %s", hipGetErrorString(e));
+    }
+    return ok();
+}
+
 // ---- group-axis circular convolution ----------------------------------------
 static bool eq_group_ok(int64_t T) { return T == 4 || T == 8 || T == 16; }
 

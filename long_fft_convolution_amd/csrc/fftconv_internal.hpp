@@ -253,15 +253,20 @@ hipError_t launch_pair_conv(int logn, int st, const void *u, const void *w, cons
                             void *out2 = nullptr);
 // dk of the backward pass at N = 1024 (fp16 / bf16): dk (H, L) <- sum over b of
 // corr(v dy, u w), the spectrum product masked like K when mask is given (w, v, mask
-// may be null)
+// may be null).  NS > 0: the same over (B, H, NS) sequences of the short-filter path
+// (L <= 1024, NS a multiple of 1024, no mask).
 hipError_t launch_pair_dk(int st, const void *dy, const void *u, const void *w, const void *v, void *dk,
-                          const uint8_t *mask, int64_t B, int64_t H, int64_t L, hipStream_t stream);
+                          const uint8_t *mask, int64_t B, int64_t H, int64_t L, hipStream_t stream,
+                          int64_t NS = 0);
 // Chunked short-filter path: (B, H, NS) sequences, NS a multiple of 1024, as
 // half-overlapping windows of 2048 samples, each a 2048-point circular convolution on
-// the N = 1024 matrix-core kernel (filters of at most 1024 taps).
+// the N = 1024 matrix-core kernel (filters of at most 1024 taps).  corr: the adjoint,
+// out = v * corr(u w, k) with corr(x, k)[t] = sum_s k[s] x[t + s], and with out2 != null
+// a second output out2 = v2 * corr(u w, k) (v and v2 then both non-null).
 hipError_t launch_pair_conv_win(int st, const void *u, const void *w, const void *v, void *out,
                                 const void *kbins, const float *kscale, int64_t B, int64_t H, int64_t NS,
-                                hipStream_t stream);
+                                hipStream_t stream, bool corr = false, const void *v2 = nullptr,
+                                void *out2 = nullptr);
 // Group-axis circular convolution composed with a channel map (eqlinear.hip).
 int eqlinear_span(int T);   // output channels per workgroup (C_out must be a multiple of span / 4)
 hipError_t launch_eqlinear_prepare(int st, int T, const void *W, void *Wf, int64_t Cout, int64_t Cin,

@@ -238,14 +238,23 @@ __device__ __forceinline__ void gate_product<__hip_bfloat16>(const uint4 &uq, co
 // (entries conj w64^{f_s (n_s + 32)} = (-1)^{f_s} conj w64^{f_s n_s}).
 // DUAL: a second output out2 = v2 * conv(u w, k) of the same convolution (the backward
 // pass forms du = w corr(v dy, k) and dw = u corr(v dy, k) in one call).
-template <typename T, bool MASKED, bool HAS_W, bool HAS_V, bool WIN = false, bool DUAL = false>
+// CORR (windows only): the adjoint of the windowed convolution, out[t] = sum_s k[s] x[t + s]
+// (the backward pass's corr(v dy, k) for the short filter).  Output block j needs the
+// input blocks j and j + 1: window j holds the samples j 1024 .. (j + 2) 1024 - 1 (zeros
+// past the sequence end), its 2048-point circular correlation with the filter,
+// IDFT(DFT(window) conj K), has no wrap-around at the outputs 0 .. 1023, so S1' takes the
+// unflipped entries of the N = 1024 path and the filter product the conjugated spectrum.
+// A pair is windows (2 jp, 2 jp + 1) fed by the blocks A = 2 jp, B = 2 jp + 1, C = 2 jp + 2.
+template <typename T, bool MASKED, bool HAS_W, bool HAS_V, bool WIN = false, bool DUAL = false,
+          bool CORR = false>
 __global__ void __launch_bounds__(64 * kPairWaves, MASKED ? 1 : 2)
 pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restrict__ v,
               T *__restrict__ out, const uint4 *__restrict__ kbins, const float *__restrict__ kscale,
               const uint8_t *__restrict__ mask, PairTables tb, int64_t B, int64_t H, int64_t NS,
               const T *__restrict__ v2, T *__restrict__ out2) {
     static_assert(!(WIN && MASKED), "the windowed path has no frequency mask");
-    static_assert(!DUAL || (HAS_V && !WIN), "a second output has an output gate of its own");
+    static_assert(!DUAL || (HAS_V && (!WIN || CORR)), "a second output has an output gate of its own");
+    static_assert(!CORR || WIN, "the correlation mode is a windowed one");
     constexpr int N = 1024;
     __shared__ h8 s_tw1[2 * 4 * 64];     // per (mt, nt, lane): cos[4], sin[4]
     __shared__ h8 s_tw3[4 * 2 * 64];     // per (nt, nt2, lane)
@@ -268,7 +277,7 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
         // windows: S1' produces n_s + 32, i.e. the entries of the odd K slots (odd f_s:
         // element j odd, the upper half of each 32-bit word) change sign
         uint4 a = reinterpret_cast<const uint4 *>(tb.f3r)[i], b = reinterpret_cast<const uint4 *>(tb.f3i)[i];
-        if (WIN) {
+        if (WIN && !CORR) {
             a = make_uint4(a.x ^ 0x80000000u, a.y ^ 0x80000000u, a.z ^ 0x80000000u, a.w ^ 0x80000000u);
             b = make_uint4(b.x ^ 0x80000000u, b.y ^ 0x80000000u, b.z ^ 0x80000000u, b.w ^ 0x80000000u);
         }
@@ -316,8 +325,9 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
 
     // (the host keeps the pair count below 2^31: 32-bit divisions).  oa, ob: where the
     // outputs (and output gates) of sequence / window a and b start; without b, ob == oa.
-    // first: a window pair at the sequence start (its block A lies before it)
-    auto offsets = [&](int64_t p, int64_t &h, int64_t &oa, int64_t &ob, bool &has_b, bool &first) {
+    // edge: a window pair at the sequence start (its block A lies before it), with CORR one
+    // at the sequence end (its block C lies past it)
+    auto offsets = [&](int64_t p, int64_t &h, int64_t &oa, int64_t &ob, bool &has_b, bool &edge) {
         int64_t bp;
         if (WIN) {
             const uint32_t h32 = (uint32_t)p / (uint32_t)PB;
@@ -334,12 +344,12 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
             const uint32_t b32 = (uint32_t)bp / (uint32_t)JP;
             const int64_t b = b32, jp = (uint32_t)bp - b32 * (uint32_t)JP;
             has_b = 2 * jp + 1 < NW;
-            first = jp == 0;
+            edge = CORR ? 2 * jp + 2 >= NW : jp == 0;
             oa = (b * H + h) * NS + 2 * jp * 1024;
             ob = has_b ? oa + 1024 : oa;
         } else {
             has_b = 2 * bp + 1 < B;
-            first = false;
+            edge = false;
             oa = (2 * bp * H + h) * N;
             ob = has_b ? oa + H * N : oa;
         }
@@ -362,6 +372,15 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
             for (int nt = 0; nt < 4; ++nt) fk.k[mt2][nt] = krow[(mt2 * 4 + nt) * 64 + lane];
         // (the four stages' table factors are undone with the channel scale)
         fk.ks = __builtin_ldexpf(kscale[h], 2 * (kPairS1Log2 + kPairS2Log2));
+        if (CORR) {   // conj K: the sign of the imaginary half (elements 4..7) of every chunk
+#pragma unroll
+            for (int mt2 = 0; mt2 < 2; ++mt2)
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) {
+                    fk.k[mt2][nt].z ^= 0x80008000u;
+                    fk.k[mt2][nt].w ^= 0x80008000u;
+                }
+        }
     };
     auto load_gate = [&](const T *gp, int64_t oa, int64_t ob, uint4 (&vg)[4]) {
 #pragma unroll
@@ -376,17 +395,21 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
         if constexpr (WIN) {
             // blocks A = [oa - 1024, oa) (before the sequence start for the first pair: the
             // load re-reads B and its product is zeroed), B = [oa, oa + 1024), C = [oa + 1024, oa + 2048):
-            // without window b, C re-reads B (its results are not stored)
-            const int64_t oA = fst ? oa : oa - 1024, oC = hb ? oa + 1024 : oa;
+            // without window b, C re-reads B (its results are not stored).  CORR: A = [oa, ..),
+            // B = [oa + 1024, ..), C = [oa + 2048, ..); a block past the sequence end re-reads A
+            // and its product is zeroed
+            const int64_t oA = CORR ? oa : (fst ? oa : oa - 1024);
+            const int64_t oB = CORR ? (hb ? oa + 1024 : oa) : oa;
+            const int64_t oC = CORR ? (fst ? oa : oa + 2048) : (hb ? oa + 1024 : oa);
             const int m = 8 * lane;
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
                 raw.q[0][r][0] = *reinterpret_cast<const uint4 *>(u + oA + 512 * r + m);
-                raw.q[1][r][0] = *reinterpret_cast<const uint4 *>(u + oa + 512 * r + m);
+                raw.q[1][r][0] = *reinterpret_cast<const uint4 *>(u + oB + 512 * r + m);
                 raw.q[2][r][0] = *reinterpret_cast<const uint4 *>(u + oC + 512 * r + m);
                 if (HAS_W) {
                     raw.q[0][r][1] = *reinterpret_cast<const uint4 *>(w + oA + 512 * r + m);
-                    raw.q[1][r][1] = *reinterpret_cast<const uint4 *>(w + oa + 512 * r + m);
+                    raw.q[1][r][1] = *reinterpret_cast<const uint4 *>(w + oB + 512 * r + m);
                     raw.q[2][r][1] = *reinterpret_cast<const uint4 *>(w + oC + 512 * r + m);
                 }
             }
@@ -416,8 +439,8 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
     for (; p < p_end; p += stride) {
         int64_t h, oa, ob;
         bool has_b;
-        bool first;
-        offsets(p, h, oa, ob, has_b, first);
+        bool edge;
+        offsets(p, h, oa, ob, has_b, edge);
         const int64_t pn = p + stride < p_end ? p + stride : p;
         uint4 vg[4], vg2[4];
         if (HAS_V) load_gate(v, oa, ob, vg);
@@ -432,7 +455,12 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
             for (int k = 0; k < 3; ++k)
 #pragma unroll
                 for (int r = 0; r < 2; ++r) gate_product<T>(cur.q[k][r][0], cur.q[k][r][1], HAS_W, xb3[k][r]);
-            if (first) xb3[0][0] = xb3[0][1] = h8{};   // zeros before the sequence start
+            if (CORR) {   // zeros past the sequence end
+                if (!has_b) xb3[1][0] = xb3[1][1] = h8{};
+                if (edge) xb3[2][0] = xb3[2][1] = h8{};
+            } else if (edge) {
+                xb3[0][0] = xb3[0][1] = h8{};   // zeros before the sequence start
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {   // window a = (A, B), window b = (B, C)
                 const int m0 = 8 * lane + 512 * r;
@@ -648,19 +676,30 @@ template <> __device__ __forceinline__ __hip_bfloat16 from_f32<__hip_bfloat16>(f
 // With a frequency mask the dropped bins of S are zeroed before the inverse (the mask
 // multiplies the spectrum product as it multiplies K in the forward pass, and it is
 // symmetric in f, so it commutes with taking the Hermitian part).
-template <typename T, bool HAS_W, bool HAS_V, bool MASKED>
+// WIN: dk of the chunked short-filter path on (B, H, NS) sequences, NS a multiple of 1024.
+// Block j of x contributes sum_t g[t + s] x[t] over its 1024 samples t, which involves g
+// at the blocks j and j + 1 only (s < 1024): with x_j zero-padded to 2048 points and the
+// window G_j = (g_j, g_{j+1}) (zeros past the sequence end), that is the circular
+// correlation IDFT(DFT(G_j) conj DFT(x_j)) at s < 1024, without wrap-around.  A pair packs
+// the blocks 2 jp and 2 jp + 1 of one sequence (z_x = x_{2jp} + i x_{2jp+1}, z_g = G_{2jp}
+// + i G_{2jp+1}, read from the g blocks A, B, C = 2 jp .. 2 jp + 2); the g chain's S1
+// contracts both K blocks as in the windowed forward kernel, the rest is unchanged.
+template <typename T, bool HAS_W, bool HAS_V, bool MASKED, bool WIN = false>
 __global__ void __launch_bounds__(64 * kDkWaves, 1)
 pair1k_dk_kernel(const T *__restrict__ dy, const T *__restrict__ u, const T *__restrict__ w,
                  const T *__restrict__ v, T *__restrict__ dk, const uint8_t *__restrict__ mask,
-                 PairTables tb, int64_t B, int64_t H, int64_t L) {
+                 PairTables tb, int64_t B, int64_t H, int64_t L, int64_t NS) {
+    static_assert(!(WIN && MASKED), "the windowed path has no frequency mask");
     constexpr int N = 1024, M = 2048, W = kDkWaves;
+    constexpr int KG = WIN ? 2 : 1, KR = 32 * KG;   // K blocks of the g chain's S1, g plane row
     __shared__ h8 s_tw1[2 * 4 * 64];
     __shared__ h8 s_tw3[4 * 2 * 64];
     __shared__ h8 s_f1[3][4][64];   // re, im, -im: S1 takes no negated data operand
     __shared__ h8 s_f3[2][4][64];
-    // per wave: the input planes of g and x (4 x kPlane fp16), later wave 0's output row;
-    // at a channel's end the whole 64 KB holds four 16 KB slots of the sum over the waves
-    __shared__ __align__(16) _Float16 s_z[W][4 * kPlane];
+    // per wave: the input planes of g and x (2 KG + 2 planes of kPlane fp16), later wave 0's
+    // output row; at a channel's end the first 64 KB hold four 16 KB slots of the sum over
+    // the waves
+    __shared__ __align__(16) _Float16 s_z[W][(2 * KG + 2) * kPlane];
 
     const int tid = threadIdx.x;
     for (int i = tid; i < 512; i += 64 * W) {
@@ -684,32 +723,52 @@ pair1k_dk_kernel(const T *__restrict__ dy, const T *__restrict__ u, const T *__r
         c2r[t] = F2r[t * 64 + lane];
         c2i[t] = F2i[t * 64 + lane];
     }
-    _Float16 *const zgr = s_z[wave], *const zgi = zgr + kPlane, *const zxr = zgi + kPlane, *const zxi = zxr + kPlane;
+    _Float16 *const zgr = s_z[wave], *const zgi = zgr + KG * kPlane, *const zxr = zgi + KG * kPlane,
+                   *const zxi = zxr + kPlane;
     const f4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
     // work items of this wave: channel slot ci, pair slot j -> h = blockIdx.x + ci gridDim.x,
-    // bp = wave + W j; slots past the channel's pairs (bp >= PB) add nothing
-    const int64_t PB = (B + 1) / 2, PPW = (PB + W - 1) / W;
+    // bp = wave + W j; slots past the channel's pairs (bp >= PB) add nothing.  Windows: bp =
+    // b JP + jp (block pairs of one sequence fastest)
+    const int64_t NW = NS / 1024, JP = (NW + 1) / 2;
+    const int64_t PB = WIN ? B * JP : (B + 1) / 2, PPW = (PB + W - 1) / W;
     const int64_t NCH = ((int64_t)H - blockIdx.x + gridDim.x - 1) / gridDim.x;   // channels of this workgroup
     const int64_t NI = NCH * PPW;
-    // raw 16-byte chunks of one pair: [r][dy_a, v_a, dy_b, v_b, u_a, w_a, u_b, w_b]
+    // raw 16-byte chunks of one pair: [r][dy_a, v_a, dy_b, v_b, u_a, w_a, u_b, w_b] (rows a
+    // and b, or the blocks A and B of a window pair), qc[r][dy, v] of block C (windows)
     struct Raw {
         uint4 q[2][8];
+        uint4 qc[2][2];
     };
-    auto locate = [&](int64_t i, int64_t &h, int64_t &bp, int64_t &oa, int64_t &ob, bool &has_b, bool &real) {
+    // oa, ob (oc): where rows a and b (blocks A, B, C) start; a missing row or block re-reads
+    // row a (block A) and its product is zeroed
+    auto locate = [&](int64_t i, int64_t &h, int64_t &bp, int64_t &oa, int64_t &ob, int64_t &oc, bool &has_b,
+                      bool &has_c, bool &real) {
         const int64_t ci = i / PPW, j = i - ci * PPW;
         h = blockIdx.x + ci * (int64_t)gridDim.x;
         bp = wave + W * j;
         real = bp < PB;
         const int64_t bq = real ? bp : PB - 1;   // (a slot without a pair reads the last pair)
-        has_b = 2 * bq + 1 < B;
-        oa = (2 * bq * H + h) * N;
-        ob = has_b ? oa + H * N : oa;
+        if (WIN) {   // (the host keeps B JP below 2^31: 32-bit division)
+            const uint32_t b32 = (uint32_t)bq / (uint32_t)JP;
+            const int64_t b = b32, jp = (uint32_t)bq - b32 * (uint32_t)JP;
+            has_b = 2 * jp + 1 < NW;
+            has_c = 2 * jp + 2 < NW;
+            oa = (b * H + h) * NS + 2 * jp * 1024;
+            ob = has_b ? oa + 1024 : oa;
+            oc = has_c ? oa + 2048 : oa;
+        } else {
+            has_b = 2 * bq + 1 < B;
+            has_c = false;
+            oa = (2 * bq * H + h) * N;
+            ob = has_b ? oa + H * N : oa;
+            oc = oa;
+        }
     };
     auto load_raw = [&](int64_t i, Raw &raw) {
-        int64_t h, bp, oa, ob;
-        bool hb, real;
-        locate(i < NI ? i : NI - 1, h, bp, oa, ob, hb, real);
+        int64_t h, bp, oa, ob, oc;
+        bool hb, hc, real;
+        locate(i < NI ? i : NI - 1, h, bp, oa, ob, oc, hb, hc, real);
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
             const int m0 = 8 * lane + 512 * r;
@@ -717,9 +776,11 @@ pair1k_dk_kernel(const T *__restrict__ dy, const T *__restrict__ u, const T *__r
             raw.q[r][2] = ldnt<uint4>(dy + ob + m0);
             raw.q[r][4] = ldnt<uint4>(u + oa + m0);
             raw.q[r][6] = ldnt<uint4>(u + ob + m0);
+            if (WIN) raw.qc[r][0] = ldnt<uint4>(dy + oc + m0);
             if (HAS_V) {
                 raw.q[r][1] = ldnt<uint4>(v + oa + m0);
                 raw.q[r][3] = ldnt<uint4>(v + ob + m0);
+                if (WIN) raw.qc[r][1] = ldnt<uint4>(v + oc + m0);
             }
             if (HAS_W) {
                 raw.q[r][5] = ldnt<uint4>(w + oa + m0);
@@ -745,10 +806,44 @@ pair1k_dk_kernel(const T *__restrict__ dy, const T *__restrict__ u, const T *__r
           for (int mt2 = 0; mt2 < 2; ++mt2) Sr[nt][mt2] = Si[nt][mt2] = zero4;
       int64_t h = 0;
       for (int64_t j = 0; j < PPW; ++j, ++i) {
-        int64_t bp, oa, ob;
-        bool has_b, real;
-        locate(i, h, bp, oa, ob, has_b, real);
-        if (real) {
+        int64_t bp, oa, ob, oc;
+        bool has_b, has_c, real;
+        locate(i, h, bp, oa, ob, oc, has_b, has_c, real);
+        if (real && WIN) {
+            // ---- windows: x blocks A, B zero-padded (32-slot rows); g windows (A, B) and
+            // (B, C) over both K blocks (64-slot rows)
+            h8 gblk[3][2];
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                gate_product<T>(cur.q[r][0], cur.q[r][1], HAS_V, gblk[0][r]);
+                gate_product<T>(cur.q[r][2], cur.q[r][3], HAS_V, gblk[1][r]);
+                gate_product<T>(cur.qc[r][0], cur.qc[r][1], HAS_V, gblk[2][r]);
+                if (!has_b) gblk[1][r] = h8{};
+                if (!has_c) gblk[2][r] = h8{};
+                const int m0 = 8 * lane + 512 * r;
+                h8 xa, xb;
+                gate_product<T>(cur.q[r][4], cur.q[r][5], HAS_W, xa);
+                gate_product<T>(cur.q[r][6], cur.q[r][7], HAS_W, xb);
+                if (!has_b) xb = h8{};
+                const int ns = m0 >> 5, nf0 = m0 & 31, kss = kslot_of(ns);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    zxr[(nf0 + e) * 32 + kss] = xa[e];
+                    zxi[(nf0 + e) * 32 + kss] = xb[e];
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m0 = 8 * lane + 512 * r;
+                const h8 ga = gblk[r >> 1][r & 1], gb = gblk[1 + (r >> 1)][r & 1];
+                const int ns = m0 >> 5, nf0 = m0 & 31, kss = 32 * (ns >> 5) + kslot_of(ns & 31);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    zgr[(nf0 + e) * KR + kss] = ga[e];
+                    zgi[(nf0 + e) * KR + kss] = gb[e];
+                }
+            }
+        } else if (real) {
             // ---- g = v dy and x = u w of both rows, scattered into the transposed planes
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
@@ -773,12 +868,15 @@ pair1k_dk_kernel(const T *__restrict__ dy, const T *__restrict__ u, const T *__r
             }
         }
         wave_sync();
-        h8 dgr[2], dgi[2], dxr[2], dxi[2];
+        h8 dgr[KG][2], dgi[KG][2], dxr[2], dxi[2];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             const int o = (16 * mt + c) * 32 + 8 * g;
-            dgr[mt] = *reinterpret_cast<const h8 *>(zgr + o);
-            dgi[mt] = *reinterpret_cast<const h8 *>(zgi + o);
+#pragma unroll
+            for (int kb = 0; kb < KG; ++kb) {
+                dgr[kb][mt] = *reinterpret_cast<const h8 *>(zgr + (16 * mt + c) * KR + 32 * kb + 8 * g);
+                dgi[kb][mt] = *reinterpret_cast<const h8 *>(zgi + (16 * mt + c) * KR + 32 * kb + 8 * g);
+            }
             dxr[mt] = *reinterpret_cast<const h8 *>(zxr + o);
             dxi[mt] = *reinterpret_cast<const h8 *>(zxi + o);
         }
@@ -791,18 +889,28 @@ pair1k_dk_kernel(const T *__restrict__ dy, const T *__restrict__ u, const T *__r
             for (int nt = 0; nt < 4; ++nt) {
                 __builtin_amdgcn_sched_barrier(0);   // (one column tile at a time: bounds the live operands)
                 const h8 f1r = s_f1[0][nt][lane], f1i = s_f1[1][nt][lane], nf1i = s_f1[2][nt][lane];
+                // (windows) the second K block's entries: column f_s = 16 nt + c changes sign
+                // for odd c
+                const uint32_t sgn1 = (c & 1) ? 0x80008000u : 0u;
                 f4 zr_[2][2], zi_[2][2];   // [g / x][mt2]: the S2 accumulators of both chains
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
-                    const h8 *dr = q ? dxr : dgr, *di = q ? dxi : dgi;
                     // S1 with twiddle w2048^{nf fs}, then S2 (as in the forward kernel)
                     h4 t1r[2], t1i[2];
 #pragma unroll
                     for (int mt = 0; mt < 2; ++mt) {
-                        f4 ar = mfma(dr[mt], f1r, zero4);
-                        ar = mfma(di[mt], nf1i, ar);
-                        f4 ai = mfma(dr[mt], f1i, zero4);
-                        ai = mfma(di[mt], f1r, ai);
+                        const h8 dr = q ? dxr[mt] : dgr[0][mt], di = q ? dxi[mt] : dgi[0][mt];
+                        f4 ar = mfma(dr, f1r, zero4);
+                        ar = mfma(di, nf1i, ar);
+                        f4 ai = mfma(dr, f1i, zero4);
+                        ai = mfma(di, f1r, ai);
+                        if (WIN && q == 0) {
+                            const h8 dr1 = dgr[KG - 1][mt], di1 = dgi[KG - 1][mt];
+                            ar = mfma(dr1, xor8(f1r, sgn1), ar);
+                            ar = mfma(di1, xor8(nf1i, sgn1), ar);
+                            ai = mfma(dr1, xor8(f1i, sgn1), ai);
+                            ai = mfma(di1, xor8(f1r, sgn1), ai);
+                        }
                         t1r[mt] = to_h4(ar);
                         t1i[mt] = to_h4(ai);
                         cmul4(t1r[mt], t1i[mt], s_tw1[(mt * 4 + nt) * 64 + lane]);
@@ -1011,8 +1119,9 @@ hipError_t launch_pair_conv(int logn, int st, const void *u, const void *w, cons
 
 hipError_t launch_pair_conv_win(int st, const void *u, const void *w, const void *v, void *out,
                                 const void *kbins, const float *kscale, int64_t B, int64_t H, int64_t NS,
-                                hipStream_t stream) {
+                                hipStream_t stream, bool corr, const void *v2, void *out2) {
     if (st == ST_F32 || NS < 1024 || NS % 1024 != 0) return hipErrorInvalidValue;
+    if (out2 != nullptr && (!corr || v == nullptr || v2 == nullptr)) return hipErrorInvalidValue;
     PairTables tb{};
     hipError_t e = get_pair_tables(&tb);
     if (e != hipSuccess) return e;
@@ -1033,11 +1142,25 @@ hipError_t launch_pair_conv_win(int st, const void *u, const void *w, const void
         hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * kPairWaves), 0, stream,
                            (const TT *)u, (const TT *)w, (const TT *)v, (TT *)out,
                            (const uint4 *)kbins, kscale, (const uint8_t *)nullptr, tb, B, H, NS,
-                           (const TT *)nullptr, (TT *)nullptr);
+                           (const TT *)v2, (TT *)out2);
     };
     auto pick = [&](auto *tp) {
         using TT = std::remove_pointer_t<decltype(tp)>;
         const int sel = (w ? 2 : 0) | (v ? 1 : 0);
+        if (corr && out2 != nullptr) {   // two outputs: both output gates present
+            if (w) go(pair1k_kernel<TT, false, true, true, true, true, true>, tp);
+            else go(pair1k_kernel<TT, false, false, true, true, true, true>, tp);
+            return;
+        }
+        if (corr) {
+            switch (sel) {
+            case 0: go(pair1k_kernel<TT, false, false, false, true, false, true>, tp); break;
+            case 1: go(pair1k_kernel<TT, false, false, true, true, false, true>, tp); break;
+            case 2: go(pair1k_kernel<TT, false, true, false, true, false, true>, tp); break;
+            default: go(pair1k_kernel<TT, false, true, true, true, false, true>, tp); break;
+            }
+            return;
+        }
         switch (sel) {
         case 0: go(pair1k_kernel<TT, false, false, false, true>, tp); break;
         case 1: go(pair1k_kernel<TT, false, false, true, true>, tp); break;
@@ -1051,9 +1174,13 @@ hipError_t launch_pair_conv_win(int st, const void *u, const void *w, const void
 }
 
 
+// NS > 0: the windowed dk of the short-filter path on (B, H, NS) sequences (no mask)
 hipError_t launch_pair_dk(int st, const void *dy, const void *u, const void *w, const void *v, void *dk,
-                          const uint8_t *mask, int64_t B, int64_t H, int64_t L, hipStream_t stream) {
+                          const uint8_t *mask, int64_t B, int64_t H, int64_t L, hipStream_t stream,
+                          int64_t NS) {
     if (st == ST_F32) return hipErrorInvalidValue;
+    if (NS != 0 && (NS < 1024 || NS % 1024 != 0 || mask != nullptr)) return hipErrorInvalidValue;
+    if (NS != 0 && B * ((NS / 1024 + 1) / 2) >= (int64_t(1) << 31)) return hipErrorInvalidValue;
     if (B <= 0 || H <= 0) return hipSuccess;
     PairTables tb{};
     hipError_t e = get_pair_tables(&tb);
@@ -1068,11 +1195,20 @@ hipError_t launch_pair_dk(int st, const void *dy, const void *u, const void *w, 
     auto go = [&](auto kern, auto *tp) {
         using TT = std::remove_pointer_t<decltype(tp)>;
         hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * kDkWaves), 0, stream, (const TT *)dy,
-                           (const TT *)u, (const TT *)w, (const TT *)v, (TT *)dk, mask, tb, B, H, L);
+                           (const TT *)u, (const TT *)w, (const TT *)v, (TT *)dk, mask, tb, B, H, L, NS);
     };
     auto pick = [&](auto *tp) {
         using TT = std::remove_pointer_t<decltype(tp)>;
         const int sel = (mask ? 4 : 0) | (w ? 2 : 0) | (v ? 1 : 0);
+        if (NS != 0) {
+            switch (sel) {
+            case 0: go(pair1k_dk_kernel<TT, false, false, false, true>, tp); break;
+            case 1: go(pair1k_dk_kernel<TT, false, true, false, true>, tp); break;
+            case 2: go(pair1k_dk_kernel<TT, true, false, false, true>, tp); break;
+            default: go(pair1k_dk_kernel<TT, true, true, false, true>, tp); break;
+            }
+            return;
+        }
         switch (sel) {
         case 0: go(pair1k_dk_kernel<TT, false, false, false>, tp); break;
         case 1: go(pair1k_dk_kernel<TT, false, true, false>, tp); break;

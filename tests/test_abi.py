@@ -215,6 +215,35 @@ def test_short_filter_abi():
     assert fwd(B=0, u=None, out=None, K=None) == 0
 
 
+def test_short_bwd_validation():
+    lib = fc.lib()
+    F16, F32 = fc.FFTCONV_F16, fc.FFTCONV_F32
+    good = dict(dy=0x10000, u=0x20000, K=0x30000, w=0x40000, v=0x50000, du=0x60000, dk=0x70000,
+                dw=0x80000, dv=0x90000, B=1, H=2, N=2048, L=100, dt=F16)
+
+    def call(**kw):
+        a = dict(good)
+        a.update(kw)
+        return lib.fftconv_bwd_short(a["dy"], a["u"], a["K"], a["w"], a["v"], a["du"], a["dk"], a["dw"],
+                                     a["dv"], a["B"], a["H"], a["N"], a["L"], a["dt"], None)
+
+    assert call(dt=F32) == 2
+    assert call(N=1000) == 2 and "multiple of 1024" in fc.fftconv_last_error()
+    assert call(L=1025) == 1 and "L_filter" in fc.fftconv_last_error()
+    assert call(L=0) == 1
+    assert call(B=-1) == 1
+    assert call(H=0) == 0
+    assert call(w=None) == 1 and "dw needs" in fc.fftconv_last_error()
+    assert call(v=None) == 1 and "dv needs" in fc.fftconv_last_error()
+    assert call(dy=None) == 1
+    assert call(K=None) == 1
+    assert call(du=0x60008) == 1 and "aligned" in fc.fftconv_last_error()
+    assert call(du=0x20000 + 256) == 1 and "overlaps" in fc.fftconv_last_error()
+    assert call(dk=0x30000 + 16) == 1 and "overlaps" in fc.fftconv_last_error()
+    # nothing asked for and no rows: nothing to do
+    assert call(B=0, dy=None, u=None, du=None, dk=None, dw=None, dv=None) == 0
+
+
 def test_eqlinear_abi():
     lib = fc.lib()
     F16, F32 = fc.FFTCONV_F16, fc.FFTCONV_F32
