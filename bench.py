@@ -21,7 +21,8 @@ sources.  The cpu_baseline object times the CPU oracle (route F) on a bounded
 sample of the same workload on this host's cores, and compares the GPU's
 output with it on that sample (relL2, worst sequence, max-abs).
 
-With --pass bwd one step is one fftconv_bwd call (du, dk, dw, dv) instead;
+With --pass bwd one step is one fftconv_bwd call (fftconv_bwd_short for the
+short-filter workload) producing du, dk, dw, dv instead;
 with --pass taps one fftconv_fwd_taps call (the filter transformed from its L
 time-domain taps inside the call).  Those lines name their own metric and carry
 no CPU baseline.
@@ -319,8 +320,8 @@ def main():
         return bench_eqlinear(args)
     if args.which != "fwd":
         wl = synth.WORKLOADS[HEADLINE if args.workload == "all" else args.workload]
-        if wl.short:
-            log("bench: the short-filter path has only the forward call")
+        if wl.short and args.which == "taps":
+            log("bench: the short-filter path takes a prepared filter only (no taps call)")
             return 2
         return bench_other(args, wl, dev)
 
@@ -365,8 +366,12 @@ def bench_other(args, wl, dev):
     w = None if inp.w is None else inp.w.to(dev)
     v = None if inp.v is None else inp.v.to(dev)
     mask = None if inp.mask is None else torch.from_numpy(inp.mask).to(dev)
-    K_f = fc.alloc_filter(wl.H, wl.N, u.dtype, dev)
-    fc.fftconv_prepare_filter(k, wl.N, K_f, fc.alloc_workspace(1, wl.H, wl.N, u.dtype, dev))
+    if wl.short:
+        K_f = torch.empty(fc.fftconv_short_filter_bytes(wl.H, u.dtype), dtype=torch.uint8, device=dev)
+        fc.fftconv_prepare_short_filter(k, K_f)
+    else:
+        K_f = fc.alloc_filter(wl.H, wl.N, u.dtype, dev)
+        fc.fftconv_prepare_filter(k, wl.N, K_f, fc.alloc_workspace(1, wl.H, wl.N, u.dtype, dev))
     torch.cuda.synchronize(dev)
     if args.which == "bwd":
         return bench_bwd(args, wl, dev, u, K_f, w, v, mask)
@@ -443,17 +448,22 @@ def bench_eqlinear(args):
 
 
 def bench_bwd(args, wl, dev, u, K_f, w, v, mask):
-    """One step = one fftconv_bwd call producing du, dk, dw, dv."""
+    """One step = one fftconv_bwd call (fftconv_bwd_short for the short-filter path)
+    producing du, dk, dw, dv."""
     g = torch.Generator().manual_seed(4242)
     dy = torch.randn(u.shape, generator=g, dtype=torch.float32).to(u.dtype).to(dev)
     du = torch.empty_like(u)
     dk = torch.empty((wl.H, wl.L), dtype=u.dtype, device=dev)
     dw = torch.empty_like(u) if w is not None else None
     dv = torch.empty_like(u) if v is not None else None
-    ws = torch.empty(fc.fftconv_bwd_workspace_bytes(wl.B, wl.H, wl.N, u.dtype), dtype=torch.uint8, device=dev)
+    ws = None if wl.short else torch.empty(fc.fftconv_bwd_workspace_bytes(wl.B, wl.H, wl.N, u.dtype),
+                                           dtype=torch.uint8, device=dev)
 
     def step():
-        fc.fftconv_bwd(dy, u, K_f, w, v, du, dk, dw, dv, wl.L, mask, ws)
+        if wl.short:
+            fc.fftconv_bwd_short(dy, u, K_f, w, v, du, dk, dw, dv, wl.L)
+        else:
+            fc.fftconv_bwd(dy, u, K_f, w, v, du, dk, dw, dv, wl.L, mask, ws)
 
     n_warm = warm_up(step, args.warmup, dev)
     log(f"bench: {n_warm} warm-up steps")
@@ -462,8 +472,9 @@ def bench_bwd(args, wl, dev, u, K_f, w, v, mask):
     e = ELEM[wl.dtype]
     # what the backward must move: dy, u (+ w, v) read, du (+ dw, dv) written,
     # dk written, the spectrum read once per channel
-    nact = 2 + (2 if w is not None else 0) + (2 if v is not None else 0)
-    alg = elems * e * nact + wl.H * wl.L * e + wl.H * (wl.N + 1) * (8 if wl.dtype == "f32" else 4)
+    nact = 3 + (2 if w is not None else 0) + (2 if v is not None else 0)
+    spec = wl.H * 2048 * 4 if wl.short else wl.H * (wl.N + 1) * (8 if wl.dtype == "f32" else 4)
+    alg = elems * e * nact + wl.H * wl.L * e + spec
     achieved = alg / (ms_per_step / 1e3) / 1e9
     log(f"bench: bwd {ms_per_step * 1e3:.1f} us/step, {elems / (ms_per_step / 1e3):.3e} elems/s")
     rec = {
@@ -482,7 +493,8 @@ def bench_bwd(args, wl, dev, u, K_f, w, v, mask):
         "data": "synthetic (seeded N(0,1) activations and output gradient, decaying random filter)",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "L_filter": wl.L,
                    "gated": wl.gated, "storage": wl.dtype, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "fftconv_bwd (several launches)", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": ("fftconv_bwd_short" if wl.short else "fftconv_bwd")
+                     + " (several launches)", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": None, "algorithmic_bytes": alg, "kernel_ms": ms_per_step},
         "cpu_baseline": None,

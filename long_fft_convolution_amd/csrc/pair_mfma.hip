@@ -692,6 +692,11 @@ pair1k_dk_kernel(const T *__restrict__ dy, const T *__restrict__ u, const T *__r
     static_assert(!(WIN && MASKED), "the windowed path has no frequency mask");
     constexpr int N = 1024, M = 2048, W = kDkWaves;
     constexpr int KG = WIN ? 2 : 1, KR = 32 * KG;   // K blocks of the g chain's S1, g plane row
+    // With a gate (more prefetched input registers) the S1 operands are re-read from the
+    // planes for every column tile rather than held across the tiles: that removes the
+    // register spills of those variants and was faster (N = 1024 backward 304 -> 294 us,
+    // gated windows 1.92 -> 1.69 ms); without a gate holding them was faster.
+    constexpr bool kTileOps = HAS_W || HAS_V;
     __shared__ h8 s_tw1[2 * 4 * 64];
     __shared__ h8 s_tw3[4 * 2 * 64];
     __shared__ h8 s_f1[3][4][64];   // re, im, -im: S1 takes no negated data operand
@@ -868,18 +873,22 @@ pair1k_dk_kernel(const T *__restrict__ dy, const T *__restrict__ u, const T *__r
             }
         }
         wave_sync();
+        // S1 operands from the planes (kTileOps: re-read for every column tile)
         h8 dgr[KG][2], dgi[KG][2], dxr[2], dxi[2];
+        auto read_ops = [&]() {
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            const int o = (16 * mt + c) * 32 + 8 * g;
+            for (int mt = 0; mt < 2; ++mt) {
+                const int o = (16 * mt + c) * 32 + 8 * g;
 #pragma unroll
-            for (int kb = 0; kb < KG; ++kb) {
-                dgr[kb][mt] = *reinterpret_cast<const h8 *>(zgr + (16 * mt + c) * KR + 32 * kb + 8 * g);
-                dgi[kb][mt] = *reinterpret_cast<const h8 *>(zgi + (16 * mt + c) * KR + 32 * kb + 8 * g);
+                for (int kb = 0; kb < KG; ++kb) {
+                    dgr[kb][mt] = *reinterpret_cast<const h8 *>(zgr + (16 * mt + c) * KR + 32 * kb + 8 * g);
+                    dgi[kb][mt] = *reinterpret_cast<const h8 *>(zgi + (16 * mt + c) * KR + 32 * kb + 8 * g);
+                }
+                dxr[mt] = *reinterpret_cast<const h8 *>(zxr + o);
+                dxi[mt] = *reinterpret_cast<const h8 *>(zxi + o);
             }
-            dxr[mt] = *reinterpret_cast<const h8 *>(zxr + o);
-            dxi[mt] = *reinterpret_cast<const h8 *>(zxi + o);
-        }
+        };
+        if (!kTileOps) read_ops();
         wave_sync();
         __builtin_amdgcn_sched_barrier(0);
         load_raw(i + 1, cur);   // the next item (clamped: issued on every path)
@@ -888,6 +897,7 @@ pair1k_dk_kernel(const T *__restrict__ dy, const T *__restrict__ u, const T *__r
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
                 __builtin_amdgcn_sched_barrier(0);   // (one column tile at a time: bounds the live operands)
+                if (kTileOps) read_ops();
                 const h8 f1r = s_f1[0][nt][lane], f1i = s_f1[1][nt][lane], nf1i = s_f1[2][nt][lane];
                 // (windows) the second K block's entries: column f_s = 16 nt + c changes sign
                 // for odd c
@@ -935,6 +945,7 @@ pair1k_dk_kernel(const T *__restrict__ dy, const T *__restrict__ u, const T *__r
                 }
             }
         }
+        if (kTileOps) wave_sync();   // (the operand reads above before the next item's scatter)
       }
 
         // ---- end of the channel: pairwise sum over the waves (8 -> 4 -> 2 -> 1) through
