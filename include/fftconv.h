@@ -186,7 +186,9 @@ fftconv_status_t fftconv_fwd_taps(const void *u, const void *k, const void *w, c
  * N or dtype).  It holds the conjugated spectrum, u*w, the spectra of the
  * B*H sequences u*w, their correlations with v*dy, and the forward
  * workspace; at N = 1024 with fp16 or bf16 storage only the conjugated
- * spectrum (dk is accumulated on chip there). */
+ * spectrum (dk is accumulated on chip there); at N = 2048 .. 16384 with fp16
+ * or bf16 storage the conjugated spectrum, the spectra of the batch-row pairs
+ * of u*w with their scales, and one correlation row per pair and channel. */
 size_t fftconv_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, fftconv_dtype_t dtype);
 
 /* Backward pass of fftconv_fwd: the gradients of sum(dy * out) (the

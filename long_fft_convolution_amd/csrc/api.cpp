@@ -781,8 +781,9 @@ fftconv_status_t fftconv_fwd_noalloc(const void *u, const void *K_f, const void 
 // x = u w; the spectra of the sequences x as filters of their own channel;
 // the per-sequence correlations; the repeated mask rows; the forward
 // workspace (the same size serves the B*H-channel prepare and forward).
-// N = 16384 (fp16 / bf16) instead: the batch-row pairs' spectra of u w and
-// their scales, and the per-pair correlations.
+// N = 2048 .. 16384 (fp16 / bf16) instead: the batch-row pairs' spectra of u w
+// and their scales (per group of channels sharing a workgroup), and the per-pair
+// correlations.
 struct BwdLayout {
     size_t kc, x, kx, part, mrep, fws, spec, pscale, total;
 };
@@ -799,12 +800,16 @@ static BwdLayout bwd_layout(int64_t B, int64_t H, int64_t N, fftconv_dtype_t dty
     o.kc = take(fftconv_filter_bytes(H, N, dtype));
     // N = 1024 (fp16 / bf16): du, dw and dk come from kernels that need no scratch beyond
     // the conjugated spectrum (the dk chain's areas below are then empty)
-    const bool p16 = log2_exact(N) == 14 && use_pair3_kernel(14, dtype);
-    const bool chain = !use_pair_kernel(log2_exact(N), dtype) && !p16;
-    const int64_t P = H * ((B + 1) / 2);
-    o.spec = take(p16 ? (size_t)P * kP16SpecBytes : 0);
-    o.pscale = take(p16 ? (size_t)P * sizeof(float) : 0);
-    o.part = take(p16 ? (size_t)P * (size_t)N * elem_bytes(dtype) : 0);
+    // N = 2048 .. 16384 (fp16 / bf16): per-group spectra of the batch-row pairs of u*w
+    // (a group is the 2^(14 - log2 N) channels of one workgroup) and one partial row per pair
+    const int l = log2_exact(N);
+    const bool p16 = use_pair3_kernel(l, dtype);
+    const bool chain = !use_pair_kernel(l, dtype) && !p16;
+    const int64_t PB = (B + 1) / 2, Pch = p16 ? (int64_t)1 << (14 - l) : 1;
+    const int64_t groups = (H + Pch - 1) / Pch * PB;
+    o.spec = take(p16 ? (size_t)groups * kP16SpecBytes : 0);
+    o.pscale = take(p16 ? (size_t)(groups * Pch) * sizeof(float) : 0);   // one per pair of rows
+    o.part = take(p16 ? (size_t)(PB * H) * (size_t)N * elem_bytes(dtype) : 0);
     o.x = take(chain ? (size_t)S * (size_t)N * elem_bytes(dtype) : 0);
     o.kx = take(chain && S > 0 ? fftconv_filter_bytes(S, N, dtype) : 0);
     if (chain) o.part = take((size_t)S * (size_t)N * elem_bytes(dtype));
@@ -912,9 +917,9 @@ fftconv_status_t fftconv_bwd(const void *dy, const void *u, const void *K_f, con
     if (dk && B > 0 && use_pair_kernel(l, dtype)) {
         hipError_t e = launch_pair_dk(dtype, dy, u, w, v, dk, mask, B, H, L, stream);
         if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "dk: %s", hipGetErrorString(e));
-    } else if (dk && B > 0 && l == 14 && use_pair3_kernel(l, dtype)) {
-        // N = 16384 (fp16 / bf16): the pairs' spectra of u w, then one correlation per pair
-        hipError_t e = launch_pair16k_dk(dtype, dy, u, w, v, ws + lay.part, ws + lay.spec,
+    } else if (dk && B > 0 && use_pair3_kernel(l, dtype)) {
+        // N = 2048 .. 16384 (fp16 / bf16): the pairs' spectra of u w, then one correlation per pair
+        hipError_t e = launch_pair16k_dk(l, dtype, dy, u, w, v, ws + lay.part, ws + lay.spec,
                                          reinterpret_cast<float *>(ws + lay.pscale), mask, B, H, stream);
         if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "dk pairs: %s", hipGetErrorString(e));
         e = launch_dk_reduce(dtype, ws + lay.part, dk, (B + 1) / 2, H, N, L, stream);

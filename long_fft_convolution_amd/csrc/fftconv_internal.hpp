@@ -240,10 +240,12 @@ hipError_t launch_pair16k_conv(int logn, int st, const void *u, const void *w, c
                                const void *kbins, const float *kscale, const uint8_t *mask,
                                int64_t B, int64_t H, hipStream_t stream, const void *v2 = nullptr,
                                void *out2 = nullptr);
-// the backward pass's filter-gradient partials at N = 16384 (two launches of the same kernel);
-// spec holds kP16SpecBytes per pair of batch rows
+// the backward pass's filter-gradient partials at N = 2^logn = 2048 .. 16384 (two launches of
+// the same kernel): part (ceil(B/2) H, N) rows bp H + h; spec holds kP16SpecBytes per
+// workgroup group (ceil(H / P) ceil(B/2) groups, P = 2^(14 - logn) channels) and pscale
+// P floats per group (one per pair of batch rows and channel)
 constexpr size_t kP16SpecBytes = (size_t)32 * 2 * 2 * 64 * 16;
-hipError_t launch_pair16k_dk(int st, const void *dy, const void *u, const void *w, const void *v,
+hipError_t launch_pair16k_dk(int logn, int st, const void *dy, const void *u, const void *w, const void *v,
                              void *part, void *spec, float *pscale, const uint8_t *mask, int64_t B,
                              int64_t H, hipStream_t stream);
 // with out2: also out2 = v2 * conv(u w, k) from the same transforms (v and v2 non-null)

@@ -140,8 +140,9 @@ using namespace p16;
 // DUAL: a second output out2 = v2 * conv(u w, k) from the same transforms (the backward
 // pass forms du and dw in one call); the second gate's rows are loaded once the staged
 // outputs have freed their registers.
-// MODE (kConv, kSpec, kCorr) above.  kSpec writes spec_out[p] and scale_out[p] for pair p;
-// kCorr reads them through kbins and kscale and writes row bp H + h of out.
+// MODE (kConv, kSpec, kCorr) above.  kSpec writes spec_out[p] and scale_out[p] for pair
+// (group) p, all 32 rows of the workgroup; kCorr reads them through kbins and kscale and
+// writes the rows bp H + h (h: the group's channels) of out.
 // LOGR < 5 (N = 512 R = 2048, 4096, 8192): the 2N-point transform is R = 2^LOGR outer
 // rows of 1024; P = 32 / R pairs of P consecutive channels (the same batch rows) share a
 // workgroup's 32 rows (sub-pair p = row / R, f_c = row mod R), so phase 2 is unchanged.
@@ -158,7 +159,6 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
     static_assert(!DUAL || HAS_V, "a second output has an output gate of its own");
     static_assert(MODE == kConv || (!DUAL && !HAS_V), "the spectrum and correlation modes have no output gate");
     static_assert(MODE != kSpec || !MASKED, "the spectrum mode stores every bin");
-    static_assert(MODE == kConv || LOGR == 5, "the spectrum and correlation modes are N = 16384 only");
     static_assert(LOGR >= 2 && LOGR <= 5, "R = 4 .. 32");
     constexpr bool SPEC = MODE == kSpec, CORR = MODE == kCorr;
     constexpr int R = 1 << LOGR, P = 32 / R, NCH = R / 2;   // outer rows, sub-pairs, non-zero n_c
@@ -173,6 +173,8 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
     uint8_t *s_mask = reinterpret_cast<uint8_t *>(s_tw3 + 4 * 64);   // mask rows of the P channels
     // R < 32: the outer DFT tiles, [phase-1 re t0, t1, im t0, t1, phase-3 re, im][lane]
     h8 *s_out = reinterpret_cast<h8 *>(s_mask + 8 * kMaskBlocks);
+    // kSpec / kCorr: per wave and slot n_c of phase 1, the sum of |input| [wave][32]
+    float *const s_part = reinterpret_cast<float *>(s_out + 6 * 64);
 
     const int tid = threadIdx.x;
     for (int i = tid; i < 256; i += 64 * kWaves) {
@@ -254,8 +256,9 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
         const int64_t r = H - hh * P;
         return (int)(r < P ? r : P);
     };
-    // kSpec: sum of |x| over the pair's transformed values (this lane's share)
-    float l1 = 0.f;
+    // kSpec / kCorr: sum of |x| over the pair's transformed values (this lane's share, per
+    // slot n_c = 4 g + j)
+    float l1j[4] = {0.f, 0.f, 0.f, 0.f};
     auto load_batch = [&](int64_t oa_, int64_t ob_, int half, Batch &x, int nv_) {
         const uint32_t *pua = reinterpret_cast<const uint32_t *>(u + oa_);
         const uint32_t *pub = reinterpret_cast<const uint32_t *>(u + ob_);
@@ -314,7 +317,7 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                     bi[j] = hb_ ? (_Float16)xb : (_Float16)0.f;
                     br[4 + j] = (_Float16)0.f;
                     bi[4 + j] = (_Float16)0.f;
-                    if (SPEC) l1 += fabsf((float)br[j]) + fabsf((float)bi[j]);
+                    if (SPEC || CORR) l1j[j] += fabsf((float)br[j]) + fabsf((float)bi[j]);
                 }
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
@@ -368,8 +371,8 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
     for (; p < p_end; p += wg_on_xcd) {
         const int64_t h = __builtin_amdgcn_readfirstlane((uint32_t)p / (uint32_t)PB);   // channel group
         // (the six stages' table factors are undone with the channel scale; kCorr: the pair's)
-        const float ks = SPEC ? 1.f : __builtin_ldexpf(kscale[CORR ? p : h], 6 * kDft32Log2);
-        const int64_t oo = CORR ? ((p - h * PB) * H + h) * N : 0;   // kCorr output row
+        const float ks = (SPEC || CORR) ? 1.f : __builtin_ldexpf(kscale[h], 6 * kDft32Log2);
+        const int64_t oo = CORR ? ((p - h * PB) * H + h * P) * N : 0;   // kCorr output row
         int64_t p_nx = p + wg_on_xcd, oa_nx, ob_nx;
         bool hb_nx;
         pair_base(p_nx < p_end ? p_nx : p, oa_nx, ob_nx, hb_nx);
@@ -391,29 +394,58 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
             phase1_batch(x0, tw0, 0, has_b);
             phase1_batch(x1, tw1, 1, has_b);
         }
-        float *const s_part = reinterpret_cast<float *>(s_mask);   // kSpec: per-wave sums of |x|
-        if (SPEC) {
+        if (SPEC || CORR) {   // per slot: the sum over the 16 lanes of one g, then per wave
 #pragma unroll
-            for (int o = 32; o > 0; o >>= 1) l1 += __shfl_xor(l1, o);
-            if (lane == 0) s_part[wave] = l1;
-            l1 = 0.f;
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                for (int o = 8; o > 0; o >>= 1) l1j[j] += __shfl_xor(l1j[j], o);
+            }
+            if (c == 0) *reinterpret_cast<f4 *>(s_part + 32 * wave + 4 * g) = f4{l1j[0], l1j[1], l1j[2], l1j[3]};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) l1j[j] = 0.f;
         }
         __syncthreads();
-        // kSpec: |Z[f]| <= sum |z| bounds every bin, so the stored spectrum, scaled by the
-        // power of two 2^e <= 64 / sum |z|, stays within |.| <= 1 after the three stages'
-        // 2^-6; the pair's scale is 1 / (2^(e - 6) 2N), the filter scale of that spectrum
-        float sc = 1.f;
-        if (SPEC) {
-            float tot = 0.f;
+        // kSpec / kCorr: |Z[f]| <= sum |z| bounds every bin of a sub-pair's transform, so a
+        // spectrum taken after the three forward stages (table factors 2^-kF) and scaled by
+        // the power of two 2^e <= 2^(kF + kSpecLog2) / sum |z| stays within |.| <= 2^kSpecLog2
+        // (kSpec: the stored spectrum of x; kCorr: the spectrum of g before the product, so
+        // that neither is far below fp16's normal range).  Each sub-pair (P > 1: its slots
+        // n_c in [sp NCH, sp NCH + NCH)) has its own scale.  kSpec stores the filter scale of
+        // that spectrum, 1 / (2^(e - kF) 2N), per sub-pair; kCorr undoes its 2^e in the output
+        constexpr int kF = R == 32 ? 3 * kDft32Log2 : 2 * kDft32Log2 + p16_outer_log2(LOGR);
+        constexpr int kSpecLog2 = 6;
+        // lane l < 16 sums slot l over the waves, then over its sub-pair's NCH slots; every
+        // lane then holds the exponent of the sub-pair of slot l (16 slots: n_c < NCH for
+        // each of the P sub-pairs)
+        int e_l = 0;
+        if (SPEC || CORR) {
+            float t = 0.f;
+            if (lane < 16) {
 #pragma unroll
-            for (int j = 0; j < kWaves; ++j) tot += s_part[j];
-            int e = 0;
-            if (tot > 0.f && isfinite(tot)) {
-                e = (int)floorf(log2f(64.f / tot));
-                e = e < -60 ? -60 : (e > 60 ? 60 : e);
+                for (int w8 = 0; w8 < kWaves; ++w8) t += s_part[32 * w8 + lane];
             }
-            sc = __builtin_ldexpf(1.f, e);
-            if (tid == 0) scale_out[p] = __builtin_ldexpf(1.f, 6 - e - 15);
+#pragma unroll
+            for (int o = 1; o < NCH; o <<= 1) t += __shfl_xor(t, o);
+            if (t > 0.f && isfinite(t)) {
+                e_l = (int)floorf(log2f(__builtin_ldexpf(1.f, kF + kSpecLog2) / t));
+                e_l = e_l < -60 ? -60 : (e_l > 60 ? 60 : e_l);
+            }
+        }
+        auto sp_exp = [&](int sp) -> int {
+            if constexpr (R == 32) return __builtin_amdgcn_readfirstlane(e_l);
+            return __shfl(e_l, sp * NCH);
+        };
+        float sc[kRowsPerWave];   // per phase-2 row rho = wave + 8 r: its sub-pair's 2^e
+#pragma unroll
+        for (int r = 0; r < kRowsPerWave; ++r) sc[r] = 1.f;
+        if (SPEC || CORR) {
+#pragma unroll
+            for (int r = 0; r < kRowsPerWave; ++r)
+                sc[r] = __builtin_ldexpf(1.f, sp_exp(R == 32 ? 0 : (wave + kWaves * r) >> LOGR));
+        }
+        if (SPEC) {
+            const int e_mine = sp_exp(lane < P ? lane : 0);   // (all lanes: a shuffle)
+            if (tid < P) scale_out[p * P + tid] = __builtin_ldexpf(1.f, kF - e_mine - (10 + LOGR));
         }
 
         // ---- phase 2a: this wave's rows f_c = wave + kWaves r into registers (S1 operands);
@@ -429,19 +461,23 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
             }
         }
         // filter rows: row rho = wave + 8 r is f_c = rho mod R of sub-pair rho / R
+        // (kCorr: the group's own spectrum, every row rho stored)
         auto kchan = [&](int rho) -> const uint4 * {
-            if constexpr (R == 32) return kbins + (CORR ? p * (int64_t)kSpecRows : h * (int64_t)kKRows);
+            if constexpr (CORR) return kbins + p * (int64_t)kSpecRows;
+            if constexpr (R == 32) return kbins + h * (int64_t)kKRows;
             return kbins + chan(h, rho >> LOGR) * (int64_t)kKRows;
         };
         // f_c of row rho (rho < 32)
         auto rowfc = [&](int rho) -> int { return R == 32 ? rho : (rho & (R - 1)); };
+        // the filter row read for row rho (kCorr: rho itself)
+        auto krow = [&](int rho) -> int { return CORR ? rho : rowfc(rho); };
         uint4 kq[2][2];
         if (!SPEC) {
 #pragma unroll
             for (int mt2 = 0; mt2 < 2; ++mt2)
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt)
-                    kq[mt2][nt] = k_load<CORR, LOGR>(kchan(wave), rowfc(wave), mt2, nt, ul);
+                    kq[mt2][nt] = k_load<CORR, LOGR>(kchan(wave), krow(wave), mt2, nt, ul);
         }
         __syncthreads();
 
@@ -466,7 +502,7 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                     for (int mt2 = 0; mt2 < 2; ++mt2)
 #pragma unroll
                         for (int nt = 0; nt < 2; ++nt)
-                            kq[mt2][nt] = k_load<CORR, LOGR>(kchan(fc + kWaves), rowfc(fc + kWaves), mt2, nt, lx);
+                            kq[mt2][nt] = k_load<CORR, LOGR>(kchan(fc + kWaves), krow(fc + kWaves), mt2, nt, lx);
                 }
 #pragma unroll
                 for (int nt3 = 0; nt3 < 2; ++nt3)
@@ -509,9 +545,13 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                     f4 cr, ci;
                     cm_constA(Fr[mt2], Fi[mt2], nFi[mt2], br, bi, cr, ci);   // rows f_a, cols f_b
                     if (SPEC) {   // conj(Z) 2^e in the order the product step reads it
-                        const h8 q = cat8(to_h4(cr * sc), to_h4(ci * -sc));
+                        const h8 q = cat8(to_h4(cr * sc[r]), to_h4(ci * -sc[r]));
                         stu(spec_out + p * (int64_t)kSpecRows + ((fc * 2 + mt2) * 2 + nt) * 64, 16u * lx, q);
                         continue;
+                    }
+                    if (CORR) {   // the spectrum of g scaled by its sub-pair's 2^e
+                        cr *= sc[r];
+                        ci *= sc[r];
                     }
                     yr[mt2][nt] = to_h4(cr);
                     yi[mt2][nt] = to_h4(ci);
@@ -587,8 +627,13 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
         // R < 32: the block-diagonal inverse DFT-R tile, and column c = (sub-pair, n_c)
         // takes its channel's scale
         float ksl = ks;
-        if constexpr (R < 32)
-            ksl = __builtin_ldexpf(kscale[chan(h, c / NCH)], 4 * kDft32Log2 + 2 * p16_outer_log2(LOGR));
+        constexpr int kBack = R == 32 ? 6 * kDft32Log2 : 4 * kDft32Log2 + 2 * p16_outer_log2(LOGR);
+        if constexpr (CORR) {   // column c: sub-pair c / NCH, its stored scale and its 2^-e
+            const int spc = R == 32 ? 0 : c / NCH;
+            ksl = __builtin_ldexpf(kscale[p * P + spc], kBack - sp_exp(spc));
+        } else if constexpr (R < 32) {
+            ksl = __builtin_ldexpf(kscale[chan(h, c / NCH)], kBack);
+        }
 #pragma unroll
         for (int tt = 0; tt < kTilesPerWave; ++tt) {
             // r2(8 g, 16 T + c)
@@ -689,9 +734,10 @@ static hipError_t p16_grid(int64_t B, int64_t H, int64_t *blocks, int logr = 5) 
 }
 
 // LDS: the two planes, the inner twiddle tables, the mask rows of up to 8 channels, the
-// outer DFT tiles of R < 32 (six planes of 64 lanes x 16 bytes)
+// outer DFT tiles of R < 32 (six planes of 64 lanes x 16 bytes), the per-wave input sums of
+// the spectrum and correlation modes
 static constexpr size_t kP16Lds =
-    (size_t)2 * kR1Plane * sizeof(_Float16) + 2 * 256 * 16 + 8 * kMaskBlocks + 6 * 64 * 16;
+    (size_t)2 * kR1Plane * sizeof(_Float16) + 2 * 256 * 16 + 8 * kMaskBlocks + 6 * 64 * 16 + 8 * 32 * 4;
 static_assert(kP16Lds <= 160 * 1024, "LDS of one workgroup");
 
 static P16Outer p16_outer(const Pair3Tables &tb, int logr) {
@@ -765,15 +811,16 @@ hipError_t launch_pair16k_conv(int logn, int st_, const void *u, const void *w, 
 // (2 bp, 2 bp + 1) of channel h, part[bp H + h] = corr(dy v, u w) summed over the two rows.
 // spec (ceil(B/2) H * 128 KiB) and pscale (ceil(B/2) H floats) hold the pairs' conjugated
 // spectra of u w between the two launches.
-hipError_t launch_pair16k_dk(int st_, const void *dy, const void *u, const void *w, const void *v,
-                             void *part, void *spec, float *pscale, const uint8_t *mask, int64_t B,
-                             int64_t H, hipStream_t stream) {
+template <int LOGR>
+static hipError_t pair16k_dk_r(int st_, const void *dy, const void *u, const void *w, const void *v, void *part,
+                               void *spec, float *pscale, const uint8_t *mask, int64_t B, int64_t H,
+                               hipStream_t stream) {
     Pair3Tables tb{};
     hipError_t e = get_pair3_tables(&tb);
     if (e != hipSuccess) return e;
     int64_t blocks = 0;
-    if ((e = p16_grid(B, H, &blocks)) != hipSuccess) return e;
-    const P16Outer ot = p16_outer(tb, 5);
+    if ((e = p16_grid(B, H, &blocks, LOGR)) != hipSuccess) return e;
+    const P16Outer ot = p16_outer(tb, LOGR);
     auto go = [&](auto kern, auto *tp, const void *in, const void *gate, void *o, const void *kb,
                   const float *ksc, const uint8_t *m) -> hipError_t {
         using TT = std::remove_pointer_t<decltype(tp)>;
@@ -787,20 +834,41 @@ hipError_t launch_pair16k_dk(int st_, const void *dy, const void *u, const void 
     };
     auto pick = [&](auto *tp) -> hipError_t {
         using TT = std::remove_pointer_t<decltype(tp)>;
-        hipError_t err = w ? go(pair16k_kernel<TT, false, true, false, false, kSpec>, tp, u, w, nullptr, nullptr,
-                                nullptr, nullptr)
-                           : go(pair16k_kernel<TT, false, false, false, false, kSpec>, tp, u, nullptr, nullptr,
-                                nullptr, nullptr, nullptr);
+        hipError_t err = w ? go(pair16k_kernel<TT, false, true, false, false, kSpec, LOGR>, tp, u, w, nullptr,
+                                nullptr, nullptr, nullptr)
+                           : go(pair16k_kernel<TT, false, false, false, false, kSpec, LOGR>, tp, u, nullptr,
+                                nullptr, nullptr, nullptr, nullptr);
         if (err != hipSuccess) return err;
         switch ((mask ? 2 : 0) | (v ? 1 : 0)) {
-        case 0: return go(pair16k_kernel<TT, false, false, false, false, kCorr>, tp, dy, nullptr, part, spec, pscale, mask);
-        case 1: return go(pair16k_kernel<TT, false, true, false, false, kCorr>, tp, dy, v, part, spec, pscale, mask);
-        case 2: return go(pair16k_kernel<TT, true, false, false, false, kCorr>, tp, dy, nullptr, part, spec, pscale, mask);
-        default: return go(pair16k_kernel<TT, true, true, false, false, kCorr>, tp, dy, v, part, spec, pscale, mask);
+        case 0:
+            return go(pair16k_kernel<TT, false, false, false, false, kCorr, LOGR>, tp, dy, nullptr, part, spec,
+                      pscale, mask);
+        case 1:
+            return go(pair16k_kernel<TT, false, true, false, false, kCorr, LOGR>, tp, dy, v, part, spec, pscale,
+                      mask);
+        case 2:
+            return go(pair16k_kernel<TT, true, false, false, false, kCorr, LOGR>, tp, dy, nullptr, part, spec,
+                      pscale, mask);
+        default:
+            return go(pair16k_kernel<TT, true, true, false, false, kCorr, LOGR>, tp, dy, v, part, spec, pscale,
+                      mask);
         }
     };
     if (st_ == ST_F16) return pick((__half *)nullptr);
     return pick((__hip_bfloat16 *)nullptr);
+}
+
+hipError_t launch_pair16k_dk(int logn, int st_, const void *dy, const void *u, const void *w, const void *v,
+                             void *part, void *spec, float *pscale, const uint8_t *mask, int64_t B,
+                             int64_t H, hipStream_t stream) {
+    if (st_ == ST_F32) return hipErrorInvalidValue;
+    switch (logn) {
+    case 11: return pair16k_dk_r<2>(st_, dy, u, w, v, part, spec, pscale, mask, B, H, stream);
+    case 12: return pair16k_dk_r<3>(st_, dy, u, w, v, part, spec, pscale, mask, B, H, stream);
+    case 13: return pair16k_dk_r<4>(st_, dy, u, w, v, part, spec, pscale, mask, B, H, stream);
+    case 14: return pair16k_dk_r<5>(st_, dy, u, w, v, part, spec, pscale, mask, B, H, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace fftconv

@@ -127,7 +127,7 @@ def test_prepare_validation():
 
 def test_bwd_workspace_bytes():
     F16, BF16, F32 = fc.FFTCONV_F16, fc.FFTCONV_BF16, fc.FFTCONV_F32
-    # conjugated K_f + u*w + the B*H sequence spectra + correlations + mask rows
+    # fp32: conjugated K_f + u*w + the B*H sequence spectra + correlations + mask rows
     # + the forward workspace, each region rounded up to 256 bytes
     B, H, N = 2, 3, 2048
 
@@ -135,9 +135,19 @@ def test_bwd_workspace_bytes():
         return (x + 255) // 256 * 256
 
     S = B * H
-    want = (up(fc.fftconv_filter_bytes(H, N, F16)) + up(S * N * 2) + up(fc.fftconv_filter_bytes(S, N, F16))
-            + up(S * N * 2) + up(S * 128) + up(fc.fftconv_workspace_bytes(1, S, N, F16)))
-    assert fc.fftconv_bwd_workspace_bytes(B, H, N, F16) == want
+    want = (up(fc.fftconv_filter_bytes(H, N, F32)) + up(S * N * 4) + up(fc.fftconv_filter_bytes(S, N, F32))
+            + up(S * N * 4) + up(S * 128) + up(fc.fftconv_workspace_bytes(1, S, N, F32)))
+    assert fc.fftconv_bwd_workspace_bytes(B, H, N, F32) == want
+    # N = 2048 .. 8192 in fp16 / bf16: the conjugated K_f, then per group (the 2^(14 - log2 N)
+    # channels of one workgroup, of one pair of batch rows) a 32-row spectrum and one scale
+    # per channel, and one correlation row per pair of batch rows and channel
+    for Nq, Pch in ((2048, 8), (4096, 4), (8192, 2)):
+        for Bq, Hq in ((1, 3), (3, 9), (4, 16)):
+            PB = (Bq + 1) // 2
+            G = (Hq + Pch - 1) // Pch * PB
+            want = (up(fc.fftconv_filter_bytes(Hq, Nq, F16)) + up(G * 32 * 1024 * 4) + up(G * Pch * 4)
+                    + up(PB * Hq * Nq * 2))
+            assert fc.fftconv_bwd_workspace_bytes(Bq, Hq, Nq, F16) == want, (Nq, Bq, Hq)
     # N = 1024 in fp16 / bf16: only the conjugated K_f (the gradients come from kernels
     # that need no other scratch); fp32 keeps the whole layout
     for dt in (F16, BF16):

@@ -195,6 +195,65 @@ def test_bwd_n16384_range(dtype, loc, dscale):
     _check(got, want, TOL[dtype])
 
 
+@pytest.mark.parametrize("N,H", [(2048, 3), (2048, 17), (4096, 5), (8192, 3)])
+@pytest.mark.parametrize("gates", ["both", "none", "w", "v"])
+def test_bwd_r_rows_groups(N, H, gates):
+    # N = 2048 .. 8192 (fp16 / bf16): dk from the per-group spectra of u w (a workgroup
+    # holds 2^(14 - log2 N) channels: 8, 4, 2) and one correlation per group; H not a
+    # multiple of the group (a partial last group), an odd batch (a lone last row)
+    B, L = 3, N - 100
+    dtype = "bf16" if N == 4096 else "f16"
+    _say(f"bwd N={N} B={B} H={H} gates={gates} {dtype}")
+    inp, dy = _case(B, H, N, L, dtype, gates, seed=N + H)
+    got = _run(inp, dy)
+    want = oracle.fft_bwd(inp.f64("u"), inp.f64("k"), dy.double().numpy(), inp.f64("w"), inp.f64("v"))
+    _check(got, want, TOL[dtype])
+
+
+@pytest.mark.parametrize("N", [2048, 4096, 8192])
+@pytest.mark.parametrize("B", [1, 4])
+def test_bwd_r_rows_batches(N, B):
+    # one lone row (B = 1) and two pairs summed by the reduction (B = 4), more channels
+    # than one group
+    H = 6
+    _say(f"bwd N={N} B={B} H={H}")
+    inp, dy = _case(B, H, N, N, "f16", "both", seed=7 * N + B)
+    got = _run(inp, dy)
+    want = oracle.fft_bwd(inp.f64("u"), inp.f64("k"), dy.double().numpy(), inp.f64("w"), inp.f64("v"))
+    _check(got, want, TOL["f16"])
+
+
+@pytest.mark.parametrize("N", [2048, 8192])
+@pytest.mark.parametrize("kind", ["band", "random"])
+def test_bwd_r_rows_mask(N, kind):
+    # the correlation mode under a frequency mask (each channel of a group its own mask row)
+    B, H = 2, 5
+    _say(f"bwd mask {kind} N={N}")
+    inp, dy = _case(B, H, N, N, "bf16", "both", seed=N + 3)
+    mask = synth.band_mask(H, 27) if kind == "band" else synth.random_mask(H, seed=N + 5)
+    got = _run(inp, dy, mask)
+    want = oracle.fft_bwd(inp.f64("u"), inp.f64("k"), dy.double().numpy(), inp.f64("w"), inp.f64("v"), mask)
+    _check(got, want, TOL["bf16"])
+
+
+@pytest.mark.parametrize("N,dtype,loc,dscale", [(2048, "bf16", 2.0, 1e3), (8192, "f16", 4.0, 1.0),
+                                                (4096, "bf16", 0.0, 1e-3)])
+def test_bwd_r_rows_range(N, dtype, loc, dscale):
+    # one spectrum scale per group: u, w ~ N(loc, 1) and dy far from unit size, with one
+    # channel of the group much smaller than the others
+    B, H = 2, 4
+    _say(f"bwd range N={N} {dtype} loc={loc} dy x{dscale}")
+    inp, dy = _case(B, H, N, N, dtype, "both", seed=N + int(loc))
+    u = inp.u.double() + loc
+    u[:, 1] *= 1e-2
+    inp.u = u.to(inp.u.dtype)
+    inp.w = (inp.w.double() + loc).to(inp.w.dtype)
+    dy = (dy.double() * dscale).to(dy.dtype)
+    got = _run(inp, dy)
+    want = oracle.fft_bwd(inp.f64("u"), inp.f64("k"), dy.double().numpy(), inp.f64("w"), inp.f64("v"))
+    _check(got, want, TOL[dtype])
+
+
 def test_bwd_gated_bf16_n16k_full_size():
     # the N = 16384 benchmark configuration (gated_bf16_n16k: B = 4, H = 2560, bf16) run
     # whole; every gradient of 12 channels spread over the range (all their batch rows,
