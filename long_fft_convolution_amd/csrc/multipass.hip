@@ -1123,6 +1123,36 @@ __device__ __forceinline__ float2 w64(int e) {
     }
 }
 constexpr float kW128c = 9.987954562e-01f, kW128s = -4.906767433e-02f;
+
+// 8-point DFT of complex values held as (re, im) fp16 pairs, out[q] = sum_r in[r] w8^{rq},
+// in packed fp16 arithmetic (fp16 storage: the values are fp16 before and after, and a
+// DFT-8 grows no partial sum beyond its largest output); radix 2 in time, as Dft<8>.
+__device__ __forceinline__ h2v h_negi(h2v a) { return h2v{a[1], -a[0]}; }   // -i a
+__device__ __forceinline__ void dft4h(h2v a0, h2v a1, h2v a2, h2v a3, h2v *o) {
+    const h2v s0 = a0 + a2, d0 = a0 - a2, s1 = a1 + a3, d1 = h_negi(a1 - a3);
+    o[0] = s0 + s1;
+    o[2] = s0 - s1;
+    o[1] = d0 + d1;
+    o[3] = d0 - d1;
+}
+__device__ __forceinline__ void dft8h(h2v *a) {
+    h2v E[4], O[4];
+    dft4h(a[0], a[2], a[4], a[6], E);
+    dft4h(a[1], a[3], a[5], a[7], O);
+    const _Float16 c = (_Float16)7.071067812e-01f;
+    // w8^q O[q]: q = 1: ((x + y) c, (y - x) c); q = 2: -i O; q = 3: ((y - x) c, -(x + y) c)
+    const h2v t1 = h2v{O[1][0] + O[1][1], O[1][1] - O[1][0]} * c;
+    const h2v t2 = h_negi(O[2]);
+    const h2v t3 = h2v{O[3][1] - O[3][0], -(O[3][0] + O[3][1])} * c;
+    a[0] = E[0] + O[0];
+    a[4] = E[0] - O[0];
+    a[1] = E[1] + t1;
+    a[5] = E[1] - t1;
+    a[2] = E[2] + t2;
+    a[6] = E[2] - t2;
+    a[3] = E[3] + t3;
+    a[7] = E[3] - t3;
+}
 }  // namespace mm
 
 struct MmTables {
@@ -1181,25 +1211,41 @@ mp_pass2m_kernel(T *__restrict__ ws, float2 *__restrict__ self_area, const __hal
         const int r = __builtin_amdgcn_readfirstlane(tid >> 8), q = (tid >> 5) & 7, na = tid & 31;
         const T *rowp = wsq + 2 * (int64_t)(r ? rowB : rowA) * N2;
         const uint32_t lo = (uint32_t)(na + 128 * q);
-        float2 y[4][8];
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-#pragma unroll
-            for (int nc = 0; nc < 8; ++nc) y[k][nc] = io<T>::load2(rowp + 2 * (32 * k + 1024 * nc), lo);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) dft_inplace<8>(y[k]);
         // n_b = 4q + k sits in K slot kslot(n_b): chunk q & 3, slot 4 (q >> 2) + k.  The
         // twiddle omega_8192^{n_ab f_c} of the four columns is one fp16 table word
         // (the same table as the inverse chain's outer twiddle), applied to the fp16 planes.
         const uint32_t o = (uint32_t)((q & 3) * 256 + na * 8 + 4 * (q >> 2));
-#pragma unroll
-        for (int fc = 0; fc < 8; ++fc) {
+        auto put = [&](int fc, h4 re, h4 im) {
             const uint32_t oc = (uint32_t)((r * 8 + fc) * 1024) + o;
-            h4 re = {(_Float16)y[0][fc].x, (_Float16)y[1][fc].x, (_Float16)y[2][fc].x, (_Float16)y[3][fc].x};
-            h4 im = {(_Float16)y[0][fc].y, (_Float16)y[1][fc].y, (_Float16)y[2][fc].y, (_Float16)y[3][fc].y};
             if (fc > 0) cmul4(re, im, ldu<h8>(mt.rtw, 16u * (uint32_t)((fc * 8 + q) * 32 + na)));
             *reinterpret_cast<h4 *>(P0 + oc) = re;
             *reinterpret_cast<h4 *>(P1 + oc) = im;
+        };
+        if constexpr (std::is_same<T, __half>::value) {   // the DFT-8 in packed fp16
+            h2v y[4][8];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+                for (int nc = 0; nc < 8; ++nc)
+                    y[k][nc] = __builtin_bit_cast(h2v, ldu<uint32_t>(rowp + 2 * (32 * k + 1024 * nc), 4u * lo));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) dft8h(y[k]);
+#pragma unroll
+            for (int fc = 0; fc < 8; ++fc)
+                put(fc, h4{y[0][fc][0], y[1][fc][0], y[2][fc][0], y[3][fc][0]},
+                    h4{y[0][fc][1], y[1][fc][1], y[2][fc][1], y[3][fc][1]});
+        } else {
+            float2 y[4][8];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+                for (int nc = 0; nc < 8; ++nc) y[k][nc] = io<T>::load2(rowp + 2 * (32 * k + 1024 * nc), lo);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) dft_inplace<8>(y[k]);
+#pragma unroll
+            for (int fc = 0; fc < 8; ++fc)
+                put(fc, h4{(_Float16)y[0][fc].x, (_Float16)y[1][fc].x, (_Float16)y[2][fc].x, (_Float16)y[3][fc].x},
+                    h4{(_Float16)y[0][fc].y, (_Float16)y[1][fc].y, (_Float16)y[2][fc].y, (_Float16)y[3][fc].y});
         }
     }
     __syncthreads();
@@ -1480,22 +1526,42 @@ mp_pass2m_kernel(T *__restrict__ ws, float2 *__restrict__ self_area, const __hal
         const int tid2 = launder(tid);
         const int r = __builtin_amdgcn_readfirstlane(tid2 >> 8), q = (tid2 >> 5) & 7, na = tid2 & 31;
         T *rowp = wsq + 2 * (int64_t)(r ? rowB : rowA) * N2;
-        float2 y[4][8];
-#pragma unroll
-        for (int fc = 0; fc < 8; ++fc) {
-            const uint32_t o = (uint32_t)((((r * 8 + fc) * 32 + na) * kR2Stride + 4 * q) * 4);
-            const uint2 a = ldu<uint2>(R2, o), b = ldu<uint2>(R2, o + 8u);
-            y[0][fc] = h2f(a.x);
-            y[1][fc] = h2f(a.y);
-            y[2][fc] = h2f(b.x);
-            y[3][fc] = h2f(b.y);
-        }
         const uint32_t lo = (uint32_t)(na + 128 * q);
+        if constexpr (std::is_same<T, __half>::value) {   // the DFT-8 in packed fp16
+            h2v y[4][8];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            dft_inplace<8>(y[k]);
+            for (int fc = 0; fc < 8; ++fc) {
+                const uint32_t o = (uint32_t)((((r * 8 + fc) * 32 + na) * kR2Stride + 4 * q) * 4);
+                const uint2 a = ldu<uint2>(R2, o), b = ldu<uint2>(R2, o + 8u);
+                y[0][fc] = __builtin_bit_cast(h2v, a.x);
+                y[1][fc] = __builtin_bit_cast(h2v, a.y);
+                y[2][fc] = __builtin_bit_cast(h2v, b.x);
+                y[3][fc] = __builtin_bit_cast(h2v, b.y);
+            }
 #pragma unroll
-            for (int nc = 0; nc < 8; ++nc) io<T>::store2(rowp + 2 * (32 * k + 1024 * nc), lo, y[k][nc]);
+            for (int k = 0; k < 4; ++k) {
+                dft8h(y[k]);
+#pragma unroll
+                for (int nc = 0; nc < 8; ++nc)
+                    stu(rowp + 2 * (32 * k + 1024 * nc), 4u * lo, __builtin_bit_cast(uint32_t, y[k][nc]));
+            }
+        } else {
+            float2 y[4][8];
+#pragma unroll
+            for (int fc = 0; fc < 8; ++fc) {
+                const uint32_t o = (uint32_t)((((r * 8 + fc) * 32 + na) * kR2Stride + 4 * q) * 4);
+                const uint2 a = ldu<uint2>(R2, o), b = ldu<uint2>(R2, o + 8u);
+                y[0][fc] = h2f(a.x);
+                y[1][fc] = h2f(a.y);
+                y[2][fc] = h2f(b.x);
+                y[3][fc] = h2f(b.y);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                dft_inplace<8>(y[k]);
+#pragma unroll
+                for (int nc = 0; nc < 8; ++nc) io<T>::store2(rowp + 2 * (32 * k + 1024 * nc), lo, y[k][nc]);
+            }
         }
     }
 }
