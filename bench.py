@@ -112,6 +112,15 @@ def algorithmic_bytes(w: synth.Workload) -> int:
     return int(act + w.H * w.N * bin_bytes * keep)
 
 
+def bwd_algorithmic_bytes(w: synth.Workload, has_w: bool, has_v: bool) -> int:
+    """What one backward call must move: dy, u (+ w, v) read, du (+ dw, dv) written,
+    dk written, the spectrum read once per channel."""
+    e = ELEM[w.dtype]
+    nact = 3 + (2 if has_w else 0) + (2 if has_v else 0)
+    spec = w.H * 2048 * 4 if w.short else w.H * (w.N + 1) * (8 if w.dtype == "f32" else 4)
+    return int(w.B * w.H * w.N * e * nact + w.H * w.L * e + spec)
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
@@ -469,12 +478,7 @@ def bench_bwd(args, wl, dev, u, K_f, w, v, mask):
     log(f"bench: {n_warm} warm-up steps")
     ms_per_step = time_steps(step, args.steps, dev)
     elems = wl.B * wl.H * wl.N
-    e = ELEM[wl.dtype]
-    # what the backward must move: dy, u (+ w, v) read, du (+ dw, dv) written,
-    # dk written, the spectrum read once per channel
-    nact = 3 + (2 if w is not None else 0) + (2 if v is not None else 0)
-    spec = wl.H * 2048 * 4 if wl.short else wl.H * (wl.N + 1) * (8 if wl.dtype == "f32" else 4)
-    alg = elems * e * nact + wl.H * wl.L * e + spec
+    alg = bwd_algorithmic_bytes(wl, w is not None, v is not None)
     achieved = alg / (ms_per_step / 1e3) / 1e9
     log(f"bench: bwd {ms_per_step * 1e3:.1f} us/step, {elems / (ms_per_step / 1e3):.3e} elems/s")
     rec = {
