@@ -499,9 +499,12 @@ int64_t mp_ws_bytes(int st) {
 }
 
 int64_t mp_chunk(int logn, int st) {
-    // keep one chunk's complex intermediate near 128 MiB
+    // keep one chunk's complex intermediate near 128 MiB; from N = 2^22 on near 1 GiB (at
+    // 16 MiB per sequence a 128 MiB chunk is 8 sequences, and the passes' launches then
+    // lose 3-4 % of a call to their tails; at N = 2^20 the chunk size made no difference)
     const int64_t per_seq = mp_ws_bytes(st) << logn;
-    int64_t c = (int64_t(128) << 20) / per_seq;
+    const int64_t target = logn >= 22 ? int64_t(1) << 30 : int64_t(128) << 20;
+    int64_t c = target / per_seq;
     return c < 1 ? 1 : c;
 }
 

@@ -140,9 +140,9 @@ using namespace p16;
 // DUAL: a second output out2 = v2 * conv(u w, k) from the same transforms (the backward
 // pass forms du and dw in one call); the second gate's rows are loaded once the staged
 // outputs have freed their registers.
-// MODE (kConv, kSpec, kCorr) above.  kSpec writes spec_out[p] and scale_out[p] for pair
-// (group) p, all 32 rows of the workgroup; kCorr reads them through kbins and kscale and
-// writes the rows bp H + h (h: the group's channels) of out.
+// MODE (kConv, kSpec, kCorr) above.  kSpec writes spec_out[p] (all 32 rows of the
+// workgroup) for group p and scale_out[p P + sp] for its sub-pair sp; kCorr reads them
+// through kbins and kscale and writes the rows bp H + h (h: the group's channels) of out.
 // LOGR < 5 (N = 512 R = 2048, 4096, 8192): the 2N-point transform is R = 2^LOGR outer
 // rows of 1024; P = 32 / R pairs of P consecutive channels (the same batch rows) share a
 // workgroup's 32 rows (sub-pair p = row / R, f_c = row mod R), so phase 2 is unchanged.
