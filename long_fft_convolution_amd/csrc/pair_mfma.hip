@@ -245,8 +245,16 @@ __device__ __forceinline__ void gate_product<__hip_bfloat16>(const uint4 &uq, co
 // IDFT(DFT(window) conj K), has no wrap-around at the outputs 0 .. 1023, so S1' takes the
 // unflipped entries of the N = 1024 path and the filter product the conjugated spectrum.
 // A pair is windows (2 jp, 2 jp + 1) fed by the blocks A = 2 jp, B = 2 jp + 1, C = 2 jp + 2.
+// LONE (not windows): the last batch row b = B - 1 of an odd B, whose rows would otherwise
+// each pair with zeros.  A pair is two channels h = 2q, h' = 2q + 1 of that row (h' = h
+// without a partner: H odd): z = x_h + i x_h'.  With the real filters' stored spectra K, K'
+// and Z the transform of z, X_h = (Z(f) + conj Z(-f)) / 2 and i X_h' = (Z(f) - conj Z(-f)) / 2,
+// so the product that yields y_h + i y_h' is
+//   Y(f) = Z(f) (K + K') / 2 + conj Z(-f) (K - K') / 2.
+// The bins of Z pass through the wave's LDS to bring Z(-f) to the lane holding Z(f); the
+// real part of the result takes h's scale, the imaginary part h''s.
 template <typename T, bool MASKED, bool HAS_W, bool HAS_V, bool WIN = false, bool DUAL = false,
-          bool CORR = false>
+          bool CORR = false, bool LONE = false>
 __global__ void __launch_bounds__(64 * kPairWaves, MASKED ? 1 : 2)
 pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restrict__ v,
               T *__restrict__ out, const uint4 *__restrict__ kbins, const float *__restrict__ kscale,
@@ -255,6 +263,7 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
     static_assert(!(WIN && MASKED), "the windowed path has no frequency mask");
     static_assert(!DUAL || (HAS_V && (!WIN || CORR)), "a second output has an output gate of its own");
     static_assert(!CORR || WIN, "the correlation mode is a windowed one");
+    static_assert(!(LONE && WIN), "channel pairs are for the batch-row path");
     constexpr int N = 1024;
     __shared__ h8 s_tw1[2 * 4 * 64];     // per (mt, nt, lane): cos[4], sin[4]
     __shared__ h8 s_tw3[4 * 2 * 64];     // per (nt, nt2, lane)
@@ -305,11 +314,11 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
     // the HBM pages are poorly used); with H < 8 the XCDs split p = bp H + h.
     const int64_t NW = NS / 1024, JP = (NW + 1) / 2;            // windows, window pairs per sequence
     const int64_t PB = WIN ? B * JP : (B + 1) / 2;               // pairs per channel
-    const int64_t P = H * PB;
+    const int64_t P = LONE ? (H + 1) / 2 : H * PB;
     const uint32_t nwg = gridDim.x, xcd = blockIdx.x % 8, wg_local = blockIdx.x / 8;
     const uint32_t wg_on_xcd = nwg / 8 + (xcd < nwg % 8 ? 1u : 0u);
     int64_t p_begin, p_end, h0 = 0, Hx = H;
-    if (!WIN && H >= 8) {
+    if (!WIN && !LONE && H >= 8) {
         h0 = H * xcd / 8;
         Hx = H * (xcd + 1) / 8 - h0;
         p_begin = 0;
@@ -329,6 +338,14 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
     // at the sequence end (its block C lies past it)
     auto offsets = [&](int64_t p, int64_t &h, int64_t &oa, int64_t &ob, bool &has_b, bool &edge) {
         int64_t bp;
+        if (LONE) {   // channels 2 p, 2 p + 1 of the last batch row
+            h = 2 * p;
+            has_b = 2 * p + 1 < H;
+            edge = false;
+            oa = ((B - 1) * H + h) * N;
+            ob = has_b ? oa + N : oa;
+            return;
+        }
         if (WIN) {
             const uint32_t h32 = (uint32_t)p / (uint32_t)PB;
             h = h32;
@@ -360,18 +377,22 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
     struct Filt {
         uint4 k[2][4];
         float ks;
+        float ks2;   // LONE: the second channel's scale (its chunks are read where used)
     };
     auto load_filt = [&](int64_t pp, Filt &fk) {
         int64_t h, oa, ob;
         bool hb, fst;
         offsets(pp, h, oa, ob, hb, fst);
         const uint4 *krow = kbins + h * 512;
+        if (!LONE) {
 #pragma unroll
-        for (int mt2 = 0; mt2 < 2; ++mt2)
+            for (int mt2 = 0; mt2 < 2; ++mt2)
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) fk.k[mt2][nt] = krow[(mt2 * 4 + nt) * 64 + lane];
+                for (int nt = 0; nt < 4; ++nt) fk.k[mt2][nt] = krow[(mt2 * 4 + nt) * 64 + lane];
+        }
         // (the four stages' table factors are undone with the channel scale)
         fk.ks = __builtin_ldexpf(kscale[h], 2 * (kPairS1Log2 + kPairS2Log2));
+        if (LONE) fk.ks2 = __builtin_ldexpf(kscale[hb ? h + 1 : h], 2 * (kPairS1Log2 + kPairS2Log2));
         if (CORR) {   // conj K: the sign of the imaginary half (elements 4..7) of every chunk
 #pragma unroll
             for (int mt2 = 0; mt2 < 2; ++mt2)
@@ -445,7 +466,8 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
         uint4 vg[4], vg2[4];
         if (HAS_V) load_gate(v, oa, ob, vg);
         if (DUAL) load_gate(v2, oa, ob, vg2);
-        const float ks = fc.ks;
+        // output scales of the real and the imaginary part (LONE: two channels)
+        float ksa = fc.ks, ksb = LONE ? fc.ks2 : fc.ks;
 
         // ---- x = u * w of both sequences (windows), scattered into the transposed LDS
         // planes: element m = n_f + 32 n_s at row n_f, K block n_s / 32, slot kslot(n_s % 32)
@@ -470,6 +492,57 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
                 for (int e = 0; e < 8; ++e) {
                     zr[(nf0 + e) * kRow + kss] = xa[e];
                     zi[(nf0 + e) * kRow + kss] = xb[e];
+                }
+            }
+        } else if constexpr (LONE) {
+            h8 xa[2], xb[2];
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                gate_product<T>(cur.q[r][0], cur.q[r][1], HAS_W, xa[r]);
+                gate_product<T>(cur.q[r][2], cur.q[r][3], HAS_W, xb[r]);
+                if (!has_b) xb[r] = h8{};
+            }
+            // The two channels share one transform and the smaller one is recovered as a
+            // difference (Z(f) - conj Z(-f)) / 2, so both are brought to one magnitude first:
+            // the smaller one times a power of two 2^d (d + 1 = the exponent gap of their
+            // maxima over the wave), undone in its output scale.
+            float ma = 0.f, mb = 0.f;
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    ma = fmaxf(ma, fabsf((float)xa[r][e]));
+                    mb = fmaxf(mb, fabsf((float)xb[r][e]));
+                }
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) {
+                ma = fmaxf(ma, __shfl_xor(ma, o));
+                mb = fmaxf(mb, __shfl_xor(mb, o));
+            }
+            if (ma > 0.f && mb > 0.f) {
+                int d = __builtin_amdgcn_frexp_expf(ma) - __builtin_amdgcn_frexp_expf(mb);
+                const bool up_b = d > 0;
+                d = (up_b ? d : -d) - 1;   // (the scaled maximum stays below the other one)
+                d = d > 14 ? 14 : d;
+                if (d > 0) {
+                    const _Float16 f = (_Float16)__builtin_ldexpf(1.f, d);
+#pragma unroll
+                    for (int r = 0; r < 2; ++r) {
+                        if (up_b) xb[r] *= f;
+                        else xa[r] *= f;
+                    }
+                    if (up_b) ksb = __builtin_ldexpf(ksb, -d);
+                    else ksa = __builtin_ldexpf(ksa, -d);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int m0 = 8 * lane + 512 * r;
+                const int ns = m0 >> 5, nf0 = m0 & 31, kss = kslot_of(ns);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    zr[(nf0 + e) * kRow + kss] = xa[r][e];
+                    zi[(nf0 + e) * kRow + kss] = xb[r][e];
                 }
             }
         } else {
@@ -518,6 +591,7 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
         // S1' operands, fp16: a[ks][nt2] (re, im); rows f_s of tiles nt = 2ks (j < 4), 2ks+1 (j >= 4)
         h8 a3r[2][2], a3i[2][2];
 
+        if constexpr (!LONE) {
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
             // ---- S1: rows n_f (tiles mt), column tile nt of f_s; twiddle w2048^{nf fs} (fp16)
@@ -588,6 +662,105 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
             }
         }
 
+        } else {
+            // LONE: S1 and S2 of every column tile, the bins of Z into the wave's LDS (word
+            // f ^ 16 ((f >> 8) & 3) for bin f, against bank conflicts), then per tile the
+            // product with the partner bin Z(-f) and S2'
+            uint32_t *const zw = reinterpret_cast<uint32_t *>(s_z[wave]);
+            const uint8_t *mrow2 = MASKED ? mask + (has_b ? h + 1 : h) * kMaskBlocks : nullptr;
+            // both channels' filter chunks, read here (not prefetched: this launch is one row)
+            const uint4 *krow1 = kbins + h * 512, *krow2 = kbins + (has_b ? h + 1 : h) * 512;
+            typedef _Float16 h2t __attribute__((ext_vector_type(2)));
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                h4 t1r[2], t1i[2];
+                const h8 f1r = s_f1[0][nt][lane], f1i = s_f1[1][nt][lane];
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    f4 ar = mfma(dr[0][mt], f1r, zero4);
+                    ar = mfma(ndi[0][mt], f1i, ar);
+                    f4 ai = mfma(dr[0][mt], f1i, zero4);
+                    ai = mfma(di[0][mt], f1r, ai);
+                    t1r[mt] = to_h4(ar);
+                    t1i[mt] = to_h4(ai);
+                    cmul4(t1r[mt], t1i[mt], s_tw1[(mt * 4 + nt) * 64 + lane]);
+                }
+                const h8 br = cat8(t1r[0], t1r[1]), bi = cat8(t1i[0], t1i[1]);
+                const h8 nbi = neg8(bi);
+#pragma unroll
+                for (int mt2 = 0; mt2 < 2; ++mt2) {
+                    f4 ar = mfma(c2r[mt2], br, zero4);
+                    ar = mfma(c2i[mt2], nbi, ar);
+                    f4 ai = mfma(c2r[mt2], bi, zero4);
+                    ai = mfma(c2i[mt2], br, ai);
+                    const h4 zr = to_h4(ar), zi = to_h4(ai);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int f = 16 * nt + c + 64 * (16 * mt2 + 4 * g + i);
+                        zw[f ^ (g << 4)] = __builtin_bit_cast(uint32_t, h2t{zr[i], zi[i]});
+                    }
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const h4 half4 = {(_Float16)0.5f, (_Float16)0.5f, (_Float16)0.5f, (_Float16)0.5f};
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                h4 yr[2], yi[2];
+#pragma unroll
+                for (int mt2 = 0; mt2 < 2; ++mt2) {
+                    const uint4 q1 = krow1[(mt2 * 4 + nt) * 64 + lane], q2 = krow2[(mt2 * 4 + nt) * 64 + lane];
+                    h8 k1 = *reinterpret_cast<const h8 *>(&q1);
+                    h8 k2 = *reinterpret_cast<const h8 *>(&q2);
+                    h4 zr, zi, mr, mi;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int f = 16 * nt + c + 64 * (16 * mt2 + 4 * g + i);
+                        if (MASKED) {
+                            const int fr = f <= N ? f : 2 * N - f;
+                            int blk = fr / (N / kMaskBlocks);
+                            blk = blk > kMaskBlocks - 1 ? kMaskBlocks - 1 : blk;
+                            if (!mrow[blk]) k1[i] = k1[4 + i] = (_Float16)0.f;
+                            if (!mrow2[blk]) k2[i] = k2[4 + i] = (_Float16)0.f;
+                        }
+                        const int fm = (2 * N - f) & (2 * N - 1);   // the partner bin -f
+                        const h2t zv = __builtin_bit_cast(h2t, zw[f ^ (g << 4)]);
+                        const h2t mv = __builtin_bit_cast(h2t, zw[fm ^ (((fm >> 8) & 3) << 4)]);
+                        zr[i] = zv[0];
+                        zi[i] = zv[1];
+                        mr[i] = mv[0];
+                        mi[i] = mv[1];
+                    }
+                    // A = (K + K') / 2, D = (K - K') / 2; Y = Z A + conj(Z(-f)) D
+                    const h4 ar = (lo4(k1) + lo4(k2)) * half4, ai = (hi4(k1) + hi4(k2)) * half4;
+                    const h4 er = (lo4(k1) - lo4(k2)) * half4, ei = (hi4(k1) - hi4(k2)) * half4;
+                    yr[mt2] = zr * ar - zi * ai + mr * er + mi * ei;
+                    yi[mt2] = zr * ai + zi * ar + mr * ei - mi * er;
+                }
+                const h8 a2r = cat8(yr[0], yr[1]), a2i = cat8(yi[0], yi[1]);
+                const h8 na2r = neg8(a2r);
+#pragma unroll
+                for (int nt2 = 0; nt2 < 2; ++nt2) {
+                    f4 ar = mfma(a2r, c2r[nt2], zero4);
+                    ar = mfma(a2i, c2i[nt2], ar);
+                    f4 ai = mfma(na2r, c2i[nt2], zero4);
+                    ai = mfma(a2i, c2r[nt2], ai);
+                    h4 t3r = to_h4(ar), t3i = to_h4(ai);
+                    cmul4(t3r, t3i, s_tw3[(nt * 2 + nt2) * 64 + lane]);
+                    const int ksi = nt >> 1, half = (nt & 1) * 4;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        a3r[ksi][nt2][half + i] = t3r[i];
+                        a3i[ksi][nt2][half + i] = t3i[i];
+                    }
+                }
+            }
+            // (the reads above before the output rows are staged in the same bytes)
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
         __builtin_amdgcn_sched_barrier(0);
         load_filt(pn, fc);
         __builtin_amdgcn_sched_barrier(0);
@@ -614,7 +787,7 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
                 // LDS (16-byte unit u = m / 4, bit 2 flipped by bit 4 against bank conflicts)
                 const int un = 8 * (16 * nt3 + c) + 4 * nt2 + g;
                 const int us = un ^ (((un >> 4) & 1) << 2);
-                f4 ya = ar * ks, yb = ai * ks;
+                f4 ya = ar * ksa, yb = ai * ksb;
                 *reinterpret_cast<f4 *>(so + 16 * us) = ya;
                 *reinterpret_cast<f4 *>(so + 4096 + 16 * us) = yb;
             }
@@ -1085,46 +1258,59 @@ hipError_t launch_pair_conv(int logn, int st, const void *u, const void *w, cons
         if (hipDeviceGetAttribute(&v_, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v_ > 0)
             cus = v_;
     }
-    const int64_t pairs = H * ((B + 1) / 2);
-    if (pairs >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-    if (pairs == 0) return hipSuccess;
-    // two resident 4-wave workgroups per CU (one for the masked variant)
-    int64_t blocks = (int64_t)cus * (mask ? 1 : 2);
-    const int64_t need = (pairs + kPairWaves - 1) / kPairWaves;
-    if (blocks > need) blocks = need < 8 ? 8 : (need + 7) / 8 * 8;
-    auto go = [&](auto kern, auto *tp) {
-        using TT = std::remove_pointer_t<decltype(tp)>;
-        hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * kPairWaves), 0, stream,
-                           (const TT *)u, (const TT *)w, (const TT *)v, (TT *)out,
-                           (const uint4 *)kbins, kscale, mask, tb, B, H, (int64_t)1024, (const TT *)v2,
-                           (TT *)out2);
-    };
-    // one instantiation per (storage type, mask, gates): no gate test sits in the pair loop
-    auto pick = [&](auto *tp) {
-        using TT = std::remove_pointer_t<decltype(tp)>;
-        if (out2 != nullptr) {   // two outputs: both output gates present
-            switch ((mask ? 2 : 0) | (w ? 1 : 0)) {
-            case 0: go(pair1k_kernel<TT, false, false, true, false, true>, tp); break;
-            case 1: go(pair1k_kernel<TT, false, true, true, false, true>, tp); break;
-            case 2: go(pair1k_kernel<TT, true, false, true, false, true>, tp); break;
-            default: go(pair1k_kernel<TT, true, true, true, false, true>, tp); break;
+    if (H * ((B + 1) / 2) >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    // An odd B: the rows 0 .. B - 2 as batch-row pairs, the last row as channel pairs (LONE)
+    const int64_t Bp = B & ~int64_t(1);
+    auto launch = [&](bool lone) {
+        const int64_t pairs = lone ? (H + 1) / 2 : H * (Bp / 2);
+        if (pairs == 0) return;
+        // two resident 4-wave workgroups per CU (one for the masked variant)
+        int64_t blocks = (int64_t)cus * (mask ? 1 : 2);
+        const int64_t need = (pairs + kPairWaves - 1) / kPairWaves;
+        if (blocks > need) blocks = need < 8 ? 8 : (need + 7) / 8 * 8;
+        auto go = [&](auto kern, auto *tp) {
+            using TT = std::remove_pointer_t<decltype(tp)>;
+            hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * kPairWaves), 0, stream,
+                               (const TT *)u, (const TT *)w, (const TT *)v, (TT *)out,
+                               (const uint4 *)kbins, kscale, mask, tb, lone ? B : Bp, H, (int64_t)1024,
+                               (const TT *)v2, (TT *)out2);
+        };
+        // one instantiation per (storage type, mask, gates, row kind): no gate test sits in
+        // the pair loop
+        auto pick = [&](auto *tp, auto lone_c) {
+            using TT = std::remove_pointer_t<decltype(tp)>;
+            constexpr bool LN = decltype(lone_c)::value;
+            if (out2 != nullptr) {   // two outputs: both output gates present
+                switch ((mask ? 2 : 0) | (w ? 1 : 0)) {
+                case 0: go(pair1k_kernel<TT, false, false, true, false, true, false, LN>, tp); break;
+                case 1: go(pair1k_kernel<TT, false, true, true, false, true, false, LN>, tp); break;
+                case 2: go(pair1k_kernel<TT, true, false, true, false, true, false, LN>, tp); break;
+                default: go(pair1k_kernel<TT, true, true, true, false, true, false, LN>, tp); break;
+                }
+                return;
             }
-            return;
-        }
-        const int sel = (mask ? 4 : 0) | (w ? 2 : 0) | (v ? 1 : 0);
-        switch (sel) {
-        case 0: go(pair1k_kernel<TT, false, false, false>, tp); break;
-        case 1: go(pair1k_kernel<TT, false, false, true>, tp); break;
-        case 2: go(pair1k_kernel<TT, false, true, false>, tp); break;
-        case 3: go(pair1k_kernel<TT, false, true, true>, tp); break;
-        case 4: go(pair1k_kernel<TT, true, false, false>, tp); break;
-        case 5: go(pair1k_kernel<TT, true, false, true>, tp); break;
-        case 6: go(pair1k_kernel<TT, true, true, false>, tp); break;
-        default: go(pair1k_kernel<TT, true, true, true>, tp); break;
+            const int sel = (mask ? 4 : 0) | (w ? 2 : 0) | (v ? 1 : 0);
+            switch (sel) {
+            case 0: go(pair1k_kernel<TT, false, false, false, false, false, false, LN>, tp); break;
+            case 1: go(pair1k_kernel<TT, false, false, true, false, false, false, LN>, tp); break;
+            case 2: go(pair1k_kernel<TT, false, true, false, false, false, false, LN>, tp); break;
+            case 3: go(pair1k_kernel<TT, false, true, true, false, false, false, LN>, tp); break;
+            case 4: go(pair1k_kernel<TT, true, false, false, false, false, false, LN>, tp); break;
+            case 5: go(pair1k_kernel<TT, true, false, true, false, false, false, LN>, tp); break;
+            case 6: go(pair1k_kernel<TT, true, true, false, false, false, false, LN>, tp); break;
+            default: go(pair1k_kernel<TT, true, true, true, false, false, false, LN>, tp); break;
+            }
+        };
+        if (lone) {
+            if (st == ST_F16) pick((__half *)nullptr, std::true_type{});
+            else pick((__hip_bfloat16 *)nullptr, std::true_type{});
+        } else {
+            if (st == ST_F16) pick((__half *)nullptr, std::false_type{});
+            else pick((__hip_bfloat16 *)nullptr, std::false_type{});
         }
     };
-    if (st == ST_F16) pick((__half *)nullptr);
-    else pick((__hip_bfloat16 *)nullptr);
+    launch(false);
+    if (B & 1) launch(true);
     return hipGetLastError();
 }
 
