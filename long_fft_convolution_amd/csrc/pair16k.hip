@@ -175,8 +175,12 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
     h8 *s_out = reinterpret_cast<h8 *>(s_mask + 8 * kMaskBlocks);
     // kSpec / kCorr: per wave and slot n_c of phase 1, the sum of |input| [wave][32]
     float *const s_part = reinterpret_cast<float *>(s_out + 6 * 64);
+    // kConv: bit 8 row + sp set when a wave saw a non-zero input of that row (a, b) of
+    // sub-pair sp, ORed over the waves
+    uint32_t *const s_zf = reinterpret_cast<uint32_t *>(s_part + kWaves * 32);
 
     const int tid = threadIdx.x;
+    if (tid == 0) *s_zf = 0u;
     for (int i = tid; i < 256; i += 64 * kWaves) {
         s_tw1[i] = reinterpret_cast<const h8 *>(tb.tw1)[i];
         s_tw3[i] = reinterpret_cast<const h8 *>(tb.tw3)[i];
@@ -259,6 +263,10 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
     // kSpec / kCorr: sum of |x| over the pair's transformed values (this lane's share, per
     // slot n_c = 4 g + j)
     float l1j[4] = {0.f, 0.f, 0.f, 0.f};
+    // kConv: the fp16 bits of this lane's inputs ORed (the sign bits are cleared when they
+    // are tested), per row and (R = 4, where the two slot halves j < 2, j >= 2 belong to two
+    // sub-pairs) slot half
+    uint32_t nz[2][2] = {{0u, 0u}, {0u, 0u}};
     auto load_batch = [&](int64_t oa_, int64_t ob_, int half, Batch &x, int nv_) {
         const uint32_t *pua = reinterpret_cast<const uint32_t *>(u + oa_);
         const uint32_t *pub = reinterpret_cast<const uint32_t *>(u + ob_);
@@ -318,6 +326,18 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                     br[4 + j] = (_Float16)0.f;
                     bi[4 + j] = (_Float16)0.f;
                     if (SPEC || CORR) l1j[j] += fabsf((float)br[j]) + fabsf((float)bi[j]);
+                }
+                if (!SPEC && !CORR) {
+                    const uint4 qa = *reinterpret_cast<const uint4 *>(&br), qb = *reinterpret_cast<const uint4 *>(&bi);
+                    if constexpr (NCH >= 4) {
+                        nz[0][0] |= qa.x | qa.y;
+                        nz[1][0] |= qb.x | qb.y;
+                    } else {
+                        nz[0][0] |= qa.x;
+                        nz[0][1] |= qa.y;
+                        nz[1][0] |= qb.x;
+                        nz[1][1] |= qb.y;
+                    }
                 }
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
@@ -404,7 +424,31 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
 #pragma unroll
             for (int j = 0; j < 4; ++j) l1j[j] = 0.f;
         }
+        if (!SPEC && !CORR) {   // this wave's non-zero rows of sub-pairs, ORed into s_zf
+            uint32_t seen = 0u;   // (wave-uniform: built from the ballots)
+#pragma unroll
+            for (int row = 0; row < 2; ++row)
+#pragma unroll
+                for (int jh = 0; jh < (NCH >= 4 ? 1 : 2); ++jh) {
+                    // (sign bits cleared once here: a product 0 * (-w) is -0)
+                    const unsigned long long m = __builtin_amdgcn_ballot_w64((nz[row][jh] & 0x7fff7fffu) != 0u);
+                    nz[row][jh] = 0u;
+#pragma unroll
+                    for (int gg = 0; gg < 4; ++gg) {   // lanes 16 gg .. 16 gg + 15: slots 4 gg + j
+                        const int sp = (4 * gg + 2 * jh) / NCH;
+                        if ((m >> (16 * gg)) & 0xffffull) seen |= 1u << (8 * row + sp);
+                    }
+                }
+            if (lane == 0 && seen != 0u) atomicOr(s_zf, seen);
+        }
         __syncthreads();
+        // kConv: a row of a sub-pair whose inputs are all zero has the result 0, not the
+        // rounding of its partner row's values: zrow bit 8 row + sp marks it
+        uint32_t zrow = 0u;
+        if (!SPEC && !CORR) {
+            constexpr uint32_t kRows = ((1u << P) - 1u) * 0x101u;
+            zrow = __builtin_amdgcn_readfirstlane(~*s_zf & kRows);
+        }
         // kSpec / kCorr: |Z[f]| <= sum |z| bounds every bin of a sub-pair's transform, so a
         // spectrum taken after the three forward stages (table factors 2^-kF) and scaled by
         // the power of two 2^e <= 2^(kF + kSpecLog2) / sum |z| stays within |.| <= 2^kSpecLog2
@@ -480,6 +524,7 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                     kq[mt2][nt] = k_load<CORR, LOGR>(kchan(wave), krow(wave), mt2, nt, ul);
         }
         __syncthreads();
+        if (tid == 0) *s_zf = 0u;   // (every thread has read it; the next pair ORs into it)
 
         // ---- phase 2b: the 1024-point chain per row, filter product, inverse chain;
         // the next row's filter chunks are fetched while this row computes
@@ -634,6 +679,9 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
         } else if constexpr (R < 32) {
             ksl = __builtin_ldexpf(kscale[chan(h, c / NCH)], kBack);
         }
+        // (an all-zero row of column c's sub-pair: the output scale 0)
+        const int spz = R == 32 ? 0 : c / NCH;
+        const float ksla = (zrow >> spz) & 1u ? 0.f : ksl, kslb = (zrow >> (8 + spz)) & 1u ? 0.f : ksl;
 #pragma unroll
         for (int tt = 0; tt < kTilesPerWave; ++tt) {
             // r2(8 g, 16 T + c)
@@ -645,8 +693,8 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                 const h8 f3r = s_out[256 + lane], f3i = s_out[320 + lane];
                 cm_dataA_conj(dr, di, f3r, f3i, neg8(f3i), ya[tt], yb[tt]);
             }
-            ya[tt] *= ksl;
-            yb[tt] *= ksl;
+            ya[tt] *= ksla;
+            yb[tt] *= kslb;
             __builtin_amdgcn_sched_barrier(0);   // (bounds the live R2 operands)
         }
         {
@@ -735,9 +783,9 @@ static hipError_t p16_grid(int64_t B, int64_t H, int64_t *blocks, int logr = 5) 
 
 // LDS: the two planes, the inner twiddle tables, the mask rows of up to 8 channels, the
 // outer DFT tiles of R < 32 (six planes of 64 lanes x 16 bytes), the per-wave input sums of
-// the spectrum and correlation modes
+// the spectrum and correlation modes, the non-zero lane masks of the rows
 static constexpr size_t kP16Lds =
-    (size_t)2 * kR1Plane * sizeof(_Float16) + 2 * 256 * 16 + 8 * kMaskBlocks + 6 * 64 * 16 + 8 * 32 * 4;
+    (size_t)2 * kR1Plane * sizeof(_Float16) + 2 * 256 * 16 + 8 * kMaskBlocks + 6 * 64 * 16 + 8 * 32 * 4 + 4 * 8;
 static_assert(kP16Lds <= 160 * 1024, "LDS of one workgroup");
 
 static P16Outer p16_outer(const Pair3Tables &tb, int logr) {

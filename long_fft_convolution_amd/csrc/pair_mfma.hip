@@ -142,6 +142,7 @@ __device__ __forceinline__ int kslot_of(int ns) {
 }
 
 constexpr int kPairWaves = 4;
+
 constexpr int kPlane = 32 * 32;     // fp16 elements per LDS plane (rows n_f, K slots)
 
 // raw 16-byte input chunks of one pair: [u_a, w_a, u_b, w_b] x [r = 0, 1]
@@ -220,6 +221,67 @@ __device__ __forceinline__ void gate_product<__hip_bfloat16>(const uint4 &uq, co
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = (_Float16)a[e];
+}
+
+// The two rows of a pair share one complex transform, and every stage rounds to fp16 at
+// the magnitude of the larger row.  zero_rows: a row that is all zero gets the output scale
+// 0 (its result is exactly 0, not the rounding of its partner's), from one ballot.
+// equalize_pair (channel pairs, where magnitudes differ more): also brings a much smaller
+// row near the other: over the wave (one pair per wave) the maxima of |x_a| and |x_b| are
+// compared, the smaller row is multiplied by 2^d (d one less than their exponent gap, at
+// most 14: exact in fp16) and its output scale by 2^-d.
+__device__ __forceinline__ void zero_rows(const h8 (&xa)[2], const h8 (&xb)[2], float &ksa, float &ksb) {
+    uint32_t oa = 0, ob = 0;   // (sign bits cleared: a row of -0 is zero too)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const uint4 qa = *reinterpret_cast<const uint4 *>(&xa[r]), qb = *reinterpret_cast<const uint4 *>(&xb[r]);
+        oa |= (qa.x | qa.y | qa.z | qa.w) & 0x7fff7fffu;
+        ob |= (qb.x | qb.y | qb.z | qb.w) & 0x7fff7fffu;
+    }
+    if (__builtin_amdgcn_ballot_w64(oa != 0) == 0) ksa = 0.f;
+    if (__builtin_amdgcn_ballot_w64(ob != 0) == 0) ksb = 0.f;
+}
+typedef unsigned short us2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ us2_t absmax2(const h8 &x, us2_t m) {
+    // fp16 magnitudes compare as unsigned integers once the sign bit is cleared
+    const uint4 q = *reinterpret_cast<const uint4 *>(&x);
+    const us2_t a = __builtin_bit_cast(us2_t, q.x & 0x7fff7fffu), b = __builtin_bit_cast(us2_t, q.y & 0x7fff7fffu);
+    const us2_t c = __builtin_bit_cast(us2_t, q.z & 0x7fff7fffu), d = __builtin_bit_cast(us2_t, q.w & 0x7fff7fffu);
+    return __builtin_elementwise_max(__builtin_elementwise_max(m, __builtin_elementwise_max(a, b)),
+                                     __builtin_elementwise_max(c, d));
+}
+__device__ __forceinline__ void equalize_pair(h8 (&xa)[2], h8 (&xb)[2], float &ksa, float &ksb) {
+    us2_t pa = {0, 0}, pb = {0, 0};
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        pa = absmax2(xa[r], pa);
+        pb = absmax2(xb[r], pb);
+    }
+    uint32_t ma = pa[0] > pa[1] ? pa[0] : pa[1], mb = pb[0] > pb[1] ? pb[0] : pb[1];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const uint32_t ta = (uint32_t)__shfl_xor((int)ma, o), tb = (uint32_t)__shfl_xor((int)mb, o);
+        ma = ma > ta ? ma : ta;
+        mb = mb > tb ? mb : tb;
+    }
+    if (ma == 0) ksa = 0.f;
+    if (mb == 0) ksb = 0.f;
+    if (ma != 0 && mb != 0) {
+        int d = (int)(ma >> 10) - (int)(mb >> 10);   // exponent gap (fp16 biased exponents)
+        const bool up_b = d > 0;
+        d = (up_b ? d : -d) - 1;   // (the scaled maximum stays below the other one)
+        d = d > 14 ? 14 : d;
+        if (d > 0) {
+            const _Float16 f = (_Float16)__builtin_ldexpf(1.f, d);
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                if (up_b) xb[r] *= f;
+                else xa[r] *= f;
+            }
+            if (up_b) ksb = __builtin_ldexpf(ksb, -d);
+            else ksa = __builtin_ldexpf(ksa, -d);
+        }
+    }
 }
 
 // WIN: the chunked short-filter path (overlap-save with the transform's own
@@ -502,39 +564,9 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
                 gate_product<T>(cur.q[r][2], cur.q[r][3], HAS_W, xb[r]);
                 if (!has_b) xb[r] = h8{};
             }
-            // The two channels share one transform and the smaller one is recovered as a
-            // difference (Z(f) - conj Z(-f)) / 2, so both are brought to one magnitude first:
-            // the smaller one times a power of two 2^d (d + 1 = the exponent gap of their
-            // maxima over the wave), undone in its output scale.
-            float ma = 0.f, mb = 0.f;
-#pragma unroll
-            for (int r = 0; r < 2; ++r)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    ma = fmaxf(ma, fabsf((float)xa[r][e]));
-                    mb = fmaxf(mb, fabsf((float)xb[r][e]));
-                }
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) {
-                ma = fmaxf(ma, __shfl_xor(ma, o));
-                mb = fmaxf(mb, __shfl_xor(mb, o));
-            }
-            if (ma > 0.f && mb > 0.f) {
-                int d = __builtin_amdgcn_frexp_expf(ma) - __builtin_amdgcn_frexp_expf(mb);
-                const bool up_b = d > 0;
-                d = (up_b ? d : -d) - 1;   // (the scaled maximum stays below the other one)
-                d = d > 14 ? 14 : d;
-                if (d > 0) {
-                    const _Float16 f = (_Float16)__builtin_ldexpf(1.f, d);
-#pragma unroll
-                    for (int r = 0; r < 2; ++r) {
-                        if (up_b) xb[r] *= f;
-                        else xa[r] *= f;
-                    }
-                    if (up_b) ksb = __builtin_ldexpf(ksb, -d);
-                    else ksa = __builtin_ldexpf(ksa, -d);
-                }
-            }
+            // (the smaller channel is recovered as a difference (Z(f) - conj Z(-f)) / 2:
+            // without the equalisation it is rounded at the larger one's magnitude)
+            equalize_pair(xa, xb, ksa, ksb);
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
                 const int m0 = 8 * lane + 512 * r;
@@ -546,18 +578,22 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
                 }
             }
         } else {
+            h8 xa[2], xb[2];
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                gate_product<T>(cur.q[r][0], cur.q[r][1], HAS_W, xa[r]);
+                gate_product<T>(cur.q[r][2], cur.q[r][3], HAS_W, xb[r]);
+                if (!has_b) xb[r] = h8{};
+            }
+            zero_rows(xa, xb, ksa, ksb);
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
                 const int m0 = 8 * lane + 512 * r;
-                h8 xa, xb;
-                gate_product<T>(cur.q[r][0], cur.q[r][1], HAS_W, xa);
-                gate_product<T>(cur.q[r][2], cur.q[r][3], HAS_W, xb);
-                if (!has_b) xb = h8{};
                 const int ns = m0 >> 5, nf0 = m0 & 31, kss = kslot_of(ns);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    zr[(nf0 + e) * kRow + kss] = xa[e];
-                    zi[(nf0 + e) * kRow + kss] = xb[e];
+                    zr[(nf0 + e) * kRow + kss] = xa[r][e];
+                    zi[(nf0 + e) * kRow + kss] = xb[r][e];
                 }
             }
         }
