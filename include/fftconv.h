@@ -111,7 +111,10 @@ int64_t fftconv_mask_blocks(int64_t N);
 /* Transform the time-domain filter k (H, L_filter) into K_f for sequences of
  * length N: K_f holds rfft(pad(k, 2N)) ("Approach": the filter spectrum the
  * convolution multiplies by; partial convolution = L_filter < N, where only
- * the input blocks holding taps are transformed).  Needs workspace of
+ * the L_filter taps are read and the padding is implicit).  fp16 / bf16 at
+ * N = 2048 .. 16384 transform on the matrix cores with fp16 stages (about
+ * 1e-3 relative error of the stored spectrum, like the forward call's own
+ * stages); other sizes and fp32 in fp32.  Needs workspace of
  * fftconv_workspace_bytes(1, H, N, dtype) bytes for N beyond the on-chip
  * size.  K_f_bytes must be >= fftconv_filter_bytes(H, N, dtype). */
 fftconv_status_t fftconv_prepare_filter(const void *k, int64_t H, int64_t L_filter, int64_t N,

@@ -628,7 +628,10 @@ static fftconv_status_t prepare_impl(const void *k, int64_t H, int64_t L, int64_
         e = launch_filter_scale(dtype, k, H, L, kf_norm_log2(l, dtype), kf_target_log2(l, dtype), kscale,
                                 stream);
     if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "filter setup launch: %s", hipGetErrorString(e));
-    if (fused) {
+    if (fused && use_pair3_kernel(l, dtype) && !conj) {
+        // N = 2048 .. 16384, half precision: the transform of the N = 16384 kernels
+        e = launch_pair16k_prepare(l, dtype, k, L, kbins, kscale, H, stream);
+    } else if (fused) {
         Tables tb{};
         e = get_tables(l, &tb);
         if (e == hipSuccess) e = launch_fused_prepare(l, dtype, k, L, kbins, kscale, tb, H, ysgn, stream);

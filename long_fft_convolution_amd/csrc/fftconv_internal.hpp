@@ -248,6 +248,11 @@ constexpr size_t kP16SpecBytes = (size_t)32 * 2 * 2 * 64 * 16;
 hipError_t launch_pair16k_dk(int logn, int st, const void *dy, const void *u, const void *w, const void *v,
                              void *part, void *spec, float *pscale, const uint8_t *mask, int64_t B,
                              int64_t H, hipStream_t stream);
+// The filter prepare of the N = 2048 .. 16384 half-precision layout (KF_PAIR3) on the
+// matrix cores: the bins of H channels from taps k[H][L], with kscale[h] already written
+// by the scale kernel (read here).
+hipError_t launch_pair16k_prepare(int logn, int st, const void *k, int64_t L, void *kbins, const float *kscale,
+                                  int64_t H, hipStream_t stream);
 // with out2: also out2 = v2 * conv(u w, k) from the same transforms (v and v2 non-null)
 hipError_t launch_pair_conv(int logn, int st, const void *u, const void *w, const void *v,
                             void *out, const void *kbins, const float *kscale, const uint8_t *mask,

@@ -103,8 +103,16 @@ static_assert(kWaves == 8, "the LDS address split below assumes 8 waves");
 // in the order in which the product step reads it.  kCorr: the convolution with such a
 // per-pair spectrum in place of K_f, keeping only the real part of the result (the
 // backward pass's filter gradient: with z_x = x_a + i x_b and z_g = g_a + i g_b,
-// Re IDFT(conj(Z_x) Z_g) = corr(g_a, x_a) + corr(g_b, x_b)).
-constexpr int kConv = 0, kSpec = 1, kCorr = 2;
+// Re IDFT(conj(Z_x) Z_g) = corr(g_a, x_a) + corr(g_b, x_b)).  kPrep: the filter prepare,
+// the forward transform of each channel's zero-padded taps k (one sequence per sub-pair,
+// no second row) stored as the prepared spectrum K s_h of that channel (rows f_c <= R/2
+// of the KF_PAIR3 layout), with s_h = 2^e from the channel scale already written.
+constexpr int kConv = 0, kSpec = 1, kCorr = 2, kPrep = 3;
+// kPrep: the taps enter the transform scaled by s_h 2^kPrepInLog2, so that sum |k s_h| <= 1
+// becomes sum |x| <= 2^14: every stage result stays below 2^14 (a DFT output is at most the
+// sum of its inputs' magnitudes, and the table factors only shrink it) while the taps of a
+// long filter stay in fp16's normal range (about 2^14 / L each)
+constexpr int kPrepInLog2 = 14;
 constexpr int kSpecRows = 32 * 2 * 2 * 64;   // uint4 per pair spectrum (all rows f_c)
 
 // filter chunk of row fc (of R = 2^LOGR) for (mt2, nt): rows f_c <= R/2 as stored, the
@@ -140,9 +148,11 @@ using namespace p16;
 // DUAL: a second output out2 = v2 * conv(u w, k) from the same transforms (the backward
 // pass forms du and dw in one call); the second gate's rows are loaded once the staged
 // outputs have freed their registers.
-// MODE (kConv, kSpec, kCorr) above.  kSpec writes spec_out[p] (all 32 rows of the
+// MODE (kConv, kSpec, kCorr, kPrep) above.  kSpec writes spec_out[p] (all 32 rows of the
 // workgroup) for group p and scale_out[p P + sp] for its sub-pair sp; kCorr reads them
 // through kbins and kscale and writes the rows bp H + h (h: the group's channels) of out.
+// kPrep (B = 1): u is the taps k[H][Lk], kscale the channel scales, and spec_out the bins
+// of the prepared filter (channel h at h (R/2 + 1) 256 uint4).
 // LOGR < 5 (N = 512 R = 2048, 4096, 8192): the 2N-point transform is R = 2^LOGR outer
 // rows of 1024; P = 32 / R pairs of P consecutive channels (the same batch rows) share a
 // workgroup's 32 rows (sub-pair p = row / R, f_c = row mod R), so phase 2 is unchanged.
@@ -155,12 +165,14 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                T *__restrict__ out, const uint4 *__restrict__ kbins, const float *__restrict__ kscale,
                const uint8_t *__restrict__ mask, Pair3Tables tb, int64_t B, int64_t H,
                const T *__restrict__ v2, T *__restrict__ out2, uint4 *__restrict__ spec_out,
-               float *__restrict__ scale_out, P16Outer ot) {
+               float *__restrict__ scale_out, P16Outer ot, int64_t Lk) {
     static_assert(!DUAL || HAS_V, "a second output has an output gate of its own");
     static_assert(MODE == kConv || (!DUAL && !HAS_V), "the spectrum and correlation modes have no output gate");
     static_assert(MODE != kSpec || !MASKED, "the spectrum mode stores every bin");
+    static_assert(MODE != kPrep || (!MASKED && !HAS_W), "the prepare mode transforms the taps alone");
     static_assert(LOGR >= 2 && LOGR <= 5, "R = 4 .. 32");
-    constexpr bool SPEC = MODE == kSpec, CORR = MODE == kCorr;
+    constexpr bool SPEC = MODE == kSpec, CORR = MODE == kCorr, PREP = MODE == kPrep;
+    constexpr bool CONV = MODE == kConv, FWD = SPEC || PREP;   // FWD: forward transform only
     constexpr int R = 1 << LOGR, P = 32 / R, NCH = R / 2;   // outer rows, sub-pairs, non-zero n_c
     constexpr int N = 512 * R;
     constexpr int M2 = 2 * N;
@@ -267,7 +279,29 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
     // are tested), per row and (R = 4, where the two slot halves j < 2, j >= 2 belong to two
     // sub-pairs) slot half
     uint32_t nz[2][2] = {{0u, 0u}, {0u, 0u}};
+    // kPrep: the input factor s_h 2^kPrepInLog2 of the channel of slot 4 g + j
+    float pin[4] = {0.f, 0.f, 0.f, 0.f};
     auto load_batch = [&](int64_t oa_, int64_t ob_, int half, Batch &x, int nv_) {
+        if constexpr (PREP) {
+            // slot 4 g + j: sub-pair sp (channel ch0 + sp), n_c; element n_ab + 1024 n_c of
+            // the taps row, zero at n >= Lk and past the group's channels
+            const int64_t ch0 = oa_ >> (9 + LOGR);   // (B = 1: oa_ = first channel * N)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int sp = P > 1 ? (4 * g + j) / NCH : 0, nc = P > 1 ? (4 * g + j) % NCH : 4 * g + j;
+                const bool okc = sp < nv_;
+                const uint16_t *row = reinterpret_cast<const uint16_t *>(u + (ch0 + (okc ? sp : 0)) * Lk);
+#pragma unroll
+                for (int qq = 0; qq < 2; ++qq) {
+                    const int64_t n = 16 * kTilesPerWave * wave + 32 * (2 * half + qq) + 2 * c + 1024 * nc;
+                    const uint32_t lo = okc && n < Lk ? (uint32_t)row[n] : 0u;
+                    const uint32_t hi = okc && n + 1 < Lk ? (uint32_t)row[n + 1] : 0u;
+                    x.xa[qq][j] = lo | (hi << 16);
+                    x.xb[qq][j] = 0u;
+                }
+            }
+            return;
+        }
         const uint32_t *pua = reinterpret_cast<const uint32_t *>(u + oa_);
         const uint32_t *pub = reinterpret_cast<const uint32_t *>(u + ob_);
         const uint32_t *pwa = reinterpret_cast<const uint32_t *>(w + oa_);
@@ -321,13 +355,14 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                         xa *= st<T>::cvt_half(x.ga[qq][j], par);
                         xb *= st<T>::cvt_half(x.gb[qq][j], par);
                     }
+                    if (PREP) xa *= pin[j];
                     br[j] = (_Float16)xa;
                     bi[j] = hb_ ? (_Float16)xb : (_Float16)0.f;
                     br[4 + j] = (_Float16)0.f;
                     bi[4 + j] = (_Float16)0.f;
                     if (SPEC || CORR) l1j[j] += fabsf((float)br[j]) + fabsf((float)bi[j]);
                 }
-                if (!SPEC && !CORR) {
+                if (CONV) {
                     const uint4 qa = *reinterpret_cast<const uint4 *>(&br), qb = *reinterpret_cast<const uint4 *>(&bi);
                     if constexpr (NCH >= 4) {
                         nz[0][0] |= qa.x | qa.y;
@@ -391,7 +426,14 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
     for (; p < p_end; p += wg_on_xcd) {
         const int64_t h = __builtin_amdgcn_readfirstlane((uint32_t)p / (uint32_t)PB);   // channel group
         // (the six stages' table factors are undone with the channel scale; kCorr: the pair's)
-        const float ks = (SPEC || CORR) ? 1.f : __builtin_ldexpf(kscale[h], 6 * kDft32Log2);
+        const float ks = CONV ? __builtin_ldexpf(kscale[h], 6 * kDft32Log2) : 1.f;
+        if constexpr (PREP) {   // s_h = 1 / (kscale 2N), times 2^kPrepInLog2
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int sp = P > 1 ? (4 * g + j) / NCH : 0;
+                pin[j] = __builtin_ldexpf(1.f / kscale[h * P + (sp < nv ? sp : 0)], kPrepInLog2 - (10 + LOGR));
+            }
+        }
         const int64_t oo = CORR ? ((p - h * PB) * H + h * P) * N : 0;   // kCorr output row
         int64_t p_nx = p + wg_on_xcd, oa_nx, ob_nx;
         bool hb_nx;
@@ -424,7 +466,7 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
 #pragma unroll
             for (int j = 0; j < 4; ++j) l1j[j] = 0.f;
         }
-        if (!SPEC && !CORR) {   // this wave's non-zero rows of sub-pairs, ORed into s_zf
+        if (CONV) {   // this wave's non-zero rows of sub-pairs, ORed into s_zf
             uint32_t seen = 0u;   // (wave-uniform: built from the ballots)
 #pragma unroll
             for (int row = 0; row < 2; ++row)
@@ -445,7 +487,7 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
         // kConv: a row of a sub-pair whose inputs are all zero has the result 0, not the
         // rounding of its partner row's values: zrow bit 8 row + sp marks it
         uint32_t zrow = 0u;
-        if (!SPEC && !CORR) {
+        if (CONV) {
             constexpr uint32_t kRows = ((1u << P) - 1u) * 0x101u;
             zrow = __builtin_amdgcn_readfirstlane(~*s_zf & kRows);
         }
@@ -516,7 +558,7 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
         // the filter row read for row rho (kCorr: rho itself)
         auto krow = [&](int rho) -> int { return CORR ? rho : rowfc(rho); };
         uint4 kq[2][2];
-        if (!SPEC) {
+        if (!FWD) {
 #pragma unroll
             for (int mt2 = 0; mt2 < 2; ++mt2)
 #pragma unroll
@@ -537,7 +579,7 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
             uint32_t lx = ul;
             asm volatile("" : "+v"(lx));
             h8 kk[2][2], two[2][2];
-            if (!SPEC) {
+            if (!FWD) {
 #pragma unroll
                 for (int mt2 = 0; mt2 < 2; ++mt2)
 #pragma unroll
@@ -589,6 +631,18 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                 for (int mt2 = 0; mt2 < 2; ++mt2) {
                     f4 cr, ci;
                     cm_constA(Fr[mt2], Fi[mt2], nFi[mt2], br, bi, cr, ci);   // rows f_a, cols f_b
+                    if (PREP) {   // K s_h: rows f_c <= R/2 of the channel's KF_PAIR3 bins
+                        constexpr int kFwd = R == 32 ? 3 * kDft32Log2 : 2 * kDft32Log2 + p16_outer_log2(LOGR);
+                        constexpr float kOut = kFwd >= kPrepInLog2 ? (float)(1u << (kFwd - kPrepInLog2))
+                                                                   : 1.f / (float)(1u << (kPrepInLog2 - kFwd));
+                        const int spr = fc >> LOGR;
+                        if (rowfc(fc) <= R / 2 && spr < nv) {
+                            const h8 q = cat8(to_h4(cr * kOut), to_h4(ci * kOut));
+                            stu(spec_out + chan(h, spr) * (int64_t)kKRows + ((rowfc(fc) * 2 + mt2) * 2 + nt) * 64,
+                                16u * lx, q);
+                        }
+                        continue;
+                    }
                     if (SPEC) {   // conj(Z) 2^e in the order the product step reads it
                         const h8 q = cat8(to_h4(cr * sc[r]), to_h4(ci * -sc[r]));
                         stu(spec_out + p * (int64_t)kSpecRows + ((fc * 2 + mt2) * 2 + nt) * 64, 16u * lx, q);
@@ -619,7 +673,7 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                     cmul4(yr[mt2][nt], yi[mt2][nt], kf);
                 }
             }
-            if (SPEC) continue;
+            if (FWD) continue;
             // S2': data A = T2^T (M = f_b tiles nt, K = f_a), const B conj F[nt2] (N = n_a); conj twiddle
             h4 t3r[2][2], t3i[2][2];
 #pragma unroll
@@ -654,7 +708,7 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                 }
             }
         }
-        if (SPEC) {   // no inverse: the next pair's second input batch, then the next pair
+        if (FWD) {   // no inverse: the next pair's second input batch, then the next pair
             load_batch(oa_nx, ob_nx, 1, x1, nv_nx);
             __syncthreads();
             oa = oa_nx;
@@ -812,7 +866,7 @@ static hipError_t pair16k_conv_r(int st_, const void *u, const void *w, const vo
         if (err != hipSuccess) return err;
         hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * kWaves), lds, stream, (const TT *)u,
                            (const TT *)w, (const TT *)v, (TT *)out, (const uint4 *)kbins, kscale, mask, tb,
-                           B, H, (const TT *)v2, (TT *)out2, (uint4 *)nullptr, (float *)nullptr, ot);
+                           B, H, (const TT *)v2, (TT *)out2, (uint4 *)nullptr, (float *)nullptr, ot, (int64_t)0);
         return hipGetLastError();
     };
     // one instantiation per (storage type, mask, gates) so that no gate test sits in the loops
@@ -877,7 +931,7 @@ static hipError_t pair16k_dk_r(int st_, const void *dy, const void *u, const voi
         if (err != hipSuccess) return err;
         hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * kWaves), kP16Lds, stream, (const TT *)in,
                            (const TT *)gate, (const TT *)nullptr, (TT *)o, (const uint4 *)kb, ksc, m, tb, B, H,
-                           (const TT *)nullptr, (TT *)nullptr, (uint4 *)spec, pscale, ot);
+                           (const TT *)nullptr, (TT *)nullptr, (uint4 *)spec, pscale, ot, (int64_t)0);
         return hipGetLastError();
     };
     auto pick = [&](auto *tp) -> hipError_t {
@@ -915,6 +969,44 @@ hipError_t launch_pair16k_dk(int logn, int st_, const void *dy, const void *u, c
     case 12: return pair16k_dk_r<3>(st_, dy, u, w, v, part, spec, pscale, mask, B, H, stream);
     case 13: return pair16k_dk_r<4>(st_, dy, u, w, v, part, spec, pscale, mask, B, H, stream);
     case 14: return pair16k_dk_r<5>(st_, dy, u, w, v, part, spec, pscale, mask, B, H, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// Filter prepare on the matrix cores (KF_PAIR3 bins of H channels from taps k[H][L]); the
+// channel scales kscale[h] are read, not written (the scale kernel runs first).
+template <int LOGR>
+static hipError_t pair16k_prep_r(int st_, const void *k, int64_t L, void *kbins, const float *kscale, int64_t H,
+                                 hipStream_t stream) {
+    Pair3Tables tb{};
+    hipError_t e = get_pair3_tables(&tb);
+    if (e != hipSuccess) return e;
+    int64_t blocks = 0;
+    if ((e = p16_grid(1, H, &blocks, LOGR)) != hipSuccess) return e;
+    const P16Outer ot = p16_outer(tb, LOGR);
+    auto go = [&](auto kern, auto *tp) -> hipError_t {
+        using TT = std::remove_pointer_t<decltype(tp)>;
+        hipError_t err = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)kP16Lds);
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * kWaves), kP16Lds, stream, (const TT *)k,
+                           (const TT *)nullptr, (const TT *)nullptr, (TT *)nullptr, (const uint4 *)nullptr, kscale,
+                           (const uint8_t *)nullptr, tb, (int64_t)1, H, (const TT *)nullptr, (TT *)nullptr,
+                           (uint4 *)kbins, (float *)nullptr, ot, L);
+        return hipGetLastError();
+    };
+    if (st_ == ST_F16) return go(pair16k_kernel<__half, false, false, false, false, kPrep, LOGR>, (__half *)nullptr);
+    return go(pair16k_kernel<__hip_bfloat16, false, false, false, false, kPrep, LOGR>, (__hip_bfloat16 *)nullptr);
+}
+
+hipError_t launch_pair16k_prepare(int logn, int st_, const void *k, int64_t L, void *kbins, const float *kscale,
+                                  int64_t H, hipStream_t stream) {
+    if (st_ == ST_F32 || L < 1 || L > (int64_t(1) << logn)) return hipErrorInvalidValue;
+    switch (logn) {
+    case 11: return pair16k_prep_r<2>(st_, k, L, kbins, kscale, H, stream);
+    case 12: return pair16k_prep_r<3>(st_, k, L, kbins, kscale, H, stream);
+    case 13: return pair16k_prep_r<4>(st_, k, L, kbins, kscale, H, stream);
+    case 14: return pair16k_prep_r<5>(st_, k, L, kbins, kscale, H, stream);
     default: return hipErrorInvalidValue;
     }
 }
