@@ -804,8 +804,10 @@ static BwdLayout bwd_layout(int64_t B, int64_t H, int64_t N, fftconv_dtype_t dty
         return at;
     };
     o.kc = take(fftconv_filter_bytes(H, N, dtype));
-    // N = 1024 (fp16 / bf16): du, dw and dk come from kernels that need no scratch beyond
-    // the conjugated spectrum (the dk chain's areas below are then empty)
+    // (kc: the conjugated spectrum, used when only one of du, dw is asked for or outside the
+    // matrix-core sizes; the two-output call conjugates the bins as it reads them)
+    // N = 1024 (fp16 / bf16): du, dw and dk come from kernels that need no other scratch
+    // (the dk chain's areas below are then empty)
     // N = 2048 .. 16384 (fp16 / bf16): per-group spectra of the batch-row pairs of u*w
     // (a group is the 2^(14 - log2 N) channels of one workgroup) and one partial row per pair
     const int l = log2_exact(N);
@@ -890,24 +892,31 @@ fftconv_status_t fftconv_bwd(const void *dy, const void *u, const void *K_f, con
     void *fws = ws + lay.fws;
     const size_t fws_bytes = lay.total - lay.fws;
     fftconv_status_t st = FFTCONV_OK;
+    // N = 2048 .. 16384 (fp16 / bf16) with dk: the dk chain below; at N = 16384 its first
+    // pass also forms dv from the same transforms of u w
+    const bool p16dk = dk && B > 0 && use_pair3_kernel(l, dtype);
+    const bool dv_in_dk = p16dk && dv && l == 14;
     // dv = dy * conv(u w, k): the forward pass with dy as the output gate
-    if (dv && B > 0) {
+    if (dv && B > 0 && !dv_in_dk) {
         st = fftconv_fwd(u, K_f, w, dy, dv, B, H, N, L, mask, dtype, fws, fws_bytes, stream);
         if (st != FFTCONV_OK) return st;
     }
-    // du = w * corr(v dy, k), dw = u * corr(v dy, k): conjugated spectrum
+    // du = w * corr(v dy, k), dw = u * corr(v dy, k): the product with conj K
     if ((du || dw) && B > 0) {
-        hipError_t e = conj_spectrum(K_f, ws + lay.kc, H, N, dtype, stream);
-        if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "conjugating K_f: %s", hipGetErrorString(e));
+        hipError_t e = hipSuccess;
         if (du && dw && (use_pair_kernel(l, dtype) || use_pair3_kernel(l, dtype))) {
-            // N = 1024, 16384: one call forms both from the same transforms
-            const char *kb = ws + lay.kc;
+            // N = 1024 .. 16384 (fp16 / bf16): one call forms both from the same transforms,
+            // conjugating the stored spectrum as it reads it
+            const char *kb = static_cast<const char *>(K_f);
             const float *ksc = reinterpret_cast<const float *>(kb + kf_scale_off());
             e = use_pair_kernel(l, dtype)
                     ? launch_pair_conv(l, dtype, dy, v, w, du, kb + kf_bins_off(H), ksc, mask, B, H, stream, u, dw)
                     : launch_pair16k_conv(l, dtype, dy, v, w, du, kb + kf_bins_off(H), ksc, mask, B, H, stream, u, dw);
             if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "du, dw: %s", hipGetErrorString(e));
         } else {
+            // otherwise the forward call on a conjugated copy of the spectrum
+            e = conj_spectrum(K_f, ws + lay.kc, H, N, dtype, stream);
+            if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "conjugating K_f: %s", hipGetErrorString(e));
             if (du) {
                 st = fftconv_fwd(dy, ws + lay.kc, v, w, du, B, H, N, L, mask, dtype, fws, fws_bytes, stream);
                 if (st != FFTCONV_OK) return st;
@@ -923,10 +932,14 @@ fftconv_status_t fftconv_bwd(const void *dy, const void *u, const void *K_f, con
     if (dk && B > 0 && use_pair_kernel(l, dtype)) {
         hipError_t e = launch_pair_dk(dtype, dy, u, w, v, dk, mask, B, H, L, stream);
         if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "dk: %s", hipGetErrorString(e));
-    } else if (dk && B > 0 && use_pair3_kernel(l, dtype)) {
-        // N = 2048 .. 16384 (fp16 / bf16): the pairs' spectra of u w, then one correlation per pair
+    } else if (p16dk) {
+        // N = 2048 .. 16384 (fp16 / bf16): the pairs' spectra of u w (at N = 16384 with dv
+        // from the same transforms), then one correlation per pair
+        const char *kb = static_cast<const char *>(K_f);
         hipError_t e = launch_pair16k_dk(l, dtype, dy, u, w, v, ws + lay.part, ws + lay.spec,
-                                         reinterpret_cast<float *>(ws + lay.pscale), mask, B, H, stream);
+                                         reinterpret_cast<float *>(ws + lay.pscale), mask, B, H, stream,
+                                         dv_in_dk ? dv : nullptr,
+                                         kb + kf_bins_off(H), reinterpret_cast<const float *>(kb + kf_scale_off()));
         if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "dk pairs: %s", hipGetErrorString(e));
         e = launch_dk_reduce(dtype, ws + lay.part, dk, (B + 1) / 2, H, N, L, stream);
         if (e != hipSuccess) return fail(FFTCONV_ERR_HIP, "dk reduction: %s", hipGetErrorString(e));

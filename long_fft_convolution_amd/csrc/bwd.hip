@@ -63,22 +63,56 @@ mask_repeat_kernel(const uint8_t *__restrict__ mask, uint8_t *__restrict__ dst, 
     dst[c * kMaskBlocks + threadIdx.x] = mask[(c % H) * kMaskBlocks + threadIdx.x];
 }
 
-// dk[h, s] = sum_b part[b H + h, s] for s < L (fp32 sum, rounded once to T)
+// dk[h, s] = sum_b part[b H + h, s] for s < L (fp32 sum, rounded once to T).  Grid
+// (ceil(L / 2048), channels): a thread sums 8 consecutive s of one channel, one 16-byte
+// load per partial row (two for fp32; rows are N-element aligned and s0 + 8 <= N).
+template <typename T> __device__ __forceinline__ void load8f(const T *p, float *o);
+template <> __device__ __forceinline__ void load8f<float>(const float *p, float *o) {
+    const float4 a = *reinterpret_cast<const float4 *>(p), b = *reinterpret_cast<const float4 *>(p + 4);
+    o[0] = a.x, o[1] = a.y, o[2] = a.z, o[3] = a.w, o[4] = b.x, o[5] = b.y, o[6] = b.z, o[7] = b.w;
+}
+template <> __device__ __forceinline__ void load8f<__half>(const __half *p, float *o) {
+    const uint4 q = *reinterpret_cast<const uint4 *>(p);
+    const __half *hv = reinterpret_cast<const __half *>(&q);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = __half2float(hv[i]);
+}
+template <> __device__ __forceinline__ void load8f<__hip_bfloat16>(const __hip_bfloat16 *p, float *o) {
+    const uint4 q = *reinterpret_cast<const uint4 *>(p);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        o[2 * i] = __uint_as_float(w[i] << 16);
+        o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256)
 dk_reduce_kernel(const T *__restrict__ part, T *__restrict__ dk, int64_t B, int64_t H, int64_t N,
                  int64_t L) {
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < H * L; i += (int64_t)gridDim.x * 256) {
-        const int64_t h = i / L, s = i - h * L;
-        float acc = 0.f;
-#pragma unroll 8
-        for (int64_t b = 0; b < B; ++b) acc += io<T>::load1(part + (b * H + h) * N + s);
-        if constexpr (std::is_same<T, float>::value) {
-            dk[i] = acc;
-        } else if constexpr (std::is_same<T, __half>::value) {
-            dk[i] = __float2half_rn(acc);
-        } else {
-            dk[i] = __float2bfloat16(acc);
+    const int64_t s0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+    if (s0 >= L) return;
+    const int n = L - s0 < 8 ? (int)(L - s0) : 8;
+    for (int64_t h = blockIdx.y; h < H; h += gridDim.y) {
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int64_t b = 0; b < B; ++b) {
+            float x[8];
+            load8f<T>(part + (b * H + h) * N + s0, x);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] += x[i];
+        }
+        T *o = dk + h * L + s0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (i >= n) break;
+            if constexpr (std::is_same<T, float>::value) {
+                o[i] = acc[i];
+            } else if constexpr (std::is_same<T, __half>::value) {
+                o[i] = __float2half_rn(acc[i]);
+            } else {
+                o[i] = __float2bfloat16(acc[i]);
+            }
         }
     }
 }
@@ -122,7 +156,8 @@ hipError_t launch_mask_repeat(const uint8_t *mask, uint8_t *dst, int64_t H, int6
 
 hipError_t launch_dk_reduce(int st, const void *part, void *dk, int64_t B, int64_t H, int64_t N, int64_t L,
                             hipStream_t stream) {
-    const dim3 grid(grid_for(H * L));
+    if (H < 1 || L < 1) return hipSuccess;
+    const dim3 grid((unsigned)((L + 2047) / 2048), (unsigned)(H < 65535 ? H : 65535));
     switch (st) {
     case ST_F32:
         hipLaunchKernelGGL(dk_reduce_kernel<float>, grid, dim3(256), 0, stream, (const float *)part,

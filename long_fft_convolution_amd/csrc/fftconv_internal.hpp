@@ -235,7 +235,8 @@ struct P16Outer {
 // power-of-two factor 2^-p16_outer_log2(logr) folded into each outer-stage table
 inline __host__ __device__ constexpr int p16_outer_log2(int logr) { return logr >= 4 ? 2 : 1; }
 hipError_t get_pair3_tables(Pair3Tables *out);
-// with out2: also out2 = v2 * conv(u w, k) from the same transforms (v and v2 non-null)
+// with out2: the adjoint with two outputs, out = v * corr(u w, k) and out2 = v2 * corr(u w, k)
+// from the same transforms (v and v2 non-null; kbins is the spectrum of k, conjugated as read)
 hipError_t launch_pair16k_conv(int logn, int st, const void *u, const void *w, const void *v, void *out,
                                const void *kbins, const float *kscale, const uint8_t *mask,
                                int64_t B, int64_t H, hipStream_t stream, const void *v2 = nullptr,
@@ -245,15 +246,20 @@ hipError_t launch_pair16k_conv(int logn, int st, const void *u, const void *w, c
 // workgroup group (ceil(H / P) ceil(B/2) groups, P = 2^(14 - logn) channels) and pscale
 // P floats per group (one per pair of batch rows and channel)
 constexpr size_t kP16SpecBytes = (size_t)32 * 2 * 2 * 64 * 16;
+// With dv (N = 16384 only; kbins, kscale: the prepared filter's bins and scales): the first
+// launch also forms dv = dy * conv(u w, k), masked like the forward call, from the same
+// transforms.
 hipError_t launch_pair16k_dk(int logn, int st, const void *dy, const void *u, const void *w, const void *v,
                              void *part, void *spec, float *pscale, const uint8_t *mask, int64_t B,
-                             int64_t H, hipStream_t stream);
+                             int64_t H, hipStream_t stream, void *dv = nullptr, const void *kbins = nullptr,
+                             const float *kscale = nullptr);
 // The filter prepare of the N = 2048 .. 16384 half-precision layout (KF_PAIR3) on the
 // matrix cores: the bins of H channels from taps k[H][L], with kscale[h] already written
 // by the scale kernel (read here).
 hipError_t launch_pair16k_prepare(int logn, int st, const void *k, int64_t L, void *kbins, const float *kscale,
                                   int64_t H, hipStream_t stream);
-// with out2: also out2 = v2 * conv(u w, k) from the same transforms (v and v2 non-null)
+// with out2: the adjoint with two outputs, out = v * corr(u w, k) and out2 = v2 * corr(u w, k)
+// from the same transforms (v and v2 non-null; kbins is the spectrum of k, conjugated as read)
 hipError_t launch_pair_conv(int logn, int st, const void *u, const void *w, const void *v,
                             void *out, const void *kbins, const float *kscale, const uint8_t *mask,
                             int64_t B, int64_t H, hipStream_t stream, const void *v2 = nullptr,

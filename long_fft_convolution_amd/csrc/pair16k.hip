@@ -107,7 +107,9 @@ static_assert(kWaves == 8, "the LDS address split below assumes 8 waves");
 // the forward transform of each channel's zero-padded taps k (one sequence per sub-pair,
 // no second row) stored as the prepared spectrum K s_h of that channel (rows f_c <= R/2
 // of the KF_PAIR3 layout), with s_h = 2^e from the channel scale already written.
-constexpr int kConv = 0, kSpec = 1, kCorr = 2, kPrep = 3;
+// kConvSpec: the convolution of kConv that also stores the pair's spectrum as kSpec does
+// (the backward pass takes dv and the spectra of u w from one pass over u, w).
+constexpr int kConv = 0, kSpec = 1, kCorr = 2, kPrep = 3, kConvSpec = 4;
 // kPrep: the taps enter the transform scaled by s_h 2^kPrepInLog2, so that sum |k s_h| <= 1
 // becomes sum |x| <= 2^14: every stage result stays below 2^14 (a DFT output is at most the
 // sum of its inputs' magnitudes, and the table factors only shrink it) while the taps of a
@@ -126,14 +128,22 @@ __device__ __forceinline__ uint4 k_load(const uint4 *kch, int fc, int mt2, int n
     const uint32_t row = mir ? R - fc : fc, a = mir ? 1 - mt2 : mt2, b = mir ? 1 - nt : nt;
     return ldu<uint4>(kch + ((row * 2 + a) * 2 + b) * 64, 16u * (mir ? 63 - lane : lane));
 }
+// (CONJ: the conjugate of that chunk, for the adjoint)
+template <bool CONJ = false>
 __device__ __forceinline__ h8 k_fix(const uint4 &q, bool mir) {
-    if (!mir) return *reinterpret_cast<const h8 *>(&q);
-    // (e0..e3 | e4..e7) -> (e3, e2, e1, e0 | -e7, -e6, -e5, -e4)
+    constexpr uint32_t sm = CONJ ? 0x80008000u : 0u, sn = CONJ ? 0u : 0x80008000u;
     uint4 t;
+    if (!mir) {
+        t = q;
+        t.z ^= sm;
+        t.w ^= sm;
+        return *reinterpret_cast<const h8 *>(&t);
+    }
+    // (e0..e3 | e4..e7) -> (e3, e2, e1, e0 | -e7, -e6, -e5, -e4)
     t.x = __builtin_amdgcn_alignbit(q.y, q.y, 16);
     t.y = __builtin_amdgcn_alignbit(q.x, q.x, 16);
-    t.z = __builtin_amdgcn_alignbit(q.w, q.w, 16) ^ 0x80008000u;
-    t.w = __builtin_amdgcn_alignbit(q.z, q.z, 16) ^ 0x80008000u;
+    t.z = __builtin_amdgcn_alignbit(q.w, q.w, 16) ^ sn;
+    t.w = __builtin_amdgcn_alignbit(q.z, q.z, 16) ^ sn;
     return *reinterpret_cast<const h8 *>(&t);
 }
 
@@ -145,9 +155,10 @@ using namespace p16;
 // XCD-local range of pairs p = h * ceil(B/2) + bp.  An odd B pairs its last row
 // with zeros: the second row's loads then re-read the first row (always in
 // bounds) and are discarded, so no load sits under a branch.
-// DUAL: a second output out2 = v2 * conv(u w, k) from the same transforms (the backward
-// pass forms du and dw in one call); the second gate's rows are loaded once the staged
-// outputs have freed their registers.
+// DUAL: the adjoint with two outputs, out = v corr(u w, k) and out2 = v2 corr(u w, k),
+// from the same transforms: the product takes conj K, the stored bins conjugated as they
+// are read (the backward pass forms du and dw in one call); the second gate's rows are
+// loaded once the staged outputs have freed their registers.
 // MODE (kConv, kSpec, kCorr, kPrep) above.  kSpec writes spec_out[p] (all 32 rows of the
 // workgroup) for group p and scale_out[p P + sp] for its sub-pair sp; kCorr reads them
 // through kbins and kscale and writes the rows bp H + h (h: the group's channels) of out.
@@ -167,12 +178,15 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                const T *__restrict__ v2, T *__restrict__ out2, uint4 *__restrict__ spec_out,
                float *__restrict__ scale_out, P16Outer ot, int64_t Lk) {
     static_assert(!DUAL || HAS_V, "a second output has an output gate of its own");
-    static_assert(MODE == kConv || (!DUAL && !HAS_V), "the spectrum and correlation modes have no output gate");
+    static_assert(MODE == kConv || MODE == kConvSpec || (!DUAL && !HAS_V),
+                  "the spectrum and correlation modes have no output gate");
+    static_assert(MODE != kConvSpec || !DUAL, "one output with the spectrum");
     static_assert(MODE != kSpec || !MASKED, "the spectrum mode stores every bin");
     static_assert(MODE != kPrep || (!MASKED && !HAS_W), "the prepare mode transforms the taps alone");
     static_assert(LOGR >= 2 && LOGR <= 5, "R = 4 .. 32");
     constexpr bool SPEC = MODE == kSpec, CORR = MODE == kCorr, PREP = MODE == kPrep;
-    constexpr bool CONV = MODE == kConv, FWD = SPEC || PREP;   // FWD: forward transform only
+    constexpr bool CONV = MODE == kConv || MODE == kConvSpec, FWD = SPEC || PREP;   // FWD: forward transform only
+    constexpr bool SPST = SPEC || MODE == kConvSpec;   // stores the pair's spectrum
     constexpr int R = 1 << LOGR, P = 32 / R, NCH = R / 2;   // outer rows, sub-pairs, non-zero n_c
     constexpr int N = 512 * R;
     constexpr int M2 = 2 * N;
@@ -360,7 +374,7 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                     bi[j] = hb_ ? (_Float16)xb : (_Float16)0.f;
                     br[4 + j] = (_Float16)0.f;
                     bi[4 + j] = (_Float16)0.f;
-                    if (SPEC || CORR) l1j[j] += fabsf((float)br[j]) + fabsf((float)bi[j]);
+                    if (SPST || CORR) l1j[j] += fabsf((float)br[j]) + fabsf((float)bi[j]);
                 }
                 if (CONV) {
                     const uint4 qa = *reinterpret_cast<const uint4 *>(&br), qb = *reinterpret_cast<const uint4 *>(&bi);
@@ -456,7 +470,7 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
             phase1_batch(x0, tw0, 0, has_b);
             phase1_batch(x1, tw1, 1, has_b);
         }
-        if (SPEC || CORR) {   // per slot: the sum over the 16 lanes of one g, then per wave
+        if (SPST || CORR) {   // per slot: the sum over the 16 lanes of one g, then per wave
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
 #pragma unroll
@@ -504,7 +518,7 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
         // lane then holds the exponent of the sub-pair of slot l (16 slots: n_c < NCH for
         // each of the P sub-pairs)
         int e_l = 0;
-        if (SPEC || CORR) {
+        if (SPST || CORR) {
             float t = 0.f;
             if (lane < 16) {
 #pragma unroll
@@ -524,12 +538,12 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
         float sc[kRowsPerWave];   // per phase-2 row rho = wave + 8 r: its sub-pair's 2^e
 #pragma unroll
         for (int r = 0; r < kRowsPerWave; ++r) sc[r] = 1.f;
-        if (SPEC || CORR) {
+        if (SPST || CORR) {
 #pragma unroll
             for (int r = 0; r < kRowsPerWave; ++r)
                 sc[r] = __builtin_ldexpf(1.f, sp_exp(R == 32 ? 0 : (wave + kWaves * r) >> LOGR));
         }
-        if (SPEC) {
+        if (SPST) {
             const int e_mine = sp_exp(lane < P ? lane : 0);   // (all lanes: a shuffle)
             if (tid < P) scale_out[p * P + tid] = __builtin_ldexpf(1.f, kF - e_mine - (10 + LOGR));
         }
@@ -583,7 +597,7 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
 #pragma unroll
                 for (int mt2 = 0; mt2 < 2; ++mt2)
 #pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) kk[mt2][nt] = k_fix(kq[mt2][nt], !CORR && rowfc(fc) > R / 2);
+                    for (int nt = 0; nt < 2; ++nt) kk[mt2][nt] = k_fix<DUAL>(kq[mt2][nt], !CORR && rowfc(fc) > R / 2);
                 if (r + 1 < kRowsPerWave) {
 #pragma unroll
                     for (int mt2 = 0; mt2 < 2; ++mt2)
@@ -643,10 +657,10 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                         }
                         continue;
                     }
-                    if (SPEC) {   // conj(Z) 2^e in the order the product step reads it
+                    if (SPST) {   // conj(Z) 2^e in the order the product step reads it
                         const h8 q = cat8(to_h4(cr * sc[r]), to_h4(ci * -sc[r]));
                         stu(spec_out + p * (int64_t)kSpecRows + ((fc * 2 + mt2) * 2 + nt) * 64, 16u * lx, q);
-                        continue;
+                        if (SPEC) continue;
                     }
                     if (CORR) {   // the spectrum of g scaled by its sub-pair's 2^e
                         cr *= sc[r];
@@ -911,12 +925,14 @@ hipError_t launch_pair16k_conv(int logn, int st_, const void *u, const void *w, 
 
 // Filter gradient partials at N = 16384: for every pair p = h ceil(B/2) + bp of batch rows
 // (2 bp, 2 bp + 1) of channel h, part[bp H + h] = corr(dy v, u w) summed over the two rows.
+// With dv (N = 16384 only): the first pass also forms dv = dy * conv(u w, k) from the filter
+// bins kbins, kscale (mode kConvSpec, masked like the forward call).
 // spec (ceil(B/2) H * 128 KiB) and pscale (ceil(B/2) H floats) hold the pairs' conjugated
 // spectra of u w between the two launches.
 template <int LOGR>
 static hipError_t pair16k_dk_r(int st_, const void *dy, const void *u, const void *w, const void *v, void *part,
                                void *spec, float *pscale, const uint8_t *mask, int64_t B, int64_t H,
-                               hipStream_t stream) {
+                               hipStream_t stream, void *dv, const void *kbins, const float *kscale) {
     Pair3Tables tb{};
     hipError_t e = get_pair3_tables(&tb);
     if (e != hipSuccess) return e;
@@ -934,12 +950,38 @@ static hipError_t pair16k_dk_r(int st_, const void *dy, const void *u, const voi
                            (const TT *)nullptr, (TT *)nullptr, (uint4 *)spec, pscale, ot, (int64_t)0);
         return hipGetLastError();
     };
+    // the first pass with dv: kConvSpec, dv = dy * conv(u w, k) with dy as the output gate
+    auto go_cs = [&](auto kern, auto *tp) -> hipError_t {
+        using TT = std::remove_pointer_t<decltype(tp)>;
+        hipError_t err = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)kP16Lds);
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * kWaves), kP16Lds, stream, (const TT *)u,
+                           (const TT *)w, (const TT *)dy, (TT *)dv, (const uint4 *)kbins, kscale, mask, tb, B, H,
+                           (const TT *)nullptr, (TT *)nullptr, (uint4 *)spec, pscale, ot, (int64_t)0);
+        return hipGetLastError();
+    };
     auto pick = [&](auto *tp) -> hipError_t {
         using TT = std::remove_pointer_t<decltype(tp)>;
-        hipError_t err = w ? go(pair16k_kernel<TT, false, true, false, false, kSpec, LOGR>, tp, u, w, nullptr,
-                                nullptr, nullptr, nullptr)
-                           : go(pair16k_kernel<TT, false, false, false, false, kSpec, LOGR>, tp, u, nullptr,
-                                nullptr, nullptr, nullptr, nullptr);
+        hipError_t err = hipSuccess;
+        if (dv != nullptr) {
+            // (N = 16384 only: at R < 32 the combined variants spill 14 to 32 registers)
+            if constexpr (LOGR == 5) {
+                switch ((mask ? 2 : 0) | (w ? 1 : 0)) {
+                case 0: err = go_cs(pair16k_kernel<TT, false, false, true, false, kConvSpec, LOGR>, tp); break;
+                case 1: err = go_cs(pair16k_kernel<TT, false, true, true, false, kConvSpec, LOGR>, tp); break;
+                case 2: err = go_cs(pair16k_kernel<TT, true, false, true, false, kConvSpec, LOGR>, tp); break;
+                default: err = go_cs(pair16k_kernel<TT, true, true, true, false, kConvSpec, LOGR>, tp); break;
+                }
+            } else {
+                return hipErrorInvalidValue;
+            }
+        } else {
+            err = w ? go(pair16k_kernel<TT, false, true, false, false, kSpec, LOGR>, tp, u, w, nullptr, nullptr,
+                         nullptr, nullptr)
+                    : go(pair16k_kernel<TT, false, false, false, false, kSpec, LOGR>, tp, u, nullptr, nullptr,
+                         nullptr, nullptr, nullptr);
+        }
         if (err != hipSuccess) return err;
         switch ((mask ? 2 : 0) | (v ? 1 : 0)) {
         case 0:
@@ -962,13 +1004,13 @@ static hipError_t pair16k_dk_r(int st_, const void *dy, const void *u, const voi
 
 hipError_t launch_pair16k_dk(int logn, int st_, const void *dy, const void *u, const void *w, const void *v,
                              void *part, void *spec, float *pscale, const uint8_t *mask, int64_t B,
-                             int64_t H, hipStream_t stream) {
-    if (st_ == ST_F32) return hipErrorInvalidValue;
+                             int64_t H, hipStream_t stream, void *dv, const void *kbins, const float *kscale) {
+    if (st_ == ST_F32 || (dv != nullptr && (kbins == nullptr || kscale == nullptr))) return hipErrorInvalidValue;
     switch (logn) {
-    case 11: return pair16k_dk_r<2>(st_, dy, u, w, v, part, spec, pscale, mask, B, H, stream);
-    case 12: return pair16k_dk_r<3>(st_, dy, u, w, v, part, spec, pscale, mask, B, H, stream);
-    case 13: return pair16k_dk_r<4>(st_, dy, u, w, v, part, spec, pscale, mask, B, H, stream);
-    case 14: return pair16k_dk_r<5>(st_, dy, u, w, v, part, spec, pscale, mask, B, H, stream);
+    case 11: return pair16k_dk_r<2>(st_, dy, u, w, v, part, spec, pscale, mask, B, H, stream, dv, kbins, kscale);
+    case 12: return pair16k_dk_r<3>(st_, dy, u, w, v, part, spec, pscale, mask, B, H, stream, dv, kbins, kscale);
+    case 13: return pair16k_dk_r<4>(st_, dy, u, w, v, part, spec, pscale, mask, B, H, stream, dv, kbins, kscale);
+    case 14: return pair16k_dk_r<5>(st_, dy, u, w, v, part, spec, pscale, mask, B, H, stream, dv, kbins, kscale);
     default: return hipErrorInvalidValue;
     }
 }

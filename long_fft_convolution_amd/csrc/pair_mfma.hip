@@ -298,8 +298,10 @@ __device__ __forceinline__ void equalize_pair(h8 (&xa)[2], h8 (&xb)[2], float &k
 // input fills the window: two K blocks, the second with DFT entries
 // w64^{(n_s + 32) f_s} = (-1)^{f_s} w64^{n_s f_s}) and S1' produces n_s = 32 .. 63
 // (entries conj w64^{f_s (n_s + 32)} = (-1)^{f_s} conj w64^{f_s n_s}).
-// DUAL: a second output out2 = v2 * conv(u w, k) of the same convolution (the backward
-// pass forms du = w corr(v dy, k) and dw = u corr(v dy, k) in one call).
+// DUAL: the adjoint with two outputs, out = v corr(u w, k) and out2 = v2 corr(u w, k)
+// from the same transforms: the product takes conj K, the stored spectrum conjugated
+// as it is read (the backward pass forms du = w corr(v dy, k) and dw = u corr(v dy, k)
+// in one call).
 // CORR (windows only): the adjoint of the windowed convolution, out[t] = sum_s k[s] x[t + s]
 // (the backward pass's corr(v dy, k) for the short filter).  Output block j needs the
 // input blocks j and j + 1: window j holds the samples j 1024 .. (j + 2) 1024 - 1 (zeros
@@ -455,7 +457,7 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
         // (the four stages' table factors are undone with the channel scale)
         fk.ks = __builtin_ldexpf(kscale[h], 2 * (kPairS1Log2 + kPairS2Log2));
         if (LONE) fk.ks2 = __builtin_ldexpf(kscale[hb ? h + 1 : h], 2 * (kPairS1Log2 + kPairS2Log2));
-        if (CORR) {   // conj K: the sign of the imaginary half (elements 4..7) of every chunk
+        if (CORR || DUAL) {   // conj K: the sign of the imaginary half (elements 4..7) of every chunk
 #pragma unroll
             for (int mt2 = 0; mt2 < 2; ++mt2)
 #pragma unroll
@@ -746,7 +748,13 @@ pair1k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__restr
                 h4 yr[2], yi[2];
 #pragma unroll
                 for (int mt2 = 0; mt2 < 2; ++mt2) {
-                    const uint4 q1 = krow1[(mt2 * 4 + nt) * 64 + lane], q2 = krow2[(mt2 * 4 + nt) * 64 + lane];
+                    uint4 q1 = krow1[(mt2 * 4 + nt) * 64 + lane], q2 = krow2[(mt2 * 4 + nt) * 64 + lane];
+                    if (DUAL) {   // conj K, conj K'
+                        q1.z ^= 0x80008000u;
+                        q1.w ^= 0x80008000u;
+                        q2.z ^= 0x80008000u;
+                        q2.w ^= 0x80008000u;
+                    }
                     h8 k1 = *reinterpret_cast<const h8 *>(&q1);
                     h8 k2 = *reinterpret_cast<const h8 *>(&q2);
                     h4 zr, zi, mr, mi;

@@ -270,3 +270,34 @@ def test_bwd_gated_bf16_n16k_full_size():
                           sub(inp.f64("v")))
     for name, a, b in zip(("du", "dk", "dw", "dv"), got, want):
         check(a[hs] if name == "dk" else a[:, hs], b, TOL["bf16"], f"{name} channels {list(hs)}")
+
+
+@pytest.mark.parametrize("dtype,N,B,H,masked", [("f16", 1024, 3, 6, False), ("bf16", 16384, 3, 5, False),
+                                                ("bf16", 16384, 2, 3, True), ("f16", 8192, 2, 5, False)])
+def test_bwd_gradient_subsets(dtype, N, B, H, masked):
+    # each gradient asked for alone, and dv with dk, du with dw: the call takes other routes
+    # then (dv from the forward call instead of the dk chain's first pass at N = 16384, du or
+    # dw alone from the forward call on a conjugated copy of the spectrum, dk alone from the
+    # spectrum-only pass); every result is checked against the oracle
+    L = N - 37
+    _say(f"bwd subsets {dtype} N={N} B={B} H={H} masked={masked}")
+    inp, dy = _case(B, H, N, L, dtype, "both", 71)
+    mask = None
+    if masked:   # a band on every channel, a random mask on the second
+        mask = synth.band_mask(H, 27)
+        mask[1] = synth.random_mask(H, seed=N + 9)[1]
+    want = oracle.fft_bwd(inp.f64("u"), inp.f64("k"), dy.double().numpy(), inp.f64("w"), inp.f64("v"), mask)
+    dev = torch.device("cuda")
+    u, k, w, v, g = (t.to(dev) for t in (inp.u, inp.k, inp.w, inp.v, dy))
+    m = None if mask is None else torch.from_numpy(mask).to(dev)
+    K_f = fc.alloc_filter(H, N, u.dtype, dev)
+    fc.fftconv_prepare_filter(k, N, K_f, fc.alloc_workspace(1, H, N, u.dtype, dev))
+    ws = torch.empty(fc.fftconv_bwd_workspace_bytes(B, H, N, u.dtype), dtype=torch.uint8, device=dev)
+    names = ("du", "dk", "dw", "dv")
+    for subset in (("du",), ("dw",), ("dv",), ("dk",), ("dv", "dk"), ("du", "dw")):
+        outs = {n: (torch.empty((H, L), dtype=u.dtype, device=dev) if n == "dk" else torch.empty_like(u))
+                for n in subset}
+        fc.fftconv_bwd(g, u, K_f, w, v, outs.get("du"), outs.get("dk"), outs.get("dw"), outs.get("dv"), L, m, ws)
+        torch.cuda.synchronize()
+        for n in subset:
+            check(outs[n].float().cpu().double().numpy(), want[names.index(n)], TOL[dtype], f"{n} of {subset}")
