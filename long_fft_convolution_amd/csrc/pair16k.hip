@@ -212,9 +212,14 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
         s_tw3[i] = reinterpret_cast<const h8 *>(tb.tw3)[i];
     }
     if constexpr (R < 32) {
+        // phase 1 contracts only the slots n_c < R/2 of each sub-pair, half of the tile's K
+        // slots (8 g + j, j < 4), so its data operand carries both planes in one h8,
+        // (x_a j = 0..3 | x_b j = 0..3), and one product per plane does:
+        // Re = [Re O | -Im O] . x, Im = [Im O | Re O] . x  (O: the block-diagonal DFT-R tile)
         if (tid < 128) {
-            s_out[tid] = reinterpret_cast<const h8 *>(ot.o1r)[tid];
-            s_out[128 + tid] = reinterpret_cast<const h8 *>(ot.o1i)[tid];
+            const h8 o_r = reinterpret_cast<const h8 *>(ot.o1r)[tid], o_i = reinterpret_cast<const h8 *>(ot.o1i)[tid];
+            s_out[tid] = cat8(lo4(o_r), lo4(neg8(o_i)));
+            s_out[128 + tid] = cat8(lo4(o_i), lo4(o_r));
         } else if (tid < 192) {
             s_out[256 + tid - 128] = reinterpret_cast<const h8 *>(ot.o3r)[tid - 128];
             s_out[320 + tid - 128] = reinterpret_cast<const h8 *>(ot.o3i)[tid - 128];
@@ -394,8 +399,10 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
                     if constexpr (R == 32) {
                         cm_constA(Fr[nt], Fi[nt], nFi[nt], br, bi, ar, ai);   // rows f_c = 16nt + 4g + i, cols n_ab
                     } else {   // block-diagonal DFT-R tile (rows: sub-pair, f_c), read at use
-                        const h8 o_r = s_out[nt * 64 + lane], o_i = s_out[128 + nt * 64 + lane];
-                        cm_constA(o_r, o_i, neg8(o_i), br, bi, ar, ai);
+                        const h8 bx = cat8(lo4(br), lo4(bi));
+                        const f4 z = {0.f, 0.f, 0.f, 0.f};
+                        ar = mfma(s_out[nt * 64 + lane], bx, z);
+                        ai = mfma(s_out[128 + nt * 64 + lane], bx, z);
                     }
                     yr[qq][par][nt] = to_h4(ar);
                     yi[qq][par][nt] = to_h4(ai);
