@@ -781,7 +781,8 @@ pair16k_kernel(const T *__restrict__ u, const T *__restrict__ w, const T *__rest
             for (int tt = 0; tt < kTilesPerWave; ++tt) {
                 const uint32_t o = stw + ((64 * tt) ^ cq);
                 stu(s8, o, ya[tt]);                                     // row n_c = c of sequence a
-                stu(s8 + 2 * kR1Plane, o, yb[tt]);                      // plane 1: sequence b
+                if (!CORR) stu(s8 + 2 * kR1Plane, o, yb[tt]);           // plane 1: sequence b (kCorr: the
+                                                                        // real part only, yb is dropped)
             }
             uint4 vq2[8];
             if (DUAL) {   // (issued before the next input batch: vmcnt waits are in order)
