@@ -186,7 +186,7 @@ fftconv_status_t fftconv_fwd_taps(const void *u, const void *k, const void *w, c
                                   void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Device scratch bytes fftconv_bwd needs for this shape (0 for unsupported
- * N or dtype).  It holds the conjugated spectrum, u*w, the spectra of the
+ * N or dtype).  It holds room for a conjugated spectrum, u*w, the spectra of the
  * B*H sequences u*w, their correlations with v*dy, and the forward
  * workspace; at N = 1024 with fp16 or bf16 storage only the conjugated
  * spectrum (dk is accumulated on chip there); at N = 2048 .. 16384 with fp16
@@ -201,8 +201,13 @@ size_t fftconv_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, fftconv_dtyp
  *   du = w * corr(g, k),  dw = u * corr(g, k)  (dw needs w; NULL = skip)
  *   dk[h, s] = sum_b sum_t g[b,h,t] x[b,h,t-s], s < L_filter  (NULL = skip)
  * where corr(g, k)[t] = sum_s k[s] g[t+s] is the adjoint of the causal
- * convolution: the forward kernels run on the conjugated spectrum of K_f.
- * With a sparsity mask the gradients are those of the masked forward pass.
+ * convolution: the forward kernels run on the conjugated spectrum of K_f
+ * (at N = 1024 .. 16384 in fp16 / bf16 with both du and dw asked for, one
+ * kernel forms both and conjugates the bins as it reads K_f; otherwise a
+ * conjugated copy is made in the workspace).  At N = 16384 in fp16 / bf16
+ * with dv and dk asked for, dv comes from the same pass over u, w as the
+ * spectra dk needs.  With a sparsity mask the gradients are those of the
+ * masked forward pass.
  *   dy, u, w, v  (B, H, N) device arrays as in fftconv_fwd (w, v may be NULL)
  *   K_f          the spectrum fftconv_fwd used (same H, L_filter, N, dtype)
  *   du, dw, dv   (B, H, N) outputs; dk (H, L_filter) output, all in dtype
